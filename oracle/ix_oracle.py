@@ -1,0 +1,226 @@
+"""CPU oracle for the indexer -> top-k -> sparse-attention path, in fp64.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package entry's smoke check and
+the benchmark's CPU-baseline leg may import or run this module.  The HIP library never
+calls it, links it or shares code with it, and this module imports nothing from the
+library or its package (inputs reach it as plain numpy arrays).
+
+It is the plain definition of what the path computes, written out with no blocking,
+fusion or reordering:
+
+  * Stage 1 (coarse scoring): an indexer scores every causal key for the current
+    query ("GLM 5.2: How Four Co-Designed Mechanisms Beat Raw Scale", Part II,
+    "DeepSeek Sparse Attention", Stage 1).  The indexer runs in FP8 (twiscan post on
+    GLM-5.2's IndexShare).  Concrete form adopted: per indexer head h, the dot product
+    of the FP8 query row q_I[t,h,:] with the FP8 key row k_I[s,:]; then ReLU; then
+    the sum over heads weighted by w[t,h].
+  * Stage 2 (fine selection): keep the k best-scoring keys (k = 2048 at full size;
+    same page, Stage 2).  Ties go to the lower key index.  Output is the ascending
+    list of kept positions padded with -1.
+  * Attention over only the kept keys: ordinary softmax attention restricted to the
+    selected rows (same page, Stage 2; the twiscan post).
+  * IndexShare: the selection is computed once per group of 4 sparse layers and
+    reused by the others (same page, "IndexShare: Amortizing the Indexer"; the
+    twiscan post; "The 1M Context Mirage", "IndexShare: What Actually Works").
+
+Exactness.  Every e4m3 value is an integer multiple of 2^-9 below 2^9 in magnitude, so
+each product is a multiple of 2^-18 below 2^18 and any partial sum of at most 128 such
+products needs at most 43 significant bits: the per-head dot products below are exact
+in fp64 whatever order BLAS adds them in.  The only roundings are in w*x, the head sum
+and the attention arithmetic (relative ~1e-16).
+
+Readings where the pages are silent (all listed with their reasons in the design notes):
+  visibility  key s is visible to the query at position p iff s <= p and s < kv_len
+              (a query sees its own key); n_t = min(p + 1, kv_len).
+  ties        lowest key index wins; fewer than k visible keys -> take all, pad -1.
+  scale       the indexer score carries no extra scale factor.
+  heads       one indexer key row per token, shared by all indexer heads;
+              head weights are per (query token, indexer head).
+  empty       an empty selection gives out = 0 and lse = -inf.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------
+# Storage formats
+# ----------------------------------------------------------------------------------
+
+
+def _e4m3_value(code: int) -> float:
+    """OCP FP8 E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+
+    Exponent field 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there is no
+    infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """e4m3 bytes (uint8 array) -> exact fp64 values."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64: a bf16 is the upper half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------
+# Stage 1: indexer scores
+# ----------------------------------------------------------------------------------
+
+
+def visible_count(pos0: int, kv_len: int, t: int) -> int:
+    """Number of keys visible to query t of a sequence: keys [0, n_t)."""
+    return max(0, min(int(pos0) + t + 1, int(kv_len)))
+
+
+def index_scores(q_row: np.ndarray, keys: np.ndarray, w_row: np.ndarray) -> np.ndarray:
+    """score[s] = sum_h w[h] * max(0, q[h,:] . k[s,:]) for the given key rows.
+
+    q_row [H_I, d_I] fp64, keys [n, d_I] fp64, w_row [H_I] fp64 -> [n] fp64.
+    (Stage 1 of "DeepSeek Sparse Attention" with the ReLU / weighted-head-sum form.)
+    """
+    x = q_row @ keys.T                    # [H_I, n]: per-head dot products (exact)
+    return w_row @ np.maximum(x, 0.0)     # ReLU, then the w-weighted sum over heads
+
+
+KEY_CHUNK = 1 << 17  # keys per call of index_scores (each key's score is independent)
+
+
+def score_row(qI_row_u8, keys_f64, w_row, n_t) -> np.ndarray:
+    """Scores of the n_t visible keys for one query (decoded keys given)."""
+    q = decode_e4m3(qI_row_u8)
+    w = np.asarray(w_row, dtype=np.float64)
+    out = np.empty(n_t, dtype=np.float64)
+    for s0 in range(0, n_t, KEY_CHUNK):
+        s1 = min(n_t, s0 + KEY_CHUNK)
+        out[s0:s1] = index_scores(q, keys_f64[s0:s1], w)
+    return out
+
+
+def score_matrix(q_I, k_I, w, q_pos0, kv_len, b: int, rows: Sequence[int], S_max: int):
+    """Dense [len(rows), S_max] fp64 score rows for sequence b; -inf where not visible."""
+    keys = decode_e4m3(k_I[b])
+    out = np.full((len(rows), S_max), -np.inf, dtype=np.float64)
+    for i, t in enumerate(rows):
+        n = visible_count(q_pos0[b], kv_len[b], t)
+        out[i, :n] = score_row(q_I[b, t], keys[:n], w[b, t], n)
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Stage 2: top-k selection
+# ----------------------------------------------------------------------------------
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Keep the first min(k, n) keys in (score descending, index ascending) order.
+
+    Returns int64 [k]: the kept positions in ascending order, then -1 padding.
+    """
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -scores))  # primary -score, then index
+    kept = np.sort(order[: min(k, n)])
+    out = np.full(k, -1, dtype=np.int64)
+    out[: kept.shape[0]] = kept
+    return out
+
+
+def topk_rows(q_I, k_I, w, q_pos0, kv_len, b: int, rows: Sequence[int], k: int,
+              keys_f64=None, return_scores=False):
+    """Selection (and optionally the score rows) for the listed queries of sequence b."""
+    keys = decode_e4m3(k_I[b]) if keys_f64 is None else keys_f64
+    idx = np.empty((len(rows), k), dtype=np.int64)
+    scores: List[np.ndarray] = []
+    for i, t in enumerate(rows):
+        n = visible_count(q_pos0[b], kv_len[b], t)
+        sc = score_row(q_I[b, t], keys[:n], w[b, t], n)
+        idx[i] = select_topk(sc, k)
+        if return_scores:
+            scores.append(sc)
+    return (idx, scores) if return_scores else idx
+
+
+# ----------------------------------------------------------------------------------
+# Attention over the selected keys
+# ----------------------------------------------------------------------------------
+
+
+def sparse_attention_row(q_row, K_seq, V_seq, idx_row, sm_scale: float):
+    """Softmax attention of one query token over its selected key rows.
+
+    q_row [H_q, d] fp64; K_seq, V_seq [S, H_kv, d] fp64; idx_row [k] (-1 = padding).
+    Query head h reads KV head h // (H_q / H_kv).  Returns out [H_q, d], lse [H_q].
+    """
+    H_q, d = q_row.shape
+    H_kv = K_seq.shape[1]
+    grp = H_q // H_kv
+    sel = np.asarray(idx_row)[np.asarray(idx_row) >= 0]
+    out = np.zeros((H_q, d), dtype=np.float64)
+    lse = np.full(H_q, -np.inf, dtype=np.float64)
+    if sel.size == 0:
+        return out, lse
+    for h in range(H_q):
+        Kh = K_seq[sel, h // grp, :]          # gathered key rows [m, d]
+        Vh = V_seq[sel, h // grp, :]
+        logits = sm_scale * (Kh @ q_row[h])   # [m]
+        mx = logits.max()
+        p = np.exp(logits - mx)
+        l = p.sum()
+        out[h] = (p @ Vh) / l
+        lse[h] = mx + math.log(l)
+    return out, lse
+
+
+def sparse_attention_rows(q_bits, K_bits, V_bits, idx, b: int, rows: Sequence[int],
+                          sm_scale: float):
+    """Attention outputs for the listed queries of sequence b (bf16 inputs as bits).
+
+    idx is indexed like rows: idx[i] is the selection of query rows[i].
+    Returns out [len(rows), H_q, d] and lse [len(rows), H_q], fp64.
+    """
+    K = decode_bf16(K_bits[b])
+    V = decode_bf16(V_bits[b])
+    H_q, d = q_bits.shape[2], q_bits.shape[3]
+    out = np.empty((len(rows), H_q, d), dtype=np.float64)
+    lse = np.empty((len(rows), H_q), dtype=np.float64)
+    for i, t in enumerate(rows):
+        q = decode_bf16(q_bits[b, t])
+        out[i], lse[i] = sparse_attention_row(q, K, V, idx[i], sm_scale)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------------
+# IndexShare: one selection per group of layers
+# ----------------------------------------------------------------------------------
+
+
+def indexshare_group(indexer: Dict[str, np.ndarray], layers: Sequence[Dict[str, np.ndarray]],
+                     k: int, b: int, rows: Sequence[int], sm_scale: float):
+    """Selection computed once from the group's indexer inputs, reused by every layer.
+
+    indexer: q_I, k_I, w, q_pos0, kv_len (numpy).  layers: per-layer q, K, V bits.
+    Returns (idx [len(rows), k], [(out, lse) per layer]).
+    """
+    idx = topk_rows(indexer["q_I"], indexer["k_I"], indexer["w"], indexer["q_pos0"],
+                    indexer["kv_len"], b, rows, k)
+    outs = [sparse_attention_rows(L["q"], L["K"], L["V"], idx, b, rows, sm_scale)
+            for L in layers]
+    return idx, outs

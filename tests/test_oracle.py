@@ -1,0 +1,371 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: exact integer arithmetic,
+rational brute force, torch library routines (fp8/bf16 casts, SDPA), closed forms and
+inputs built so that the answer is known by construction.
+"""
+import json
+import math
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ix_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- storage formats
+
+
+def test_e4m3_table_matches_torch_and_spec_points():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.decode_e4m3(np.arange(256, dtype=np.uint8))
+    nan = np.isnan(ref)
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # spec points of OCP E4M3
+    assert ours[0x00] == 0.0 and ours[0x80] == 0.0 and math.copysign(1, ours[0x80]) == -1
+    assert ours[0x01] == 2.0 ** -9          # smallest subnormal
+    assert ours[0x08] == 2.0 ** -6          # smallest normal
+    assert ours[0x38] == 1.0
+    assert ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+
+
+def test_e4m3_values_are_multiples_of_2pow_minus9():
+    v = O.decode_e4m3(np.arange(256, dtype=np.uint8))
+    v = v[~np.isnan(v)]
+    scaled = v * 512.0
+    assert np.array_equal(scaled, np.round(scaled))
+    assert np.abs(v).max() < 2 ** 9
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = O.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------- stage 1: scores
+
+
+def _rand_codes(rng, shape, finite=True):
+    c = rng.integers(0, 256, size=shape, dtype=np.uint32).astype(np.uint8)
+    if finite:
+        c[(c & 0x7F) == 0x7F] = 0x7E  # no NaN codes
+    return c
+
+
+def test_per_head_dot_is_exact_against_int64():
+    rng = np.random.default_rng(1)
+    for d in (64, 128):
+        q = _rand_codes(rng, (64, d))
+        k = _rand_codes(rng, (300, d))
+        q[0, :] = 0x7E   # +448 everywhere: the largest magnitude case
+        k[0, :] = 0x7E
+        k[1, :] = 0xFE   # -448
+        qi = (O.decode_e4m3(q) * 512).astype(np.int64)
+        ki = (O.decode_e4m3(k) * 512).astype(np.int64)
+        exact = qi @ ki.T                          # integers, exact in int64
+        x = O.decode_e4m3(q) @ O.decode_e4m3(k).T  # what index_scores forms
+        assert np.array_equal(x * 2.0 ** 18, exact.astype(np.float64))
+        assert np.array_equal((x * 2.0 ** 18).astype(np.int64), exact)
+
+
+def _fraction_scores(q_codes, k_codes, w, n):
+    """Brute force: sum_h w_h * max(0, sum_c q*k) in exact rationals."""
+    H, d = q_codes.shape
+    qv = [[Fraction(float(O.E4M3_TABLE[q_codes[h, c]])) for c in range(d)] for h in range(H)]
+    out = []
+    for s in range(n):
+        kv = [Fraction(float(O.E4M3_TABLE[k_codes[s, c]])) for c in range(d)]
+        tot = Fraction(0)
+        for h in range(H):
+            x = sum(qv[h][c] * kv[c] for c in range(d))
+            tot += Fraction(float(w[h])) * max(Fraction(0), x)
+        out.append(tot)
+    return out
+
+
+def test_scores_against_rational_brute_force():
+    rng = np.random.default_rng(2)
+    T, S, H, d = 7, 11, 3, 8
+    q = _rand_codes(rng, (1, T, H, d))
+    k = _rand_codes(rng, (1, S, d))
+    w = rng.random((1, T, H)).astype(np.float32)
+    pos0, kvl = np.array([2]), np.array([9])   # ragged: kv_len < S, queries start at 2
+    got = O.score_matrix(q, k, w, pos0, kvl, 0, list(range(T)), S)
+    for t in range(T):
+        n = O.visible_count(2, 9, t)
+        assert n == min(2 + t + 1, 9)
+        ex = _fraction_scores(q[0, t], k[0], w[0, t], n)
+        for s in range(S):
+            if s < n:
+                assert got[t, s] == pytest.approx(float(ex[s]), rel=1e-14, abs=1e-300)
+            else:
+                assert got[t, s] == -np.inf
+
+
+def test_score_special_cases():
+    rng = np.random.default_rng(3)
+    q = _rand_codes(rng, (20, 1, 64))
+    k = _rand_codes(rng, (50, 64))
+    keys = O.decode_e4m3(k)
+    # one head, weight 1: plain ReLU of the dot product
+    for t in range(20):
+        got = O.index_scores(O.decode_e4m3(q[t]), keys, np.ones(1))
+        want = np.maximum(O.decode_e4m3(q[t, 0]) @ keys.T, 0)
+        assert np.array_equal(got, want)
+    # zero weights -> zero scores; doubling weights doubles scores exactly
+    qh = O.decode_e4m3(_rand_codes(rng, (8, 64)))
+    w = rng.random(8)
+    assert np.all(O.index_scores(qh, keys, np.zeros(8)) == 0)
+    assert np.array_equal(O.index_scores(qh, keys, 2 * w), 2 * O.index_scores(qh, keys, w))
+    # permuting heads (queries and weights together) leaves scores unchanged
+    perm = rng.permutation(8)
+    a = O.index_scores(qh, keys, w)
+    b = O.index_scores(qh[perm], keys, w[perm])
+    assert np.allclose(a, b, rtol=1e-15, atol=0)
+    # scores are >= 0 and are 0 exactly when every head's dot is <= 0
+    x = qh @ keys.T
+    assert np.all(a >= 0)
+    assert np.array_equal(a == 0, np.all(x <= 0, axis=0))
+
+
+# ---------------------------------------------------------------- stage 2: selection
+
+
+def test_select_against_python_sort_with_ties():
+    rng = random.Random(4)
+    for trial in range(200):
+        n = rng.randint(1, 40)
+        k = rng.randint(1, 45)
+        sc = np.array([rng.choice([0.0, 0.0, 1.5, 2.25, rng.random()]) for _ in range(n)])
+        want = sorted(sorted(range(n), key=lambda s: (-sc[s], s))[: min(k, n)])
+        got = O.select_topk(sc, k)
+        assert got[: len(want)].tolist() == want
+        assert np.all(got[len(want):] == -1)
+
+
+def test_select_invariants():
+    rng = np.random.default_rng(6)
+    for n, k in [(1, 1), (5, 8), (100, 17), (64, 64), (1000, 1)]:
+        sc = rng.random(n)
+        sc[rng.integers(0, n, size=n // 3)] = 0.0
+        got = O.select_topk(sc, k)
+        sel = got[got >= 0]
+        assert sel.size == min(k, n)
+        assert np.all(np.diff(sel) > 0)              # ascending, distinct
+        assert sel.min() >= 0 and sel.max() < n
+        if k >= n:
+            assert np.array_equal(sel, np.arange(n))  # everything visible is kept
+
+
+def _e4m3_code(v):
+    codes = np.nonzero(O.E4M3_TABLE == v)[0]
+    assert codes.size >= 1
+    return int(codes[0])
+
+
+def test_sign_partitioned_planting_has_known_top_set():
+    """Queries >= 0, unplanted keys <= 0: their scores are exactly 0.
+
+    Planted keys have all coordinates equal to a distinct positive e4m3 value v_j, the
+    query has all coordinates u, w = 1: score_j = H * d * u * v_j (closed form).
+    The kept set is the planted keys, then the lowest-index zero-score keys.
+    """
+    rng = np.random.default_rng(7)
+    S, H, d, k = 300, 4, 64, 40
+    neg = [c for c in range(256) if O.E4M3_TABLE[c] <= 0 and not np.isnan(O.E4M3_TABLE[c])]
+    k_codes = rng.choice(neg, size=(1, S, d)).astype(np.uint8)
+    planted = sorted(rng.choice(np.arange(50, S), size=12, replace=False).tolist())
+    vals = [0.5 + 0.0625 * i for i in range(8)] + [1.0 + 0.125 * i for i in range(4)]  # exact e4m3
+    rng.shuffle(vals)
+    for s, v in zip(planted, vals):
+        k_codes[0, s, :] = _e4m3_code(v)
+    u = 0.25
+    q_codes = np.full((1, 1, H, d), _e4m3_code(u), dtype=np.uint8)
+    w = np.ones((1, 1, H), dtype=np.float32)
+    pos0, kvl = np.array([S - 1]), np.array([S])
+    idx, scores = O.topk_rows(q_codes, k_codes, w, pos0, kvl, 0, [0], k, return_scores=True)
+    sc = scores[0]
+    for s, v in zip(planted, vals):
+        assert sc[s] == H * d * u * v
+    others = [s for s in range(S) if s not in planted]
+    assert np.all(sc[others] == 0.0)
+    want = sorted(planted + others[: k - len(planted)])
+    assert idx[0].tolist() == want
+    # with k below the planted count, only the best planted keys survive
+    idx2 = O.topk_rows(q_codes, k_codes, w, pos0, kvl, 0, [0], 5)
+    best = [s for s, _ in sorted(zip(planted, vals), key=lambda p: -p[1])[:5]]
+    assert idx2[0].tolist() == sorted(best)
+
+
+def test_query_sees_its_own_key_and_not_the_next():
+    """Self-inclusion: only key p scores > 0 for the query at position p."""
+    S, H, d = 16, 1, 64
+    one = _e4m3_code(1.0)
+    for p in range(S):
+        k_codes = np.zeros((1, S, d), dtype=np.uint8)
+        k_codes[0, p, :] = one
+        if p + 1 < S:
+            k_codes[0, p + 1, :] = _e4m3_code(2.0)   # future key, must stay invisible
+        q_codes = np.full((1, 1, H, d), one, dtype=np.uint8)
+        idx = O.topk_rows(q_codes, k_codes, np.ones((1, 1, H), np.float32),
+                          np.array([p]), np.array([S]), 0, [0], 1)
+        assert idx[0].tolist() == [p]
+
+
+def test_golden_selection_constants():
+    g = json.load(open(os.path.join(GOLDEN, "pages_constants.json")))
+    e = g["selection_limit_example"]
+    rng = np.random.default_rng(8)
+    sc = rng.random(e["previous_tokens"])
+    got = O.select_topk(sc, e["limit"])
+    assert (got >= 0).sum() == e["attended"]
+    s = g["selection_size_at_1m"]
+    assert round(100.0 * s["k"] / s["context"], 1) == s["percent_of_context_stated"]
+
+
+# ---------------------------------------------------------------- attention
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(
+        torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _attn_case(rng, T=40, S=40, H_q=4, H_kv=2, d=16, scale_q=1.0):
+    q = _bf16_bits(rng.standard_normal((1, T, H_q, d)) * scale_q)
+    K = _bf16_bits(rng.standard_normal((1, S, H_kv, d)))
+    V = _bf16_bits(rng.standard_normal((1, S, H_kv, d)))
+    return q, K, V
+
+
+def test_full_selection_equals_dense_causal_sdpa():
+    rng = np.random.default_rng(9)
+    T = S = 40
+    H_q, H_kv, d = 4, 2, 16
+    q, K, V = _attn_case(rng, T, S, H_q, H_kv, d)
+    idx = np.array([[s if s <= t else -1 for s in range(S)] for t in range(T)])
+    sm = 1.0 / math.sqrt(d)
+    out, lse = O.sparse_attention_rows(q, K, V, idx, 0, list(range(T)), sm)
+    qt = torch.from_numpy(O.decode_bf16(q[0])).permute(1, 0, 2)           # [H_q, T, d]
+    Kt = torch.from_numpy(O.decode_bf16(K[0])).permute(1, 0, 2).repeat_interleave(H_q // H_kv, 0)
+    Vt = torch.from_numpy(O.decode_bf16(V[0])).permute(1, 0, 2).repeat_interleave(H_q // H_kv, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, is_causal=True, scale=sm)
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    logits = (qt @ Kt.transpose(1, 2)) * sm
+    mask = torch.ones(T, S, dtype=torch.bool).tril()
+    ref_lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)  # [H_q, T]
+    assert np.allclose(lse, ref_lse.T.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_window_selection_equals_banded_sdpa():
+    rng = np.random.default_rng(10)
+    T = S = 48
+    W, H_q, H_kv, d = 5, 2, 1, 32
+    q, K, V = _attn_case(rng, T, S, H_q, H_kv, d)
+    idx = np.full((T, 8), -1)
+    for t in range(T):
+        win = list(range(max(0, t - W + 1), t + 1))
+        idx[t, : len(win)] = win
+    sm = 0.3
+    out, _ = O.sparse_attention_rows(q, K, V, idx, 0, list(range(T)), sm)
+    qt = torch.from_numpy(O.decode_bf16(q[0])).permute(1, 0, 2)
+    Kt = torch.from_numpy(O.decode_bf16(K[0])).permute(1, 0, 2).expand(H_q, S, d)
+    Vt = torch.from_numpy(O.decode_bf16(V[0])).permute(1, 0, 2).expand(H_q, S, d)
+    tt = torch.arange(T)[:, None]
+    ss = torch.arange(S)[None, :]
+    band = (ss <= tt) & (ss > tt - W)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=band, scale=sm)
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(11)
+    T, S, H_q, H_kv, d = 6, 30, 4, 1, 16
+    q, K, V = _attn_case(rng, T, S, H_q, H_kv, d)
+    Kf, Vf = O.decode_bf16(K[0]), O.decode_bf16(V[0])
+    # k = 1: the output is the selected V row exactly, lse the single logit
+    for t in range(T):
+        j = int(rng.integers(0, S))
+        out, lse = O.sparse_attention_row(O.decode_bf16(q[0, t]), Kf, Vf, np.array([j]), 0.7)
+        for h in range(H_q):
+            assert np.array_equal(out[h], Vf[j, 0])
+            assert lse[h] == pytest.approx(0.7 * O.decode_bf16(q[0, t, h]) @ Kf[j, 0], rel=1e-15)
+    # q = 0: uniform weights -> mean of the selected rows, lse = log(count)
+    sel = np.array([3, 7, 8, 20, -1, -1])
+    out, lse = O.sparse_attention_row(np.zeros((H_q, d)), Kf, Vf, sel, 1.0)
+    assert np.allclose(out, Vf[[3, 7, 8, 20], 0].mean(axis=0)[None, :], rtol=1e-14, atol=1e-15)
+    assert np.allclose(lse, math.log(4), rtol=1e-15)
+    # empty selection: zero output, lse = -inf
+    out, lse = O.sparse_attention_row(np.ones((H_q, d)), Kf, Vf, np.array([-1, -1]), 1.0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    # order of the index list does not matter
+    sel = rng.choice(S, size=12, replace=False)
+    a, la = O.sparse_attention_row(O.decode_bf16(q[0, 0]), Kf, Vf, sel, 0.5)
+    b, lb = O.sparse_attention_row(O.decode_bf16(q[0, 0]), Kf, Vf, sel[::-1].copy(), 0.5)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15) and np.allclose(la, lb, rtol=1e-14)
+
+
+def test_attention_against_python_brute_force():
+    rng = np.random.default_rng(12)
+    T, S, H_q, H_kv, d = 3, 10, 4, 2, 8
+    q, K, V = _attn_case(rng, T, S, H_q, H_kv, d)
+    idx = np.array([[0, 4, 9, -1], [2, 3, -1, -1], [1, 5, 6, 7]])
+    out, lse = O.sparse_attention_rows(q, K, V, idx, 0, [0, 1, 2], 0.35)
+    qf, Kf, Vf = O.decode_bf16(q[0]), O.decode_bf16(K[0]), O.decode_bf16(V[0])
+    for t in range(T):
+        sel = [j for j in idx[t] if j >= 0]
+        for h in range(H_q):
+            g = h // (H_q // H_kv)
+            lg = [0.35 * sum(qf[t, h, c] * Kf[j, g, c] for c in range(d)) for j in sel]
+            z = sum(math.exp(x) for x in lg)
+            for c in range(d):
+                want = sum(math.exp(lg[i]) * Vf[j, g, c] for i, j in enumerate(sel)) / z
+                assert out[t, h, c] == pytest.approx(want, rel=1e-12, abs=1e-13)
+            assert lse[t, h] == pytest.approx(math.log(z), rel=1e-13, abs=1e-13)
+
+
+# ---------------------------------------------------------------- IndexShare
+
+
+def test_indexshare_selection_once_per_group(monkeypatch):
+    g = json.load(open(os.path.join(GOLDEN, "pages_constants.json")))["indexshare_group"]
+    rng = np.random.default_rng(13)
+    T, S, H, dI, k = 9, 9, 4, 64, 4
+    ind = {"q_I": _rand_codes(rng, (1, T, H, dI)), "k_I": _rand_codes(rng, (1, S, dI)),
+           "w": rng.random((1, T, H)).astype(np.float32), "q_pos0": np.array([0]),
+           "kv_len": np.array([S])}
+    layers = []
+    for _ in range(g["group_layers"]):
+        q, K, V = _attn_case(rng, T, S, 2, 1, 16)
+        layers.append({"q": q, "K": K, "V": V})
+    calls = {"n": 0}
+    real = O.topk_rows
+
+    def counting(*a, **kw):
+        calls["n"] += 1
+        return real(*a, **kw)
+
+    monkeypatch.setattr(O, "topk_rows", counting)
+    rows = list(range(T))
+    idx, outs = O.indexshare_group(ind, layers, k, 0, rows, 0.25)
+    assert calls["n"] == 1
+    per_layer_calls = g["group_layers"]   # per-layer indexing runs it once per layer
+    removed = 100 * (1 - calls["n"] / per_layer_calls)
+    assert removed == g["indexer_cost_removed_percent"]
+    for L, (out, lse) in zip(layers, outs):
+        o2, l2 = O.sparse_attention_rows(L["q"], L["K"], L["V"], idx, 0, rows, 0.25)
+        assert np.array_equal(out, o2) and np.array_equal(lse, l2)
