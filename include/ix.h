@@ -1,0 +1,152 @@
+/*
+ * ix.h -- C ABI of the indexed sparse-attention library (libix.so, gfx950).
+ *
+ * The path: an FP8 indexer scores every causal key for each query, the k best keys
+ * are kept, and attention runs over only the kept K/V rows; under IndexShare one
+ * selection serves a group of sparse layers.
+ *   Stage 1 (coarse scoring) and Stage 2 (fine selection, k = 2048 at 1M context):
+ *     "GLM 5.2: How Four Co-Designed Mechanisms Beat Raw Scale", Part II,
+ *     section "DeepSeek Sparse Attention".
+ *   FP8 indexer, ReLU-free statement of "score the keys, keep the top-k", one
+ *   indexer shared across a group of 4 layers: the twiscan post on GLM-5.2's
+ *   IndexShare.
+ *   Selection computed once per block of 4 layers and shared across the block:
+ *     same irys.ai page, section "IndexShare: Amortizing the Indexer".
+ * Concrete indexer form implemented here: for query token t and key token s,
+ *     score(t,s) = sum_h w[t,h] * max(0, sum_c q_I[t,h,c] * k_I[s,c])
+ * with FP8 (OCP e4m3) q_I/k_I, fp32 w, fp32 accumulation.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE memory owned by the caller; the library never
+ *     allocates, frees or synchronises.  Every call is asynchronous on `stream`
+ *     (NULL = the default stream).  Tensors are dense row-major with the listed
+ *     shapes (innermost dimension last); FP8 rows must be 16-byte aligned, bf16 rows
+ *     16-byte aligned (true for any contiguous tensor from a hipMalloc'd base).
+ *   - Visibility: query t of sequence b sits at position q_pos0[b] + t and sees the
+ *     keys s with s <= q_pos0[b] + t and s < kv_len[b] (its own key included):
+ *     n_t = clamp(q_pos0[b] + t + 1, 0, min(kv_len[b], S_max)).
+ *   - Arguments are validated before anything is launched.  On a non-OK status the
+ *     outputs are untouched (IX_ERR_HIP: launch failure, outputs undefined), and
+ *     ix_last_error() returns a message for the calling thread.  No exception or
+ *     abort crosses the ABI.
+ *   - B == 0 or T == 0 is a valid empty call: IX_OK, nothing launched.
+ *   - Supported shapes: d_I in {64,128}; H_I a multiple of 4 in [4,64];
+ *     d in {64,128}; H_q a multiple of H_kv with H_q/H_kv <= 16; 1 <= k <= 2048.
+ *     Other shapes return IX_ERR_UNSUPPORTED (no fallback path exists).
+ *   - Calls are re-entrant; concurrent calls must not share a workspace.
+ */
+#ifndef IX_H
+#define IX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum ix_status {
+  IX_OK = 0,
+  IX_ERR_INVALID = -1,     /* null pointer, negative size, bad range, bad alignment */
+  IX_ERR_UNSUPPORTED = -2, /* shape outside the supported set */
+  IX_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes() */
+  IX_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} ix_status;
+
+/* Indexer inputs (Stage 1 of "DeepSeek Sparse Attention").  All device pointers. */
+typedef struct ix_indexer_args {
+  const uint8_t *q;      /* [B, T, H_I, d_I]  FP8 e4m3 indexer queries             */
+  const uint8_t *k;      /* [B, S_max, d_I]   FP8 e4m3 indexer keys, one row per key
+                                              token, shared by all H_I heads        */
+  const float *w;        /* [B, T, H_I]       fp32 head weights                      */
+  const int32_t *q_pos0; /* [B] position of query t = 0 (query t at q_pos0[b] + t)   */
+  const int32_t *kv_len; /* [B] valid keys per sequence (clamped to S_max)           */
+  int32_t B, T, S_max, H_I, d_I;
+} ix_indexer_args;
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define IX_ABI_VERSION 1
+int32_t ix_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *ix_last_error(void);
+
+/*
+ * ix_score -- indexer scores (Stage 1) for query rows [t_begin, t_end).
+ * scores: fp32 [B, t_end - t_begin, S_max]; entry (b, i, s) is the score of key s
+ * for query t_begin + i, or -inf where s is not visible.  Written for every s.
+ * This materialises score rows and exists to check Stage 1 on its own; ix_topk never
+ * writes the T x S score matrix.
+ * Errors: IX_ERR_INVALID for null pointers, negative dims or
+ * 0 <= t_begin <= t_end <= T violated.
+ */
+ix_status ix_score(const ix_indexer_args *a, int32_t t_begin, int32_t t_end, float *scores,
+                   hipStream_t stream);
+
+/* Workspace bytes ix_topk needs for these arguments (0 on invalid arguments). */
+size_t ix_topk_workspace_bytes(const ix_indexer_args *a, int32_t k);
+
+/*
+ * ix_topk -- Stage 1 + Stage 2 fused: per query, the min(k, n_t) visible keys with
+ * the largest scores, ties broken towards the lower key index ("DeepSeek Sparse
+ * Attention", Stage 2: fine selection).  Scores are streamed through the selection
+ * and never written to memory.
+ * idx:        int32 [B, T, k]: kept key positions in ascending order, then -1.
+ * sel_scores: nullable fp32 [B, T, k]: the score of each kept key, -inf at padding.
+ * ws:         device workspace of at least ix_topk_workspace_bytes(a, k) bytes
+ *             (contents need no initialisation; clobbered).
+ */
+ix_status ix_topk(const ix_indexer_args *a, int32_t k, int32_t *idx, float *sel_scores,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes sparse_attn_fwd needs (0 on invalid arguments; may be 0). */
+size_t sparse_attn_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32_t H_kv, int32_t d,
+                                   int32_t k);
+
+/*
+ * sparse_attn_fwd -- softmax attention of each query over only its selected K/V
+ * rows ("DeepSeek Sparse Attention", Stage 2: the kept tokens get full attention).
+ * q:   bf16 [B, T, H_q, d];  kc, vc: bf16 caches [B, S_max, H_kv, d];
+ * idx: int32 [B, T, k] key positions; entries < 0, >= S_max or >= kv_len[b] are
+ *      skipped (padding).  Query head h reads KV head h / (H_q / H_kv).
+ * kv_len: nullable device int32 [B] (NULL: S_max for every sequence).
+ * out: bf16 [B, T, H_q, d] (round to nearest even).
+ * lse: nullable fp32 [B, T, H_q], natural-log sum of exp of the scaled logits
+ *      (-inf, with out = 0, when a query has no valid entry).
+ * logits are sm_scale * q . k.
+ */
+ix_status sparse_attn_fwd(const void *q, const void *kc, const void *vc, const int32_t *idx,
+                          const int32_t *kv_len, int32_t B, int32_t T, int32_t S_max,
+                          int32_t H_q, int32_t H_kv, int32_t d, int32_t k, float sm_scale,
+                          void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes indexshare_group_fwd needs. */
+size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H_q,
+                                  int32_t H_kv, int32_t d);
+
+/*
+ * indexshare_group_fwd -- IndexShare over a group of n_layers sparse layers: the
+ * selection is computed once from the group's indexer inputs and every layer
+ * attends over that same index tensor ("IndexShare: Amortizing the Indexer";
+ * group of 4 in the pages).  Equivalent to ix_topk(a, k, idx) followed by
+ * sparse_attn_fwd for each layer l with q[l], kc[l], vc[l], out[l], lse[l] and the
+ * shared idx, bit for bit.
+ * q, kc, vc, out: HOST arrays of n_layers device pointers (shapes as in
+ *                 sparse_attn_fwd; kc/vc use S_max = a->S_max, kv_len = a->kv_len).
+ * lse:            nullable host array of n_layers nullable device pointers.
+ * idx:            caller-owned int32 [B, T, k]: written once, read n_layers times.
+ */
+ix_status indexshare_group_fwd(const ix_indexer_args *a, int32_t k, int32_t n_layers,
+                               const void *const *q, const void *const *kc,
+                               const void *const *vc, void *const *out, float *const *lse,
+                               int32_t H_q, int32_t H_kv, int32_t d, float sm_scale,
+                               int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IX_H */

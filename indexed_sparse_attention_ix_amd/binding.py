@@ -1,0 +1,252 @@
+"""ctypes binding of libix.so: the C ABI of include/ix.h with the same entry-point names.
+
+Two layers, both argument marshalling only:
+  * raw functions (`ix_score`, `ix_topk`, `sparse_attn_fwd`, `indexshare_group_fwd`,
+    the `*_workspace_bytes` queries, `ix_last_error`) take device pointers as ints and
+    a HIP stream handle, exactly like the C functions, and raise IxError on a non-OK
+    status;
+  * tensor helpers (`score`, `topk`, `sparse_attention`, `indexshare_group`) take torch
+    device tensors, allocate outputs and workspaces with torch (device memory is
+    plumbing) and launch on torch's current stream.
+Every step of the computation runs in the HIP kernels; there is no other code path.
+If the library is not built (or cannot be loaded) every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_size_t, c_void_p
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
+
+IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4
+STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
+                -3: "IX_ERR_WORKSPACE", -4: "IX_ERR_HIP"}
+
+# every symbol include/ix.h declares
+EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
+           "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
+           "indexshare_group_fwd")
+
+
+class IxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class IndexerArgs(ctypes.Structure):
+    _fields_ = [("q", c_void_p), ("k", c_void_p), ("w", c_void_p), ("q_pos0", c_void_p),
+                ("kv_len", c_void_p), ("B", c_int32), ("T", c_int32), ("S_max", c_int32),
+                ("H_I", c_int32), ("d_I", c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Loads libix.so (once) and declares the prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libix.so not built at {path}; run __graft_entry__.build() or "
+                           f"python -m indexed_sparse_attention_ix_amd.build")
+    L = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    L.ix_abi_version.restype = c_int32
+    L.ix_abi_version.argtypes = []
+    L.ix_last_error.restype = ctypes.c_char_p
+    L.ix_last_error.argtypes = []
+    L.ix_score.restype = c_int32
+    L.ix_score.argtypes = [P(IndexerArgs), c_int32, c_int32, c_void_p, c_void_p]
+    L.ix_topk_workspace_bytes.restype = c_size_t
+    L.ix_topk_workspace_bytes.argtypes = [P(IndexerArgs), c_int32]
+    L.ix_topk.restype = c_int32
+    L.ix_topk.argtypes = [P(IndexerArgs), c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
+                          c_void_p]
+    L.sparse_attn_workspace_bytes.restype = c_size_t
+    L.sparse_attn_workspace_bytes.argtypes = [c_int32] * 6
+    L.sparse_attn_fwd.restype = c_int32
+    L.sparse_attn_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                  c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.indexshare_workspace_bytes.restype = c_size_t
+    L.indexshare_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32, c_int32, c_int32]
+    L.indexshare_group_fwd.restype = c_int32
+    L.indexshare_group_fwd.argtypes = [P(IndexerArgs), c_int32, c_int32, P(c_void_p),
+                                       P(c_void_p), P(c_void_p), P(c_void_p), P(c_void_p),
+                                       c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
+                                       c_size_t, c_void_p]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != IX_OK:
+        raise IxError(status, load().ix_last_error().decode(errors="replace"))
+
+
+# ------------------------------------------------------------------ raw C-ABI mirrors
+
+
+def ix_abi_version() -> int:
+    return load().ix_abi_version()
+
+
+def ix_last_error() -> str:
+    return load().ix_last_error().decode(errors="replace")
+
+
+def ix_score(args: IndexerArgs, t_begin: int, t_end: int, scores: int, stream: int = 0):
+    _check(load().ix_score(ctypes.byref(args), t_begin, t_end, scores, stream))
+
+
+def ix_topk_workspace_bytes(args: IndexerArgs, k: int) -> int:
+    return load().ix_topk_workspace_bytes(ctypes.byref(args), k)
+
+
+def ix_topk(args: IndexerArgs, k: int, idx: int, sel_scores: int, ws: int, ws_bytes: int,
+            stream: int = 0):
+    _check(load().ix_topk(ctypes.byref(args), k, idx, sel_scores, ws, ws_bytes, stream))
+
+
+def sparse_attn_workspace_bytes(B, T, H_q, H_kv, d, k) -> int:
+    return load().sparse_attn_workspace_bytes(B, T, H_q, H_kv, d, k)
+
+
+def sparse_attn_fwd(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k, sm_scale, out, lse,
+                    ws, ws_bytes, stream=0):
+    _check(load().sparse_attn_fwd(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
+                                  sm_scale, out, lse, ws, ws_bytes, stream))
+
+
+def indexshare_workspace_bytes(args: IndexerArgs, k, H_q, H_kv, d) -> int:
+    return load().indexshare_workspace_bytes(ctypes.byref(args), k, H_q, H_kv, d)
+
+
+def _ptr_array(ptrs: Optional[Sequence[int]]):
+    if ptrs is None:
+        return None
+    arr = (c_void_p * len(ptrs))(*[p if p else None for p in ptrs])
+    return ctypes.cast(arr, ctypes.POINTER(c_void_p)), arr
+
+
+def indexshare_group_fwd(args: IndexerArgs, k, n_layers, q, kc, vc, out, lse, H_q, H_kv, d,
+                         sm_scale, idx, ws, ws_bytes, stream=0):
+    keep = []
+    conv = []
+    for ptrs in (q, kc, vc, out, lse):
+        r = _ptr_array(ptrs)
+        if r is None:
+            conv.append(None)
+        else:
+            conv.append(r[0])
+            keep.append(r[1])
+    _check(load().indexshare_group_fwd(ctypes.byref(args), k, n_layers, conv[0], conv[1],
+                                       conv[2], conv[3], conv[4], H_q, H_kv, d, sm_scale, idx,
+                                       ws, ws_bytes, stream))
+
+
+# ------------------------------------------------------------------ torch tensor helpers
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream() -> int:
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def indexer_args(q_I, k_I, w, q_pos0, kv_len) -> IndexerArgs:
+    """Builds the C struct from device tensors q_I [B,T,H_I,d_I] u8, k_I [B,S,d_I] u8,
+    w [B,T,H_I] f32, q_pos0 [B] i32, kv_len [B] i32 (all contiguous)."""
+    B, T, H, D = q_I.shape
+    S = k_I.shape[1]
+    for t in (q_I, k_I, w, q_pos0, kv_len):
+        assert t.is_contiguous(), "indexer tensors must be contiguous"
+    return IndexerArgs(_ptr(q_I), _ptr(k_I), _ptr(w), _ptr(q_pos0), _ptr(kv_len), B, T, S, H, D)
+
+
+def workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def score(q_I, k_I, w, q_pos0, kv_len, t_begin=0, t_end=None):
+    """fp32 scores [B, t_end - t_begin, S_max] (-inf where not visible)."""
+    torch = _torch()
+    a = indexer_args(q_I, k_I, w, q_pos0, kv_len)
+    t_end = a.T if t_end is None else t_end
+    out = torch.empty((a.B, t_end - t_begin, a.S_max), dtype=torch.float32, device=q_I.device)
+    ix_score(a, t_begin, t_end, _ptr(out), _stream())
+    return out
+
+
+def topk(q_I, k_I, w, q_pos0, kv_len, k, with_scores=False, ws=None):
+    """idx int32 [B,T,k] (ascending, -1 padded) and optionally the kept scores."""
+    torch = _torch()
+    a = indexer_args(q_I, k_I, w, q_pos0, kv_len)
+    idx = torch.empty((a.B, a.T, k), dtype=torch.int32, device=q_I.device)
+    sel = torch.empty((a.B, a.T, k), dtype=torch.float32, device=q_I.device) if with_scores else None
+    nb = ix_topk_workspace_bytes(a, k)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, q_I.device)
+    ix_topk(a, k, _ptr(idx), _ptr(sel), _ptr(ws), ws.numel(), _stream())
+    return (idx, sel) if with_scores else idx
+
+
+def sparse_attention(q, K, V, idx, sm_scale, kv_len=None, with_lse=False, ws=None):
+    """bf16 out [B,T,H_q,d] (and fp32 lse [B,T,H_q]) over the selected rows."""
+    torch = _torch()
+    B, T, H_q, d = q.shape
+    S, H_kv = K.shape[1], K.shape[2]
+    k = idx.shape[2]
+    for t in (q, K, V, idx):
+        assert t.is_contiguous(), "attention tensors must be contiguous"
+    out = torch.empty_like(q)
+    lse = torch.empty((B, T, H_q), dtype=torch.float32, device=q.device) if with_lse else None
+    nb = sparse_attn_workspace_bytes(B, T, H_q, H_kv, d, k)
+    if nb and (ws is None or ws.numel() < nb):
+        ws = workspace(nb, q.device)
+    sparse_attn_fwd(_ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(kv_len), B, T, S, H_q, H_kv, d,
+                    k, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws) if nb else 0,
+                    ws.numel() if (nb and ws is not None) else 0, _stream())
+    return (out, lse) if with_lse else out
+
+
+def indexshare_group(q_I, k_I, w, q_pos0, kv_len, k, layers, sm_scale, with_lse=False,
+                     ws=None, idx=None, outs=None):
+    """One selection for the group, attention for every layer.
+
+    layers: list of dicts with q, K, V device tensors.  Returns (idx, [out per layer])
+    (and [lse per layer] when with_lse).
+    """
+    torch = _torch()
+    a = indexer_args(q_I, k_I, w, q_pos0, kv_len)
+    q0 = layers[0]["q"]
+    B, T, H_q, d = q0.shape
+    H_kv = layers[0]["K"].shape[2]
+    if idx is None:
+        idx = torch.empty((a.B, a.T, k), dtype=torch.int32, device=q_I.device)
+    if outs is None:
+        outs = [torch.empty_like(L["q"]) for L in layers]
+    lses = ([torch.empty((B, T, H_q), dtype=torch.float32, device=q0.device) for _ in layers]
+            if with_lse else None)
+    nb = indexshare_workspace_bytes(a, k, H_q, H_kv, d)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, q_I.device)
+    indexshare_group_fwd(a, k, len(layers), [_ptr(L["q"]) for L in layers],
+                         [_ptr(L["K"]) for L in layers], [_ptr(L["V"]) for L in layers],
+                         [_ptr(o) for o in outs], [_ptr(x) for x in lses] if lses else None,
+                         H_q, H_kv, d, float(sm_scale), _ptr(idx), _ptr(ws), ws.numel(),
+                         _stream())
+    return (idx, outs, lses) if with_lse else (idx, outs)

@@ -1,0 +1,215 @@
+// C ABI of libix: argument validation, workspace sizing, dispatch, error reporting,
+// and the IndexShare group driver ("IndexShare: Amortizing the Indexer" in "GLM 5.2:
+// How Four Co-Designed Mechanisms Beat Raw Scale", Part II: the selection runs once
+// per block of layers and is shared across the block).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ix_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ix_status fail(ix_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ix_status fail(ix_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ix_status ok() {
+  g_err.clear();
+  return IX_OK;
+}
+
+ix_status hip_fail(hipError_t e, const char* what) {
+  return fail(IX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Returns IX_OK and sets *empty when B*T == 0.
+ix_status check_indexer(const ix_indexer_args* a, bool* empty) {
+  if (!a) return fail(IX_ERR_INVALID, "indexer args pointer is NULL");
+  if (a->B < 0 || a->T < 0 || a->S_max < 0 || a->H_I < 0 || a->d_I < 0)
+    return fail(IX_ERR_INVALID, "negative size (B=%d T=%d S_max=%d H_I=%d d_I=%d)", a->B, a->T,
+                a->S_max, a->H_I, a->d_I);
+  if (a->d_I != 64 && a->d_I != 128)
+    return fail(IX_ERR_UNSUPPORTED, "d_I=%d unsupported (64 or 128)", a->d_I);
+  if (a->H_I < 4 || a->H_I > 64 || a->H_I % 4 != 0)
+    return fail(IX_ERR_UNSUPPORTED, "H_I=%d unsupported (multiple of 4 in [4,64])", a->H_I);
+  *empty = (a->B == 0 || a->T == 0);
+  if (*empty) return IX_OK;
+  if (a->S_max < 1) return fail(IX_ERR_INVALID, "S_max=%d must be >= 1", a->S_max);
+  if (!a->q || !a->k || !a->w || !a->q_pos0 || !a->kv_len)
+    return fail(IX_ERR_INVALID, "NULL indexer tensor pointer");
+  if (!aligned16(a->q) || !aligned16(a->k))
+    return fail(IX_ERR_INVALID, "FP8 q/k base pointers must be 16-byte aligned");
+  const double k_bytes = (double)a->B * a->S_max * a->d_I;
+  const double q_bytes = (double)a->B * a->T * a->H_I * a->d_I;
+  if (k_bytes > 9.0e18 || q_bytes > 9.0e18) return fail(IX_ERR_INVALID, "tensor too large");
+  if ((int64_t)a->B * a->T > (int64_t)0x7FFFFFFF)
+    return fail(IX_ERR_UNSUPPORTED, "B*T=%lld exceeds the grid limit",
+                (long long)((int64_t)a->B * a->T));
+  return IX_OK;
+}
+
+ix_status check_k(int32_t k) {
+  if (k < 1 || k > 2048) return fail(IX_ERR_UNSUPPORTED, "k=%d unsupported (1..2048)", k);
+  return IX_OK;
+}
+
+ix_status check_attn_shape(int32_t B, int32_t T, int32_t S_max, int32_t H_q, int32_t H_kv,
+                           int32_t d, int32_t k, bool* empty) {
+  if (B < 0 || T < 0 || S_max < 0 || H_q < 0 || H_kv < 0 || d < 0)
+    return fail(IX_ERR_INVALID, "negative size (B=%d T=%d S_max=%d H_q=%d H_kv=%d d=%d)", B, T,
+                S_max, H_q, H_kv, d);
+  if (d != 64 && d != 128) return fail(IX_ERR_UNSUPPORTED, "d=%d unsupported (64 or 128)", d);
+  if (H_kv < 1 || H_q < 1 || H_q % H_kv != 0 || H_q / H_kv > 16)
+    return fail(IX_ERR_UNSUPPORTED, "H_q=%d H_kv=%d unsupported (H_q multiple of H_kv, ratio <= 16)",
+                H_q, H_kv);
+  ix_status st = check_k(k);
+  if (st != IX_OK) return st;
+  *empty = (B == 0 || T == 0);
+  if (*empty) return IX_OK;
+  if (S_max < 1) return fail(IX_ERR_INVALID, "S_max=%d must be >= 1", S_max);
+  if ((int64_t)B * T * H_kv > (int64_t)0x7FFFFFFF / 64)
+    return fail(IX_ERR_UNSUPPORTED, "B*T*H_kv too large for one launch");
+  return IX_OK;
+}
+
+ix_status check_attn_ptrs(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                          const void* out) {
+  if (!q || !kc || !vc || !idx || !out) return fail(IX_ERR_INVALID, "NULL attention tensor pointer");
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc))
+    return fail(IX_ERR_INVALID, "bf16 q/kc/vc base pointers must be 16-byte aligned");
+  return IX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ix_abi_version(void) { return IX_ABI_VERSION; }
+
+const char* ix_last_error(void) { return g_err.c_str(); }
+
+ix_status ix_score(const ix_indexer_args* a, int32_t t_begin, int32_t t_end, float* scores,
+                   hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_indexer(a, &empty);
+  if (st != IX_OK) return st;
+  if (t_begin < 0 || t_end < t_begin || t_end > a->T)
+    return fail(IX_ERR_INVALID, "row range [%d,%d) outside [0,%d)", t_begin, t_end, a->T);
+  if (empty || t_end == t_begin) return ok();
+  if (!scores) return fail(IX_ERR_INVALID, "scores pointer is NULL");
+  hipError_t e = ix::launch_ix_score(*a, t_begin, t_end, scores, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_score launch");
+  return ok();
+}
+
+size_t ix_topk_workspace_bytes(const ix_indexer_args* a, int32_t k) {
+  bool empty = false;
+  if (check_indexer(a, &empty) != IX_OK || check_k(k) != IX_OK) return 0;
+  if (empty) return 0;
+  return ix::make_topk_plan(*a, k).ws_bytes;
+}
+
+ix_status ix_topk(const ix_indexer_args* a, int32_t k, int32_t* idx, float* sel_scores, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_indexer(a, &empty);
+  if (st != IX_OK) return st;
+  if ((st = check_k(k)) != IX_OK) return st;
+  if (empty) return ok();
+  if (!idx) return fail(IX_ERR_INVALID, "idx pointer is NULL");
+  const ix::TopkPlan plan = ix::make_topk_plan(*a, k);
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
+                plan.ws_bytes);
+  hipError_t e = ix::launch_ix_topk(*a, k, plan, idx, sel_scores, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_topk launch");
+  return ok();
+}
+
+size_t sparse_attn_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32_t H_kv, int32_t d,
+                                   int32_t k) {
+  bool empty = false;
+  if (check_attn_shape(B, T, 1, H_q, H_kv, d, k, &empty) != IX_OK || empty) return 0;
+  return ix::make_attn_plan(B, T, H_q, H_kv, d, k).ws_bytes;
+}
+
+ix_status sparse_attn_fwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                          const int32_t* kv_len, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
+                          int32_t H_kv, int32_t d, int32_t k, float sm_scale, void* out,
+                          float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
+  if (st != IX_OK) return st;
+  if (empty) return ok();
+  if ((st = check_attn_ptrs(q, kc, vc, idx, out)) != IX_OK) return st;
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  const ix::AttnPlan plan = ix::make_attn_plan(B, T, H_q, H_kv, d, k);
+  if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
+    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
+                plan.ws_bytes);
+  hipError_t e = ix::launch_sparse_attn(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
+                                        sm_scale, out, lse, plan, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse_attn_fwd launch");
+  return ok();
+}
+
+size_t indexshare_workspace_bytes(const ix_indexer_args* a, int32_t k, int32_t H_q, int32_t H_kv,
+                                  int32_t d) {
+  bool empty = false, empty2 = false;
+  if (check_indexer(a, &empty) != IX_OK || check_k(k) != IX_OK) return 0;
+  if (check_attn_shape(a->B, a->T, a->S_max, H_q, H_kv, d, k, &empty2) != IX_OK) return 0;
+  if (empty) return 0;
+  const size_t t = ix::make_topk_plan(*a, k).ws_bytes;
+  const size_t s = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k).ws_bytes;
+  return t > s ? t : s;  // used one after the other on the same stream
+}
+
+ix_status indexshare_group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_layers,
+                               const void* const* q, const void* const* kc, const void* const* vc,
+                               void* const* out, float* const* lse, int32_t H_q, int32_t H_kv,
+                               int32_t d, float sm_scale, int32_t* idx, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  bool empty = false, empty2 = false;
+  ix_status st = check_indexer(a, &empty);
+  if (st != IX_OK) return st;
+  if ((st = check_k(k)) != IX_OK) return st;
+  if ((st = check_attn_shape(a->B, a->T, a->S_max, H_q, H_kv, d, k, &empty2)) != IX_OK) return st;
+  if (n_layers < 1) return fail(IX_ERR_INVALID, "n_layers=%d must be >= 1", n_layers);
+  if (empty) return ok();
+  if (!idx) return fail(IX_ERR_INVALID, "idx pointer is NULL");
+  if (!q || !kc || !vc || !out) return fail(IX_ERR_INVALID, "NULL per-layer pointer array");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_attn_ptrs(q[l], kc[l], vc[l], idx, out[l])) != IX_OK) return st;
+  }
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  const ix::TopkPlan tp = ix::make_topk_plan(*a, k);
+  const ix::AttnPlan ap = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k);
+  const size_t need = tp.ws_bytes > ap.ws_bytes ? tp.ws_bytes : ap.ws_bytes;
+  if (!ws || ws_bytes < need)
+    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
+  hipError_t e = ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexshare selection launch");
+  for (int l = 0; l < n_layers; ++l) {
+    e = ix::launch_sparse_attn(q[l], kc[l], vc[l], idx, a->kv_len, a->B, a->T, a->S_max, H_q,
+                               H_kv, d, k, sm_scale, out[l], lse ? lse[l] : nullptr, ap, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexshare attention launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Host-side plans and launcher entry points shared by the ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ix.h"
+
+namespace ix {
+
+// How the fused indexer + selection is cut into wave units.
+struct TopkPlan {
+  int qc;         // queries per wave (4: 4 queries x 4 heads per MFMA column block;
+                  //                   1: 1 query  x 16 heads)
+  int hc;         // heads per MFMA column block (16 / qc)
+  int g;          // MFMA column blocks per key tile (H_I / hc)
+  int gmax;       // compiled bound on g
+  int qgroups;    // ceil(T / qc) query groups per sequence
+  int n_splits;   // key splits per query (1: the wave writes the final selection)
+  int split_len;  // keys per split (multiple of 16)
+  int cap;        // candidate-buffer entries per (query, split)
+  int64_t units;  // wave units = B * qgroups * n_splits
+  size_t cand_bytes, cnt_bytes, ws_bytes;
+};
+
+TopkPlan make_topk_plan(const ix_indexer_args& a, int k);
+
+// Sparse attention launch shape.
+struct AttnPlan {
+  int n_splits;     // blocks per (query, kv head); >1 writes partials then combines
+  int chunks;       // ceil(k / 32)
+  int chunks_per_split;
+  size_t ws_bytes;
+};
+
+AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k);
+
+hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, float* scores,
+                           hipStream_t stream);
+hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& p, int32_t* idx,
+                          float* sel_scores, void* ws, hipStream_t stream);
+hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                              const int32_t* kv_len, int B, int T, int S_max, int H_q, int H_kv,
+                              int d, int k, float sm_scale, void* out, float* lse,
+                              const AttnPlan& p, void* ws, hipStream_t stream);
+
+}  // namespace ix

@@ -1,0 +1,354 @@
+// Sparse attention over the selected keys ("GLM 5.2: How Four Co-Designed Mechanisms
+// Beat Raw Scale", Part II, "DeepSeek Sparse Attention", Stage 2: the kept tokens get
+// full attention).  For each query token and KV head:
+//   p = softmax_j(sm_scale * q_h . K[idx_j]),  out_h = sum_j p_j V[idx_j].
+//
+// Block = 4 waves on one (query token, KV head); the selection is cut into chunks
+// of 32 entries and wave w takes chunks w, w+4, ...  Per chunk, the 32 gathered K rows
+// go straight from memory into bf16 MFMA A operands (one 64-byte contiguous piece of a
+// row per lane per instruction), S^T = K Q^T puts keys on rows and the (up to 16)
+// query heads sharing the KV head on columns, and an online softmax in the exp2
+// domain keeps one running max per head.  The gathered V rows are staged in LDS so
+// that the PV product can read them key-major; the probability operand comes
+// straight from the lanes that computed S^T (keys {4g+i, 16+4g+i} in lane group g,
+// matched by the same key order in the V operand).  The four waves' (m, l, O) are
+// merged through LDS at the end.  Small batches split the selection over several
+// blocks and merge the normalised partials by their log-sum-exp.
+#include "ix_common.h"
+#include "ix_internal.h"
+
+namespace ix {
+
+namespace {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnBlock = kAttnWaves * kWave;
+constexpr int kChunk = 32;
+constexpr int kVPad = 4;  // bf16 elements of padding per staged V row
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* idx;
+  const int32_t* kv_len;
+  int B, T, S_max, H_q, H_kv, grp, k;
+  float scale_log2;  // sm_scale * log2(e)
+  uint16_t* out;
+  float* lse;
+  int n_splits, chunks, chunks_per_split;
+  float* part_o;    // [rows * H_kv * n_splits][16][D] normalised partial outputs
+  float* part_lse;  // [rows * H_kv * n_splits][16] natural-log partial lse
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, ld_global_16(p));
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) {
+  constexpr int MC = D / 32;   // depth chunks of the QK^T product
+  constexpr int NT = D / 16;   // output column tiles of the PV product
+  constexpr int VROW = D + kVPad;
+  __shared__ __attribute__((aligned(16))) uint16_t vs_all[kAttnWaves][kChunk * VROW];
+  __shared__ float ml_all[kAttnWaves][2][16];
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int r16 = lane & 15, lg = lane >> 4;
+  const int split = blockIdx.x % p.n_splits;
+  const int64_t rk = blockIdx.x / p.n_splits;  // (b*T + t) * H_kv + kvh
+  const int kvh = (int)(rk % p.H_kv);
+  const int64_t row = rk / p.H_kv;             // b*T + t
+  const int b = (int)(row / p.T);
+  int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
+  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+
+  // Q as the B operand of S^T = K Q^T: column = head, depth slice [32m + 8lg, +8)
+  bf16x8 qb[MC];
+  const bool hvalid = r16 < p.grp;
+  {
+    const int head = kvh * p.grp + (hvalid ? r16 : 0);
+    const uint16_t* qrow = p.q + ((size_t)row * p.H_q + head) * D;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      qb[m] = load_bf16x8(qrow + 32 * m + 8 * lg);
+      if (!hvalid) qb[m] = (bf16x8){};
+    }
+  }
+
+  const int32_t* irow = p.idx + (size_t)row * p.k;
+  const size_t kv_stride = (size_t)p.H_kv * D;
+  const uint16_t* kbase = p.kc + (size_t)b * p.S_max * kv_stride + (size_t)kvh * D;
+  const uint16_t* vbase = p.vc + (size_t)b * p.S_max * kv_stride + (size_t)kvh * D;
+  uint16_t* vs = vs_all[wid];
+
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  f32x4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int c_begin = split * p.chunks_per_split;
+  const int c_end = min(c_begin + p.chunks_per_split, p.chunks);
+  auto load_idx = [&](int c, int tt) -> int {
+    const int e = c * kChunk + tt * 16 + r16;
+    int j = (c < c_end && e < p.k) ? irow[e] : -1;
+    return (j >= 0 && j < kvl) ? j : -1;
+  };
+  int jn0 = load_idx(c_begin + wid, 0), jn1 = load_idx(c_begin + wid, 1);
+
+  for (int c = c_begin + wid; c < c_end; c += kAttnWaves) {
+    const int j0 = jn0, j1 = jn1;
+    jn0 = load_idx(c + kAttnWaves, 0);
+    jn1 = load_idx(c + kAttnWaves, 1);
+    const size_t r0 = (size_t)(j0 >= 0 ? j0 : 0) * kv_stride;
+    const size_t r1 = (size_t)(j1 >= 0 ? j1 : 0) * kv_stride;
+    bf16x8 ka0[MC], ka1[MC];
+    i32x4 va0[MC], va1[MC];
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      ka0[m] = load_bf16x8(kbase + r0 + 32 * m + 8 * lg);
+      ka1[m] = load_bf16x8(kbase + r1 + 32 * m + 8 * lg);
+      va0[m] = ld_global_16(vbase + r0 + 32 * m + 8 * lg);
+      va1[m] = ld_global_16(vbase + r1 + 32 * m + 8 * lg);
+    }
+    const uint64_t vm0 = ballot64(j0 >= 0), vm1 = ballot64(j1 >= 0);
+
+    // stage V rows (row = key within the chunk)
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      uint16_t* d0 = vs + r16 * VROW + 32 * m + 8 * lg;
+      uint16_t* d1 = vs + (16 + r16) * VROW + 32 * m + 8 * lg;
+      *reinterpret_cast<uint64_t*>(d0) = ((uint64_t)(uint32_t)va0[m][1] << 32) | (uint32_t)va0[m][0];
+      *reinterpret_cast<uint64_t*>(d0 + 4) = ((uint64_t)(uint32_t)va0[m][3] << 32) | (uint32_t)va0[m][2];
+      *reinterpret_cast<uint64_t*>(d1) = ((uint64_t)(uint32_t)va1[m][1] << 32) | (uint32_t)va1[m][0];
+      *reinterpret_cast<uint64_t*>(d1 + 4) = ((uint64_t)(uint32_t)va1[m][3] << 32) | (uint32_t)va1[m][2];
+    }
+
+    // S^T tiles: lane holds keys 16*tt + 4*lg + i for head r16
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      s0 = mfma_bf16_16x16x32(ka0[m], qb[m], s0);
+      s1 = mfma_bf16_16x16x32(ka1[m], qb[m], s1);
+    }
+    float x[8];
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok0 = (vm0 >> (4 * lg + i)) & 1ull;
+      const bool ok1 = (vm1 >> (4 * lg + i)) & 1ull;
+      x[i] = ok0 ? s0[i] * p.scale_log2 : -__builtin_inff();
+      x[4 + i] = ok1 ? s1[i] * p.scale_log2 : -__builtin_inff();
+      mloc = fmaxf(mloc, fmaxf(x[i], x[4 + i]));
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const bool any = m_new != -__builtin_inff();
+    const float alpha = (any && m_run != -__builtin_inff()) ? exp2f(m_run - m_new) : (any ? 0.f : 1.f);
+    float pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pr[e] = (x[e] != -__builtin_inff()) ? exp2f(x[e] - m_new) : 0.f;
+      psum += pr[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // rescale O rows (heads 4*lg + i) by their head's alpha (held by lane 4*lg + i)
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
+
+    // P as the A operand of O += P V: row = head r16, depth slots = keys
+    // {4lg..4lg+3, 16+4lg..16+4lg+3}
+    bf16x8 pa;
+    {
+      uint16_t pb[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = f32_to_bf16_rne(pr[e]);
+      i32x4 pk;
+      pk[0] = (int)((uint32_t)pb[0] | ((uint32_t)pb[1] << 16));
+      pk[1] = (int)((uint32_t)pb[2] | ((uint32_t)pb[3] << 16));
+      pk[2] = (int)((uint32_t)pb[4] | ((uint32_t)pb[5] << 16));
+      pk[3] = (int)((uint32_t)pb[6] | ((uint32_t)pb[7] << 16));
+      pa = __builtin_bit_cast(bf16x8, pk);
+    }
+    lds_wait();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = 16 * nt + r16;
+      uint16_t vv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vv[i] = vs[(4 * lg + i) * VROW + col];
+        vv[4 + i] = vs[(16 + 4 * lg + i) * VROW + col];
+      }
+      i32x4 vk;
+      vk[0] = (int)((uint32_t)vv[0] | ((uint32_t)vv[1] << 16));
+      vk[1] = (int)((uint32_t)vv[2] | ((uint32_t)vv[3] << 16));
+      vk[2] = (int)((uint32_t)vv[4] | ((uint32_t)vv[5] << 16));
+      vk[3] = (int)((uint32_t)vv[6] | ((uint32_t)vv[7] << 16));
+      o[nt] = mfma_bf16_16x16x32(pa, __builtin_bit_cast(bf16x8, vk), o[nt]);
+    }
+    lds_wait();
+  }
+
+  // per-head l: sum the lane-group partials
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  // merge the 4 waves through LDS
+  __syncthreads();
+  float* os = reinterpret_cast<float*>(vs);  // [16][D] floats of this wave
+  static_assert(16 * D * sizeof(float) <= kChunk * VROW * sizeof(uint16_t), "O staging");
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) os[(4 * lg + i) * D + 16 * nt + r16] = o[nt][i];
+  if (lg == 0) {
+    ml_all[wid][0][r16] = m_run;
+    ml_all[wid][1][r16] = l_run;
+  }
+  __syncthreads();
+
+  const float ln2 = 0.69314718055994530942f;
+  for (int e = threadIdx.x; e < 16 * D; e += kAttnBlock) {
+    const int h = e / D, dcol = e % D;
+    if (h >= p.grp) continue;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_all[w][0][h]);
+    float L = 0.f, acc = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = ml_all[w][0][h];
+        const float f = mw == -__builtin_inff() ? 0.f : exp2f(mw - M);
+        L += f * ml_all[w][1][h];
+        acc += f * reinterpret_cast<float*>(vs_all[w])[h * D + dcol];
+      }
+    }
+    const float val = L > 0.f ? acc / L : 0.f;
+    const float lse_v = L > 0.f ? (M + log2f(L)) * ln2 : -__builtin_inff();
+    const int head = kvh * p.grp + h;
+    if (p.n_splits == 1) {
+      p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(val);
+      if (p.lse && dcol == 0) p.lse[(size_t)row * p.H_q + head] = lse_v;
+    } else {
+      const size_t pr = (size_t)blockIdx.x;  // (row*H_kv + kvh) * n_splits + split
+      p.part_o[(pr * 16 + h) * D + dcol] = val;
+      if (dcol == 0) p.part_lse[pr * 16 + h] = lse_v;
+    }
+  }
+}
+
+// Merge of split partials: out = sum_s exp(lse_s - LSE) o_s, LSE = log sum_s exp(lse_s).
+template <int D>
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p) {
+  const int64_t rk = blockIdx.x;  // row * H_kv + kvh
+  const int kvh = (int)(rk % p.H_kv);
+  const int64_t row = rk / p.H_kv;
+  for (int e = threadIdx.x; e < 16 * D; e += blockDim.x) {
+    const int h = e / D, dcol = e % D;
+    if (h >= p.grp) continue;
+    float M = -__builtin_inff();
+    for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, p.part_lse[((size_t)rk * p.n_splits + s) * 16 + h]);
+    float acc = 0.f, L = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int s = 0; s < p.n_splits; ++s) {
+        const size_t pr = (size_t)rk * p.n_splits + s;
+        const float ls = p.part_lse[pr * 16 + h];
+        const float f = ls == -__builtin_inff() ? 0.f : __expf(ls - M);
+        L += f;
+        acc += f * p.part_o[(pr * 16 + h) * D + dcol];
+      }
+    }
+    const int head = kvh * p.grp + h;
+    p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(L > 0.f ? acc / L : 0.f);
+    if (p.lse && dcol == 0)
+      p.lse[(size_t)row * p.H_q + head] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+  }
+}
+
+}  // namespace
+
+AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
+  (void)H_q;
+  AttnPlan p{};
+  p.chunks = (k + kChunk - 1) / kChunk;
+  const int64_t base = (int64_t)B * T * H_kv;
+  int ns = 1;
+  if (base > 0 && base < 1024) {
+    const int64_t want = (2048 + base - 1) / base;
+    int64_t by_chunks = p.chunks / kAttnWaves;  // at least one chunk per wave
+    if (by_chunks < 1) by_chunks = 1;
+    ns = (int)(want < by_chunks ? want : by_chunks);
+  }
+  p.n_splits = ns;
+  p.chunks_per_split = (p.chunks + ns - 1) / ns;
+  if (ns > 1) {
+    const size_t parts = (size_t)base * ns;
+    const size_t o_bytes = parts * 16 * d * sizeof(float);
+    const size_t l_bytes = parts * 16 * sizeof(float);
+    p.ws_bytes = ((o_bytes + 255) / 256) * 256 + ((l_bytes + 255) / 256) * 256;
+  }
+  return p;
+}
+
+hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                              const int32_t* kv_len, int B, int T, int S_max, int H_q, int H_kv,
+                              int d, int k, float sm_scale, void* out, float* lse,
+                              const AttnPlan& pl, void* ws, hipStream_t stream) {
+  AttnArgs x{};
+  x.q = reinterpret_cast<const uint16_t*>(q);
+  x.kc = reinterpret_cast<const uint16_t*>(kc);
+  x.vc = reinterpret_cast<const uint16_t*>(vc);
+  x.idx = idx;
+  x.kv_len = kv_len;
+  x.B = B;
+  x.T = T;
+  x.S_max = S_max;
+  x.H_q = H_q;
+  x.H_kv = H_kv;
+  x.grp = H_q / H_kv;
+  x.k = k;
+  x.scale_log2 = sm_scale * 1.4426950408889634f;
+  x.out = reinterpret_cast<uint16_t*>(out);
+  x.lse = lse;
+  x.n_splits = pl.n_splits;
+  x.chunks = pl.chunks;
+  x.chunks_per_split = pl.chunks_per_split;
+  if (pl.n_splits > 1) {
+    const size_t parts = (size_t)B * T * H_kv * pl.n_splits;
+    const size_t o_bytes = ((parts * 16 * d * sizeof(float) + 255) / 256) * 256;
+    x.part_o = reinterpret_cast<float*>(ws);
+    x.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + o_bytes);
+  }
+  const size_t blocks = (size_t)B * T * H_kv * pl.n_splits;
+  if (d == 128)
+    hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
+  else
+    hipLaunchKernelGGL(sparse_attn_kernel<64>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || pl.n_splits == 1) return err;
+  const size_t cblocks = (size_t)B * T * H_kv;
+  if (d == 128)
+    hipLaunchKernelGGL(sparse_attn_combine_kernel<128>, dim3((unsigned)cblocks), dim3(256), 0, stream, x);
+  else
+    hipLaunchKernelGGL(sparse_attn_combine_kernel<64>, dim3((unsigned)cblocks), dim3(256), 0, stream, x);
+  return hipGetLastError();
+}
+
+}  // namespace ix

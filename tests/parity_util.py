@@ -1,0 +1,94 @@
+"""Acceptance checks shared by the GPU parity tests (HIP path vs the fp64 oracle)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from indexed_sparse_attention_ix_amd import synth
+from oracle import ix_oracle as O
+
+# tolerances
+SCORE_RTOL = 1e-2          # indexer scores, relative
+SCORE_ATOL_FRAC = 1e-6     # absolute floor, as a fraction of the row's largest score
+INDEX_BAND = 1e-3          # swaps allowed among keys within this relative band of the k-th score
+ATTN_MAX_ABS = 2e-2
+ATTN_MEAN_ABS = 2e-3
+ATTN_ROW_REL = 2e-2        # per (row, head) ||o - o_ref||_2 / ||o_ref||_2
+LSE_ABS = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_host_indexer(ind):
+    return {k: v.detach().cpu().numpy() for k, v in ind.items()}
+
+
+def to_host_attn(att):
+    return {k: synth.bf16_bits(v) for k, v in att.items()}
+
+
+def check_scores(gpu_rows: np.ndarray, ref_rows: np.ndarray):
+    """gpu_rows, ref_rows: [R, S] (ref fp64, -inf where not visible)."""
+    masked = np.isneginf(ref_rows)
+    assert np.array_equal(np.isneginf(gpu_rows), masked), "visibility mask differs"
+    g = gpu_rows[~masked].astype(np.float64)
+    r = ref_rows[~masked]
+    rowmax = np.where(masked, 0.0, ref_rows).max(axis=1, keepdims=True)
+    floor = (SCORE_ATOL_FRAC * np.broadcast_to(rowmax, ref_rows.shape))[~masked]
+    err = np.abs(g - r)
+    bad = err > SCORE_RTOL * np.abs(r) + floor
+    assert not bad.any(), f"{bad.sum()} scores outside tolerance; worst rel {np.max(err / np.maximum(np.abs(r), 1e-30))}"
+
+
+def check_index_row(gpu_row: np.ndarray, ref_scores: np.ndarray, k: int, n_t: int, where=""):
+    """Selection acceptance for one query.
+
+    Structure: ascending distinct positions < n_t, exactly min(k, n_t) of them, then -1.
+    Set: equal to the oracle's set except for swaps among keys whose oracle score lies
+    within INDEX_BAND (relative) of the oracle's k-th score (when that score is 0 the band
+    is {0}); the number of keys swapped in equals the number swapped out.
+    """
+    m = min(k, n_t)
+    g = gpu_row[:m]
+    assert np.all(gpu_row[m:] == -1), f"{where}: padding"
+    assert np.all(g >= 0) and np.all(g < n_t), f"{where}: out of visible range"
+    assert np.all(np.diff(g) > 0), f"{where}: not ascending/distinct"
+    ref = O.select_topk(ref_scores, k)[:m]
+    sg, so = set(g.tolist()), set(ref.tolist())
+    d_in, d_out = sg - so, so - sg
+    assert len(d_in) == len(d_out), f"{where}: swap counts differ"
+    if d_in:
+        sk = ref_scores[ref].min()
+        for s in d_in | d_out:
+            if sk == 0.0:
+                assert ref_scores[s] == 0.0, f"{where}: key {s} outside the zero band"
+            else:
+                assert abs(ref_scores[s] - sk) <= INDEX_BAND * sk, (
+                    f"{where}: key {s} score {ref_scores[s]} outside band of {sk}")
+    return len(d_in)
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return O.decode_bf16(synth.bf16_bits(t))
+
+
+def check_attention(out_gpu: np.ndarray, out_ref: np.ndarray, lse_gpu=None, lse_ref=None,
+                    where=""):
+    """out_*: [R, H, d] fp64 (GPU bf16 decoded)."""
+    err = np.abs(out_gpu - out_ref)
+    assert err.max() <= ATTN_MAX_ABS, f"{where}: max abs {err.max()}"
+    assert err.mean() <= ATTN_MEAN_ABS, f"{where}: mean abs {err.mean()}"
+    num = np.linalg.norm(out_gpu - out_ref, axis=-1)
+    den = np.linalg.norm(out_ref, axis=-1)
+    rel_ok = (num <= ATTN_ROW_REL * den) | ((den == 0) & (num == 0))
+    assert rel_ok.all(), f"{where}: per-row relative error {np.max(num / np.maximum(den, 1e-30))}"
+    if lse_gpu is not None:
+        both_inf = np.isneginf(lse_gpu) & np.isneginf(lse_ref)
+        assert np.array_equal(np.isneginf(lse_gpu), np.isneginf(lse_ref)), f"{where}: lse -inf"
+        d = np.abs(lse_gpu[~both_inf] - lse_ref[~both_inf])
+        assert d.size == 0 or d.max() <= LSE_ABS, f"{where}: lse err {d.max()}"

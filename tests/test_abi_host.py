@@ -1,0 +1,142 @@
+"""C-ABI library on the host (no GPU): it loads, exports every declared symbol, sizes
+workspaces, and rejects invalid arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from indexed_sparse_attention_ix_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ix.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="libix.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(bd.EXPORTS)
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_clean_error():
+    assert bd.ix_abi_version() == 1
+
+
+FAKE = 1 << 20  # 16-byte aligned non-null stand-in address; never dereferenced on failure
+
+
+def args(**kw):
+    d = dict(q=FAKE, k=FAKE, w=FAKE, q_pos0=FAKE, kv_len=FAKE, B=1, T=128, S_max=128, H_I=64,
+             d_I=128)
+    d.update(kw)
+    return bd.IndexerArgs(d["q"], d["k"], d["w"], d["q_pos0"], d["kv_len"], d["B"], d["T"],
+                          d["S_max"], d["H_I"], d["d_I"])
+
+
+def status_of(fn, *a):
+    try:
+        fn(*a)
+    except bd.IxError as e:
+        return e.status
+    return bd.IX_OK
+
+
+def test_indexer_validation_codes():
+    L = bd.load()
+    assert L.ix_topk(None, 64, FAKE, None, FAKE, 1 << 30, None) == bd.IX_ERR_INVALID
+    assert "NULL" in bd.ix_last_error()
+    assert status_of(bd.ix_topk, args(d_I=96), 64, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_UNSUPPORTED
+    assert status_of(bd.ix_topk, args(H_I=6), 64, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_UNSUPPORTED
+    assert status_of(bd.ix_topk, args(H_I=68), 64, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_UNSUPPORTED
+    assert status_of(bd.ix_topk, args(), 0, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_UNSUPPORTED
+    assert status_of(bd.ix_topk, args(), 4096, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_UNSUPPORTED
+    assert status_of(bd.ix_topk, args(B=-1), 64, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_topk, args(w=0), 64, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_topk, args(q=FAKE + 8), 64, FAKE, 0, FAKE, 1 << 30) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_topk, args(), 64, 0, 0, FAKE, 1 << 30) == bd.IX_ERR_INVALID
+    need = bd.ix_topk_workspace_bytes(args(), 64)
+    assert need > 0
+    assert status_of(bd.ix_topk, args(), 64, FAKE, 0, FAKE, need - 1) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.ix_topk, args(), 64, FAKE, 0, 0, need) == bd.IX_ERR_WORKSPACE
+    assert "workspace" in bd.ix_last_error()
+    # ix_score row range
+    assert status_of(bd.ix_score, args(), -1, 4, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_score, args(), 5, 4, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_score, args(), 0, 129, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_score, args(), 0, 4, 0) == bd.IX_ERR_INVALID
+
+
+def test_empty_calls_launch_nothing():
+    # B == 0 or T == 0: OK without touching any pointer
+    assert status_of(bd.ix_topk, args(B=0, q=0, k=0, w=0, q_pos0=0, kv_len=0), 64, 0, 0, 0, 0) == bd.IX_OK
+    assert status_of(bd.ix_topk, args(T=0, q=0, k=0, w=0, q_pos0=0, kv_len=0), 64, 0, 0, 0, 0) == bd.IX_OK
+    assert status_of(bd.ix_score, args(T=0), 0, 0, 0) == bd.IX_OK
+    assert status_of(bd.ix_score, args(), 3, 3, 0) == bd.IX_OK
+    assert bd.ix_topk_workspace_bytes(args(B=0), 64) == 0
+    assert status_of(bd.sparse_attn_fwd, 0, 0, 0, 0, 0, 0, 5, 100, 16, 1, 128, 64, 0.1, 0, 0,
+                     0, 0) == bd.IX_OK
+
+
+def test_attention_validation_codes():
+    ok = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, kv_len=0, B=1, T=4, S_max=64, H_q=16, H_kv=1,
+              d=128, k=64, sm_scale=0.1, out=FAKE, lse=0, ws=0, ws_bytes=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return status_of(bd.sparse_attn_fwd, a["q"], a["kc"], a["vc"], a["idx"], a["kv_len"],
+                         a["B"], a["T"], a["S_max"], a["H_q"], a["H_kv"], a["d"], a["k"],
+                         a["sm_scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"])
+
+    assert call(d=96) == bd.IX_ERR_UNSUPPORTED
+    assert call(H_q=12, H_kv=5) == bd.IX_ERR_UNSUPPORTED
+    assert call(H_q=32, H_kv=1) == bd.IX_ERR_UNSUPPORTED
+    assert call(k=0) == bd.IX_ERR_UNSUPPORTED
+    assert call(T=-1) == bd.IX_ERR_INVALID
+    assert call(out=0) == bd.IX_ERR_INVALID
+    assert call(kc=FAKE + 2) == bd.IX_ERR_INVALID
+    assert call(sm_scale=float("nan")) == bd.IX_ERR_INVALID
+    # decode-sized batches split the selection and need a workspace
+    need = bd.sparse_attn_workspace_bytes(64, 1, 16, 1, 128, 2048)
+    assert need > 0
+    assert call(B=64, T=1, k=2048) == bd.IX_ERR_WORKSPACE
+    assert bd.sparse_attn_workspace_bytes(1, 4096, 16, 1, 128, 2048) == 0
+
+
+def test_indexshare_validation_codes():
+    a = args()
+    L = bd.load()
+    P = ctypes.POINTER(ctypes.c_void_p)
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    pa = ctypes.cast(arr, P)
+    need = bd.indexshare_workspace_bytes(a, 64, 16, 1, 128)
+    assert need >= bd.ix_topk_workspace_bytes(a, 64)
+    assert L.indexshare_group_fwd(ctypes.byref(a), 64, 0, pa, pa, pa, pa, None, 16, 1, 128,
+                                  ctypes.c_float(0.1), FAKE, FAKE, need, None) == bd.IX_ERR_INVALID
+    assert L.indexshare_group_fwd(ctypes.byref(a), 64, 4, None, pa, pa, pa, None, 16, 1, 128,
+                                  ctypes.c_float(0.1), FAKE, FAKE, need, None) == bd.IX_ERR_INVALID
+    assert L.indexshare_group_fwd(ctypes.byref(a), 64, 4, pa, pa, pa, pa, None, 16, 1, 128,
+                                  ctypes.c_float(0.1), FAKE, FAKE, need - 1, None) == bd.IX_ERR_WORKSPACE
+    assert L.indexshare_group_fwd(ctypes.byref(a), 64, 4, pa, pa, pa, pa, None, 16, 1, 96,
+                                  ctypes.c_float(0.1), FAKE, FAKE, need, None) == bd.IX_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_for_the_named_workloads():
+    from indexed_sparse_attention_ix_amd.workloads import WORKLOADS
+    for wl in WORKLOADS.values():
+        a = args(B=wl.B, T=wl.T, S_max=wl.S, H_I=wl.H_I, d_I=wl.d_I)
+        nb = bd.ix_topk_workspace_bytes(a, wl.k)
+        assert 0 < nb < 16 << 30   # fits comfortably in 288 GB of HBM
+        assert bd.indexshare_workspace_bytes(a, wl.k, wl.H_q, wl.H_kv, wl.d) >= nb

@@ -1,0 +1,147 @@
+"""GPU parity: indexer scores (ix_score) and the fused top-k (ix_topk) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from indexed_sparse_attention_ix_amd import binding as bd
+from indexed_sparse_attention_ix_amd import synth
+from indexed_sparse_attention_ix_amd.workloads import WORKLOADS, Workload
+from oracle import ix_oracle as O
+from parity_util import check_index_row, check_scores, say, to_host_indexer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _wl(**kw):
+    base = dict(name="case", B=1, T=64, S=64, pos0=0, H_I=64, d_I=128, k=64, H_q=16, H_kv=1,
+                d=128, layers=1, seed=11, qkv_std=1.0)
+    base.update(kw)
+    return Workload(**base)
+
+
+def _run_scores(wl, t_begin=0, t_end=None):
+    say(f"[ix_score] {wl.name} B={wl.B} T={wl.T} S={wl.S} H_I={wl.H_I} d_I={wl.d_I} seed={wl.seed}")
+    ind = synth.indexer_inputs(wl, device=DEV)
+    t_end = wl.T if t_end is None else t_end
+    sc = bd.score(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], t_begin, t_end)
+    torch.cuda.synchronize()
+    h = to_host_indexer(ind)
+    for b in range(wl.B):
+        ref = O.score_matrix(h["q_I"], h["k_I"], h["w"], h["q_pos0"], h["kv_len"], b,
+                             list(range(t_begin, t_end)), wl.S)
+        check_scores(sc[b].cpu().numpy(), ref)
+
+
+def test_score_tiny_all_rows():
+    _run_scores(WORKLOADS["tiny_prefill_1k"])
+
+
+def test_score_ragged_lengths_and_head_counts():
+    # kv_len below the query positions, a sequence whose queries outrun its cache,
+    # 12 heads (3 MFMA column blocks), ragged tails on every tile size
+    wl = _wl(B=2, T=77, S=300, pos0s=(100, 0), kv_lens=(250, 60), H_I=12, d_I=128, seed=12)
+    _run_scores(wl, 5, 70)
+    wl2 = _wl(B=1, T=45, S=133, pos0=88, H_I=8, d_I=64, seed=13)
+    _run_scores(wl2)
+
+
+def _run_topk(wl, check_sel=True):
+    say(f"[ix_topk] {wl.name} B={wl.B} T={wl.T} S={wl.S} H_I={wl.H_I} d_I={wl.d_I} k={wl.k} "
+        f"seed={wl.seed}")
+    ind = synth.indexer_inputs(wl, device=DEV)
+    idx, sel = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k,
+                       with_scores=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    sel = sel.cpu().numpy()
+    h = to_host_indexer(ind)
+    swaps = 0
+    for b in range(wl.B):
+        keys = O.decode_e4m3(h["k_I"][b])
+        for t in range(wl.T):
+            n = O.visible_count(h["q_pos0"][b], h["kv_len"][b], t)
+            sc = O.score_row(h["q_I"][b, t], keys[:n], h["w"][b, t], n)
+            swaps += check_index_row(idx[b, t], sc, wl.k, n, where=f"b={b} t={t}")
+            if check_sel:
+                m = min(wl.k, n)
+                g = sel[b, t, :m].astype(np.float64)
+                r = sc[idx[b, t, :m]]
+                assert np.all(np.abs(g - r) <= 1e-2 * np.abs(r) + 1e-6 * max(sc.max(), 1e-30))
+                assert np.all(np.isneginf(sel[b, t, m:]))
+    say(f"  swaps inside the tie band: {swaps}")
+    return idx
+
+
+def test_topk_tiny_all_rows():
+    _run_topk(WORKLOADS["tiny_prefill_1k"])
+
+
+def test_topk_buffer_compaction_ragged():
+    # visible prefixes far beyond the candidate capacity (several compactions per query),
+    # ragged kv_len, queries not a multiple of the wave's 4
+    wl = _wl(B=2, T=203, S=6000, pos0s=(5797, 2000), kv_lens=(6000, 4100), H_I=64, k=300,
+             seed=14, planted=8)
+    _run_topk(wl)
+
+
+def test_topk_key_splits_and_merge():
+    # one query per sequence: one query per wave, keys split over several waves, merged
+    wl = _wl(B=5, T=1, S=40000, pos0=39999, H_I=64, k=2048, seed=15, planted=32)
+    _run_topk(wl)
+    wl2 = _wl(B=3, T=2, S=20000, pos0=19998, H_I=16, d_I=64, k=100, seed=16)
+    _run_topk(wl2)
+
+
+def test_topk_k_at_least_visible_keeps_everything():
+    wl = _wl(B=1, T=40, S=50, pos0=10, H_I=4, d_I=64, k=64, seed=17)
+    idx = _run_topk(wl)
+    for t in range(wl.T):
+        n = min(10 + t + 1, 50)
+        assert idx[0, t, :n].tolist() == list(range(n))
+
+
+def _e4m3_code(v):
+    return int(np.nonzero(O.E4M3_TABLE == v)[0][0])
+
+
+def test_topk_known_top_set_with_zero_ties():
+    """Queries >= 0 and unplanted keys <= 0 give exact zero scores; planted keys have
+    closed-form distinct scores.  The kept set is known exactly (no tie band)."""
+    rng = np.random.default_rng(21)
+    B, T, S, H, d, k = 2, 8, 3000, 8, 128, 100
+    neg = [c for c in range(256) if O.E4M3_TABLE[c] <= 0 and not np.isnan(O.E4M3_TABLE[c])]
+    kc = rng.choice(neg, size=(B, S, d)).astype(np.uint8)
+    vals = [0.5 + 0.0625 * i for i in range(8)] + [1.0 + 0.125 * i for i in range(8)]
+    planted = {}
+    for b in range(B):
+        pos = sorted(rng.choice(np.arange(S), size=len(vals), replace=False).tolist())
+        v = list(vals)
+        rng.shuffle(v)
+        planted[b] = dict(zip(pos, v))
+        for s, x in planted[b].items():
+            kc[b, s, :] = _e4m3_code(x)
+    qc = np.full((B, T, H, d), _e4m3_code(0.25), dtype=np.uint8)
+    w = np.ones((B, T, H), dtype=np.float32)
+    pos0 = np.array([S - T, 1500], dtype=np.int32)
+    kvl = np.array([S, S], dtype=np.int32)
+    dev = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    say("[ix_topk] sign-partitioned planting")
+    idx = bd.topk(dev(qc), dev(kc), dev(w), dev(pos0), dev(kvl), k).cpu().numpy()
+    for b in range(B):
+        for t in range(T):
+            n = min(int(pos0[b]) + t + 1, S)
+            vis = {s: x for s, x in planted[b].items() if s < n}
+            order = sorted(vis, key=lambda s: -vis[s])[:k]
+            zeros = [s for s in range(n) if s not in vis][: k - len(order)]
+            assert idx[b, t].tolist() == sorted(order + zeros), f"b={b} t={t}"
+
+
+def test_topk_is_deterministic():
+    wl = _wl(B=1, T=64, S=9000, pos0=8936, k=512, seed=18)
+    ind = synth.indexer_inputs(wl, device=DEV)
+    say("[ix_topk] determinism")
+    a = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k)
+    b = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
