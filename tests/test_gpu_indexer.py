@@ -7,7 +7,8 @@ from indexed_sparse_attention_ix_amd import binding as bd
 from indexed_sparse_attention_ix_amd import synth
 from indexed_sparse_attention_ix_amd.workloads import WORKLOADS, Workload
 from oracle import ix_oracle as O
-from parity_util import check_index_row, check_scores, say, to_host_indexer
+from parity_util import (check_index_row, check_scores, say, score_magnitude, score_tolerance,
+                         to_host_indexer)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,9 +29,11 @@ def _run_scores(wl, t_begin=0, t_end=None):
     torch.cuda.synchronize()
     h = to_host_indexer(ind)
     for b in range(wl.B):
-        ref = O.score_matrix(h["q_I"], h["k_I"], h["w"], h["q_pos0"], h["kv_len"], b,
-                             list(range(t_begin, t_end)), wl.S)
-        check_scores(sc[b].cpu().numpy(), ref)
+        rows = list(range(t_begin, t_end))
+        ref = O.score_matrix(h["q_I"], h["k_I"], h["w"], h["q_pos0"], h["kv_len"], b, rows, wl.S)
+        kabs = np.abs(O.decode_e4m3(h["k_I"][b]))
+        mag = np.stack([score_magnitude(h["q_I"][b, t], kabs, h["w"][b, t]) for t in rows])
+        check_scores(sc[b].cpu().numpy(), ref, mag, wl.d_I, wl.H_I)
 
 
 def test_score_tiny_all_rows():
@@ -67,7 +70,8 @@ def _run_topk(wl, check_sel=True):
                 m = min(wl.k, n)
                 g = sel[b, t, :m].astype(np.float64)
                 r = sc[idx[b, t, :m]]
-                assert np.all(np.abs(g - r) <= 1e-2 * np.abs(r) + 1e-6 * max(sc.max(), 1e-30))
+                mag = score_magnitude(h["q_I"][b, t], np.abs(keys[idx[b, t, :m]]), h["w"][b, t])
+                assert np.all(np.abs(g - r) <= score_tolerance(r, mag, wl.d_I, wl.H_I))
                 assert np.all(np.isneginf(sel[b, t, m:]))
     say(f"  swaps inside the tie band: {swaps}")
     return idx

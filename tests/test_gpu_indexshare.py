@@ -17,7 +17,7 @@ DEV = "cuda"
 
 
 def _group_case(**kw):
-    base = dict(name="group", B=2, T=150, S=3000, pos0s=(2850, 1000), kv_lens=(3000, 2500),
+    base = dict(name="group", B=2, T=150, S=3000, pos0=0, pos0s=(2850, 1000), kv_lens=(3000, 2500),
                 H_I=64, d_I=128, k=256, H_q=16, H_kv=1, d=128, layers=4, seed=41,
                 qkv_std=1.0 / math.sqrt(128), planted=8)
     base.update(kw)
