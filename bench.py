@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 indexer -> top-k -> sparse-attention path on one MI355X.
+
+A step is one IndexShare group pass over one batch of synthetic input: the selection
+(FP8 MFMA indexer fused with the streaming top-k) computed once, then sparse attention
+for each layer of the group over that selection (indexshare_group_fwd).  Default
+workload: 128K causal prefill, batch 1, 64 indexer heads of width 128, top-2048,
+16-query-head MQA of width 128, a group of 4 layers.
+
+Prints one JSON line: query tokens/s through the whole step, the roofline of the
+dominant kernel (per-kernel times measured with events on the launch stream), the
+per-layer-indexing comparison (IndexShare speedup) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["indexed_sparse_attention_ix_amd/csrc/indexer.hip",
+                  "indexed_sparse_attention_ix_amd/csrc/sparse_attn.hip",
+                  "indexed_sparse_attention_ix_amd/csrc/ix_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-layer", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="query rows in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (reference kernel for HBM counters)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(wl):
+    """Indexer flops (2*H_I*d_I per visible pair) and attention bytes per layer
+    (gathered K and V rows, plus q, out and the index rows)."""
+    pairs = 0
+    sel = 0
+    for b in range(wl.B):
+        for_t = [wl.visible(b, t) for t in range(wl.T)] if wl.T <= 8192 else None
+        if for_t is None:
+            # closed form for pos0 + t + 1 clipped at kv_len
+            import numpy as np
+            n = np.minimum(np.arange(wl.T, dtype=np.int64) + wl.pos0_list()[b] + 1,
+                           wl.kv_len_list()[b]).clip(min=0)
+            pairs += int(n.sum())
+            sel += int(np.minimum(n, wl.k).sum())
+        else:
+            pairs += sum(for_t)
+            sel += sum(min(wl.k, n) for n in for_t)
+    flops = 2.0 * wl.H_I * wl.d_I * pairs
+    gathered = sel * 2.0 * wl.d * 2 * wl.H_kv
+    other = wl.B * wl.T * (2.0 * wl.H_q * wl.d * 2 + wl.k * 4)
+    return flops, gathered + other, pairs, sel
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU: the path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from indexed_sparse_attention_ix_amd import binding as bd
+    from indexed_sparse_attention_ix_amd import synth
+    from indexed_sparse_attention_ix_amd.workloads import BENCH_WORKLOAD, WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.load()  # fails loudly if libix.so is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    name = args.workload or BENCH_WORKLOAD
+    wl = WORKLOADS[name]
+    L = wl.layers
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    # ---------------------------------------------------------------- inputs in HBM
+    ind = synth.indexer_inputs(wl, device=dev)
+    layers = [synth.attention_inputs(wl, layer=l, device=dev) for l in range(L)]
+    a = bd.indexer_args(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"])
+    idx = torch.empty((wl.B, wl.T, wl.k), dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(Lr["q"]) for Lr in layers]
+    ws_bytes = bd.indexshare_workspace_bytes(a, wl.k, wl.H_q, wl.H_kv, wl.d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    qp = [Lr["q"].data_ptr() for Lr in layers]
+    kp = [Lr["K"].data_ptr() for Lr in layers]
+    vp = [Lr["V"].data_ptr() for Lr in layers]
+    op = [o.data_ptr() for o in outs]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def group_step():
+        bd.indexshare_group_fwd(a, wl.k, L, qp, kp, vp, op, None, wl.H_q, wl.H_kv, wl.d,
+                                wl.sm_scale, idx.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+
+    # ---------------------------------------------------------------- timed region
+    for _ in range(args.warmup):
+        group_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        group_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = wl.B * wl.T
+    value = tokens / (ms / 1e3)
+
+    # ---------------------------------------------------------------- per-kernel times
+    # the same launches as the group entry point, bracketed by events on its stream
+    topk_ws = bd.ix_topk_workspace_bytes(a, wl.k)
+    attn_ws = bd.sparse_attn_workspace_bytes(wl.B, wl.T, wl.H_q, wl.H_kv, wl.d, wl.k)
+    reps = max(2, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 2)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        bd.ix_topk(a, wl.k, idx.data_ptr(), 0, ws.data_ptr(), topk_ws, sh)
+        ev[r][1].record(stream)
+        for l in range(L):
+            bd.sparse_attn_fwd(qp[l], kp[l], vp[l], idx.data_ptr(), ind["kv_len"].data_ptr(),
+                               wl.B, wl.T, wl.S, wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale,
+                               op[l], 0, ws.data_ptr() if attn_ws else 0, attn_ws, sh)
+            ev[r][2 + l].record(stream)
+    torch.cuda.synchronize()
+    t_topk = sum(ev[r][0].elapsed_time(ev[r][1]) for r in range(reps)) / reps
+    t_attn = sum(ev[r][1 + l].elapsed_time(ev[r][2 + l]) for r in range(reps)
+                 for l in range(L)) / (reps * L)
+
+    flops, attn_bytes, pairs, sel = algorithmic_work(wl)
+    idx_tflops = flops / (t_topk / 1e3) / 1e12
+    attn_gbs = attn_bytes / (t_attn / 1e3) / 1e9
+    idx_roof = {"bound": "mfma", "achieved": round(idx_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(idx_tflops / PEAK_FP8_TFLOPS, 4)}
+    attn_roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4)}
+    traffic = {"indexer": None, "attention": None}
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == name:
+                traffic = {"indexer": tr.get("indexer_bytes"), "attention": tr.get("attention_bytes")}
+        except (OSError, ValueError):
+            pass
+    idx_roof["traffic"] = traffic["indexer"]
+    attn_roof["traffic"] = traffic["attention"]
+    dominant_is_indexer = t_topk >= t_attn * L
+    roofline = idx_roof if dominant_is_indexer else attn_roof
+    roofline = dict(roofline, kernel="ix_topk (indexer + selection)" if dominant_is_indexer
+                    else "sparse_attn_fwd")
+
+    # ---------------------------------------------------------------- per-layer indexing
+    indexshare = None
+    if not args.no_per_layer and L > 1:
+        inds = [ind] + [synth.indexer_inputs(wl, layer=l, device=dev) for l in range(1, L)]
+        aa = [bd.indexer_args(x["q_I"], x["k_I"], x["w"], x["q_pos0"], x["kv_len"]) for x in inds]
+
+        def per_layer_step():
+            for l in range(L):
+                bd.ix_topk(aa[l], wl.k, idx.data_ptr(), 0, ws.data_ptr(), topk_ws, sh)
+                bd.sparse_attn_fwd(qp[l], kp[l], vp[l], idx.data_ptr(),
+                                   inds[l]["kv_len"].data_ptr(), wl.B, wl.T, wl.S, wl.H_q,
+                                   wl.H_kv, wl.d, wl.k, wl.sm_scale, op[l], 0,
+                                   ws.data_ptr() if attn_ws else 0, attn_ws, sh)
+        per_layer_step()
+        torch.cuda.synchronize()
+        n_pl = max(2, args.steps // 2)
+        e0.record(stream)
+        for _ in range(n_pl):
+            per_layer_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_pl = e0.elapsed_time(e1) / n_pl
+        indexshare = {"group_ms": round(ms, 3), "per_layer_ms": round(ms_pl, 3),
+                      "speedup": round(ms_pl / ms, 3), "layers": L}
+        del inds, aa
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import ix_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        except Exception:  # noqa: BLE001
+            threads = os.cpu_count() or 1
+        rng = np.random.default_rng(1234)
+        b = 0
+        rows = sorted(rng.choice(wl.T, size=min(args.cpu_rows, wl.T), replace=False).tolist())
+        ri = torch.tensor(rows, device=dev)
+        qI_h = np.zeros((wl.B, wl.T, wl.H_I, wl.d_I), dtype=np.uint8)
+        w_h = np.zeros((wl.B, wl.T, wl.H_I), dtype=np.float32)
+        qI_h[b, rows] = ind["q_I"][b, ri].cpu().numpy()
+        w_h[b, rows] = ind["w"][b, ri].cpu().numpy()
+        indexer_np = {"q_I": qI_h, "k_I": ind["k_I"].cpu().numpy(), "w": w_h,
+                      "q_pos0": ind["q_pos0"].cpu().numpy(), "kv_len": ind["kv_len"].cpu().numpy()}
+        layers_np = []
+        for Lr in layers:
+            qb = np.zeros((wl.B, wl.T, wl.H_q, wl.d), dtype=np.uint16)
+            qb[b, rows] = synth.bf16_bits(Lr["q"][b, ri])
+            layers_np.append({"q": qb, "K": synth.bf16_bits(Lr["K"][b:b + 1]),
+                              "V": synth.bf16_bits(Lr["V"][b:b + 1])})
+        t0 = time.perf_counter()
+        O.indexshare_group(indexer_np, layers_np, wl.k, b, rows, wl.sm_scale)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(len(rows) / t_cpu, 3), "unit": "query tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{len(rows)} query rows drawn uniformly from {name} (seed 1234): "
+                         f"fp64 scores, selection and {L}-layer attention per row, "
+                         f"{t_cpu:.1f} s"}
+
+    line = {
+        "metric": "query tokens/s (indexer+topk+sparse attn) at 128K",
+        "value": round(value, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": name, "B": wl.B, "T": wl.T, "S": wl.S, "H_I": wl.H_I,
+                   "d_I": wl.d_I, "k": wl.k, "H_q": wl.H_q, "H_kv": wl.H_kv, "d": wl.d,
+                   "layers": L, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {
+            "ix_topk_ms": round(t_topk, 3),
+            "sparse_attn_ms_per_layer": round(t_attn, 3),
+            "indexer_roofline": idx_roof,
+            "attention_roofline": attn_roof,
+            "indexer_tflop": round(flops / 1e12, 3),
+            "attention_gb_per_layer": round(attn_bytes / 1e9, 3),
+            "visible_pairs": pairs,
+            "selected_pairs": sel,
+            "indexshare": indexshare,
+            "wall_s_timed_region": round(t_wall, 3),
+            "kernel_source_hash": kernel_source_hash(),
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
