@@ -29,7 +29,6 @@ namespace {
 
 constexpr int kBlockWaves = 4;
 constexpr int kBlock = kBlockWaves * kWave;
-constexpr int kPrefetch = 4;       // key tiles in flight per wave
 constexpr int kHistBins = 256;
 
 struct IxArgs {
@@ -92,20 +91,47 @@ struct QueryOperands {
     }
   }
 
+  // ReLU on the float bits: a signed-integer max with 0 maps every negative float
+  // (sign bit set) and -0 to +0 and leaves non-negative floats unchanged; one VALU op.
+  static __device__ __forceinline__ float relu(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+  }
+  static __device__ __forceinline__ void accumulate(f32x4& acc, const f32x4& x, float w) {
+    acc[0] = fmaf(w, relu(x[0]), acc[0]);
+    acc[1] = fmaf(w, relu(x[1]), acc[1]);
+    acc[2] = fmaf(w, relu(x[2]), acc[2]);
+    acc[3] = fmaf(w, relu(x[3]), acc[3]);
+  }
+
   // Score of one (query, key) pair per lane for the 16-key tile held in `a`.
   // Lane l ends up with key 4*(l>>4) + (j & 3) and query (l & 15) / HC, where
   // j = (l & 15) % HC; for HC = 16 only lanes with j < 4 carry a distinct pair.
+  // EXACT: all GMAX head blocks are used; the MFMA of block g+1 is issued before the
+  // epilogue of block g so that the matrix core and the VALU overlap.
+  template <bool EXACT>
   __device__ __forceinline__ float tile_score(const i32x8& a, int g_rt, int jsel) const {
     constexpr int HC = 16 / QC;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EXACT) {
+      f32x4 x = mfma_e4m3_16x16x128(a, bq[0]);
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g < g_rt) {
-        const f32x4 x = mfma_e4m3_16x16x128(a, bq[g]);
-        acc[0] = fmaf(wv[g], fmaxf(x[0], 0.f), acc[0]);
-        acc[1] = fmaf(wv[g], fmaxf(x[1], 0.f), acc[1]);
-        acc[2] = fmaf(wv[g], fmaxf(x[2], 0.f), acc[2]);
-        acc[3] = fmaf(wv[g], fmaxf(x[3], 0.f), acc[3]);
+      for (int g = 1; g < GMAX; ++g) {
+        const f32x4 y = mfma_e4m3_16x16x128(a, bq[g]);
+        accumulate(acc, x, wv[g - 1]);
+        x = y;
+      }
+      accumulate(acc, x, wv[GMAX - 1]);
+      // keep the interleave: MFMA(g) issued, then the 8 VALU ops of block g-1
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int g = 1; g < GMAX; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (g < g_rt) accumulate(acc, mfma_e4m3_16x16x128(a, bq[g]), wv[g]);
       }
     }
     // sum over the HC heads of a column block (adjacent lanes)
@@ -260,9 +286,11 @@ __device__ __forceinline__ void mem_fence_wave() {
 
 // ------------------------------------------------------------------ fused indexer + top-k
 
-template <int QC, int GMAX, int DI>
+template <int QC, int GMAX, int DI, bool EXACT>
 __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   constexpr int HC = 16 / QC;
+  // key tiles in flight per wave (the 16-block case keeps 128 VGPRs of query operands)
+  constexpr int kPrefetch = GMAX >= 16 ? 2 : 4;
   __shared__ uint32_t hist_all[kBlockWaves][kHistBins];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -326,7 +354,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
           const int srow = min(st + 16 * kPrefetch + r16, last_row);
           ring[ui] = load_row_slice<DI>(kbase + (size_t)srow * DI, lg);
         }
-        const float sc = qo.tile_score(a, p.g, jsel);
+        const float sc = qo.template tile_score<EXACT>(a, p.g, jsel);
         const int s = st + 4 * lg + jsel;
         const bool vis = act && s < n_q && s < ke;
         const uint32_t hi = f32_to_ordered(sc);
@@ -380,16 +408,13 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     uint64_t* buf = p.cand + ((row_base + ti) * p.n_splits + split) * (size_t)p.cap;
     const int n = cnt[i];
     uint64_t theta = 0ull;
-    int kept = n;
     if (n > p.ksel) {
       const uint32_t lo_r = wave_min_u32(qi == i ? mn_hi : 0xFFFFFFFFu);
       const uint32_t hi_r = wave_max_u32(qi == i ? mx_hi : 0u);
       uint64_t prefix;
       int rem;
       select_start(lo_r, hi_r, prefix, rem);
-      const SelectResult sr = wave_radix_select(buf, n, p.ksel, 0, prefix, rem, hist);
-      theta = sr.theta;
-      kept = sr.kept;
+      theta = wave_radix_select(buf, n, p.ksel, 0, prefix, rem, hist).theta;
     }
     if (p.n_splits == 1) {
       // stream the kept entries (ascending index) into the output row, then pad
@@ -542,7 +567,7 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
 
 // ------------------------------------------------------------------ score rows (Stage 1 only)
 
-template <int GMAX, int DI>
+template <int GMAX, int DI, bool EXACT>
 __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
   constexpr int QC = 4, HC = 4;
   const int lane = threadIdx.x & 63;
@@ -572,7 +597,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
   for (int s0 = 0; s0 < p.S_max; s0 += 16) {
     const int srow = min(s0 + r16, p.S_max - 1);
     const i32x8 a = load_row_slice<DI>(kbase + (size_t)srow * DI, lg);
-    const float sc = qo.tile_score(a, p.g, jsel);
+    const float sc = qo.template tile_score<EXACT>(a, p.g, jsel);
     const int s = s0 + 4 * lg + jsel;
     if (qvalid && s < p.S_max) orow[s] = s < n_q ? sc + 0.0f : -__builtin_inff();
   }
@@ -651,19 +676,21 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
   x.idx = idx;
   x.sel = sel_scores;
   const dim3 grid((unsigned)((pl.units + kBlockWaves - 1) / kBlockWaves));
+  const bool exact = pl.g == pl.gmax;
   hipError_t err = dispatch_g(pl.gmax, [&](auto GM) -> hipError_t {
     constexpr int G = decltype(GM)::value;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, stream, x); };
     if (pl.qc == 4) {
       if (a.d_I == 128)
-        hipLaunchKernelGGL((ix_topk_partial_kernel<4, G, 128>), grid, dim3(kBlock), 0, stream, x);
+        exact ? go(ix_topk_partial_kernel<4, G, 128, true>) : go(ix_topk_partial_kernel<4, G, 128, false>);
       else
-        hipLaunchKernelGGL((ix_topk_partial_kernel<4, G, 64>), grid, dim3(kBlock), 0, stream, x);
+        exact ? go(ix_topk_partial_kernel<4, G, 64, true>) : go(ix_topk_partial_kernel<4, G, 64, false>);
     } else {
       if constexpr (G <= 4) {
         if (a.d_I == 128)
-          hipLaunchKernelGGL((ix_topk_partial_kernel<1, G, 128>), grid, dim3(kBlock), 0, stream, x);
+          exact ? go(ix_topk_partial_kernel<1, G, 128, true>) : go(ix_topk_partial_kernel<1, G, 128, false>);
         else
-          hipLaunchKernelGGL((ix_topk_partial_kernel<1, G, 64>), grid, dim3(kBlock), 0, stream, x);
+          exact ? go(ix_topk_partial_kernel<1, G, 64, true>) : go(ix_topk_partial_kernel<1, G, 64, false>);
       } else {
         return hipErrorInvalidValue;
       }
@@ -691,12 +718,14 @@ hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, flo
   x.scores = scores;
   const int gmax = x.g <= 1 ? 1 : x.g <= 2 ? 2 : x.g <= 4 ? 4 : x.g <= 8 ? 8 : 16;
   const dim3 grid((unsigned)((x.units + kBlockWaves - 1) / kBlockWaves));
+  const bool exact = x.g == gmax;
   return dispatch_g(gmax, [&](auto GM) -> hipError_t {
     constexpr int G = decltype(GM)::value;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, stream, x); };
     if (a.d_I == 128)
-      hipLaunchKernelGGL((ix_score_kernel<G, 128>), grid, dim3(kBlock), 0, stream, x);
+      exact ? go(ix_score_kernel<G, 128, true>) : go(ix_score_kernel<G, 128, false>);
     else
-      hipLaunchKernelGGL((ix_score_kernel<G, 64>), grid, dim3(kBlock), 0, stream, x);
+      exact ? go(ix_score_kernel<G, 64, true>) : go(ix_score_kernel<G, 64, false>);
     return hipGetLastError();
   });
 }
