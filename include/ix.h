@@ -7,9 +7,9 @@
  *   Stage 1 (coarse scoring) and Stage 2 (fine selection, k = 2048 at 1M context):
  *     "GLM 5.2: How Four Co-Designed Mechanisms Beat Raw Scale", Part II,
  *     section "DeepSeek Sparse Attention".
- *   FP8 indexer, ReLU-free statement of "score the keys, keep the top-k", one
- *   indexer shared across a group of 4 layers: the twiscan post on GLM-5.2's
- *   IndexShare.
+ *   The indexer runs in FP8, scores the keys and keeps the top-k, and one
+ *   indexer's selection is shared across a group of 4 layers: the twiscan post on
+ *   GLM-5.2's IndexShare.
  *   Selection computed once per block of 4 layers and shared across the block:
  *     same irys.ai page, section "IndexShare: Amortizing the Indexer".
  * Concrete indexer form implemented here: for query token t and key token s,
