@@ -30,6 +30,7 @@ namespace {
 constexpr int kBlockWaves = 4;
 constexpr int kBlock = kBlockWaves * kWave;
 constexpr int kHistBins = 256;
+constexpr int kHistBatch = 4;  // 16-byte loads in flight per lane in a histogram pass
 
 struct IxArgs {
   const uint8_t* q;
@@ -196,6 +197,42 @@ __device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, int nbins,
   count = __shfl(fh, src);
 }
 
+// 16-byte view of entries (e, e+1) of a candidate buffer.  Buffers start 16-byte aligned
+// and have an even capacity, so for even e < n <= capacity the pair stays inside.
+__device__ __forceinline__ void load_pair(const uint64_t* buf, int e, int n, uint64_t& x0,
+                                          uint64_t& x1) {
+  if (e < n) {
+    const i32x4 v = ld_global_16(buf + e);
+    x0 = ((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0];
+    x1 = ((uint64_t)(uint32_t)v[3] << 32) | (uint32_t)v[2];
+  } else {
+    x0 = x1 = 0ull;
+  }
+}
+
+// Histogram of the digit (v >> shift) & dmask over the entries of buf[0, n) whose bits
+// at and above hs equal prefix.  Lane l reads entries 2l, 2l+1 of each 128-entry chunk;
+// kHistBatch chunks are loaded before any is counted, so the L2 latency is paid once per
+// 128 * kHistBatch entries.
+__device__ void wave_hist(const uint64_t* buf, int n, uint64_t prefix, int hs, int shift,
+                          uint32_t dmask, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  for (int e0 = 0; e0 < n; e0 += 128 * kHistBatch) {
+    uint64_t x[kHistBatch][2];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = e0 + 128 * u + 2 * lane + j;
+        const bool in = e < n && (hs >= 64 || (x[u][j] >> hs) == prefix);
+        if (in) atomicAdd(&hist[(uint32_t)(x[u][j] >> shift) & dmask], 1u);
+      }
+    }
+  }
+}
+
 // Radix select over buf[0, n) (distinct keys, all sharing their bits above `rem`
 // equal to `prefix`).  Keeps the k largest: returns theta with #(v >= theta) = kept,
 // where kept == k when exact, else the first kept <= limit reached while refining.
@@ -209,21 +246,7 @@ __device__ SelectResult wave_radix_select(const uint64_t* buf, int n, int k, int
     const int nbins = 1 << dbits;
     for (int i = lane; i < kHistBins; i += 64) hist[i] = 0u;
     lds_wait();
-    const int hs = shift + dbits;  // bits at and above hs must equal prefix
-    for (int e0 = 0; e0 < n; e0 += 64 * 4) {
-      uint64_t v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * 64 + lane;
-        v[u] = e < n ? buf[e] : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * 64 + lane;
-        const bool in = e < n && (hs >= 64 || (v[u] >> hs) == prefix);
-        if (in) atomicAdd(&hist[(uint32_t)(v[u] >> shift) & (uint32_t)(nbins - 1)], 1u);
-      }
-    }
+    wave_hist(buf, n, prefix, rem, shift, (uint32_t)(nbins - 1), hist);
     lds_wait();
     int d;
     uint32_t above, cnt;
@@ -253,20 +276,32 @@ __device__ __forceinline__ void select_start(uint32_t mn_hi, uint32_t mx_hi, uin
   }
 }
 
-// Order-preserving in-place filter of buf[0, n) to the entries >= theta.
-__device__ int wave_compact(uint64_t* buf, int n, uint64_t theta) {
+// Walks buf[0, n) in order and calls out(pos, v) for each entry >= theta, pos being its
+// rank among the kept entries; returns how many were kept.  Lane l handles entries
+// 2l, 2l+1 of each 128-entry chunk; four chunks are loaded before any is written, and
+// a write never lands past the entry it came from, so in-place use is safe.
+template <typename Out>
+__device__ int wave_filter(const uint64_t* buf, int n, uint64_t theta, Out&& out) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = lanemask_lt();
-  int out = 0;
-  for (int e0 = 0; e0 < n; e0 += 64) {
-    const int e = e0 + lane;
-    const uint64_t v = e < n ? buf[e] : 0ull;
-    const bool keep = e < n && v >= theta;
-    const uint64_t bal = ballot64(keep);
-    if (keep) buf[out + popc64(bal & lt)] = v;
-    out += popc64(bal);
+  int total = 0;
+  for (int e0 = 0; e0 < n; e0 += 128 * 4) {
+    uint64_t x[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + 128 * u + 2 * lane;
+      const bool k0 = e < n && x[u][0] >= theta;
+      const bool k1 = e + 1 < n && x[u][1] >= theta;
+      const uint64_t b0 = ballot64(k0), b1 = ballot64(k1);
+      const int pos = total + popc64(b0 & lt) + popc64(b1 & lt);
+      if (k0) out(pos, x[u][0]);
+      if (k1) out(pos + (k0 ? 1 : 0), x[u][1]);
+      total += popc64(b0) + popc64(b1);
+    }
   }
-  return out;
+  return total;
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -284,17 +319,36 @@ __device__ __forceinline__ void mem_fence_wave() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One 16-row key tile as the A operand: lane (row r, group g) gets bytes [32g, 32g+32) of
+// its row (rows of width 64 repeat bytes [32(g&1), ...) in groups 2, 3; the query
+// operand is zero there, so they add nothing).
+__device__ __forceinline__ i32x8 load_key_tile(__amdgpu_buffer_rsrc_t rs, int off) {
+  const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  const i32x4 hi =
+      __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+  return (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // ------------------------------------------------------------------ fused indexer + top-k
 
 template <int QC, int GMAX, int DI, bool EXACT>
 __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   constexpr int HC = 16 / QC;
   // key tiles in flight per wave (the 16-block case keeps 128 VGPRs of query operands)
-  constexpr int kPrefetch = GMAX >= 16 ? 2 : 4;
+  constexpr int PF = GMAX >= 16 ? 2 : 4;
+  constexpr int STG = 2 * 16 * PF;  // per-query LDS staging of appended keys (two blocks' worth)
   __shared__ uint32_t hist_all[kBlockWaves][kHistBins];
+  __shared__ uint64_t stage_all[kBlockWaves][QC * STG];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   uint32_t* hist = hist_all[wid];
+  uint64_t* stage = stage_all[wid];
   const int64_t u = (int64_t)blockIdx.x * kBlockWaves + wid;
   if (u >= p.units) return;
   const int split = (int)(u % p.n_splits);
@@ -320,126 +374,131 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   QueryOperands<QC, GMAX, DI> qo;
   qo.load(p, b, t, qvalid, t0, j, lg);
 
-  const bool act = (QC == 4) || (j < 4);  // lane carries a distinct (query, key) pair
+  // lane constants: the key offset of this lane's pair within a tile, and the bound on
+  // key positions that are candidates for it (0 for lanes without a pair)
+  const bool act = (QC == 4) || (j < 4);
+  const int koff = 4 * lg + jsel;
+  const int lim = (act && qvalid) ? min(n_q, ke) : 0;
   const uint64_t qmask_base = 0x000F000F000F000Full;
   const uint64_t my_qmask = (QC == 4) ? (qmask_base << (4 * qi)) : qmask_base;
   const uint64_t lt = lanemask_lt();
-
-  // buffers of the wave's queries (query rows past T map to a dummy row that is never used)
   const size_t row_base = (size_t)b * p.T;
-  uint64_t* my_buf = p.cand + ((row_base + (qvalid ? t : t0)) * p.n_splits + split) * (size_t)p.cap;
+  auto qbuf = [&](int i) -> uint64_t* {
+    return p.cand + ((row_base + t0 + i) * p.n_splits + split) * (size_t)p.cap;
+  };
 
-  int cnt[QC];
+  int gcnt[QC], scnt[QC];  // entries in the global buffer / in the LDS stage, per query
 #pragma unroll
-  for (int i = 0; i < QC; ++i) cnt[i] = 0;
-  uint64_t th_lane = 0ull;
-  uint32_t mn_hi = 0xFFFFFFFFu, mx_hi = 0u;  // range of appended high words (own query)
+  for (int i = 0; i < QC; ++i) gcnt[i] = scnt[i] = 0;
+  uint64_t th_lane = 0ull;                    // own query's threshold: keep keys >= it
+  uint32_t mn_hi = 0xFFFFFFFFu, mx_hi = 0u;   // range of appended high words (own query)
+  const int limit = p.ksel + (p.cap - 2 * STG - p.ksel) / 2;
 
-  const uint8_t* kbase = p.k + (size_t)b * p.S_max * DI;
-  const int last_row = p.S_max - 1;
-  i32x8 ring[kPrefetch];
-#pragma unroll
-  for (int i = 0; i < kPrefetch; ++i) {
-    const int srow = min(ks + 16 * i + r16, last_row);
-    ring[i] = load_row_slice<DI>(kbase + (size_t)srow * DI, lg);
-  }
+  auto flush = [&](int i) {
+    for (int l = lane; l < scnt[i]; l += 64) qbuf(i)[gcnt[i] + l] = stage[i * STG + l];
+    gcnt[i] += scnt[i];
+    scnt[i] = 0;
+  };
+  auto range_of = [&](int i, uint64_t& prefix, int& rem) {
+    const uint32_t lo_r = wave_min_u32(qi == i ? mn_hi : 0xFFFFFFFFu);
+    const uint32_t hi_r = wave_max_u32(qi == i ? mx_hi : 0u);
+    select_start(lo_r, hi_r, prefix, rem);
+  };
 
-  for (int s0 = ks; s0 < ke; s0 += 16 * kPrefetch) {
+  // key rows of this sequence behind a bounds-checked buffer: rows >= kv_len read as 0
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(p.k + (size_t)b * p.S_max * DI, (uint32_t)kvl * DI);
+  const int voff = r16 * DI + 32 * (DI == 128 ? lg : (lg & 1));
+
+  i32x8 ring[PF];
 #pragma unroll
-    for (int ui = 0; ui < kPrefetch; ++ui) {
-      const int st = s0 + 16 * ui;
-      if (st < ke) {
-        const i32x8 a = ring[ui];
-        {
-          const int srow = min(st + 16 * kPrefetch + r16, last_row);
-          ring[ui] = load_row_slice<DI>(kbase + (size_t)srow * DI, lg);
+  for (int i = 0; i < PF; ++i) ring[i] = load_key_tile(krs, voff + (ks + 16 * i) * DI);
+
+  for (int s0 = ks; s0 < ke; s0 += 16 * PF) {
+    float sc[PF];
+#pragma unroll
+    for (int ui = 0; ui < PF; ++ui) {
+      sc[ui] = qo.template tile_score<EXACT>(ring[ui], p.g, jsel);
+      ring[ui] = load_key_tile(krs, voff + (s0 + 16 * (ui + PF)) * DI);
+    }
+#pragma unroll
+    for (int ui = 0; ui < PF; ++ui) {
+      const int s = s0 + 16 * ui + koff;
+      const uint32_t hi = f32_to_ordered(sc[ui]);
+      const uint64_t key = ((uint64_t)hi << 32) | (uint64_t)(~(uint32_t)s);
+      const bool pass = s < lim && key >= th_lane;
+      const uint64_t bal = ballot64(pass);
+      if (bal) {
+        int sb = scnt[0];
+#pragma unroll
+        for (int i = 1; i < QC; ++i) sb = (qi == i) ? scnt[i] : sb;
+        if (pass) {
+          stage[qi * STG + sb + popc64(bal & my_qmask & lt)] = key;
+          mn_hi = min(mn_hi, hi);
+          mx_hi = max(mx_hi, hi);
         }
-        const float sc = qo.template tile_score<EXACT>(a, p.g, jsel);
-        const int s = st + 4 * lg + jsel;
-        const bool vis = act && s < n_q && s < ke;
-        const uint32_t hi = f32_to_ordered(sc);
-        const uint64_t key = ((uint64_t)hi << 32) | (uint64_t)(~(uint32_t)s);
-        const bool pass = vis && key >= th_lane;
-        const uint64_t bal = ballot64(pass);
-        if (bal) {
-          int cl = cnt[0];
 #pragma unroll
-          for (int i = 1; i < QC; ++i) cl = (qi == i) ? cnt[i] : cl;
-          if (pass) {
-            my_buf[cl + popc64(bal & my_qmask & lt)] = key;
-            mn_hi = min(mn_hi, hi);
-            mx_hi = max(mx_hi, hi);
-          }
-#pragma unroll
-          for (int i = 0; i < QC; ++i) cnt[i] += popc64(bal & (QC == 4 ? (qmask_base << (4 * i)) : qmask_base));
-        }
+        for (int i = 0; i < QC; ++i)
+          scnt[i] += popc64(bal & (QC == 4 ? (qmask_base << (4 * i)) : qmask_base));
       }
     }
-    // make room: every buffer must take another kPrefetch tiles (16 entries each)
+    // a stage that cannot take two more blocks is flushed; a buffer that cannot take
+    // another flush is compacted
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
-      if (cnt[i] > p.cap - 16 * kPrefetch) {
-        mem_fence_wave();
-        const uint32_t lo_r = wave_min_u32(qi == i ? mn_hi : 0xFFFFFFFFu);
-        const uint32_t hi_r = wave_max_u32(qi == i ? mx_hi : 0u);
-        uint64_t* buf = p.cand + ((row_base + t0 + i) * p.n_splits + split) * (size_t)p.cap;
-        uint64_t prefix;
-        int rem;
-        select_start(lo_r, hi_r, prefix, rem);
-        const int limit = p.ksel + (p.cap - 16 * kPrefetch - p.ksel) / 2;
-        const SelectResult sr = wave_radix_select(buf, cnt[i], p.ksel, limit, prefix, rem, hist);
-        const int kept = wave_compact(buf, cnt[i], sr.theta);
-        mem_fence_wave();
-        cnt[i] = kept;
-        if (qi == i) {
-          th_lane = sr.theta;
-          mn_hi = max(mn_hi, (uint32_t)(sr.theta >> 32));
+      if (scnt[i] > STG - 16 * PF) {
+        flush(i);
+        if (gcnt[i] > p.cap - STG) {
+          mem_fence_wave();
+          uint64_t* buf = qbuf(i);
+          uint64_t prefix;
+          int rem;
+          range_of(i, prefix, rem);
+          const SelectResult sr = wave_radix_select(buf, gcnt[i], p.ksel, limit, prefix, rem, hist);
+          gcnt[i] = wave_filter(buf, gcnt[i], sr.theta, [&](int pos, uint64_t v) { buf[pos] = v; });
+          mem_fence_wave();
+          if (qi == i) {
+            th_lane = sr.theta;
+            mn_hi = max(mn_hi, (uint32_t)(sr.theta >> 32));
+          }
         }
       }
     }
   }
 
   // final exact selection for each query of the wave
+#pragma unroll
+  for (int i = 0; i < QC; ++i) flush(i);
   mem_fence_wave();
 #pragma unroll
   for (int i = 0; i < QC; ++i) {
     const int ti = t0 + i;
     if (ti >= p.T) break;
-    uint64_t* buf = p.cand + ((row_base + ti) * p.n_splits + split) * (size_t)p.cap;
-    const int n = cnt[i];
+    uint64_t* buf = qbuf(i);
+    const int n = gcnt[i];
     uint64_t theta = 0ull;
     if (n > p.ksel) {
-      const uint32_t lo_r = wave_min_u32(qi == i ? mn_hi : 0xFFFFFFFFu);
-      const uint32_t hi_r = wave_max_u32(qi == i ? mx_hi : 0u);
       uint64_t prefix;
       int rem;
-      select_start(lo_r, hi_r, prefix, rem);
+      range_of(i, prefix, rem);
       theta = wave_radix_select(buf, n, p.ksel, 0, prefix, rem, hist).theta;
     }
     if (p.n_splits == 1) {
-      // stream the kept entries (ascending index) into the output row, then pad
+      // kept entries (ascending index) straight into the output row, then padding
       int32_t* orow = p.idx + (row_base + ti) * (size_t)p.ksel;
       float* srow = p.sel ? p.sel + (row_base + ti) * (size_t)p.ksel : nullptr;
-      int out = 0;
-      for (int e0 = 0; e0 < n; e0 += 64) {
-        const int e = e0 + lane;
-        const uint64_t v = e < n ? buf[e] : 0ull;
-        const bool keep = e < n && v >= theta;
-        const uint64_t bal = ballot64(keep);
-        if (keep) {
-          const int pos = out + popc64(bal & lt);
-          orow[pos] = (int32_t)(~(uint32_t)v);
-          if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
-        }
-        out += popc64(bal);
-      }
+      const int out = wave_filter(buf, n, theta, [&](int pos, uint64_t v) {
+        orow[pos] = (int32_t)(~(uint32_t)v);
+        if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
+      });
       for (int pos = out + lane; pos < p.ksel; pos += 64) {
         orow[pos] = -1;
         if (srow) srow[pos] = -__builtin_inff();
       }
     } else {
-      const int kept2 = (n > p.ksel) ? wave_compact(buf, n, theta) : n;
-      if (lane == 0) p.cand_cnt[(row_base + ti) * p.n_splits + split] = kept2;
+      const int kept =
+          (n > p.ksel) ? wave_filter(buf, n, theta, [&](int pos, uint64_t v) { buf[pos] = v; }) : n;
+      if (lane == 0) p.cand_cnt[(row_base + ti) * p.n_splits + split] = kept;
     }
   }
 }
@@ -571,7 +630,7 @@ template <int GMAX, int DI, bool EXACT>
 __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
   constexpr int QC = 4, HC = 4;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int64_t u = (int64_t)blockIdx.x * kBlockWaves + wid;
   if (u >= p.units) return;
   const int b = (int)(u % p.B);
