@@ -122,32 +122,24 @@ struct QueryOperands {
         x = y;
       }
       accumulate(acc, x, wv[GMAX - 1]);
-      // keep the interleave: MFMA(g) issued, then the 8 VALU ops of block g-1
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-      for (int g = 1; g < GMAX; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-      }
+
     } else {
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
         if (g < g_rt) accumulate(acc, mfma_e4m3_16x16x128(a, bq[g]), wv[g]);
       }
     }
-    // sum over the HC heads of a column block (adjacent lanes)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = acc[r];
-      v += dpp_f32<kDppQuadXor1>(v);
-      v += dpp_f32<kDppQuadXor2>(v);
-      if (HC == 16) {
-        v += dpp_f32<kDppRowRor4>(v);
-        v += dpp_f32<kDppRowRor8>(v);
-      }
-      acc[r] = v;
+    const bool b1 = (jsel & 2) != 0, b0 = (jsel & 1) != 0;
+    const float keep0 = b1 ? acc[2] : acc[0], send0 = b1 ? acc[0] : acc[2];
+    const float keep1 = b1 ? acc[3] : acc[1], send1 = b1 ? acc[1] : acc[3];
+    const float c0 = keep0 + dpp_f32<kDppQuadXor2>(send0);
+    const float c1 = keep1 + dpp_f32<kDppQuadXor2>(send1);
+    float v = (b0 ? c1 : c0) + dpp_f32<kDppQuadXor1>(b0 ? c0 : c1);
+    if (HC == 16) {
+      v += dpp_f32<kDppRowRor4>(v);
+      v += dpp_f32<kDppRowRor8>(v);
     }
-    return jsel == 0 ? acc[0] : (jsel == 1 ? acc[1] : (jsel == 2 ? acc[2] : acc[3]));
+    return v;
   }
 };
 
@@ -337,14 +329,50 @@ __device__ __forceinline__ i32x8 load_key_tile(__amdgpu_buffer_rsrc_t rs, int of
 
 // ------------------------------------------------------------------ fused indexer + top-k
 
+// Smallest and largest high word (score bits) over buf[0, n), wave-reduced.
+__device__ void wave_hi_range(const uint64_t* buf, int n, uint32_t& mn, uint32_t& mx) {
+  const int lane = threadIdx.x & 63;
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  for (int e0 = 0; e0 < n; e0 += 128 * kHistBatch) {
+    uint64_t x[kHistBatch][2];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (e0 + 128 * u + 2 * lane + j < n) {
+          mn = min(mn, (uint32_t)(x[u][j] >> 32));
+          mx = max(mx, (uint32_t)(x[u][j] >> 32));
+        }
+      }
+    }
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+}
+
+// Low word of a selection key: ~s with bits 29-30 replaced by the query's slot in the
+// wave (keys stay below 2^29, where those bits of ~s are always set), so one LDS stage
+// can hold all of a wave's queries and ordering among one query's keys is unchanged.
+constexpr uint32_t kTagShift = 29;
+constexpr uint32_t kIndexMask = (1u << kTagShift) - 1u;
+__device__ __forceinline__ uint32_t tagged_lo_base(int slot) {
+  return 0x9FFFFFFFu | ((uint32_t)slot << kTagShift);  // minus s gives the tagged ~s
+}
+__device__ __forceinline__ int32_t untag_index(uint64_t key) {
+  return (int32_t)(kIndexMask - ((uint32_t)key & kIndexMask));
+}
+
 template <int QC, int GMAX, int DI, bool EXACT>
 __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   constexpr int HC = 16 / QC;
   // key tiles in flight per wave (the 16-block case keeps 128 VGPRs of query operands)
   constexpr int PF = GMAX >= 16 ? 2 : 4;
-  constexpr int STG = 2 * 16 * PF;  // per-query LDS staging of appended keys (two blocks' worth)
+  constexpr int WSTG = 2 * 64 * PF;  // wave stage: two blocks of appends from every lane
   __shared__ uint32_t hist_all[kBlockWaves][kHistBins];
-  __shared__ uint64_t stage_all[kBlockWaves][QC * STG];
+  __shared__ uint64_t stage_all[kBlockWaves][WSTG];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   uint32_t* hist = hist_all[wid];
@@ -374,35 +402,50 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   QueryOperands<QC, GMAX, DI> qo;
   qo.load(p, b, t, qvalid, t0, j, lg);
 
-  // lane constants: the key offset of this lane's pair within a tile, and the bound on
-  // key positions that are candidates for it (0 for lanes without a pair)
+  // lane constants: key offset of the lane's pair within a tile, the bound on candidate
+  // key positions (0 for lanes without a pair) and the tagged-index base
   const bool act = (QC == 4) || (j < 4);
   const int koff = 4 * lg + jsel;
   const int lim = (act && qvalid) ? min(n_q, ke) : 0;
-  const uint64_t qmask_base = 0x000F000F000F000Full;
-  const uint64_t my_qmask = (QC == 4) ? (qmask_base << (4 * qi)) : qmask_base;
-  const uint64_t lt = lanemask_lt();
+  const uint32_t lo_base = tagged_lo_base(qi);
   const size_t row_base = (size_t)b * p.T;
   auto qbuf = [&](int i) -> uint64_t* {
     return p.cand + ((row_base + t0 + i) * p.n_splits + split) * (size_t)p.cap;
   };
 
-  int gcnt[QC], scnt[QC];  // entries in the global buffer / in the LDS stage, per query
+  int gcnt[QC];  // entries in each query's global buffer
 #pragma unroll
-  for (int i = 0; i < QC; ++i) gcnt[i] = scnt[i] = 0;
-  uint64_t th_lane = 0ull;                    // own query's threshold: keep keys >= it
-  uint32_t mn_hi = 0xFFFFFFFFu, mx_hi = 0u;   // range of appended high words (own query)
-  const int limit = p.ksel + (p.cap - 2 * STG - p.ksel) / 2;
+  for (int i = 0; i < QC; ++i) gcnt[i] = 0;
+  int stotal = 0;             // entries in the wave stage
+  uint64_t th_lane = 0ull;    // own query's threshold: keep keys >= it
+  const int limit = p.ksel + (p.cap - WSTG - p.ksel) / 2;
 
-  auto flush = [&](int i) {
-    for (int l = lane; l < scnt[i]; l += 64) qbuf(i)[gcnt[i] + l] = stage[i * STG + l];
-    gcnt[i] += scnt[i];
-    scnt[i] = 0;
+  // stage -> per-query buffers, each query's entries in stage (= key) order
+  auto flush = [&]() {
+    for (int e0 = 0; e0 < stotal; e0 += 64) {
+      const int e = e0 + lane;
+      const bool valid = e < stotal;
+      const uint64_t v = valid ? stage[e] : 0ull;
+      const int q = (int)(((uint32_t)v >> kTagShift) & 3u);
+#pragma unroll
+      for (int i = 0; i < QC; ++i) {
+        const bool mine = valid && q == i;
+        const uint64_t m = ballot64(mine);
+        if (mine)
+          qbuf(i)[gcnt[i] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))] = v;
+        gcnt[i] += popc64(m);
+      }
+    }
+    stotal = 0;
   };
-  auto range_of = [&](int i, uint64_t& prefix, int& rem) {
-    const uint32_t lo_r = wave_min_u32(qi == i ? mn_hi : 0xFFFFFFFFu);
-    const uint32_t hi_r = wave_max_u32(qi == i ? mx_hi : 0u);
-    select_start(lo_r, hi_r, prefix, rem);
+  auto select_on = [&](uint64_t* buf, int n, int lim_kept) -> SelectResult {
+    uint32_t mn, mx;
+    wave_hi_range(buf, n, mn, mx);
+    uint64_t prefix;
+    int rem;
+    select_start(mn, mx, prefix, rem);
+    return wave_radix_select(buf, n, p.ksel, lim_kept, prefix, rem, hist);
   };
 
   // key rows of this sequence behind a bounds-checked buffer: rows >= kv_len read as 0
@@ -424,51 +467,35 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
 #pragma unroll
     for (int ui = 0; ui < PF; ++ui) {
       const int s = s0 + 16 * ui + koff;
-      const uint32_t hi = f32_to_ordered(sc[ui]);
-      const uint64_t key = ((uint64_t)hi << 32) | (uint64_t)(~(uint32_t)s);
-      const bool pass = s < lim && key >= th_lane;
+      const uint64_t key = ((uint64_t)f32_to_ordered(sc[ui]) << 32) | (uint64_t)(lo_base - (uint32_t)s);
+      const bool pass = (s < lim) & (key >= th_lane);
       const uint64_t bal = ballot64(pass);
       if (bal) {
-        int sb = scnt[0];
-#pragma unroll
-        for (int i = 1; i < QC; ++i) sb = (qi == i) ? scnt[i] : sb;
-        if (pass) {
-          stage[qi * STG + sb + popc64(bal & my_qmask & lt)] = key;
-          mn_hi = min(mn_hi, hi);
-          mx_hi = max(mx_hi, hi);
-        }
-#pragma unroll
-        for (int i = 0; i < QC; ++i)
-          scnt[i] += popc64(bal & (QC == 4 ? (qmask_base << (4 * i)) : qmask_base));
+        if (pass)
+          stage[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, stotal))] = key;
+        stotal += popc64(bal);
       }
     }
-    // a stage that cannot take two more blocks is flushed; a buffer that cannot take
-    // another flush is compacted
+    // the stage must take another block; each buffer must take a full stage
+    if (stotal > WSTG - 64 * PF) {
+      flush();
 #pragma unroll
-    for (int i = 0; i < QC; ++i) {
-      if (scnt[i] > STG - 16 * PF) {
-        flush(i);
-        if (gcnt[i] > p.cap - STG) {
+      for (int i = 0; i < QC; ++i) {
+        if (gcnt[i] > p.cap - WSTG) {
           mem_fence_wave();
           uint64_t* buf = qbuf(i);
-          uint64_t prefix;
-          int rem;
-          range_of(i, prefix, rem);
-          const SelectResult sr = wave_radix_select(buf, gcnt[i], p.ksel, limit, prefix, rem, hist);
+          const SelectResult sr = select_on(buf, gcnt[i], limit);
           gcnt[i] = wave_filter(buf, gcnt[i], sr.theta, [&](int pos, uint64_t v) { buf[pos] = v; });
           mem_fence_wave();
-          if (qi == i) {
-            th_lane = sr.theta;
-            mn_hi = max(mn_hi, (uint32_t)(sr.theta >> 32));
-          }
+          if (qi == i) th_lane = sr.theta;
         }
       }
     }
   }
 
   // final exact selection for each query of the wave
-#pragma unroll
-  for (int i = 0; i < QC; ++i) flush(i);
+  flush();
   mem_fence_wave();
 #pragma unroll
   for (int i = 0; i < QC; ++i) {
@@ -476,19 +503,13 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     if (ti >= p.T) break;
     uint64_t* buf = qbuf(i);
     const int n = gcnt[i];
-    uint64_t theta = 0ull;
-    if (n > p.ksel) {
-      uint64_t prefix;
-      int rem;
-      range_of(i, prefix, rem);
-      theta = wave_radix_select(buf, n, p.ksel, 0, prefix, rem, hist).theta;
-    }
+    const uint64_t theta = (n > p.ksel) ? select_on(buf, n, 0).theta : 0ull;
     if (p.n_splits == 1) {
       // kept entries (ascending index) straight into the output row, then padding
       int32_t* orow = p.idx + (row_base + ti) * (size_t)p.ksel;
       float* srow = p.sel ? p.sel + (row_base + ti) * (size_t)p.ksel : nullptr;
       const int out = wave_filter(buf, n, theta, [&](int pos, uint64_t v) {
-        orow[pos] = (int32_t)(~(uint32_t)v);
+        orow[pos] = untag_index(v);
         if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
       });
       for (int pos = out + lane; pos < p.ksel; pos += 64) {
@@ -611,7 +632,7 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
       for (int w = 0; w < kMergeBlock / 64; ++w) total += wave_cnt[w];
       if (keep) {
         const int pos = before + popc64(bal & lt);
-        orow[pos] = (int32_t)(~(uint32_t)v);
+        orow[pos] = untag_index(v);
         if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
       }
       out += total;
@@ -697,7 +718,7 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   const int64_t sl = ((int64_t)a.S_max + ns - 1) / ns;
   p.split_len = (int)(((sl + 15) / 16) * 16);
   const int kpad = ((k + 63) / 64) * 64;
-  p.cap = 2 * kpad + 128;
+  p.cap = 2 * kpad + 1024;  // room for k, a full wave stage and slack
   p.units = base_units * ns;
   const size_t rows = (size_t)a.B * a.T * ns;
   p.cand_bytes = rows * (size_t)p.cap * sizeof(uint64_t);

@@ -55,6 +55,9 @@ ix_status check_indexer(const ix_indexer_args* a, bool* empty) {
   const double k_bytes = (double)a->B * a->S_max * a->d_I;
   const double q_bytes = (double)a->B * a->T * a->H_I * a->d_I;
   if (k_bytes > 9.0e18 || q_bytes > 9.0e18) return fail(IX_ERR_INVALID, "tensor too large");
+  if ((int64_t)a->S_max * a->d_I >= ((int64_t)1 << 31))
+    return fail(IX_ERR_UNSUPPORTED, "S_max*d_I=%lld: one sequence's indexer keys must stay below 2 GiB",
+                (long long)a->S_max * a->d_I);
   if ((int64_t)a->B * a->T > (int64_t)0x7FFFFFFF)
     return fail(IX_ERR_UNSUPPORTED, "B*T=%lld exceeds the grid limit",
                 (long long)((int64_t)a->B * a->T));

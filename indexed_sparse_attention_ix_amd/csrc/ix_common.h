@@ -39,16 +39,15 @@ constexpr int kDppRowRor8 = 0x128;  // row_ror:8
 
 template <int Ctrl>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, false));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, true));
 }
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger integer); -0 is first
 // folded onto +0 so both zeros share one key.
 __device__ __forceinline__ uint32_t f32_to_ordered(float f) {
-  f = f + 0.0f;
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float ordered_to_f32(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
