@@ -4,16 +4,20 @@
 //   p = softmax_j(sm_scale * q_h . K[idx_j]),  out_h = sum_j p_j V[idx_j].
 //
 // Block = 4 waves on one (query token, KV head); the selection is cut into chunks
-// of 32 entries and wave w takes chunks w, w+4, ...  Per chunk, the 32 gathered K rows
-// go straight from memory into bf16 MFMA A operands (one 64-byte contiguous piece of a
-// row per lane per instruction), S^T = K Q^T puts keys on rows and the (up to 16)
-// query heads sharing the KV head on columns, and an online softmax in the exp2
-// domain keeps one running max per head.  The gathered V rows are staged in LDS so
-// that the PV product can read them key-major; the probability operand comes
-// straight from the lanes that computed S^T (keys {4g+i, 16+4g+i} in lane group g,
-// matched by the same key order in the V operand).  The four waves' (m, l, O) are
-// merged through LDS at the end.  Small batches split the selection over several
-// blocks and merge the normalised partials by their log-sum-exp.
+// of 32 entries and wave w takes chunks w, w+4, ...  Per chunk:
+//  * S^T = K Q^T (bf16 MFMA 16x16x32): the 32 gathered K rows go straight from memory
+//    into A operands (each lane reads one contiguous 64-byte piece of a row per
+//    instruction, whole 256-byte rows per 4 lanes); the (up to 16) query heads that
+//    share the KV head are the columns, so lane (g, h) holds keys {4g+i, 16+4g+i} of
+//    head h.
+//  * online softmax in the exp2 domain, one running max per head; the max across the
+//    four lane groups uses permlane swaps (no LDS round trip).
+//  * O^T += V^T P^T: P^T is the B operand straight from the lanes that computed S^T;
+//    V rows are staged row-major in LDS and V^T operands are read with the gfx950
+//    transposing LDS read (each lane receives four keys of one column), so output lane
+//    (g, h) holds head h and the per-head rescale stays in-lane.
+// The four waves' (m, l, O) are merged through LDS at the end.  Small batches split
+// the selection over several blocks and merge the normalised partials by lse.
 #include "ix_common.h"
 #include "ix_internal.h"
 
@@ -24,7 +28,7 @@ namespace {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = kAttnWaves * kWave;
 constexpr int kChunk = 32;
-constexpr int kVPad = 4;  // bf16 elements of padding per staged V row
+constexpr int kVPad = 16;  // bf16 elements of padding per staged V row (bank spread)
 
 struct AttnArgs {
   const uint16_t* q;
@@ -51,15 +55,53 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, ld_global_16(p));
 }
 
+// Reductions across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48).
+// v_permlane16_swap x, y exchanges x's rows 1, 3 with y's rows 0, 2 (v_permlane32_swap:
+// x's upper half with y's lower half).  With y a copy of x, x and y then hold each row
+// and its neighbour, so one max/add per stage pairs the rows.  Written as asm with both
+// registers read-write: the compiler's model of the builtin drops one of the two
+// results when the operands are equal.  The s_nop's give the VALU <-> permlane hazard
+// its wait states.
+__device__ __forceinline__ void row_pair_swap16(uint32_t& x, uint32_t& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void row_pair_swap32(uint32_t& x, uint32_t& y) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ float max_across_rows(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  row_pair_swap16(x, y);
+  v = fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+  x = y = __builtin_bit_cast(uint32_t, v);
+  row_pair_swap32(x, y);
+  return fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  row_pair_swap16(x, y);
+  v = __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+  x = y = __builtin_bit_cast(uint32_t, v);
+  row_pair_swap32(x, y);
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+
+// Transposing LDS read: within each 16-lane group, lane i receives element (i & 3) of
+// the 8-byte reads of lanes 4r + (i >> 2), r = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) {
   constexpr int MC = D / 32;   // depth chunks of the QK^T product
-  constexpr int NT = D / 16;   // output column tiles of the PV product
+  constexpr int NT = D / 16;   // 16-column tiles of the PV product
   constexpr int VROW = D + kVPad;
   __shared__ __attribute__((aligned(16))) uint16_t vs_all[kAttnWaves][kChunk * VROW];
   __shared__ float ml_all[kAttnWaves][2][16];
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, lg = lane >> 4;
   const int split = blockIdx.x % p.n_splits;
   const int64_t rk = blockIdx.x / p.n_splits;  // (b*T + t) * H_kv + kvh
@@ -87,10 +129,12 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   const uint16_t* kbase = p.kc + (size_t)b * p.S_max * kv_stride + (size_t)kvh * D;
   const uint16_t* vbase = p.vc + (size_t)b * p.S_max * kv_stride + (size_t)kvh * D;
   uint16_t* vs = vs_all[wid];
+  // transposed-read source address of this lane: row 4*lg + r16/4 (+16), column 4*(r16&3)
+  const uint16_t* vt_src = vs + (4 * lg + (r16 >> 2)) * VROW + 4 * (r16 & 3);
 
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-  f32x4 o[NT];
+  float m_run = -__builtin_inff();  // running max of head r16 (log2 domain)
+  float l_run = 0.f;                // this lane's share of the running sum
+  f32x4 o[NT];                      // O^T: rows 16nt + 4lg + i (d), column r16 (head)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -120,15 +164,11 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     }
     const uint64_t vm0 = ballot64(j0 >= 0), vm1 = ballot64(j1 >= 0);
 
-    // stage V rows (row = key within the chunk)
+    // stage V rows (row = key within the chunk), 16-byte writes
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-      uint16_t* d0 = vs + r16 * VROW + 32 * m + 8 * lg;
-      uint16_t* d1 = vs + (16 + r16) * VROW + 32 * m + 8 * lg;
-      *reinterpret_cast<uint64_t*>(d0) = ((uint64_t)(uint32_t)va0[m][1] << 32) | (uint32_t)va0[m][0];
-      *reinterpret_cast<uint64_t*>(d0 + 4) = ((uint64_t)(uint32_t)va0[m][3] << 32) | (uint32_t)va0[m][2];
-      *reinterpret_cast<uint64_t*>(d1) = ((uint64_t)(uint32_t)va1[m][1] << 32) | (uint32_t)va1[m][0];
-      *reinterpret_cast<uint64_t*>(d1 + 4) = ((uint64_t)(uint32_t)va1[m][3] << 32) | (uint32_t)va1[m][2];
+      *reinterpret_cast<i32x4*>(vs + r16 * VROW + 32 * m + 8 * lg) = va0[m];
+      *reinterpret_cast<i32x4*>(vs + (16 + r16) * VROW + 32 * m + 8 * lg) = va1[m];
     }
 
     // S^T tiles: lane holds keys 16*tt + 4*lg + i for head r16
@@ -148,8 +188,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
       x[4 + i] = ok1 ? s1[i] * p.scale_log2 : -__builtin_inff();
       mloc = fmaxf(mloc, fmaxf(x[i], x[4 + i]));
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = max_across_rows(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const bool any = m_new != -__builtin_inff();
     const float alpha = (any && m_run != -__builtin_inff()) ? exp2f(m_run - m_new) : (any ? 0.f : 1.f);
@@ -162,61 +201,46 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // rescale O rows (heads 4*lg + i) by their head's alpha (held by lane 4*lg + i)
-    float al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * lg + i);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= al[i];
+      for (int i = 0; i < 4; ++i) o[nt][i] *= alpha;
 
-    // P as the A operand of O += P V: row = head r16, depth slots = keys
+    // P^T as the B operand: column = head r16, depth slots = keys
     // {4lg..4lg+3, 16+4lg..16+4lg+3}
-    bf16x8 pa;
+    bf16x8 pb;
     {
-      uint16_t pb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = f32_to_bf16_rne(pr[e]);
       i32x4 pk;
-      pk[0] = (int)((uint32_t)pb[0] | ((uint32_t)pb[1] << 16));
-      pk[1] = (int)((uint32_t)pb[2] | ((uint32_t)pb[3] << 16));
-      pk[2] = (int)((uint32_t)pb[4] | ((uint32_t)pb[5] << 16));
-      pk[3] = (int)((uint32_t)pb[6] | ((uint32_t)pb[7] << 16));
-      pa = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[e] = (int)((uint32_t)f32_to_bf16_rne(pr[2 * e]) |
+                      ((uint32_t)f32_to_bf16_rne(pr[2 * e + 1]) << 16));
+      pb = __builtin_bit_cast(bf16x8, pk);
     }
     lds_wait();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int col = 16 * nt + r16;
-      uint16_t vv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vv[i] = vs[(4 * lg + i) * VROW + col];
-        vv[4 + i] = vs[(16 + 4 * lg + i) * VROW + col];
-      }
-      i32x4 vk;
-      vk[0] = (int)((uint32_t)vv[0] | ((uint32_t)vv[1] << 16));
-      vk[1] = (int)((uint32_t)vv[2] | ((uint32_t)vv[3] << 16));
-      vk[2] = (int)((uint32_t)vv[4] | ((uint32_t)vv[5] << 16));
-      vk[3] = (int)((uint32_t)vv[6] | ((uint32_t)vv[7] << 16));
-      o[nt] = mfma_bf16_16x16x32(pa, __builtin_bit_cast(bf16x8, vk), o[nt]);
+      // V^T rows 16nt..16nt+15 (d), depth = the same 8 keys as P^T
+      const i16x4 lo = lds_read_tr16(vt_src + 16 * nt);
+      const i16x4 hi = lds_read_tr16(vt_src + 16 * VROW + 16 * nt);
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      o[nt] = mfma_bf16_16x16x32(va, pb, o[nt]);
     }
     lds_wait();
   }
 
-  // per-head l: sum the lane-group partials
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  // per-head l: sum the four lane groups' shares
+  l_run = sum_across_rows(l_run);
 
-  // merge the 4 waves through LDS
+  // merge the 4 waves through LDS: os[head][d]
   __syncthreads();
-  float* os = reinterpret_cast<float*>(vs);  // [16][D] floats of this wave
+  float* os = reinterpret_cast<float*>(vs);
   static_assert(16 * D * sizeof(float) <= kChunk * VROW * sizeof(uint16_t), "O staging");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) os[(4 * lg + i) * D + 16 * nt + r16] = o[nt][i];
+    for (int i = 0; i < 4; ++i) os[r16 * D + 16 * nt + 4 * lg + i] = o[nt][i];
   if (lg == 0) {
     ml_all[wid][0][r16] = m_run;
     ml_all[wid][1][r16] = l_run;
