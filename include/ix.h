@@ -31,7 +31,9 @@
  *     abort crosses the ABI.
  *   - B == 0 or T == 0 is a valid empty call: IX_OK, nothing launched.
  *   - Supported shapes: d_I in {64,128}; H_I a multiple of 4 in [4,64];
- *     d in {64,128}; H_q a multiple of H_kv with H_q/H_kv <= 16; 1 <= k <= 2048.
+ *     d in {64,128}; H_q a multiple of H_kv with H_q/H_kv <= 16; 1 <= k <= 2048;
+ *     one sequence's indexer keys (S_max*d_I bytes) below 2 GiB and its K and V
+ *     caches (S_max*H_kv*d*2 bytes each) within 2 GiB.
  *     Other shapes return IX_ERR_UNSUPPORTED (no fallback path exists).
  *   - Calls are re-entrant; concurrent calls must not share a workspace.
  */

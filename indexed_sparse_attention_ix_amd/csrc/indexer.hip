@@ -311,12 +311,6 @@ __device__ __forceinline__ void mem_fence_wave() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 }
 
-// Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
 // One 16-row key tile as the A operand: lane (row r, group g) gets bytes [32g, 32g+32) of
 // its row (rows of width 64 repeat bytes [32(g&1), ...) in groups 2, 3; the query
 // operand is zero there, so they add nothing).

@@ -85,6 +85,10 @@ ix_status check_attn_shape(int32_t B, int32_t T, int32_t S_max, int32_t H_q, int
   if (S_max < 1) return fail(IX_ERR_INVALID, "S_max=%d must be >= 1", S_max);
   if ((int64_t)B * T * H_kv > (int64_t)0x7FFFFFFF / 64)
     return fail(IX_ERR_UNSUPPORTED, "B*T*H_kv too large for one launch");
+  if ((int64_t)S_max * H_kv * d * 2 > ((int64_t)1 << 31))
+    return fail(IX_ERR_UNSUPPORTED,
+                "S_max*H_kv*d=%lld: one sequence's K (or V) cache must stay within 2 GiB",
+                (long long)S_max * H_kv * d);
   return IX_OK;
 }
 

@@ -72,6 +72,12 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // Wait for this wave's outstanding vector-memory operations.
 __device__ __forceinline__ void vmem_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 __device__ __forceinline__ i32x4 ld_global_16(const void* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }

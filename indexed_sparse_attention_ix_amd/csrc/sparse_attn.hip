@@ -5,17 +5,20 @@
 //
 // Block = 4 waves on one (query token, KV head); the selection is cut into chunks
 // of 32 entries and wave w takes chunks w, w+4, ...  Per chunk:
-//  * S^T = K Q^T (bf16 MFMA 16x16x32): the 32 gathered K rows go straight from memory
-//    into A operands (each lane reads one contiguous 64-byte piece of a row per
-//    instruction, whole 256-byte rows per 4 lanes); the (up to 16) query heads that
-//    share the KV head are the columns, so lane (g, h) holds keys {4g+i, 16+4g+i} of
-//    head h.
+//  * gather: the chunk's 32 K rows and 32 V rows are fetched with 16-byte loads in
+//    which consecutive lanes read consecutive pieces of one row (a whole row per
+//    D/8 lanes), so every load touches only a few cache lines; rows are staged in
+//    LDS with a bank swizzle.  The next chunk's gathers are issued before this
+//    chunk's arithmetic, so they overlap it.
+//  * S^T = K Q^T (bf16 MFMA 16x16x32): K rows come from LDS as A operands; the (up
+//    to 16) query heads that share the KV head are the columns, so lane (g, h) holds
+//    keys {4g+i, 16+4g+i} of head h.
 //  * online softmax in the exp2 domain, one running max per head; the max across the
 //    four lane groups uses permlane swaps (no LDS round trip).
 //  * O^T += V^T P^T: P^T is the B operand straight from the lanes that computed S^T;
-//    V rows are staged row-major in LDS and V^T operands are read with the gfx950
-//    transposing LDS read (each lane receives four keys of one column), so output lane
-//    (g, h) holds head h and the per-head rescale stays in-lane.
+//    V^T operands are read with the gfx950 transposing LDS read (each lane receives
+//    four keys of one column), so output lane (g, h) holds head h and the per-head
+//    rescale stays in-lane.
 // The four waves' (m, l, O) are merged through LDS at the end.  Small batches split
 // the selection over several blocks and merge the normalised partials by lse.
 #include "ix_common.h"
@@ -28,7 +31,6 @@ namespace {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = kAttnWaves * kWave;
 constexpr int kChunk = 32;
-constexpr int kVPad = 16;  // bf16 elements of padding per staged V row (bank spread)
 
 struct AttnArgs {
   const uint16_t* q;
@@ -87,26 +89,47 @@ __device__ __forceinline__ float sum_across_rows(float v) {
 
 // Transposing LDS read: within each 16-lane group, lane i receives element (i & 3) of
 // the 8-byte reads of lanes 4r + (i >> 2), r = 0..3.
-__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// Bank swizzle of the staged K/V rows: 16-byte piece p of chunk slot n sits at piece
+// position p ^ swz(n).  Rows are 256 B (D = 128: one row per 64-bank line) or 128 B
+// (D = 64: two rows per line); swz rotates the slot's position within the line left by
+// one bit, so the 16 slots of an A-operand read hit 16 distinct 16-byte bank groups and
+// the 8 slots of a half-wave transposed read hit 8 distinct 32-byte groups.
+template <int D>
+__device__ __forceinline__ int stage_swz(int n) {
+  constexpr int PI = D / 8;                     // 16-byte pieces per row
+  constexpr int LOG = D == 128 ? 4 : 3;
+  const int m = (D == 128 ? n : (n >> 1)) & (PI - 1);
+  return ((m << 1) & (PI - 1)) | (m >> (LOG - 1));
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) {
-  constexpr int MC = D / 32;   // depth chunks of the QK^T product
-  constexpr int NT = D / 16;   // 16-column tiles of the PV product
-  constexpr int VROW = D + kVPad;
-  __shared__ __attribute__((aligned(16))) uint16_t vs_all[kAttnWaves][kChunk * VROW];
+  constexpr int MC = D / 32;          // depth tiles of the QK^T product
+  constexpr int NT = D / 16;          // 16-row tiles of O^T
+  constexpr int ROWB = D * 2;         // bytes per K or V row
+  constexpr int PI = ROWB / 16;       // 16-byte pieces per row
+  constexpr int RPI = kWave / PI;     // rows per 64-lane load
+  constexpr int NI = kChunk / RPI;    // loads per chunk per tensor
+  __shared__ __attribute__((aligned(16))) unsigned char stage_all[kAttnWaves][2][kChunk * ROWB];
   __shared__ float ml_all[kAttnWaves][2][16];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, lg = lane >> 4;
-  const int split = blockIdx.x % p.n_splits;
-  const int64_t rk = blockIdx.x / p.n_splits;  // (b*T + t) * H_kv + kvh
+  // XCD-aware order: the hardware deals consecutive blocks to the 8 XCDs in turn, so
+  // block i runs on XCD i % 8; give each XCD a contiguous range of rows so nearby
+  // queries (which tend to select overlapping keys) share one L2.
+  unsigned bid = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+  const int split = bid % p.n_splits;
+  const int64_t rk = bid / p.n_splits;  // (b*T + t) * H_kv + kvh
   const int kvh = (int)(rk % p.H_kv);
-  const int64_t row = rk / p.H_kv;             // b*T + t
+  const int64_t row = rk / p.H_kv;      // b*T + t
   const int b = (int)(row / p.T);
   int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
   kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
@@ -125,12 +148,34 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   }
 
   const int32_t* irow = p.idx + (size_t)row * p.k;
-  const size_t kv_stride = (size_t)p.H_kv * D;
-  const uint16_t* kbase = p.kc + (size_t)b * p.S_max * kv_stride + (size_t)kvh * D;
-  const uint16_t* vbase = p.vc + (size_t)b * p.S_max * kv_stride + (size_t)kvh * D;
-  uint16_t* vs = vs_all[wid];
-  // transposed-read source address of this lane: row 4*lg + r16/4 (+16), column 4*(r16&3)
-  const uint16_t* vt_src = vs + (4 * lg + (r16 >> 2)) * VROW + 4 * (r16 & 3);
+  const uint32_t kv_stride_b = (uint32_t)(p.H_kv * ROWB);
+  const size_t seq_off = ((size_t)b * p.S_max * p.H_kv + kvh) * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.kc + seq_off, (uint32_t)kvl * kv_stride_b);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.vc + seq_off, (uint32_t)kvl * kv_stride_b);
+  unsigned char* kst = stage_all[wid][0];
+  unsigned char* vst = stage_all[wid][1];
+
+  // Gather layout: lane (rho = lane / PI, s = lane % PI) of load j fetches piece s of
+  // chunk slot n = rho * NI + j, so each row is read by PI consecutive lanes.
+  const int rho = lane / PI, s = lane % PI;
+  uint32_t woff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int n = rho * NI + j;
+    woff[j] = (uint32_t)(n * ROWB + 16 * (s ^ stage_swz<D>(n)));
+  }
+  // A operand of S^T (key tile tt = 0; tile 1 is 16 rows further): slot r16, piece 4m+lg
+  uint32_t koff[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) koff[m] = (uint32_t)(r16 * ROWB + 16 * ((4 * m + lg) ^ stage_swz<D>(r16)));
+  // transposed V read: slot 4lg + r16/4 (+16), logical bytes [32nt + 8(r16 & 3), +8)
+  uint32_t voff[NT];
+  {
+    const int n = 4 * lg + (r16 >> 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      voff[nt] = (uint32_t)(n * ROWB + 16 * ((2 * nt + ((r16 >> 1) & 1)) ^ stage_swz<D>(n)) + 8 * (r16 & 1));
+  }
 
   float m_run = -__builtin_inff();  // running max of head r16 (log2 domain)
   float l_run = 0.f;                // this lane's share of the running sum
@@ -140,50 +185,84 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
 
   const int c_begin = split * p.chunks_per_split;
   const int c_end = min(c_begin + p.chunks_per_split, p.chunks);
-  auto load_idx = [&](int c, int tt) -> int {
-    const int e = c * kChunk + tt * 16 + r16;
-    int j = (c < c_end && e < p.k) ? irow[e] : -1;
-    return (j >= 0 && j < kvl) ? j : -1;
+  const bool idx_vec = (p.k & 3) == 0;
+
+  // Selected positions of this lane's NI slots of chunk c (-1: padding or not visible).
+  auto load_idx = [&](int c, int (&jv)[NI]) {
+    const int e0 = c * kChunk + rho * NI;
+    if (c >= c_end) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) jv[j] = -1;
+    } else if (idx_vec && c * kChunk + kChunk <= p.k) {
+#pragma unroll
+      for (int j = 0; j < NI; j += 4) {
+        const i32x4 v = ld_global_16(irow + e0 + j);
+        jv[j] = v[0]; jv[j + 1] = v[1]; jv[j + 2] = v[2]; jv[j + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) jv[j] = e0 + j < p.k ? irow[e0 + j] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) jv[j] = (jv[j] >= 0 && jv[j] < kvl) ? jv[j] : -1;
   };
-  int jn0 = load_idx(c_begin + wid, 0), jn1 = load_idx(c_begin + wid, 1);
-
-  for (int c = c_begin + wid; c < c_end; c += kAttnWaves) {
-    const int j0 = jn0, j1 = jn1;
-    jn0 = load_idx(c + kAttnWaves, 0);
-    jn1 = load_idx(c + kAttnWaves, 1);
-    const size_t r0 = (size_t)(j0 >= 0 ? j0 : 0) * kv_stride;
-    const size_t r1 = (size_t)(j1 >= 0 ? j1 : 0) * kv_stride;
-    bf16x8 ka0[MC], ka1[MC];
-    i32x4 va0[MC], va1[MC];
+  // Bit n of the result: slot n of the chunk holds a valid key.
+  auto slot_mask = [&](const int (&jv)[NI]) -> uint32_t {
+    uint32_t bits = 0;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      ka0[m] = load_bf16x8(kbase + r0 + 32 * m + 8 * lg);
-      ka1[m] = load_bf16x8(kbase + r1 + 32 * m + 8 * lg);
-      va0[m] = ld_global_16(vbase + r0 + 32 * m + 8 * lg);
-      va1[m] = ld_global_16(vbase + r1 + 32 * m + 8 * lg);
-    }
-    const uint64_t vm0 = ballot64(j0 >= 0), vm1 = ballot64(j1 >= 0);
-
-    // stage V rows (row = key within the chunk), 16-byte writes
+    for (int j = 0; j < NI; ++j) bits |= (jv[j] >= 0 ? 1u : 0u) << j;
+    uint32_t mask = 0;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      *reinterpret_cast<i32x4*>(vs + r16 * VROW + 32 * m + 8 * lg) = va0[m];
-      *reinterpret_cast<i32x4*>(vs + (16 + r16) * VROW + 32 * m + 8 * lg) = va1[m];
+    for (int r = 0; r < RPI; ++r) mask |= (uint32_t)__builtin_amdgcn_readlane((int)bits, r * PI) << (r * NI);
+    return mask;
+  };
+  i32x4 kd[NI], vd[NI];
+  auto issue_rows = [&](const int (&jv)[NI]) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * kv_stride_b + 16u * s : 0x80000000u;
+      kd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
     }
+  };
+
+  int jv[NI];
+  const int c0 = c_begin + wid;
+  load_idx(c0, jv);
+  uint32_t mask_next = slot_mask(jv);
+  issue_rows(jv);
+  load_idx(c0 + kAttnWaves, jv);
+
+  for (int c = c0; c < c_end; c += kAttnWaves) {
+    // stage this chunk's rows (bank-swizzled) and start the next chunk's gathers
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      *reinterpret_cast<i32x4*>(kst + woff[j]) = kd[j];
+      *reinterpret_cast<i32x4*>(vst + woff[j]) = vd[j];
+    }
+    const uint32_t vmask = mask_next;
+    if (c + kAttnWaves < c_end) {
+      mask_next = slot_mask(jv);
+      issue_rows(jv);
+      load_idx(c + 2 * kAttnWaves, jv);
+    }
+    lds_wait();
 
     // S^T tiles: lane holds keys 16*tt + 4*lg + i for head r16
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-      s0 = mfma_bf16_16x16x32(ka0[m], qb[m], s0);
-      s1 = mfma_bf16_16x16x32(ka1[m], qb[m], s1);
+      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(kst + koff[m]);
+      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(kst + koff[m] + 16 * ROWB);
+      s0 = mfma_bf16_16x16x32(ka0, qb[m], s0);
+      s1 = mfma_bf16_16x16x32(ka1, qb[m], s1);
     }
     float x[8];
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok0 = (vm0 >> (4 * lg + i)) & 1ull;
-      const bool ok1 = (vm1 >> (4 * lg + i)) & 1ull;
+      const bool ok0 = (vmask >> (4 * lg + i)) & 1u;
+      const bool ok1 = (vmask >> (16 + 4 * lg + i)) & 1u;
       x[i] = ok0 ? s0[i] * p.scale_log2 : -__builtin_inff();
       x[4 + i] = ok1 ? s1[i] * p.scale_log2 : -__builtin_inff();
       mloc = fmaxf(mloc, fmaxf(x[i], x[4 + i]));
@@ -217,12 +296,11 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
                       ((uint32_t)f32_to_bf16_rne(pr[2 * e + 1]) << 16));
       pb = __builtin_bit_cast(bf16x8, pk);
     }
-    lds_wait();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       // V^T rows 16nt..16nt+15 (d), depth = the same 8 keys as P^T
-      const i16x4 lo = lds_read_tr16(vt_src + 16 * nt);
-      const i16x4 hi = lds_read_tr16(vt_src + 16 * VROW + 16 * nt);
+      const i16x4 lo = lds_read_tr16(vst + voff[nt]);
+      const i16x4 hi = lds_read_tr16(vst + voff[nt] + 16 * ROWB);
       const bf16x8 va = __builtin_bit_cast(
           bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       o[nt] = mfma_bf16_16x16x32(va, pb, o[nt]);
@@ -235,8 +313,8 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
 
   // merge the 4 waves through LDS: os[head][d]
   __syncthreads();
-  float* os = reinterpret_cast<float*>(vs);
-  static_assert(16 * D * sizeof(float) <= kChunk * VROW * sizeof(uint16_t), "O staging");
+  float* os = reinterpret_cast<float*>(kst);
+  static_assert(16 * D * sizeof(float) <= 2 * kChunk * ROWB, "O staging");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -261,7 +339,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
         const float mw = ml_all[w][0][h];
         const float f = mw == -__builtin_inff() ? 0.f : exp2f(mw - M);
         L += f * ml_all[w][1][h];
-        acc += f * reinterpret_cast<float*>(vs_all[w])[h * D + dcol];
+        acc += f * reinterpret_cast<const float*>(stage_all[w][0])[h * D + dcol];
       }
     }
     const float val = L > 0.f ? acc / L : 0.f;
@@ -271,7 +349,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
       p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(val);
       if (p.lse && dcol == 0) p.lse[(size_t)row * p.H_q + head] = lse_v;
     } else {
-      const size_t pr = (size_t)blockIdx.x;  // (row*H_kv + kvh) * n_splits + split
+      const size_t pr = (size_t)rk * p.n_splits + split;
       p.part_o[(pr * 16 + h) * D + dcol] = val;
       if (dcol == 0) p.part_lse[pr * 16 + h] = lse_v;
     }

@@ -108,6 +108,9 @@ def test_attention_validation_codes():
     assert call(out=0) == bd.IX_ERR_INVALID
     assert call(kc=FAKE + 2) == bd.IX_ERR_INVALID
     assert call(sm_scale=float("nan")) == bd.IX_ERR_INVALID
+    # one sequence's K/V cache is addressed with 32-bit buffer offsets: at most 2 GiB
+    assert call(S_max=(1 << 23) + 1, H_kv=1, H_q=16) == bd.IX_ERR_UNSUPPORTED
+    assert call(S_max=1 << 20, H_kv=16, H_q=16) == bd.IX_ERR_UNSUPPORTED
     # decode-sized batches split the selection and need a workspace
     need = bd.sparse_attn_workspace_bytes(64, 1, 16, 1, 128, 2048)
     assert need > 0
