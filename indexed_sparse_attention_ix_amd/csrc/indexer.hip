@@ -20,6 +20,13 @@
 // threshold that keeps at least k entries and the buffer is compacted in place
 // (order preserved).  At the end an exact select leaves exactly min(k, count)
 // entries, already in ascending index order, so no sort is needed.
+//
+// Key splits (small batches): each (query, split) keeps only its top-k' (k' <= k) and
+// notes the smallest key it kept whenever it dropped any.  The merge takes the exact
+// top-k of the union; that is the true top-k whenever every split that dropped keys
+// kept nothing below the union's k-th key (all dropped keys then rank below it).
+// Queries that fail the check are recomputed by an unsplit pass; k' only trades
+// merge work against how often that happens, never the result.
 #include "ix_common.h"
 #include "ix_internal.h"
 
@@ -32,6 +39,12 @@ constexpr int kBlock = kBlockWaves * kWave;
 constexpr int kHistBins = 256;
 constexpr int kHistBatch = 4;  // 16-byte loads in flight per lane in a histogram pass
 
+// Key tiles in flight per wave: as many as the registers left beside the query operands
+// allow (GMAX head blocks of 8 VGPRs each).  The wave's LDS stage takes two blocks of
+// appends from every lane per tile in flight.
+constexpr int prefetch_tiles(int gmax) { return gmax >= 16 ? 2 : gmax >= 8 ? 4 : 8; }
+constexpr int wave_stage_entries(int gmax) { return 2 * 64 * prefetch_tiles(gmax); }
+
 struct IxArgs {
   const uint8_t* q;
   const uint8_t* k;
@@ -41,11 +54,16 @@ struct IxArgs {
   int B, T, S_max, H_I;
   int g;          // head blocks actually used (<= GMAX)
   int qgroups;    // query groups per sequence (over the row window for ix_score)
-  int n_splits, split_len, cap, ksel;
+  int n_splits, split_len, cap;
+  int ksel;       // entries each wave unit keeps (per split when n_splits > 1)
+  int kout;       // k of the final selection (row width of idx)
+  int fallback;   // 1: redo only the query groups flagged in fb_flags, unsplit
   int64_t units;
   int t_begin, rows;  // ix_score row window
   uint64_t* cand;
   int32_t* cand_cnt;
+  uint64_t* split_min;  // per (query, split): smallest kept key if any key was dropped, else 0
+  int32_t* fb_flags;    // per query: the merge could not prove its union held the top-k
   int32_t* idx;
   float* sel;
   float* scores;
@@ -307,6 +325,30 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+// Smallest entry of buf[0, n) (n > 0), wave-reduced.
+__device__ uint64_t wave_min_key(const uint64_t* buf, int n) {
+  const int lane = threadIdx.x & 63;
+  uint64_t m = ~0ull;
+  for (int e = 2 * lane; e < n; e += 128) {
+    uint64_t x0, x1;
+    load_pair(buf, e, n, x0, x1);
+    m = x0 < m ? x0 : m;
+    if (e + 1 < n) m = x1 < m ? x1 : m;
+  }
+  return wave_min_u64(m);
+}
+
 __device__ __forceinline__ void mem_fence_wave() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 }
@@ -363,8 +405,8 @@ template <int QC, int GMAX, int DI, bool EXACT>
 __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   constexpr int HC = 16 / QC;
   // key tiles in flight per wave (the 16-block case keeps 128 VGPRs of query operands)
-  constexpr int PF = GMAX >= 16 ? 2 : 4;
-  constexpr int WSTG = 2 * 64 * PF;  // wave stage: two blocks of appends from every lane
+  constexpr int PF = prefetch_tiles(GMAX);
+  constexpr int WSTG = wave_stage_entries(GMAX);
   __shared__ uint32_t hist_all[kBlockWaves][kHistBins];
   __shared__ uint64_t stage_all[kBlockWaves][WSTG];
   const int lane = threadIdx.x & 63;
@@ -383,6 +425,13 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   const int jsel = j & 3;
   const int t = t0 + qi;
   const bool qvalid = t < p.T;
+  if (p.fallback) {
+    bool redo = false;
+#pragma unroll
+    for (int i = 0; i < QC; ++i)
+      if (t0 + i < p.T && p.fb_flags[(size_t)b * p.T + t0 + i]) redo = true;
+    if (!redo) return;
+  }
 
   const int pos0 = p.q_pos0[b];
   int kvl = p.kv_len[b];
@@ -407,7 +456,8 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     return p.cand + ((row_base + t0 + i) * p.n_splits + split) * (size_t)p.cap;
   };
 
-  int gcnt[QC];  // entries in each query's global buffer
+  int gcnt[QC];         // entries in each query's global buffer
+  uint32_t dropped = 0;  // bit i: a compaction removed entries from query i's buffer
 #pragma unroll
   for (int i = 0; i < QC; ++i) gcnt[i] = 0;
   int stotal = 0;             // entries in the wave stage
@@ -482,6 +532,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
           const SelectResult sr = select_on(buf, gcnt[i], limit);
           gcnt[i] = wave_filter(buf, gcnt[i], sr.theta, [&](int pos, uint64_t v) { buf[pos] = v; });
           mem_fence_wave();
+          dropped |= 1u << i;
           if (qi == i) th_lane = sr.theta;
         }
       }
@@ -500,27 +551,36 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     const uint64_t theta = (n > p.ksel) ? select_on(buf, n, 0).theta : 0ull;
     if (p.n_splits == 1) {
       // kept entries (ascending index) straight into the output row, then padding
-      int32_t* orow = p.idx + (row_base + ti) * (size_t)p.ksel;
-      float* srow = p.sel ? p.sel + (row_base + ti) * (size_t)p.ksel : nullptr;
+      int32_t* orow = p.idx + (row_base + ti) * (size_t)p.kout;
+      float* srow = p.sel ? p.sel + (row_base + ti) * (size_t)p.kout : nullptr;
       const int out = wave_filter(buf, n, theta, [&](int pos, uint64_t v) {
         orow[pos] = untag_index(v);
         if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
       });
-      for (int pos = out + lane; pos < p.ksel; pos += 64) {
+      for (int pos = out + lane; pos < p.kout; pos += 64) {
         orow[pos] = -1;
         if (srow) srow[pos] = -__builtin_inff();
       }
     } else {
       const int kept =
           (n > p.ksel) ? wave_filter(buf, n, theta, [&](int pos, uint64_t v) { buf[pos] = v; }) : n;
-      if (lane == 0) p.cand_cnt[(row_base + ti) * p.n_splits + split] = kept;
+      uint64_t low = 0ull;
+      if ((((dropped >> i) & 1u) || n > p.ksel) && kept > 0) {
+        mem_fence_wave();
+        low = wave_min_key(buf, kept);
+      }
+      if (lane == 0) {
+        p.cand_cnt[(row_base + ti) * p.n_splits + split] = kept;
+        p.split_min[(row_base + ti) * p.n_splits + split] = low;
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ merge of key splits
 
-constexpr int kMergeBlock = 256;
+constexpr int kMergeBlock = 512;
+constexpr int kMergeWaves = kMergeBlock / 64;
 
 __device__ __forceinline__ uint32_t block_reduce_minmax(uint32_t v, bool is_min, uint32_t* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -528,37 +588,64 @@ __device__ __forceinline__ uint32_t block_reduce_minmax(uint32_t v, bool is_min,
   if (lane == 0) red[wid] = v;
   __syncthreads();
   uint32_t r = red[0];
-  for (int i = 1; i < kMergeBlock / 64; ++i) r = is_min ? min(r, red[i]) : max(r, red[i]);
+  for (int i = 1; i < kMergeWaves; ++i) r = is_min ? min(r, red[i]) : max(r, red[i]);
   __syncthreads();
   return r;
 }
 
 // One block per query: union of the per-split lists (each ascending, splits in key
-// order), exact top-k of the union, written in ascending index order.
+// order), exact top-k of the union, written in ascending index order.  Also decides
+// whether the union provably held the true top-k (see the file header) and flags the
+// query for the unsplit pass if not.  The lists are walked as one flat range of
+// n_splits * ksel slots (slot j of split i valid when j < count_i), so every pass keeps
+// many independent loads in flight.
 __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ int cnts[64];
-  __shared__ uint32_t red[kMergeBlock / 64];
+  __shared__ uint64_t smin[64];
+  __shared__ uint32_t red[kMergeWaves];
+  __shared__ uint64_t red64[kMergeWaves];
   __shared__ int pick[3];
-  __shared__ int wave_cnt[kMergeBlock / 64];
+  __shared__ int wave_cnt[kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const size_t row = blockIdx.x;  // b * T + t
   const int NS = p.n_splits;
-  for (int i = tid; i < NS; i += kMergeBlock) cnts[i] = p.cand_cnt[row * NS + i];
+  for (int i = tid; i < NS; i += kMergeBlock) {
+    cnts[i] = p.cand_cnt[row * NS + i];
+    smin[i] = p.split_min[row * NS + i];
+  }
   __syncthreads();
   int N = 0;
-  for (int i = 0; i < NS; ++i) N += cnts[i];
+  uint64_t trunc_max = 0ull;  // largest "smallest kept key" over splits that dropped keys
+  for (int i = 0; i < NS; ++i) {
+    N += cnts[i];
+    trunc_max = smin[i] > trunc_max ? smin[i] : trunc_max;
+  }
   const uint64_t* base = p.cand + row * NS * (size_t)p.cap;
+  const int per = p.ksel;      // slots per split
+  const int P = NS * per;      // padded slot count
+  auto slot = [&](int e, uint64_t& v) -> bool {
+    if (e >= P) return false;
+    const int i = e / per, j = e - i * per;
+    if (j >= cnts[i]) return false;
+    v = base[(size_t)i * p.cap + j];
+    return true;
+  };
 
   uint64_t theta = 0ull;
-  if (N > p.ksel) {
+  if (N > p.kout) {
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int i = 0; i < NS; ++i) {
-      const uint64_t* sb = base + (size_t)i * p.cap;
-      for (int e = tid; e < cnts[i]; e += kMergeBlock) {
-        const uint32_t hi = (uint32_t)(sb[e] >> 32);
-        mn = min(mn, hi);
-        mx = max(mx, hi);
+    for (int e0 = 0; e0 < P; e0 += 4 * kMergeBlock) {
+      uint64_t v[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ok[u] = slot(e0 + u * kMergeBlock + tid, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ok[u]) {
+          mn = min(mn, (uint32_t)(v[u] >> 32));
+          mx = max(mx, (uint32_t)(v[u] >> 32));
+        }
       }
     }
     mn = block_reduce_minmax(mn, true, red);
@@ -566,7 +653,7 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
     uint64_t prefix;
     int rem;
     select_start(mn, mx, prefix, rem);
-    uint32_t needed = (uint32_t)p.ksel;
+    uint32_t needed = (uint32_t)p.kout;
     while (true) {
       const int dbits = rem < 8 ? rem : 8;
       const int shift = rem - dbits;
@@ -574,12 +661,15 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
       const int hs = shift + dbits;
       for (int i = tid; i < kHistBins; i += kMergeBlock) hist[i] = 0u;
       __syncthreads();
-      for (int i = 0; i < NS; ++i) {
-        const uint64_t* sb = base + (size_t)i * p.cap;
-        for (int e = tid; e < cnts[i]; e += kMergeBlock) {
-          const uint64_t v = sb[e];
-          if (hs >= 64 || (v >> hs) == prefix)
-            atomicAdd(&hist[(uint32_t)(v >> shift) & (uint32_t)(nbins - 1)], 1u);
+      for (int e0 = 0; e0 < P; e0 += 4 * kMergeBlock) {
+        uint64_t v[4];
+        bool ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ok[u] = slot(e0 + u * kMergeBlock + tid, v[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (ok[u] && (hs >= 64 || (v[u] >> hs) == prefix))
+            atomicAdd(&hist[(uint32_t)(v[u] >> shift) & (uint32_t)(nbins - 1)], 1u);
         }
       }
       __syncthreads();
@@ -605,37 +695,47 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
     theta = rem >= 64 ? 0ull : (prefix << rem);
   }
 
-  // ordered write of the kept entries
-  int32_t* orow = p.idx + row * (size_t)p.ksel;
-  float* srow = p.sel ? p.sel + row * (size_t)p.ksel : nullptr;
+  // ordered write of the kept entries (slot order is split order, then list order)
+  int32_t* orow = p.idx + row * (size_t)p.kout;
+  float* srow = p.sel ? p.sel + row * (size_t)p.kout : nullptr;
   const uint64_t lt = lanemask_lt();
   int out = 0;
-  for (int i = 0; i < NS; ++i) {
-    const uint64_t* sb = base + (size_t)i * p.cap;
-    const int ci = cnts[i];
-    for (int e0 = 0; e0 < ci; e0 += kMergeBlock) {
-      const int e = e0 + tid;
-      const uint64_t v = e < ci ? sb[e] : 0ull;
-      const bool keep = e < ci && v >= theta;
-      const uint64_t bal = ballot64(keep);
-      if (lane == 0) wave_cnt[wid] = popc64(bal);
-      __syncthreads();
-      int before = out;
-      for (int w = 0; w < wid; ++w) before += wave_cnt[w];
-      int total = 0;
-      for (int w = 0; w < kMergeBlock / 64; ++w) total += wave_cnt[w];
-      if (keep) {
-        const int pos = before + popc64(bal & lt);
-        orow[pos] = untag_index(v);
-        if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
-      }
-      out += total;
-      __syncthreads();
+  uint64_t kept_min = ~0ull;
+  for (int e0 = 0; e0 < P; e0 += kMergeBlock) {
+    uint64_t v = 0ull;
+    const bool keep = slot(e0 + tid, v) && v >= theta;
+    const uint64_t bal = ballot64(keep);
+    if (lane == 0) wave_cnt[wid] = popc64(bal);
+    __syncthreads();
+    int before = out, total = 0;
+    for (int w = 0; w < kMergeWaves; ++w) {
+      before += w < wid ? wave_cnt[w] : 0;
+      total += wave_cnt[w];
     }
+    if (keep) {
+      const int pos = before + popc64(bal & lt);
+      orow[pos] = untag_index(v);
+      if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
+      kept_min = v < kept_min ? v : kept_min;
+    }
+    out += total;
+    __syncthreads();
   }
-  for (int pos = out + tid; pos < p.ksel; pos += kMergeBlock) {
+  for (int pos = out + tid; pos < p.kout; pos += kMergeBlock) {
     orow[pos] = -1;
     if (srow) srow[pos] = -__builtin_inff();
+  }
+  if (p.fb_flags) {
+    // k-th key of the union = smallest kept entry (when the union has >= k entries)
+    kept_min = wave_min_u64(kept_min);
+    if (lane == 0) red64[wid] = kept_min;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t kth = red64[0];
+      for (int w = 1; w < kMergeWaves; ++w) kth = red64[w] < kth ? red64[w] : kth;
+      const bool proven = trunc_max == 0ull || (N >= p.kout && trunc_max <= kth);
+      p.fb_flags[row] = proven ? 0 : 1;
+    }
   }
 }
 
@@ -712,12 +812,32 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   const int64_t sl = ((int64_t)a.S_max + ns - 1) / ns;
   p.split_len = (int)(((sl + 15) / 16) * 16);
   const int kpad = ((k + 63) / 64) * 64;
-  p.cap = 2 * kpad + 1024;  // room for k, a full wave stage and slack
+  // With many splits each keeps about four times its even share of the top-k (at least
+  // 256); the merge proves or refutes that this was enough.
+  int ks = k;
+  if (ns > 1) {
+    const int share = ((4 * ((k + ns - 1) / ns) + 63) / 64) * 64;
+    ks = share > 256 ? share : 256;
+    if (ks > k) ks = k;
+  }
+  p.ksplit = ks;
+  const int kspad = ((ks + 63) / 64) * 64;
+  // room for k', a full wave stage and slack for a run of appends between compactions
+  const int stage = wave_stage_entries(p.gmax);
+  const int slack = 2 * stage > 1024 ? 2 * stage : 1024;
+  p.cap = 2 * kspad + slack;
+  p.fb_cap = 2 * kpad + slack;
   p.units = base_units * ns;
-  const size_t rows = (size_t)a.B * a.T * ns;
-  p.cand_bytes = rows * (size_t)p.cap * sizeof(uint64_t);
-  p.cnt_bytes = ((rows * sizeof(int32_t)) + 255) / 256 * 256;
-  p.ws_bytes = p.cand_bytes + p.cnt_bytes;
+  const size_t qrows = (size_t)a.B * a.T;
+  const size_t rows = qrows * ns;
+  size_t cand = rows * (size_t)p.cap;
+  if (ks < k && qrows * (size_t)p.fb_cap > cand) cand = qrows * (size_t)p.fb_cap;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.cand_bytes = up(cand * sizeof(uint64_t));
+  p.cnt_bytes = up(rows * sizeof(int32_t));
+  p.min_bytes = up(rows * sizeof(uint64_t));
+  p.flag_bytes = up(qrows * sizeof(int32_t));
+  p.ws_bytes = p.cand_bytes + p.cnt_bytes + p.min_bytes + p.flag_bytes;
   return p;
 }
 
@@ -743,17 +863,25 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
   x.n_splits = pl.n_splits;
   x.split_len = pl.split_len;
   x.cap = pl.cap;
-  x.ksel = k;
+  x.ksel = pl.ksplit;
+  x.kout = k;
+  x.fallback = 0;
   x.units = pl.units;
-  x.cand = reinterpret_cast<uint64_t*>(ws);
-  x.cand_cnt = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + pl.cand_bytes);
+  char* w = reinterpret_cast<char*>(ws);
+  x.cand = reinterpret_cast<uint64_t*>(w);
+  x.cand_cnt = reinterpret_cast<int32_t*>(w + pl.cand_bytes);
+  x.split_min = reinterpret_cast<uint64_t*>(w + pl.cand_bytes + pl.cnt_bytes);
+  x.fb_flags = pl.ksplit < k
+                   ? reinterpret_cast<int32_t*>(w + pl.cand_bytes + pl.cnt_bytes + pl.min_bytes)
+                   : nullptr;
   x.idx = idx;
   x.sel = sel_scores;
-  const dim3 grid((unsigned)((pl.units + kBlockWaves - 1) / kBlockWaves));
   const bool exact = pl.g == pl.gmax;
-  hipError_t err = dispatch_g(pl.gmax, [&](auto GM) -> hipError_t {
+  auto partial = [&](const IxArgs& xa) -> hipError_t {
+    const dim3 grid((unsigned)((xa.units + kBlockWaves - 1) / kBlockWaves));
+    return dispatch_g(pl.gmax, [&](auto GM) -> hipError_t {
     constexpr int G = decltype(GM)::value;
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, stream, x); };
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kBlock), 0, stream, xa); };
     if (pl.qc == 4) {
       if (a.d_I == 128)
         exact ? go(ix_topk_partial_kernel<4, G, 128, true>) : go(ix_topk_partial_kernel<4, G, 128, false>);
@@ -770,14 +898,23 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
       }
     }
     return hipGetLastError();
-  });
-  if (err != hipSuccess) return err;
-  if (pl.n_splits > 1) {
-    hipLaunchKernelGGL(ix_topk_merge_kernel, dim3((unsigned)((size_t)a.B * a.T)),
-                       dim3(kMergeBlock), 0, stream, x);
-    err = hipGetLastError();
-  }
-  return err;
+    });
+  };
+  hipError_t err = partial(x);
+  if (err != hipSuccess || pl.n_splits == 1) return err;
+  hipLaunchKernelGGL(ix_topk_merge_kernel, dim3((unsigned)((size_t)a.B * a.T)), dim3(kMergeBlock),
+                     0, stream, x);
+  err = hipGetLastError();
+  if (err != hipSuccess || !x.fb_flags) return err;
+  // unsplit exact pass over the flagged queries only (the others exit at once)
+  IxArgs f = x;
+  f.fallback = 1;
+  f.n_splits = 1;
+  f.split_len = (int)(((int64_t)a.S_max + 15) / 16 * 16);
+  f.cap = pl.fb_cap;
+  f.ksel = k;
+  f.units = (int64_t)a.B * pl.qgroups;
+  return partial(f);
 }
 
 hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, float* scores,

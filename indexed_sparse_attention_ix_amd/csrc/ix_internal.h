@@ -20,8 +20,11 @@ struct TopkPlan {
   int n_splits;   // key splits per query (1: the wave writes the final selection)
   int split_len;  // keys per split (multiple of 16)
   int cap;        // candidate-buffer entries per (query, split)
+  int ksplit;     // entries each split keeps (k when n_splits == 1)
+  int fb_cap;     // candidate-buffer entries per query of the unsplit recompute pass
   int64_t units;  // wave units = B * qgroups * n_splits
-  size_t cand_bytes, cnt_bytes, ws_bytes;
+  // workspace: candidates | per-split counts | per-split smallest kept key | query flags
+  size_t cand_bytes, cnt_bytes, min_bytes, flag_bytes, ws_bytes;
 };
 
 TopkPlan make_topk_plan(const ix_indexer_args& a, int k);

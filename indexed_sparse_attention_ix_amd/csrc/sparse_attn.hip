@@ -357,31 +357,35 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
 }
 
 // Merge of split partials: out = sum_s exp(lse_s - LSE) o_s, LSE = log sum_s exp(lse_s).
+// One thread per output element (row, KV head, head of the group, column).
 template <int D>
-__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p) {
-  const int64_t rk = blockIdx.x;  // row * H_kv + kvh
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, int64_t total) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int dcol = (int)(gid % D);
+  const int64_t rh = gid / D;
+  const int h = (int)(rh % p.grp);
+  const int64_t rk = rh / p.grp;  // row * H_kv + kvh
   const int kvh = (int)(rk % p.H_kv);
   const int64_t row = rk / p.H_kv;
-  for (int e = threadIdx.x; e < 16 * D; e += blockDim.x) {
-    const int h = e / D, dcol = e % D;
-    if (h >= p.grp) continue;
-    float M = -__builtin_inff();
-    for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, p.part_lse[((size_t)rk * p.n_splits + s) * 16 + h]);
-    float acc = 0.f, L = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int s = 0; s < p.n_splits; ++s) {
-        const size_t pr = (size_t)rk * p.n_splits + s;
-        const float ls = p.part_lse[pr * 16 + h];
-        const float f = ls == -__builtin_inff() ? 0.f : __expf(ls - M);
-        L += f;
-        acc += f * p.part_o[(pr * 16 + h) * D + dcol];
-      }
+  const float* lse_p = p.part_lse + (size_t)rk * p.n_splits * 16 + h;
+  const float* o_p = p.part_o + ((size_t)rk * p.n_splits * 16 + h) * D + dcol;
+  float M = -__builtin_inff();
+  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, lse_p[s * 16]);
+  float acc = 0.f, L = 0.f;
+  if (M != -__builtin_inff()) {
+#pragma unroll 4
+    for (int s = 0; s < p.n_splits; ++s) {
+      const float ls = lse_p[s * 16];
+      const float f = ls == -__builtin_inff() ? 0.f : __expf(ls - M);
+      L += f;
+      acc += f * o_p[(size_t)s * 16 * D];
     }
-    const int head = kvh * p.grp + h;
-    p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(L > 0.f ? acc / L : 0.f);
-    if (p.lse && dcol == 0)
-      p.lse[(size_t)row * p.H_q + head] = L > 0.f ? M + __logf(L) : -__builtin_inff();
   }
+  const int head = kvh * p.grp + h;
+  p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(L > 0.f ? acc / L : 0.f);
+  if (p.lse && dcol == 0)
+    p.lse[(size_t)row * p.H_q + head] = L > 0.f ? M + __logf(L) : -__builtin_inff();
 }
 
 }  // namespace
@@ -393,8 +397,10 @@ AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
   const int64_t base = (int64_t)B * T * H_kv;
   int ns = 1;
   if (base > 0 && base < 1024) {
-    const int64_t want = (2048 + base - 1) / base;
-    int64_t by_chunks = p.chunks / kAttnWaves;  // at least one chunk per wave
+    // one round of resident blocks (2 per CU), at least two chunks per wave so the
+    // gathers of a wave's next chunk overlap the current one
+    const int64_t want = (512 + base - 1) / base;
+    int64_t by_chunks = p.chunks / (2 * kAttnWaves);
     if (by_chunks < 1) by_chunks = 1;
     ns = (int)(want < by_chunks ? want : by_chunks);
   }
@@ -445,11 +451,12 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
     hipLaunchKernelGGL(sparse_attn_kernel<64>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || pl.n_splits == 1) return err;
-  const size_t cblocks = (size_t)B * T * H_kv;
+  const int64_t total = (int64_t)B * T * H_q * d;
+  const dim3 cgrid((unsigned)((total + 255) / 256));
   if (d == 128)
-    hipLaunchKernelGGL(sparse_attn_combine_kernel<128>, dim3((unsigned)cblocks), dim3(256), 0, stream, x);
+    hipLaunchKernelGGL(sparse_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, x, total);
   else
-    hipLaunchKernelGGL(sparse_attn_combine_kernel<64>, dim3((unsigned)cblocks), dim3(256), 0, stream, x);
+    hipLaunchKernelGGL(sparse_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, x, total);
   return hipGetLastError();
 }
 

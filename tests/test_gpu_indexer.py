@@ -97,6 +97,35 @@ def test_topk_key_splits_and_merge():
     _run_topk(wl2)
 
 
+def _run_topk_concentrated(wl, hot_keys):
+    """Scale the first `hot_keys` indexer keys by 2 so that nearly the whole top-k sits in
+    the first key split: more than that split keeps, so the merge cannot prove its union
+    and the query takes the unsplit recompute pass."""
+    say(f"[ix_topk] concentrated top-k B={wl.B} T={wl.T} S={wl.S} k={wl.k} hot={hot_keys}")
+    ind = synth.indexer_inputs(wl, device=DEV)
+    kf = synth.decode_e4m3_torch(ind["k_I"])
+    kf[:, :hot_keys] *= 2.0
+    ind["k_I"] = synth.encode_e4m3(kf)
+    idx, sel = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k,
+                       with_scores=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    h = to_host_indexer(ind)
+    for b in range(wl.B):
+        keys = O.decode_e4m3(h["k_I"][b])
+        for t in range(wl.T):
+            n = O.visible_count(h["q_pos0"][b], h["kv_len"][b], t)
+            sc = O.score_row(h["q_I"][b, t], keys[:n], h["w"][b, t], n)
+            check_index_row(idx[b, t], sc, wl.k, n, where=f"b={b} t={t}")
+            assert (idx[b, t, : wl.k] < hot_keys).sum() > wl.k // 2  # the case it is meant to be
+
+
+def test_topk_split_union_unproven_takes_recompute_pass():
+    # one query per wave (16 heads per MFMA column block) and four per wave
+    _run_topk_concentrated(_wl(B=2, T=1, S=65536, pos0=65535, k=2048, seed=19, qkv_std=1.0), 4096)
+    _run_topk_concentrated(_wl(B=1, T=4, S=65536, pos0=65532, k=2048, seed=20, qkv_std=1.0), 4096)
+
+
 def test_topk_k_at_least_visible_keeps_everything():
     wl = _wl(B=1, T=40, S=50, pos0=10, H_I=4, d_I=64, k=64, seed=17)
     idx = _run_topk(wl)
