@@ -58,6 +58,7 @@ struct IxArgs {
   int ksel;       // entries each wave unit keeps (per split when n_splits > 1)
   int kout;       // k of the final selection (row width of idx)
   int fallback;   // 1: redo only the query groups flagged in fb_flags, unsplit
+  int samp_tiles; // tiles in the threshold sample (0: no sampling)
   int64_t units;
   int t_begin, rows;  // ix_score row window
   uint64_t* cand;
@@ -483,13 +484,19 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     }
     stotal = 0;
   };
-  auto select_on = [&](uint64_t* buf, int n, int lim_kept) -> SelectResult {
+  auto select_on = [&](uint64_t* buf, int n, int kk, int lim_kept) -> SelectResult {
     uint32_t mn, mx;
     wave_hi_range(buf, n, mn, mx);
     uint64_t prefix;
     int rem;
     select_start(mn, mx, prefix, rem);
-    return wave_radix_select(buf, n, p.ksel, lim_kept, prefix, rem, hist);
+    return wave_radix_select(buf, n, kk, lim_kept, prefix, rem, hist);
+  };
+  // visible keys of query slot i inside this unit's key range
+  auto unit_keys = [&](int i) -> int {
+    if (t0 + i >= p.T) return 0;
+    const int n = min(visible_keys(pos0, kvl, t0 + i), ke) - ks;
+    return n > 0 ? n : 0;
   };
 
   // key rows of this sequence behind a bounds-checked buffer: rows >= kv_len read as 0
@@ -497,58 +504,101 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       make_rsrc(p.k + (size_t)b * p.S_max * DI, (uint32_t)kvl * DI);
   const int voff = r16 * DI + 32 * (DI == 128 ? lg : (lg & 1));
 
-  i32x8 ring[PF];
+  // Scores tiles base + 16 * step * jj (jj < count) of the unit, PF tiles in flight, and
+  // appends every visible key >= the lane's threshold; buffers that near capacity are
+  // compacted to a threshold that keeps at least k' entries.
+  auto sweep = [&](int base, int step, int count) __attribute__((always_inline)) {
+    auto tile_off = [&](int jj) { return voff + min(base + 16 * step * jj, kvl) * DI; };
+    i32x8 ring[PF];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) ring[i] = load_key_tile(krs, voff + (ks + 16 * i) * DI);
-
-  for (int s0 = ks; s0 < ke; s0 += 16 * PF) {
-    float sc[PF];
+    for (int i = 0; i < PF; ++i) ring[i] = load_key_tile(krs, tile_off(i));
+    for (int j0 = 0; j0 < count; j0 += PF) {
+      float sc[PF];
 #pragma unroll
-    for (int ui = 0; ui < PF; ++ui) {
-      sc[ui] = qo.template tile_score<EXACT>(ring[ui], p.g, jsel);
-      ring[ui] = load_key_tile(krs, voff + (s0 + 16 * (ui + PF)) * DI);
-    }
-#pragma unroll
-    for (int ui = 0; ui < PF; ++ui) {
-      const int s = s0 + 16 * ui + koff;
-      const uint64_t key = ((uint64_t)f32_to_ordered(sc[ui]) << 32) | (uint64_t)(lo_base - (uint32_t)s);
-      const bool pass = (s < lim) & (key >= th_lane);
-      const uint64_t bal = ballot64(pass);
-      if (bal) {
-        if (pass)
-          stage[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, stotal))] = key;
-        stotal += popc64(bal);
+      for (int ui = 0; ui < PF; ++ui) {
+        sc[ui] = qo.template tile_score<EXACT>(ring[ui], p.g, jsel);
+        ring[ui] = load_key_tile(krs, tile_off(j0 + ui + PF));
       }
-    }
-    // the stage must take another block; each buffer must take a full stage
-    if (stotal > WSTG - 64 * PF) {
-      flush();
 #pragma unroll
-      for (int i = 0; i < QC; ++i) {
-        if (gcnt[i] > p.cap - WSTG) {
-          mem_fence_wave();
-          uint64_t* buf = qbuf(i);
-          const SelectResult sr = select_on(buf, gcnt[i], limit);
-          gcnt[i] = wave_filter(buf, gcnt[i], sr.theta, [&](int pos, uint64_t v) { buf[pos] = v; });
-          mem_fence_wave();
-          dropped |= 1u << i;
-          if (qi == i) th_lane = sr.theta;
+      for (int ui = 0; ui < PF; ++ui) {
+        const int s = base + 16 * step * (j0 + ui) + koff;
+        const uint64_t key =
+            ((uint64_t)f32_to_ordered(sc[ui]) << 32) | (uint64_t)(lo_base - (uint32_t)s);
+        const bool pass = (j0 + ui < count) & (s < lim) & (key >= th_lane);
+        const uint64_t bal = ballot64(pass);
+        if (bal) {
+          if (pass)
+            stage[__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, stotal))] = key;
+          stotal += popc64(bal);
+        }
+      }
+      // the stage must take another block; each buffer must take a full stage
+      if (stotal > WSTG - 64 * PF) {
+        flush();
+#pragma unroll
+        for (int i = 0; i < QC; ++i) {
+          if (gcnt[i] > p.cap - WSTG) {
+            mem_fence_wave();
+            uint64_t* buf = qbuf(i);
+            const SelectResult sr = select_on(buf, gcnt[i], p.ksel, limit);
+            gcnt[i] = wave_filter(buf, gcnt[i], sr.theta, [&](int pos, uint64_t v) { buf[pos] = v; });
+            mem_fence_wave();
+            dropped |= 1u << i;
+            if (qi == i) th_lane = sr.theta;
+          }
         }
       }
     }
+    flush();
+    mem_fence_wave();
+  };
+
+  // Sampled starting threshold: score every stride-th tile first (stride >= 4) and start
+  // each query at the r-th best sampled key, r a few standard deviations above the
+  // number of the query's top-k' keys the sample is expected to hold.  That is a guess;
+  // the check after the sweep keeps the result exact.
+  const int n_tiles = ke > ks ? (ke - ks + 15) / 16 : 0;
+  const int stride = p.samp_tiles > 0 ? n_tiles / p.samp_tiles : 0;
+  if (stride >= 4) {
+    sweep(ks, stride, p.samp_tiles);
+#pragma unroll
+    for (int i = 0; i < QC; ++i) {
+      const int keff = min(p.ksel, unit_keys(i));
+      const float c = (float)keff / (float)stride;
+      const int rank = (int)ceilf(c + 4.f * sqrtf(c)) + 1;
+      uint64_t th = 0ull;
+      if (rank < gcnt[i]) {
+        th = select_on(qbuf(i), gcnt[i], rank, 0).theta;
+        dropped |= 1u << i;
+      }
+      if (qi == i) th_lane = th;
+      gcnt[i] = 0;
+    }
+    mem_fence_wave();
+  }
+  sweep(ks, 1, n_tiles);
+  // Every query must end with at least min(k', visible) entries, which proves that its
+  // k'-th key is at or above its starting threshold; otherwise sweep again from zero.
+  bool short_q = false;
+#pragma unroll
+  for (int i = 0; i < QC; ++i) short_q |= gcnt[i] < min(p.ksel, unit_keys(i));
+  if (short_q) {
+#pragma unroll
+    for (int i = 0; i < QC; ++i) gcnt[i] = 0;
+    dropped = 0;
+    th_lane = 0ull;
+    sweep(ks, 1, n_tiles);
   }
 
   // final exact selection for each query of the wave
-  flush();
-  mem_fence_wave();
 #pragma unroll
   for (int i = 0; i < QC; ++i) {
     const int ti = t0 + i;
     if (ti >= p.T) break;
     uint64_t* buf = qbuf(i);
     const int n = gcnt[i];
-    const uint64_t theta = (n > p.ksel) ? select_on(buf, n, 0).theta : 0ull;
+    const uint64_t theta = (n > p.ksel) ? select_on(buf, n, p.ksel, 0).theta : 0ull;
     if (p.n_splits == 1) {
       // kept entries (ascending index) straight into the output row, then padding
       int32_t* orow = p.idx + (row_base + ti) * (size_t)p.kout;
@@ -827,6 +877,10 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   const int slack = 2 * stage > 1024 ? 2 * stage : 1024;
   p.cap = 2 * kspad + slack;
   p.fb_cap = 2 * kpad + slack;
+  // a threshold sample must fit a candidate buffer without a compaction
+  auto samp = [&](int cap) { const int t = (cap - stage) / 16; return t < 128 ? t : 128; };
+  p.samp_tiles = samp(p.cap);
+  p.fb_samp_tiles = samp(p.fb_cap);
   p.units = base_units * ns;
   const size_t qrows = (size_t)a.B * a.T;
   const size_t rows = qrows * ns;
@@ -866,6 +920,7 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
   x.ksel = pl.ksplit;
   x.kout = k;
   x.fallback = 0;
+  x.samp_tiles = pl.samp_tiles;
   x.units = pl.units;
   char* w = reinterpret_cast<char*>(ws);
   x.cand = reinterpret_cast<uint64_t*>(w);
@@ -912,6 +967,7 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
   f.n_splits = 1;
   f.split_len = (int)(((int64_t)a.S_max + 15) / 16 * 16);
   f.cap = pl.fb_cap;
+  f.samp_tiles = pl.fb_samp_tiles;
   f.ksel = k;
   f.units = (int64_t)a.B * pl.qgroups;
   return partial(f);
