@@ -126,6 +126,46 @@ def test_topk_split_union_unproven_takes_recompute_pass():
     _run_topk_concentrated(_wl(B=1, T=4, S=65536, pos0=65532, k=2048, seed=20, qkv_std=1.0), 4096)
 
 
+def test_topk_sampled_threshold_all_rows():
+    # long enough prefixes (>= 4 tiles per sampled tile) for the starting-threshold sample;
+    # the second sequence's prefixes are too short for it
+    wl = _wl(B=2, T=37, S=8000, pos0s=(7963, 5000), H_I=64, k=256, seed=22, planted=8)
+    _run_topk(wl)
+
+
+def _sample_stride(n_keys, k, pf=2):
+    """Tile stride of the starting-threshold sample for one unsplit query group with 16
+    MFMA head blocks: the sample is at most 128 tiles and must fit a candidate buffer."""
+    kpad = (k + 63) // 64 * 64
+    stage = 2 * 64 * pf
+    cap = 2 * kpad + max(1024, 2 * stage)
+    samp = min(128, (cap - stage) // 16)
+    return ((n_keys + 15) // 16) // samp
+
+
+def test_topk_misleading_sample_takes_second_sweep():
+    """The sampled tiles get doubled keys, so the sampled threshold sits far above the
+    true k-th score: too few keys pass and the wave must sweep again from zero."""
+    wl = _wl(B=1, T=4, S=8000, pos0=7996, H_I=64, k=256, seed=23)
+    stride = _sample_stride(8000, wl.k)
+    assert stride >= 4
+    say(f"[ix_topk] misleading sample, stride {stride}")
+    ind = synth.indexer_inputs(wl, device=DEV)
+    kf = synth.decode_e4m3_torch(ind["k_I"])
+    tiles = torch.arange(wl.S, device=DEV) // 16
+    kf[:, (tiles % stride) == 0] *= 2.0
+    ind["k_I"] = synth.encode_e4m3(kf)
+    idx = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    h = to_host_indexer(ind)
+    keys = O.decode_e4m3(h["k_I"][0])
+    for t in range(wl.T):
+        n = O.visible_count(h["q_pos0"][0], h["kv_len"][0], t)
+        sc = O.score_row(h["q_I"][0, t], keys[:n], h["w"][0, t], n)
+        check_index_row(idx[0, t], sc, wl.k, n, where=f"t={t}")
+
+
 def test_topk_k_at_least_visible_keeps_everything():
     wl = _wl(B=1, T=40, S=50, pos0=10, H_I=4, d_I=64, k=64, seed=17)
     idx = _run_topk(wl)
