@@ -42,11 +42,111 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference kernel for HBM counters)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_STATS", "FETCH", "WRITE"),
+                    help="write profiles/ summaries from rocprofv3 CSVs of this workload: "
+                         "--kernel-trace --stats kernel_stats.csv, then the counter_collection.csv "
+                         "of a FETCH_SIZE run and of a WRITE_SIZE run (both with "
+                         "--copy-calibration); no GPU needed")
+    ap.add_argument("--profile-commands", nargs=3, metavar=("KT_CMD", "FETCH_CMD", "WRITE_CMD"),
+                    default=("", "", ""), help="the three commands, quoted into the summaries")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30  # the --copy-calibration copy reads and writes this many bytes
+
+
+def short_kernel_name(name):
+    n = name.replace("void ", "").replace("ix::(anonymous namespace)::", "")
+    n = n.replace("(ix::(anonymous namespace)::AttnArgs)", "").replace("(ix::(anonymous namespace)::IxArgs)", "")
+    n = n.replace(", ix::(anonymous namespace)::AttnArgs, long)", "").replace("(ix::(anonymous namespace)::AttnArgs, long)", "")
+    return n if len(n) <= 70 else n[:67] + "..."
+
+
+def summarize_profiles(args, name):
+    """Kernel-trace table, HBM traffic per dispatch (FETCH_SIZE / WRITE_SIZE in KiB, scaled
+    by what the same counters read for a copy of known size) and profiles/traffic.json."""
+    import csv
+    import collections
+    kt_path, fetch_path, write_path = args.summarize_profiles
+    kt_cmd, fetch_cmd, write_cmd = args.profile_commands
+    stats = list(csv.DictReader(open(kt_path)))
+
+    def per_dispatch(path, counter):
+        acc = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        return [(names[d], v) for d, v in acc.items()]
+
+    def scale_and_means(rows):
+        copies = [v for n, v in rows if "copy" in n.lower()]
+        if not copies:
+            raise SystemExit("no copy dispatch in the counter run: use --copy-calibration")
+        copy_kib = max(copies)
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        means = {}
+        for key in ("ix_topk_partial_kernel", "sparse_attn_kernel", "ix_topk_merge_kernel"):
+            vals = [v for n, v in rows if key in n]
+            if vals:
+                means[key] = (sum(vals) / len(vals), len(vals))
+        return copy_kib, factor, means
+
+    f_copy, f_fac, f_means = scale_and_means(per_dispatch(fetch_path, "FETCH_SIZE"))
+    w_copy, w_fac, w_means = scale_and_means(per_dispatch(write_path, "WRITE_SIZE"))
+
+    def traffic_bytes(key):
+        if key not in f_means or key not in w_means:
+            return None
+        return round(f_means[key][0] * 1024 * f_fac + w_means[key][0] * 1024 * w_fac)
+
+    tr = {"workload": name, "source_hash": kernel_source_hash(),
+          "indexer_bytes": traffic_bytes("ix_topk_partial_kernel"),
+          "attention_bytes": traffic_bytes("sparse_attn_kernel"),
+          "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(tr, f, indent=1)
+        f.write("\n")
+
+    kt_md = [f"# Kernel trace: {name}", "",
+             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):",
+             "", "```", kt_cmd, "```", "",
+             "From `kernel_stats.csv`; durations in microseconds.", "",
+             "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:12]:
+        kt_md.append(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md"), "w") as f:
+        f.write("\n".join(kt_md) + "\n")
+
+    tm = [f"# HBM traffic per dispatch: {name}", "",
+          "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the TCC instances) from two",
+          "counter runs, each scaled so that the 1 GiB device copy of `--copy-calibration` reads",
+          "as 1 GiB fetched and 1 GiB written.  These are L2-to-fabric bytes: reads served by the",
+          "Infinity Cache count as fetched.", "",
+          "```", fetch_cmd, write_cmd, "```", "",
+          f"| counter | copy kernel reads (KiB) | scale |", "|---|---|---|",
+          f"| FETCH_SIZE | {f_copy:.0f} | {f_fac:.4f} |",
+          f"| WRITE_SIZE | {w_copy:.0f} | {w_fac:.4f} |", "",
+          "| kernel | dispatches | FETCH KiB (raw) | WRITE KiB (raw) | scaled bytes per dispatch |",
+          "|---|---|---|---|---|"]
+    for key in ("ix_topk_partial_kernel", "ix_topk_merge_kernel", "sparse_attn_kernel"):
+        if key in f_means and key in w_means:
+            tm.append(f"| `{key}` | {f_means[key][1]} | {f_means[key][0]:.0f} | "
+                      f"{w_means[key][0]:.0f} | {traffic_bytes(key):.4g} |")
+    tm += ["", f"Kernel sources hash {tr['source_hash']} (bench.py reads these numbers only while the",
+           "kernels are unchanged)."]
+    with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md"), "w") as f:
+        f.write("\n".join(tm) + "\n")
+    print(json.dumps(tr))
 
 
 def kernel_source_hash():
@@ -88,12 +188,16 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
+    from indexed_sparse_attention_ix_amd.workloads import BENCH_WORKLOAD, WORKLOADS
+    if args.summarize_profiles:
+        summarize_profiles(args, args.workload or BENCH_WORKLOAD)
+        return
+
     import numpy as np
     import torch
 
     from indexed_sparse_attention_ix_amd import binding as bd
     from indexed_sparse_attention_ix_amd import synth
-    from indexed_sparse_attention_ix_amd.workloads import BENCH_WORKLOAD, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
