@@ -25,8 +25,9 @@
 // notes the smallest key it kept whenever it dropped any.  The merge takes the exact
 // top-k of the union; that is the true top-k whenever every split that dropped keys
 // kept nothing below the union's k-th key (all dropped keys then rank below it).
-// Queries that fail the check are recomputed by an unsplit pass; k' only trades
-// merge work against how often that happens, never the result.
+// Queries that fail the check are recomputed, still split, with every split keeping its
+// exact top-k (then the union always holds the top-k); k' only trades merge work
+// against how often that happens, never the result.
 #include "ix_common.h"
 #include "ix_internal.h"
 
@@ -57,7 +58,7 @@ struct IxArgs {
   int n_splits, split_len, cap;
   int ksel;       // entries each wave unit keeps (per split when n_splits > 1)
   int kout;       // k of the final selection (row width of idx)
-  int fallback;   // 1: redo only the query groups flagged in fb_flags, unsplit
+  int fallback;   // 1: redo only the queries flagged in fb_flags (every split keeps k)
   int samp_tiles; // tiles in the threshold sample (0: no sampling)
   int64_t units;
   int t_begin, rows;  // ix_score row window
@@ -647,9 +648,13 @@ __device__ __forceinline__ uint32_t block_reduce_minmax(uint32_t v, bool is_min,
 // order), exact top-k of the union, written in ascending index order.  Also decides
 // whether the union provably held the true top-k (see the file header) and flags the
 // query for the unsplit pass if not.  The lists are walked as one flat range of
-// n_splits * ksel slots (slot j of split i valid when j < count_i), so every pass keeps
-// many independent loads in flight.
+// n_splits * ksel slots (slot j of split i valid when j < count_i).  When the slots fit
+// (dynamic LDS of 8 bytes per slot), they are copied to LDS once and every pass reads
+// them there (an empty slot holds 0, which no key equals); otherwise each pass reads
+// them from memory with several loads in flight.
+constexpr int kMergeLdsSlots = 12288;
 __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
+  extern __shared__ uint64_t lds_slots[];
   __shared__ uint32_t hist[kHistBins];
   __shared__ int cnts[64];
   __shared__ uint64_t smin[64];
@@ -659,6 +664,7 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
   __shared__ int wave_cnt[kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const size_t row = blockIdx.x;  // b * T + t
+  if (p.fallback && !p.fb_flags[row]) return;  // whole block: row is per block
   const int NS = p.n_splits;
   for (int i = tid; i < NS; i += kMergeBlock) {
     cnts[i] = p.cand_cnt[row * NS + i];
@@ -674,12 +680,33 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
   const uint64_t* base = p.cand + row * NS * (size_t)p.cap;
   const int per = p.ksel;      // slots per split
   const int P = NS * per;      // padded slot count
-  auto slot = [&](int e, uint64_t& v) -> bool {
+  const bool in_lds = P <= kMergeLdsSlots;
+  auto mem_slot = [&](int e, uint64_t& v) -> bool {
     if (e >= P) return false;
     const int i = e / per, j = e - i * per;
     if (j >= cnts[i]) return false;
     v = base[(size_t)i * p.cap + j];
     return true;
+  };
+  if (in_lds) {
+    for (int e0 = 0; e0 < P; e0 += 4 * kMergeBlock) {
+      uint64_t v[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ok[u] = mem_slot(e0 + u * kMergeBlock + tid, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kMergeBlock + tid;
+        if (e < P) lds_slots[e] = ok[u] ? v[u] : 0ull;
+      }
+    }
+    __syncthreads();
+  }
+  auto slot = [&](int e, uint64_t& v) -> bool {
+    if (!in_lds) return mem_slot(e, v);
+    if (e >= P) return false;
+    v = lds_slots[e];
+    return v != 0ull;
   };
 
   uint64_t theta = 0ull;
@@ -775,7 +802,7 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
     orow[pos] = -1;
     if (srow) srow[pos] = -__builtin_inff();
   }
-  if (p.fb_flags) {
+  if (p.fb_flags && !p.fallback) {
     // k-th key of the union = smallest kept entry (when the union has >= k entries)
     kept_min = wave_min_u64(kept_min);
     if (lane == 0) red64[wid] = kept_min;
@@ -885,7 +912,7 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   const size_t qrows = (size_t)a.B * a.T;
   const size_t rows = qrows * ns;
   size_t cand = rows * (size_t)p.cap;
-  if (ks < k && qrows * (size_t)p.fb_cap > cand) cand = qrows * (size_t)p.fb_cap;
+  if (ks < k && rows * (size_t)p.fb_cap > cand) cand = rows * (size_t)p.fb_cap;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   p.cand_bytes = up(cand * sizeof(uint64_t));
   p.cnt_bytes = up(rows * sizeof(int32_t));
@@ -957,20 +984,30 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
   };
   hipError_t err = partial(x);
   if (err != hipSuccess || pl.n_splits == 1) return err;
-  hipLaunchKernelGGL(ix_topk_merge_kernel, dim3((unsigned)((size_t)a.B * a.T)), dim3(kMergeBlock),
-                     0, stream, x);
-  err = hipGetLastError();
+  auto merge = [&](const IxArgs& xa) -> hipError_t {
+    const int slots = xa.n_splits * xa.ksel;
+    const size_t lds = slots <= kMergeLdsSlots ? (size_t)slots * sizeof(uint64_t) : 0;
+    if (lds > 48 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(ix_topk_merge_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(ix_topk_merge_kernel, dim3((unsigned)((size_t)a.B * a.T)),
+                       dim3(kMergeBlock), lds, stream, xa);
+    return hipGetLastError();
+  };
+  err = merge(x);
   if (err != hipSuccess || !x.fb_flags) return err;
-  // unsplit exact pass over the flagged queries only (the others exit at once)
+  // the flagged queries again, every split keeping its exact top-k (the other waves and
+  // merge blocks exit at once)
   IxArgs f = x;
   f.fallback = 1;
-  f.n_splits = 1;
-  f.split_len = (int)(((int64_t)a.S_max + 15) / 16 * 16);
   f.cap = pl.fb_cap;
-  f.samp_tiles = pl.fb_samp_tiles;
   f.ksel = k;
-  f.units = (int64_t)a.B * pl.qgroups;
-  return partial(f);
+  f.samp_tiles = pl.fb_samp_tiles;
+  err = partial(f);
+  if (err != hipSuccess) return err;
+  return merge(f);
 }
 
 hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, float* scores,

@@ -21,7 +21,7 @@ struct TopkPlan {
   int split_len;  // keys per split (multiple of 16)
   int cap;        // candidate-buffer entries per (query, split)
   int ksplit;     // entries each split keeps (k when n_splits == 1)
-  int fb_cap;     // candidate-buffer entries per query of the unsplit recompute pass
+  int fb_cap;     // candidate-buffer entries per (query, split) of the recompute pass (k per split)
   int samp_tiles, fb_samp_tiles;  // key tiles in a starting-threshold sample
   int64_t units;  // wave units = B * qgroups * n_splits
   // workspace: candidates | per-split counts | per-split smallest kept key | query flags

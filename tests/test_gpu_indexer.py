@@ -100,7 +100,7 @@ def test_topk_key_splits_and_merge():
 def _run_topk_concentrated(wl, hot_keys):
     """Scale the first `hot_keys` indexer keys by 2 so that nearly the whole top-k sits in
     the first key split: more than that split keeps, so the merge cannot prove its union
-    and the query takes the unsplit recompute pass."""
+    and the query takes the recompute pass (every split keeping its exact top-k)."""
     say(f"[ix_topk] concentrated top-k B={wl.B} T={wl.T} S={wl.S} k={wl.k} hot={hot_keys}")
     ind = synth.indexer_inputs(wl, device=DEV)
     kf = synth.decode_e4m3_torch(ind["k_I"])
