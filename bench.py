@@ -309,6 +309,40 @@ def main():
     roofline = dict(roofline, kernel="ix_topk (indexer + selection)" if dominant_is_indexer
                     else "sparse_attn_fwd")
 
+    # ---------------------------------------------------------------- cache append (producer)
+    # The step before the indexer in a serving loop: this step's T tokens per sequence go
+    # into the group's FP8 key cache (rounded from fp32) and every layer's K/V caches.  The
+    # new rows are the ones already at those positions, so the caches stay byte-identical.
+    append = None
+    p0s = wl.pos0_list()
+    if all(p == p0s[0] for p in p0s) and p0s[0] >= 0 and p0s[0] + wl.T <= wl.S:
+        p0 = p0s[0]
+        pos_t = torch.full((wl.B,), p0, dtype=torch.int32, device=dev)
+        kn = ind["k_I"][:, p0:p0 + wl.T].view(torch.float8_e4m3fn).float().contiguous()
+        kvn = [(Lr["K"][:, p0:p0 + wl.T].contiguous(), Lr["V"][:, p0:p0 + wl.T].contiguous())
+               for Lr in layers]
+
+        def append_step():
+            for l in range(L):
+                Kn, Vn = kvn[l]
+                bd.ix_append_kv(kn.data_ptr() if l == 0 else 0, Kn.data_ptr(), Vn.data_ptr(),
+                                pos_t.data_ptr(), wl.B, wl.T, wl.S, wl.d_I, wl.H_kv, wl.d,
+                                ind["k_I"].data_ptr() if l == 0 else 0, layers[l]["K"].data_ptr(),
+                                layers[l]["V"].data_ptr(), sh)
+        append_step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            append_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_app = e0.elapsed_time(e1) / reps
+        rows = wl.B * wl.T
+        moved = rows * (wl.d_I * 5 + L * 2 * 2 * wl.H_kv * wl.d * 2)  # read + write
+        append = {"ms": round(ms_app, 4), "GB_per_s": round(moved / (ms_app / 1e3) / 1e9, 1),
+                  "tokens": rows, "launches": 2 + (L - 1)}
+        del kn, kvn
+
     # ---------------------------------------------------------------- per-layer indexing
     indexshare = None
     if not args.no_per_layer and L > 1:
@@ -397,6 +431,7 @@ def main():
             "visible_pairs": pairs,
             "selected_pairs": sel,
             "indexshare": indexshare,
+            "cache_append": append,
             "wall_s_timed_region": round(t_wall, 3),
             "kernel_source_hash": kernel_source_hash(),
         },

@@ -147,6 +147,26 @@ ix_status indexshare_group_fwd(const ix_indexer_args *a, int32_t k, int32_t n_la
                                int32_t H_q, int32_t H_kv, int32_t d, float sm_scale,
                                int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ix_append_kv -- the producer side of the caches, the step just before Stage 1 in a
+ * decode loop: appends T_new tokens per sequence at positions pos0[b] + t.  New indexer
+ * keys are rounded to FP8 e4m3 for the cache the FP8 indexer reads (the twiscan post on
+ * GLM-5.2's IndexShare: the indexer runs in FP8): clamped to +-448, then rounded to the
+ * nearest e4m3 value, ties to even (NaN stays NaN).  New K/V rows are copied as they are.
+ * k_I_new:   fp32 [B, T_new, d_I] (16-byte aligned), or NULL to skip the indexer keys.
+ * K_new, V_new: bf16 [B, T_new, H_kv, d] (16-byte aligned), each may be NULL to skip it.
+ * pos0:      device int32 [B]; a token whose position falls outside [0, S_max) is skipped.
+ * k_I_cache: [B, S_max, d_I] u8 (8-byte aligned); K_cache, V_cache: bf16 [B, S_max, H_kv, d].
+ * A cache pointer must be given exactly when its new rows are.  kv_len stays the
+ * caller's: the call writes cache rows only.
+ * Errors: IX_ERR_INVALID for negative sizes, unpaired or misaligned pointers, a NULL pos0;
+ * IX_ERR_UNSUPPORTED for d_I or d outside {64, 128} or H_kv outside 1..16.
+ */
+ix_status ix_append_kv(const float *k_I_new, const void *K_new, const void *V_new,
+                       const int32_t *pos0, int32_t B, int32_t T_new, int32_t S_max, int32_t d_I,
+                       int32_t H_kv, int32_t d, uint8_t *k_I_cache, void *K_cache, void *V_cache,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 # every symbol include/ix.h declares
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
-           "indexshare_group_fwd")
+           "indexshare_group_fwd", "ix_append_kv")
 
 
 class IxError(RuntimeError):
@@ -79,6 +79,9 @@ def load(path: str = LIB_PATH):
                                        P(c_void_p), P(c_void_p), P(c_void_p), P(c_void_p),
                                        c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                        c_size_t, c_void_p]
+    L.ix_append_kv.restype = c_int32
+    L.ix_append_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                               c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
     _lib = L
     return L
 
@@ -147,6 +150,12 @@ def indexshare_group_fwd(args: IndexerArgs, k, n_layers, q, kc, vc, out, lse, H_
     _check(load().indexshare_group_fwd(ctypes.byref(args), k, n_layers, conv[0], conv[1],
                                        conv[2], conv[3], conv[4], H_q, H_kv, d, sm_scale, idx,
                                        ws, ws_bytes, stream))
+
+
+def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I_cache,
+                 K_cache, V_cache, stream=0):
+    _check(load().ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
+                               k_I_cache, K_cache, V_cache, stream))
 
 
 # ------------------------------------------------------------------ torch tensor helpers
@@ -250,3 +259,21 @@ def indexshare_group(q_I, k_I, w, q_pos0, kv_len, k, layers, sm_scale, with_lse=
                          H_q, H_kv, d, float(sm_scale), _ptr(idx), _ptr(ws), ws.numel(),
                          _stream())
     return (idx, outs, lses) if with_lse else (idx, outs)
+
+
+def append_kv(pos0, k_I_new=None, k_I_cache=None, K_new=None, V_new=None, K_cache=None,
+              V_cache=None):
+    """Writes new tokens into the caches in place at positions pos0[b] + t: indexer keys
+    (fp32 [B,T_new,d_I]) rounded to e4m3 into k_I_cache (u8 [B,S,d_I]); K/V rows (bf16
+    [B,T_new,H_kv,d]) into K_cache/V_cache (bf16 [B,S,H_kv,d])."""
+    ref_new = k_I_new if k_I_new is not None else (K_new if K_new is not None else V_new)
+    ref_cache = k_I_cache if k_I_cache is not None else (K_cache if K_cache is not None else V_cache)
+    B, T_new = ref_new.shape[0], ref_new.shape[1]
+    S = ref_cache.shape[1]
+    d_I = k_I_new.shape[2] if k_I_new is not None else 0
+    kv = K_new if K_new is not None else V_new
+    H_kv, d = (kv.shape[2], kv.shape[3]) if kv is not None else (0, 0)
+    for t in (k_I_new, K_new, V_new, k_I_cache, K_cache, V_cache, pos0):
+        assert t is None or t.is_contiguous(), "append tensors must be contiguous"
+    ix_append_kv(_ptr(k_I_new), _ptr(K_new), _ptr(V_new), _ptr(pos0), B, T_new, S, d_I, H_kv, d,
+                 _ptr(k_I_cache), _ptr(K_cache), _ptr(V_cache), _stream())

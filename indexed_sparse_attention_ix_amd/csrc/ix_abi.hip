@@ -219,4 +219,36 @@ ix_status indexshare_group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_la
   return ok();
 }
 
+ix_status ix_append_kv(const float* k_I_new, const void* K_new, const void* V_new,
+                       const int32_t* pos0, int32_t B, int32_t T_new, int32_t S_max, int32_t d_I,
+                       int32_t H_kv, int32_t d, uint8_t* k_I_cache, void* K_cache, void* V_cache,
+                       hipStream_t stream) {
+  if (B < 0 || T_new < 0 || S_max < 0)
+    return fail(IX_ERR_INVALID, "negative size (B=%d T_new=%d S_max=%d)", B, T_new, S_max);
+  if (!k_I_new != !k_I_cache)
+    return fail(IX_ERR_INVALID, "k_I_new and k_I_cache must both be given or both be NULL");
+  if (!K_new != !K_cache || !V_new != !V_cache)
+    return fail(IX_ERR_INVALID, "each of K/V needs both its new rows and its cache, or neither");
+  if (k_I_new && d_I != 64 && d_I != 128)
+    return fail(IX_ERR_UNSUPPORTED, "d_I=%d unsupported (64 or 128)", d_I);
+  if (K_new || V_new) {
+    if (d != 64 && d != 128) return fail(IX_ERR_UNSUPPORTED, "d=%d unsupported (64 or 128)", d);
+    if (H_kv < 1 || H_kv > 16) return fail(IX_ERR_UNSUPPORTED, "H_kv=%d unsupported (1..16)", H_kv);
+  }
+  if (B == 0 || T_new == 0 || (!k_I_new && !K_new && !V_new)) return ok();
+  if (S_max < 1) return fail(IX_ERR_INVALID, "S_max=%d must be >= 1", S_max);
+  if (!pos0) return fail(IX_ERR_INVALID, "pos0 pointer is NULL");
+  if ((k_I_new && (!aligned16(k_I_new) || (reinterpret_cast<uintptr_t>(k_I_cache) & 7u))) ||
+      (K_new && (!aligned16(K_new) || !aligned16(K_cache))) ||
+      (V_new && (!aligned16(V_new) || !aligned16(V_cache))))
+    return fail(IX_ERR_INVALID,
+                "k_I_new, K/V rows and caches must be 16-byte aligned (k_I_cache 8-byte)");
+  if ((int64_t)B * T_new * 16 > (int64_t)0x7FFFFFFF * 32)
+    return fail(IX_ERR_UNSUPPORTED, "B*T_new too large for one launch");
+  hipError_t e = ix::launch_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
+                                      k_I_cache, K_cache, V_cache, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_append_kv launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -22,6 +22,11 @@ fusion or reordering:
   * IndexShare: the selection is computed once per group of 4 sparse layers and
     reused by the others (same page, "IndexShare: Amortizing the Indexer"; the
     twiscan post; "The 1M Context Mirage", "IndexShare: What Actually Works").
+  * Cache append (the step before Stage 1 in a decode loop): new indexer keys are
+    rounded to FP8 e4m3 and written into the FP8 key cache, new K/V rows into theirs.
+    The pages say only that the indexer runs in FP8 (twiscan post); the rounding read
+    here is the plain one: clamp to the largest finite e4m3 magnitude (448), then round
+    to the nearest e4m3 value, ties to the even code.
 
 Exactness.  Every e4m3 value is an integer multiple of 2^-9 below 2^9 in magnitude, so
 each product is a multiple of 2^-18 below 2^18 and any partial sum of at most 128 such
@@ -72,6 +77,42 @@ E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     """e4m3 bytes (uint8 array) -> exact fp64 values."""
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """Values -> e4m3 bytes: clamp to [-448, 448], then round to nearest, ties to even.
+
+    Constructive form of the OCP E4M3 grid: in the binade [2^E, 2^(E+1)) (E >= -6) the
+    spacing is 2^(E-3); below 2^-6 (subnormals) it is 2^-9.  Dividing by the spacing,
+    rounding half to even and multiplying back gives the rounded value exactly in fp64
+    (a value that rounds up to 2^(E+1) is the next binade's first value).  The sign is
+    kept (so -0 and values rounding to zero from below give the negative-zero code);
+    NaN gives the NaN code S.1111.111.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat = x.reshape(-1)
+    res = out.reshape(-1)
+    for i, v in enumerate(flat):
+        sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+        if math.isnan(v):
+            res[i] = sign | 0x7F
+            continue
+        a = min(abs(v), 448.0)
+        if a < 2.0 ** -6:
+            spacing = 2.0 ** -9
+        else:
+            spacing = 2.0 ** (math.floor(math.log2(a)) - 3)
+        r = float(np.rint(a / spacing)) * spacing
+        # the code of the rounded magnitude: exponent field and mantissa from r
+        if r < 2.0 ** -6:
+            code = int(round(r / 2.0 ** -9))           # subnormal: m/8 * 2^-6
+        else:
+            e = math.floor(math.log2(r))
+            m = int(round((r / 2.0 ** e - 1.0) * 8))
+            code = ((e + 7) << 3) | m
+        res[i] = sign | code
+    return out
 
 
 def decode_bf16(bits: np.ndarray) -> np.ndarray:
@@ -224,3 +265,36 @@ def indexshare_group(indexer: Dict[str, np.ndarray], layers: Sequence[Dict[str, 
     outs = [sparse_attention_rows(L["q"], L["K"], L["V"], idx, b, rows, sm_scale)
             for L in layers]
     return idx, outs
+
+
+# ----------------------------------------------------------------------------------
+# Cache append: the producer side of the FP8 key cache and the K/V caches
+# ----------------------------------------------------------------------------------
+
+
+def append_kv(k_I_cache, K_cache, V_cache, k_I_new, K_new, V_new, pos0):
+    """Copies of the caches after appending T_new tokens per sequence at pos0[b] + t.
+
+    k_I_cache [B, S, d_I] uint8, K_cache/V_cache [B, S, H_kv, d] uint16 (bf16 bits) or
+    None; k_I_new [B, T_new, d_I] float32 values, K_new/V_new [B, T_new, H_kv, d] bf16
+    bits or None.  Positions outside [0, S) are skipped.
+    """
+    kc = None if k_I_cache is None else np.array(k_I_cache, copy=True)
+    Kc = None if K_cache is None else np.array(K_cache, copy=True)
+    Vc = None if V_cache is None else np.array(V_cache, copy=True)
+    ref = kc if kc is not None else Kc
+    B, S = ref.shape[0], ref.shape[1]
+    new = k_I_new if k_I_new is not None else K_new
+    T_new = new.shape[1]
+    for b in range(B):
+        for t in range(T_new):
+            pos = int(pos0[b]) + t
+            if pos < 0 or pos >= S:
+                continue
+            if kc is not None:
+                kc[b, pos] = encode_e4m3(k_I_new[b, t])
+            if Kc is not None:
+                Kc[b, pos] = K_new[b, t]
+            if Vc is not None:
+                Vc[b, pos] = V_new[b, t]
+    return kc, Kc, Vc

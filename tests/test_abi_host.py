@@ -136,6 +136,30 @@ def test_indexshare_validation_codes():
                                   ctypes.c_float(0.1), FAKE, FAKE, need, None) == bd.IX_ERR_UNSUPPORTED
 
 
+def test_append_validation_codes():
+    ok = dict(kn=FAKE, Kn=FAKE, Vn=FAKE, pos0=FAKE, B=2, T=1, S=64, d_I=128, H_kv=1, d=128,
+              kc=FAKE, Kc=FAKE, Vc=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return status_of(bd.ix_append_kv, a["kn"], a["Kn"], a["Vn"], a["pos0"], a["B"], a["T"],
+                         a["S"], a["d_I"], a["H_kv"], a["d"], a["kc"], a["Kc"], a["Vc"])
+
+    assert call(kc=0) == bd.IX_ERR_INVALID            # new keys without a cache
+    assert call(Kn=0) == bd.IX_ERR_INVALID            # K cache without new rows
+    assert call(pos0=0) == bd.IX_ERR_INVALID
+    assert call(B=-1) == bd.IX_ERR_INVALID
+    assert call(kn=FAKE + 4) == bd.IX_ERR_INVALID     # fp32 rows must be 16-byte aligned
+    assert call(kc=FAKE + 4) == bd.IX_ERR_INVALID     # FP8 cache rows 8-byte aligned
+    assert call(d_I=96) == bd.IX_ERR_UNSUPPORTED
+    assert call(d=80) == bd.IX_ERR_UNSUPPORTED
+    assert call(H_kv=0) == bd.IX_ERR_UNSUPPORTED
+    # empty calls launch nothing
+    assert call(B=0) == bd.IX_OK and call(T=0) == bd.IX_OK
+    assert call(kn=0, kc=0, Kn=0, Kc=0, Vn=0, Vc=0) == bd.IX_OK
+
+
 def test_workspace_sizes_for_the_named_workloads():
     from indexed_sparse_attention_ix_amd.workloads import WORKLOADS
     for wl in WORKLOADS.values():

@@ -46,6 +46,85 @@ def test_e4m3_values_are_multiples_of_2pow_minus9():
     assert np.abs(v).max() < 2 ** 9
 
 
+def _nearest_e4m3_brute_force(v):
+    """Nearest finite e4m3 code to clamp(v, -448, 448) by scanning all 256 codes; ties go
+    to the code with an even mantissa (even code), zero keeps the sign of v."""
+    a = max(-448.0, min(448.0, v))
+    best, best_d = None, None
+    for c in range(256):
+        x = O.E4M3_TABLE[c]
+        if math.isnan(x) or (x == 0 and (c & 0x80) != (0x80 if math.copysign(1, v) < 0 else 0)):
+            continue
+        if x != 0 and (x < 0) != (a < 0):
+            continue
+        d = abs(Fraction(x) - Fraction(a))
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    return best
+
+
+def test_encode_e4m3_round_trips_every_code():
+    codes = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    back = O.encode_e4m3(O.E4M3_TABLE[codes])
+    assert back.tolist() == codes
+
+
+def test_encode_e4m3_matches_brute_force_nearest():
+    rng = np.random.default_rng(5)
+    vals = list(rng.standard_normal(300) * 4.0) + list(rng.standard_normal(200) * 2.0 ** -7)
+    vals += list(rng.uniform(-500, 500, 100))
+    # every midpoint between neighbouring finite magnitudes, and just either side of it
+    mags = sorted(set(abs(x) for x in O.E4M3_TABLE if not math.isnan(x)))
+    for lo, hi in zip(mags, mags[1:]):
+        m = (lo + hi) / 2
+        vals += [m, -m, np.nextafter(m, 0.0), np.nextafter(m, 1e9)]
+    vals = [float(np.float32(v)) for v in vals]
+    got = O.encode_e4m3(np.array(vals))
+    want = [_nearest_e4m3_brute_force(v) for v in vals]
+    assert got.tolist() == want
+
+
+def test_encode_e4m3_matches_torch_cast_after_clamp():
+    rng = np.random.default_rng(6)
+    x = np.concatenate([rng.standard_normal(4000) * 3, rng.standard_normal(1000) * 1e-2,
+                        rng.uniform(-1000, 1000, 1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3(x), ref)
+
+
+def test_encode_e4m3_specials():
+    enc = lambda v: int(O.encode_e4m3(np.array([v]))[0])  # noqa: E731
+    assert enc(1e30) == 0x7E and enc(-1e30) == 0xFE and enc(464.0) == 0x7E   # saturate
+    assert enc(0.0) == 0x00 and enc(-0.0) == 0x80
+    assert enc(2.0 ** -10) == 0x00 and enc(-(2.0 ** -10)) == 0x80             # tie to 0
+    assert enc(3 * 2.0 ** -10) == 0x02                                          # tie to even
+    assert enc(1.0625) == 0x38 and enc(1.1875) == 0x3A                          # ties to even
+    assert enc(float("nan")) in (0x7F, 0xFF)
+
+
+def test_append_kv_writes_only_target_rows():
+    rng = np.random.default_rng(7)
+    B, S, T_new, d_I, H, d = 3, 10, 2, 8, 2, 4
+    kc = rng.integers(0, 256, (B, S, d_I), dtype=np.uint8)
+    Kc = rng.integers(0, 1 << 16, (B, S, H, d), dtype=np.uint16)
+    Vc = rng.integers(0, 1 << 16, (B, S, H, d), dtype=np.uint16)
+    kn = rng.standard_normal((B, T_new, d_I)).astype(np.float32)
+    Kn = rng.integers(0, 1 << 16, (B, T_new, H, d), dtype=np.uint16)
+    Vn = rng.integers(0, 1 << 16, (B, T_new, H, d), dtype=np.uint16)
+    pos0 = np.array([3, 9, -1])   # sequence 1's second token and sequence 2's first fall outside
+    k2, K2, V2 = O.append_kv(kc, Kc, Vc, kn, Kn, Vn, pos0)
+    written = {(0, 3): (0, 0), (0, 4): (0, 1), (1, 9): (1, 0), (2, 0): (2, 1)}
+    for b in range(B):
+        for s in range(S):
+            if (b, s) in written:
+                bb, t = written[(b, s)]
+                assert np.array_equal(k2[b, s], O.encode_e4m3(kn[bb, t]))
+                assert np.array_equal(K2[b, s], Kn[bb, t]) and np.array_equal(V2[b, s], Vn[bb, t])
+            else:
+                assert np.array_equal(k2[b, s], kc[b, s])
+                assert np.array_equal(K2[b, s], Kc[b, s]) and np.array_equal(V2[b, s], Vc[b, s])
+
+
 def test_bf16_decode_matches_torch():
     rng = np.random.default_rng(5)
     bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint32).astype(np.uint16)
