@@ -38,7 +38,8 @@ namespace {
 constexpr int kBlockWaves = 4;
 constexpr int kBlock = kBlockWaves * kWave;
 constexpr int kHistBins = 256;
-constexpr int kHistBatch = 4;  // 16-byte loads in flight per lane in a histogram pass
+constexpr int kHistBatch = 4;    // 16-byte loads in flight per lane in a pass over a buffer
+constexpr int kFinalBatch = 16;  // the same after the sweep, when the query operands are dead
 
 // Key tiles in flight per wave: as many as the registers left beside the query operands
 // allow (GMAX head blocks of 8 VGPRs each).  The wave's LDS stage takes two blocks of
@@ -224,17 +225,18 @@ __device__ __forceinline__ void load_pair(const uint64_t* buf, int e, int n, uin
 
 // Histogram of the digit (v >> shift) & dmask over the entries of buf[0, n) whose bits
 // at and above hs equal prefix.  Lane l reads entries 2l, 2l+1 of each 128-entry chunk;
-// kHistBatch chunks are loaded before any is counted, so the L2 latency is paid once per
-// 128 * kHistBatch entries.
+// NB chunks are loaded before any is counted, so the L2 latency is paid once per
+// 128 * NB entries.
+template <int NB>
 __device__ void wave_hist(const uint64_t* buf, int n, uint64_t prefix, int hs, int shift,
                           uint32_t dmask, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
-  for (int e0 = 0; e0 < n; e0 += 128 * kHistBatch) {
-    uint64_t x[kHistBatch][2];
+  for (int e0 = 0; e0 < n; e0 += 128 * NB) {
+    uint64_t x[NB][2];
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
+    for (int u = 0; u < NB; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int e = e0 + 128 * u + 2 * lane + j;
@@ -248,6 +250,7 @@ __device__ void wave_hist(const uint64_t* buf, int n, uint64_t prefix, int hs, i
 // Radix select over buf[0, n) (distinct keys, all sharing their bits above `rem`
 // equal to `prefix`).  Keeps the k largest: returns theta with #(v >= theta) = kept,
 // where kept == k when exact, else the first kept <= limit reached while refining.
+template <int NB>
 __device__ SelectResult wave_radix_select(const uint64_t* buf, int n, int k, int limit,
                                           uint64_t prefix, int rem, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
@@ -258,7 +261,7 @@ __device__ SelectResult wave_radix_select(const uint64_t* buf, int n, int k, int
     const int nbins = 1 << dbits;
     for (int i = lane; i < kHistBins; i += 64) hist[i] = 0u;
     lds_wait();
-    wave_hist(buf, n, prefix, rem, shift, (uint32_t)(nbins - 1), hist);
+    wave_hist<NB>(buf, n, prefix, rem, shift, (uint32_t)(nbins - 1), hist);
     lds_wait();
     int d;
     uint32_t above, cnt;
@@ -292,17 +295,17 @@ __device__ __forceinline__ void select_start(uint32_t mn_hi, uint32_t mx_hi, uin
 // rank among the kept entries; returns how many were kept.  Lane l handles entries
 // 2l, 2l+1 of each 128-entry chunk; four chunks are loaded before any is written, and
 // a write never lands past the entry it came from, so in-place use is safe.
-template <typename Out>
+template <int NB, typename Out>
 __device__ int wave_filter(const uint64_t* buf, int n, uint64_t theta, Out&& out) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = lanemask_lt();
   int total = 0;
-  for (int e0 = 0; e0 < n; e0 += 128 * 4) {
-    uint64_t x[4][2];
+  for (int e0 = 0; e0 < n; e0 += 128 * NB) {
+    uint64_t x[NB][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
+    for (int u = 0; u < NB; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const int e = e0 + 128 * u + 2 * lane;
       const bool k0 = e < n && x[u][0] >= theta;
       const bool k1 = e + 1 < n && x[u][1] >= theta;
@@ -368,16 +371,17 @@ __device__ __forceinline__ i32x8 load_key_tile(__amdgpu_buffer_rsrc_t rs, int of
 // ------------------------------------------------------------------ fused indexer + top-k
 
 // Smallest and largest high word (score bits) over buf[0, n), wave-reduced.
+template <int NB>
 __device__ void wave_hi_range(const uint64_t* buf, int n, uint32_t& mn, uint32_t& mx) {
   const int lane = threadIdx.x & 63;
   mn = 0xFFFFFFFFu;
   mx = 0u;
-  for (int e0 = 0; e0 < n; e0 += 128 * kHistBatch) {
-    uint64_t x[kHistBatch][2];
+  for (int e0 = 0; e0 < n; e0 += 128 * NB) {
+    uint64_t x[NB][2];
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
+    for (int u = 0; u < NB; ++u) load_pair(buf, e0 + 128 * u + 2 * lane, n, x[u][0], x[u][1]);
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if (e0 + 128 * u + 2 * lane + j < n) {
@@ -485,14 +489,17 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     }
     stotal = 0;
   };
-  auto select_on = [&](uint64_t* buf, int n, int kk, int lim_kept) -> SelectResult {
+  auto select_on = [&](auto nb, uint64_t* buf, int n, int kk, int lim_kept) -> SelectResult {
+    constexpr int NB = decltype(nb)::value;
     uint32_t mn, mx;
-    wave_hi_range(buf, n, mn, mx);
+    wave_hi_range<NB>(buf, n, mn, mx);
     uint64_t prefix;
     int rem;
     select_start(mn, mx, prefix, rem);
-    return wave_radix_select(buf, n, kk, lim_kept, prefix, rem, hist);
+    return wave_radix_select<NB>(buf, n, kk, lim_kept, prefix, rem, hist);
   };
+  using SweepBatch = std::integral_constant<int, kHistBatch>;
+  using FinalBatch = std::integral_constant<int, kFinalBatch>;
   // visible keys of query slot i inside this unit's key range
   auto unit_keys = [&](int i) -> int {
     if (t0 + i >= p.T) return 0;
@@ -542,8 +549,9 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
           if (gcnt[i] > p.cap - WSTG) {
             mem_fence_wave();
             uint64_t* buf = qbuf(i);
-            const SelectResult sr = select_on(buf, gcnt[i], p.ksel, limit);
-            gcnt[i] = wave_filter(buf, gcnt[i], sr.theta, [&](int pos, uint64_t v) { buf[pos] = v; });
+            const SelectResult sr = select_on(SweepBatch{}, buf, gcnt[i], p.ksel, limit);
+            gcnt[i] = wave_filter<kHistBatch>(buf, gcnt[i], sr.theta,
+                                              [&](int pos, uint64_t v) { buf[pos] = v; });
             mem_fence_wave();
             dropped |= 1u << i;
             if (qi == i) th_lane = sr.theta;
@@ -555,10 +563,10 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     mem_fence_wave();
   };
 
-  // Sampled starting threshold: score every stride-th tile first (stride >= 4) and start
-  // each query at the r-th best sampled key, r a few standard deviations above the
-  // number of the query's top-k' keys the sample is expected to hold.  That is a guess;
-  // the check after the sweep keeps the result exact.
+  // Sampled starting threshold: score every stride-th tile first (stride >= 4, at most 64
+  // tiles) and start each query at the r-th best sampled key, r a few standard deviations
+  // above the number of the query's top-k' keys the sample is expected to hold.  That is
+  // a guess; the check after the sweep keeps the result exact.
   const int n_tiles = ke > ks ? (ke - ks + 15) / 16 : 0;
   const int stride = p.samp_tiles > 0 ? n_tiles / p.samp_tiles : 0;
   if (stride >= 4) {
@@ -570,7 +578,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       const int rank = (int)ceilf(c + 4.f * sqrtf(c)) + 1;
       uint64_t th = 0ull;
       if (rank < gcnt[i]) {
-        th = select_on(qbuf(i), gcnt[i], rank, 0).theta;
+        th = select_on(SweepBatch{}, qbuf(i), gcnt[i], rank, 0).theta;
         dropped |= 1u << i;
       }
       if (qi == i) th_lane = th;
@@ -599,12 +607,12 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     if (ti >= p.T) break;
     uint64_t* buf = qbuf(i);
     const int n = gcnt[i];
-    const uint64_t theta = (n > p.ksel) ? select_on(buf, n, p.ksel, 0).theta : 0ull;
+    const uint64_t theta = (n > p.ksel) ? select_on(FinalBatch{}, buf, n, p.ksel, 0).theta : 0ull;
     if (p.n_splits == 1) {
       // kept entries (ascending index) straight into the output row, then padding
       int32_t* orow = p.idx + (row_base + ti) * (size_t)p.kout;
       float* srow = p.sel ? p.sel + (row_base + ti) * (size_t)p.kout : nullptr;
-      const int out = wave_filter(buf, n, theta, [&](int pos, uint64_t v) {
+      const int out = wave_filter<kFinalBatch>(buf, n, theta, [&](int pos, uint64_t v) {
         orow[pos] = untag_index(v);
         if (srow) srow[pos] = ordered_to_f32((uint32_t)(v >> 32));
       });
@@ -614,7 +622,9 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       }
     } else {
       const int kept =
-          (n > p.ksel) ? wave_filter(buf, n, theta, [&](int pos, uint64_t v) { buf[pos] = v; }) : n;
+          (n > p.ksel) ? wave_filter<kFinalBatch>(buf, n, theta,
+                                                  [&](int pos, uint64_t v) { buf[pos] = v; })
+                       : n;
       uint64_t low = 0ull;
       if ((((dropped >> i) & 1u) || n > p.ksel) && kept > 0) {
         mem_fence_wave();
@@ -905,7 +915,7 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   p.cap = 2 * kspad + slack;
   p.fb_cap = 2 * kpad + slack;
   // a threshold sample must fit a candidate buffer without a compaction
-  auto samp = [&](int cap) { const int t = (cap - stage) / 16; return t < 128 ? t : 128; };
+  auto samp = [&](int cap) { const int t = (cap - stage) / 16; return t < 64 ? t : 64; };
   p.samp_tiles = samp(p.cap);
   p.fb_samp_tiles = samp(p.fb_cap);
   p.units = base_units * ns;

@@ -135,11 +135,11 @@ def test_topk_sampled_threshold_all_rows():
 
 def _sample_stride(n_keys, k, pf=2):
     """Tile stride of the starting-threshold sample for one unsplit query group with 16
-    MFMA head blocks: the sample is at most 128 tiles and must fit a candidate buffer."""
+    MFMA head blocks: the sample is at most 64 tiles and must fit a candidate buffer."""
     kpad = (k + 63) // 64 * 64
     stage = 2 * 64 * pf
     cap = 2 * kpad + max(1024, 2 * stage)
-    samp = min(128, (cap - stage) // 16)
+    samp = min(64, (cap - stage) // 16)
     return ((n_keys + 15) // 16) // samp
 
 
