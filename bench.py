@@ -343,6 +343,47 @@ def main():
                   "tokens": rows, "launches": 2 + (L - 1)}
         del kn, kvn
 
+    # ---------------------------------------------------------------- IndexPool
+    # The same selection budget over block keys (4 consecutive indexer keys pooled into
+    # one): pooling pre-pass + block top-k of k/4 blocks expanded to k token positions.
+    indexpool = None
+    if wl.k % 4 == 0:
+        pool, kb = 4, wl.k // 4
+        kpool = torch.empty((wl.B, (wl.S + pool - 1) // pool, wl.d_I), dtype=torch.uint8, device=dev)
+        ap = bd.IndexerArgs(ind["q_I"].data_ptr(), kpool.data_ptr(), ind["w"].data_ptr(),
+                            ind["q_pos0"].data_ptr(), ind["kv_len"].data_ptr(), wl.B, wl.T, wl.S,
+                            wl.H_I, wl.d_I)
+        pw = bd.ix_topk_pooled_workspace_bytes(ap, pool, kb)
+        pws = torch.empty(max(pw, 256), dtype=torch.uint8, device=dev)
+        idx_p = torch.empty_like(idx)
+
+        def pool_pass():
+            bd.ix_pool_keys(ind["k_I"].data_ptr(), ind["kv_len"].data_ptr(), wl.B, wl.S, wl.d_I,
+                            pool, kpool.data_ptr(), sh)
+
+        def pooled_topk():
+            bd.ix_topk_pooled(ap, pool, kb, idx_p.data_ptr(), pws.data_ptr(), pw, sh)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+        ms_pp = timed(pool_pass)
+        ms_pt = timed(pooled_topk)
+        # a decode loop keeps the block keys up to date as blocks fill, so only prefill
+        # pays the pooling pass with its selection
+        sel = ms_pt if wl.T == 1 else ms_pp + ms_pt
+        indexpool = {"pool": pool, "k_blocks": kb, "pool_keys_ms": round(ms_pp, 4),
+                     "topk_pooled_ms": round(ms_pt, 4), "token_selection_ms": round(t_topk, 4),
+                     "selection_speedup": round(t_topk / sel, 3),
+                     "group_step_ms_estimate": round(sel + L * t_attn, 3)}
+        del kpool, pws, idx_p
+
     # ---------------------------------------------------------------- per-layer indexing
     indexshare = None
     if not args.no_per_layer and L > 1:
@@ -432,6 +473,7 @@ def main():
             "selected_pairs": sel,
             "indexshare": indexshare,
             "cache_append": append,
+            "indexpool": indexpool,
             "wall_s_timed_region": round(t_wall, 3),
             "kernel_source_hash": kernel_source_hash(),
         },

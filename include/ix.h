@@ -148,6 +148,40 @@ ix_status indexshare_group_fwd(const ix_indexer_args *a, int32_t k, int32_t n_la
                                int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * IndexPool: pooling four indexer keys into one to cut long-context indexing cost
+ * (GLM-5.3-Flash as recorded on worldresearchstate.com, "What changed").  The page says
+ * no more; the reading implemented: a block key is the mean of `pool` consecutive
+ * tokens' FP8 indexer keys rounded to e4m3 (tokens at or past kv_len count as zero), the
+ * fused indexer + top-k scores blocks exactly as it scores keys, a query at position p
+ * sees block j once pool*j <= p, and each kept block expands to its token positions.
+ *
+ * ix_pool_keys -- k_pooled [B, ceil(S_max/pool), d_I] e4m3 from k_I [B, S_max, d_I]
+ * (both 8-byte aligned); kv_len: nullable device int32 [B] (NULL: S_max).
+ * pool in {1, 2, 4, 8, 16} (a power of two keeps the mean exact before rounding).
+ */
+ix_status ix_pool_keys(const uint8_t *k_I, const int32_t *kv_len, int32_t B, int32_t S_max,
+                       int32_t d_I, int32_t pool, uint8_t *k_pooled, hipStream_t stream);
+
+/* Workspace bytes ix_topk_pooled needs (0 on invalid arguments). */
+size_t ix_topk_pooled_workspace_bytes(const ix_indexer_args *a, int32_t pool, int32_t k_blocks);
+
+/*
+ * ix_topk_pooled -- Stage 1 + Stage 2 over block keys: per query the min(k_blocks,
+ * visible blocks) best blocks (ties to the lower block), each expanded to its `pool`
+ * token positions.
+ * a:   as for ix_topk except that a->k points to the block keys [B, ceil(S_max/pool), d_I]
+ *      (from ix_pool_keys); a->S_max, a->q_pos0 and a->kv_len count token positions.
+ * idx: int32 [B, T, k_blocks * pool]: token positions in ascending order, then -1 (a kept
+ *      block's tokens the query does not see are -1; only the last kept block can have
+ *      them).
+ * ws:  at least ix_topk_pooled_workspace_bytes(a, pool, k_blocks) bytes.
+ * Errors as ix_topk; IX_ERR_UNSUPPORTED for pool outside {1, 2, 4, 8, 16} or k_blocks
+ * outside 1..2048.
+ */
+ix_status ix_topk_pooled(const ix_indexer_args *a, int32_t pool, int32_t k_blocks, int32_t *idx,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ix_append_kv -- the producer side of the caches, the step just before Stage 1 in a
  * decode loop: appends T_new tokens per sequence at positions pos0[b] + t.  New indexer
  * keys are rounded to FP8 e4m3 for the cache the FP8 indexer reads (the twiscan post on

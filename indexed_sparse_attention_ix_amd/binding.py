@@ -27,7 +27,8 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 # every symbol include/ix.h declares
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
-           "indexshare_group_fwd", "ix_append_kv")
+           "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
+           "ix_topk_pooled")
 
 
 class IxError(RuntimeError):
@@ -79,6 +80,14 @@ def load(path: str = LIB_PATH):
                                        P(c_void_p), P(c_void_p), P(c_void_p), P(c_void_p),
                                        c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                        c_size_t, c_void_p]
+    L.ix_pool_keys.restype = c_int32
+    L.ix_pool_keys.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                               c_void_p]
+    L.ix_topk_pooled_workspace_bytes.restype = c_size_t
+    L.ix_topk_pooled_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32]
+    L.ix_topk_pooled.restype = c_int32
+    L.ix_topk_pooled.argtypes = [P(IndexerArgs), c_int32, c_int32, c_void_p, c_void_p, c_size_t,
+                                 c_void_p]
     L.ix_append_kv.restype = c_int32
     L.ix_append_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
@@ -156,6 +165,18 @@ def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I
                  K_cache, V_cache, stream=0):
     _check(load().ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
                                k_I_cache, K_cache, V_cache, stream))
+
+
+def ix_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream=0):
+    _check(load().ix_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream))
+
+
+def ix_topk_pooled_workspace_bytes(args: IndexerArgs, pool: int, k_blocks: int) -> int:
+    return load().ix_topk_pooled_workspace_bytes(ctypes.byref(args), pool, k_blocks)
+
+
+def ix_topk_pooled(args: IndexerArgs, pool, k_blocks, idx, ws, ws_bytes, stream=0):
+    _check(load().ix_topk_pooled(ctypes.byref(args), pool, k_blocks, idx, ws, ws_bytes, stream))
 
 
 # ------------------------------------------------------------------ torch tensor helpers
@@ -277,3 +298,28 @@ def append_kv(pos0, k_I_new=None, k_I_cache=None, K_new=None, V_new=None, K_cach
         assert t is None or t.is_contiguous(), "append tensors must be contiguous"
     ix_append_kv(_ptr(k_I_new), _ptr(K_new), _ptr(V_new), _ptr(pos0), B, T_new, S, d_I, H_kv, d,
                  _ptr(k_I_cache), _ptr(K_cache), _ptr(V_cache), _stream())
+
+
+def pool_keys(k_I, kv_len, pool=4):
+    """Block keys u8 [B, ceil(S/pool), d_I] from FP8 indexer keys u8 [B, S, d_I]."""
+    torch = _torch()
+    B, S, D = k_I.shape
+    out = torch.empty((B, (S + pool - 1) // pool, D), dtype=torch.uint8, device=k_I.device)
+    ix_pool_keys(_ptr(k_I), _ptr(kv_len), B, S, D, pool, _ptr(out), _stream())
+    return out
+
+
+def topk_pooled(q_I, k_pooled, w, q_pos0, kv_len, S_max, pool, k_blocks, ws=None):
+    """idx int32 [B, T, k_blocks * pool]: token positions of the best k_blocks blocks."""
+    torch = _torch()
+    B, T, H, D = q_I.shape
+    for t in (q_I, k_pooled, w, q_pos0, kv_len):
+        assert t.is_contiguous(), "indexer tensors must be contiguous"
+    a = IndexerArgs(_ptr(q_I), _ptr(k_pooled), _ptr(w), _ptr(q_pos0), _ptr(kv_len), B, T, S_max,
+                    H, D)
+    idx = torch.empty((B, T, k_blocks * pool), dtype=torch.int32, device=q_I.device)
+    nb = ix_topk_pooled_workspace_bytes(a, pool, k_blocks)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, q_I.device)
+    ix_topk_pooled(a, pool, k_blocks, _ptr(idx), _ptr(ws), ws.numel(), _stream())
+    return idx

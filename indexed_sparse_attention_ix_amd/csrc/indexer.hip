@@ -61,6 +61,7 @@ struct IxArgs {
   int kout;       // k of the final selection (row width of idx)
   int fallback;   // 1: redo only the queries flagged in fb_flags (every split keeps k)
   int samp_tiles; // tiles in the threshold sample (0: no sampling)
+  int pool;       // positions per key row (1: token keys; IndexPool: pooled block keys)
   int64_t units;
   int t_begin, rows;  // ix_score row window
   uint64_t* cand;
@@ -83,6 +84,16 @@ __device__ __forceinline__ i32x8 load_row_slice(const uint8_t* row, int lg) {
     v = (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
   return v;
+}
+
+// Keys (or pooled key blocks) visible to query t: unit j covers positions
+// [pool*j, pool*j + pool) and is visible once its first position is (pool*j <= pos0 + t);
+// kvl_units caps the count.  pool = 1 is the plain causal prefix.
+__device__ __forceinline__ int visible_units(int pos0, int kvl_units, int t, int pool) {
+  const long p = (long)pos0 + t;
+  if (p < 0) return 0;
+  const long v = p / pool + 1;
+  return (int)(v > kvl_units ? kvl_units : v);
 }
 
 __device__ __forceinline__ int visible_keys(int pos0, int kvl, int t) {
@@ -440,11 +451,14 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   }
 
   const int pos0 = p.q_pos0[b];
+  // key rows here are units of `pool` positions (1: tokens); kv_len counts positions
+  const int pool = p.pool;
   int kvl = p.kv_len[b];
-  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
-  const int n_q = qvalid ? visible_keys(pos0, kvl, t) : 0;
+  kvl = kvl < 0 ? 0 : (kvl + pool - 1) / pool;
+  kvl = kvl > p.S_max ? p.S_max : kvl;
+  const int n_q = qvalid ? visible_units(pos0, kvl, t, pool) : 0;
   const int t_last = (t0 + QC < p.T ? t0 + QC : p.T) - 1;
-  const int n_max = visible_keys(pos0, kvl, t_last);
+  const int n_max = visible_units(pos0, kvl, t_last, pool);
   const int ks = split * p.split_len;
   const int ke = min(ks + p.split_len, n_max);
 
@@ -503,7 +517,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   // visible keys of query slot i inside this unit's key range
   auto unit_keys = [&](int i) -> int {
     if (t0 + i >= p.T) return 0;
-    const int n = min(visible_keys(pos0, kvl, t0 + i), ke) - ks;
+    const int n = min(visible_units(pos0, kvl, t0 + i, pool), ke) - ks;
     return n > 0 ? n : 0;
   };
 
@@ -947,7 +961,7 @@ static IxArgs make_args(const ix_indexer_args& a) {
 }
 
 hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, int32_t* idx,
-                          float* sel_scores, void* ws, hipStream_t stream) {
+                          float* sel_scores, void* ws, hipStream_t stream, int pool) {
   IxArgs x = make_args(a);
   x.g = pl.g;
   x.qgroups = pl.qgroups;
@@ -958,6 +972,7 @@ hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, i
   x.kout = k;
   x.fallback = 0;
   x.samp_tiles = pl.samp_tiles;
+  x.pool = pool;
   x.units = pl.units;
   char* w = reinterpret_cast<char*>(ws);
   x.cand = reinterpret_cast<uint64_t*>(w);

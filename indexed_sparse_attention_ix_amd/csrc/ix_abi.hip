@@ -92,6 +92,19 @@ ix_status check_attn_shape(int32_t B, int32_t T, int32_t S_max, int32_t H_q, int
   return IX_OK;
 }
 
+bool pool_ok(int32_t pool) { return pool == 1 || pool == 2 || pool == 4 || pool == 8 || pool == 16; }
+
+// The indexer arguments as the top-k sees them under IndexPool: one key row per block.
+ix_indexer_args pooled_args(const ix_indexer_args& a, int32_t pool) {
+  ix_indexer_args u = a;
+  u.S_max = a.S_max < 0 ? a.S_max : (a.S_max + pool - 1) / pool;
+  return u;
+}
+
+size_t pooled_blocks_bytes(const ix_indexer_args& u, int32_t k_blocks) {
+  return ((size_t)u.B * u.T * k_blocks * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 ix_status check_attn_ptrs(const void* q, const void* kc, const void* vc, const int32_t* idx,
                           const void* out) {
   if (!q || !kc || !vc || !idx || !out) return fail(IX_ERR_INVALID, "NULL attention tensor pointer");
@@ -248,6 +261,53 @@ ix_status ix_append_kv(const float* k_I_new, const void* K_new, const void* V_ne
   hipError_t e = ix::launch_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
                                       k_I_cache, K_cache, V_cache, stream);
   if (e != hipSuccess) return hip_fail(e, "ix_append_kv launch");
+  return ok();
+}
+
+ix_status ix_pool_keys(const uint8_t* k_I, const int32_t* kv_len, int32_t B, int32_t S_max,
+                       int32_t d_I, int32_t pool, uint8_t* k_pooled, hipStream_t stream) {
+  if (B < 0 || S_max < 0) return fail(IX_ERR_INVALID, "negative size (B=%d S_max=%d)", B, S_max);
+  if (d_I != 64 && d_I != 128) return fail(IX_ERR_UNSUPPORTED, "d_I=%d unsupported (64 or 128)", d_I);
+  if (!pool_ok(pool)) return fail(IX_ERR_UNSUPPORTED, "pool=%d unsupported (1, 2, 4, 8 or 16)", pool);
+  if (B == 0 || S_max == 0) return ok();
+  if (!k_I || !k_pooled) return fail(IX_ERR_INVALID, "NULL key pointer");
+  if ((reinterpret_cast<uintptr_t>(k_I) | reinterpret_cast<uintptr_t>(k_pooled)) & 7u)
+    return fail(IX_ERR_INVALID, "key arrays must be 8-byte aligned");
+  hipError_t e = ix::launch_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_pool_keys launch");
+  return ok();
+}
+
+size_t ix_topk_pooled_workspace_bytes(const ix_indexer_args* a, int32_t pool, int32_t k_blocks) {
+  bool empty = false;
+  if (!a || !pool_ok(pool) || check_k(k_blocks) != IX_OK) return 0;
+  const ix_indexer_args u = pooled_args(*a, pool);
+  if (check_indexer(&u, &empty) != IX_OK || empty) return 0;
+  const ix::TopkPlan plan = ix::make_topk_plan(u, k_blocks);
+  return plan.ws_bytes + pooled_blocks_bytes(u, k_blocks);
+}
+
+ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_blocks, int32_t* idx,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!a) return fail(IX_ERR_INVALID, "indexer args pointer is NULL");
+  if (!pool_ok(pool)) return fail(IX_ERR_UNSUPPORTED, "pool=%d unsupported (1, 2, 4, 8 or 16)", pool);
+  ix_status st = check_k(k_blocks);
+  if (st != IX_OK) return st;
+  bool empty = false;
+  const ix_indexer_args u = pooled_args(*a, pool);
+  if ((st = check_indexer(&u, &empty)) != IX_OK) return st;
+  if (empty) return ok();
+  if (!idx) return fail(IX_ERR_INVALID, "idx pointer is NULL");
+  const ix::TopkPlan plan = ix::make_topk_plan(u, k_blocks);
+  const size_t need = plan.ws_bytes + pooled_blocks_bytes(u, k_blocks);
+  if (!ws || ws_bytes < need)
+    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
+  int32_t* blocks = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + plan.ws_bytes);
+  hipError_t e = ix::launch_ix_topk(u, k_blocks, plan, blocks, nullptr, ws, stream, pool);
+  if (e != hipSuccess) return hip_fail(e, "ix_topk_pooled launch");
+  e = ix::launch_expand_blocks(blocks, a->q_pos0, a->kv_len, a->B, a->T, a->S_max, k_blocks, pool,
+                               idx, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_topk_pooled expansion launch");
   return ok();
 }
 

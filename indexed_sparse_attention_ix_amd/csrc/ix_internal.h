@@ -42,8 +42,15 @@ AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k);
 
 hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, float* scores,
                            hipStream_t stream);
+// a.k holds one key row per unit of `pool` positions (1: tokens) and a.S_max counts
+// units; a.q_pos0 and a.kv_len count positions.
 hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& p, int32_t* idx,
-                          float* sel_scores, void* ws, hipStream_t stream);
+                          float* sel_scores, void* ws, hipStream_t stream, int pool = 1);
+hipError_t launch_pool_keys(const uint8_t* k_I, const int32_t* kv_len, int B, int S_max, int d_I,
+                            int pool, uint8_t* k_pooled, hipStream_t stream);
+hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* q_pos0,
+                                const int32_t* kv_len, int B, int T, int S_max, int k_blocks,
+                                int pool, int32_t* idx, hipStream_t stream);
 hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* idx,
                               const int32_t* kv_len, int B, int T, int S_max, int H_q, int H_kv,
                               int d, int k, float sm_scale, void* out, float* lse,

@@ -22,6 +22,15 @@ fusion or reordering:
   * IndexShare: the selection is computed once per group of 4 sparse layers and
     reused by the others (same page, "IndexShare: Amortizing the Indexer"; the
     twiscan post; "The 1M Context Mirage", "IndexShare: What Actually Works").
+  * IndexPool (GLM-5.3-Flash, worldresearchstate.com record, "What changed": four
+    indexer keys pooled into one to cut long-context indexing cost).  The page does not
+    say how keys are pooled or how a pooled selection maps back to tokens; the reading
+    here is the plainest one: a block key is the mean of 4 consecutive tokens' FP8
+    indexer keys, rounded to e4m3 (a block cut short by kv_len counts its missing tokens
+    as zero, so every block divides by 4 and the mean is exact before rounding); the indexer
+    scores blocks exactly as it scores keys; a query at position p sees block j iff
+    4j <= p; the best k/4 blocks are kept (ties to the lower block) and each expands to
+    its tokens that the query sees, in ascending order, padded with -1.
   * Cache append (the step before Stage 1 in a decode loop): new indexer keys are
     rounded to FP8 e4m3 and written into the FP8 key cache, new K/V rows into theirs.
     The pages say only that the indexer runs in FP8 (twiscan post); the rounding read
@@ -298,3 +307,44 @@ def append_kv(k_I_cache, K_cache, V_cache, k_I_new, K_new, V_new, pos0):
             if Vc is not None:
                 Vc[b, pos] = V_new[b, t]
     return kc, Kc, Vc
+
+
+# ----------------------------------------------------------------------------------
+# IndexPool: scoring blocks of pooled indexer keys
+# ----------------------------------------------------------------------------------
+
+
+def pool_keys(k_I_seq: np.ndarray, kv_len: int, pool: int) -> np.ndarray:
+    """[S, d_I] e4m3 bytes of one sequence -> [ceil(S/pool), d_I] e4m3 bytes: the sum of
+    each block's keys below kv_len divided by pool (the mean of a full block; missing
+    tokens count as zero), rounded to e4m3."""
+    S, d_I = k_I_seq.shape
+    nb = (S + pool - 1) // pool
+    vals = decode_e4m3(k_I_seq)
+    out = np.zeros((nb, d_I), dtype=np.uint8)
+    for j in range(nb):
+        lo, hi = pool * j, min(pool * j + pool, S, max(kv_len, 0))
+        if hi > lo:
+            out[j] = encode_e4m3(vals[lo:hi].sum(axis=0) / pool)
+    return out
+
+
+def visible_blocks(pos0: int, kv_len: int, t: int, pool: int) -> int:
+    """Blocks visible to query t: block j iff pool*j <= pos0 + t and pool*j < kv_len."""
+    p = pos0 + t
+    if p < 0:
+        return 0
+    return min(p // pool + 1, (max(kv_len, 0) + pool - 1) // pool)
+
+
+def pooled_topk_row(qI_row, pooled_keys_f64, w_row, pos0, kv_len, t, pool, k_blocks):
+    """(block scores over the visible blocks, kept blocks, expanded token row of length
+    k_blocks * pool)."""
+    nb = visible_blocks(pos0, kv_len, t, pool)
+    sc = score_row(qI_row, pooled_keys_f64[:nb], w_row, nb)
+    blocks = select_topk(sc, k_blocks)
+    n_t = visible_count(pos0, kv_len, t)
+    toks = [pool * j + r for j in blocks if j >= 0 for r in range(pool) if pool * j + r < n_t]
+    row = np.full(k_blocks * pool, -1, dtype=np.int64)
+    row[:len(toks)] = toks
+    return sc, blocks, row

@@ -448,3 +448,72 @@ def test_indexshare_selection_once_per_group(monkeypatch):
     for L, (out, lse) in zip(layers, outs):
         o2, l2 = O.sparse_attention_rows(L["q"], L["K"], L["V"], idx, 0, rows, 0.25)
         assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+
+
+# ---------------------------------------------------------------- IndexPool (reading)
+
+
+def test_pool_keys_against_exact_mean():
+    rng = np.random.default_rng(41)
+    S, d_I, pool = 23, 16, 4
+    codes = rng.integers(0, 256, (S, d_I)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38          # no NaN codes in a cache
+    for kv_len in (23, 22, 9, 0):
+        got = O.pool_keys(codes, kv_len, pool)
+        assert got.shape == ((S + pool - 1) // pool, d_I)
+        for j in range(got.shape[0]):
+            rows = [s for s in range(pool * j, pool * j + pool) if s < min(S, kv_len)]
+            for c in range(d_I):
+                exact = sum((Fraction(float(O.E4M3_TABLE[codes[s, c]])) for s in rows),
+                            Fraction(0)) / pool
+                want = _nearest_e4m3_brute_force(float(exact)) if rows else 0
+                assert got[j, c] == want, (kv_len, j, c)
+
+
+def test_pooled_selection_with_pool_1_is_the_token_selection():
+    rng = np.random.default_rng(42)
+    S, H, d_I, k = 300, 4, 64, 20
+    q = rng.integers(0, 256, (H, d_I)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0
+    keys = rng.integers(0, 256, (S, d_I)).astype(np.uint8)
+    keys[(keys & 0x7F) == 0x7F] = 0
+    w = rng.uniform(0, 1, H)
+    pooled = O.decode_e4m3(O.pool_keys(keys, S, 1))
+    for t in (0, 5, 150, 299):
+        n = O.visible_count(0, S, t)
+        _, blocks, row = O.pooled_topk_row(q, pooled, w, 0, S, t, 1, k)
+        want = O.select_topk(O.score_row(q, O.decode_e4m3(keys)[:n], w, n), k)
+        assert np.array_equal(blocks, want) and np.array_equal(row, want)
+
+
+def test_visible_blocks_brute_force():
+    for pool in (1, 2, 4, 8):
+        for pos0 in (-5, 0, 3, 17):
+            for kv_len in (0, 1, 7, 30):
+                for t in range(12):
+                    p = pos0 + t
+                    want = sum(1 for j in range(64) if pool * j <= p and pool * j < kv_len)
+                    assert O.visible_blocks(pos0, kv_len, t, pool) == want
+
+
+def test_pooled_selection_known_blocks_and_expansion():
+    """Every block holds 4 copies of one key, so each block key is that key exactly and
+    the block scores are known; a query whose position cuts the last block sees only its
+    first tokens."""
+    pool, nb, d_I = 4, 12, 64
+    vals = [1.0 + 0.125 * i for i in range(8)] + [2.0, 2.25, 2.5, 2.75]   # e4m3 values
+    order = [7, 2, 11, 0, 5, 9, 1, 3, 10, 4, 6, 8]            # block j gets vals[order[j]]
+    keys = np.zeros((nb * pool, d_I), dtype=np.uint8)
+    for j in range(nb):
+        keys[pool * j: pool * j + pool, :] = int(np.nonzero(O.E4M3_TABLE == vals[order[j]])[0][0])
+    pooled = O.decode_e4m3(O.pool_keys(keys, nb * pool, pool))
+    assert np.all(pooled[:, 0] == np.array([vals[o] for o in order]))
+    q = np.full((1, d_I), int(np.nonzero(O.E4M3_TABLE == 1.0)[0][0]), dtype=np.uint8)
+    w = np.ones(1)
+    pos0, t, kb = 42, 0, 3             # sees blocks 0..10, tokens 0..42 (block 10 cut at 42)
+    sc, blocks, row = O.pooled_topk_row(q, pooled, w, pos0, nb * pool, t, pool, kb)
+    assert len(sc) == 11
+    best = sorted(range(11), key=lambda j: -order[j])[:kb]  # blocks 2, 10, 9
+    assert blocks.tolist() == sorted(best)
+    toks = [pool * j + r for j in sorted(best) for r in range(pool) if pool * j + r <= 42]
+    assert row.tolist() == toks + [-1] * (kb * pool - len(toks))
