@@ -900,7 +900,10 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   p.qgroups = (a.T + p.qc - 1) / p.qc;
   const int64_t base_units = (int64_t)a.B * p.qgroups;
   int ns = 1;
-  const int target = 2048;  // resident waves on 256 CUs at 2 waves per SIMD
+  // waves to aim for: two per SIMD for the MFMA-bound 4-query kernel; the 1-query (decode)
+  // kernel streams keys and does better with half as many, twice as long splits (its
+  // threshold sample then kicks in and the merge has fewer lists)
+  const int target = p.qc == 1 ? 1024 : 2048;
   if (base_units < target) {
     const int64_t want = (target + base_units - 1) / base_units;
     int64_t by_len = a.S_max / 4096;
@@ -913,11 +916,11 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   const int64_t sl = ((int64_t)a.S_max + ns - 1) / ns;
   p.split_len = (int)(((sl + 15) / 16) * 16);
   const int kpad = ((k + 63) / 64) * 64;
-  // With many splits each keeps about four times its even share of the top-k (at least
-  // 256); the merge proves or refutes that this was enough.
+  // With many splits each keeps about twice its even share of the top-k (at least 256);
+  // the merge proves or refutes that this was enough.
   int ks = k;
   if (ns > 1) {
-    const int share = ((4 * ((k + ns - 1) / ns) + 63) / 64) * 64;
+    const int share = ((2 * ((k + ns - 1) / ns) + 63) / 64) * 64;
     ks = share > 256 ? share : 256;
     if (ks > k) ks = k;
   }
