@@ -31,6 +31,9 @@ fusion or reordering:
     scores blocks exactly as it scores keys; a query at position p sees block j iff
     4j <= p; the best k/4 blocks are kept (ties to the lower block) and each expands to
     its tokens that the query sees, in ascending order, padded with -1.
+  * Training side (the twiscan post: the indexer is trained to imitate the attention
+    distribution): gradients of the sparse attention with respect to q, K and V, the
+    plain chain rule through softmax over the selected rows.
   * Cache append (the step before Stage 1 in a decode loop): new indexer keys are
     rounded to FP8 e4m3 and written into the FP8 key cache, new K/V rows into theirs.
     The pages say only that the indexer runs in FP8 (twiscan post); the rounding read
@@ -255,6 +258,45 @@ def sparse_attention_rows(q_bits, K_bits, V_bits, idx, b: int, rows: Sequence[in
         q = decode_bf16(q_bits[b, t])
         out[i], lse[i] = sparse_attention_row(q, K, V, idx[i], sm_scale)
     return out, lse
+
+
+def sparse_attention_backward_rows(q_bits, K_bits, V_bits, idx, dout, b: int,
+                                   rows: Sequence[int], sm_scale: float):
+    """Gradients of out = softmax(sm_scale * q K_sel^T) V_sel for the listed queries of
+    sequence b, given dout [len(rows), H_q, d] (fp64).
+
+    Per query head h with selected rows J: p = softmax(l), l_j = sm_scale q.K_j;
+    dV_j += p_j dO;  dp_j = dO.V_j;  D = sum_j p_j dp_j (= dO.o);  dl_j = p_j (dp_j - D);
+    dq = sm_scale sum_j dl_j K_j;  dK_j += sm_scale dl_j q.
+    Returns dq [len(rows), H_q, d] and dK, dV [S, H_kv, d] (summed over the rows).
+    """
+    K = decode_bf16(K_bits[b])
+    V = decode_bf16(V_bits[b])
+    S, H_kv, d = K.shape
+    H_q = q_bits.shape[2]
+    grp = H_q // H_kv
+    dq = np.zeros((len(rows), H_q, d), dtype=np.float64)
+    dK = np.zeros((S, H_kv, d), dtype=np.float64)
+    dV = np.zeros((S, H_kv, d), dtype=np.float64)
+    for i, t in enumerate(rows):
+        q = decode_bf16(q_bits[b, t])
+        sel = np.asarray(idx[i])[np.asarray(idx[i]) >= 0]
+        if sel.size == 0:
+            continue
+        for h in range(H_q):
+            g = h // grp
+            Kh, Vh = K[sel, g, :], V[sel, g, :]
+            logits = sm_scale * (Kh @ q[h])
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            do = dout[i, h]
+            dp = Vh @ do
+            D = float(p @ dp)
+            dl = p * (dp - D)
+            dq[i, h] = sm_scale * (dl @ Kh)
+            np.add.at(dK[:, g, :], sel, sm_scale * dl[:, None] * q[h][None, :])
+            np.add.at(dV[:, g, :], sel, p[:, None] * do[None, :])
+    return dq, dK, dV
 
 
 # ----------------------------------------------------------------------------------

@@ -517,3 +517,75 @@ def test_pooled_selection_known_blocks_and_expansion():
     assert blocks.tolist() == sorted(best)
     toks = [pool * j + r for j in sorted(best) for r in range(pool) if pool * j + r <= 42]
     assert row.tolist() == toks + [-1] * (kb * pool - len(toks))
+
+
+# ---------------------------------------------------------------- attention backward
+
+
+def _torch_bf16_bits(t):
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_attention_backward_against_torch_autograd():
+    """Dense attention with every unselected key masked out, differentiated by torch in
+    fp64, gives the same gradients as the oracle's explicit chain rule."""
+    g = torch.Generator().manual_seed(61)
+    B, T, S, H_q, H_kv, d, k = 1, 6, 20, 4, 2, 8, 7
+    q = torch.randn(B, T, H_q, d, generator=g)
+    K = torch.randn(B, S, H_kv, d, generator=g)
+    V = torch.randn(B, S, H_kv, d, generator=g)
+    qb, Kb, Vb = _torch_bf16_bits(q), _torch_bf16_bits(K), _torch_bf16_bits(V)
+    qf = torch.from_numpy(O.decode_bf16(qb)).requires_grad_()
+    Kf = torch.from_numpy(O.decode_bf16(Kb)).requires_grad_()
+    Vf = torch.from_numpy(O.decode_bf16(Vb)).requires_grad_()
+    rng = np.random.default_rng(62)
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = rng.integers(1, k + 1)
+        idx[t, :n] = np.sort(rng.choice(S, size=n, replace=False))
+    mask = torch.full((T, S), float("-inf"), dtype=torch.float64)
+    for t in range(T):
+        mask[t, idx[t][idx[t] >= 0]] = 0.0
+    scale = 0.37
+    grp = H_q // H_kv
+    outs = []
+    for h in range(H_q):
+        logits = scale * qf[0, :, h, :] @ Kf[0, :, h // grp, :].T + mask
+        outs.append(torch.softmax(logits, dim=-1) @ Vf[0, :, h // grp, :])
+    out = torch.stack(outs, dim=1)                      # [T, H_q, d]
+    dout = torch.randn(T, H_q, d, generator=g, dtype=torch.float64)
+    (out * dout).sum().backward()
+    dq, dK, dV = O.sparse_attention_backward_rows(qb, Kb, Vb, idx, dout.numpy(), 0, list(range(T)),
+                                                  scale)
+    assert np.allclose(dq, qf.grad[0].numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dK, Kf.grad[0].numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dV, Vf.grad[0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_backward_finite_differences_and_closed_forms():
+    rng = np.random.default_rng(63)
+    S, H, d = 9, 1, 4
+    K = rng.standard_normal((1, S, 1, d)).astype(np.float32)
+    V = rng.standard_normal((1, S, 1, d)).astype(np.float32)
+    q = rng.standard_normal((1, 1, H, d)).astype(np.float32)
+    Kb, Vb, qb = (_torch_bf16_bits(torch.from_numpy(x)) for x in (K, V, q))
+    idx = np.array([[1, 4, 6, -1]])
+    dout = rng.standard_normal((1, H, d))
+    dq, dK, dV = O.sparse_attention_backward_rows(qb, Kb, Vb, idx, dout, 0, [0], 0.5)
+    # d/dq of sum(out * dout) by central differences on the decoded values
+    qv = O.decode_bf16(qb)[0, 0, 0].copy()
+    Kv, Vv = O.decode_bf16(Kb)[0], O.decode_bf16(Vb)[0]
+
+    def f(qrow):
+        o, _ = O.sparse_attention_row(qrow[None, :], Kv, Vv, idx[0], 0.5)
+        return float((o[0] * dout[0, 0]).sum())
+    eps = 1e-6
+    num = np.array([(f(qv + eps * e) - f(qv - eps * e)) / (2 * eps) for e in np.eye(d)])
+    assert np.allclose(dq[0, 0], num, rtol=1e-6, atol=1e-8)
+    # one selected key: softmax is 1, so dq = 0, dK = 0 and dV = dout
+    dq1, dK1, dV1 = O.sparse_attention_backward_rows(qb, Kb, Vb, np.array([[4, -1]]), dout, 0, [0], 0.5)
+    assert np.all(dq1 == 0) and np.all(dK1 == 0)
+    assert np.allclose(dV1[4, 0], dout[0, 0]) and np.all(np.delete(dV1, 4, axis=0) == 0)
+    # unselected rows get no gradient; the dV rows sum to dout (the weights sum to 1)
+    assert np.all(dK[[0, 2, 3, 5, 7, 8]] == 0) and np.all(dV[[0, 2, 3, 5, 7, 8]] == 0)
+    assert np.allclose(dV[:, 0].sum(axis=0), dout[0, 0])
