@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-layer", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the attention backward (detail.attention_backward)")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -377,12 +379,46 @@ def main():
         ms_pt = timed(pooled_topk)
         # a decode loop keeps the block keys up to date as blocks fill, so only prefill
         # pays the pooling pass with its selection
-        sel = ms_pt if wl.T == 1 else ms_pp + ms_pt
+        ms_sel = ms_pt if wl.T == 1 else ms_pp + ms_pt
         indexpool = {"pool": pool, "k_blocks": kb, "pool_keys_ms": round(ms_pp, 4),
                      "topk_pooled_ms": round(ms_pt, 4), "token_selection_ms": round(t_topk, 4),
-                     "selection_speedup": round(t_topk / sel, 3),
-                     "group_step_ms_estimate": round(sel + L * t_attn, 3)}
+                     "selection_speedup": round(t_topk / ms_sel, 3),
+                     "group_step_ms_estimate": round(ms_sel + L * t_attn, 3)}
         del kpool, pws, idx_p
+
+    # ---------------------------------------------------------------- attention backward
+    # Gradients of one layer's attention over the same selection (the training side).
+    backward = None
+    if not args.no_backward:
+        Lr = layers[0]
+        lse0 = torch.empty((wl.B, wl.T, wl.H_q), dtype=torch.float32, device=dev)
+        bd.sparse_attn_fwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(), wl.B,
+                           wl.T, wl.S, wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale, op[0],
+                           lse0.data_ptr(), ws.data_ptr() if attn_ws else 0, attn_ws, sh)
+        dout = torch.randn_like(Lr["q"], dtype=torch.float32).to(torch.bfloat16)
+        dq = torch.empty((wl.B, wl.T, wl.H_q, wl.d), dtype=torch.float32, device=dev)
+        dK = torch.zeros((wl.B, wl.S, wl.H_kv, wl.d), dtype=torch.float32, device=dev)
+        dV = torch.zeros_like(dK)
+
+        def bwd():
+            bd.sparse_attn_bwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(),
+                               op[0], lse0.data_ptr(), dout.data_ptr(), wl.B, wl.T, wl.S, wl.H_q,
+                               wl.H_kv, wl.d, wl.k, wl.sm_scale, dq.data_ptr(), dK.data_ptr(),
+                               dV.data_ptr(), sh)
+        bwd()
+        torch.cuda.synchronize()
+        nb = max(2, min(reps, 5))
+        e0.record(stream)
+        for _ in range(nb):
+            bwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b = e0.elapsed_time(e1) / nb
+        bflops = sel * 10.0 * wl.H_q * wl.d   # S, dP, dq, dK, dV: 2 H_q d flop each per pair
+        backward = {"ms_per_layer": round(ms_b, 3), "bf16_tflops": round(bflops / (ms_b / 1e3) / 1e12, 2),
+                    "gathered_GB_per_s": round(sel * 2.0 * wl.d * 2 * wl.H_kv / (ms_b / 1e3) / 1e9, 1),
+                    "fp32_atomic_adds": int(sel * 2 * wl.H_kv * wl.d)}
+        del lse0, dout, dq, dK, dV
 
     # ---------------------------------------------------------------- per-layer indexing
     indexshare = None
@@ -474,6 +510,7 @@ def main():
             "indexshare": indexshare,
             "cache_append": append,
             "indexpool": indexpool,
+            "attention_backward": backward,
             "wall_s_timed_region": round(t_wall, 3),
             "kernel_source_hash": kernel_source_hash(),
         },

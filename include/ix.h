@@ -125,6 +125,27 @@ ix_status sparse_attn_fwd(const void *q, const void *kc, const void *vc, const i
                           int32_t H_q, int32_t H_kv, int32_t d, int32_t k, float sm_scale,
                           void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * sparse_attn_bwd -- gradients of sparse_attn_fwd over the same selection (the training
+ * side: the twiscan post has the indexer learn from the attention distribution; these
+ * are the attention's own gradients).  With p = softmax(sm_scale q K_J^T) per query head
+ * (J the valid entries of idx) and D = dout . out:
+ *   dq = sm_scale sum_j p_j (dout . V_j - D) K_j,
+ *   dK_j += sm_scale p_j (dout . V_j - D) q,  dV_j += p_j dout  (summed over heads and
+ *   over every query that selected row j).
+ * q, kc, vc, idx, kv_len, B..sm_scale: as passed to sparse_attn_fwd; out and lse: its
+ * outputs for these inputs (lse is required); dout: bf16 [B, T, H_q, d].
+ * dq:       fp32 [B, T, H_q, d], written (0 for a query with no valid entry).
+ * dkc, dvc: fp32 [B, S_max, H_kv, d], ADDED TO (float atomics, so the order of additions
+ *           and the last bits vary from run to run); the caller clears them first.
+ * Errors: as sparse_attn_fwd, plus IX_ERR_INVALID for NULL lse, dout or gradients.
+ */
+ix_status sparse_attn_bwd(const void *q, const void *kc, const void *vc, const int32_t *idx,
+                          const int32_t *kv_len, const void *out, const float *lse,
+                          const void *dout, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
+                          int32_t H_kv, int32_t d, int32_t k, float sm_scale, float *dq,
+                          float *dkc, float *dvc, hipStream_t stream);
+
 /* Workspace bytes indexshare_group_fwd needs. */
 size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H_q,
                                   int32_t H_kv, int32_t d);

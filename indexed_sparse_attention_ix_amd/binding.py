@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled")
+           "ix_topk_pooled", "sparse_attn_bwd")
 
 
 class IxError(RuntimeError):
@@ -80,6 +80,8 @@ def load(path: str = LIB_PATH):
                                        P(c_void_p), P(c_void_p), P(c_void_p), P(c_void_p),
                                        c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                        c_size_t, c_void_p]
+    L.sparse_attn_bwd.restype = c_int32
+    L.sparse_attn_bwd.argtypes = [c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4
     L.ix_pool_keys.restype = c_int32
     L.ix_pool_keys.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                c_void_p]
@@ -165,6 +167,12 @@ def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I
                  K_cache, V_cache, stream=0):
     _check(load().ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
                                k_I_cache, K_cache, V_cache, stream))
+
+
+def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_kv, d, k,
+                    sm_scale, dq, dkc, dvc, stream=0):
+    _check(load().sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q,
+                                  H_kv, d, k, sm_scale, dq, dkc, dvc, stream))
 
 
 def ix_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream=0):
@@ -323,3 +331,21 @@ def topk_pooled(q_I, k_pooled, w, q_pos0, kv_len, S_max, pool, k_blocks, ws=None
         ws = workspace(nb, q_I.device)
     ix_topk_pooled(a, pool, k_blocks, _ptr(idx), _ptr(ws), ws.numel(), _stream())
     return idx
+
+
+def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=None):
+    """(dq fp32 [B,T,H_q,d], dK fp32 [B,S,H_kv,d], dV fp32 [B,S,H_kv,d]) of
+    sparse_attention(q, K, V, idx) for the given dout (out, lse: its forward outputs)."""
+    torch = _torch()
+    B, T, H_q, d = q.shape
+    S, H_kv = K.shape[1], K.shape[2]
+    k = idx.shape[2]
+    for t in (q, K, V, idx, out, lse, dout):
+        assert t.is_contiguous(), "attention tensors must be contiguous"
+    dq = torch.empty((B, T, H_q, d), dtype=torch.float32, device=q.device)
+    dK = torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q.device)
+    dV = torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q.device)
+    sparse_attn_bwd(_ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(kv_len), _ptr(out), _ptr(lse),
+                    _ptr(dout), B, T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(dq), _ptr(dK),
+                    _ptr(dV), _stream())
+    return dq, dK, dV

@@ -311,4 +311,26 @@ ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_block
   return ok();
 }
 
+ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                          const int32_t* kv_len, const void* out, const float* lse,
+                          const void* dout, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
+                          int32_t H_kv, int32_t d, int32_t k, float sm_scale, float* dq,
+                          float* dkc, float* dvc, hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
+  if (st != IX_OK) return st;
+  if (empty) return ok();
+  if ((st = check_attn_ptrs(q, kc, vc, idx, out)) != IX_OK) return st;
+  if (!lse || !dout || !dq || !dkc || !dvc)
+    return fail(IX_ERR_INVALID, "NULL lse, dout or gradient pointer");
+  if (!aligned16(out) || !aligned16(dout))
+    return fail(IX_ERR_INVALID, "bf16 out/dout base pointers must be 16-byte aligned");
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  hipError_t e = ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
+                                            H_q, H_kv, d, k, sm_scale, dq, dkc, dvc, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse_attn_bwd launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -388,6 +388,308 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, in
     p.lse[(size_t)row * p.H_q + head] = L > 0.f ? M + __logf(L) : -__builtin_inff();
 }
 
+// ------------------------------------------------------------------ backward
+
+struct AttnBwdArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* idx;
+  const int32_t* kv_len;
+  const uint16_t* out;
+  const float* lse;
+  const uint16_t* dout;
+  int B, T, S_max, H_q, H_kv, grp, k, chunks;
+  float scale;       // sm_scale
+  float scale_log2;  // sm_scale * log2(e)
+  float* dq;
+  float* dkc;
+  float* dvc;
+};
+
+// bf16 16x16x16: D += A(16x16) * B(16x16); lane l supplies A[l & 15][4(l>>4) .. +3] and
+// B[4(l>>4) .. +3][l & 15].
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __builtin_bit_cast(float, (uint32_t)v << 16);
+}
+
+// Gradients of the sparse attention (the training side named by the twiscan post: the
+// indexer learns from the attention distribution; these are the attention's own
+// gradients over the selected rows).  With p = softmax(sm_scale q K_J^T) per head,
+// D = dO . O:  dV_j += p_j dO,  dS_j = p_j (dO . V_j - D),  dq = sm_scale sum_j dS_j K_j,
+// dK_j += sm_scale dS_j q.
+// Block = 4 waves on one (query token, KV head), wave w taking chunks w, w+4, ... of 32
+// selected rows, gathered into LDS exactly as in the forward kernel.  Per chunk:
+//  * S^T = K Q^T and dP^T = V dO^T (bf16 MFMA 16x16x32, K and V rows from LDS as A
+//    operands, heads as columns); P and dS are formed in the lanes that hold them, with
+//    the forward's lse;
+//  * dq^T += K^T dS^T, as the forward's O^T += V^T P^T (transposing LDS reads of K);
+//  * P and sm_scale * dS go to a small LDS tile [head][key] and come back through the
+//    transposing read as the A operands (keys x heads) of 16x16x16 products with Q and dO
+//    (heads x d), giving dV and dK rows that are added to the fp32 gradient caches with
+//    float atomics (the same key is selected by many queries).
+// The four waves' dq^T partials are summed through LDS.
+template <int D>
+__global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdArgs p) {
+  constexpr int MC = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int ROWB = D * 2;
+  constexpr int PI = ROWB / 16;
+  constexpr int RPI = kWave / PI;
+  constexpr int NI = kChunk / RPI;
+  constexpr int PROW = kChunk + 4;  // bf16 per row of a P / dS tile (4 of padding)
+  __shared__ __attribute__((aligned(16))) unsigned char stage_all[kAttnWaves][2][kChunk * ROWB];
+  __shared__ __attribute__((aligned(16))) uint16_t pt_all[kAttnWaves][2][16 * PROW];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  unsigned bid = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+  const int64_t rk = bid;  // (b*T + t) * H_kv + kvh
+  const int kvh = (int)(rk % p.H_kv);
+  const int64_t row = rk / p.H_kv;
+  const int b = (int)(row / p.T);
+  int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
+  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+
+  // this lane's head r16: q and dO as B operands [head][32m + 8lg, +8), D = dO . O, lse
+  const bool hvalid = r16 < p.grp;
+  const int head = kvh * p.grp + (hvalid ? r16 : 0);
+  const size_t hrow = ((size_t)row * p.H_q + head) * D;
+  bf16x8 qb[MC], dob[MC];
+  float dpart = 0.f;
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    qb[m] = load_bf16x8(p.q + hrow + 32 * m + 8 * lg);
+    dob[m] = load_bf16x8(p.dout + hrow + 32 * m + 8 * lg);
+    const i32x4 ov = ld_global_16(p.out + hrow + 32 * m + 8 * lg);
+    const i32x4 dv = __builtin_bit_cast(i32x4, dob[m]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t o2 = (uint32_t)ov[e], d2 = (uint32_t)dv[e];
+      dpart = fmaf(bf16_to_f32((uint16_t)o2), bf16_to_f32((uint16_t)d2), dpart);
+      dpart = fmaf(bf16_to_f32((uint16_t)(o2 >> 16)), bf16_to_f32((uint16_t)(d2 >> 16)), dpart);
+    }
+    if (!hvalid) {
+      qb[m] = (bf16x8){};
+      dob[m] = (bf16x8){};
+    }
+  }
+  const float Dh = hvalid ? sum_across_rows(dpart) : 0.f;
+  const float lse_h = hvalid ? p.lse[(size_t)row * p.H_q + head] : -__builtin_inff();
+  const float lse2 = lse_h == -__builtin_inff() ? __builtin_inff() : lse_h * 1.4426950408889634f;
+
+  // q and dO as B operands of the 16x16x16 products: rows (heads) 4lg..4lg+3, column
+  // 16nt + r16
+  i16x4 qB[NT], doB[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h2 = 4 * lg + i;
+      const size_t off = ((size_t)row * p.H_q + kvh * p.grp + h2) * D + 16 * nt + r16;
+      qB[nt][i] = h2 < p.grp ? (short)p.q[off] : (short)0;
+      doB[nt][i] = h2 < p.grp ? (short)p.dout[off] : (short)0;
+    }
+  }
+
+  const int32_t* irow = p.idx + (size_t)row * p.k;
+  const uint32_t kv_stride_b = (uint32_t)(p.H_kv * ROWB);
+  const size_t seq_off = ((size_t)b * p.S_max * p.H_kv + kvh) * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.kc + seq_off, (uint32_t)kvl * kv_stride_b);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.vc + seq_off, (uint32_t)kvl * kv_stride_b);
+  float* dk_seq = p.dkc + seq_off;
+  float* dv_seq = p.dvc + seq_off;
+  unsigned char* kst = stage_all[wid][0];
+  unsigned char* vst = stage_all[wid][1];
+  uint16_t* ptp = pt_all[wid][0];
+  uint16_t* pts = pt_all[wid][1];
+
+  const int rho = lane / PI, s = lane % PI;
+  uint32_t woff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int n = rho * NI + j;
+    woff[j] = (uint32_t)(n * ROWB + 16 * (s ^ stage_swz<D>(n)));
+  }
+  uint32_t koff[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) koff[m] = (uint32_t)(r16 * ROWB + 16 * ((4 * m + lg) ^ stage_swz<D>(r16)));
+  uint32_t toff[NT];  // transposed reads of the staged K rows (as V in the forward)
+  {
+    const int n = 4 * lg + (r16 >> 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      toff[nt] = (uint32_t)(n * ROWB + 16 * ((2 * nt + ((r16 >> 1) & 1)) ^ stage_swz<D>(n)) + 8 * (r16 & 1));
+  }
+  // P / dS tiles: written as rows [head][key] by the lanes that hold them, read
+  // transposed: lane (lg, r16) reads row 4lg + r16/4, keys 4(r16 & 3) .. +3 of a half
+  const int pt_w = r16 * PROW + 4 * lg;
+  const int pt_r = (4 * lg + (r16 >> 2)) * PROW + 4 * (r16 & 3);
+
+  f32x4 dqa[NT];  // dq^T: rows 16nt + 4lg + i (d), column r16 (head)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) dqa[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int c_end = p.chunks;
+  const bool idx_vec = (p.k & 3) == 0;
+  auto load_idx = [&](int c, int (&jv)[NI]) {
+    const int e0 = c * kChunk + rho * NI;
+    if (c >= c_end) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) jv[j] = -1;
+    } else if (idx_vec && c * kChunk + kChunk <= p.k) {
+#pragma unroll
+      for (int j = 0; j < NI; j += 4) {
+        const i32x4 v = ld_global_16(irow + e0 + j);
+        jv[j] = v[0]; jv[j + 1] = v[1]; jv[j + 2] = v[2]; jv[j + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) jv[j] = e0 + j < p.k ? irow[e0 + j] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) jv[j] = (jv[j] >= 0 && jv[j] < kvl) ? jv[j] : -1;
+  };
+  i32x4 kd[NI], vd[NI];
+  auto issue_rows = [&](const int (&jv)[NI]) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * kv_stride_b + 16u * s : 0x80000000u;
+      kd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+    }
+  };
+  // cache rows of the keys this lane's S^T values belong to: keys 16tt + 4lg + i
+  auto key_rows = [&](int c, int (&kr)[8]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = c * kChunk + 16 * tt + 4 * lg + i;
+        int j = e < p.k ? irow[e] : -1;
+        kr[4 * tt + i] = (j >= 0 && j < kvl) ? j : -1;
+      }
+  };
+
+  // (no cross-chunk prefetch here: the registers go to the gradient operands instead)
+  for (int c = wid; c < c_end; c += kAttnWaves) {
+    int jv[NI];
+    load_idx(c, jv);
+    issue_rows(jv);
+    int kr[8];
+    key_rows(c, kr);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      *reinterpret_cast<i32x4*>(kst + woff[j]) = kd[j];
+      *reinterpret_cast<i32x4*>(vst + woff[j]) = vd[j];
+    }
+    lds_wait();
+
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, dp0 = s0, dp1 = s0;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(kst + koff[m]);
+      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(kst + koff[m] + 16 * ROWB);
+      const bf16x8 va0 = *reinterpret_cast<const bf16x8*>(vst + koff[m]);
+      const bf16x8 va1 = *reinterpret_cast<const bf16x8*>(vst + koff[m] + 16 * ROWB);
+      s0 = mfma_bf16_16x16x32(ka0, qb[m], s0);
+      s1 = mfma_bf16_16x16x32(ka1, qb[m], s1);
+      dp0 = mfma_bf16_16x16x32(va0, dob[m], dp0);
+      dp1 = mfma_bf16_16x16x32(va1, dob[m], dp1);
+    }
+    float pr[8], ds[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok0 = kr[i] >= 0, ok1 = kr[4 + i] >= 0;
+      pr[i] = ok0 ? exp2f(s0[i] * p.scale_log2 - lse2) : 0.f;
+      pr[4 + i] = ok1 ? exp2f(s1[i] * p.scale_log2 - lse2) : 0.f;
+      ds[i] = pr[i] * (dp0[i] - Dh);
+      ds[4 + i] = pr[4 + i] * (dp1[i] - Dh);
+    }
+
+    // dq^T += K^T dS^T: dS^T as the B operand (column = head r16)
+    {
+      i32x4 dk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dk[e] = (int)((uint32_t)f32_to_bf16_rne(ds[2 * e]) |
+                      ((uint32_t)f32_to_bf16_rne(ds[2 * e + 1]) << 16));
+      const bf16x8 dsb = __builtin_bit_cast(bf16x8, dk);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const i16x4 lo = lds_read_tr16(kst + toff[nt]);
+        const i16x4 hi = lds_read_tr16(kst + toff[nt] + 16 * ROWB);
+        const bf16x8 ka = __builtin_bit_cast(
+            bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        dqa[nt] = mfma_bf16_16x16x32(ka, dsb, dqa[nt]);
+      }
+    }
+
+    // P and sm_scale * dS as [head][key] tiles
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      i16x4 pv, sv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = (short)f32_to_bf16_rne(pr[4 * tt + i]);
+        sv[i] = (short)f32_to_bf16_rne(ds[4 * tt + i] * p.scale);
+      }
+      *reinterpret_cast<i16x4*>(ptp + pt_w + 16 * tt) = pv;
+      *reinterpret_cast<i16x4*>(pts + pt_w + 16 * tt) = sv;
+    }
+    lds_wait();
+
+    // dV += P^T dO and dK += (sm_scale dS)^T Q, row by row into the gradient caches
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const i16x4 pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(ptp + pt_r + 16 * tt));
+      const i16x4 sa = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(pts + pt_r + 16 * tt));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 dv = mfma_bf16_16x16x16(pa, doB[nt], z);
+        const f32x4 dk = mfma_bf16_16x16x16(sa, qB[nt], z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = kr[4 * tt + i];
+          if (j >= 0) {
+            const size_t off = (size_t)j * p.H_kv * D + 16 * nt + r16;
+            atomicAdd(dv_seq + off, dv[i]);
+            atomicAdd(dk_seq + off, dk[i]);
+          }
+        }
+      }
+    }
+    lds_wait();
+  }
+
+  // sum the four waves' dq^T partials through LDS: qs[head][d]
+  __syncthreads();
+  float* qs = reinterpret_cast<float*>(kst);
+  static_assert(16 * D * sizeof(float) <= 2 * kChunk * ROWB, "dq staging");
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qs[r16 * D + 16 * nt + 4 * lg + i] = dqa[nt][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * D; e += kAttnBlock) {
+    const int h = e / D, dcol = e % D;
+    if (h >= p.grp) continue;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) acc += reinterpret_cast<const float*>(stage_all[w][0])[h * D + dcol];
+    p.dq[((size_t)row * p.H_q + kvh * p.grp + h) * D + dcol] = acc * p.scale;
+  }
+}
+
 }  // namespace
 
 AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
@@ -457,6 +759,41 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
     hipLaunchKernelGGL(sparse_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, x, total);
   else
     hipLaunchKernelGGL(sparse_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, x, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                                  const int32_t* kv_len, const void* out, const float* lse,
+                                  const void* dout, int B, int T, int S_max, int H_q, int H_kv,
+                                  int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
+                                  hipStream_t stream) {
+  AttnBwdArgs x{};
+  x.q = reinterpret_cast<const uint16_t*>(q);
+  x.kc = reinterpret_cast<const uint16_t*>(kc);
+  x.vc = reinterpret_cast<const uint16_t*>(vc);
+  x.idx = idx;
+  x.kv_len = kv_len;
+  x.out = reinterpret_cast<const uint16_t*>(out);
+  x.lse = lse;
+  x.dout = reinterpret_cast<const uint16_t*>(dout);
+  x.B = B;
+  x.T = T;
+  x.S_max = S_max;
+  x.H_q = H_q;
+  x.H_kv = H_kv;
+  x.grp = H_q / H_kv;
+  x.k = k;
+  x.chunks = (k + kChunk - 1) / kChunk;
+  x.scale = sm_scale;
+  x.scale_log2 = sm_scale * 1.4426950408889634f;
+  x.dq = dq;
+  x.dkc = dkc;
+  x.dvc = dvc;
+  const size_t blocks = (size_t)B * T * H_kv;
+  if (d == 128)
+    hipLaunchKernelGGL(sparse_attn_bwd_kernel<128>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
+  else
+    hipLaunchKernelGGL(sparse_attn_bwd_kernel<64>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
   return hipGetLastError();
 }
 

@@ -1,0 +1,88 @@
+"""GPU parity: sparse-attention gradients (sparse_attn_bwd) against the oracle's chain rule.
+
+Tolerance.  The kernel rounds P and dS to bf16 for the matrix products (relative 2^-9
+each) and takes D = dout . out from the bf16-rounded forward output; everything else is
+fp32 accumulation of exact bf16 products.  A gradient is a sum of such terms, so it is
+checked in norm: per query (dq) and per sequence (dK, dV), ||g - g_ref|| <= 2e-2 ||g_ref||
+plus an absolute floor of 1e-4 sqrt(n) times the size of one term,
+sm_scale max|K| max|dout| max|V| (an exact zero, e.g. dq of a query with one valid key,
+comes back as bf16 rounding noise).
+"""
+import numpy as np
+import pytest
+import torch
+
+from indexed_sparse_attention_ix_amd import binding as bd
+from oracle import ix_oracle as O
+from parity_util import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+REL = 2e-2
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _close(g, ref, term, what):
+    scale = np.linalg.norm(ref)
+    err = np.linalg.norm(g - ref)
+    assert err <= REL * scale + 1e-4 * term * np.sqrt(ref.size), \
+        f"{what}: |err| {err:.3e} vs |ref| {scale:.3e}"
+
+
+def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=()):
+    say(f"[sparse_attn_bwd] B={B} T={T} S={S} H_q={H_q} H_kv={H_kv} d={d} k={k} seed={seed}")
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = (torch.randn(B, T, H_q, d, generator=g) * 0.3).to(torch.bfloat16)
+    K = (torch.randn(B, S, H_kv, d, generator=g) * 0.3).to(torch.bfloat16)
+    V = torch.randn(B, S, H_kv, d, generator=g).to(torch.bfloat16)
+    dout = torch.randn(B, T, H_q, d, generator=g).to(torch.bfloat16)
+    kvl = np.array(kv_lens if kv_lens is not None else [S] * B, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            if (b, t) in empty_rows:
+                continue
+            n = int(rng.integers(1, k + 1))
+            sel = np.sort(rng.choice(S, size=n, replace=False))   # may include >= kv_len: skipped
+            idx[b, t, :n] = sel
+    dq_, dK_, dV_ = (x.to(DEV) for x in (q, K, V))
+    didx = torch.from_numpy(idx).to(DEV)
+    dkvl = torch.from_numpy(kvl).to(DEV)
+    scale = d ** -0.5
+    out, lse = bd.sparse_attention(dq_, dK_, dV_, didx, scale, kv_len=dkvl, with_lse=True)
+    gq, gK, gV = bd.sparse_attention_backward(dq_, dK_, dV_, didx, out, lse, dout.to(DEV), scale,
+                                              kv_len=dkvl)
+    torch.cuda.synchronize()
+    gq, gK, gV = gq.cpu().numpy(), gK.cpu().numpy(), gV.cpu().numpy()
+    term = scale * float(K.float().abs().max() * dout.float().abs().max() * V.float().abs().max())
+    for b in range(B):
+        ridx = np.where((idx[b] >= 0) & (idx[b] < kvl[b]), idx[b], -1)
+        rq, rK, rV = O.sparse_attention_backward_rows(
+            _bits(q), _bits(K), _bits(V), ridx, dout[b].float().numpy().astype(np.float64), b,
+            list(range(T)), scale)
+        for t in range(T):
+            if (ridx[t] < 0).all():
+                assert np.all(gq[b, t] == 0), f"empty row b={b} t={t}"
+            else:
+                _close(gq[b, t], rq[t], term, f"dq b={b} t={t}")
+        _close(gK[b], rK, term, f"dK b={b}")
+        _close(gV[b], rV, term, f"dV b={b}")
+        untouched = np.setdiff1d(np.arange(S), ridx[ridx >= 0])
+        assert np.all(gK[b, untouched] == 0) and np.all(gV[b, untouched] == 0)
+
+
+def test_backward_gqa_ragged_d64():
+    _run(B=2, T=40, S=300, H_q=8, H_kv=2, d=64, k=48, seed=71, kv_lens=[300, 170],
+         empty_rows={(0, 3)})
+
+
+def test_backward_mqa_d128_many_chunks():
+    _run(B=1, T=64, S=4096, H_q=16, H_kv=1, d=128, k=256, seed=72)
+
+
+def test_backward_k_not_a_multiple_of_4():
+    _run(B=1, T=33, S=500, H_q=16, H_kv=1, d=128, k=37, seed=73)
