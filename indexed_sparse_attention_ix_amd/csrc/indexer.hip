@@ -932,7 +932,9 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k) {
   p.cap = 2 * kspad + slack;
   p.fb_cap = 2 * kpad + slack;
   // a threshold sample must fit a candidate buffer without a compaction
-  auto samp = [&](int cap) { const int t = (cap - stage) / 16; return t < 64 ? t : 64; };
+  // (the 1-query decode kernel reads its sample from memory a second time: a smaller one)
+  const int samp_max = p.qc == 1 ? 32 : 64;
+  auto samp = [&](int cap) { const int t = (cap - stage) / 16; return t < samp_max ? t : samp_max; };
   p.samp_tiles = samp(p.cap);
   p.fb_samp_tiles = samp(p.fb_cap);
   p.units = base_units * ns;
