@@ -32,8 +32,15 @@ fusion or reordering:
     4j <= p; the best k/4 blocks are kept (ties to the lower block) and each expands to
     its tokens that the query sees, in ascending order, padded with -1.
   * Training side (the twiscan post: the indexer is trained to imitate the attention
-    distribution): gradients of the sparse attention with respect to q, K and V, the
-    plain chain rule through softmax over the selected rows.
+    distribution with a KL loss): gradients of the sparse attention with respect to q, K
+    and V, the plain chain rule through softmax over the selected rows; and the KL
+    objective, read as: target t over the selected keys = the attention probabilities
+    exp(l_hj - lse_h) summed over the query heads and normalised to sum 1 over the
+    selection (lse_h defaults to the log-sum-exp over the selection itself, which makes
+    t the mean of the heads' sparse distributions; a dense lse gives the dense
+    distribution restricted to the kept keys), prediction = softmax of the indexer
+    scores of the same keys, loss = KL(t || prediction), gradient with respect to the
+    scores = prediction - t.
   * Cache append (the step before Stage 1 in a decode loop): new indexer keys are
     rounded to FP8 e4m3 and written into the FP8 key cache, new K/V rows into theirs.
     The pages say only that the indexer runs in FP8 (twiscan post); the rounding read
@@ -297,6 +304,50 @@ def sparse_attention_backward_rows(q_bits, K_bits, V_bits, idx, dout, b: int,
             np.add.at(dK[:, g, :], sel, sm_scale * dl[:, None] * q[h][None, :])
             np.add.at(dV[:, g, :], sel, p[:, None] * do[None, :])
     return dq, dK, dV
+
+
+def indexer_kl_rows(q_bits, K_bits, idx, scores, b: int, rows: Sequence[int], sm_scale: float,
+                    kv_len: int, lse=None):
+    """KL objective of the indexer for the listed queries of sequence b.
+
+    idx [len(rows), k] selections (entries < 0 or >= kv_len are padding), scores
+    [len(rows), k] the indexer's scores of those entries, lse optional [len(rows), H_q]
+    natural-log normalisers of the attention heads.  Per query:
+      u_j = sum_h exp(sm_scale q_h.K_j - lse_h),  t = u / sum(u),
+      pred = softmax(scores over the kept entries),
+      loss = sum_j t_j (log t_j - log pred_j),  dscores = pred - t (0 at padding).
+    Returns loss [len(rows)] and dscores [len(rows), k]; an empty selection gives 0.
+    """
+    K = decode_bf16(K_bits[b])
+    H_q = q_bits.shape[2]
+    grp = H_q // K.shape[1]
+    loss = np.zeros(len(rows), dtype=np.float64)
+    dsc = np.zeros(np.asarray(scores).shape, dtype=np.float64)
+    for i, t in enumerate(rows):
+        q = decode_bf16(q_bits[b, t])
+        row = np.asarray(idx[i])
+        valid = (row >= 0) & (row < kv_len)
+        if not valid.any():
+            continue
+        sel = row[valid]
+        u = np.zeros(sel.size)
+        for h in range(H_q):
+            logits = sm_scale * (K[sel, h // grp, :] @ q[h])
+            if lse is None:
+                mx = logits.max()
+                lse_h = mx + np.log(np.exp(logits - mx).sum())
+            else:
+                lse_h = float(lse[i][h])
+            u += np.exp(logits - lse_h)
+        target = u / u.sum()
+        sc = np.asarray(scores[i], dtype=np.float64)[valid]
+        mx = sc.max()
+        log_pred = sc - mx - np.log(np.exp(sc - mx).sum())
+        with np.errstate(divide="ignore", invalid="ignore"):
+            terms = np.where(target > 0, target * (np.log(target) - log_pred), 0.0)
+        loss[i] = terms.sum()
+        dsc[i, valid] = np.exp(log_pred) - target
+    return loss, dsc
 
 
 # ----------------------------------------------------------------------------------

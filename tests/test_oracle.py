@@ -589,3 +589,99 @@ def test_attention_backward_finite_differences_and_closed_forms():
     # unselected rows get no gradient; the dV rows sum to dout (the weights sum to 1)
     assert np.all(dK[[0, 2, 3, 5, 7, 8]] == 0) and np.all(dV[[0, 2, 3, 5, 7, 8]] == 0)
     assert np.allclose(dV[:, 0].sum(axis=0), dout[0, 0])
+
+
+# ---------------------------------------------------------------- indexer KL objective (reading)
+
+
+def test_indexer_kl_against_torch():
+    """torch's kl_div on log-softmax of the scores and autograd for the score gradient."""
+    g = torch.Generator().manual_seed(81)
+    B, T, S, H_q, H_kv, d, k = 1, 5, 30, 4, 2, 8, 9
+    q = torch.randn(B, T, H_q, d, generator=g)
+    K = torch.randn(B, S, H_kv, d, generator=g)
+    qb, Kb = _torch_bf16_bits(q), _torch_bf16_bits(K)
+    rng = np.random.default_rng(82)
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = rng.integers(1, k + 1)
+        idx[t, :n] = np.sort(rng.choice(S, size=n, replace=False))
+    scores = rng.standard_normal((T, k)) * 3
+    loss, dsc = O.indexer_kl_rows(qb, Kb, idx, scores, 0, list(range(T)), 0.4, S)
+    qf, Kf = torch.from_numpy(O.decode_bf16(qb)), torch.from_numpy(O.decode_bf16(Kb))
+    for t in range(T):
+        sel = idx[t][idx[t] >= 0]
+        tgt = torch.zeros(len(sel), dtype=torch.float64)
+        for h in range(H_q):
+            tgt += torch.softmax(0.4 * Kf[0, sel, h // 2, :] @ qf[0, t, h], dim=0)
+        tgt /= H_q
+        sc = torch.tensor(scores[t, :len(sel)], requires_grad=True)
+        kl = torch.nn.functional.kl_div(torch.log_softmax(sc, dim=0), tgt, reduction="sum")
+        kl.backward()
+        assert abs(kl.item() - loss[t]) <= 1e-12 * max(1.0, abs(loss[t]))
+        assert np.allclose(dsc[t, :len(sel)], sc.grad.numpy(), atol=1e-14)
+        assert np.all(dsc[t, len(sel):] == 0)
+
+
+def test_indexer_kl_closed_forms():
+    rng = np.random.default_rng(83)
+    S, H, d = 12, 2, 4
+    K = rng.standard_normal((1, S, 1, d)).astype(np.float32)
+    q = rng.standard_normal((1, 1, H, d)).astype(np.float32)
+    Kb, qb = _torch_bf16_bits(torch.from_numpy(K)), _torch_bf16_bits(torch.from_numpy(q))
+    idx = np.array([[2, 5, 7, -1]])
+    # scores equal to the log of the target make the prediction equal to it: loss 0, gradient 0
+    Kv, qv = O.decode_bf16(Kb)[0], O.decode_bf16(qb)[0, 0]
+    tgt = np.zeros(3)
+    for h in range(H):
+        lg = 0.5 * (Kv[[2, 5, 7], 0, :] @ qv[h])
+        e = np.exp(lg - lg.max())
+        tgt += e / e.sum()
+    tgt /= H
+    scores = np.array([[*np.log(tgt) + 1.7, 0.0]])          # a shift changes nothing
+    loss, dsc = O.indexer_kl_rows(qb, Kb, idx, scores, 0, [0], 0.5, S)
+    assert abs(loss[0]) < 1e-12 and np.all(np.abs(dsc) < 1e-12)
+    # one selected key: target = prediction = 1
+    loss1, dsc1 = O.indexer_kl_rows(qb, Kb, np.array([[4, -1]]), np.array([[3.0, 9.0]]), 0, [0], 0.5, S)
+    assert loss1[0] == 0 and np.all(dsc1 == 0)
+    # an entry past kv_len is padding; an empty selection gives 0
+    loss2, _ = O.indexer_kl_rows(qb, Kb, np.array([[11, -1]]), np.array([[1.0, 1.0]]), 0, [0], 0.5, 10)
+    assert loss2[0] == 0
+
+
+def test_indexer_kl_dense_lse_against_torch():
+    """With the dense (all visible keys) lse, the target is the dense attention summed over
+    heads, restricted to the kept keys and renormalised: built here with torch's softmax
+    over the full causal row; the gradient from autograd."""
+    g = torch.Generator().manual_seed(84)
+    S, H_q, H_kv, d, k = 40, 8, 2, 16, 7
+    q = torch.randn(1, 3, H_q, d, generator=g) * 2
+    K = torch.randn(1, S, H_kv, d, generator=g)
+    qb, Kb = _torch_bf16_bits(q), _torch_bf16_bits(K)
+    qf, Kf = torch.from_numpy(O.decode_bf16(qb)), torch.from_numpy(O.decode_bf16(Kb))
+    rng = np.random.default_rng(85)
+    idx = np.stack([np.sort(rng.choice(S, size=k, replace=False)) for _ in range(3)])
+    scores = rng.standard_normal((3, k))
+    lse = np.zeros((3, H_q))
+    tgts = []
+    for t in range(3):
+        dense = torch.zeros(S, dtype=torch.float64)
+        for h in range(H_q):
+            lg = 0.3 * Kf[0, :, h // 4, :] @ qf[0, t, h]
+            lse[t, h] = torch.logsumexp(lg, 0).item()
+            dense += torch.softmax(lg, 0)
+        tg = dense[idx[t]]
+        tgts.append(tg / tg.sum())
+    loss, dsc = O.indexer_kl_rows(qb, Kb, idx, scores, 0, [0, 1, 2], 0.3, S, lse=lse)
+    for t in range(3):
+        sc = torch.tensor(scores[t], requires_grad=True)
+        kl = torch.nn.functional.kl_div(torch.log_softmax(sc, 0), tgts[t], reduction="sum")
+        kl.backward()
+        assert abs(kl.item() - loss[t]) <= 1e-12 * max(1.0, abs(loss[t]))
+        assert np.allclose(dsc[t], sc.grad.numpy(), atol=1e-14)
+    # the sparse lse (over the kept keys) gives the default target
+    sparse_lse = np.array([[torch.logsumexp(0.3 * Kf[0, idx[t], h // 4, :] @ qf[0, t, h], 0).item()
+                            for h in range(H_q)] for t in range(3)])
+    l1, d1 = O.indexer_kl_rows(qb, Kb, idx, scores, 0, [0, 1, 2], 0.3, S, lse=sparse_lse)
+    l0, d0 = O.indexer_kl_rows(qb, Kb, idx, scores, 0, [0, 1, 2], 0.3, S)
+    assert np.allclose(l1, l0, rtol=1e-12, atol=1e-15) and np.allclose(d1, d0, atol=1e-15)
