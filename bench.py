@@ -418,7 +418,33 @@ def main():
         backward = {"ms_per_layer": round(ms_b, 3), "bf16_tflops": round(bflops / (ms_b / 1e3) / 1e12, 2),
                     "gathered_GB_per_s": round(sel * 2.0 * wl.d * 2 * wl.H_kv / (ms_b / 1e3) / 1e9, 1),
                     "fp32_atomic_adds": int(sel * 2 * wl.H_kv * wl.d)}
-        del lse0, dout, dq, dK, dV
+        del dout, dq, dK, dV
+
+        # the indexer's KL objective over the same selection: the kept scores come from
+        # ix_topk, the attention normalisers from the forward above
+        sel_sc = torch.empty((wl.B, wl.T, wl.k), dtype=torch.float32, device=dev)
+        bd.ix_topk(a, wl.k, idx.data_ptr(), sel_sc.data_ptr(), ws.data_ptr(), topk_ws, sh)
+        kl_loss = torch.empty((wl.B, wl.T), dtype=torch.float32, device=dev)
+        kl_dsc = torch.empty_like(sel_sc)
+
+        def kl():
+            bd.ix_indexer_kl(qp[0], kp[0], idx.data_ptr(), ind["kv_len"].data_ptr(),
+                             lse0.data_ptr(), sel_sc.data_ptr(), wl.B, wl.T, wl.S, wl.H_q,
+                             wl.H_kv, wl.d, wl.k, wl.sm_scale, kl_loss.data_ptr(),
+                             kl_dsc.data_ptr(), sh)
+        kl()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(nb):
+            kl()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_kl = e0.elapsed_time(e1) / nb
+        backward["indexer_kl"] = {
+            "ms_per_layer": round(ms_kl, 3),
+            "bf16_tflops": round(sel * 2.0 * wl.H_q * wl.d / (ms_kl / 1e3) / 1e12, 2),
+            "gathered_GB_per_s": round(sel * wl.d * 2 * wl.H_kv / (ms_kl / 1e3) / 1e9, 1)}
+        del lse0, sel_sc, kl_loss, kl_dsc
 
     # ---------------------------------------------------------------- per-layer indexing
     indexshare = None

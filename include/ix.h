@@ -146,6 +146,30 @@ ix_status sparse_attn_bwd(const void *q, const void *kc, const void *vc, const i
                           int32_t H_kv, int32_t d, int32_t k, float sm_scale, float *dq,
                           float *dkc, float *dvc, hipStream_t stream);
 
+/*
+ * ix_indexer_kl -- the indexer's training objective (the twiscan post on GLM-5.2's
+ * IndexShare: the indexer is trained to imitate the attention distribution with a KL
+ * loss).  The page names the loss only; the reading implemented: for each query and the
+ * valid entries j of its selection (0 <= idx < kv_len),
+ *   u_j = sum over all H_q heads of exp(sm_scale q_h . K_j - lse_h),  t = u / sum_j u_j,
+ *   pred = softmax_j(sel_scores_j),
+ *   loss = sum_j t_j (log t_j - log pred_j),  dscores_j = pred_j - t_j.
+ * With lse from sparse_attn_fwd over the same selection, t is the mean of the heads'
+ * attention distributions; with a dense lse (every visible key), t is the dense
+ * distribution restricted to the kept keys and renormalised.
+ * q, kc, idx, kv_len, B..sm_scale: as passed to sparse_attn_fwd (vc is not needed).
+ * lse:        fp32 [B, T, H_q] natural-log normalisers of the attention heads.
+ * sel_scores: fp32 [B, T, k] indexer scores of the entries (ix_topk's sel_scores).
+ * loss:       fp32 [B, T], written (0 for a query with no valid entry).
+ * dscores:    fp32 [B, T, k], written: d loss / d sel_scores, 0 at padding.
+ * Errors: as sparse_attn_fwd, plus IX_ERR_INVALID for NULL lse, sel_scores, loss or
+ * dscores.
+ */
+ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const int32_t *kv_len,
+                        const float *lse, const float *sel_scores, int32_t B, int32_t T,
+                        int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,
+                        float sm_scale, float *loss, float *dscores, hipStream_t stream);
+
 /* Workspace bytes indexshare_group_fwd needs. */
 size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H_q,
                                   int32_t H_kv, int32_t d);

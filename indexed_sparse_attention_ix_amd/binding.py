@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd")
+           "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl")
 
 
 class IxError(RuntimeError):
@@ -82,6 +82,8 @@ def load(path: str = LIB_PATH):
                                        c_size_t, c_void_p]
     L.sparse_attn_bwd.restype = c_int32
     L.sparse_attn_bwd.argtypes = [c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4
+    L.ix_indexer_kl.restype = c_int32
+    L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
     L.ix_pool_keys.restype = c_int32
     L.ix_pool_keys.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                c_void_p]
@@ -173,6 +175,12 @@ def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_
                     sm_scale, dq, dkc, dvc, stream=0):
     _check(load().sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q,
                                   H_kv, d, k, sm_scale, dq, dkc, dvc, stream))
+
+
+def ix_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv, d, k, sm_scale,
+                  loss, dscores, stream=0):
+    _check(load().ix_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv, d,
+                                k, sm_scale, loss, dscores, stream))
 
 
 def ix_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream=0):
@@ -349,3 +357,21 @@ def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=Non
                     _ptr(dout), B, T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(dq), _ptr(dK),
                     _ptr(dV), _stream())
     return dq, dK, dV
+
+
+def indexer_kl(q, K, idx, lse, sel_scores, sm_scale, kv_len=None):
+    """(loss fp32 [B,T], dscores fp32 [B,T,k]) of the indexer's KL objective: the target is
+    the head-summed attention probabilities exp(sm_scale q.K_j - lse) over the selection,
+    normalised; the prediction is the softmax of sel_scores."""
+    torch = _torch()
+    B, T, H_q, d = q.shape
+    S, H_kv = K.shape[1], K.shape[2]
+    k = idx.shape[2]
+    for t in (q, K, idx, lse, sel_scores):
+        assert t.is_contiguous(), "KL tensors must be contiguous"
+    assert lse.dtype == torch.float32 and sel_scores.dtype == torch.float32
+    loss = torch.empty((B, T), dtype=torch.float32, device=q.device)
+    dsc = torch.empty((B, T, k), dtype=torch.float32, device=q.device)
+    ix_indexer_kl(_ptr(q), _ptr(K), _ptr(idx), _ptr(kv_len), _ptr(lse), _ptr(sel_scores), B, T, S,
+                  H_q, H_kv, d, k, float(sm_scale), _ptr(loss), _ptr(dsc), _stream())
+    return loss, dsc

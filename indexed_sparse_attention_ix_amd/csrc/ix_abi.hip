@@ -333,4 +333,24 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
   return ok();
 }
 
+ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const int32_t* kv_len,
+                        const float* lse, const float* sel_scores, int32_t B, int32_t T,
+                        int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,
+                        float sm_scale, float* loss, float* dscores, hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
+  if (st != IX_OK) return st;
+  if (empty) return ok();
+  if (!q || !kc || !idx || !lse || !sel_scores || !loss || !dscores)
+    return fail(IX_ERR_INVALID, "NULL q, kc, idx, lse, sel_scores, loss or dscores pointer");
+  if (!aligned16(q) || !aligned16(kc))
+    return fail(IX_ERR_INVALID, "bf16 q/kc base pointers must be 16-byte aligned");
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  hipError_t e = ix::launch_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv,
+                                       d, k, sm_scale, loss, dscores, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_indexer_kl launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -61,6 +61,10 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,
                                   int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
                                   hipStream_t stream);
+hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
+                             const int32_t* kv_len, const float* lse, const float* sel_scores,
+                             int B, int T, int S_max, int H_q, int H_kv, int d, int k,
+                             float sm_scale, float* loss, float* dscores, hipStream_t stream);
 hipError_t launch_append_kv(const float* k_I_new, const void* K_new, const void* V_new,
                             const int32_t* pos0, int B, int T_new, int S_max, int d_I, int H_kv,
                             int d, uint8_t* k_I_cache, void* K_cache, void* V_cache,

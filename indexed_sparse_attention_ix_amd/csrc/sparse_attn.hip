@@ -690,6 +690,244 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
   }
 }
 
+
+// ------------------------------------------------------------------ indexer KL objective
+
+// Training side of the indexer (the twiscan post on GLM-5.2's IndexShare: the indexer
+// learns to imitate the attention distribution through a KL loss).  Per query, over the
+// valid entries j of its selection:
+//   u_j = sum_h exp(sm_scale q_h.K_j - lse_h)   (all H_q heads, lse from the forward)
+//   t = u / sum_j u_j,  pred = softmax_j(score_j),
+//   loss = sum_j t_j (log t_j - log pred_j),  dscore_j = pred_j - t_j.
+// Block = 4 waves on one query; wave w takes chunks w, w+4, ... of 32 entries, gathers
+// their K rows as the forward does and forms S = Q K^T with the heads as rows (lane
+// (g, key) holds heads 4g+i), so the head sum is four in-lane adds and two permlane
+// stages.  u goes to LDS; the block then reduces sum(u) and the scores' (max, sum exp)
+// and writes the per-entry gradient and the loss.
+struct KlArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const int32_t* idx;
+  const int32_t* kv_len;
+  const float* lse;  // [B*T][H_q] natural log
+  const float* sc;   // [B*T][k] indexer scores of the entries
+  int B, T, S_max, H_q, H_kv, grp, k, chunks;
+  float scale_log2;  // sm_scale * log2(e)
+  float* loss;       // [B*T]
+  float* dsc;        // [B*T][k]
+};
+
+constexpr int kKlMaxK = 2048;  // the largest k the library accepts
+
+// (max, sum exp(x - max)) pairs: combine without touching exp(-inf - -inf).
+__device__ __forceinline__ void lse_combine(float& m, float& z, float m2, float z2) {
+  if (m2 == -__builtin_inff()) return;
+  if (m == -__builtin_inff()) { m = m2; z = z2; return; }
+  if (m2 > m) { z = z * expf(m - m2) + z2; m = m2; }
+  else z += z2 * expf(m2 - m);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnBlock, 2) void indexer_kl_kernel(KlArgs p) {
+  constexpr int MC = D / 32;
+  constexpr int ROWB = D * 2;
+  constexpr int PI = ROWB / 16;
+  constexpr int RPI = kWave / PI;
+  constexpr int NI = kChunk / RPI;
+  __shared__ __attribute__((aligned(16))) unsigned char stage_all[kAttnWaves][kChunk * ROWB];
+  __shared__ float ubuf[kKlMaxK];
+  __shared__ float red[kAttnWaves][3];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  unsigned bid = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+  const int64_t row = bid;  // b*T + t
+  const int b = (int)(row / p.T);
+  int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
+  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+
+  const int32_t* irow = p.idx + (size_t)row * p.k;
+  const uint32_t kv_stride_b = (uint32_t)(p.H_kv * ROWB);
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(p.kc + (size_t)b * p.S_max * p.H_kv * D, (uint32_t)kvl * kv_stride_b);
+  unsigned char* kst = stage_all[wid];
+
+  const int rho = lane / PI, s = lane % PI;
+  uint32_t woff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int n = rho * NI + j;
+    woff[j] = (uint32_t)(n * ROWB + 16 * (s ^ stage_swz<D>(n)));
+  }
+  // B operand of S = Q K^T: column = key slot r16 (+16 for the second tile), depth piece 4m+lg
+  uint32_t koff[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) koff[m] = (uint32_t)(r16 * ROWB + 16 * ((4 * m + lg) ^ stage_swz<D>(r16)));
+
+  // Q rows (A operand: row = head r16 of the group, depth [32m + 8lg, +8)) and the
+  // log2-domain normalisers of heads 4lg+i (+inf for heads past the group: weight 0).
+  const bool hvalid = r16 < p.grp;
+  bf16x8 qa[MC];
+  float lse2[4];
+  auto load_head_data = [&](int kvh) {
+    const uint16_t* qrow = p.q + ((size_t)row * p.H_q + kvh * p.grp + (hvalid ? r16 : 0)) * D;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      qa[m] = load_bf16x8(qrow + 32 * m + 8 * lg);
+      if (!hvalid) qa[m] = (bf16x8){};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * lg + i;
+      lse2[i] = h < p.grp ? p.lse[(size_t)row * p.H_q + kvh * p.grp + h] * 1.4426950408889634f
+                          : __builtin_inff();
+    }
+  };
+
+  const bool idx_vec = (p.k & 3) == 0;
+  auto load_idx = [&](int c, int (&jv)[NI]) {
+    const int e0 = c * kChunk + rho * NI;
+    if (c >= p.chunks) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) jv[j] = -1;
+    } else if (idx_vec && c * kChunk + kChunk <= p.k) {
+#pragma unroll
+      for (int j = 0; j < NI; j += 4) {
+        const i32x4 v = ld_global_16(irow + e0 + j);
+        jv[j] = v[0]; jv[j + 1] = v[1]; jv[j + 2] = v[2]; jv[j + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) jv[j] = e0 + j < p.k ? irow[e0 + j] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) jv[j] = (jv[j] >= 0 && jv[j] < kvl) ? jv[j] : -1;
+  };
+  auto slot_mask = [&](const int (&jv)[NI]) -> uint32_t {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) bits |= (jv[j] >= 0 ? 1u : 0u) << j;
+    uint32_t mask = 0;
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) mask |= (uint32_t)__builtin_amdgcn_readlane((int)bits, r * PI) << (r * NI);
+    return mask;
+  };
+  i32x4 kd[NI];
+  auto issue_rows = [&](const int (&jv)[NI], int kvh) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * kv_stride_b + (uint32_t)(kvh * ROWB) + 16u * s
+                                      : 0x80000000u;
+      kd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+    }
+  };
+
+  load_head_data(0);
+  int jc[NI], jn[NI];
+  const int c0 = wid;
+  load_idx(c0, jc);
+  uint32_t mask_c = slot_mask(jc);
+  issue_rows(jc, 0);
+  load_idx(c0 + kAttnWaves, jn);
+
+  for (int c = c0; c < p.chunks; c += kAttnWaves) {
+    const uint32_t vmask = mask_c;
+    float u0 = 0.f, u1 = 0.f;  // this lane's heads, keys r16 and 16 + r16
+    for (int kvh = 0; kvh < p.H_kv; ++kvh) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) *reinterpret_cast<i32x4*>(kst + woff[j]) = kd[j];
+      if (kvh + 1 < p.H_kv) {
+        issue_rows(jc, kvh + 1);
+      } else if (c + kAttnWaves < p.chunks) {
+        mask_c = slot_mask(jn);
+        issue_rows(jn, 0);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) jc[j] = jn[j];
+        load_idx(c + 2 * kAttnWaves, jn);
+      }
+      if (p.H_kv > 1) load_head_data(kvh);  // one KV head: loaded once above
+      lds_wait();
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        const bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(kst + koff[m]);
+        const bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kst + koff[m] + 16 * ROWB);
+        s0 = mfma_bf16_16x16x32(qa[m], kb0, s0);
+        s1 = mfma_bf16_16x16x32(qa[m], kb1, s1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u0 += exp2f(s0[i] * p.scale_log2 - lse2[i]);
+        u1 += exp2f(s1[i] * p.scale_log2 - lse2[i]);
+      }
+      lds_wait();
+    }
+    u0 = sum_across_rows(u0);
+    u1 = sum_across_rows(u1);
+    if (lg == 0) {
+      ubuf[c * kChunk + r16] = ((vmask >> r16) & 1u) ? u0 : 0.f;
+      ubuf[c * kChunk + 16 + r16] = ((vmask >> (16 + r16)) & 1u) ? u1 : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // block reductions: sum(u), and (max, sum exp) of the valid entries' scores
+  const float* srow = p.sc + (size_t)row * p.k;
+  float U = 0.f, m = -__builtin_inff(), z = 0.f;
+  for (int j = threadIdx.x; j < p.k; j += kAttnBlock) {
+    const int e = irow[j];
+    if (e < 0 || e >= kvl) continue;
+    U += ubuf[j];
+    lse_combine(m, z, srow[j], 1.f);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    U += __shfl_xor(U, off);
+    const float m2 = __shfl_xor(m, off), z2 = __shfl_xor(z, off);
+    lse_combine(m, z, m2, z2);
+  }
+  if (lane == 0) {
+    red[wid][0] = U;
+    red[wid][1] = m;
+    red[wid][2] = z;
+  }
+  __syncthreads();
+  U = red[0][0];
+  m = red[0][1];
+  z = red[0][2];
+#pragma unroll
+  for (int w = 1; w < kAttnWaves; ++w) {
+    U += red[w][0];
+    lse_combine(m, z, red[w][1], red[w][2]);
+  }
+  const float log_z = m + logf(z);
+  const float inv_u = U > 0.f ? 1.f / U : 0.f;
+  float lsum = 0.f;
+  float* drow = p.dsc + (size_t)row * p.k;
+  for (int j = threadIdx.x; j < p.k; j += kAttnBlock) {
+    const int e = irow[j];
+    float g = 0.f;
+    if (e >= 0 && e < kvl) {
+      const float t = ubuf[j] * inv_u;
+      const float lp = srow[j] - log_z;
+      g = expf(lp) - t;
+      if (t > 0.f) lsum += t * (logf(t) - lp);
+    }
+    drow[j] = g;
+  }
+  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
+  __syncthreads();
+  if (lane == 0) red[wid][0] = lsum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) tot += red[w][0];
+    p.loss[row] = tot;
+  }
+}
+
 }  // namespace
 
 AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
@@ -794,6 +1032,36 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc,
     hipLaunchKernelGGL(sparse_attn_bwd_kernel<128>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
   else
     hipLaunchKernelGGL(sparse_attn_bwd_kernel<64>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
+                             const int32_t* kv_len, const float* lse, const float* sel_scores,
+                             int B, int T, int S_max, int H_q, int H_kv, int d, int k,
+                             float sm_scale, float* loss, float* dscores, hipStream_t stream) {
+  KlArgs x{};
+  x.q = reinterpret_cast<const uint16_t*>(q);
+  x.kc = reinterpret_cast<const uint16_t*>(kc);
+  x.idx = idx;
+  x.kv_len = kv_len;
+  x.lse = lse;
+  x.sc = sel_scores;
+  x.B = B;
+  x.T = T;
+  x.S_max = S_max;
+  x.H_q = H_q;
+  x.H_kv = H_kv;
+  x.grp = H_q / H_kv;
+  x.k = k;
+  x.chunks = (k + kChunk - 1) / kChunk;
+  x.scale_log2 = sm_scale * 1.4426950408889634f;
+  x.loss = loss;
+  x.dsc = dscores;
+  const size_t blocks = (size_t)B * T;
+  if (d == 128)
+    hipLaunchKernelGGL(indexer_kl_kernel<128>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
+  else
+    hipLaunchKernelGGL(indexer_kl_kernel<64>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
   return hipGetLastError();
 }
 

@@ -160,6 +160,27 @@ def test_append_validation_codes():
     assert call(kn=0, kc=0, Kn=0, Kc=0, Vn=0, Vc=0) == bd.IX_OK
 
 
+def test_indexer_kl_validation_codes():
+    ok = dict(q=FAKE, kc=FAKE, idx=FAKE, kvl=FAKE, lse=FAKE, sc=FAKE, B=2, T=3, S=64, H_q=16,
+              H_kv=1, d=128, k=16, scale=0.1, loss=FAKE, dsc=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return status_of(bd.ix_indexer_kl, a["q"], a["kc"], a["idx"], a["kvl"], a["lse"], a["sc"],
+                         a["B"], a["T"], a["S"], a["H_q"], a["H_kv"], a["d"], a["k"], a["scale"],
+                         a["loss"], a["dsc"])
+
+    for name in ("q", "kc", "idx", "lse", "sc", "loss", "dsc"):
+        assert call(**{name: 0}) == bd.IX_ERR_INVALID, name
+    assert call(q=FAKE + 2) == bd.IX_ERR_INVALID
+    assert call(scale=float("nan")) == bd.IX_ERR_INVALID
+    assert call(k=4096) == bd.IX_ERR_UNSUPPORTED
+    assert call(d=96) == bd.IX_ERR_UNSUPPORTED
+    assert call(H_q=12, H_kv=8) == bd.IX_ERR_UNSUPPORTED
+    assert call(B=0) == bd.IX_OK and call(T=0, q=0) == bd.IX_OK
+
+
 def test_workspace_sizes_for_the_named_workloads():
     from indexed_sparse_attention_ix_amd.workloads import WORKLOADS
     for wl in WORKLOADS.values():
