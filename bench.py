@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-per-layer", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the attention backward (detail.attention_backward)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured ceilings (detail.measured_peaks)")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows in the oracle's timed sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -149,6 +151,56 @@ def summarize_profiles(args, name):
     with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md"), "w") as f:
         f.write("\n".join(tm) + "\n")
     print(json.dumps(tr))
+
+
+def measured_peaks(dev, sh):
+    """What the chip delivers on the path's three shapes of work (ix_peaks.h): FP8 MFMA
+    alone and with 4/8/12 fp32 VALU ops per MFMA (the indexer's epilogue is 8), a 1 GiB
+    device copy, and random 256-byte row gathers from a 64 MiB table (one layer's K and V
+    at 128K) and from a 2 GiB table (past the 256 MB Infinity Cache)."""
+    import torch
+    from indexed_sparse_attention_ix_amd import binding as bd
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    g = torch.Generator(device="cpu").manual_seed(77)
+    codes = torch.randint(0, 256, (34 * 64 * 32,), generator=g, dtype=torch.int32)
+    codes = torch.where((codes & 0x7F) == 0x7F, torch.full_like(codes, 0x38), codes)
+    ops = codes.to(torch.uint8).to(dev)
+    chk = torch.zeros(1, dtype=torch.float32, device=dev)
+    blocks, iters = 512, 2048
+    mfma = {}
+    for nv in (0, 4, 8, 12):
+        t = timed(lambda: bd.ix_peak_mfma_fp8(ops.data_ptr(), nv, blocks, iters, chk.data_ptr(), sh))
+        mfma[str(nv)] = round(blocks * 4 * iters * 16 * 65536 / t / 1e12, 1)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: bd.ix_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
+    copy = round(2 * nbytes / t / 1e9, 1)
+    del src, dst
+    gather = {}
+    n = 1 << 25
+    xor = torch.zeros(1, dtype=torch.int32, device=dev)
+    for label, tbytes in (("64MiB", 64 << 20), ("2GiB", 2 << 30)):
+        table = torch.empty(tbytes, dtype=torch.uint8, device=dev)
+        rows = torch.randint(0, tbytes // 256, (n,), generator=torch.Generator(device="cpu").manual_seed(78),
+                             dtype=torch.int32)
+        rows = torch.sort(rows.view(-1, 2048), dim=1).values.reshape(-1).to(dev)  # ascending per 2048, like idx rows
+        t = timed(lambda: bd.ix_peak_gather(table.data_ptr(), tbytes, rows.data_ptr(), n, xor.data_ptr(), sh))
+        gather[label] = round(n * 256 / t / 1e9, 1)
+        del table, rows
+    return {"fp8_mfma_tflops_by_valu_per_mfma": mfma, "copy_GB_per_s": copy,
+            "gather_256B_rows_GB_per_s": gather}
 
 
 def kernel_source_hash():
@@ -472,6 +524,18 @@ def main():
                       "speedup": round(ms_pl / ms, 3), "layers": L}
         del inds, aa
 
+    # ---------------------------------------------------------------- measured ceilings
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks(dev, sh)
+        if idx_roof["bound"] == "mfma":
+            peaks["indexer_frac_of_mfma_with_8_valu"] = round(
+                idx_roof["achieved"] / peaks["fp8_mfma_tflops_by_valu_per_mfma"]["8"], 3)
+        else:
+            peaks["indexer_frac_of_copy"] = round(idx_roof["achieved"] / peaks["copy_GB_per_s"], 3)
+        peaks["attention_frac_of_gather_64MiB"] = round(
+            attn_roof["achieved"] / peaks["gather_256B_rows_GB_per_s"]["64MiB"], 3)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -537,6 +601,7 @@ def main():
             "cache_append": append,
             "indexpool": indexpool,
             "attention_backward": backward,
+            "measured_peaks": peaks,
             "wall_s_timed_region": round(t_wall, 3),
             "kernel_source_hash": kernel_source_hash(),
         },

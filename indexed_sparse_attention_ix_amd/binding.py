@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_float, c_int32, c_size_t, c_void_p
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
 from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl")
+           "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl", "ix_peak_mfma_fp8", "ix_peak_copy",
+           "ix_peak_gather")
 
 
 class IxError(RuntimeError):
@@ -84,6 +85,12 @@ def load(path: str = LIB_PATH):
     L.sparse_attn_bwd.argtypes = [c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4
     L.ix_indexer_kl.restype = c_int32
     L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
+    L.ix_peak_mfma_fp8.restype = c_int32
+    L.ix_peak_mfma_fp8.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
+    L.ix_peak_copy.restype = c_int32
+    L.ix_peak_copy.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
+    L.ix_peak_gather.restype = c_int32
+    L.ix_peak_gather.argtypes = [c_void_p, c_size_t, c_void_p, c_int64, c_void_p, c_void_p]
     L.ix_pool_keys.restype = c_int32
     L.ix_pool_keys.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                c_void_p]
@@ -175,6 +182,18 @@ def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_
                     sm_scale, dq, dkc, dvc, stream=0):
     _check(load().sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q,
                                   H_kv, d, k, sm_scale, dq, dkc, dvc, stream))
+
+
+def ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream=0):
+    _check(load().ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream))
+
+
+def ix_peak_copy(src, dst, nbytes, stream=0):
+    _check(load().ix_peak_copy(src, dst, nbytes, stream))
+
+
+def ix_peak_gather(table, table_bytes, rows, n, out, stream=0):
+    _check(load().ix_peak_gather(table, table_bytes, rows, n, out, stream))
 
 
 def ix_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv, d, k, sm_scale,

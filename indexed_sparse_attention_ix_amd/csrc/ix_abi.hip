@@ -8,6 +8,7 @@
 #include <string>
 
 #include "ix_internal.h"
+#include "../../include/ix_peaks.h"
 
 namespace {
 
@@ -350,6 +351,41 @@ ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const
   hipError_t e = ix::launch_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv,
                                        d, k, sm_scale, loss, dscores, stream);
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_kl launch");
+  return ok();
+}
+
+ix_status ix_peak_mfma_fp8(const void* operands, int32_t valu_per_mfma, int32_t blocks,
+                           int32_t iters, float* out, hipStream_t stream) {
+  if (!operands || !out) return fail(IX_ERR_INVALID, "NULL operands or out");
+  if (blocks < 1 || iters < 1) return fail(IX_ERR_INVALID, "blocks=%d iters=%d must be >= 1", blocks, iters);
+  if (valu_per_mfma != 0 && valu_per_mfma != 4 && valu_per_mfma != 8 && valu_per_mfma != 12)
+    return fail(IX_ERR_INVALID, "valu_per_mfma=%d (0, 4, 8 or 12)", valu_per_mfma);
+  if (!aligned16(operands)) return fail(IX_ERR_INVALID, "operands must be 16-byte aligned");
+  hipError_t e = ix::launch_peak_mfma(operands, valu_per_mfma, blocks, iters, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_peak_mfma_fp8 launch");
+  return ok();
+}
+
+ix_status ix_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  if (!src || !dst) return fail(IX_ERR_INVALID, "NULL src or dst");
+  if (bytes % 16 || !aligned16(src) || !aligned16(dst))
+    return fail(IX_ERR_INVALID, "bytes and both pointers must be multiples of 16");
+  if (bytes == 0) return ok();
+  hipError_t e = ix::launch_peak_copy(src, dst, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_peak_copy launch");
+  return ok();
+}
+
+ix_status ix_peak_gather(const void* table, size_t table_bytes, const int32_t* rows, int64_t n,
+                         uint32_t* out, hipStream_t stream) {
+  if (!table || !rows || !out) return fail(IX_ERR_INVALID, "NULL table, rows or out");
+  if (n < 0) return fail(IX_ERR_INVALID, "n=%lld must be >= 0", (long long)n);
+  if (table_bytes == 0 || table_bytes % 256 || table_bytes > ((size_t)1 << 31))
+    return fail(IX_ERR_INVALID, "table_bytes must be a positive multiple of 256, at most 2 GiB");
+  if (!aligned16(table)) return fail(IX_ERR_INVALID, "table must be 16-byte aligned");
+  if (n == 0) return ok();
+  hipError_t e = ix::launch_peak_gather(table, table_bytes, rows, n, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_peak_gather launch");
   return ok();
 }
 

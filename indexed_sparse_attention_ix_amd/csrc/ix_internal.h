@@ -65,6 +65,11 @@ hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
                              const int32_t* kv_len, const float* lse, const float* sel_scores,
                              int B, int T, int S_max, int H_q, int H_kv, int d, int k,
                              float sm_scale, float* loss, float* dscores, hipStream_t stream);
+hipError_t launch_peak_mfma(const void* operands, int valu_per_mfma, int blocks, int iters,
+                            float* out, hipStream_t stream);
+hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_peak_gather(const void* table, size_t table_bytes, const int32_t* rows, int64_t n,
+                              uint32_t* out, hipStream_t stream);
 hipError_t launch_append_kv(const float* k_I_new, const void* K_new, const void* V_new,
                             const int32_t* pos0, int B, int T_new, int S_max, int d_I, int H_kv,
                             int d, uint8_t* k_I_cache, void* K_cache, void* V_cache,

@@ -9,13 +9,14 @@ import pytest
 from indexed_sparse_attention_ix_amd import binding as bd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ix.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="libix.so not built")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                        text, flags=re.M)
@@ -179,6 +180,18 @@ def test_indexer_kl_validation_codes():
     assert call(d=96) == bd.IX_ERR_UNSUPPORTED
     assert call(H_q=12, H_kv=8) == bd.IX_ERR_UNSUPPORTED
     assert call(B=0) == bd.IX_OK and call(T=0, q=0) == bd.IX_OK
+
+
+def test_peak_validation_codes():
+    assert status_of(bd.ix_peak_mfma_fp8, 0, 8, 1, 1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_mfma_fp8, FAKE, 6, 1, 1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_mfma_fp8, FAKE, 8, 0, 1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_copy, FAKE, FAKE, 24) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_copy, FAKE, FAKE, 0) == bd.IX_OK
+    assert status_of(bd.ix_peak_gather, FAKE, 1000, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_gather, FAKE, 1 << 32, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_gather, FAKE, 256, FAKE, -1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_gather, FAKE, 256, FAKE, 0, FAKE) == bd.IX_OK
 
 
 def test_workspace_sizes_for_the_named_workloads():
