@@ -47,7 +47,9 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured ceilings (detail.measured_peaks)")
     ap.add_argument("--cpu-rows", type=int, default=512,
-                    help="query rows in the oracle's timed sample")
+                    help="at most this many query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="stop the oracle's sample once this much oracle time is spent")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (reference kernel for HBM counters)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("KT_STATS", "FETCH", "WRITE"),
@@ -545,29 +547,56 @@ def main():
             threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
         except Exception:  # noqa: BLE001
             threads = os.cpu_count() or 1
+        # Sample: query rows drawn uniformly (seed 1234) from the workload; a decode step
+        # has one query per sequence, so its sample is the first sequences.  Rows are run in
+        # chunks of up to 32 (one sequence per chunk) until --cpu-seconds of oracle time is
+        # spent or --cpu-rows rows are done.
         rng = np.random.default_rng(1234)
-        b = 0
-        rows = sorted(rng.choice(wl.T, size=min(args.cpu_rows, wl.T), replace=False).tolist())
-        ri = torch.tensor(rows, device=dev)
-        qI_h = np.zeros((wl.B, wl.T, wl.H_I, wl.d_I), dtype=np.uint8)
-        w_h = np.zeros((wl.B, wl.T, wl.H_I), dtype=np.float32)
-        qI_h[b, rows] = ind["q_I"][b, ri].cpu().numpy()
-        w_h[b, rows] = ind["w"][b, ri].cpu().numpy()
-        indexer_np = {"q_I": qI_h, "k_I": ind["k_I"].cpu().numpy(), "w": w_h,
-                      "q_pos0": ind["q_pos0"].cpu().numpy(), "kv_len": ind["kv_len"].cpu().numpy()}
-        layers_np = []
-        for Lr in layers:
-            qb = np.zeros((wl.B, wl.T, wl.H_q, wl.d), dtype=np.uint16)
-            qb[b, rows] = synth.bf16_bits(Lr["q"][b, ri])
-            layers_np.append({"q": qb, "K": synth.bf16_bits(Lr["K"][b:b + 1]),
-                              "V": synth.bf16_bits(Lr["V"][b:b + 1])})
-        t0 = time.perf_counter()
-        O.indexshare_group(indexer_np, layers_np, wl.k, b, rows, wl.sm_scale)
-        t_cpu = time.perf_counter() - t0
-        cpu = {"value": round(len(rows) / t_cpu, 3), "unit": "query tokens/s", "cores": threads,
+        n_max = min(args.cpu_rows, wl.B * wl.T)
+        if wl.T == 1:
+            picks = [(b, 0) for b in range(n_max)]
+        else:
+            flat = rng.choice(wl.B * wl.T, size=n_max, replace=False)
+            picks = [(int(f) // wl.T, int(f) % wl.T) for f in flat]
+        chunks = []
+        for b in sorted({b for b, _ in picks}):
+            rows_b = [t for bb, t in picks if bb == b]
+            chunks += [(b, sorted(rows_b[i:i + 32])) for i in range(0, len(rows_b), 32)]
+        order = rng.permutation(len(chunks))
+        done, t_cpu = 0, 0.0
+        host = {}
+        for ci in order:
+            b, rows = chunks[ci]
+            if b not in host:
+                host = {b: {"k_I": ind["k_I"][b:b + 1].cpu().numpy(),
+                            "K": [synth.bf16_bits(Lr["K"][b:b + 1]) for Lr in layers],
+                            "V": [synth.bf16_bits(Lr["V"][b:b + 1]) for Lr in layers]}}
+            hb = host[b]
+            ri = torch.tensor(rows, device=dev)
+            qI_h = np.zeros((1, wl.T, wl.H_I, wl.d_I), dtype=np.uint8)
+            w_h = np.zeros((1, wl.T, wl.H_I), dtype=np.float32)
+            qI_h[0, rows] = ind["q_I"][b, ri].cpu().numpy()
+            w_h[0, rows] = ind["w"][b, ri].cpu().numpy()
+            indexer_np = {"q_I": qI_h, "k_I": hb["k_I"], "w": w_h,
+                          "q_pos0": ind["q_pos0"][b:b + 1].cpu().numpy(),
+                          "kv_len": ind["kv_len"][b:b + 1].cpu().numpy()}
+            layers_np = []
+            for li, Lr in enumerate(layers):
+                qb = np.zeros((1, wl.T, wl.H_q, wl.d), dtype=np.uint16)
+                qb[0, rows] = synth.bf16_bits(Lr["q"][b, ri])
+                layers_np.append({"q": qb, "K": hb["K"][li], "V": hb["V"][li]})
+            t0 = time.perf_counter()
+            O.indexshare_group(indexer_np, layers_np, wl.k, 0, rows, wl.sm_scale)
+            t_cpu += time.perf_counter() - t0
+            done += len(rows)
+            if t_cpu >= args.cpu_seconds:
+                break
+        what = (f"the first {done} sequences' decode queries" if wl.T == 1 else
+                f"{done} query rows drawn uniformly")
+        cpu = {"value": round(done / t_cpu, 3), "unit": "query tokens/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{len(rows)} query rows drawn uniformly from {name} (seed 1234): "
-                         f"fp64 scores, selection and {L}-layer attention per row, "
+               "sample": f"{what} from {name} (seed 1234), run until {args.cpu_seconds:.0f} s of "
+                         f"oracle time: fp64 scores, selection and {L}-layer attention per row, "
                          f"{t_cpu:.1f} s"}
 
     line = {
