@@ -170,7 +170,8 @@ ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const
                         int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,
                         float sm_scale, float *loss, float *dscores, hipStream_t stream);
 
-/* Workspace bytes indexshare_group_fwd needs. */
+/* Workspace bytes indexshare_group_fwd needs, for any n_layers: the selection's, or the
+ * split partials of the attention of up to 8 layers, which run in one launch. */
 size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H_q,
                                   int32_t H_kv, int32_t d);
 
@@ -185,6 +186,11 @@ size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H
  *                 sparse_attn_fwd; kc/vc use S_max = a->S_max, kv_len = a->kv_len).
  * lse:            nullable host array of n_layers nullable device pointers.
  * idx:            caller-owned int32 [B, T, k]: written once, read n_layers times.
+ * When one layer's attention grid is small (decode), the attention of up to 8 layers
+ * runs in one launch; each block serves one layer and does the work of the standalone
+ * call, so the outputs stay bit for bit those of sparse_attn_fwd.
+ * ws_bytes: at least indexshare_workspace_bytes (less is accepted while it covers the
+ * selection and min(n_layers, 8) layers' split partials).
  */
 ix_status indexshare_group_fwd(const ix_indexer_args *a, int32_t k, int32_t n_layers,
                                const void *const *q, const void *const *kc,

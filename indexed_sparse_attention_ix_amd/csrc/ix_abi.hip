@@ -195,8 +195,10 @@ size_t indexshare_workspace_bytes(const ix_indexer_args* a, int32_t k, int32_t H
   if (check_attn_shape(a->B, a->T, a->S_max, H_q, H_kv, d, k, &empty2) != IX_OK) return 0;
   if (empty) return 0;
   const size_t t = ix::make_topk_plan(*a, k).ws_bytes;
-  const size_t s = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k).ws_bytes;
-  return t > s ? t : s;  // used one after the other on the same stream
+  // the selection, then the attention of up to 8 layers per launch (one partial buffer
+  // per layer of a launch), one after the other on the same stream
+  const size_t s = ix::kAttnLayersPerLaunch * ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k).ws_bytes;
+  return t > s ? t : s;
 }
 
 ix_status indexshare_group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_layers,
@@ -220,16 +222,16 @@ ix_status indexshare_group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_la
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
   const ix::TopkPlan tp = ix::make_topk_plan(*a, k);
   const ix::AttnPlan ap = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k);
-  const size_t need = tp.ws_bytes > ap.ws_bytes ? tp.ws_bytes : ap.ws_bytes;
+  const int per_launch = n_layers < ix::kAttnLayersPerLaunch ? n_layers : ix::kAttnLayersPerLaunch;
+  const size_t attn_need = (size_t)per_launch * ap.ws_bytes;
+  const size_t need = tp.ws_bytes > attn_need ? tp.ws_bytes : attn_need;
   if (!ws || ws_bytes < need)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
   hipError_t e = ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "indexshare selection launch");
-  for (int l = 0; l < n_layers; ++l) {
-    e = ix::launch_sparse_attn(q[l], kc[l], vc[l], idx, a->kv_len, a->B, a->T, a->S_max, H_q,
-                               H_kv, d, k, sm_scale, out[l], lse ? lse[l] : nullptr, ap, ws, stream);
-    if (e != hipSuccess) return hip_fail(e, "indexshare attention launch");
-  }
+  e = ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, a->kv_len, a->B, a->T, a->S_max,
+                                    H_q, H_kv, d, k, sm_scale, out, lse, ap, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexshare attention launch");
   return ok();
 }
 

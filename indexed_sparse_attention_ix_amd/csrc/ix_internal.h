@@ -56,6 +56,16 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                               int d, int k, float sm_scale, void* out, float* lse,
                               const AttnPlan& p, void* ws, hipStream_t stream);
 
+// The attention of n_layers layers over one selection: up to 8 layers per launch when one
+// layer's grid is small (fewer than 1024 blocks), else one launch per layer; layer l of a
+// launch uses ws + l * pl.ws_bytes for its split partials.
+hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const void* const* kc,
+                                     const void* const* vc, const int32_t* idx,
+                                     const int32_t* kv_len, int B, int T, int S_max, int H_q,
+                                     int H_kv, int d, int k, float sm_scale, void* const* out,
+                                     float* const* lse, const AttnPlan& pl, void* ws,
+                                     hipStream_t stream);
+constexpr int kAttnLayersPerLaunch = 8;
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,

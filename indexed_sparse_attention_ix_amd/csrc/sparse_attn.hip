@@ -32,20 +32,36 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = kAttnWaves * kWave;
 constexpr int kChunk = 32;
 
+// Layers whose attention one launch can run: each block serves one layer, with the same
+// work and the same result as a launch for that layer alone.
+constexpr int kAttnMaxLayers = 8;
+
 struct AttnArgs {
-  const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const uint16_t* q[kAttnMaxLayers];
+  const uint16_t* kc[kAttnMaxLayers];
+  const uint16_t* vc[kAttnMaxLayers];
+  uint16_t* out[kAttnMaxLayers];
+  float* lse[kAttnMaxLayers];
+  float* part_o[kAttnMaxLayers];    // [rows * H_kv * n_splits][16][D] normalised partials
+  float* part_lse[kAttnMaxLayers];  // [rows * H_kv * n_splits][16] natural-log partial lse
   const int32_t* idx;
   const int32_t* kv_len;
   int B, T, S_max, H_q, H_kv, grp, k;
   float scale_log2;  // sm_scale * log2(e)
-  uint16_t* out;
-  float* lse;
   int n_splits, chunks, chunks_per_split;
-  float* part_o;    // [rows * H_kv * n_splits][16][D] normalised partial outputs
-  float* part_lse;  // [rows * H_kv * n_splits][16] natural-log partial lse
+  int layers;
+  unsigned blocks_per_layer;
 };
+
+// Entry `layer` (wave-uniform) of a per-layer pointer array, picked with selects so the
+// argument block is never copied to private memory.
+template <typename T>
+__device__ __forceinline__ T pick_layer(T const (&a)[kAttnMaxLayers], int layer) {
+  T v = a[0];
+#pragma unroll
+  for (int l = 1; l < kAttnMaxLayers; ++l) v = layer == l ? a[l] : v;
+  return v;
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -107,7 +123,9 @@ __device__ __forceinline__ int stage_swz(int n) {
   return ((m << 1) & (PI - 1)) | (m >> (LOG - 1));
 }
 
-template <int D>
+// ML: the grid covers several layers (p.layers > 1); a single-layer launch reads entry 0
+// of the pointer arrays directly.
+template <int D, bool ML>
 __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) {
   constexpr int MC = D / 32;          // depth tiles of the QK^T product
   constexpr int NT = D / 16;          // 16-row tiles of O^T
@@ -126,6 +144,11 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   // queries (which tend to select overlapping keys) share one L2.
   unsigned bid = blockIdx.x;
   if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+  const int layer = ML ? (int)(bid / p.blocks_per_layer) : 0;
+  if (ML) bid -= (unsigned)layer * p.blocks_per_layer;
+  const uint16_t* const q_l = pick_layer(p.q, layer);
+  const uint16_t* const kc_l = pick_layer(p.kc, layer);
+  const uint16_t* const vc_l = pick_layer(p.vc, layer);
   const int split = bid % p.n_splits;
   const int64_t rk = bid / p.n_splits;  // (b*T + t) * H_kv + kvh
   const int kvh = (int)(rk % p.H_kv);
@@ -139,7 +162,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   const bool hvalid = r16 < p.grp;
   {
     const int head = kvh * p.grp + (hvalid ? r16 : 0);
-    const uint16_t* qrow = p.q + ((size_t)row * p.H_q + head) * D;
+    const uint16_t* qrow = q_l + ((size_t)row * p.H_q + head) * D;
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
       qb[m] = load_bf16x8(qrow + 32 * m + 8 * lg);
@@ -150,8 +173,8 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   const int32_t* irow = p.idx + (size_t)row * p.k;
   const uint32_t kv_stride_b = (uint32_t)(p.H_kv * ROWB);
   const size_t seq_off = ((size_t)b * p.S_max * p.H_kv + kvh) * D;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(p.kc + seq_off, (uint32_t)kvl * kv_stride_b);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(p.vc + seq_off, (uint32_t)kvl * kv_stride_b);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc_l + seq_off, (uint32_t)kvl * kv_stride_b);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc_l + seq_off, (uint32_t)kvl * kv_stride_b);
   unsigned char* kst = stage_all[wid][0];
   unsigned char* vst = stage_all[wid][1];
 
@@ -346,12 +369,13 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     const float lse_v = L > 0.f ? (M + log2f(L)) * ln2 : -__builtin_inff();
     const int head = kvh * p.grp + h;
     if (p.n_splits == 1) {
-      p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(val);
-      if (p.lse && dcol == 0) p.lse[(size_t)row * p.H_q + head] = lse_v;
+      pick_layer(p.out, layer)[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(val);
+      float* const lse_l = pick_layer(p.lse, layer);
+      if (lse_l && dcol == 0) lse_l[(size_t)row * p.H_q + head] = lse_v;
     } else {
       const size_t pr = (size_t)rk * p.n_splits + split;
-      p.part_o[(pr * 16 + h) * D + dcol] = val;
-      if (dcol == 0) p.part_lse[pr * 16 + h] = lse_v;
+      pick_layer(p.part_o, layer)[(pr * 16 + h) * D + dcol] = val;
+      if (dcol == 0) pick_layer(p.part_lse, layer)[pr * 16 + h] = lse_v;
     }
   }
 }
@@ -359,17 +383,19 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
 // Merge of split partials: out = sum_s exp(lse_s - LSE) o_s, LSE = log sum_s exp(lse_s).
 // One thread per output element (row, KV head, head of the group, column).
 template <int D>
-__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, int64_t total) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= total) return;
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, int64_t per_layer) {
+  int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= per_layer * p.layers) return;
+  const int layer = (int)(gid / per_layer);
+  gid -= layer * per_layer;
   const int dcol = (int)(gid % D);
   const int64_t rh = gid / D;
   const int h = (int)(rh % p.grp);
   const int64_t rk = rh / p.grp;  // row * H_kv + kvh
   const int kvh = (int)(rk % p.H_kv);
   const int64_t row = rk / p.H_kv;
-  const float* lse_p = p.part_lse + (size_t)rk * p.n_splits * 16 + h;
-  const float* o_p = p.part_o + ((size_t)rk * p.n_splits * 16 + h) * D + dcol;
+  const float* lse_p = pick_layer(p.part_lse, layer) + (size_t)rk * p.n_splits * 16 + h;
+  const float* o_p = pick_layer(p.part_o, layer) + ((size_t)rk * p.n_splits * 16 + h) * D + dcol;
   float M = -__builtin_inff();
   for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, lse_p[s * 16]);
   float acc = 0.f, L = 0.f;
@@ -383,9 +409,11 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, in
     }
   }
   const int head = kvh * p.grp + h;
-  p.out[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(L > 0.f ? acc / L : 0.f);
-  if (p.lse && dcol == 0)
-    p.lse[(size_t)row * p.H_q + head] = L > 0.f ? M + __logf(L) : -__builtin_inff();
+  pick_layer(p.out, layer)[((size_t)row * p.H_q + head) * D + dcol] =
+      f32_to_bf16_rne(L > 0.f ? acc / L : 0.f);
+  float* const lse_l = pick_layer(p.lse, layer);
+  if (lse_l && dcol == 0)
+    lse_l[(size_t)row * p.H_q + head] = L > 0.f ? M + __logf(L) : -__builtin_inff();
 }
 
 // ------------------------------------------------------------------ backward
@@ -955,14 +983,13 @@ AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
   return p;
 }
 
-hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* idx,
-                              const int32_t* kv_len, int B, int T, int S_max, int H_q, int H_kv,
-                              int d, int k, float sm_scale, void* out, float* lse,
-                              const AttnPlan& pl, void* ws, hipStream_t stream) {
+hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const void* const* kc,
+                                     const void* const* vc, const int32_t* idx,
+                                     const int32_t* kv_len, int B, int T, int S_max, int H_q,
+                                     int H_kv, int d, int k, float sm_scale, void* const* out,
+                                     float* const* lse, const AttnPlan& pl, void* ws,
+                                     hipStream_t stream) {
   AttnArgs x{};
-  x.q = reinterpret_cast<const uint16_t*>(q);
-  x.kc = reinterpret_cast<const uint16_t*>(kc);
-  x.vc = reinterpret_cast<const uint16_t*>(vc);
   x.idx = idx;
   x.kv_len = kv_len;
   x.B = B;
@@ -973,31 +1000,55 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
   x.grp = H_q / H_kv;
   x.k = k;
   x.scale_log2 = sm_scale * 1.4426950408889634f;
-  x.out = reinterpret_cast<uint16_t*>(out);
-  x.lse = lse;
   x.n_splits = pl.n_splits;
   x.chunks = pl.chunks;
   x.chunks_per_split = pl.chunks_per_split;
-  if (pl.n_splits > 1) {
-    const size_t parts = (size_t)B * T * H_kv * pl.n_splits;
-    const size_t o_bytes = ((parts * 16 * d * sizeof(float) + 255) / 256) * 256;
-    x.part_o = reinterpret_cast<float*>(ws);
-    x.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + o_bytes);
+  const size_t parts = (size_t)B * T * H_kv * pl.n_splits;
+  const size_t o_bytes = ((parts * 16 * d * sizeof(float) + 255) / 256) * 256;
+  // Layers share a launch only when one layer's grid is short of two rounds of resident
+  // blocks (decode): there the launches are latency-bound and the layers overlap.
+  const int per_launch = parts < 1024 ? kAttnMaxLayers : 1;
+  for (int l0 = 0; l0 < n_layers; l0 += per_launch) {
+    const int nl = n_layers - l0 < per_launch ? n_layers - l0 : per_launch;
+    x.layers = nl;
+    for (int l = 0; l < kAttnMaxLayers; ++l) {
+      const int src = l0 + (l < nl ? l : 0);
+      x.q[l] = reinterpret_cast<const uint16_t*>(q[src]);
+      x.kc[l] = reinterpret_cast<const uint16_t*>(kc[src]);
+      x.vc[l] = reinterpret_cast<const uint16_t*>(vc[src]);
+      x.out[l] = reinterpret_cast<uint16_t*>(out[src]);
+      x.lse[l] = lse ? lse[src] : nullptr;
+      char* part = reinterpret_cast<char*>(ws) + (size_t)(l < nl ? l : 0) * pl.ws_bytes;
+      x.part_o[l] = pl.n_splits > 1 ? reinterpret_cast<float*>(part) : nullptr;
+      x.part_lse[l] = pl.n_splits > 1 ? reinterpret_cast<float*>(part + o_bytes) : nullptr;
+    }
+    const size_t per_layer = (size_t)B * T * H_kv * pl.n_splits;
+    x.blocks_per_layer = (unsigned)per_layer;
+    const dim3 grid((unsigned)(per_layer * nl));
+    auto* kern = d == 128 ? (nl > 1 ? &sparse_attn_kernel<128, true> : &sparse_attn_kernel<128, false>)
+                          : (nl > 1 ? &sparse_attn_kernel<64, true> : &sparse_attn_kernel<64, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(kAttnBlock), 0, stream, x);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (pl.n_splits == 1) continue;
+    const int64_t per = (int64_t)B * T * H_q * d;
+    const dim3 cgrid((unsigned)((per * nl + 255) / 256));
+    if (d == 128)
+      hipLaunchKernelGGL(sparse_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, x, per);
+    else
+      hipLaunchKernelGGL(sparse_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, x, per);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  const size_t blocks = (size_t)B * T * H_kv * pl.n_splits;
-  if (d == 128)
-    hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
-  else
-    hipLaunchKernelGGL(sparse_attn_kernel<64>, dim3((unsigned)blocks), dim3(kAttnBlock), 0, stream, x);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || pl.n_splits == 1) return err;
-  const int64_t total = (int64_t)B * T * H_q * d;
-  const dim3 cgrid((unsigned)((total + 255) / 256));
-  if (d == 128)
-    hipLaunchKernelGGL(sparse_attn_combine_kernel<128>, cgrid, dim3(256), 0, stream, x, total);
-  else
-    hipLaunchKernelGGL(sparse_attn_combine_kernel<64>, cgrid, dim3(256), 0, stream, x, total);
-  return hipGetLastError();
+  return hipSuccess;
+}
+
+hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                              const int32_t* kv_len, int B, int T, int S_max, int H_q, int H_kv,
+                              int d, int k, float sm_scale, void* out, float* lse,
+                              const AttnPlan& pl, void* ws, hipStream_t stream) {
+  return launch_sparse_attn_layers(1, &q, &kc, &vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
+                                   sm_scale, &out, &lse, pl, ws, stream);
 }
 
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,

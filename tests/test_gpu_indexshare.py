@@ -75,8 +75,15 @@ def test_group_decode_shape():
     ind = synth.indexer_inputs(wl, device=DEV)
     layers = [synth.attention_inputs(wl, layer=l, device=DEV) for l in range(wl.layers)]
     args = (ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"])
-    idx, outs = bd.indexshare_group(*args, wl.k, [dict(q=L["q"], K=L["K"], V=L["V"])
-                                                  for L in layers], wl.sm_scale)
+    idx, outs, lses = bd.indexshare_group(*args, wl.k, [dict(q=L["q"], K=L["K"], V=L["V"])
+                                                        for L in layers], wl.sm_scale,
+                                          with_lse=True)
+    # the layers share one attention launch (split partials per layer, one combine): the
+    # same bits as standalone calls
+    for l, L in enumerate(layers):
+        o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
+                                     kv_len=ind["kv_len"], with_lse=True)
+        assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2), f"layer {l}"
     torch.cuda.synchronize()
     h = to_host_indexer(ind)
     idx_np = idx.cpu().numpy()
@@ -90,3 +97,23 @@ def test_group_decode_shape():
             ref_o, _ = O.sparse_attention_rows(hl["q"], hl["K"], hl["V"], idx_np[b], b, [0],
                                                wl.sm_scale)
             check_attention(bf16_to_f64(outs[l])[b], ref_o, where=f"layer={l} b={b}")
+
+
+def test_group_of_ten_layers_decode_two_launches():
+    """More layers than one launch takes (8): the attention runs as 8 + 2, still bit for bit
+    the standalone calls."""
+    wl = _group_case(B=4, T=1, S=5000, pos0s=None, kv_lens=None, pos0=4999, k=512, seed=44,
+                     layers=10, planted=16)
+    say(f"[indexshare_group_fwd] decode B={wl.B} S={wl.S} layers={wl.layers}")
+    ind = synth.indexer_inputs(wl, device=DEV)
+    layers = [synth.attention_inputs(wl, layer=l, device=DEV) for l in range(wl.layers)]
+    args = (ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"])
+    idx, outs, lses = bd.indexshare_group(*args, wl.k, [dict(q=L["q"], K=L["K"], V=L["V"])
+                                                        for L in layers], wl.sm_scale,
+                                          with_lse=True)
+    assert torch.equal(idx, bd.topk(*args, wl.k))
+    for l, L in enumerate(layers):
+        o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
+                                     kv_len=ind["kv_len"], with_lse=True)
+        assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2), f"layer {l}"
+    torch.cuda.synchronize()
