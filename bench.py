@@ -155,11 +155,14 @@ def summarize_profiles(args, name):
     print(json.dumps(tr))
 
 
-def measured_peaks(dev, sh):
+def measured_peaks(dev, sh, codes=None):
     """What the chip delivers on the path's three shapes of work (ix_peaks.h): FP8 MFMA
     alone and with 4/8/12 fp32 VALU ops per MFMA (the indexer's epilogue is 8), a 1 GiB
     device copy, and random 256-byte row gathers from a 64 MiB table (one layer's K and V
-    at 128K) and from a 2 GiB table (past the 256 MB Infinity Cache)."""
+    at 128K) and from a 2 GiB table (past the 256 MB Infinity Cache).
+
+    codes: e4m3 bytes for the MFMA operands -- the workload's own indexer codes, since the
+    MFMA rate depends on the operands' bit activity (power); uniform random codes if None."""
     import torch
     from indexed_sparse_attention_ix_amd import binding as bd
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -174,10 +177,14 @@ def measured_peaks(dev, sh):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps / 1e3
 
-    g = torch.Generator(device="cpu").manual_seed(77)
-    codes = torch.randint(0, 256, (34 * 64 * 32,), generator=g, dtype=torch.int32)
-    codes = torch.where((codes & 0x7F) == 0x7F, torch.full_like(codes, 0x38), codes)
-    ops = codes.to(torch.uint8).to(dev)
+    n_ops = 34 * 64 * 32
+    if codes is None:
+        g = torch.Generator(device="cpu").manual_seed(77)
+        r = torch.randint(0, 256, (n_ops,), generator=g, dtype=torch.int32)
+        ops = torch.where((r & 0x7F) == 0x7F, torch.full_like(r, 0x38), r).to(torch.uint8).to(dev)
+    else:
+        flat = codes.reshape(-1)
+        ops = flat.repeat((n_ops + flat.numel() - 1) // flat.numel())[:n_ops].contiguous()
     chk = torch.zeros(1, dtype=torch.float32, device=dev)
     blocks, iters = 512, 2048
     mfma = {}
@@ -529,7 +536,8 @@ def main():
     # ---------------------------------------------------------------- measured ceilings
     peaks = None
     if not args.no_peaks:
-        peaks = measured_peaks(dev, sh)
+        peaks = measured_peaks(dev, sh, codes=torch.cat([ind["k_I"].reshape(-1)[:1 << 20],
+                                                          ind["q_I"].reshape(-1)[:1 << 20]]))
         if idx_roof["bound"] == "mfma":
             peaks["indexer_frac_of_mfma_with_8_valu"] = round(
                 idx_roof["achieved"] / peaks["fp8_mfma_tflops_by_valu_per_mfma"]["8"], 3)
