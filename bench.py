@@ -608,7 +608,7 @@ def main():
                          f"{t_cpu:.1f} s"}
 
     line = {
-        "metric": "query tokens/s (indexer+topk+sparse attn) at 128K",
+        "metric": "query tokens/s (indexer+topk+sparse attn) at 128K; FP8 MFMA % and HBM % of peak",
         "value": round(value, 1),
         "unit": "query tokens/s",
         "n_gpus": 1,
