@@ -122,7 +122,7 @@ def summarize_profiles(args, name):
         f.write("\n")
 
     kt_md = [f"# Kernel trace: {name}", "",
-             "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):",
+             "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):",
              "", "```", kt_cmd, "```", "",
              "From `kernel_stats.csv`; durations in microseconds.", "",
              "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
