@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 KERNEL_SOURCES = ["indexed_sparse_attention_ix_amd/csrc/indexer.hip",
                   "indexed_sparse_attention_ix_amd/csrc/sparse_attn.hip",
                   "indexed_sparse_attention_ix_amd/csrc/ix_common.h"]
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--no-per-layer", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the attention backward (detail.attention_backward)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the path only: no cache append, IndexPool, backward or measured "
+                         "ceilings (the profiling runs use it so every traced launch is the path's)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured ceilings (detail.measured_peaks)")
     ap.add_argument("--cpu-rows", type=int, default=512,
@@ -57,6 +61,8 @@ def parse():
                          "--kernel-trace --stats kernel_stats.csv, then the counter_collection.csv "
                          "of a FETCH_SIZE run and of a WRITE_SIZE run (both with "
                          "--copy-calibration); no GPU needed")
+    ap.add_argument("--profile-bench-json", default=None,
+                    help="the JSON line the kernel-trace run printed (quoted beside the trace)")
     ap.add_argument("--profile-commands", nargs=3, metavar=("KT_CMD", "FETCH_CMD", "WRITE_CMD"),
                     default=("", "", ""), help="the three commands, quoted into the summaries")
     return ap.parse_args()
@@ -74,7 +80,7 @@ def short_kernel_name(name):
 
 def summarize_profiles(args, name):
     """Kernel-trace table, HBM traffic per dispatch (FETCH_SIZE / WRITE_SIZE in KiB, scaled
-    by what the same counters read for a copy of known size) and profiles/traffic.json."""
+    by what the same counters read for a copy of known size) and profiles/traffic_<workload>.json."""
     import csv
     import collections
     kt_path, fetch_path, write_path = args.summarize_profiles
@@ -91,39 +97,89 @@ def summarize_profiles(args, name):
             names[r["Dispatch_Id"]] = r["Kernel_Name"]
         return [(names[d], v) for d, v in acc.items()]
 
-    def scale_and_means(rows):
+    def scale(rows):
         copies = [v for n, v in rows if "copy" in n.lower()]
         if not copies:
             raise SystemExit("no copy dispatch in the counter run: use --copy-calibration")
         copy_kib = max(copies)
-        factor = (COPY_BYTES / 1024.0) / copy_kib
-        means = {}
-        for key in ("ix_topk_partial_kernel", "sparse_attn_kernel", "ix_topk_merge_kernel"):
-            vals = [v for n, v in rows if key in n]
-            if vals:
-                means[key] = (sum(vals) / len(vals), len(vals))
-        return copy_kib, factor, means
+        return copy_kib, (COPY_BYTES / 1024.0) / copy_kib
 
-    f_copy, f_fac, f_means = scale_and_means(per_dispatch(fetch_path, "FETCH_SIZE"))
-    w_copy, w_fac, w_means = scale_and_means(per_dispatch(write_path, "WRITE_SIZE"))
+    f_rows = per_dispatch(fetch_path, "FETCH_SIZE")
+    w_rows = per_dispatch(write_path, "WRITE_SIZE")
+    f_copy, f_fac = scale(f_rows)
+    w_copy, w_fac = scale(w_rows)
 
-    def traffic_bytes(key):
-        if key not in f_means or key not in w_means:
-            return None
-        return round(f_means[key][0] * 1024 * f_fac + w_means[key][0] * 1024 * w_fac)
+    # Bytes per call of each path kernel.  An ix_topk call is its main sweep plus, with key
+    # splits, a merge and a recompute pass whose waves mostly exit at once: its traffic is
+    # the sum over all those dispatches divided by the number of main sweeps (the
+    # dispatches within 10 % of the largest).  Attention: the single-layer launches (the
+    # ones timed per launch), without the small combine kernel.
+    def is_topk(n):
+        return "ix_topk_partial_kernel" in n or "ix_topk_merge_kernel" in n
 
+    def is_attn(n):
+        return "sparse_attn_kernel<" in n and ", false>" in n
+
+    def per_call(rows, fac, pick, main_key):
+        sel = [(n, v) for n, v in rows if pick(n)]
+        if not sel:
+            return None, 0, 0.0
+        mains = [v for n, v in sel if main_key in n]
+        top = max(mains) if mains else 0.0
+        n_main = sum(1 for v in mains if v >= 0.1 * top) or 1
+        total = sum(v for _, v in sel)
+        return total * 1024 * fac / n_main, n_main, total / n_main
+
+    def traffic_bytes(pick, main_key):
+        fb, n_main, f_kib = per_call(f_rows, f_fac, pick, main_key)
+        wb, _, w_kib = per_call(w_rows, w_fac, pick, main_key)
+        if fb is None or wb is None:
+            return None, 0, 0.0, 0.0
+        return round(fb + wb), n_main, f_kib, w_kib
+
+    idx_tr = traffic_bytes(is_topk, "ix_topk_partial_kernel")
+    attn_tr = traffic_bytes(is_attn, "sparse_attn_kernel")
     tr = {"workload": name, "source_hash": kernel_source_hash(),
-          "indexer_bytes": traffic_bytes("ix_topk_partial_kernel"),
-          "attention_bytes": traffic_bytes("sparse_attn_kernel"),
+          "indexer_bytes": idx_tr[0], "attention_bytes": attn_tr[0],
           "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(name), "w") as f:
         json.dump(tr, f, indent=1)
         f.write("\n")
 
+    # per-call durations from the per-dispatch trace next to kernel_stats.csv, by the same
+    # rule as the traffic: an ix_topk call = sweeps + merges + recompute pass / main sweeps
+    trace_path = kt_path.replace("kernel_stats.csv", "kernel_trace.csv")
+    per_call_md = []
+    if os.path.exists(trace_path):
+        durs = [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                for r in csv.DictReader(open(trace_path))]
+        tk = [(n, d) for n, d in durs if is_topk(n)]
+        sweeps = [d for n, d in tk if "ix_topk_partial_kernel" in n]
+        at = [d for n, d in durs if is_attn(n)]
+        per_call_md = ["Per call, from `kernel_trace.csv` (microseconds):", "",
+                       "| call | calls | average us |", "|---|---|---|"]
+        if sweeps:
+            top = max(sweeps)
+            n_main = sum(1 for d in sweeps if d >= 0.1 * top) or 1
+            per_call_md.append(f"| `ix_topk` (sweeps, merges and recompute pass) | {n_main} | "
+                               f"{sum(d for _, d in tk) / n_main:.1f} |")
+        if at:
+            per_call_md.append(f"| `sparse_attn_kernel` (one layer) | {len(at)} | {sum(at) / len(at):.1f} |")
+        if args.profile_bench_json and os.path.exists(args.profile_bench_json):
+            try:
+                bj = json.loads(open(args.profile_bench_json).read().strip().splitlines()[-1])
+                per_call_md += ["", f"`bench.py` in the same run, timed with events on the launch stream: "
+                                f"`ix_topk` {bj['detail']['ix_topk_ms'] * 1e3:.1f} us, "
+                                f"`sparse_attn_fwd` {bj['detail']['sparse_attn_ms_per_layer'] * 1e3:.1f} us "
+                                "per layer (with the combine kernel when the selection is split)."]
+            except (ValueError, KeyError, IndexError):
+                pass
+        per_call_md.append("")
+
     kt_md = [f"# Kernel trace: {name}", "",
              "Command (from the repository root, after `cd /tmp && export TMPDIR=/tmp`):",
-             "", "```", kt_cmd, "```", "",
+             "", "```", kt_cmd, "```", ""] + per_call_md + [
              "From `kernel_stats.csv`; durations in microseconds.", "",
              "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:12]:
@@ -142,12 +198,14 @@ def summarize_profiles(args, name):
           f"| counter | copy kernel reads (KiB) | scale |", "|---|---|---|",
           f"| FETCH_SIZE | {f_copy:.0f} | {f_fac:.4f} |",
           f"| WRITE_SIZE | {w_copy:.0f} | {w_fac:.4f} |", "",
-          "| kernel | dispatches | FETCH KiB (raw) | WRITE KiB (raw) | scaled bytes per dispatch |",
+          "Per call: `ix_topk` = its sweep plus, with key splits, the merges and the recompute",
+          "pass (summed, divided by the number of sweeps); attention = one single-layer",
+          "`sparse_attn_kernel` launch (the small combine kernel of split launches excluded).", "",
+          "| call | calls counted | FETCH KiB (raw) | WRITE KiB (raw) | scaled bytes per call |",
           "|---|---|---|---|---|"]
-    for key in ("ix_topk_partial_kernel", "ix_topk_merge_kernel", "sparse_attn_kernel"):
-        if key in f_means and key in w_means:
-            tm.append(f"| `{key}` | {f_means[key][1]} | {f_means[key][0]:.0f} | "
-                      f"{w_means[key][0]:.0f} | {traffic_bytes(key):.4g} |")
+    for label, t in (("ix_topk", idx_tr), ("sparse_attn_kernel (one layer)", attn_tr)):
+        if t[0] is not None:
+            tm.append(f"| `{label}` | {t[1]} | {t[2]:.0f} | {t[3]:.0f} | {t[0]:.4g} |")
     tm += ["", f"Kernel sources hash {tr['source_hash']} (bench.py reads these numbers only while the",
            "kernels are unchanged)."]
     with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md"), "w") as f:
@@ -358,9 +416,9 @@ def main():
     attn_roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS,
                  "unit": "GB/s", "frac": round(attn_gbs / PEAK_HBM_GBS, 4)}
     traffic = {"indexer": None, "attention": None}
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(traffic_file(name)):
         try:
-            tr = json.load(open(TRAFFIC_FILE))
+            tr = json.load(open(traffic_file(name)))
             if tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == name:
                 traffic = {"indexer": tr.get("indexer_bytes"), "attention": tr.get("attention_bytes")}
         except (OSError, ValueError):
@@ -378,7 +436,8 @@ def main():
     # new rows are the ones already at those positions, so the caches stay byte-identical.
     append = None
     p0s = wl.pos0_list()
-    if all(p == p0s[0] for p in p0s) and p0s[0] >= 0 and p0s[0] + wl.T <= wl.S:
+    if (not args.no_extras and all(p == p0s[0] for p in p0s) and p0s[0] >= 0
+            and p0s[0] + wl.T <= wl.S):
         p0 = p0s[0]
         pos_t = torch.full((wl.B,), p0, dtype=torch.int32, device=dev)
         kn = ind["k_I"][:, p0:p0 + wl.T].view(torch.float8_e4m3fn).float().contiguous()
@@ -410,7 +469,7 @@ def main():
     # The same selection budget over block keys (4 consecutive indexer keys pooled into
     # one): pooling pre-pass + block top-k of k/4 blocks expanded to k token positions.
     indexpool = None
-    if wl.k % 4 == 0:
+    if not args.no_extras and wl.k % 4 == 0:
         pool, kb = 4, wl.k // 4
         kpool = torch.empty((wl.B, (wl.S + pool - 1) // pool, wl.d_I), dtype=torch.uint8, device=dev)
         ap = bd.IndexerArgs(ind["q_I"].data_ptr(), kpool.data_ptr(), ind["w"].data_ptr(),
@@ -450,7 +509,7 @@ def main():
     # ---------------------------------------------------------------- attention backward
     # Gradients of one layer's attention over the same selection (the training side).
     backward = None
-    if not args.no_backward:
+    if not args.no_backward and not args.no_extras:
         Lr = layers[0]
         lse0 = torch.empty((wl.B, wl.T, wl.H_q), dtype=torch.float32, device=dev)
         bd.sparse_attn_fwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(), wl.B,
@@ -535,7 +594,7 @@ def main():
 
     # ---------------------------------------------------------------- measured ceilings
     peaks = None
-    if not args.no_peaks:
+    if not args.no_peaks and not args.no_extras:
         peaks = measured_peaks(dev, sh, codes=torch.cat([ind["k_I"].reshape(-1)[:1 << 20],
                                                           ind["q_I"].reshape(-1)[:1 << 20]]))
         if idx_roof["bound"] == "mfma":
