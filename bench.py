@@ -540,6 +540,28 @@ def main():
                     "fp32_atomic_adds": int(sel * 2 * wl.H_kv * wl.d)}
         del dout, dq, dK, dV
 
+        # fp32 atomic ceiling for that accumulation: 128-float rows added at uniformly random
+        # rows of a table the size of dK, one row per wave step (ix_peak_atomic_add)
+        rows_tab = wl.B * wl.S * wl.H_kv
+        if rows_tab <= (1 << 24):
+            tab = torch.zeros(rows_tab * 128, dtype=torch.float32, device=dev)
+            n_at = 1 << 22
+            rr = torch.randint(0, rows_tab, (n_at,), dtype=torch.int32,
+                               generator=torch.Generator(device="cpu").manual_seed(79)).to(dev)
+            bd.ix_peak_atomic_add(tab.data_ptr(), rows_tab, rr.data_ptr(), n_at, sh)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(3):
+                bd.ix_peak_atomic_add(tab.data_ptr(), rows_tab, rr.data_ptr(), n_at, sh)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_at = e0.elapsed_time(e1) / 3 / 1e3
+            peak_rate = n_at * 128 / t_at
+            backward["fp32_atomic_adds_per_s_measured_peak"] = round(peak_rate / 1e9, 1)
+            backward["fp32_atomic_adds_per_s"] = round(sel * 2 * wl.H_kv * wl.d / (ms_b / 1e3) / 1e9, 1)
+            backward["frac_of_atomic_peak"] = round(backward["fp32_atomic_adds_per_s"] * 1e9 / peak_rate, 3)
+            del tab, rr
+
         # the indexer's KL objective over the same selection: the kept scores come from
         # ix_topk, the attention normalisers from the forward above
         sel_sc = torch.empty((wl.B, wl.T, wl.k), dtype=torch.float32, device=dev)

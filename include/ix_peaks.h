@@ -42,6 +42,15 @@ ix_status ix_peak_copy(const void *src, void *dst, size_t bytes, hipStream_t str
 ix_status ix_peak_gather(const void *table, size_t table_bytes, const int32_t *rows, int64_t n,
                          uint32_t *out, hipStream_t stream);
 
+/*
+ * ix_peak_atomic_add -- for each i < n, adds 1.0f with fp32 atomics to all 128 floats of
+ * row idx[i] of table (rows with idx outside [0, rows) are skipped): one row per wave,
+ * lanes adding to consecutive floats, as the attention backward accumulates dK and dV.
+ * table: fp32 [rows, 128], ADDED TO; rows <= 2^24.
+ */
+ix_status ix_peak_atomic_add(float *table, int64_t rows, const int32_t *idx, int64_t n,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_byt
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
            "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl", "ix_peak_mfma_fp8", "ix_peak_copy",
-           "ix_peak_gather")
+           "ix_peak_gather", "ix_peak_atomic_add")
 
 
 class IxError(RuntimeError):
@@ -87,6 +87,8 @@ def load(path: str = LIB_PATH):
     L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
     L.ix_peak_mfma_fp8.restype = c_int32
     L.ix_peak_mfma_fp8.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
+    L.ix_peak_atomic_add.restype = c_int32
+    L.ix_peak_atomic_add.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_void_p]
     L.ix_peak_copy.restype = c_int32
     L.ix_peak_copy.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
     L.ix_peak_gather.restype = c_int32
@@ -186,6 +188,10 @@ def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_
 
 def ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream=0):
     _check(load().ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream))
+
+
+def ix_peak_atomic_add(table, rows, idx, n, stream=0):
+    _check(load().ix_peak_atomic_add(table, rows, idx, n, stream))
 
 
 def ix_peak_copy(src, dst, nbytes, stream=0):

@@ -368,6 +368,17 @@ ix_status ix_peak_mfma_fp8(const void* operands, int32_t valu_per_mfma, int32_t 
   return ok();
 }
 
+ix_status ix_peak_atomic_add(float* table, int64_t rows, const int32_t* idx, int64_t n,
+                            hipStream_t stream) {
+  if (!table || !idx) return fail(IX_ERR_INVALID, "NULL table or idx");
+  if (rows < 1 || rows > ((int64_t)1 << 31) / 128 || n < 0)
+    return fail(IX_ERR_INVALID, "rows=%lld n=%lld out of range", (long long)rows, (long long)n);
+  if (n == 0) return ok();
+  hipError_t e = ix::launch_peak_atomic(table, rows, idx, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_peak_atomic_add launch");
+  return ok();
+}
+
 ix_status ix_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   if (!src || !dst) return fail(IX_ERR_INVALID, "NULL src or dst");
   if (bytes % 16 || !aligned16(src) || !aligned16(dst))

@@ -77,6 +77,8 @@ hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
                              float sm_scale, float* loss, float* dscores, hipStream_t stream);
 hipError_t launch_peak_mfma(const void* operands, int valu_per_mfma, int blocks, int iters,
                             float* out, hipStream_t stream);
+hipError_t launch_peak_atomic(float* table, int64_t rows, const int32_t* idx, int64_t n,
+                              hipStream_t stream);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_peak_gather(const void* table, size_t table_bytes, const int32_t* rows, int64_t n,
                               uint32_t* out, hipStream_t stream);

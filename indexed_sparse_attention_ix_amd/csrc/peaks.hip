@@ -5,7 +5,9 @@
 //    max and an FMA per output element), so N = 8 is the rate its core can reach.
 //  * a device copy with 16-byte loads and stores (the HBM stream rate);
 //  * gathers of whole 256-byte rows at random from a table (the attention's access
-//    pattern: a bf16 K or V row at d = 128), read by 16 consecutive lanes per row.
+//    pattern: a bf16 K or V row at d = 128), read by 16 consecutive lanes per row;
+//  * fp32 atomic adds of whole 128-float rows at random rows of a table (the attention
+//    backward's dK/dV accumulation: one row per selected key, two 64-lane instructions).
 // None of these kernels touches memory outside the caller's buffers.
 #include "ix_common.h"
 #include "ix_internal.h"
@@ -33,8 +35,9 @@ __device__ __forceinline__ void peak_epilogue(f32x4& acc, const f32x4& x, float 
 }
 
 // Each iteration: one A tile (loaded one iteration ahead, like the indexer's key tiles)
-// against the 16 register-resident B operands.  NV > 0: the epilogue of MFMA g-2 follows the issue of MFMA g (two in
-// flight, so no dependent stall); NV = 0: results feed the accumulator of MFMA g+2.
+// against the 16 register-resident B operands.  NV > 0: the epilogue of MFMA g-2 follows
+// the issue of MFMA g (two in flight, so no dependent stall); NV = 0: results feed the
+// accumulator of MFMA g+2.
 template <int NV>
 __global__ __launch_bounds__(kPeakBlock, 2) void peak_mfma_kernel(const i32x8* __restrict__ tab,
                                                                   int iters, float* __restrict__ out) {
@@ -116,7 +119,31 @@ __global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const void* __r
   if (lane == 0) atomicXor(out, x);
 }
 
+// One listed row per wave and step: lanes add 1 to floats [0, 64) and [64, 128) of the row
+// (the row index is wave-uniform); rows outside [0, rows) are skipped.
+__global__ __launch_bounds__(kPeakBlock) void peak_atomic_kernel(float* __restrict__ table, int64_t rows,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 int64_t n) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * kPeakBlock + threadIdx.x) >> 6;
+  const int64_t waves = ((int64_t)gridDim.x * kPeakBlock) >> 6;
+  for (int64_t e = wave; e < n; e += waves) {
+    const int r = __builtin_amdgcn_readfirstlane(idx[e]);
+    if (r < 0 || r >= rows) continue;
+    float* row = table + (int64_t)r * 128;
+    atomicAdd(row + lane, 1.f);
+    atomicAdd(row + 64 + lane, 1.f);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_peak_atomic(float* table, int64_t rows, const int32_t* idx, int64_t n,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(peak_atomic_kernel, dim3(256 * 8), dim3(kPeakBlock), 0, stream, table, rows,
+                     idx, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_peak_mfma(const void* operands, int valu_per_mfma, int blocks, int iters,
                             float* out, hipStream_t stream) {

@@ -192,6 +192,10 @@ def test_peak_validation_codes():
     assert status_of(bd.ix_peak_gather, FAKE, 1 << 32, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
     assert status_of(bd.ix_peak_gather, FAKE, 256, FAKE, -1, FAKE) == bd.IX_ERR_INVALID
     assert status_of(bd.ix_peak_gather, FAKE, 256, FAKE, 0, FAKE) == bd.IX_OK
+    assert status_of(bd.ix_peak_atomic_add, 0, 10, FAKE, 5) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_atomic_add, FAKE, 0, FAKE, 5) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_atomic_add, FAKE, (1 << 24) + 1, FAKE, 5) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_peak_atomic_add, FAKE, 10, FAKE, 0) == bd.IX_OK
 
 
 def test_workspace_sizes_for_the_named_workloads():

@@ -50,3 +50,18 @@ def test_peak_mfma_runs():
                             torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         assert torch.isfinite(out).all() and out.item() != 0.0
+
+
+def test_peak_atomic_add_counts():
+    say("[ix_peak_atomic_add] 1000 rows, 50007 listed rows with out-of-range entries")
+    g = torch.Generator().manual_seed(9)
+    rows = torch.randint(-3, 1003, (50007,), generator=g, dtype=torch.int32)
+    table = torch.zeros(1000 * 128, dtype=torch.float32, device=DEV)
+    rows_d = rows.to(DEV)
+    bd.ix_peak_atomic_add(table.data_ptr(), 1000, rows_d.data_ptr(), rows.numel(),
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    r = rows.numpy()
+    want = np.bincount(r[(r >= 0) & (r < 1000)], minlength=1000).astype(np.float32)
+    got = table.view(1000, 128).cpu().numpy()
+    assert np.array_equal(got, np.repeat(want[:, None], 128, axis=1))
