@@ -530,7 +530,12 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   // appends every visible key >= the lane's threshold; buffers that near capacity are
   // compacted to a threshold that keeps at least k' entries.
   auto sweep = [&](int base, int step, int count) __attribute__((always_inline)) {
-    auto tile_off = [&](int jj) { return voff + min(base + 16 * step * jj, kvl) * DI; };
+    // tile jj of the sweep: jj itself (step 1), or a hashed tile inside stride group jj, so
+    // that a sample cannot alias with periodic structure in the keys
+    auto tile_idx = [&](int jj) {
+      return step * jj + (step > 1 ? (int)((((uint32_t)jj * 2654435761u) >> 16) % (uint32_t)step) : 0);
+    };
+    auto tile_off = [&](int jj) { return voff + min(base + 16 * tile_idx(jj), kvl) * DI; };
     i32x8 ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) ring[i] = load_key_tile(krs, tile_off(i));
@@ -543,7 +548,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       }
 #pragma unroll
       for (int ui = 0; ui < PF; ++ui) {
-        const int s = base + 16 * step * (j0 + ui) + koff;
+        const int s = base + 16 * tile_idx(j0 + ui) + koff;
         const uint64_t key =
             ((uint64_t)f32_to_ordered(sc[ui]) << 32) | (uint64_t)(lo_base - (uint32_t)s);
         const bool pass = (j0 + ui < count) & (s < lim) & (key >= th_lane);
@@ -577,8 +582,8 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     mem_fence_wave();
   };
 
-  // Sampled starting threshold: score every stride-th tile first (stride >= 4, at most 64
-  // tiles) and start each query at the r-th best sampled key, r a few standard deviations
+  // Sampled starting threshold: score one tile of every stride first (stride >= 4, at most
+  // 64 tiles) and start each query at the r-th best sampled key, r a few standard deviations
   // above the number of the query's top-k' keys the sample is expected to hold.  That is
   // a guess; the check after the sweep keeps the result exact.
   const int n_tiles = ke > ks ? (ke - ks + 15) / 16 : 0;

@@ -133,27 +133,30 @@ def test_topk_sampled_threshold_all_rows():
     _run_topk(wl)
 
 
-def _sample_stride(n_keys, k, pf=2):
-    """Tile stride of the starting-threshold sample for one unsplit query group with 16
-    MFMA head blocks: the sample is at most 64 tiles and must fit a candidate buffer."""
+def _sample_tiles(n_keys, k, pf=2):
+    """Stride and tiles of the starting-threshold sample for one unsplit query group with
+    16 MFMA head blocks: at most 64 tiles (they must fit a candidate buffer), one per
+    stride group, picked inside group jj by the multiplicative hash the kernel uses."""
     kpad = (k + 63) // 64 * 64
     stage = 2 * 64 * pf
     cap = 2 * kpad + max(1024, 2 * stage)
     samp = min(64, (cap - stage) // 16)
-    return ((n_keys + 15) // 16) // samp
+    stride = ((n_keys + 15) // 16) // samp
+    tiles = [stride * jj + (((jj * 2654435761) % (1 << 32)) >> 16) % stride for jj in range(samp)]
+    return stride, tiles
 
 
 def test_topk_misleading_sample_takes_second_sweep():
     """The sampled tiles get doubled keys, so the sampled threshold sits far above the
     true k-th score: too few keys pass and the wave must sweep again from zero."""
     wl = _wl(B=1, T=4, S=8000, pos0=7996, H_I=64, k=256, seed=23)
-    stride = _sample_stride(8000, wl.k)
+    stride, sampled = _sample_tiles(8000, wl.k)
     assert stride >= 4
     say(f"[ix_topk] misleading sample, stride {stride}")
     ind = synth.indexer_inputs(wl, device=DEV)
     kf = synth.decode_e4m3_torch(ind["k_I"])
     tiles = torch.arange(wl.S, device=DEV) // 16
-    kf[:, (tiles % stride) == 0] *= 2.0
+    kf[:, torch.isin(tiles, torch.tensor(sampled, device=DEV))] *= 2.0
     ind["k_I"] = synth.encode_e4m3(kf)
     idx = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k)
     torch.cuda.synchronize()
