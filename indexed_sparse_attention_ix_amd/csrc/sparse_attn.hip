@@ -8,8 +8,8 @@
 //  * gather: the chunk's 32 K rows and 32 V rows are fetched with 16-byte loads in
 //    which consecutive lanes read consecutive pieces of one row (a whole row per
 //    D/8 lanes), so every load touches only a few cache lines; rows are staged in
-//    LDS with a bank swizzle.  The next chunk's gathers are issued before this
-//    chunk's arithmetic, so they overlap it.
+//    LDS with a bank swizzle.  The gathers of the wave's next two chunks are in
+//    flight during a chunk's arithmetic (two register sets alternate).
 //  * S^T = K Q^T (bf16 MFMA 16x16x32): K rows come from LDS as A operands; the (up
 //    to 16) query heads that share the KV head are the columns, so lane (g, h) holds
 //    keys {4g+i, 16+4g+i} of head h.
@@ -239,8 +239,10 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     for (int r = 0; r < RPI; ++r) mask |= (uint32_t)__builtin_amdgcn_readlane((int)bits, r * PI) << (r * NI);
     return mask;
   };
-  i32x4 kd[NI], vd[NI];
-  auto issue_rows = [&](const int (&jv)[NI]) {
+  // Two register sets of chunk rows alternate: while a chunk is computed, the gathers of
+  // the next two chunks of this wave are in flight.
+  i32x4 kdA[NI], vdA[NI], kdB[NI], vdB[NI];
+  auto issue_rows = [&](const int (&jv)[NI], i32x4 (&kd)[NI], i32x4 (&vd)[NI]) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * kv_stride_b + 16u * s : 0x80000000u;
@@ -249,25 +251,30 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     }
   };
 
-  int jv[NI];
+  constexpr int W = kAttnWaves;
+  int jv[NI];  // positions of the next chunk to gather
   const int c0 = c_begin + wid;
   load_idx(c0, jv);
-  uint32_t mask_next = slot_mask(jv);
-  issue_rows(jv);
-  load_idx(c0 + kAttnWaves, jv);
+  uint32_t maskA = slot_mask(jv);
+  issue_rows(jv, kdA, vdA);
+  load_idx(c0 + W, jv);
+  uint32_t maskB = slot_mask(jv);
+  issue_rows(jv, kdB, vdB);
+  load_idx(c0 + 2 * W, jv);
 
-  for (int c = c0; c < c_end; c += kAttnWaves) {
-    // stage this chunk's rows (bank-swizzled) and start the next chunk's gathers
+  // chunk c, whose rows are in (kd, vd): stage them (bank-swizzled), refill the set with
+  // chunk c + 2W, then compute
+  auto step = [&](int c, i32x4 (&kd)[NI], i32x4 (&vd)[NI], uint32_t& mask) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       *reinterpret_cast<i32x4*>(kst + woff[j]) = kd[j];
       *reinterpret_cast<i32x4*>(vst + woff[j]) = vd[j];
     }
-    const uint32_t vmask = mask_next;
-    if (c + kAttnWaves < c_end) {
-      mask_next = slot_mask(jv);
-      issue_rows(jv);
-      load_idx(c + 2 * kAttnWaves, jv);
+    const uint32_t vmask = mask;
+    if (c + 2 * W < c_end) {
+      mask = slot_mask(jv);
+      issue_rows(jv, kd, vd);
+      load_idx(c + 3 * W, jv);
     }
     lds_wait();
 
@@ -329,6 +336,10 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
       o[nt] = mfma_bf16_16x16x32(va, pb, o[nt]);
     }
     lds_wait();
+  };
+  for (int c = c0; c < c_end; c += 2 * W) {
+    step(c, kdA, vdA, maskA);
+    if (c + W < c_end) step(c + W, kdB, vdB, maskB);
   }
 
   // per-head l: sum the four lane groups' shares
