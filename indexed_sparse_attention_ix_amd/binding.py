@@ -20,6 +20,7 @@ from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
+ABI_VERSION = 1  # IX_ABI_VERSION of include/ix.h
 IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
                 -3: "IX_ERR_WORKSPACE", -4: "IX_ERR_HIP"}
@@ -104,6 +105,9 @@ def load(path: str = LIB_PATH):
     L.ix_append_kv.restype = c_int32
     L.ix_append_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+    if L.ix_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {L.ix_abi_version()}, this binding expects "
+                           f"{ABI_VERSION}: rebuild with __graft_entry__.build()")
     _lib = L
     return L
 
