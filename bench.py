@@ -271,10 +271,16 @@ def measured_peaks(dev, sh, codes=None):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and blank lines are left out, so that a
+    comment edit does not invalidate counters taken with the same code."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -18,8 +18,10 @@
 // in the workspace: keys >= the running threshold are appended in ascending key-index
 // order; when a buffer nears capacity, a wave-level radix select over it finds a new
 // threshold that keeps at least k entries and the buffer is compacted in place
-// (order preserved).  At the end an exact select leaves exactly min(k, count)
-// entries, already in ascending index order, so no sort is needed.
+// (order preserved).  The threshold starts at an estimate from a sample (one hashed
+// tile per stride group, scored first); a count check after the sweep proves it, or the
+// sweep runs again from zero.  At the end an exact select leaves exactly
+// min(k, count) entries, already in ascending index order, so no sort is needed.
 //
 // Key splits (small batches): each (query, split) keeps only its top-k' (k' <= k) and
 // notes the smallest key it kept whenever it dropped any.  The merge takes the exact

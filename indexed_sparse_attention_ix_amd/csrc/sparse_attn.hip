@@ -20,7 +20,9 @@
 //    four keys of one column), so output lane (g, h) holds head h and the per-head
 //    rescale stays in-lane.
 // The four waves' (m, l, O) are merged through LDS at the end.  Small batches split
-// the selection over several blocks and merge the normalised partials by lse.
+// the selection over several blocks and merge the normalised partials by lse; when one
+// layer's grid is that small, the layers of an IndexShare group share one launch (each
+// block serves one layer and does exactly the work of the single-layer launch).
 #include "ix_common.h"
 #include "ix_internal.h"
 
