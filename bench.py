@@ -436,6 +436,32 @@ def main():
     roofline = dict(roofline, kernel="ix_topk (indexer + selection)" if dominant_is_indexer
                     else "sparse_attn_fwd")
 
+    # ---------------------------------------------------------------- cold attention
+    # Where one layer's K and V exceed the 256 MB Infinity Cache (decode, the 1M chunk) the
+    # gathers are HBM-bound: time the attention also after writing a 512 MiB scratch buffer
+    # before every launch, so no row is left in the caches from the previous launch.
+    attn_cold = None
+    kv_layer_bytes = 2 * wl.B * wl.S * wl.H_kv * wl.d * 2
+    if not args.no_extras and kv_layer_bytes > (256 << 20):
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        n_cold = max(3, min(reps, 10))
+        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_cold)]
+        for r in range(n_cold):
+            scratch.fill_(r & 0xFF)
+            evc[r][0].record(stream)
+            bd.sparse_attn_fwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(),
+                               wl.B, wl.T, wl.S, wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale,
+                               op[0], 0, ws.data_ptr() if attn_ws else 0, attn_ws, sh)
+            evc[r][1].record(stream)
+        torch.cuda.synchronize()
+        t_cold = sum(a_.elapsed_time(b_) for a_, b_ in evc) / n_cold
+        attn_cold = {"ms_per_layer": round(t_cold, 4),
+                     "GB_per_s": round(attn_bytes / (t_cold / 1e3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(attn_bytes / (t_cold / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "flush": "512 MiB scratch written before each launch"}
+        del scratch
+
     # ---------------------------------------------------------------- cache append (producer)
     # The step before the indexer in a serving loop: this step's T tokens per sequence go
     # into the group's FP8 key cache (rounded from fp32) and every layer's K/V caches.  The
@@ -650,17 +676,25 @@ def main():
         n_max = min(args.cpu_rows, wl.B * wl.T)
         if wl.T == 1:
             picks = [(b, 0) for b in range(n_max)]
+            special = []
         else:
+            # Always sampled, as one chunk that runs first: rows 0 and T-1 of the first
+            # sequence (the chunk's first and last queries) and rows k-2, k-1, k, which see
+            # fewer than, exactly and one more than k keys when the chunk starts at position 0.
+            special = sorted({t for t in (0, wl.k - 2, wl.k - 1, wl.k, wl.T - 1) if 0 <= t < wl.T})
             flat = rng.choice(wl.B * wl.T, size=n_max, replace=False)
-            picks = [(int(f) // wl.T, int(f) % wl.T) for f in flat]
-        chunks = []
+            picks = [p for p in dict.fromkeys((int(f) // wl.T, int(f) % wl.T) for f in flat)
+                     if not (p[0] == 0 and p[1] in special)][:max(0, n_max - len(special))]
+        chunks = [(0, special)] if special else []
         for b in sorted({b for b, _ in picks}):
             rows_b = [t for bb, t in picks if bb == b]
             chunks += [(b, sorted(rows_b[i:i + 32])) for i in range(0, len(rows_b), 32)]
-        order = rng.permutation(len(chunks))
-        done, t_cpu = 0, 0.0
+        order = (list(range(len(chunks))) if not special else
+                 [0] + [1 + int(i) for i in rng.permutation(len(chunks) - 1)])
         host = {}
-        for ci in order:
+
+        def run_chunk(ci):
+            nonlocal host
             b, rows = chunks[ci]
             if b not in host:
                 host = {b: {"k_I": ind["k_I"][b:b + 1].cpu().numpy(),
@@ -682,17 +716,38 @@ def main():
                 layers_np.append({"q": qb, "K": hb["K"][li], "V": hb["V"][li]})
             t0 = time.perf_counter()
             O.indexshare_group(indexer_np, layers_np, wl.k, 0, rows, wl.sm_scale)
-            t_cpu += time.perf_counter() - t0
-            done += len(rows)
-            if t_cpu >= args.cpu_seconds:
-                break
+            return len(rows), time.perf_counter() - t0
+
+        def timed(limit_s):
+            done, spent = 0, 0.0
+            for ci in order:
+                n, dt = run_chunk(ci)
+                done, spent = done + n, spent + dt
+                if spent >= limit_s:
+                    break
+            return done, spent
+
+        done, t_cpu = timed(args.cpu_seconds)
+        # the same chunks again with the BLAS pool held to one thread, for a shorter time
+        one = None
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = timed(max(2.0, args.cpu_seconds / 4))
+        except ImportError:
+            pass
         what = (f"the first {done} sequences' decode queries" if wl.T == 1 else
-                f"{done} query rows drawn uniformly")
+                f"{done} query rows ({len(special)} fixed: t = {special} of sequence 0; "
+                f"the rest drawn uniformly)")
         cpu = {"value": round(done / t_cpu, 3), "unit": "query tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{what} from {name} (seed 1234), run until {args.cpu_seconds:.0f} s of "
                          f"oracle time: fp64 scores, selection and {L}-layer attention per row, "
-                         f"{t_cpu:.1f} s"}
+                         f"{t_cpu:.1f} s",
+               "host_cpus": os.cpu_count(),
+               "one_thread_value": round(one[0] / one[1], 3) if one else None,
+               "one_thread_sample": (f"the first {one[0]} of the same rows, {one[1]:.1f} s"
+                                     if one else None)}
 
     line = {
         "metric": "query tokens/s (indexer+topk+sparse attn) at 128K; FP8 MFMA % and HBM % of peak",
@@ -725,6 +780,7 @@ def main():
             "cache_append": append,
             "indexpool": indexpool,
             "attention_backward": backward,
+            "attention_cold": attn_cold,
             "measured_peaks": peaks,
             "wall_s_timed_region": round(t_wall, 3),
             "kernel_source_hash": kernel_source_hash(),
