@@ -40,7 +40,9 @@ fusion or reordering:
     t the mean of the heads' sparse distributions; a dense lse gives the dense
     distribution restricted to the kept keys), prediction = softmax of the indexer
     scores of the same keys, loss = KL(t || prediction), gradient with respect to the
-    scores = prediction - t.
+    scores = prediction - t; and that gradient carried back into the indexer's inputs
+    q_I, k_I and w by the chain rule through the head sum and the ReLU (gradient with
+    respect to the decoded e4m3 values; the ReLU's step at 0 gets gradient 0).
   * Cache append (the step before Stage 1 in a decode loop): new indexer keys are
     rounded to FP8 e4m3 and written into the FP8 key cache, new K/V rows into theirs.
     The pages say only that the indexer runs in FP8 (twiscan post); the rounding read
@@ -348,6 +350,44 @@ def indexer_kl_rows(q_bits, K_bits, idx, scores, b: int, rows: Sequence[int], sm
         loss[i] = terms.sum()
         dsc[i, valid] = np.exp(log_pred) - target
     return loss, dsc
+
+
+def indexer_backward_rows(q_I, k_I, w, idx, dscores, b: int, rows: Sequence[int], kv_len: int):
+    """Gradients of the kept keys' indexer scores with respect to the indexer's inputs,
+    for the listed queries of sequence b, given g_j = d loss / d score_j (the KL's dscores).
+
+    With x_hj = q_I[t,h,:] . k_I[s_j,:] and score_j = sum_h w[t,h] max(0, x_hj):
+      dw[t,h]     = sum_j g_j max(0, x_hj)
+      dq_I[t,h,:] = sum_j g_j w[t,h] [x_hj > 0] k_I[s_j,:]
+      dk_I[s,:]   = sum over the listed (t, j) with s_j = s of sum_h g_j w[t,h] [x_hj > 0] q_I[t,h,:]
+    Gradients are taken with respect to the decoded e4m3 values, and the ReLU's step at
+    x = 0 gets gradient 0 (both readings; the pages give no more than the KL objective).
+    idx [len(rows), k] (entries < 0 or >= min(kv_len, S_max) are padding), dscores
+    [len(rows), k].  Returns dq [len(rows), H_I, d_I], dw [len(rows), H_I] and dk
+    [S_max, d_I], the listed rows' share of the key gradient.  The dot products x are exact
+    (see Exactness above), so the mask [x > 0] is the exact one.
+    """
+    keys = decode_e4m3(k_I[b])
+    n_keys = min(int(kv_len), keys.shape[0])
+    H_I, d_I = q_I.shape[2], q_I.shape[3]
+    dq = np.zeros((len(rows), H_I, d_I), dtype=np.float64)
+    dw = np.zeros((len(rows), H_I), dtype=np.float64)
+    dk = np.zeros_like(keys)
+    for i, t in enumerate(rows):
+        row = np.asarray(idx[i])
+        valid = (row >= 0) & (row < n_keys)
+        if not valid.any():
+            continue
+        sel = row[valid]
+        g = np.asarray(dscores[i], dtype=np.float64)[valid]
+        q = decode_e4m3(q_I[b, t])                  # [H_I, d_I]
+        wt = np.asarray(w[b, t], dtype=np.float64)  # [H_I]
+        x = q @ keys[sel].T                         # [H_I, n], exact
+        dw[i] = np.maximum(x, 0.0) @ g
+        G = (x > 0) * wt[:, None] * g[None, :]     # d loss / d x
+        dq[i] = G @ keys[sel]
+        np.add.at(dk, sel, G.T @ q)
+    return dq, dw, dk
 
 
 # ----------------------------------------------------------------------------------

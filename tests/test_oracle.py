@@ -685,3 +685,148 @@ def test_indexer_kl_dense_lse_against_torch():
     l1, d1 = O.indexer_kl_rows(qb, Kb, idx, scores, 0, [0, 1, 2], 0.3, S, lse=sparse_lse)
     l0, d0 = O.indexer_kl_rows(qb, Kb, idx, scores, 0, [0, 1, 2], 0.3, S)
     assert np.allclose(l1, l0, rtol=1e-12, atol=1e-15) and np.allclose(d1, d0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- indexer backward
+
+
+def _torch_e4m3_codes(x):
+    """fp32 tensor -> e4m3 bytes through torch's own cast (saturating first)."""
+    return x.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def _indexer_bwd_case(seed, B=2, T=6, S=40, H=8, dI=16, k=10):
+    g = torch.Generator().manual_seed(seed)
+    qI = _torch_e4m3_codes(torch.randn(B, T, H, dI, generator=g) * 2)
+    kI = _torch_e4m3_codes(torch.randn(B, S, dI, generator=g))
+    # exact zeros of x: head 0 of query 0 is all zero; head 1 reads only dimension 0,
+    # which keys 0..9 of sequence 0 have at zero
+    qI[0, 0, 0] = 0
+    qI[0, 0, 1] = 0
+    qI[0, 0, 1, 0] = _torch_e4m3_codes(torch.tensor([1.5]))[0]
+    kI[0, :10, 0] = 0
+    w = (torch.randn(B, T, H, generator=g)).numpy()
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, T, k), -1)
+    for b in range(B):
+        for t in range(T):
+            n = int(rng.integers(0, k + 1))
+            idx[b, t, :n] = np.sort(rng.choice(S, size=n, replace=False))
+    idx[0, 0, :3] = [0, 3, 7]   # keys whose x is 0 for head 1
+    ds = rng.standard_normal((B, T, k))
+    return qI, kI, w, idx, ds
+
+
+def test_indexer_backward_against_torch_autograd():
+    """Autograd of sum_j ds_j * score[idx_j] with the scores built densely in torch (e4m3
+    decoded by torch's own float8 type); torch's ReLU gives gradient 0 at 0."""
+    B, T, S = 2, 6, 40
+    qI, kI, w, idx, ds = _indexer_bwd_case(91, B=B, T=T, S=S)
+    kv_len = [S, 31]
+    for b in range(B):
+        Q = _torch_e4m3_values(qI[b]).requires_grad_(True)      # [T, H, d]
+        Kt = _torch_e4m3_values(kI[b]).requires_grad_(True)     # [S, d]
+        W = torch.tensor(w[b], dtype=torch.float64, requires_grad=True)
+        X = torch.einsum("thd,sd->ths", Q, Kt)
+        score = (W[:, :, None] * torch.relu(X)).sum(1)           # [T, S]
+        loss = torch.zeros((), dtype=torch.float64)
+        for t in range(T):
+            for j in range(idx.shape[2]):
+                s = int(idx[b, t, j])
+                if 0 <= s < kv_len[b]:
+                    loss = loss + float(ds[b, t, j]) * score[t, s]
+        loss.backward()
+        dq, dw, dk = O.indexer_backward_rows(qI, kI, w, idx[b], ds[b], b, list(range(T)), kv_len[b])
+        scale = 1 + float(Q.grad.abs().max())
+        assert np.allclose(dq, Q.grad.numpy(), rtol=0, atol=1e-12 * scale)
+        assert np.allclose(dw, W.grad.numpy(), rtol=0, atol=1e-12 * (1 + float(W.grad.abs().max())))
+        assert np.allclose(dk, Kt.grad.numpy(), rtol=0, atol=1e-12 * (1 + float(Kt.grad.abs().max())))
+    # the planted zeros: head 0 of query 0 contributes nothing and gets no gradient
+    dq, dw, _ = O.indexer_backward_rows(qI, kI, w, idx[0], ds[0], 0, [0], S)
+    assert dw[0, 0] == 0 and np.all(dq[0, 0] == 0)
+
+
+def test_indexer_backward_identities_and_finite_differences():
+    """score is linear in w and positively homogeneous of degree 1 in q and in k, so
+    <dw, w> = <dq, q> = <dk, k>; finite differences along directions that cross no zero
+    of x; padding and empty selections."""
+    T, S = 6, 40
+    qI, kI, w, idx, ds = _indexer_bwd_case(92, B=1, T=T, S=S)
+    rows = list(range(T))
+    dq, dw, dk = O.indexer_backward_rows(qI, kI, w, idx[0], ds[0], 0, rows, S)
+    q = O.decode_e4m3(qI[0])
+    keys = O.decode_e4m3(kI[0])
+    e_w = float(np.sum(dw * w[0]))
+    e_q = float(np.sum(dq * q))
+    e_k = float(np.sum(dk * keys))
+    assert abs(e_q - e_w) <= 1e-10 * (1 + abs(e_w)) and abs(e_k - e_w) <= 1e-10 * (1 + abs(e_w))
+
+    def loss(qv, kv, wv):
+        tot = 0.0
+        for t in rows:
+            sel = idx[0, t][idx[0, t] >= 0]
+            if sel.size:
+                tot += float(ds[0, t, :sel.size] @ O.index_scores(qv[t], kv[sel], wv[t]))
+        return tot
+
+    rng = np.random.default_rng(93)
+    eps = 1e-6
+    for name, base, grad in (("q", q, dq), ("k", keys, dk), ("w", np.asarray(w[0], np.float64), dw)):
+        d = rng.standard_normal(base.shape)
+        if name == "q":   # keep the planted exact zeros of x fixed
+            d[0, :2] = 0
+        if name == "k":
+            d[:10, 0] = 0
+        args = {"q": q, "k": keys, "w": np.asarray(w[0], np.float64)}
+        lp = loss(*[base + eps * d if n == name else args[n] for n in ("q", "k", "w")])
+        lm = loss(*[base - eps * d if n == name else args[n] for n in ("q", "k", "w")])
+        fd = (lp - lm) / (2 * eps)
+        assert abs(fd - float(np.sum(grad * d))) <= 1e-6 * (1 + abs(fd)), name
+
+    # entries at or past kv_len are padding: the same as removing them
+    cut = 25
+    idx_cut = np.where(idx[0] < cut, idx[0], -1)
+    a = O.indexer_backward_rows(qI, kI, w, idx[0], ds[0], 0, rows, cut)
+    b_ = O.indexer_backward_rows(qI, kI, w, idx_cut, ds[0], 0, rows, S)
+    for x, y in zip(a, b_):
+        assert np.array_equal(x, y)
+    # an empty selection gives zeros
+    e = O.indexer_backward_rows(qI, kI, w, np.full((1, 10), -1), ds[0, :1], 0, [2], S)
+    assert all(not np.any(x) for x in e)
+
+
+def test_indexer_backward_through_the_kl_against_torch():
+    """The KL's gradient carried into q_I, k_I and w: autograd of KL(target || softmax of
+    the kept scores), with the target held fixed, equals indexer_kl_rows' dscores fed to
+    indexer_backward_rows."""
+    T, S, H_q, d = 4, 30, 2, 8
+    qI, kI, w, idx, _ = _indexer_bwd_case(94, B=1, T=T, S=S, H=4, dI=16, k=8)
+    g = torch.Generator().manual_seed(95)
+    qa = _torch_bf16_bits(torch.randn(1, T, H_q, d, generator=g))
+    Ka = _torch_bf16_bits(torch.randn(1, S, 1, d, generator=g))
+    rows = list(range(T))
+    Q = _torch_e4m3_values(qI[0]).requires_grad_(True)
+    Kt = _torch_e4m3_values(kI[0]).requires_grad_(True)
+    W = torch.tensor(w[0], dtype=torch.float64, requires_grad=True)
+    score = (W[:, :, None] * torch.relu(torch.einsum("thd,sd->ths", Q, Kt))).sum(1)
+    sel_scores = np.zeros(idx[0].shape)
+    total = torch.zeros((), dtype=torch.float64)
+    qf, Kf = torch.from_numpy(O.decode_bf16(qa)), torch.from_numpy(O.decode_bf16(Ka))
+    for t in rows:
+        sel = idx[0, t][idx[0, t] >= 0]
+        if sel.size == 0:
+            continue
+        sel_scores[t, :sel.size] = score[t, sel].detach().numpy()
+        tgt = sum(torch.softmax(0.5 * Kf[0, sel, 0, :] @ qf[0, t, h], 0) for h in range(H_q)) / H_q
+        total = total + torch.nn.functional.kl_div(torch.log_softmax(score[t, sel], 0), tgt,
+                                                   reduction="sum")
+    total.backward()
+    _, dsc = O.indexer_kl_rows(qa, Ka, idx[0], sel_scores, 0, rows, 0.5, S)
+    dq, dw, dk = O.indexer_backward_rows(qI, kI, w, idx[0], dsc, 0, rows, S)
+    assert np.allclose(dq, Q.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dw, W.grad.numpy(), rtol=0, atol=1e-12)
+    assert np.allclose(dk, Kt.grad.numpy(), rtol=0, atol=1e-12)
