@@ -618,7 +618,34 @@ def main():
             "ms_per_layer": round(ms_kl, 3),
             "bf16_tflops": round(sel * 2.0 * wl.H_q * wl.d / (ms_kl / 1e3) / 1e12, 2),
             "gathered_GB_per_s": round(sel * wl.d * 2 * wl.H_kv / (ms_kl / 1e3) / 1e9, 1)}
-        del lse0, sel_sc, kl_loss, kl_dsc
+
+        # the KL's score gradient carried into the indexer's inputs (once per group: the
+        # layers share the indexer); dk_I accumulates over the reps, which changes no timing
+        dq_I = torch.empty((wl.B, wl.T, wl.H_I, wl.d_I), dtype=torch.float32, device=dev)
+        dw_I = torch.empty((wl.B, wl.T, wl.H_I), dtype=torch.float32, device=dev)
+        dk_I = torch.zeros((wl.B, wl.S, wl.d_I), dtype=torch.float32, device=dev)
+
+        def ibwd():
+            bd.ix_indexer_bwd(a, wl.k, idx.data_ptr(), kl_dsc.data_ptr(), dq_I.data_ptr(),
+                              dw_I.data_ptr(), dk_I.data_ptr(), sh)
+        ibwd()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(nb):
+            ibwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_ib = e0.elapsed_time(e1) / nb
+        adds = sel * wl.d_I
+        backward["indexer_backward"] = {
+            "ms_per_group": round(ms_ib, 3),
+            "mfma_tflops": round(sel * 6.0 * wl.H_I * wl.d_I / (ms_ib / 1e3) / 1e12, 2),
+            "fp32_atomic_adds": int(adds),
+            "fp32_atomic_adds_per_s": round(adds / (ms_ib / 1e3) / 1e9, 1)}
+        if "fp32_atomic_adds_per_s_measured_peak" in backward:
+            backward["indexer_backward"]["frac_of_atomic_peak"] = round(
+                adds / (ms_ib / 1e3) / 1e9 / backward["fp32_atomic_adds_per_s_measured_peak"], 3)
+        del lse0, sel_sc, kl_loss, kl_dsc, dq_I, dw_I, dk_I
 
     # ---------------------------------------------------------------- per-layer indexing
     indexshare = None

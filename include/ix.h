@@ -170,6 +170,30 @@ ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const
                         int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,
                         float sm_scale, float *loss, float *dscores, hipStream_t stream);
 
+/*
+ * ix_indexer_bwd -- the KL objective's score gradient carried back into the indexer's own
+ * inputs (the twiscan post on GLM-5.2's IndexShare: the indexer learns from the attention
+ * distribution through a KL loss; the chain rule of the Stage-1 score form of "DeepSeek
+ * Sparse Attention").  For each query, with x_hj = q_I[h,:] . k_I[s_j,:] over the valid
+ * entries s_j of its selection (0 <= idx < min(kv_len, S_max)) and g_j = dscores:
+ *   dw[h]      = sum_j g_j max(0, x_hj)
+ *   dq_I[h,:]  = sum_j g_j w[h] [x_hj > 0] k_I[s_j,:]
+ *   dk_I[s_j,:] += sum_h g_j w[h] [x_hj > 0] q_I[h,:]
+ * Gradients are with respect to the decoded e4m3 values; the ReLU's step at x = 0 gets
+ * gradient 0, and the mask [x > 0] is decided exactly.
+ * a:       the indexer inputs of the forward (q_pos0 is not read: idx says what is kept).
+ * idx:     int32 [B, T, k] (ix_topk's output or any selection; invalid entries are skipped).
+ * dscores: fp32 [B, T, k] (ix_indexer_kl's dscores); ignored at invalid entries.
+ * dq_I:    fp32 [B, T, H_I, d_I], written.   dw: fp32 [B, T, H_I], written.
+ * dk_I:    fp32 [B, S_max, d_I], ADDED TO (float atomics, so the order of additions and the
+ *          last bits vary from run to run); the caller clears it first.
+ * Errors: as ix_topk for the indexer arguments and k, plus IX_ERR_INVALID for NULL idx,
+ * dscores or gradients.
+ */
+ix_status ix_indexer_bwd(const ix_indexer_args *a, int32_t k, const int32_t *idx,
+                         const float *dscores, float *dq_I, float *dw, float *dk_I,
+                         hipStream_t stream);
+
 /* Workspace bytes indexshare_group_fwd needs, for any n_layers: the selection's, or the
  * split partials of the attention of up to 8 layers, which run in one launch. */
 size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H_q,

@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl", "ix_peak_mfma_fp8", "ix_peak_copy",
+           "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl", "ix_indexer_bwd", "ix_peak_mfma_fp8", "ix_peak_copy",
            "ix_peak_gather", "ix_peak_atomic_add")
 
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH):
                                        c_size_t, c_void_p]
     L.sparse_attn_bwd.restype = c_int32
     L.sparse_attn_bwd.argtypes = [c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4
+    L.ix_indexer_bwd.restype = c_int32
+    L.ix_indexer_bwd.argtypes = [P(IndexerArgs), c_int32] + [c_void_p] * 6
     L.ix_indexer_kl.restype = c_int32
     L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
     L.ix_peak_mfma_fp8.restype = c_int32
@@ -386,6 +388,27 @@ def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=Non
                     _ptr(dout), B, T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(dq), _ptr(dK),
                     _ptr(dV), _stream())
     return dq, dK, dV
+
+
+def ix_indexer_bwd(args: IndexerArgs, k: int, idx: int, dscores: int, dq_I: int, dw: int,
+                   dk_I: int, stream: int = 0):
+    _check(load().ix_indexer_bwd(ctypes.byref(args), k, idx, dscores, dq_I, dw, dk_I, stream))
+
+
+def indexer_bwd(args: IndexerArgs, idx, dscores, device):
+    """(dq_I fp32 [B,T,H_I,d_I], dw fp32 [B,T,H_I], dk_I fp32 [B,S_max,d_I]): the indexer
+    inputs' gradients from d loss / d sel_scores (dk_I starts from zero here)."""
+    torch = _torch()
+    for t in (idx, dscores):
+        assert t.is_contiguous(), "indexer backward tensors must be contiguous"
+    assert dscores.dtype == torch.float32 and tuple(dscores.shape) == tuple(idx.shape)
+    B, T, H, D, S = args.B, args.T, args.H_I, args.d_I, args.S_max
+    dq = torch.empty((B, T, H, D), dtype=torch.float32, device=device)
+    dw = torch.empty((B, T, H), dtype=torch.float32, device=device)
+    dk = torch.zeros((B, S, D), dtype=torch.float32, device=device)
+    ix_indexer_bwd(args, idx.shape[2], _ptr(idx), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
+                   _stream())
+    return dq, dw, dk
 
 
 def indexer_kl(q, K, idx, lse, sel_scores, sm_scale, kv_len=None):

@@ -356,6 +356,23 @@ ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const
   return ok();
 }
 
+ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx,
+                         const float* dscores, float* dq_I, float* dw, float* dk_I,
+                         hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_indexer(a, &empty);
+  if (st != IX_OK) return st;
+  st = check_k(k);
+  if (st != IX_OK) return st;
+  if (empty) return ok();
+  if (!idx || !dscores || !dq_I || !dw || !dk_I)
+    return fail(IX_ERR_INVALID, "NULL idx, dscores, dq_I, dw or dk_I pointer");
+  hipError_t e = ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
+                                        a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, stream);
+  if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");
+  return ok();
+}
+
 ix_status ix_peak_mfma_fp8(const void* operands, int32_t valu_per_mfma, int32_t blocks,
                            int32_t iters, float* out, hipStream_t stream) {
   if (!operands || !out) return fail(IX_ERR_INVALID, "NULL operands or out");

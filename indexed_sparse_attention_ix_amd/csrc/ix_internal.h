@@ -75,6 +75,10 @@ hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
                              const int32_t* kv_len, const float* lse, const float* sel_scores,
                              int B, int T, int S_max, int H_q, int H_kv, int d, int k,
                              float sm_scale, float* loss, float* dscores, hipStream_t stream);
+hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float* w,
+                              const int32_t* kv_len, const int32_t* idx, const float* dscores,
+                              int B, int T, int S_max, int H_I, int d_I, int k, float* dq,
+                              float* dw, float* dk, hipStream_t stream);
 hipError_t launch_peak_mfma(const void* operands, int valu_per_mfma, int blocks, int iters,
                             float* out, hipStream_t stream);
 hipError_t launch_peak_atomic(float* table, int64_t rows, const int32_t* idx, int64_t n,

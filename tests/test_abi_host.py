@@ -182,6 +182,23 @@ def test_indexer_kl_validation_codes():
     assert call(B=0) == bd.IX_OK and call(T=0, q=0) == bd.IX_OK
 
 
+def test_indexer_bwd_validation_codes():
+    def call(a=None, k=16, idx=FAKE, ds=FAKE, dq=FAKE, dw=FAKE, dk=FAKE):
+        return status_of(bd.ix_indexer_bwd, a if a is not None else args(), k, idx, ds, dq, dw, dk)
+
+    for name in ("idx", "ds", "dq", "dw", "dk"):
+        assert call(**{name: 0}) == bd.IX_ERR_INVALID, name
+    assert "NULL" in bd.ix_last_error()
+    assert call(a=args(w=0)) == bd.IX_ERR_INVALID
+    assert call(a=args(q=FAKE + 8)) == bd.IX_ERR_INVALID
+    assert call(a=args(d_I=96)) == bd.IX_ERR_UNSUPPORTED
+    assert call(a=args(H_I=6)) == bd.IX_ERR_UNSUPPORTED
+    assert call(k=0) == bd.IX_ERR_UNSUPPORTED and call(k=4096) == bd.IX_ERR_UNSUPPORTED
+    assert bd.load().ix_indexer_bwd(None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.IX_ERR_INVALID
+    # empty calls launch nothing
+    assert call(a=args(B=0, q=0, k=0, w=0, q_pos0=0, kv_len=0), idx=0, ds=0, dq=0, dw=0, dk=0) == bd.IX_OK
+
+
 def test_peak_validation_codes():
     assert status_of(bd.ix_peak_mfma_fp8, 0, 8, 1, 1, FAKE) == bd.IX_ERR_INVALID
     assert status_of(bd.ix_peak_mfma_fp8, FAKE, 6, 1, 1, FAKE) == bd.IX_ERR_INVALID
