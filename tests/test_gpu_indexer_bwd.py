@@ -21,50 +21,10 @@ import torch
 from indexed_sparse_attention_ix_amd import binding as bd
 from indexed_sparse_attention_ix_amd import synth
 from oracle import ix_oracle as O
-from parity_util import FP32_U, say
+from parity_util import abs_codes, check_indexer_bwd, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-MFMA_REL = 2.0 ** -13
-
-
-def _abs_codes(c):
-    return (np.asarray(c) & 0x7F).astype(np.uint8)
-
-
-def _oracle(qI, kI, w, idx, ds, kvl):
-    """Oracle gradients and their magnitude bounds for every row of every sequence."""
-    B, T = idx.shape[:2]
-    out = []
-    for b in range(B):
-        rows = list(range(T))
-        ref = O.indexer_backward_rows(qI, kI, w, idx[b], ds[b], b, rows, int(kvl[b]))
-        mag = O.indexer_backward_rows(_abs_codes(qI), _abs_codes(kI), np.abs(w), idx[b],
-                                      np.abs(ds[b]), b, rows, int(kvl[b]))
-        out.append((ref, mag))
-    return out
-
-
-def _check(got, qI, kI, w, idx, ds, kvl, extra=None):
-    """got = (dq, dw, dk) host arrays.  extra: optional per-sequence additive bounds
-    (dq, dw, dk) for errors that come in with dscores."""
-    dq, dw, dk = got
-    B, T, k = idx.shape
-    worst = [0.0, 0.0, 0.0]
-    for b, (ref, mag) in enumerate(_oracle(qI, kI, w, idx, ds, kvl)):
-        tols = (MFMA_REL + (64 + k) * FP32_U, MFMA_REL + (k + 2) * FP32_U,
-                MFMA_REL + (64 + T) * FP32_U)
-        for n, (g, r, m, tol) in enumerate(zip((dq[b], dw[b], dk[b]), ref, mag, tols)):
-            bound = tol * m + (extra[b][n] if extra is not None else 0.0)
-            err = np.abs(g.astype(np.float64) - r)
-            name = ("dq_I", "dw", "dk_I")[n]
-            bad = err > bound
-            assert not bad.any(), (f"{name} b={b}: {int(bad.sum())} entries out of tolerance; "
-                                   f"max err {err.max():.3e}, e.g. got {g[bad][:3]} ref {r[bad][:3]}")
-            with np.errstate(divide="ignore", invalid="ignore"):
-                ratio = np.where(m > 0, err / m, 0.0)
-            worst[n] = max(worst[n], float(ratio.max()) if ratio.size else 0.0)
-    say(f"  worst err / magnitude: dq {worst[0]:.2e}  dw {worst[1]:.2e}  dk {worst[2]:.2e}")
 
 
 def _run(qI, kI, w, kvl, idx, ds):
@@ -112,7 +72,7 @@ def test_indexer_bwd_ragged_64_heads_d128():
                                     past_kv=20)
     got = _run(qI, kI, w, kvl, idx, ds)
     assert np.all(got[0][1, 7] == 0) and np.all(got[1][1, 7] == 0)
-    _check(got, qI, kI, w, idx, ds, kvl)
+    check_indexer_bwd(got, qI, kI, w, idx, ds, kvl)
 
 
 def test_indexer_bwd_exact_zero_dots_partial_head_tile_d64():
@@ -125,13 +85,13 @@ def test_indexer_bwd_exact_zero_dots_partial_head_tile_d64():
     x0 = O.decode_e4m3(qI[0]) @ keys.T
     say(f"  exact zero dot products: {int((x0 == 0).sum())} of {x0.size}")
     assert (x0 == 0).sum() > 100
-    _check(_run(qI, kI, w, kvl, idx, ds), qI, kI, w, idx, ds, kvl)
+    check_indexer_bwd(_run(qI, kI, w, kvl, idx, ds), qI, kI, w, idx, ds, kvl)
 
 
 def test_indexer_bwd_full_k_and_few_heads():
     say("[ix_indexer_bwd] B=1 T=6 S=2300 H_I=4 d_I=128 k=2048")
     qI, kI, w, kvl, idx, ds = _case(203, 1, 6, 2300, 4, 128, 2048, [2300])
-    _check(_run(qI, kI, w, kvl, idx, ds), qI, kI, w, idx, ds, kvl)
+    check_indexer_bwd(_run(qI, kI, w, kvl, idx, ds), qI, kI, w, idx, ds, kvl)
 
 
 def test_indexer_bwd_zero_dscores_and_all_padding():
@@ -142,7 +102,7 @@ def test_indexer_bwd_zero_dscores_and_all_padding():
     assert not dq.any() and not dw.any() and not dk.any()
     dq, dw, dk = _run(qI, kI, w, kvl, idx, ds)
     assert not dq[1].any() and not dw[1].any() and not dk[1].any()
-    _check((dq, dw, dk), qI, kI, w, idx, ds, kvl)
+    check_indexer_bwd((dq, dw, dk), qI, kI, w, idx, ds, kvl)
 
 
 def test_indexer_bwd_training_chain_exact_scores():
@@ -203,9 +163,9 @@ def test_indexer_bwd_training_chain_exact_scores():
         e = np.exp(s - s.max())
         pred = e / e.sum()
         eps[t, v] = 2e-5 * (1 + L) * np.maximum(pred, np.abs(pred - ref_ds[t, v])) + 1e-7
-    prop = O.indexer_backward_rows(_abs_codes(qI_h), _abs_codes(kI_h), np.abs(w_h), ref_idx,
+    prop = O.indexer_backward_rows(abs_codes(qI_h), abs_codes(kI_h), np.abs(w_h), ref_idx,
                                    eps, 0, rows, S)
     got_ds = dsc[0].cpu().numpy()
     assert np.all(np.abs(got_ds - ref_ds) <= eps), "dscores out of the KL tolerance"
-    _check(got, qI_h, kI_h, w_h, ref_idx[None].astype(np.int32), ref_ds[None], kvl.numpy(),
+    check_indexer_bwd(got, qI_h, kI_h, w_h, ref_idx[None].astype(np.int32), ref_ds[None], kvl.numpy(),
            extra=[prop])

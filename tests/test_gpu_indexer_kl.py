@@ -13,9 +13,8 @@ import torch
 
 from indexed_sparse_attention_ix_amd import binding as bd
 from indexed_sparse_attention_ix_amd import synth
-from indexed_sparse_attention_ix_amd.workloads import Workload
 from oracle import ix_oracle as O
-from parity_util import say
+from parity_util import kl_tolerance, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -120,25 +119,44 @@ def test_kl_dense_lse_and_k_not_multiple_of_4():
 
 
 def test_kl_on_the_indexer_selection():
-    """The training chain: ix_topk's selection and kept scores, the forward's lse, the KL."""
-    wl = Workload(name="kl_chain", B=1, T=64, S=1500, pos0=1436, H_I=16, d_I=128, k=256,
-                  H_q=16, H_kv=1, d=128, layers=1, seed=94, qkv_std=1.0)
-    say("[ix_indexer_kl] ix_topk -> sparse_attn_fwd -> ix_indexer_kl, T=64 S=1500 k=256")
-    ind = synth.indexer_inputs(wl, device=DEV)
-    idx, sel = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k,
-                       with_scores=True)
-    g = torch.Generator(device="cpu").manual_seed(95)
-    q = torch.randn(1, wl.T, 16, 128, generator=g).to(torch.bfloat16)
-    K = (torch.randn(1, wl.S, 1, 128, generator=g) * 128 ** -0.5).to(torch.bfloat16)
-    V = torch.randn(1, wl.S, 1, 128, generator=g).to(torch.bfloat16)
-    scale = 128 ** -0.5
-    dq, dK, dV = (x.to(DEV) for x in (q, K, V))
-    _, lse = bd.sparse_attention(dq, dK, dV, idx, scale, kv_len=ind["kv_len"], with_lse=True)
-    # the kept scores are of order 1e2-1e3: a temperature keeps the prediction soft
-    temp = 1.0 / float(sel[sel > -float("inf")].std())
-    sel_t = (sel * temp).contiguous()
-    loss, dsc = bd.indexer_kl(dq, dK, idx, lse, sel_t, scale, kv_len=ind["kv_len"])
+    """The training chain ix_topk -> sparse_attn_fwd (lse) -> ix_indexer_kl against the
+    oracle's own chain.  Indexer codes in {0, +-0.5, +-1} and head weights that are multiples
+    of 1/64 make every score exact in fp32, so both sides keep the same keys (ties to the
+    lower index) with the same kept scores."""
+    B, T, S, H_I, d_I, k, pos0 = 1, 64, 1500, 16, 128, 256, 1436
+    say(f"[ix_indexer_kl] ix_topk -> sparse_attn_fwd -> ix_indexer_kl, T={T} S={S} k={k}")
+    g = torch.Generator(device="cpu").manual_seed(94)
+    vals = torch.tensor([0.0, 0.5, -0.5, 1.0, -1.0])
+    qI = synth.encode_e4m3(vals[torch.randint(5, (B, T, H_I, d_I), generator=g)])
+    kI = synth.encode_e4m3(vals[torch.randint(5, (B, S, d_I), generator=g)])
+    w = torch.randint(-16, 17, (B, T, H_I), generator=g).float() / 64.0
+    p0 = torch.tensor([pos0], dtype=torch.int32)
+    kvl = torch.tensor([S], dtype=torch.int32)
+    q = torch.randn(1, T, 16, 128, generator=g).to(torch.bfloat16)
+    K = (torch.randn(1, S, 1, 128, generator=g) * 128 ** -0.5).to(torch.bfloat16)
+    V = torch.randn(1, S, 1, 128, generator=g).to(torch.bfloat16)
+    scale, temp = 128 ** -0.5, 0.25
+    dv = [x.to(DEV) for x in (qI, kI, w, p0, kvl, q, K, V)]
+    idx, sel = bd.topk(*dv[:5], k, with_scores=True)
+    _, lse = bd.sparse_attention(dv[5], dv[6], dv[7], idx, scale, kv_len=dv[4], with_lse=True)
+    loss, dsc = bd.indexer_kl(dv[5], dv[6], idx, lse, (sel * temp).contiguous(), scale,
+                              kv_len=dv[4])
     torch.cuda.synchronize()
-    kvl = ind["kv_len"].cpu().numpy()
-    _check(loss.cpu().numpy(), dsc.cpu().numpy(), idx.cpu().numpy(), sel_t.cpu().numpy(), q, K,
-           kvl, scale)
+    rows = list(range(T))
+    ref_idx, ref_sc = O.topk_rows(qI.numpy(), kI.numpy(), w.numpy().astype(np.float64),
+                                  p0.numpy(), kvl.numpy(), 0, rows, k, return_scores=True)
+    assert np.array_equal(idx[0].cpu().numpy(), ref_idx), "selection differs"
+    kept = np.full((T, k), -np.inf)
+    for t in rows:
+        v = ref_idx[t] >= 0
+        kept[t, v] = ref_sc[t][ref_idx[t][v]]
+    got_sel = sel[0].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got_sel, kept), "kept scores differ"
+    qb, Kb = _bits(q), _bits(K)
+    ref_l, ref_d = O.indexer_kl_rows(qb, Kb, ref_idx, kept * temp, 0, rows, scale, S)
+    qf, Kf = O.decode_bf16(qb)[0], O.decode_bf16(Kb)[0]
+    got_l, got_d = loss[0].cpu().numpy(), dsc[0].cpu().numpy()
+    for t in rows:
+        eps, bound = kl_tolerance(qf[t], Kf, ref_idx[t], kept[t] * temp, ref_d[t], scale)
+        assert abs(got_l[t] - ref_l[t]) <= eps + 1e-5 * abs(ref_l[t]), f"loss t={t}"
+        assert np.all(np.abs(got_d[t] - ref_d[t]) <= bound), f"dscores t={t}"

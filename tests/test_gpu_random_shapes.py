@@ -2,10 +2,12 @@
 indexer head dim 64/128, indexer heads any multiple of 4, GQA ratios 1..16, attention head
 dim 64/128, ragged kv_len (including 0), q_pos0 before the start and late in the cache, k
 below and above the visible count, batches large enough for key splits.  Every query row's
-selection is checked against the oracle (tie band) and every row's attention output on the
-GPU's own index tensor; grouped shapes go through indexshare_group_fwd.  The same shapes also
-run IndexPool (pool 4, k/4 blocks) and the training side (KL objective on the kept scores,
-attention gradients), each against the oracle."""
+selection is checked against the oracle (tie band), and every row where the GPU kept the
+oracle's own set has its attention output checked against the oracle on that selection;
+grouped shapes go through indexshare_group_fwd.  The same shapes also run IndexPool (pool 4,
+k/4 blocks) and the training side (the KL objective, the attention gradients and the indexer
+gradients, run on the oracle's selection and the oracle's kept scores), each against the
+oracle."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,9 @@ from indexed_sparse_attention_ix_amd import binding as bd
 from indexed_sparse_attention_ix_amd import synth
 from indexed_sparse_attention_ix_amd.workloads import Workload
 from oracle import ix_oracle as O
-from parity_util import bf16_to_f64, check_attention, check_index_row, say, to_host_attn, to_host_indexer
+from parity_util import (abs_codes, bf16_to_f64, check_attention, check_index_row,
+                         check_indexer_bwd, kl_tolerance, oracle_selection, say, to_host_attn,
+                         to_host_indexer)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -63,19 +67,26 @@ def test_random_shape(wl):
     torch.cuda.synchronize()
     h = to_host_indexer(ind)
     idx_np = idx.cpu().numpy()
+    ref_idx, same = [], []
     for b in range(wl.B):
         keys = O.decode_e4m3(h["k_I"][b])
-        for t in range(wl.T):
-            n = O.visible_count(h["q_pos0"][b], h["kv_len"][b], t)
-            sc = O.score_row(h["q_I"][b, t], keys[:n], h["w"][b, t], n)
-            check_index_row(idx_np[b, t], sc, wl.k, n, where=f"{wl.name} b={b} t={t}")
+        ns = [O.visible_count(h["q_pos0"][b], h["kv_len"][b], t) for t in range(wl.T)]
+        scs = [O.score_row(h["q_I"][b, t], keys[:ns[t]], h["w"][b, t], ns[t]) for t in range(wl.T)]
+        r, m = oracle_selection(idx_np[b], scs, wl.k, ns, where=f"{wl.name} b={b}")
+        ref_idx.append(r)
+        same.append(m)
+    n_same = int(sum(m.sum() for m in same))
+    assert n_same >= 0.9 * wl.B * wl.T, f"{wl.name}: only {n_same} rows kept the oracle's own set"
     for l, L in enumerate(layers):
         hl = to_host_attn(L)
         for b in range(wl.B):
-            ref_o, ref_l = O.sparse_attention_rows(hl["q"], hl["K"], hl["V"], idx_np[b], b,
+            ref_o, ref_l = O.sparse_attention_rows(hl["q"], hl["K"], hl["V"], ref_idx[b], b,
                                                    list(range(wl.T)), wl.sm_scale)
-            check_attention(bf16_to_f64(outs[l])[b], ref_o, lses[l].cpu().numpy()[b], ref_l,
-                            where=f"{wl.name} layer={l} b={b}")
+            m = same[b]
+            if not m.any():
+                continue
+            check_attention(bf16_to_f64(outs[l])[b][m], ref_o[m], lses[l].cpu().numpy()[b][m],
+                            ref_l[m], where=f"{wl.name} layer={l} b={b}")
 
 
 @pytest.mark.parametrize("wl", _configs()[:12], ids=lambda w: w.name)
@@ -109,29 +120,48 @@ def test_random_shape_indexpool(wl):
 
 @pytest.mark.parametrize("wl", _configs()[:12], ids=lambda w: w.name)
 def test_random_shape_training(wl):
-    """KL loss / score gradient per row within 2e-5 (1 + max |logit|) (+1e-5 relative for
-    the loss); dq per row and dK, dV per sequence within 2e-2 relative in norm plus a floor
-    of 1e-4 sqrt(n) times one term's size (bf16 P and dS in the products)."""
+    """The training side on the oracle's own selection and kept scores (ix_topk's selection
+    is checked against them first): KL loss and score gradient per row within the KL
+    tolerance; dq per row and dK, dV per sequence within 2e-2 relative in norm plus a floor
+    of 1e-4 sqrt(n) times one term's size (bf16 P and dS in the products); the indexer
+    gradients per entry (check_indexer_bwd) with the KL tolerance carried through."""
     say(f"[random shape training] {wl.name}: B={wl.B} T={wl.T} S={wl.S} H_q={wl.H_q} "
         f"H_kv={wl.H_kv} d={wl.d} k={wl.k}")
     ind = synth.indexer_inputs(wl, device=DEV)
     att = synth.attention_inputs(wl, layer=0, device=DEV)
     args = (ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"])
-    idx, sel = bd.topk(*args, wl.k, with_scores=True)
-    out, lse = bd.sparse_attention(att["q"], att["K"], att["V"], idx, wl.sm_scale,
+    idx = bd.topk(*args, wl.k)
+    torch.cuda.synchronize()
+    h = to_host_indexer(ind)
+    idx_np = idx.cpu().numpy()
+    ref_idx = np.full((wl.B, wl.T, wl.k), -1, dtype=np.int32)
+    kept = np.full((wl.B, wl.T, wl.k), -np.inf)
+    for b in range(wl.B):
+        keys = O.decode_e4m3(h["k_I"][b])
+        ns = [O.visible_count(h["q_pos0"][b], h["kv_len"][b], t) for t in range(wl.T)]
+        scs = [O.score_row(h["q_I"][b, t], keys[:ns[t]], h["w"][b, t], ns[t]) for t in range(wl.T)]
+        r, _ = oracle_selection(idx_np[b], scs, wl.k, ns, where=f"{wl.name} b={b}")
+        ref_idx[b] = r
+        for t in range(wl.T):
+            v = r[t] >= 0
+            kept[b, t, v] = scs[t][r[t][v]]
+    finite = kept[np.isfinite(kept)]
+    temp = 1.0 / max(float(finite.std()), 1e-3) if finite.size > 1 else 1.0
+    kept_t = (kept * temp).astype(np.float32)            # the scores both sides use
+    ridx = torch.from_numpy(ref_idx).to(DEV)
+    out, lse = bd.sparse_attention(att["q"], att["K"], att["V"], ridx, wl.sm_scale,
                                    kv_len=ind["kv_len"], with_lse=True)
-    finite = sel[sel > -float("inf")]
-    temp = 1.0 / max(float(finite.std()), 1e-3) if finite.numel() > 1 else 1.0
-    sel_t = (sel * temp).contiguous()
-    loss, dsc = bd.indexer_kl(att["q"], att["K"], idx, lse, sel_t, wl.sm_scale, kv_len=ind["kv_len"])
+    loss, dsc = bd.indexer_kl(att["q"], att["K"], ridx, lse, torch.from_numpy(kept_t).to(DEV),
+                              wl.sm_scale, kv_len=ind["kv_len"])
     g = torch.Generator(device="cpu").manual_seed(wl.seed)
     dout = torch.randn(att["q"].shape, generator=g).to(torch.bfloat16).to(DEV)
-    dq, dK, dV = bd.sparse_attention_backward(att["q"], att["K"], att["V"], idx, out, lse, dout,
+    dq, dK, dV = bd.sparse_attention_backward(att["q"], att["K"], att["V"], ridx, out, lse, dout,
                                               wl.sm_scale, kv_len=ind["kv_len"])
+    ib = bd.indexer_bwd(bd.indexer_args(*args), ridx, dsc, DEV)
     torch.cuda.synchronize()
     hl = to_host_attn(att)
-    kvl = ind["kv_len"].cpu().numpy()
-    idx_np, sc_np = idx.cpu().numpy(), sel_t.cpu().numpy().astype(np.float64)
+    kvl = h["kv_len"]
+    sc_np = kept_t.astype(np.float64)
     loss_np, dsc_np = loss.cpu().numpy(), dsc.cpu().numpy()
     dq_np, dK_np, dV_np = dq.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()
     dout_np = dout.float().cpu().numpy().astype(np.float64)
@@ -144,27 +174,28 @@ def test_random_shape_training(wl):
         assert err <= 2e-2 * np.linalg.norm(r_) + 1e-4 * term * np.sqrt(r_.size), \
             f"{wl.name} {what}: {err:.3e} vs {np.linalg.norm(r_):.3e}"
 
+    ref_ds = np.zeros((wl.B, wl.T, wl.k))
+    carried = []
     for b in range(wl.B):
-        ridx = np.where((idx_np[b] >= 0) & (idx_np[b] < kvl[b]), idx_np[b], -1)
-        rl, rd = O.indexer_kl_rows(hl["q"], hl["K"], idx_np[b], sc_np[b], b, list(range(wl.T)),
+        rl, rd = O.indexer_kl_rows(hl["q"], hl["K"], ref_idx[b], sc_np[b], b, list(range(wl.T)),
                                    wl.sm_scale, int(kvl[b]))
-        rq, rK, rV = O.sparse_attention_backward_rows(hl["q"], hl["K"], hl["V"], ridx, dout_np[b], b,
-                                                      list(range(wl.T)), wl.sm_scale)
+        ref_ds[b] = rd
+        rq, rK, rV = O.sparse_attention_backward_rows(hl["q"], hl["K"], hl["V"], ref_idx[b],
+                                                      dout_np[b], b, list(range(wl.T)), wl.sm_scale)
+        eps_ds = np.zeros((wl.T, wl.k))
         for t in range(wl.T):
-            v = ridx[t][ridx[t] >= 0]
-            L = float(np.abs(wl.sm_scale * np.einsum("jgd,hd->jgh", Kf[b, v], qf[b, t])).max()) if v.size else 0.0
-            eps = 2e-5 * (1 + L)
+            eps, bound = kl_tolerance(qf[b, t], Kf[b], ref_idx[b, t], sc_np[b, t], rd[t], wl.sm_scale)
+            eps_ds[t] = bound
             assert abs(loss_np[b, t] - rl[t]) <= eps + 1e-5 * abs(rl[t]), f"{wl.name} KL b={b} t={t}"
-            valid = ridx[t] >= 0
-            pred = np.zeros(wl.k)
-            if valid.any():
-                e = np.exp(sc_np[b, t][valid] - sc_np[b, t][valid].max())
-                pred[valid] = e / e.sum()
-            bound = eps * np.maximum(pred, np.abs(pred - rd[t])) + 1e-7
             assert np.all(np.abs(dsc_np[b, t] - rd[t]) <= bound), f"{wl.name} dscores b={b} t={t}"
-            if v.size == 0:
+            if (ref_idx[b, t] < 0).all():
                 assert np.all(dq_np[b, t] == 0)
             else:
                 close(dq_np[b, t], rq[t], f"dq b={b} t={t}")
         close(dK_np[b], rK, f"dK b={b}")
         close(dV_np[b], rV, f"dV b={b}")
+        carried.append(O.indexer_backward_rows(abs_codes(h["q_I"]), abs_codes(h["k_I"]),
+                                               np.abs(h["w"]), ref_idx[b], eps_ds, b,
+                                               list(range(wl.T)), int(kvl[b])))
+    check_indexer_bwd(tuple(x.cpu().numpy() for x in ib), h["q_I"], h["k_I"], h["w"], ref_idx,
+                      ref_ds, kvl, extra=carried, where=wl.name)

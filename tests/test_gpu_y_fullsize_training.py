@@ -1,15 +1,22 @@
 """GPU parity of the training side at the 32K prefill's full size (T = S = 32,768, k = 2048,
-16 query heads over one KV head), in the configuration the benchmark times: ix_topk with
-the kept scores, sparse_attn_fwd with lse, then ix_indexer_kl and sparse_attn_bwd.
+16 query heads over one KV head, 64 indexer heads), in the configuration the benchmark
+times: ix_topk with the kept scores, sparse_attn_fwd with lse, then ix_indexer_kl,
+sparse_attn_bwd and ix_indexer_bwd.
 
-Sampled queries are checked one by one against the oracle on the GPU's own index tensor
-(KL loss and score gradient; dq).  dK and dV sum over every query that kept a row, which the
-oracle cannot sample, so they are checked through two identities of the softmax chain rule
-that hold at any size: for each query and head the row gradients dl_j = p_j (dp_j - D) sum
-to zero, so sum_j dK_j = 0; and sum_j p_j = 1, so sum_j dV_j = the sum of dout over the
-(query, head) pairs with a non-empty selection.  Tolerances as the small-size tests: per
-query 2e-2 relative in norm for dq (bf16 P and dS in the products), KL as
-test_gpu_indexer_kl; the identities within 1e-2 of the gradients' own size.
+Sampled queries are checked one by one against the oracle's own chain: its selection (the
+GPU's is checked against the oracle's scores; rows where the GPU kept another, equally
+valid set are left out of the checks downstream), its kept scores (which the GPU's KL is
+given for those rows, so that both sides start from the same values), the KL loss and score
+gradient, the attention's dq, and the indexer's dq_I and dw with the KL tolerance carried
+through.  dK, dV and dk_I sum over every query that kept a row, which the oracle cannot
+sample, so they are checked through identities that hold at any size: for each query and
+head the row gradients dl_j = p_j (dp_j - D) sum to zero, so sum_j dK_j = 0; sum_j p_j = 1,
+so sum_j dV_j = the sum of dout over the (query, head) pairs with a non-empty selection; and
+the score is linear in w and positively homogeneous of degree 1 in q_I and in k_I, so
+<dk_I, k_I> = <dq_I, q_I> = <dw, w>.  Tolerances as the small-size tests: per query 2e-2
+relative in norm for dq (bf16 P and dS in the products), KL as test_gpu_indexer_kl, the
+indexer gradients per entry as test_gpu_indexer_bwd; the attention identities within 1e-2 of
+the gradients' own size, the indexer identity within 1e-3 of the sum of |terms|.
 """
 import numpy as np
 import pytest
@@ -19,10 +26,11 @@ from indexed_sparse_attention_ix_amd import binding as bd
 from indexed_sparse_attention_ix_amd import synth
 from indexed_sparse_attention_ix_amd.workloads import WORKLOADS
 from oracle import ix_oracle as O
-from parity_util import say
+from parity_util import (FP32_U, MFMA_REL, abs_codes, kl_tolerance, oracle_selection, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+TEMP = 0.01   # kept scores are large (hundreds); a fixed temperature keeps the prediction soft
 
 
 def test_prefill_32k_kl_and_backward_full_size():
@@ -35,59 +43,88 @@ def test_prefill_32k_kl_and_backward_full_size():
     idx, sel = bd.topk(*args, wl.k, with_scores=True)
     out, lse = bd.sparse_attention(att["q"], att["K"], att["V"], idx, wl.sm_scale,
                                    kv_len=ind["kv_len"], with_lse=True)
-    # kept scores are large (hundreds); a fixed temperature keeps the prediction soft
-    sel_t = (sel * 0.01).contiguous()
-    say("  ix_indexer_kl")
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(321)
+    rows = sorted(set([0, 1, wl.k - 2, wl.k - 1, wl.k, wl.T - 1]) |
+                  set(rng.choice(wl.T, size=26, replace=False).tolist()))
+    say(f"  oracle selection on {len(rows)} rows")
+    qI_h = ind["q_I"].cpu().numpy()
+    kI_h = ind["k_I"].cpu().numpy()
+    w_h = ind["w"].cpu().numpy()
+    pos0 = int(ind["q_pos0"][0].item())
+    kvl = int(ind["kv_len"][0].item())
+    keys = O.decode_e4m3(kI_h[0])
+    ns = [O.visible_count(pos0, kvl, t) for t in rows]
+    scs = [O.score_row(qI_h[0, t], keys[:n], w_h[0, t], n) for t, n in zip(rows, ns)]
+    ref_idx, same = oracle_selection(idx[0, rows].cpu().numpy(), scs, wl.k, ns, where="32K")
+    assert same.mean() >= 0.9, f"{int((~same).sum())} of {len(rows)} rows kept another tied set"
+    kept = np.full((len(rows), wl.k), -np.inf)
+    for i in range(len(rows)):
+        v = ref_idx[i] >= 0
+        kept[i, v] = scs[i][ref_idx[i][v]]
+    kept_t = (kept * TEMP).astype(np.float32)
+    # the GPU's KL gets the oracle's kept scores on the sampled rows where the sets agree
+    sel_t = (sel * TEMP).contiguous()
+    rows_same = [t for t, m in zip(rows, same) if m]
+    sel_t[0, rows_same] = torch.from_numpy(kept_t[same]).to(DEV)
+
+    say("  ix_indexer_kl, sparse_attn_bwd, ix_indexer_bwd")
     loss, dsc = bd.indexer_kl(att["q"], att["K"], idx, lse, sel_t, wl.sm_scale,
                               kv_len=ind["kv_len"])
     g = torch.Generator(device="cpu").manual_seed(7)
     dout = torch.randn(att["q"].shape, generator=g).to(torch.bfloat16).to(DEV)
-    say("  sparse_attn_bwd")
     dq, dK, dV = bd.sparse_attention_backward(att["q"], att["K"], att["V"], idx, out, lse, dout,
                                               wl.sm_scale, kv_len=ind["kv_len"])
+    dq_I, dw, dk_I = bd.indexer_bwd(bd.indexer_args(*args), idx, dsc, DEV)
     torch.cuda.synchronize()
 
-    rng = np.random.default_rng(321)
-    rows = sorted(set([0, 1, wl.k - 1, wl.k, wl.T - 1]) |
-                  set(rng.choice(wl.T, size=27, replace=False).tolist()))
-    say(f"  oracle on {len(rows)} rows")
+    say(f"  oracle chain on {int(same.sum())} rows")
+    sub = [i for i in range(len(rows)) if same[i]]
     q_bits = synth.bf16_bits(att["q"][0, rows])[None]
     K_bits = synth.bf16_bits(att["K"][0])[None]
     V_bits = synth.bf16_bits(att["V"][0])[None]
-    idx_r = idx[0, rows].cpu().numpy()
-    sc_r = sel_t[0, rows].cpu().numpy().astype(np.float64)
-    kvl = int(ind["kv_len"][0].item())
-
-    # KL: loss and score gradient per sampled query
-    ref_l, ref_d = O.indexer_kl_rows(q_bits, K_bits, idx_r, sc_r, 0, list(range(len(rows))),
-                                     wl.sm_scale, kvl)
+    ref_l, ref_d = O.indexer_kl_rows(q_bits, K_bits, ref_idx, kept_t.astype(np.float64), 0,
+                                     list(range(len(rows))), wl.sm_scale, kvl)
     got_l = loss[0, rows].cpu().numpy()
     got_d = dsc[0, rows].cpu().numpy()
     qf = O.decode_bf16(q_bits)[0]
     Kf = O.decode_bf16(K_bits)[0]
-    for i, t in enumerate(rows):
-        v = idx_r[i][(idx_r[i] >= 0) & (idx_r[i] < kvl)]
-        L = float(np.abs(wl.sm_scale * (Kf[v, 0, :] @ qf[i].T)).max())
-        eps = 2e-5 * (1 + L)
-        assert abs(got_l[i] - ref_l[i]) <= eps + 1e-5 * abs(ref_l[i]), f"KL loss t={t}"
-        valid = (idx_r[i] >= 0) & (idx_r[i] < kvl)
-        e = np.exp(sc_r[i][valid] - sc_r[i][valid].max())
-        pred = np.zeros(wl.k)
-        pred[valid] = e / e.sum()
-        bound = eps * np.maximum(pred, np.abs(pred - ref_d[i])) + 1e-7
-        assert np.all(np.abs(got_d[i] - ref_d[i]) <= bound), f"KL dscores t={t}"
+    eps_ds = np.zeros((len(rows), wl.k))
+    for i in sub:
+        eps, bound = kl_tolerance(qf[i], Kf, ref_idx[i], kept_t[i], ref_d[i], wl.sm_scale)
+        eps_ds[i] = bound
+        assert abs(got_l[i] - ref_l[i]) <= eps + 1e-5 * abs(ref_l[i]), f"KL loss t={rows[i]}"
+        assert np.all(np.abs(got_d[i] - ref_d[i]) <= bound), f"KL dscores t={rows[i]}"
 
-    # dq per sampled query
+    # attention dq per sampled query
     dout_r = dout[0, rows].float().cpu().numpy().astype(np.float64)
-    ref_dq, _, _ = O.sparse_attention_backward_rows(q_bits, K_bits, V_bits, idx_r, dout_r, 0,
+    ref_dq, _, _ = O.sparse_attention_backward_rows(q_bits, K_bits, V_bits, ref_idx, dout_r, 0,
                                                     list(range(len(rows))), wl.sm_scale)
     got_dq = dq[0, rows].cpu().numpy()
     term = wl.sm_scale * float(att["K"].float().abs().max() * dout.float().abs().max() *
                                att["V"].float().abs().max())
-    for i, t in enumerate(rows):
+    for i in sub:
         err = np.linalg.norm(got_dq[i] - ref_dq[i])
         assert err <= 2e-2 * np.linalg.norm(ref_dq[i]) + 1e-4 * term * np.sqrt(ref_dq[i].size), \
-            f"dq t={t}: {err:.3e} vs {np.linalg.norm(ref_dq[i]):.3e}"
+            f"dq t={rows[i]}: {err:.3e} vs {np.linalg.norm(ref_dq[i]):.3e}"
+
+    # indexer dq_I and dw per sampled query (dk_I through the identity below)
+    qI_r = qI_h[0, rows][None]
+    w_r = w_h[0, rows][None]
+    r_dq, r_dw, _ = O.indexer_backward_rows(qI_r, kI_h, w_r, ref_idx, ref_d, 0,
+                                            list(range(len(rows))), kvl)
+    m_dq, m_dw, _ = O.indexer_backward_rows(abs_codes(qI_r), abs_codes(kI_h), np.abs(w_r),
+                                            ref_idx, np.abs(ref_d), 0, list(range(len(rows))), kvl)
+    c_dq, c_dw, _ = O.indexer_backward_rows(abs_codes(qI_r), abs_codes(kI_h), np.abs(w_r),
+                                            ref_idx, eps_ds, 0, list(range(len(rows))), kvl)
+    g_dq = dq_I[0, rows].cpu().numpy().astype(np.float64)
+    g_dw = dw[0, rows].cpu().numpy().astype(np.float64)
+    for i in sub:
+        b_dq = (MFMA_REL + (64 + wl.k) * FP32_U) * m_dq[i] + c_dq[i]
+        b_dw = (MFMA_REL + (wl.k + 2) * FP32_U) * m_dw[i] + c_dw[i]
+        assert np.all(np.abs(g_dq[i] - r_dq[i]) <= b_dq), f"dq_I t={rows[i]}"
+        assert np.all(np.abs(g_dw[i] - r_dw[i]) <= b_dw), f"dw t={rows[i]}"
 
     # dK and dV through the identities
     dK64 = dK[0, :, 0].double()
@@ -99,5 +136,17 @@ def test_prefill_32k_kl_and_backward_full_size():
     sum_dk = dK64.sum(dim=0)
     assert float(sum_dk.norm()) <= 1e-2 * float(dK64.norm()), \
         f"sum of dK {float(sum_dk.norm()):.3e} vs |dK| {float(dK64.norm()):.3e}"
+
+    # the indexer gradients through <dk_I, k_I> = <dq_I, q_I> = <dw, w>
+    qv = synth.decode_e4m3_torch(ind["q_I"]).double()
+    kv = synth.decode_e4m3_torch(ind["k_I"]).double()
+    t_q = dq_I.double() * qv
+    t_k = dk_I.double() * kv
+    t_w = dw.double() * ind["w"].double()
+    e_q, e_k, e_w = float(t_q.sum()), float(t_k.sum()), float(t_w.sum())
+    scale_id = float(t_q.abs().sum() + t_k.abs().sum() + t_w.abs().sum())
+    assert abs(e_q - e_w) <= 1e-3 * scale_id and abs(e_k - e_w) <= 1e-3 * scale_id, \
+        f"indexer identity: <dq,q> {e_q:.6e} <dk,k> {e_k:.6e} <dw,w> {e_w:.6e}"
     say(f"  ok; |sum dV - want| / |want| = {float((got_dv - want_dv).norm() / want_dv.norm()):.2e}, "
-        f"|sum dK| / |dK| = {float(sum_dk.norm() / dK64.norm()):.2e}")
+        f"|sum dK| / |dK| = {float(sum_dk.norm() / dK64.norm()):.2e}, indexer identity "
+        f"{max(abs(e_q - e_w), abs(e_k - e_w)) / scale_id:.2e} of the sum of |terms|")
