@@ -169,3 +169,15 @@ def test_indexer_bwd_training_chain_exact_scores():
     assert np.all(np.abs(got_ds - ref_ds) <= eps), "dscores out of the KL tolerance"
     check_indexer_bwd(got, qI_h, kI_h, w_h, ref_idx[None].astype(np.int32), ref_ds[None], kvl.numpy(),
            extra=[prop])
+
+
+def test_indexer_bwd_deterministic_dq_dw():
+    """dq_I and dw are plain sums in a fixed order: bitwise equal from run to run.  dk_I is
+    accumulated with float atomics, so only its value (not its last bits) is fixed."""
+    say("[ix_indexer_bwd] determinism")
+    qI, kI, w, kvl, idx, ds = _case(206, 1, 24, 700, 64, 128, 160, [700])
+    a = _run(qI, kI, w, kvl, idx, ds)
+    b = _run(qI, kI, w, kvl, idx, ds)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    scale = np.abs(a[2]).max()
+    assert np.abs(a[2] - b[2]).max() <= 1e-5 * scale
