@@ -138,7 +138,8 @@ ix_status sparse_attn_fwd(const void *q, const void *kc, const void *vc, const i
  * dq:       fp32 [B, T, H_q, d], written (0 for a query with no valid entry).
  * dkc, dvc: fp32 [B, S_max, H_kv, d], ADDED TO (float atomics, so the order of additions
  *           and the last bits vary from run to run); the caller clears them first.
- * Errors: as sparse_attn_fwd, plus IX_ERR_INVALID for NULL lse, dout or gradients.
+ * Errors: as sparse_attn_fwd, plus IX_ERR_INVALID for NULL lse, dout or gradients, for
+ * out/dout not 16-byte aligned, or for lse or a gradient not 4-byte aligned.
  */
 ix_status sparse_attn_bwd(const void *q, const void *kc, const void *vc, const int32_t *idx,
                           const int32_t *kv_len, const void *out, const float *lse,
@@ -181,14 +182,15 @@ ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const
  *   dk_I[s_j,:] += sum_h g_j w[h] [x_hj > 0] q_I[h,:]
  * Gradients are with respect to the decoded e4m3 values; the ReLU's step at x = 0 gets
  * gradient 0, and the mask [x > 0] is decided exactly.
- * a:       the indexer inputs of the forward (q_pos0 is not read: idx says what is kept).
+ * a:       the indexer inputs of the forward, validated as for ix_topk (q_pos0 must be a
+ *          valid pointer but is not read: idx says what is kept).
  * idx:     int32 [B, T, k] (ix_topk's output or any selection; invalid entries are skipped).
  * dscores: fp32 [B, T, k] (ix_indexer_kl's dscores); ignored at invalid entries.
  * dq_I:    fp32 [B, T, H_I, d_I], written.   dw: fp32 [B, T, H_I], written.
  * dk_I:    fp32 [B, S_max, d_I], ADDED TO (float atomics, so the order of additions and the
  *          last bits vary from run to run); the caller clears it first.
  * Errors: as ix_topk for the indexer arguments and k, plus IX_ERR_INVALID for NULL idx,
- * dscores or gradients.
+ * dscores or gradients, or for w, idx, dscores or a gradient not 4-byte aligned.
  */
 ix_status ix_indexer_bwd(const ix_indexer_args *a, int32_t k, const int32_t *idx,
                          const float *dscores, float *dq_I, float *dw, float *dk_I,

@@ -35,6 +35,7 @@ ix_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Returns IX_OK and sets *empty when B*T == 0.
 ix_status check_indexer(const ix_indexer_args* a, bool* empty) {
@@ -328,6 +329,8 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
     return fail(IX_ERR_INVALID, "NULL lse, dout or gradient pointer");
   if (!aligned16(out) || !aligned16(dout))
     return fail(IX_ERR_INVALID, "bf16 out/dout base pointers must be 16-byte aligned");
+  if (!aligned4(lse) || !aligned4(dq) || !aligned4(dkc) || !aligned4(dvc))
+    return fail(IX_ERR_INVALID, "fp32 lse and gradient pointers must be 4-byte aligned");
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
   hipError_t e = ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
@@ -367,6 +370,9 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
   if (empty) return ok();
   if (!idx || !dscores || !dq_I || !dw || !dk_I)
     return fail(IX_ERR_INVALID, "NULL idx, dscores, dq_I, dw or dk_I pointer");
+  if (!aligned4(a->w) || !aligned4(idx) || !aligned4(dscores) || !aligned4(dq_I) || !aligned4(dw) ||
+      !aligned4(dk_I))
+    return fail(IX_ERR_INVALID, "w, idx, dscores and gradient pointers must be 4-byte aligned");
   hipError_t e = ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
                                         a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, stream);
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");

@@ -182,6 +182,29 @@ def test_indexer_kl_validation_codes():
     assert call(B=0) == bd.IX_OK and call(T=0, q=0) == bd.IX_OK
 
 
+def test_attention_bwd_validation_codes():
+    ok = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, kvl=FAKE, out=FAKE, lse=FAKE, dout=FAKE, B=2,
+              T=3, S=64, H_q=16, H_kv=1, d=128, k=16, scale=0.1, dq=FAKE, dk=FAKE, dv=FAKE)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return status_of(bd.sparse_attn_bwd, a["q"], a["kc"], a["vc"], a["idx"], a["kvl"], a["out"],
+                         a["lse"], a["dout"], a["B"], a["T"], a["S"], a["H_q"], a["H_kv"], a["d"],
+                         a["k"], a["scale"], a["dq"], a["dk"], a["dv"])
+
+    for name in ("q", "kc", "vc", "idx", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert call(**{name: 0}) == bd.IX_ERR_INVALID, name
+    for name in ("q", "kc", "vc", "out", "dout"):
+        assert call(**{name: FAKE + 4}) == bd.IX_ERR_INVALID, name      # bf16: 16-byte aligned
+    for name in ("lse", "dq", "dk", "dv"):
+        assert call(**{name: FAKE + 2}) == bd.IX_ERR_INVALID, name      # fp32: 4-byte aligned
+    assert call(scale=float("inf")) == bd.IX_ERR_INVALID
+    assert call(k=0) == bd.IX_ERR_UNSUPPORTED and call(d=96) == bd.IX_ERR_UNSUPPORTED
+    assert call(H_q=12, H_kv=8) == bd.IX_ERR_UNSUPPORTED
+    assert call(B=0, q=0, kc=0, vc=0, idx=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0) == bd.IX_OK
+
+
 def test_indexer_bwd_validation_codes():
     def call(a=None, k=16, idx=FAKE, ds=FAKE, dq=FAKE, dw=FAKE, dk=FAKE):
         return status_of(bd.ix_indexer_bwd, a if a is not None else args(), k, idx, ds, dq, dw, dk)
@@ -190,6 +213,9 @@ def test_indexer_bwd_validation_codes():
         assert call(**{name: 0}) == bd.IX_ERR_INVALID, name
     assert "NULL" in bd.ix_last_error()
     assert call(a=args(w=0)) == bd.IX_ERR_INVALID
+    for name in ("idx", "ds", "dq", "dw", "dk"):
+        assert call(**{name: FAKE + 2}) == bd.IX_ERR_INVALID, name
+    assert call(a=args(w=FAKE + 2)) == bd.IX_ERR_INVALID
     assert call(a=args(q=FAKE + 8)) == bd.IX_ERR_INVALID
     assert call(a=args(d_I=96)) == bd.IX_ERR_UNSUPPORTED
     assert call(a=args(H_I=6)) == bd.IX_ERR_UNSUPPORTED
