@@ -552,22 +552,39 @@ def main():
         dK = torch.zeros((wl.B, wl.S, wl.H_kv, wl.d), dtype=torch.float32, device=dev)
         dV = torch.zeros_like(dK)
 
-        def bwd():
+        # two forms: fp32 atomics (no workspace), and the atomic-free one (inverted
+        # selection, per-pair bf16 rows, key-major sums) in passes that fit a 32 GiB workspace
+        per_row = bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, 2) - \
+            bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, 1)
+        rows_pp = int(max(1, min(wl.B * wl.T, (32 << 30) // max(per_row, 1))))
+        bws_n = bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, rows_pp)
+        bws = torch.empty(bws_n, dtype=torch.uint8, device=dev)
+
+        def bwd(use_ws):
             bd.sparse_attn_bwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(),
                                op[0], lse0.data_ptr(), dout.data_ptr(), wl.B, wl.T, wl.S, wl.H_q,
                                wl.H_kv, wl.d, wl.k, wl.sm_scale, dq.data_ptr(), dK.data_ptr(),
-                               dV.data_ptr(), sh)
-        bwd()
-        torch.cuda.synchronize()
+                               dV.data_ptr(), bws.data_ptr() if use_ws else 0,
+                               bws_n if use_ws else 0, sh)
         nb = max(2, min(reps, 5))
-        e0.record(stream)
-        for _ in range(nb):
-            bwd()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_b = e0.elapsed_time(e1) / nb
+        ms_form = {}
+        for use_ws in (False, True):
+            bwd(use_ws)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(nb):
+                bwd(use_ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_form[use_ws] = e0.elapsed_time(e1) / nb
+        del bws
+        ms_b = ms_form[False]
         bflops = sel * 10.0 * wl.H_q * wl.d   # S, dP, dq, dK, dV: 2 H_q d flop each per pair
-        backward = {"ms_per_layer": round(ms_b, 3), "bf16_tflops": round(bflops / (ms_b / 1e3) / 1e12, 2),
+        backward = {"ms_per_layer": round(min(ms_form.values()), 3),
+                    "ms_per_layer_atomics": round(ms_form[False], 3),
+                    "ms_per_layer_atomic_free": round(ms_form[True], 3),
+                    "atomic_free_rows_per_pass": rows_pp,
+                    "bf16_tflops": round(bflops / (ms_b / 1e3) / 1e12, 2),
                     "gathered_GB_per_s": round(sel * 2.0 * wl.d * 2 * wl.H_kv / (ms_b / 1e3) / 1e9, 1),
                     "fp32_atomic_adds": int(sel * 2 * wl.H_kv * wl.d)}
         del dout, dq, dK, dV

@@ -70,7 +70,7 @@ typedef struct ix_indexer_args {
 } ix_indexer_args;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define IX_ABI_VERSION 1
+#define IX_ABI_VERSION 2
 int32_t ix_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
@@ -136,16 +136,31 @@ ix_status sparse_attn_fwd(const void *q, const void *kc, const void *vc, const i
  * q, kc, vc, idx, kv_len, B..sm_scale: as passed to sparse_attn_fwd; out and lse: its
  * outputs for these inputs (lse is required); dout: bf16 [B, T, H_q, d].
  * dq:       fp32 [B, T, H_q, d], written (0 for a query with no valid entry).
- * dkc, dvc: fp32 [B, S_max, H_kv, d], ADDED TO (float atomics, so the order of additions
- *           and the last bits vary from run to run); the caller clears them first.
+ * dkc, dvc: fp32 [B, S_max, H_kv, d], ADDED TO; the caller clears them first.  The order
+ *           of the additions, and so the last bits, vary from run to run.
+ * ws, ws_bytes: NULL and 0 -> dK / dV rows are added with fp32 atomics, 2 d per selected
+ *           pair.  A workspace (16-byte aligned, at least sparse_attn_bwd_workspace_bytes(...,
+ *           1) bytes, contents clobbered) -> no atomics: the query rows are taken in passes
+ *           of as many rows as the workspace holds; each pass inverts the selection (pairs
+ *           listed per key), writes every pair's dV and dK rows rounded to bf16, and sums
+ *           them per key in fp32.
  * Errors: as sparse_attn_fwd, plus IX_ERR_INVALID for NULL lse, dout or gradients, for
- * out/dout not 16-byte aligned, or for lse or a gradient not 4-byte aligned.
+ * out/dout not 16-byte aligned, for lse or a gradient not 4-byte aligned, or for a
+ * misaligned workspace; IX_ERR_WORKSPACE for a workspace below one row's need, or ws_bytes
+ * without a workspace.
  */
 ix_status sparse_attn_bwd(const void *q, const void *kc, const void *vc, const int32_t *idx,
                           const int32_t *kv_len, const void *out, const float *lse,
                           const void *dout, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
                           int32_t H_kv, int32_t d, int32_t k, float sm_scale, float *dq,
-                          float *dkc, float *dvc, hipStream_t stream);
+                          float *dkc, float *dvc, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for sparse_attn_bwd's atomic-free form in passes of rows_per_pass query
+ * rows (clamped to B * T): the per-key offsets and cursors (B * S_max + 1 each), the
+ * inverted selection (4 bytes per pair) and the pairs' bf16 dV | dK rows (4 d H_kv bytes
+ * per pair).  0 on invalid arguments. */
+size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int32_t H_kv,
+                                       int32_t d, int32_t k, int32_t rows_per_pass);
 
 /*
  * ix_indexer_kl -- the indexer's training objective (the twiscan post on GLM-5.2's

@@ -20,7 +20,7 @@ from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 1  # IX_ABI_VERSION of include/ix.h
+ABI_VERSION = 2  # IX_ABI_VERSION of include/ix.h
 IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
                 -3: "IX_ERR_WORKSPACE", -4: "IX_ERR_HIP"}
@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd", "ix_indexer_kl", "ix_indexer_bwd", "ix_peak_mfma_fp8", "ix_peak_copy",
+           "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "ix_indexer_kl", "ix_indexer_bwd", "ix_peak_mfma_fp8", "ix_peak_copy",
            "ix_peak_gather", "ix_peak_atomic_add")
 
 
@@ -83,7 +83,10 @@ def load(path: str = LIB_PATH):
                                        c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                        c_size_t, c_void_p]
     L.sparse_attn_bwd.restype = c_int32
-    L.sparse_attn_bwd.argtypes = [c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4
+    L.sparse_attn_bwd.argtypes = ([c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4 +
+                                  [c_size_t, c_void_p])
+    L.sparse_attn_bwd_workspace_bytes.restype = c_size_t
+    L.sparse_attn_bwd_workspace_bytes.argtypes = [c_int32] * 7
     L.ix_indexer_bwd.restype = c_int32
     L.ix_indexer_bwd.argtypes = [P(IndexerArgs), c_int32] + [c_void_p] * 6
     L.ix_indexer_kl.restype = c_int32
@@ -187,9 +190,13 @@ def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I
 
 
 def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_kv, d, k,
-                    sm_scale, dq, dkc, dvc, stream=0):
+                    sm_scale, dq, dkc, dvc, ws=0, ws_bytes=0, stream=0):
     _check(load().sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q,
-                                  H_kv, d, k, sm_scale, dq, dkc, dvc, stream))
+                                  H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes, stream))
+
+
+def sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass):
+    return load().sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass)
 
 
 def ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream=0):
@@ -372,9 +379,12 @@ def topk_pooled(q_I, k_pooled, w, q_pos0, kv_len, S_max, pool, k_blocks, ws=None
     return idx
 
 
-def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=None):
+def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=None,
+                              rows_per_pass=None):
     """(dq fp32 [B,T,H_q,d], dK fp32 [B,S,H_kv,d], dV fp32 [B,S,H_kv,d]) of
-    sparse_attention(q, K, V, idx) for the given dout (out, lse: its forward outputs)."""
+    sparse_attention(q, K, V, idx) for the given dout (out, lse: its forward outputs).
+    rows_per_pass: None adds dK / dV with atomics; a row count takes the atomic-free form
+    with a workspace for passes of that many query rows."""
     torch = _torch()
     B, T, H_q, d = q.shape
     S, H_kv = K.shape[1], K.shape[2]
@@ -384,9 +394,13 @@ def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=Non
     dq = torch.empty((B, T, H_q, d), dtype=torch.float32, device=q.device)
     dK = torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q.device)
     dV = torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q.device)
+    ws, nb = None, 0
+    if rows_per_pass is not None:
+        nb = sparse_attn_bwd_workspace_bytes(B, T, S, H_kv, d, k, rows_per_pass)
+        ws = workspace(nb, q.device)
     sparse_attn_bwd(_ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(kv_len), _ptr(out), _ptr(lse),
                     _ptr(dout), B, T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(dq), _ptr(dK),
-                    _ptr(dV), _stream())
+                    _ptr(dV), _ptr(ws) if ws is not None else 0, nb, _stream())
     return dq, dK, dV
 
 

@@ -1,3 +1,4 @@
+#include <algorithm>
 // C ABI of libix: argument validation, workspace sizing, dispatch, error reporting,
 // and the IndexShare group driver ("IndexShare: Amortizing the Indexer" in "GLM 5.2:
 // How Four Co-Designed Mechanisms Beat Raw Scale", Part II: the selection runs once
@@ -315,11 +316,21 @@ ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_block
   return ok();
 }
 
+size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int32_t H_kv,
+                                       int32_t d, int32_t k, int32_t rows_per_pass) {
+  bool empty = false;
+  if (check_attn_shape(B, T, S_max, H_kv, H_kv, d, k, &empty) != IX_OK || empty) return 0;
+  if (rows_per_pass < 1) return 0;
+  const int64_t rows = std::min<int64_t>(rows_per_pass, (int64_t)B * T);
+  if (rows * k > ((int64_t)1 << 31)) return 0;
+  return ix::attn_bwd_workspace_bytes(B, S_max, H_kv, d, k, rows);
+}
+
 ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                           const int32_t* kv_len, const void* out, const float* lse,
                           const void* dout, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
                           int32_t H_kv, int32_t d, int32_t k, float sm_scale, float* dq,
-                          float* dkc, float* dvc, hipStream_t stream) {
+                          float* dkc, float* dvc, void* ws, size_t ws_bytes, hipStream_t stream) {
   bool empty = false;
   ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
   if (st != IX_OK) return st;
@@ -333,8 +344,17 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
     return fail(IX_ERR_INVALID, "fp32 lse and gradient pointers must be 4-byte aligned");
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  if (ws) {
+    if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (ix::attn_bwd_rows_per_pass(B, T, S_max, H_kv, d, k, ws_bytes) < 1)
+      return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
+                  ws_bytes, ix::attn_bwd_workspace_bytes(B, S_max, H_kv, d, k, 1));
+  } else if (ws_bytes != 0) {
+    return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
+  }
   hipError_t e = ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
-                                            H_q, H_kv, d, k, sm_scale, dq, dkc, dvc, stream);
+                                            H_q, H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes,
+                                            stream);
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_bwd launch");
   return ok();
 }

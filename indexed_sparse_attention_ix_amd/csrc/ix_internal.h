@@ -66,11 +66,13 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
                                      float* const* lse, const AttnPlan& pl, void* ws,
                                      hipStream_t stream);
 constexpr int kAttnLayersPerLaunch = 8;
+size_t attn_bwd_workspace_bytes(int B, int S_max, int H_kv, int d, int k, int64_t rows_per_pass);
+int64_t attn_bwd_rows_per_pass(int B, int T, int S_max, int H_kv, int d, int k, size_t ws_bytes);
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,
                                   int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
-                                  hipStream_t stream);
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
                              const int32_t* kv_len, const float* lse, const float* sel_scores,
                              int B, int T, int S_max, int H_q, int H_kv, int d, int k,

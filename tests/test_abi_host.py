@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_clean_error():
-    assert bd.ix_abi_version() == 1
+    assert bd.ix_abi_version() == bd.ABI_VERSION == 2
 
 
 FAKE = 1 << 20  # 16-byte aligned non-null stand-in address; never dereferenced on failure
@@ -203,6 +203,18 @@ def test_attention_bwd_validation_codes():
     assert call(k=0) == bd.IX_ERR_UNSUPPORTED and call(d=96) == bd.IX_ERR_UNSUPPORTED
     assert call(H_q=12, H_kv=8) == bd.IX_ERR_UNSUPPORTED
     assert call(B=0, q=0, kc=0, vc=0, idx=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0) == bd.IX_OK
+    # the atomic-free form's workspace
+    a = [ok[n] for n in ("q", "kc", "vc", "idx", "kvl", "out", "lse", "dout", "B", "T", "S", "H_q",
+                         "H_kv", "d", "k", "scale", "dq", "dk", "dv")]
+    one = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 1)
+    six = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 6)
+    assert 0 < one < six
+    assert bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 100) == six   # clamped to B*T
+    assert bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 96, 16, 1) == 0
+    assert bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 0) == 0
+    assert status_of(bd.sparse_attn_bwd, *a, FAKE, one - 1) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.sparse_attn_bwd, *a, 0, one) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.sparse_attn_bwd, *a, FAKE + 8, one) == bd.IX_ERR_INVALID
 
 
 def test_indexer_bwd_validation_codes():

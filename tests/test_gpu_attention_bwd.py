@@ -32,8 +32,9 @@ def _close(g, ref, term, what):
         f"{what}: |err| {err:.3e} vs |ref| {scale:.3e}"
 
 
-def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=()):
-    say(f"[sparse_attn_bwd] B={B} T={T} S={S} H_q={H_q} H_kv={H_kv} d={d} k={k} seed={seed}")
+def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=(), rows_per_pass=None):
+    say(f"[sparse_attn_bwd] B={B} T={T} S={S} H_q={H_q} H_kv={H_kv} d={d} k={k} seed={seed} "
+        f"{'atomics' if rows_per_pass is None else f'key-major, {rows_per_pass} rows per pass'}")
     g = torch.Generator(device="cpu").manual_seed(seed)
     q = (torch.randn(B, T, H_q, d, generator=g) * 0.3).to(torch.bfloat16)
     K = (torch.randn(B, S, H_kv, d, generator=g) * 0.3).to(torch.bfloat16)
@@ -55,7 +56,7 @@ def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=()):
     scale = d ** -0.5
     out, lse = bd.sparse_attention(dq_, dK_, dV_, didx, scale, kv_len=dkvl, with_lse=True)
     gq, gK, gV = bd.sparse_attention_backward(dq_, dK_, dV_, didx, out, lse, dout.to(DEV), scale,
-                                              kv_len=dkvl)
+                                              kv_len=dkvl, rows_per_pass=rows_per_pass)
     torch.cuda.synchronize()
     gq, gK, gV = gq.cpu().numpy(), gK.cpu().numpy(), gV.cpu().numpy()
     term = scale * float(K.float().abs().max() * dout.float().abs().max() * V.float().abs().max())
@@ -75,14 +76,48 @@ def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=()):
         assert np.all(gK[b, untouched] == 0) and np.all(gV[b, untouched] == 0)
 
 
-def test_backward_gqa_ragged_d64():
+# None: dK / dV added with atomics; a row count: the atomic-free form (inverted selection,
+# per-pair rows, key-major sums), in passes of that many query rows
+MODES = [None, 1 << 20, 7]
+
+
+@pytest.mark.parametrize("rows_per_pass", MODES)
+def test_backward_gqa_ragged_d64(rows_per_pass):
     _run(B=2, T=40, S=300, H_q=8, H_kv=2, d=64, k=48, seed=71, kv_lens=[300, 170],
-         empty_rows={(0, 3)})
+         empty_rows={(0, 3)}, rows_per_pass=rows_per_pass)
 
 
-def test_backward_mqa_d128_many_chunks():
-    _run(B=1, T=64, S=4096, H_q=16, H_kv=1, d=128, k=256, seed=72)
+@pytest.mark.parametrize("rows_per_pass", MODES)
+def test_backward_mqa_d128_many_chunks(rows_per_pass):
+    _run(B=1, T=64, S=4096, H_q=16, H_kv=1, d=128, k=256, seed=72, rows_per_pass=rows_per_pass)
 
 
-def test_backward_k_not_a_multiple_of_4():
-    _run(B=1, T=33, S=500, H_q=16, H_kv=1, d=128, k=37, seed=73)
+@pytest.mark.parametrize("rows_per_pass", MODES)
+def test_backward_k_not_a_multiple_of_4(rows_per_pass):
+    _run(B=1, T=33, S=500, H_q=16, H_kv=1, d=128, k=37, seed=73, rows_per_pass=rows_per_pass)
+
+
+def test_backward_atomic_free_matches_atomics():
+    """The two forms sum the same fp32 products; the atomic-free one rounds each pair's rows
+    to bf16 first, so dK and dV agree to bf16 rounding of the terms, and dq is the same
+    computation (bitwise)."""
+    say("[sparse_attn_bwd] atomic-free vs atomics, hot keys shared by every query")
+    g = torch.Generator(device="cpu").manual_seed(74)
+    B, T, S, H_q, d, k = 2, 48, 600, 16, 128, 64
+    q = (torch.randn(B, T, H_q, d, generator=g) * 0.3).to(torch.bfloat16).to(DEV)
+    K = (torch.randn(B, S, 1, d, generator=g) * 0.3).to(torch.bfloat16).to(DEV)
+    V = torch.randn(B, S, 1, d, generator=g).to(torch.bfloat16).to(DEV)
+    dout = torch.randn(B, T, H_q, d, generator=g).to(torch.bfloat16).to(DEV)
+    rng = np.random.default_rng(74)
+    idx = np.stack([np.stack([np.sort(np.concatenate([np.arange(16), 16 + rng.choice(S - 16, k - 16,
+                                                                                  replace=False)]))
+                              for _ in range(T)]) for _ in range(B)]).astype(np.int32)
+    didx = torch.from_numpy(idx).to(DEV)
+    out, lse = bd.sparse_attention(q, K, V, didx, d ** -0.5, with_lse=True)
+    a = bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, d ** -0.5)
+    f = bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, d ** -0.5, rows_per_pass=10)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], f[0]), "dq differs"
+    for n, (x, y) in enumerate(zip(a[1:], f[1:])):
+        err = float((x - y).norm())
+        assert err <= 4e-3 * float(x.norm()), f"{('dK', 'dV')[n]}: {err:.3e} vs {float(x.norm()):.3e}"
