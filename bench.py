@@ -642,20 +642,34 @@ def main():
         dw_I = torch.empty((wl.B, wl.T, wl.H_I), dtype=torch.float32, device=dev)
         dk_I = torch.zeros((wl.B, wl.S, wl.d_I), dtype=torch.float32, device=dev)
 
-        def ibwd():
+        # the two forms, as for the attention: atomics, and atomic-free within 32 GiB
+        per_row_i = bd.ix_indexer_bwd_workspace_bytes(a, wl.k, 2) - bd.ix_indexer_bwd_workspace_bytes(a, wl.k, 1)
+        rows_i = int(max(1, min(wl.B * wl.T, (32 << 30) // max(per_row_i, 1))))
+        iws_n = bd.ix_indexer_bwd_workspace_bytes(a, wl.k, rows_i)
+        iws = torch.empty(iws_n, dtype=torch.uint8, device=dev)
+
+        def ibwd(use_ws):
             bd.ix_indexer_bwd(a, wl.k, idx.data_ptr(), kl_dsc.data_ptr(), dq_I.data_ptr(),
-                              dw_I.data_ptr(), dk_I.data_ptr(), sh)
-        ibwd()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(nb):
-            ibwd()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_ib = e0.elapsed_time(e1) / nb
+                              dw_I.data_ptr(), dk_I.data_ptr(), iws.data_ptr() if use_ws else 0,
+                              iws_n if use_ws else 0, sh)
+        ms_iform = {}
+        for use_ws in (False, True):
+            ibwd(use_ws)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(nb):
+                ibwd(use_ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_iform[use_ws] = e0.elapsed_time(e1) / nb
+        del iws
+        ms_ib = ms_iform[False]
         adds = sel * wl.d_I
         backward["indexer_backward"] = {
-            "ms_per_group": round(ms_ib, 3),
+            "ms_per_group": round(min(ms_iform.values()), 3),
+            "ms_per_group_atomics": round(ms_iform[False], 3),
+            "ms_per_group_atomic_free": round(ms_iform[True], 3),
+            "atomic_free_rows_per_pass": rows_i,
             "mfma_tflops": round(sel * 6.0 * wl.H_I * wl.d_I / (ms_ib / 1e3) / 1e12, 2),
             "fp32_atomic_adds": int(adds),
             "fp32_atomic_adds_per_s": round(adds / (ms_ib / 1e3) / 1e9, 1)}

@@ -70,7 +70,7 @@ typedef struct ix_indexer_args {
 } ix_indexer_args;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define IX_ABI_VERSION 2
+#define IX_ABI_VERSION 3
 int32_t ix_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
@@ -202,14 +202,27 @@ ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const
  * idx:     int32 [B, T, k] (ix_topk's output or any selection; invalid entries are skipped).
  * dscores: fp32 [B, T, k] (ix_indexer_kl's dscores); ignored at invalid entries.
  * dq_I:    fp32 [B, T, H_I, d_I], written.   dw: fp32 [B, T, H_I], written.
- * dk_I:    fp32 [B, S_max, d_I], ADDED TO (float atomics, so the order of additions and the
- *          last bits vary from run to run); the caller clears it first.
+ * dk_I:    fp32 [B, S_max, d_I], ADDED TO; the caller clears it first.  The order of the
+ *          additions, and so the last bits, vary from run to run.
+ * ws, ws_bytes: NULL and 0 -> dk_I rows are added with fp32 atomics, d_I per kept pair.  A
+ *          workspace (16-byte aligned, at least ix_indexer_bwd_workspace_bytes(a, k, 1)
+ *          bytes, contents clobbered) -> no atomics: passes of as many query rows as it
+ *          holds, each inverting the selection, writing every pair's dk_I row rounded to
+ *          bf16 and summing them per key in fp32 (as sparse_attn_bwd).
  * Errors: as ix_topk for the indexer arguments and k, plus IX_ERR_INVALID for NULL idx,
- * dscores or gradients, or for w, idx, dscores or a gradient not 4-byte aligned.
+ * dscores or gradients, for w, idx, dscores or a gradient not 4-byte aligned, or for a
+ * misaligned workspace; IX_ERR_WORKSPACE for a workspace below one row's need, or
+ * ws_bytes without a workspace.
  */
 ix_status ix_indexer_bwd(const ix_indexer_args *a, int32_t k, const int32_t *idx,
-                         const float *dscores, float *dq_I, float *dw, float *dk_I,
-                         hipStream_t stream);
+                         const float *dscores, float *dq_I, float *dw, float *dk_I, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for ix_indexer_bwd's atomic-free form in passes of rows_per_pass query
+ * rows (clamped to B * T): per-key offsets and cursors (B * S_max + 1 each), the inverted
+ * selection (4 bytes per pair) and the pairs' bf16 dk_I rows (2 d_I bytes per pair).
+ * 0 on invalid arguments. */
+size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t rows_per_pass);
 
 /* Workspace bytes indexshare_group_fwd needs, for any n_layers: the selection's, or the
  * split partials of the attention of up to 8 layers, which run in one launch. */

@@ -20,7 +20,7 @@ from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 2  # IX_ABI_VERSION of include/ix.h
+ABI_VERSION = 3  # IX_ABI_VERSION of include/ix.h
 IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
                 -3: "IX_ERR_WORKSPACE", -4: "IX_ERR_HIP"}
@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "ix_indexer_kl", "ix_indexer_bwd", "ix_peak_mfma_fp8", "ix_peak_copy",
+           "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "ix_indexer_kl", "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes", "ix_peak_mfma_fp8", "ix_peak_copy",
            "ix_peak_gather", "ix_peak_atomic_add")
 
 
@@ -88,7 +88,9 @@ def load(path: str = LIB_PATH):
     L.sparse_attn_bwd_workspace_bytes.restype = c_size_t
     L.sparse_attn_bwd_workspace_bytes.argtypes = [c_int32] * 7
     L.ix_indexer_bwd.restype = c_int32
-    L.ix_indexer_bwd.argtypes = [P(IndexerArgs), c_int32] + [c_void_p] * 6
+    L.ix_indexer_bwd.argtypes = [P(IndexerArgs), c_int32] + [c_void_p] * 6 + [c_size_t, c_void_p]
+    L.ix_indexer_bwd_workspace_bytes.restype = c_size_t
+    L.ix_indexer_bwd_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32]
     L.ix_indexer_kl.restype = c_int32
     L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
     L.ix_peak_mfma_fp8.restype = c_int32
@@ -405,13 +407,20 @@ def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=Non
 
 
 def ix_indexer_bwd(args: IndexerArgs, k: int, idx: int, dscores: int, dq_I: int, dw: int,
-                   dk_I: int, stream: int = 0):
-    _check(load().ix_indexer_bwd(ctypes.byref(args), k, idx, dscores, dq_I, dw, dk_I, stream))
+                   dk_I: int, ws: int = 0, ws_bytes: int = 0, stream: int = 0):
+    _check(load().ix_indexer_bwd(ctypes.byref(args), k, idx, dscores, dq_I, dw, dk_I, ws,
+                                 ws_bytes, stream))
 
 
-def indexer_bwd(args: IndexerArgs, idx, dscores, device):
+def ix_indexer_bwd_workspace_bytes(args: IndexerArgs, k: int, rows_per_pass: int) -> int:
+    return load().ix_indexer_bwd_workspace_bytes(ctypes.byref(args), k, rows_per_pass)
+
+
+def indexer_bwd(args: IndexerArgs, idx, dscores, device, rows_per_pass=None):
     """(dq_I fp32 [B,T,H_I,d_I], dw fp32 [B,T,H_I], dk_I fp32 [B,S_max,d_I]): the indexer
-    inputs' gradients from d loss / d sel_scores (dk_I starts from zero here)."""
+    inputs' gradients from d loss / d sel_scores (dk_I starts from zero here).
+    rows_per_pass: None adds dk_I with atomics; a row count takes the atomic-free form
+    with a workspace for passes of that many query rows."""
     torch = _torch()
     for t in (idx, dscores):
         assert t.is_contiguous(), "indexer backward tensors must be contiguous"
@@ -420,8 +429,12 @@ def indexer_bwd(args: IndexerArgs, idx, dscores, device):
     dq = torch.empty((B, T, H, D), dtype=torch.float32, device=device)
     dw = torch.empty((B, T, H), dtype=torch.float32, device=device)
     dk = torch.zeros((B, S, D), dtype=torch.float32, device=device)
+    ws, nb = None, 0
+    if rows_per_pass is not None:
+        nb = ix_indexer_bwd_workspace_bytes(args, idx.shape[2], rows_per_pass)
+        ws = workspace(nb, device)
     ix_indexer_bwd(args, idx.shape[2], _ptr(idx), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
-                   _stream())
+                   _ptr(ws), nb, _stream())
     return dq, dw, dk
 
 

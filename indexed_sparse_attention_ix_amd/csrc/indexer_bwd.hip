@@ -27,6 +27,8 @@
 //    fp32 atomics: 32 keys x d_I floats per chunk, which bound the kernel;
 //  * d loss / d x enters the bf16 products as a hi + lo pair of bf16 (residual below
 //    2^-17 relative); the e4m3 operands are exact in bf16.
+#include <algorithm>
+
 #include "ix_common.h"
 #include "ix_internal.h"
 
@@ -111,14 +113,14 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ kI, const float* __restrict__ w,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ idx,
     const float* __restrict__ dsc, int T, int S_max, int H, int k, float* __restrict__ dq,
-    float* __restrict__ dw, float* __restrict__ dk) {
+    float* __restrict__ dw, float* __restrict__ dk, int64_t row0, uint16_t* __restrict__ contrib) {
   __shared__ BwdSmem<DI> sm;
   constexpr int kPieces = DI / 16;   // 16-byte pieces per row
   constexpr int kDimTiles = DI / 16;
   constexpr int kOwnTiles = DI / 32;  // dk output tiles of one wave (of 2 * DI / 16)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int64_t row = blockIdx.x;  // b * T + t
+  const int64_t row = row0 + blockIdx.x;  // b * T + t
   const int b = (int)(row / T);
   int n_keys = kv_len[b];
   n_keys = n_keys < 0 ? 0 : (n_keys > S_max ? S_max : n_keys);
@@ -202,7 +204,8 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
         sm.ds[kk] = dsv;
         sm.key[kk] = s;
       }
-      if (!__syncthreads_or(s >= 0 && dsv != 0.f)) continue;  // nothing to add in this chunk
+      // nothing to add in this chunk (with a pair buffer every kept pair's row is written)
+      if (!__syncthreads_or(s >= 0 && (contrib != nullptr || dsv != 0.f))) continue;
     }
 
     // ---- x^T, the exact mask, d loss / d x, dw, and dq
@@ -288,6 +291,20 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
     }
     __syncthreads();
 
+    // ---- with a pair buffer: the chunk's rows in bf16, in pair order (summed per key later)
+    if (contrib) {
+      uint16_t* dst0 = contrib + ((size_t)(row - row0) * k + j0) * DI;
+      for (int r = 8 * wv; r < 8 * wv + 8; ++r) {
+        if (j0 + r >= k) break;
+        if (2 * lane < DI) {
+          const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)sm.dk[r][2 * lane]) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)sm.dk[r][2 * lane + 1]) << 16);
+          *reinterpret_cast<uint32_t*>(dst0 + (size_t)r * DI + 2 * lane) = v;
+        }
+      }
+      __syncthreads();
+      continue;
+    }
     // ---- add them to dk_I: wave w takes keys 8w .. 8w + 7, 64 consecutive floats per instruction
     for (int kk = 8 * wv; kk < 8 * wv + 8; ++kk) {
       const int s = sm.key[kk];
@@ -318,15 +335,36 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
 hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float* w,
                               const int32_t* kv_len, const int32_t* idx, const float* dscores,
                               int B, int T, int S_max, int H_I, int d_I, int k, float* dq,
-                              float* dw, float* dk, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)B * T)), block(kBwdThreads);
-  if (d_I == 128)
-    hipLaunchKernelGGL(indexer_bwd_kernel<128>, grid, block, 0, stream, qI, kI, w, kv_len, idx,
-                       dscores, T, S_max, H_I, k, dq, dw, dk);
-  else
-    hipLaunchKernelGGL(indexer_bwd_kernel<64>, grid, block, 0, stream, qI, kI, w, kv_len, idx,
-                       dscores, T, S_max, H_I, k, dq, dw, dk);
-  return hipGetLastError();
+                              float* dw, float* dk, void* ws, size_t ws_bytes, hipStream_t stream) {
+  auto grad = [&](int64_t row0, int64_t rows, uint16_t* contrib) {
+    const dim3 grid((unsigned)rows), block(kBwdThreads);
+    if (d_I == 128)
+      hipLaunchKernelGGL(indexer_bwd_kernel<128>, grid, block, 0, stream, qI, kI, w, kv_len, idx,
+                         dscores, T, S_max, H_I, k, dq, dw, dk, row0, contrib);
+    else
+      hipLaunchKernelGGL(indexer_bwd_kernel<64>, grid, block, 0, stream, qI, kI, w, kv_len, idx,
+                         dscores, T, S_max, H_I, k, dq, dw, dk, row0, contrib);
+  };
+  const int64_t all = (int64_t)B * T;
+  if (!ws) {
+    grad(0, all, nullptr);
+    return hipGetLastError();
+  }
+  // atomic-free: per pass, the inverted selection, pair rows of dk_I in bf16, key sums
+  const size_t row_bytes = (size_t)d_I * 2;
+  const int64_t per_pass = pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes);
+  if (per_pass < 1) return hipErrorInvalidValue;
+  const PairLayout L = pair_layout(B, S_max, k, per_pass, row_bytes);
+  uint16_t* contrib = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.contrib);
+  for (int64_t r0 = 0; r0 < all; r0 += per_pass) {
+    const int64_t rows = std::min(per_pass, all - r0);
+    hipError_t e = launch_pair_index(idx, kv_len, T, S_max, k, r0, rows, L, ws, stream);
+    if (e != hipSuccess) return e;
+    grad(r0, rows, contrib);
+    e = launch_pair_reduce(L, ws, d_I, 1, dk, dk + d_I / 2, d_I, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ix

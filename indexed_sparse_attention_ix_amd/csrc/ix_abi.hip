@@ -323,7 +323,7 @@ size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int3
   if (rows_per_pass < 1) return 0;
   const int64_t rows = std::min<int64_t>(rows_per_pass, (int64_t)B * T);
   if (rows * k > ((int64_t)1 << 31)) return 0;
-  return ix::attn_bwd_workspace_bytes(B, S_max, H_kv, d, k, rows);
+  return ix::pair_layout(B, S_max, k, rows, (size_t)H_kv * 2 * d * 2).total;
 }
 
 ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
@@ -346,9 +346,10 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
   if (ws) {
     if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
-    if (ix::attn_bwd_rows_per_pass(B, T, S_max, H_kv, d, k, ws_bytes) < 1)
+    const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
+    if (ix::pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes) < 1)
       return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
-                  ws_bytes, ix::attn_bwd_workspace_bytes(B, S_max, H_kv, d, k, 1));
+                  ws_bytes, ix::pair_layout(B, S_max, k, 1, row_bytes).total);
   } else if (ws_bytes != 0) {
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
@@ -379,9 +380,18 @@ ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const
   return ok();
 }
 
+size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args* a, int32_t k, int32_t rows_per_pass) {
+  bool empty = false;
+  if (check_indexer(a, &empty) != IX_OK || empty || check_k(k) != IX_OK) return 0;
+  if (rows_per_pass < 1) return 0;
+  const int64_t rows = std::min<int64_t>(rows_per_pass, (int64_t)a->B * a->T);
+  if (rows * k > ((int64_t)1 << 31)) return 0;
+  return ix::pair_layout(a->B, a->S_max, k, rows, (size_t)a->d_I * 2).total;
+}
+
 ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx,
-                         const float* dscores, float* dq_I, float* dw, float* dk_I,
-                         hipStream_t stream) {
+                         const float* dscores, float* dq_I, float* dw, float* dk_I, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
   bool empty = false;
   ix_status st = check_indexer(a, &empty);
   if (st != IX_OK) return st;
@@ -393,8 +403,18 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
   if (!aligned4(a->w) || !aligned4(idx) || !aligned4(dscores) || !aligned4(dq_I) || !aligned4(dw) ||
       !aligned4(dk_I))
     return fail(IX_ERR_INVALID, "w, idx, dscores and gradient pointers must be 4-byte aligned");
+  if (ws) {
+    if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
+    const size_t row_bytes = (size_t)a->d_I * 2;
+    if (ix::pair_rows_per_pass(a->B, a->T, a->S_max, k, row_bytes, ws_bytes) < 1)
+      return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
+                  ws_bytes, ix::pair_layout(a->B, a->S_max, k, 1, row_bytes).total);
+  } else if (ws_bytes != 0) {
+    return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
+  }
   hipError_t e = ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
-                                        a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, stream);
+                                        a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, ws, ws_bytes,
+                                        stream);
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");
   return ok();
 }

@@ -66,8 +66,22 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
                                      float* const* lse, const AttnPlan& pl, void* ws,
                                      hipStream_t stream);
 constexpr int kAttnLayersPerLaunch = 8;
-size_t attn_bwd_workspace_bytes(int B, int S_max, int H_kv, int d, int k, int64_t rows_per_pass);
-int64_t attn_bwd_rows_per_pass(int B, int T, int S_max, int H_kv, int d, int k, size_t ws_bytes);
+// Atomic-free key gradients (pair_reduce.hip): workspace layout for passes of `rows` query
+// rows whose pairs carry row_bytes of bf16 gradient rows each.
+struct PairLayout {
+  int64_t n_keys, nparts;
+  size_t off, cur, part, inv, contrib, total;
+};
+PairLayout pair_layout(int B, int S_max, int k, int64_t rows, size_t row_bytes);
+int64_t pair_rows_per_pass(int B, int T, int S_max, int k, size_t row_bytes, size_t ws_bytes);
+// Offsets and the inverted selection of query rows [row0, row0 + rows).
+hipError_t launch_pair_index(const int32_t* idx, const int32_t* kv_len, int T, int S_max, int k,
+                             int64_t row0, int64_t rows, const PairLayout& L, void* ws,
+                             hipStream_t stream);
+// Per-key sums of the pass's pair rows (row_width bf16 per (pair, head), H heads), first
+// half added to dst_a, second half to dst_b, at row (key * H + head) of `stride` floats.
+hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, int H,
+                              float* dst_a, float* dst_b, int64_t stride, hipStream_t stream);
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,
@@ -80,7 +94,7 @@ hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
 hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float* w,
                               const int32_t* kv_len, const int32_t* idx, const float* dscores,
                               int B, int T, int S_max, int H_I, int d_I, int k, float* dq,
-                              float* dw, float* dk, hipStream_t stream);
+                              float* dw, float* dk, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_peak_mfma(const void* operands, int valu_per_mfma, int blocks, int iters,
                             float* out, hipStream_t stream);
 hipError_t launch_peak_atomic(float* table, int64_t rows, const int32_t* idx, int64_t n,

@@ -1,0 +1,270 @@
+// Atomic-free accumulation of per-pair gradient rows into per-key rows, for the two
+// backward passes whose key gradients sum over every query that kept a key: the sparse
+// attention's dK / dV and the indexer's dk_I.  The fp32 atomic units of the L2 take about
+// one 32-bit add per clock per channel, which bounds the atomic form at one add per
+// gradient element per kept pair.  Instead, per pass over a range of query rows:
+//  1. count the kept pairs of each key (b, s) and scan the counts into segment offsets;
+//  2. list every pair's position in the pass under its key (the inverted selection);
+//  3. the gradient kernel writes each pair's rows (bf16) in pair order;
+//  4. one wave per (key, head) sums its pairs' rows in fp32 and adds the sums to the
+//     gradient rows with ordinary loads and stores (the wave owns those rows).
+// The order of a key's pairs depends on atomic arrival, so the last bits of the sums vary
+// from run to run.
+#include <algorithm>
+
+#include "ix_common.h"
+#include "ix_internal.h"
+
+namespace ix {
+
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = 8;
+constexpr int kScanTile = kScanThreads * kScanPer;
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+__global__ __launch_bounds__(256) void pair_zero_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+// Key id b * S_max + s of pair e of the pass (query row row0 + e / k, entry e % k), or -1
+// for padding (s < 0 or s >= kv_len[b], kv_len clamped to S_max; NULL kv_len: S_max).
+__device__ __forceinline__ int64_t pair_key(const int32_t* idx, const int32_t* kv_len, int T,
+                                            int S_max, int k, int64_t row0, int64_t e) {
+  const int64_t row = row0 + e / k;
+  const int b = (int)(row / T);
+  int kvl = kv_len ? kv_len[b] : S_max;
+  kvl = kvl < 0 ? 0 : (kvl > S_max ? S_max : kvl);
+  const int s = idx[row * k + e % k];
+  return (s >= 0 && s < kvl) ? (int64_t)b * S_max + s : -1;
+}
+
+__global__ __launch_bounds__(256) void pair_count_kernel(const int32_t* idx, const int32_t* kv_len,
+                                                         int T, int S_max, int k, int64_t row0,
+                                                         int64_t pairs, uint32_t* cnt) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < pairs; e += (int64_t)gridDim.x * 256) {
+    const int64_t g = pair_key(idx, kv_len, T, S_max, k, row0, e);
+    if (g >= 0) atomicAdd(cnt + g, 1u);
+  }
+}
+
+// Block-wide exclusive scan of one value per thread; the block total goes to *total.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  uint32_t base = 0, all = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wid) base += wsum[w];
+    all += wsum[w];
+  }
+  __syncthreads();
+  *total = all;
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void pair_scan_tiles(const uint32_t* cnt, int64_t n,
+                                                               uint32_t* part) {
+  __shared__ uint32_t wsum[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanPer;
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i)
+    if (base + i < n) v += cnt[base + i];
+  uint32_t total;
+  block_exclusive_scan(v, wsum, &total);
+  if (threadIdx.x == 0) part[blockIdx.x] = total;
+}
+
+// One block: exclusive scan of the tile totals, in place.
+__global__ __launch_bounds__(1024) void pair_scan_top(uint32_t* part, int64_t nparts) {
+  __shared__ uint32_t wsum[16];
+  uint32_t carry = 0;
+  for (int64_t i0 = 0; i0 < nparts; i0 += 1024) {
+    const int64_t i = i0 + threadIdx.x;
+    const uint32_t v = i < nparts ? part[i] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan(v, wsum, &total);
+    if (i < nparts) part[i] = carry + ex;
+    carry += total;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void pair_scan_apply(uint32_t* cnt, int64_t n,
+                                                               const uint32_t* part) {
+  __shared__ uint32_t wsum[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanPer;
+  uint32_t v[kScanPer], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    v[i] = base + i < n ? cnt[base + i] : 0u;
+    sum += v[i];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(sum, wsum, &total) + part[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    if (base + i < n) cnt[base + i] = run;
+    run += v[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void pair_fill_inv_kernel(const int32_t* idx, const int32_t* kv_len,
+                                                            int T, int S_max, int k, int64_t row0,
+                                                            int64_t pairs, const uint32_t* off,
+                                                            uint32_t* cur, uint32_t* inv) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < pairs; e += (int64_t)gridDim.x * 256) {
+    const int64_t g = pair_key(idx, kv_len, T, S_max, k, row0, e);
+    if (g >= 0) inv[off[g] + atomicAdd(cur + g, 1u)] = (uint32_t)e;
+  }
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
+  return __builtin_bit_cast(float, v << 16);
+}
+
+// One wave per (key, head), grid-stride over all of them.  A pair's row for head h is W
+// bf16 at contrib + (pair * H + h) * W; lanes 0..31 sum elements [0, W/2) into dst_a,
+// lanes 32..63 elements [W/2, W) into dst_b, EPL consecutive columns each, four pairs in
+// flight; the sums are added to row (key * H + h) of stride `stride` floats.
+template <int W>
+__global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, const uint32_t* inv,
+                                                          const uint16_t* contrib, int64_t n_keys,
+                                                          int H, float* dst_a, float* dst_b,
+                                                          int64_t stride) {
+  constexpr int EPL = W / kWave;
+  static_assert(EPL == 1 || EPL == 2 || EPL == 4, "row width");
+  const int lane = threadIdx.x & 63;
+  const int part = lane >> 5;
+  const int col = (lane & 31) * EPL;
+  const int64_t waves = ((int64_t)gridDim.x * 256) >> 6;
+  for (int64_t it = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; it < n_keys * H; it += waves) {
+    const int64_t g = it / H;
+    const int h = (int)(it % H);
+    const uint32_t n0 = off[g], n1 = off[g + 1];
+    if (n0 == n1) continue;
+    float acc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+    auto add_pair = [&](uint32_t pr) {
+      const uint16_t* src = contrib + ((size_t)pr * H + h) * W + part * (W / 2) + col;
+      if constexpr (EPL == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        acc[0] += bf16_bits_to_f32(v.x & 0xFFFFu);
+        acc[1] += bf16_bits_to_f32(v.x >> 16);
+        acc[2] += bf16_bits_to_f32(v.y & 0xFFFFu);
+        acc[3] += bf16_bits_to_f32(v.y >> 16);
+      } else if constexpr (EPL == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(src);
+        acc[0] += bf16_bits_to_f32(v & 0xFFFFu);
+        acc[1] += bf16_bits_to_f32(v >> 16);
+      } else {
+        acc[0] += bf16_bits_to_f32(*src);
+      }
+    };
+    uint32_t e = n0;
+    for (; e + 4 <= n1; e += 4) {
+      const uint32_t p0 = inv[e], p1 = inv[e + 1], p2 = inv[e + 2], p3 = inv[e + 3];
+      add_pair(p0);
+      add_pair(p1);
+      add_pair(p2);
+      add_pair(p3);
+    }
+    for (; e < n1; ++e) add_pair(inv[e]);
+    float* dst = (part ? dst_b : dst_a) + ((size_t)g * H + h) * stride + col;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) dst[i] += acc[i];
+  }
+}
+
+dim3 grid_for(int64_t n) { return dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)); }
+
+}  // namespace
+
+PairLayout pair_layout(int B, int S_max, int k, int64_t rows, size_t row_bytes) {
+  PairLayout L{};
+  L.n_keys = (int64_t)B * S_max;
+  L.nparts = (L.n_keys + 1 + kScanTile - 1) / kScanTile;
+  L.off = 0;
+  L.cur = L.off + up256((size_t)(L.n_keys + 1) * 4);
+  L.part = L.cur + up256((size_t)L.n_keys * 4);
+  L.inv = L.part + up256((size_t)L.nparts * 4);
+  L.contrib = L.inv + up256((size_t)rows * k * 4);
+  L.total = L.contrib + up256((size_t)rows * k * row_bytes);
+  return L;
+}
+
+int64_t pair_rows_per_pass(int B, int T, int S_max, int k, size_t row_bytes, size_t ws_bytes) {
+  const int64_t all = (int64_t)B * T;
+  // pair positions are 32-bit: at most 2^31 pairs per pass
+  int64_t hi = std::min<int64_t>(all, ((int64_t)1 << 31) / k);
+  if (pair_layout(B, S_max, k, 1, row_bytes).total > ws_bytes) return 0;
+  int64_t lo = 1;
+  while (lo < hi) {  // the largest row count that fits
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (pair_layout(B, S_max, k, mid, row_bytes).total <= ws_bytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+hipError_t launch_pair_index(const int32_t* idx, const int32_t* kv_len, int T, int S_max, int k,
+                             int64_t row0, int64_t rows, const PairLayout& L, void* ws,
+                             hipStream_t stream) {
+  char* w = reinterpret_cast<char*>(ws);
+  uint32_t* off = reinterpret_cast<uint32_t*>(w + L.off);
+  uint32_t* cur = reinterpret_cast<uint32_t*>(w + L.cur);
+  uint32_t* part = reinterpret_cast<uint32_t*>(w + L.part);
+  uint32_t* inv = reinterpret_cast<uint32_t*>(w + L.inv);
+  const int64_t pairs = rows * k;
+  hipLaunchKernelGGL(pair_zero_kernel, grid_for(L.n_keys + 1), dim3(256), 0, stream, off, L.n_keys + 1);
+  hipLaunchKernelGGL(pair_zero_kernel, grid_for(L.n_keys), dim3(256), 0, stream, cur, L.n_keys);
+  hipLaunchKernelGGL(pair_count_kernel, grid_for(pairs), dim3(256), 0, stream, idx, kv_len, T, S_max,
+                     k, row0, pairs, off);
+  hipLaunchKernelGGL(pair_scan_tiles, dim3((unsigned)L.nparts), dim3(kScanThreads), 0, stream, off,
+                     L.n_keys + 1, part);
+  hipLaunchKernelGGL(pair_scan_top, dim3(1), dim3(1024), 0, stream, part, L.nparts);
+  hipLaunchKernelGGL(pair_scan_apply, dim3((unsigned)L.nparts), dim3(kScanThreads), 0, stream, off,
+                     L.n_keys + 1, part);
+  hipLaunchKernelGGL(pair_fill_inv_kernel, grid_for(pairs), dim3(256), 0, stream, idx, kv_len, T,
+                     S_max, k, row0, pairs, off, cur, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, int H,
+                              float* dst_a, float* dst_b, int64_t stride, hipStream_t stream) {
+  const char* w = reinterpret_cast<const char*>(ws);
+  const uint32_t* off = reinterpret_cast<const uint32_t*>(w + L.off);
+  const uint32_t* inv = reinterpret_cast<const uint32_t*>(w + L.inv);
+  const uint16_t* contrib = reinterpret_cast<const uint16_t*>(w + L.contrib);
+  const int64_t items = L.n_keys * H;
+  const dim3 grid((unsigned)std::min<int64_t>((items + 3) / 4, 65536));
+  switch (row_width) {
+    case 256:
+      hipLaunchKernelGGL(pair_reduce_kernel<256>, grid, dim3(256), 0, stream, off, inv, contrib,
+                         L.n_keys, H, dst_a, dst_b, stride);
+      break;
+    case 128:
+      hipLaunchKernelGGL(pair_reduce_kernel<128>, grid, dim3(256), 0, stream, off, inv, contrib,
+                         L.n_keys, H, dst_a, dst_b, stride);
+      break;
+    case 64:
+      hipLaunchKernelGGL(pair_reduce_kernel<64>, grid, dim3(256), 0, stream, off, inv, contrib,
+                         L.n_keys, H, dst_a, dst_b, stride);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ix

@@ -774,172 +774,6 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
 }
 
 
-// ------------------------------------------------------------------ key-major dK / dV
-// With a workspace, sparse_attn_bwd adds no atomics: the fp32 atomic units of the L2 take
-// about one 32-bit add per clock per channel, which bounds the atomic form at 2 d adds
-// per selected pair.  Instead, per pass over a range of query rows:
-//  1. count the pairs of each key (b, s) and scan the counts into segment offsets;
-//  2. list every pair's position in the pass under its key (the inverted selection);
-//  3. the gradient kernel writes each pair's dV | dK rows (bf16) in pair order;
-//  4. one wave per (key, KV head) sums its pairs' rows in fp32 and adds the sums to the
-//     gradient caches with ordinary loads and stores (the wave owns those rows).
-// The order of the pairs inside a key's list depends on atomic arrival, so the last bits
-// of dK / dV still vary from run to run.
-
-constexpr int kScanThreads = 256;
-constexpr int kScanPer = 8;
-constexpr int kScanTile = kScanThreads * kScanPer;
-
-__global__ __launch_bounds__(256) void bwd_zero_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = 0u;
-}
-
-// Key id of pair e of the pass (row0 + e / k, entry e % k), or -1 for padding.
-__device__ __forceinline__ int64_t pair_key(const int32_t* idx, const int32_t* kv_len, int T,
-                                            int S_max, int k, int64_t row0, int64_t e) {
-  const int64_t row = row0 + e / k;
-  const int b = (int)(row / T);
-  int kvl = kv_len ? kv_len[b] : S_max;
-  kvl = kvl < 0 ? 0 : (kvl > S_max ? S_max : kvl);
-  const int s = idx[row * k + e % k];
-  return (s >= 0 && s < kvl) ? (int64_t)b * S_max + s : -1;
-}
-
-__global__ __launch_bounds__(256) void bwd_count_kernel(const int32_t* idx, const int32_t* kv_len,
-                                                        int T, int S_max, int k, int64_t row0,
-                                                        int64_t pairs, uint32_t* cnt) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < pairs; e += (int64_t)gridDim.x * 256) {
-    const int64_t g = pair_key(idx, kv_len, T, S_max, k, row0, e);
-    if (g >= 0) atomicAdd(cnt + g, 1u);
-  }
-}
-
-// Block-wide exclusive scan of one value per thread; returns the block total in *total.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[wid] = x;
-  __syncthreads();
-  uint32_t base = 0, all = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wid) base += wsum[w];
-    all += wsum[w];
-  }
-  __syncthreads();
-  *total = all;
-  return base + x - v;
-}
-
-__global__ __launch_bounds__(kScanThreads) void bwd_scan_tiles(const uint32_t* cnt, int64_t n,
-                                                              uint32_t* part) {
-  __shared__ uint32_t wsum[kScanThreads / 64];
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanPer;
-  uint32_t v = 0;
-#pragma unroll
-  for (int i = 0; i < kScanPer; ++i)
-    if (base + i < n) v += cnt[base + i];
-  uint32_t total;
-  block_exclusive_scan(v, wsum, &total);
-  if (threadIdx.x == 0) part[blockIdx.x] = total;
-}
-
-// One block: exclusive scan of the tile totals, in place.
-__global__ __launch_bounds__(1024) void bwd_scan_top(uint32_t* part, int64_t nparts) {
-  __shared__ uint32_t wsum[16];
-  uint32_t carry = 0;
-  for (int64_t i0 = 0; i0 < nparts; i0 += 1024) {
-    const int64_t i = i0 + threadIdx.x;
-    const uint32_t v = i < nparts ? part[i] : 0u;
-    uint32_t total;
-    const uint32_t ex = block_exclusive_scan(v, wsum, &total);
-    if (i < nparts) part[i] = carry + ex;
-    carry += total;
-  }
-}
-
-__global__ __launch_bounds__(kScanThreads) void bwd_scan_apply(uint32_t* cnt, int64_t n,
-                                                              const uint32_t* part) {
-  __shared__ uint32_t wsum[kScanThreads / 64];
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanPer;
-  uint32_t v[kScanPer], sum = 0;
-#pragma unroll
-  for (int i = 0; i < kScanPer; ++i) {
-    v[i] = base + i < n ? cnt[base + i] : 0u;
-    sum += v[i];
-  }
-  uint32_t total;
-  uint32_t run = block_exclusive_scan(sum, wsum, &total) + part[blockIdx.x];
-#pragma unroll
-  for (int i = 0; i < kScanPer; ++i) {
-    if (base + i < n) cnt[base + i] = run;
-    run += v[i];
-  }
-}
-
-__global__ __launch_bounds__(256) void bwd_fill_inv_kernel(const int32_t* idx, const int32_t* kv_len,
-                                                           int T, int S_max, int k, int64_t row0,
-                                                           int64_t pairs, const uint32_t* off,
-                                                           uint32_t* cur, uint32_t* inv) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < pairs; e += (int64_t)gridDim.x * 256) {
-    const int64_t g = pair_key(idx, kv_len, T, S_max, k, row0, e);
-    if (g >= 0) inv[off[g] + atomicAdd(cur + g, 1u)] = (uint32_t)e;
-  }
-}
-
-// One wave per (key, KV head), grid-stride over all of them: lanes 0..31 sum the dV row,
-// lanes 32..63 the dK row, EPL consecutive columns each, four pairs in flight.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const uint32_t* off, const uint32_t* inv,
-                                                         const uint16_t* contrib, int64_t n_keys,
-                                                         int H_kv, float* dkc, float* dvc) {
-  constexpr int EPL = 2 * D / kWave;
-  const int lane = threadIdx.x & 63;
-  const int part = lane >> 5;
-  const int col = (lane & 31) * EPL;
-  const int64_t waves = ((int64_t)gridDim.x * 256) >> 6;
-  for (int64_t it = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; it < n_keys * H_kv; it += waves) {
-    const int64_t g = it / H_kv;
-    const int kvh = (int)(it % H_kv);
-    const uint32_t n0 = off[g], n1 = off[g + 1];
-    if (n0 == n1) continue;
-    float acc[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-    auto add_pair = [&](uint32_t pr) {
-      const uint16_t* src = contrib + ((size_t)pr * H_kv + kvh) * 2 * D + part * D + col;
-      if constexpr (EPL == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        acc[0] += bf16_to_f32((uint16_t)v.x);
-        acc[1] += bf16_to_f32((uint16_t)(v.x >> 16));
-        acc[2] += bf16_to_f32((uint16_t)v.y);
-        acc[3] += bf16_to_f32((uint16_t)(v.y >> 16));
-      } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(src);
-        acc[0] += bf16_to_f32((uint16_t)v);
-        acc[1] += bf16_to_f32((uint16_t)(v >> 16));
-      }
-    };
-    uint32_t e = n0;
-    for (; e + 4 <= n1; e += 4) {
-      const uint32_t p0 = inv[e], p1 = inv[e + 1], p2 = inv[e + 2], p3 = inv[e + 3];
-      add_pair(p0);
-      add_pair(p1);
-      add_pair(p2);
-      add_pair(p3);
-    }
-    for (; e < n1; ++e) add_pair(inv[e]);
-    float* dst = (part ? dkc : dvc) + ((size_t)g * H_kv + kvh) * D + col;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) dst[i] += acc[i];
-  }
-}
-
 // ------------------------------------------------------------------ indexer KL objective
 
 // Training side of the indexer (the twiscan post on GLM-5.2's IndexShare: the indexer
@@ -1272,44 +1106,6 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                                    sm_scale, &out, &lse, pl, ws, stream);
 }
 
-namespace {
-size_t up256(size_t x) { return (x + 255) / 256 * 256; }
-struct BwdLayout {
-  int64_t n_keys, nparts;
-  size_t off, cur, part, inv, contrib, total;
-};
-BwdLayout bwd_layout(int B, int S_max, int H_kv, int d, int k, int64_t rows) {
-  BwdLayout L{};
-  L.n_keys = (int64_t)B * S_max;
-  L.nparts = (L.n_keys + 1 + kScanTile - 1) / kScanTile;
-  L.off = 0;
-  L.cur = L.off + up256((size_t)(L.n_keys + 1) * 4);
-  L.part = L.cur + up256((size_t)L.n_keys * 4);
-  L.inv = L.part + up256((size_t)L.nparts * 4);
-  L.contrib = L.inv + up256((size_t)rows * k * 4);
-  L.total = L.contrib + up256((size_t)rows * k * H_kv * 2 * d * 2);
-  return L;
-}
-}  // namespace
-
-size_t attn_bwd_workspace_bytes(int B, int S_max, int H_kv, int d, int k, int64_t rows_per_pass) {
-  return bwd_layout(B, S_max, H_kv, d, k, rows_per_pass).total;
-}
-
-int64_t attn_bwd_rows_per_pass(int B, int T, int S_max, int H_kv, int d, int k, size_t ws_bytes) {
-  const int64_t all = (int64_t)B * T;
-  // pair positions are 32-bit: at most 2^31 pairs per pass
-  int64_t hi = std::min<int64_t>(all, ((int64_t)1 << 31) / k);
-  if (attn_bwd_workspace_bytes(B, S_max, H_kv, d, k, 1) > ws_bytes) return 0;
-  int64_t lo = 1;
-  while (lo < hi) {  // largest row count that fits
-    const int64_t mid = lo + (hi - lo + 1) / 2;
-    if (attn_bwd_workspace_bytes(B, S_max, H_kv, d, k, mid) <= ws_bytes) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,
@@ -1351,41 +1147,19 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc,
     grad(all);
     return hipGetLastError();
   }
-  const int64_t per_pass = attn_bwd_rows_per_pass(B, T, S_max, H_kv, d, k, ws_bytes);
+  // atomic-free: per pass, the inverted selection, pair rows [dV | dK] in bf16, key sums
+  const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
+  const int64_t per_pass = pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes);
   if (per_pass < 1) return hipErrorInvalidValue;
-  const BwdLayout L = bwd_layout(B, S_max, H_kv, d, k, per_pass);
-  char* w = reinterpret_cast<char*>(ws);
-  uint32_t* off = reinterpret_cast<uint32_t*>(w + L.off);
-  uint32_t* cur = reinterpret_cast<uint32_t*>(w + L.cur);
-  uint32_t* part = reinterpret_cast<uint32_t*>(w + L.part);
-  uint32_t* inv = reinterpret_cast<uint32_t*>(w + L.inv);
-  x.contrib = reinterpret_cast<uint16_t*>(w + L.contrib);
-  auto grid_for = [](int64_t n) { return dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)); };
+  const PairLayout L = pair_layout(B, S_max, k, per_pass, row_bytes);
+  x.contrib = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.contrib);
   for (int64_t r0 = 0; r0 < all; r0 += per_pass) {
     const int64_t rows = std::min(per_pass, all - r0);
-    const int64_t pairs = rows * k;
     x.row0 = r0;
-    hipLaunchKernelGGL(bwd_zero_kernel, grid_for(L.n_keys + 1), dim3(256), 0, stream, off, L.n_keys + 1);
-    hipLaunchKernelGGL(bwd_zero_kernel, grid_for(L.n_keys), dim3(256), 0, stream, cur, L.n_keys);
-    hipLaunchKernelGGL(bwd_count_kernel, grid_for(pairs), dim3(256), 0, stream, idx, kv_len, T,
-                       S_max, k, r0, pairs, off);
-    hipLaunchKernelGGL(bwd_scan_tiles, dim3((unsigned)L.nparts), dim3(kScanThreads), 0, stream, off,
-                       L.n_keys + 1, part);
-    hipLaunchKernelGGL(bwd_scan_top, dim3(1), dim3(1024), 0, stream, part, L.nparts);
-    hipLaunchKernelGGL(bwd_scan_apply, dim3((unsigned)L.nparts), dim3(kScanThreads), 0, stream, off,
-                       L.n_keys + 1, part);
-    hipLaunchKernelGGL(bwd_fill_inv_kernel, grid_for(pairs), dim3(256), 0, stream, idx, kv_len, T,
-                       S_max, k, r0, pairs, off, cur, inv);
+    hipError_t e = launch_pair_index(idx, kv_len, T, S_max, k, r0, rows, L, ws, stream);
+    if (e != hipSuccess) return e;
     grad(rows);
-    const int64_t items = L.n_keys * H_kv;
-    const dim3 rgrid((unsigned)std::min<int64_t>((items + 3) / 4, 65536));
-    if (d == 128)
-      hipLaunchKernelGGL(bwd_reduce_kernel<128>, rgrid, dim3(256), 0, stream, off, inv, x.contrib,
-                         L.n_keys, H_kv, dkc, dvc);
-    else
-      hipLaunchKernelGGL(bwd_reduce_kernel<64>, rgrid, dim3(256), 0, stream, off, inv, x.contrib,
-                         L.n_keys, H_kv, dkc, dvc);
-    const hipError_t e = hipGetLastError();
+    e = launch_pair_reduce(L, ws, 2 * d, H_kv, dvc, dkc, d, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

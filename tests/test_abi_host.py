@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_clean_error():
-    assert bd.ix_abi_version() == bd.ABI_VERSION == 2
+    assert bd.ix_abi_version() == bd.ABI_VERSION == 3
 
 
 FAKE = 1 << 20  # 16-byte aligned non-null stand-in address; never dereferenced on failure
@@ -232,9 +232,19 @@ def test_indexer_bwd_validation_codes():
     assert call(a=args(d_I=96)) == bd.IX_ERR_UNSUPPORTED
     assert call(a=args(H_I=6)) == bd.IX_ERR_UNSUPPORTED
     assert call(k=0) == bd.IX_ERR_UNSUPPORTED and call(k=4096) == bd.IX_ERR_UNSUPPORTED
-    assert bd.load().ix_indexer_bwd(None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == bd.IX_ERR_INVALID
+    assert bd.load().ix_indexer_bwd(None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == bd.IX_ERR_INVALID
     # empty calls launch nothing
     assert call(a=args(B=0, q=0, k=0, w=0, q_pos0=0, kv_len=0), idx=0, ds=0, dq=0, dw=0, dk=0) == bd.IX_OK
+    # the atomic-free form's workspace
+    one = bd.ix_indexer_bwd_workspace_bytes(args(), 16, 1)
+    assert 0 < one < bd.ix_indexer_bwd_workspace_bytes(args(), 16, 7)
+    assert bd.ix_indexer_bwd_workspace_bytes(args(), 16, 10 ** 6) == \
+        bd.ix_indexer_bwd_workspace_bytes(args(), 16, 128)                      # clamped to B*T
+    assert bd.ix_indexer_bwd_workspace_bytes(args(d_I=96), 16, 1) == 0
+    a = args()
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, one - 1) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, one) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, one) == bd.IX_ERR_INVALID
 
 
 def test_peak_validation_codes():

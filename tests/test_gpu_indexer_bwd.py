@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(qI, kI, w, kvl, idx, ds):
+def _run(qI, kI, w, kvl, idx, ds, rows_per_pass=None):
     B, T, H, d_I = qI.shape
     t = {n: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
          for n, v in (("q", qI), ("k", kI), ("w", w.astype(np.float32)),
@@ -35,7 +35,7 @@ def _run(qI, kI, w, kvl, idx, ds):
                       ("ds", ds.astype(np.float32)))}
     pos0 = torch.zeros(B, dtype=torch.int32, device=DEV)
     args = bd.indexer_args(t["q"], t["k"], t["w"], pos0, t["kvl"])
-    dq, dw, dk = bd.indexer_bwd(args, t["idx"], t["ds"], DEV)
+    dq, dw, dk = bd.indexer_bwd(args, t["idx"], t["ds"], DEV, rows_per_pass=rows_per_pass)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), dw.cpu().numpy(), dk.cpu().numpy()
 
@@ -66,26 +66,36 @@ def _case(seed, B, T, S, H, d_I, k, kv_lens, values=None, empty_rows=(), past_kv
     return qI, kI, w, kvl, idx, ds
 
 
-def test_indexer_bwd_ragged_64_heads_d128():
-    say("[ix_indexer_bwd] B=2 T=40 S=500 H_I=64 d_I=128 k=96, ragged kv_len, empty row")
+# None: dk_I added with atomics; a row count: the atomic-free form (inverted selection,
+# per-pair bf16 rows, key-major sums) in passes of that many query rows
+MODES = [None, 1 << 20, 7]
+
+
+@pytest.mark.parametrize("rows_per_pass", MODES)
+def test_indexer_bwd_ragged_64_heads_d128(rows_per_pass):
+    say(f"[ix_indexer_bwd] B=2 T=40 S=500 H_I=64 d_I=128 k=96, ragged kv_len, empty row, "
+        f"rows per pass {rows_per_pass}")
     qI, kI, w, kvl, idx, ds = _case(201, 2, 40, 500, 64, 128, 96, [500, 213], empty_rows={(1, 7)},
                                     past_kv=20)
-    got = _run(qI, kI, w, kvl, idx, ds)
+    got = _run(qI, kI, w, kvl, idx, ds, rows_per_pass)
     assert np.all(got[0][1, 7] == 0) and np.all(got[1][1, 7] == 0)
-    check_indexer_bwd(got, qI, kI, w, idx, ds, kvl)
+    check_indexer_bwd(got, qI, kI, w, idx, ds, kvl, bf16_rows=rows_per_pass is not None)
 
 
-def test_indexer_bwd_exact_zero_dots_partial_head_tile_d64():
+@pytest.mark.parametrize("rows_per_pass", MODES)
+def test_indexer_bwd_exact_zero_dots_partial_head_tile_d64(rows_per_pass):
     """Codes in {0, +-1, +-2}: many dot products are exactly 0 (gradient 0 there on both
     sides); 20 heads leave a partial tile of 16; k = 37 leaves a ragged chunk."""
-    say("[ix_indexer_bwd] B=1 T=33 S=300 H_I=20 d_I=64 k=37, integer codes")
+    say(f"[ix_indexer_bwd] B=1 T=33 S=300 H_I=20 d_I=64 k=37, integer codes, rows per pass "
+        f"{rows_per_pass}")
     qI, kI, w, kvl, idx, ds = _case(202, 1, 33, 300, 20, 64, 37, [300],
                                     values=[0.0, 0.0, 0.0, 1.0, -1.0, 2.0, -2.0])
     keys = O.decode_e4m3(kI[0])
     x0 = O.decode_e4m3(qI[0]) @ keys.T
     say(f"  exact zero dot products: {int((x0 == 0).sum())} of {x0.size}")
     assert (x0 == 0).sum() > 100
-    check_indexer_bwd(_run(qI, kI, w, kvl, idx, ds), qI, kI, w, idx, ds, kvl)
+    check_indexer_bwd(_run(qI, kI, w, kvl, idx, ds, rows_per_pass), qI, kI, w, idx, ds, kvl,
+                      bf16_rows=rows_per_pass is not None)
 
 
 def test_indexer_bwd_full_k_and_few_heads():

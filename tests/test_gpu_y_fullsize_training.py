@@ -147,6 +147,19 @@ def test_prefill_32k_kl_and_backward_full_size():
     scale_id = float(t_q.abs().sum() + t_k.abs().sum() + t_w.abs().sum())
     assert abs(e_q - e_w) <= 1e-3 * scale_id and abs(e_k - e_w) <= 1e-3 * scale_id, \
         f"indexer identity: <dq,q> {e_q:.6e} <dk,k> {e_k:.6e} <dw,w> {e_w:.6e}"
+    # the atomic-free forms (inverted selection, per-pair bf16 rows, key-major sums), in four
+    # passes: dq, dq_I and dw are the same computation; the key gradients agree to the bf16
+    # rounding of each pair's rows
+    say("  atomic-free sparse_attn_bwd and ix_indexer_bwd, 8192 rows per pass")
+    dq2, dK2, dV2 = bd.sparse_attention_backward(att["q"], att["K"], att["V"], idx, out, lse, dout,
+                                                 wl.sm_scale, kv_len=ind["kv_len"],
+                                                 rows_per_pass=8192)
+    dq_I2, dw2, dk_I2 = bd.indexer_bwd(bd.indexer_args(*args), idx, dsc, DEV, rows_per_pass=8192)
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, dq) and torch.equal(dq_I2, dq_I) and torch.equal(dw2, dw)
+    for x, y, nm in ((dK, dK2, "dK"), (dV, dV2, "dV"), (dk_I, dk_I2, "dk_I")):
+        err = float((x.double() - y.double()).norm())
+        assert err <= 4e-3 * float(x.double().norm()), f"{nm}: {err:.3e}"
     say(f"  ok; |sum dV - want| / |want| = {float((got_dv - want_dv).norm() / want_dv.norm()):.2e}, "
         f"|sum dK| / |dK| = {float(sum_dk.norm() / dK64.norm()):.2e}, indexer identity "
         f"{max(abs(e_q - e_w), abs(e_k - e_w)) / scale_id:.2e} of the sum of |terms|")
