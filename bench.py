@@ -403,9 +403,10 @@ def main():
                                op[l], 0, ws.data_ptr() if attn_ws else 0, attn_ws, sh)
             ev[r][2 + l].record(stream)
     torch.cuda.synchronize()
-    t_topk = sum(ev[r][0].elapsed_time(ev[r][1]) for r in range(reps)) / reps
-    t_attn = sum(ev[r][1 + l].elapsed_time(ev[r][2 + l]) for r in range(reps)
-                 for l in range(L)) / (reps * L)
+    topk_times = [ev[r][0].elapsed_time(ev[r][1]) for r in range(reps)]
+    attn_times = [ev[r][1 + l].elapsed_time(ev[r][2 + l]) for r in range(reps) for l in range(L)]
+    t_topk = sum(topk_times) / reps
+    t_attn = sum(attn_times) / (reps * L)
 
     flops, attn_bytes, pairs, sel = algorithmic_work(wl)
     idx_tflops = flops / (t_topk / 1e3) / 1e12
@@ -431,6 +432,12 @@ def main():
             pass
     idx_roof["traffic"] = traffic["indexer"]
     attn_roof["traffic"] = traffic["attention"]
+    # the counter-measured bytes as a rate and an HBM fraction too (for the gathers, part of
+    # them come from the Infinity Cache, which the counters count as fabric traffic)
+    for roof, tb, tm in ((idx_roof, traffic["indexer"], t_topk), (attn_roof, traffic["attention"], t_attn)):
+        if tb:
+            roof["traffic_GB_per_s"] = round(tb / (tm / 1e3) / 1e9, 1)
+            roof["traffic_frac"] = round(tb / (tm / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
     dominant_is_indexer = t_topk >= t_attn * L
     roofline = idx_roof if dominant_is_indexer else attn_roof
     roofline = dict(roofline, kernel="ix_topk (indexer + selection)" if dominant_is_indexer
@@ -830,6 +837,9 @@ def main():
         "detail": {
             "ix_topk_ms": round(t_topk, 3),
             "sparse_attn_ms_per_layer": round(t_attn, 3),
+            "ix_topk_ms_median": round(float(np.median(topk_times)), 3),
+            "sparse_attn_ms_per_layer_median": round(float(np.median(attn_times)), 3),
+            "per_kernel_reps": reps,
             "indexer_roofline": idx_roof,
             "attention_roofline": attn_roof,
             "indexer_tflop": round(flops / 1e12, 3),
