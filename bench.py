@@ -584,6 +584,25 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             ms_form[use_ws] = e0.elapsed_time(e1) / nb
+        # IndexShare group: the L layers' backward with the selection inverted once per pass
+        # (layer 0's inputs stand in for every layer: the same work per layer)
+        ms_group = None
+        if L > 1:
+            def gbwd():
+                bd.indexshare_group_bwd(idx.data_ptr(), ind["kv_len"].data_ptr(), L, [qp[0]] * L,
+                                        [kp[0]] * L, [vp[0]] * L, [op[0]] * L,
+                                        [lse0.data_ptr()] * L, [dout.data_ptr()] * L, wl.B, wl.T,
+                                        wl.S, wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale,
+                                        [dq.data_ptr()] * L, [dK.data_ptr()] * L,
+                                        [dV.data_ptr()] * L, bws.data_ptr(), bws_n, sh)
+            gbwd()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(nb):
+                gbwd()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_group = e0.elapsed_time(e1) / nb
         del bws
         ms_b = ms_form[False]
         bflops = sel * 10.0 * wl.H_q * wl.d   # S, dP, dq, dK, dV: 2 H_q d flop each per pair
@@ -591,6 +610,8 @@ def main():
                     "ms_per_layer_atomics": round(ms_form[False], 3),
                     "ms_per_layer_atomic_free": round(ms_form[True], 3),
                     "atomic_free_rows_per_pass": rows_pp,
+                    "group_ms_per_layer_atomic_free": (round(ms_group / L, 3)
+                                                       if ms_group is not None else None),
                     # rates of the faster form; the atomic rates below are the atomic form's
                     "bf16_tflops": round(bflops / (min(ms_form.values()) / 1e3) / 1e12, 2),
                     "gathered_GB_per_s": round(sel * 2.0 * wl.d * 2 * wl.H_kv /

@@ -70,7 +70,7 @@ typedef struct ix_indexer_args {
 } ix_indexer_args;
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define IX_ABI_VERSION 3
+#define IX_ABI_VERSION 4
 int32_t ix_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
@@ -161,6 +161,30 @@ ix_status sparse_attn_bwd(const void *q, const void *kc, const void *vc, const i
  * per pair).  0 on invalid arguments. */
 size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int32_t H_kv,
                                        int32_t d, int32_t k, int32_t rows_per_pass);
+
+/*
+ * indexshare_group_bwd -- the attention backward of the n_layers layers of an IndexShare
+ * group, which all attend over the same selection idx ("IndexShare: Amortizing the
+ * Indexer" shares the selection; here its inversion is shared too): the atomic-free form of
+ * sparse_attn_bwd in which, per pass over the query rows, the selection is inverted once
+ * and every layer's dV | dK rows are summed per key through that inversion.  Layer l gets
+ * what sparse_attn_bwd with a workspace gives for q[l], kc[l], ... (dq bit for bit; dK and
+ * dV up to the order of the per-key sums).
+ * q, kc, vc, out, lse, dout, dq, dkc, dvc: HOST arrays of n_layers device pointers, each as in
+ *          sparse_attn_bwd (dkc[l], dvc[l] ADDED TO; the caller clears them first).
+ * idx, kv_len, B..sm_scale: shared by the layers, as in sparse_attn_bwd.
+ * ws:      required: at least sparse_attn_bwd_workspace_bytes(..., 1) bytes, 16-byte aligned;
+ *          the same layout and pass size as sparse_attn_bwd.
+ * Errors: as sparse_attn_bwd for every layer, plus IX_ERR_INVALID for n_layers < 1 or a NULL
+ * pointer array, IX_ERR_WORKSPACE without a workspace.
+ */
+ix_status indexshare_group_bwd(const int32_t *idx, const int32_t *kv_len, int32_t n_layers,
+                               const void *const *q, const void *const *kc, const void *const *vc,
+                               const void *const *out, const float *const *lse,
+                               const void *const *dout, int32_t B, int32_t T, int32_t S_max,
+                               int32_t H_q, int32_t H_kv, int32_t d, int32_t k, float sm_scale,
+                               float *const *dq, float *const *dkc, float *const *dvc, void *ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /*
  * ix_indexer_kl -- the indexer's training objective (the twiscan post on GLM-5.2's

@@ -20,7 +20,7 @@ from typing import Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
 
-ABI_VERSION = 3  # IX_ABI_VERSION of include/ix.h
+ABI_VERSION = 4  # IX_ABI_VERSION of include/ix.h
 IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
                 -3: "IX_ERR_WORKSPACE", -4: "IX_ERR_HIP"}
@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
            "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "ix_indexer_kl", "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes", "ix_peak_mfma_fp8", "ix_peak_copy",
+           "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "indexshare_group_bwd", "ix_indexer_kl", "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes", "ix_peak_mfma_fp8", "ix_peak_copy",
            "ix_peak_gather", "ix_peak_atomic_add")
 
 
@@ -85,6 +85,10 @@ def load(path: str = LIB_PATH):
     L.sparse_attn_bwd.restype = c_int32
     L.sparse_attn_bwd.argtypes = ([c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4 +
                                   [c_size_t, c_void_p])
+    L.indexshare_group_bwd.restype = c_int32
+    L.indexshare_group_bwd.argtypes = ([c_void_p, c_void_p, c_int32] + [P(c_void_p)] * 6 +
+                                       [c_int32] * 7 + [c_float] + [P(c_void_p)] * 3 +
+                                       [c_void_p, c_size_t, c_void_p])
     L.sparse_attn_bwd_workspace_bytes.restype = c_size_t
     L.sparse_attn_bwd_workspace_bytes.argtypes = [c_int32] * 7
     L.ix_indexer_bwd.restype = c_int32
@@ -195,6 +199,19 @@ def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_
                     sm_scale, dq, dkc, dvc, ws=0, ws_bytes=0, stream=0):
     _check(load().sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q,
                                   H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes, stream))
+
+
+def indexshare_group_bwd(idx, kv_len, n_layers, q, kc, vc, out, lse, dout, B, T, S_max, H_q,
+                         H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes, stream=0):
+    keep = []
+    conv = []
+    for ptrs in (q, kc, vc, out, lse, dout, dq, dkc, dvc):
+        r = _ptr_array(ptrs)
+        conv.append(None if r is None else r[0])
+        if r is not None:
+            keep.append(r[1])
+    _check(load().indexshare_group_bwd(idx, kv_len, n_layers, *conv[:6], B, T, S_max, H_q, H_kv,
+                                       d, k, sm_scale, *conv[6:], ws, ws_bytes, stream))
 
 
 def sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass):
@@ -404,6 +421,29 @@ def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=Non
                     _ptr(dout), B, T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(dq), _ptr(dK),
                     _ptr(dV), _ptr(ws) if ws is not None else 0, nb, _stream())
     return dq, dK, dV
+
+
+def group_attention_backward(idx, layers, sm_scale, kv_len=None, rows_per_pass=None):
+    """The attention backward of every layer of an IndexShare group over the shared idx,
+    atomic-free with the selection inverted once per pass.  layers: list of dicts with q, K,
+    V, out, lse, dout device tensors.  Returns [(dq, dK, dV) per layer].  rows_per_pass:
+    None takes all rows in one pass."""
+    torch = _torch()
+    q0 = layers[0]["q"]
+    B, T, H_q, d = q0.shape
+    S, H_kv = layers[0]["K"].shape[1], layers[0]["K"].shape[2]
+    k = idx.shape[2]
+    grads = [(torch.empty((B, T, H_q, d), dtype=torch.float32, device=q0.device),
+              torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q0.device),
+              torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q0.device)) for _ in layers]
+    nb = sparse_attn_bwd_workspace_bytes(B, T, S, H_kv, d, k, rows_per_pass or B * T)
+    ws = workspace(nb, q0.device)
+    names = ("q", "K", "V", "out", "lse", "dout")
+    ptrs = [[_ptr(L[n]) for L in layers] for n in names]
+    indexshare_group_bwd(_ptr(idx), _ptr(kv_len), len(layers), *ptrs, B, T, S, H_q, H_kv, d, k,
+                         float(sm_scale), [_ptr(g[0]) for g in grads], [_ptr(g[1]) for g in grads],
+                         [_ptr(g[2]) for g in grads], _ptr(ws), nb, _stream())
+    return grads
 
 
 def ix_indexer_bwd(args: IndexerArgs, k: int, idx: int, dscores: int, dq_I: int, dw: int,

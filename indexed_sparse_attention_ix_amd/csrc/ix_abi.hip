@@ -360,6 +360,44 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
   return ok();
 }
 
+ix_status indexshare_group_bwd(const int32_t* idx, const int32_t* kv_len, int32_t n_layers,
+                               const void* const* q, const void* const* kc, const void* const* vc,
+                               const void* const* out, const float* const* lse,
+                               const void* const* dout, int32_t B, int32_t T, int32_t S_max,
+                               int32_t H_q, int32_t H_kv, int32_t d, int32_t k, float sm_scale,
+                               float* const* dq, float* const* dkc, float* const* dvc, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
+  if (st != IX_OK) return st;
+  if (n_layers < 1) return fail(IX_ERR_INVALID, "n_layers=%d must be >= 1", n_layers);
+  if (empty) return ok();
+  if (!q || !kc || !vc || !out || !lse || !dout || !dq || !dkc || !dvc)
+    return fail(IX_ERR_INVALID, "NULL per-layer pointer array");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_attn_ptrs(q[l], kc[l], vc[l], idx, out[l])) != IX_OK) return st;
+    if (!lse[l] || !dout[l] || !dq[l] || !dkc[l] || !dvc[l])
+      return fail(IX_ERR_INVALID, "layer %d: NULL lse, dout or gradient pointer", l);
+    if (!aligned16(dout[l])) return fail(IX_ERR_INVALID, "layer %d: dout must be 16-byte aligned", l);
+    if (!aligned16(out[l])) return fail(IX_ERR_INVALID, "layer %d: out must be 16-byte aligned", l);
+    if (!aligned4(lse[l]) || !aligned4(dq[l]) || !aligned4(dkc[l]) || !aligned4(dvc[l]))
+      return fail(IX_ERR_INVALID, "layer %d: fp32 lse and gradients must be 4-byte aligned", l);
+  }
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  if (!ws) return fail(IX_ERR_WORKSPACE, "the group backward needs a workspace");
+  if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
+  const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
+  if (ix::pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes) < 1)
+    return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
+                ws_bytes, ix::pair_layout(B, S_max, k, 1, row_bytes).total);
+  hipError_t e = ix::launch_sparse_attn_bwd_layers(n_layers, q, kc, vc, idx, kv_len, out, lse, dout,
+                                                   B, T, S_max, H_q, H_kv, d, k, sm_scale, dq, dkc,
+                                                   dvc, ws, ws_bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexshare_group_bwd launch");
+  return ok();
+}
+
 ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const int32_t* kv_len,
                         const float* lse, const float* sel_scores, int32_t B, int32_t T,
                         int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,

@@ -82,6 +82,14 @@ hipError_t launch_pair_index(const int32_t* idx, const int32_t* kv_len, int T, i
 // half added to dst_a, second half to dst_b, at row (key * H + head) of `stride` floats.
 hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, int H,
                               float* dst_a, float* dst_b, int64_t stride, hipStream_t stream);
+hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, const void* const* kc,
+                                         const void* const* vc, const int32_t* idx,
+                                         const int32_t* kv_len, const void* const* out,
+                                         const float* const* lse, const void* const* dout, int B,
+                                         int T, int S_max, int H_q, int H_kv, int d, int k,
+                                         float sm_scale, float* const* dq, float* const* dkc,
+                                         float* const* dvc, void* ws, size_t ws_bytes,
+                                         hipStream_t stream);
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,

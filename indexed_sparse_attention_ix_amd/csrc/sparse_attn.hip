@@ -1106,34 +1106,43 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                                    sm_scale, &out, &lse, pl, ws, stream);
 }
 
-hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
-                                  const int32_t* kv_len, const void* out, const float* lse,
-                                  const void* dout, int B, int T, int S_max, int H_q, int H_kv,
-                                  int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
-                                  void* ws, size_t ws_bytes, hipStream_t stream) {
-  AttnBwdArgs x{};
-  x.q = reinterpret_cast<const uint16_t*>(q);
-  x.kc = reinterpret_cast<const uint16_t*>(kc);
-  x.vc = reinterpret_cast<const uint16_t*>(vc);
-  x.idx = idx;
-  x.kv_len = kv_len;
-  x.out = reinterpret_cast<const uint16_t*>(out);
-  x.lse = lse;
-  x.dout = reinterpret_cast<const uint16_t*>(dout);
-  x.B = B;
-  x.T = T;
-  x.S_max = S_max;
-  x.H_q = H_q;
-  x.H_kv = H_kv;
-  x.grp = H_q / H_kv;
-  x.k = k;
-  x.chunks = (k + kChunk - 1) / kChunk;
-  x.scale = sm_scale;
-  x.scale_log2 = sm_scale * 1.4426950408889634f;
-  x.dq = dq;
-  x.dkc = dkc;
-  x.dvc = dvc;
-  auto grad = [&](int64_t rows) {
+// The backward of n_layers layers over one selection: with atomics, each layer on its own;
+// atomic-free, the selection is inverted once per pass of query rows and every layer's
+// dV | dK rows are summed per key through that inversion (the layers of an IndexShare group).
+hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, const void* const* kc,
+                                         const void* const* vc, const int32_t* idx,
+                                         const int32_t* kv_len, const void* const* out,
+                                         const float* const* lse, const void* const* dout, int B,
+                                         int T, int S_max, int H_q, int H_kv, int d, int k,
+                                         float sm_scale, float* const* dq, float* const* dkc,
+                                         float* const* dvc, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  auto args = [&](int l) {
+    AttnBwdArgs x{};
+    x.q = reinterpret_cast<const uint16_t*>(q[l]);
+    x.kc = reinterpret_cast<const uint16_t*>(kc[l]);
+    x.vc = reinterpret_cast<const uint16_t*>(vc[l]);
+    x.idx = idx;
+    x.kv_len = kv_len;
+    x.out = reinterpret_cast<const uint16_t*>(out[l]);
+    x.lse = lse[l];
+    x.dout = reinterpret_cast<const uint16_t*>(dout[l]);
+    x.B = B;
+    x.T = T;
+    x.S_max = S_max;
+    x.H_q = H_q;
+    x.H_kv = H_kv;
+    x.grp = H_q / H_kv;
+    x.k = k;
+    x.chunks = (k + kChunk - 1) / kChunk;
+    x.scale = sm_scale;
+    x.scale_log2 = sm_scale * 1.4426950408889634f;
+    x.dq = dq[l];
+    x.dkc = dkc[l];
+    x.dvc = dvc[l];
+    return x;
+  };
+  auto grad = [&](const AttnBwdArgs& x, int64_t rows) {
     const dim3 grid((unsigned)(rows * H_kv));
     if (d == 128)
       hipLaunchKernelGGL(sparse_attn_bwd_kernel<128>, grid, dim3(kAttnBlock), 0, stream, x);
@@ -1142,27 +1151,45 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc,
   };
   const int64_t all = (int64_t)B * T;
   if (!ws) {
-    x.row0 = 0;
-    x.contrib = nullptr;
-    grad(all);
+    for (int l = 0; l < n_layers; ++l) {
+      AttnBwdArgs x = args(l);
+      x.row0 = 0;
+      x.contrib = nullptr;
+      grad(x, all);
+    }
     return hipGetLastError();
   }
-  // atomic-free: per pass, the inverted selection, pair rows [dV | dK] in bf16, key sums
+  // atomic-free: per pass, the inverted selection, then per layer the pair rows [dV | dK]
+  // in bf16 and their key sums
   const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
   const int64_t per_pass = pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes);
   if (per_pass < 1) return hipErrorInvalidValue;
   const PairLayout L = pair_layout(B, S_max, k, per_pass, row_bytes);
-  x.contrib = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.contrib);
+  uint16_t* contrib = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.contrib);
   for (int64_t r0 = 0; r0 < all; r0 += per_pass) {
     const int64_t rows = std::min(per_pass, all - r0);
-    x.row0 = r0;
     hipError_t e = launch_pair_index(idx, kv_len, T, S_max, k, r0, rows, L, ws, stream);
     if (e != hipSuccess) return e;
-    grad(rows);
-    e = launch_pair_reduce(L, ws, 2 * d, H_kv, dvc, dkc, d, stream);
-    if (e != hipSuccess) return e;
+    for (int l = 0; l < n_layers; ++l) {
+      AttnBwdArgs x = args(l);
+      x.row0 = r0;
+      x.contrib = contrib;
+      grad(x, rows);
+      e = launch_pair_reduce(L, ws, 2 * d, H_kv, dvc[l], dkc[l], d, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
+}
+
+hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                                  const int32_t* kv_len, const void* out, const float* lse,
+                                  const void* dout, int B, int T, int S_max, int H_q, int H_kv,
+                                  int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  return launch_sparse_attn_bwd_layers(1, &q, &kc, &vc, idx, kv_len, &out, &lse, &dout, B, T, S_max,
+                                       H_q, H_kv, d, k, sm_scale, &dq, &dkc, &dvc, ws, ws_bytes,
+                                       stream);
 }
 
 hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_clean_error():
-    assert bd.ix_abi_version() == bd.ABI_VERSION == 3
+    assert bd.ix_abi_version() == bd.ABI_VERSION == 4
 
 
 FAKE = 1 << 20  # 16-byte aligned non-null stand-in address; never dereferenced on failure
@@ -215,6 +215,33 @@ def test_attention_bwd_validation_codes():
     assert status_of(bd.sparse_attn_bwd, *a, FAKE, one - 1) == bd.IX_ERR_WORKSPACE
     assert status_of(bd.sparse_attn_bwd, *a, 0, one) == bd.IX_ERR_WORKSPACE
     assert status_of(bd.sparse_attn_bwd, *a, FAKE + 8, one) == bd.IX_ERR_INVALID
+
+
+def test_group_bwd_validation_codes():
+    n = 2
+    arr = [FAKE] * n
+    ok = dict(idx=FAKE, kvl=FAKE, n=n, q=arr, kc=arr, vc=arr, out=arr, lse=arr, dout=arr, B=2, T=3,
+              S=64, H_q=16, H_kv=1, d=128, k=16, scale=0.1, dq=arr, dk=arr, dv=arr)
+    one = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 1)
+
+    def call(ws=FAKE, nb=one, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return status_of(bd.indexshare_group_bwd, a["idx"], a["kvl"], a["n"], a["q"], a["kc"], a["vc"],
+                         a["out"], a["lse"], a["dout"], a["B"], a["T"], a["S"], a["H_q"], a["H_kv"],
+                         a["d"], a["k"], a["scale"], a["dq"], a["dk"], a["dv"], ws, nb)
+
+    assert call(n=0) == bd.IX_ERR_INVALID
+    for name in ("q", "kc", "vc", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert call(**{name: None}) == bd.IX_ERR_INVALID, name
+        assert call(**{name: [FAKE, 0]}) == bd.IX_ERR_INVALID, name
+    assert call(idx=0) == bd.IX_ERR_INVALID
+    assert call(dk=[FAKE, FAKE + 2]) == bd.IX_ERR_INVALID
+    assert call(ws=0, nb=0) == bd.IX_ERR_WORKSPACE
+    assert call(nb=one - 1) == bd.IX_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == bd.IX_ERR_INVALID
+    assert call(d=96) == bd.IX_ERR_UNSUPPORTED
+    assert call(B=0, ws=0, nb=0) == bd.IX_OK
 
 
 def test_indexer_bwd_validation_codes():

@@ -121,3 +121,57 @@ def test_backward_atomic_free_matches_atomics():
     for n, (x, y) in enumerate(zip(a[1:], f[1:])):
         err = float((x - y).norm())
         assert err <= 4e-3 * float(x.norm()), f"{('dK', 'dV')[n]}: {err:.3e} vs {float(x.norm()):.3e}"
+
+
+@pytest.mark.parametrize("rows_per_pass", [None, 10])
+def test_group_backward_shares_the_inversion(rows_per_pass):
+    """indexshare_group_bwd: three layers over one selection, the selection inverted once per
+    pass.  Each layer equals sparse_attn_bwd's atomic-free form on its own inputs (dq bit for
+    bit; dK, dV up to the order of the per-key fp32 sums), and the oracle's chain rule."""
+    say(f"[indexshare_group_bwd] 3 layers, rows per pass {rows_per_pass}")
+    g = torch.Generator(device="cpu").manual_seed(75)
+    B, T, S, H_q, H_kv, d, k = 2, 30, 400, 8, 2, 64, 40
+    rng = np.random.default_rng(75)
+    kvl = np.array([400, 260], dtype=np.int32)
+    idx = np.full((B, T, k), -1, dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = int(rng.integers(1, k + 1))
+            idx[b, t, :n] = np.sort(rng.choice(S, size=n, replace=False))
+    didx = torch.from_numpy(idx).to(DEV)
+    dkvl = torch.from_numpy(kvl).to(DEV)
+    scale = d ** -0.5
+    layers = []
+    for _ in range(3):
+        q = (torch.randn(B, T, H_q, d, generator=g) * 0.3).to(torch.bfloat16)
+        K = (torch.randn(B, S, H_kv, d, generator=g) * 0.3).to(torch.bfloat16)
+        V = torch.randn(B, S, H_kv, d, generator=g).to(torch.bfloat16)
+        dout = torch.randn(B, T, H_q, d, generator=g).to(torch.bfloat16)
+        L = {n: x.to(DEV) for n, x in (("q", q), ("K", K), ("V", V), ("dout", dout))}
+        L["out"], L["lse"] = bd.sparse_attention(L["q"], L["K"], L["V"], didx, scale, kv_len=dkvl,
+                                                 with_lse=True)
+        layers.append(L)
+    grads = bd.group_attention_backward(didx, layers, scale, kv_len=dkvl, rows_per_pass=rows_per_pass)
+    torch.cuda.synchronize()
+    for l, L in enumerate(layers):
+        ref = bd.sparse_attention_backward(L["q"], L["K"], L["V"], didx, L["out"], L["lse"], L["dout"],
+                                           scale, kv_len=dkvl, rows_per_pass=rows_per_pass or B * T)
+        torch.cuda.synchronize()
+        assert torch.equal(grads[l][0], ref[0]), f"layer {l}: dq differs"
+        for n in (1, 2):
+            err = float((grads[l][n].double() - ref[n].double()).norm())
+            assert err <= 1e-5 * float(ref[n].double().norm()), f"layer {l}: {('dK', 'dV')[n - 1]}"
+    # and layer 1 against the oracle
+    L = layers[1]
+    gq, gK, gV = (x.cpu().numpy() for x in grads[1])
+    term = scale * float(L["K"].float().abs().max() * L["dout"].float().abs().max() *
+                         L["V"].float().abs().max())
+    for b in range(B):
+        ridx = np.where((idx[b] >= 0) & (idx[b] < kvl[b]), idx[b], -1)
+        rq, rK, rV = O.sparse_attention_backward_rows(
+            _bits(L["q"]), _bits(L["K"]), _bits(L["V"]), ridx,
+            L["dout"][b].float().cpu().numpy().astype(np.float64), b, list(range(T)), scale)
+        for t in range(T):
+            _close(gq[b, t], rq[t], term, f"dq b={b} t={t}")
+        _close(gK[b], rK, term, f"dK b={b}")
+        _close(gV[b], rV, term, f"dV b={b}")
