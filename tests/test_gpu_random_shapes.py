@@ -158,7 +158,12 @@ def test_random_shape_training(wl):
     dq, dK, dV = bd.sparse_attention_backward(att["q"], att["K"], att["V"], ridx, out, lse, dout,
                                               wl.sm_scale, kv_len=ind["kv_len"])
     ib = bd.indexer_bwd(bd.indexer_args(*args), ridx, dsc, DEV)
+    # the atomic-free forms, in passes of 3 query rows
+    dq3, dK3, dV3 = bd.sparse_attention_backward(att["q"], att["K"], att["V"], ridx, out, lse, dout,
+                                                 wl.sm_scale, kv_len=ind["kv_len"], rows_per_pass=3)
+    ib3 = bd.indexer_bwd(bd.indexer_args(*args), ridx, dsc, DEV, rows_per_pass=3)
     torch.cuda.synchronize()
+    assert torch.equal(dq3, dq) and torch.equal(ib3[0], ib[0]) and torch.equal(ib3[1], ib[1])
     hl = to_host_attn(att)
     kvl = h["kv_len"]
     sc_np = kept_t.astype(np.float64)
@@ -194,8 +199,12 @@ def test_random_shape_training(wl):
                 close(dq_np[b, t], rq[t], f"dq b={b} t={t}")
         close(dK_np[b], rK, f"dK b={b}")
         close(dV_np[b], rV, f"dV b={b}")
+        close(dK3[b].cpu().numpy(), rK, f"dK (atomic-free) b={b}")
+        close(dV3[b].cpu().numpy(), rV, f"dV (atomic-free) b={b}")
         carried.append(O.indexer_backward_rows(abs_codes(h["q_I"]), abs_codes(h["k_I"]),
                                                np.abs(h["w"]), ref_idx[b], eps_ds, b,
                                                list(range(wl.T)), int(kvl[b])))
     check_indexer_bwd(tuple(x.cpu().numpy() for x in ib), h["q_I"], h["k_I"], h["w"], ref_idx,
                       ref_ds, kvl, extra=carried, where=wl.name)
+    check_indexer_bwd(tuple(x.cpu().numpy() for x in ib3), h["q_I"], h["k_I"], h["w"], ref_idx,
+                      ref_ds, kvl, extra=carried, where=wl.name + " (atomic-free)", bf16_rows=True)
