@@ -32,6 +32,7 @@ def traffic_file(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 KERNEL_SOURCES = ["indexed_sparse_attention_ix_amd/csrc/indexer.hip",
                   "indexed_sparse_attention_ix_amd/csrc/sparse_attn.hip",
+                  "indexed_sparse_attention_ix_amd/csrc/attn_common.h",
                   "indexed_sparse_attention_ix_amd/csrc/ix_common.h"]
 
 
