@@ -34,6 +34,11 @@
  *     d in {64,128}; H_q a multiple of H_kv with H_q/H_kv <= 16; 1 <= k <= 2048;
  *     one sequence's indexer keys (S_max*d_I bytes) below 2 GiB and its K and V
  *     caches (S_max*H_kv*d*2 bytes each) within 2 GiB.
+ *     One call runs each kernel as one launch, and a launch counts its work-items in
+ *     32 bits.  Hence at most 2^24 - 1 query rows per indexer call (B*T), per attention
+ *     call (B*T*H_kv) and per append (B*T_new).  Likewise at most 2^32 - 256 expanded
+ *     entries (B*T*k_blocks*pool) for ix_topk_pooled, and at most 2^32 - 256 key pieces
+ *     (B*ceil(S_max/pool)*d_I/8) for ix_pool_keys.
  *     Other shapes return IX_ERR_UNSUPPORTED (no fallback path exists).
  *   - Calls are re-entrant; concurrent calls must not share a workspace.
  */

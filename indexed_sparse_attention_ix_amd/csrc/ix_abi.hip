@@ -35,6 +35,13 @@ ix_status hip_fail(hipError_t e, const char* what) {
   return fail(IX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A launch gives its grid in blocks, but the dispatch counts work-items in 32 bits.  The
+// kernels run 256-thread blocks over at most one block per query row (and KV head), and
+// the element-wise kernels at most 256 threads per row.  So one call covers fewer than
+// 2^24 rows, and an element-wise launch at most kMaxBlocks full blocks.
+constexpr int64_t kMaxBlocks = (int64_t)0xFFFFFFFF / 256;  // 2^24 - 1
+bool items_fit(int64_t threads) { return threads >= 0 && (threads + 255) / 256 <= kMaxBlocks; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -61,9 +68,9 @@ ix_status check_indexer(const ix_indexer_args* a, bool* empty) {
   if ((int64_t)a->S_max * a->d_I >= ((int64_t)1 << 31))
     return fail(IX_ERR_UNSUPPORTED, "S_max*d_I=%lld: one sequence's indexer keys must stay below 2 GiB",
                 (long long)a->S_max * a->d_I);
-  if ((int64_t)a->B * a->T > (int64_t)0x7FFFFFFF)
-    return fail(IX_ERR_UNSUPPORTED, "B*T=%lld exceeds the grid limit",
-                (long long)((int64_t)a->B * a->T));
+  if ((int64_t)a->B * a->T > kMaxBlocks)
+    return fail(IX_ERR_UNSUPPORTED, "B*T=%lld query rows: one launch holds at most %lld",
+                (long long)((int64_t)a->B * a->T), (long long)kMaxBlocks);
   return IX_OK;
 }
 
@@ -86,8 +93,9 @@ ix_status check_attn_shape(int32_t B, int32_t T, int32_t S_max, int32_t H_q, int
   *empty = (B == 0 || T == 0);
   if (*empty) return IX_OK;
   if (S_max < 1) return fail(IX_ERR_INVALID, "S_max=%d must be >= 1", S_max);
-  if ((int64_t)B * T * H_kv > (int64_t)0x7FFFFFFF / 64)
-    return fail(IX_ERR_UNSUPPORTED, "B*T*H_kv too large for one launch");
+  if ((int64_t)B * T * H_kv > kMaxBlocks)
+    return fail(IX_ERR_UNSUPPORTED, "B*T*H_kv=%lld query rows: one launch holds at most %lld",
+                (long long)((int64_t)B * T * H_kv), (long long)kMaxBlocks);
   if ((int64_t)S_max * H_kv * d * 2 > ((int64_t)1 << 31))
     return fail(IX_ERR_UNSUPPORTED,
                 "S_max*H_kv*d=%lld: one sequence's K (or V) cache must stay within 2 GiB",
@@ -261,8 +269,9 @@ ix_status ix_append_kv(const float* k_I_new, const void* K_new, const void* V_ne
       (V_new && (!aligned16(V_new) || !aligned16(V_cache))))
     return fail(IX_ERR_INVALID,
                 "k_I_new, K/V rows and caches must be 16-byte aligned (k_I_cache 8-byte)");
-  if ((int64_t)B * T_new * 16 > (int64_t)0x7FFFFFFF * 32)
-    return fail(IX_ERR_UNSUPPORTED, "B*T_new too large for one launch");
+  if ((int64_t)B * T_new > kMaxBlocks)
+    return fail(IX_ERR_UNSUPPORTED, "B*T_new=%lld rows: one launch holds at most %lld",
+                (long long)((int64_t)B * T_new), (long long)kMaxBlocks);
   hipError_t e = ix::launch_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
                                       k_I_cache, K_cache, V_cache, stream);
   if (e != hipSuccess) return hip_fail(e, "ix_append_kv launch");
@@ -278,6 +287,11 @@ ix_status ix_pool_keys(const uint8_t* k_I, const int32_t* kv_len, int32_t B, int
   if (!k_I || !k_pooled) return fail(IX_ERR_INVALID, "NULL key pointer");
   if ((reinterpret_cast<uintptr_t>(k_I) | reinterpret_cast<uintptr_t>(k_pooled)) & 7u)
     return fail(IX_ERR_INVALID, "key arrays must be 8-byte aligned");
+  const int64_t pieces_per_row = d_I / 8;
+  const int64_t block_rows = (int64_t)B * ((S_max + pool - 1) / pool);
+  if (block_rows > ((int64_t)1 << 40) || !items_fit(block_rows * pieces_per_row))
+    return fail(IX_ERR_UNSUPPORTED, "B*ceil(S_max/pool)=%lld block keys: too many for one launch",
+                (long long)block_rows);
   hipError_t e = ix::launch_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream);
   if (e != hipSuccess) return hip_fail(e, "ix_pool_keys launch");
   return ok();
@@ -288,6 +302,7 @@ size_t ix_topk_pooled_workspace_bytes(const ix_indexer_args* a, int32_t pool, in
   if (!a || !pool_ok(pool) || check_k(k_blocks) != IX_OK) return 0;
   const ix_indexer_args u = pooled_args(*a, pool);
   if (check_indexer(&u, &empty) != IX_OK || empty) return 0;
+  if (!items_fit((int64_t)a->B * a->T * k_blocks * pool)) return 0;
   const ix::TopkPlan plan = ix::make_topk_plan(u, k_blocks);
   return plan.ws_bytes + pooled_blocks_bytes(u, k_blocks);
 }
@@ -303,6 +318,9 @@ ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_block
   if ((st = check_indexer(&u, &empty)) != IX_OK) return st;
   if (empty) return ok();
   if (!idx) return fail(IX_ERR_INVALID, "idx pointer is NULL");
+  if (!items_fit((int64_t)a->B * a->T * k_blocks * pool))
+    return fail(IX_ERR_UNSUPPORTED, "B*T*k_blocks*pool=%lld entries: too many for one launch",
+                (long long)((int64_t)a->B * a->T * k_blocks * pool));
   const ix::TopkPlan plan = ix::make_topk_plan(u, k_blocks);
   const size_t need = plan.ws_bytes + pooled_blocks_bytes(u, k_blocks);
   if (!ws || ws_bytes < need)

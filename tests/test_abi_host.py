@@ -161,6 +161,33 @@ def test_append_validation_codes():
     assert call(kn=0, kc=0, Kn=0, Kc=0, Vn=0, Vc=0) == bd.IX_OK
 
 
+def test_one_launch_row_limits():
+    # a launch counts its work-items in 32 bits: at most 2^24 - 1 rows of 256-thread blocks
+    top = (1 << 24) - 1
+    assert bd.ix_topk_workspace_bytes(args(T=top), 64) > 0
+    assert bd.ix_topk_workspace_bytes(args(T=top + 1), 64) == 0
+    assert bd.ix_topk_workspace_bytes(args(B=1 << 12, T=1 << 12), 64) == 0
+    assert status_of(bd.ix_topk, args(B=1 << 12, T=1 << 12), 64, FAKE, 0, FAKE, 1 << 30) == \
+        bd.IX_ERR_UNSUPPORTED
+    assert "one launch" in bd.ix_last_error()
+    assert status_of(bd.ix_score, args(T=top + 1), 0, 4, FAKE) == bd.IX_ERR_UNSUPPORTED
+    # attention rows count KV heads too
+    assert bd.sparse_attn_bwd_workspace_bytes(1, top // 4, 128, 4, 128, 64, 1024) > 0
+    assert bd.sparse_attn_bwd_workspace_bytes(1, (top + 1) // 4, 128, 4, 128, 64, 1024) == 0
+    assert status_of(bd.sparse_attn_fwd, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 22, 1, 128, 16, 4,
+                     128, 64, 0.1, FAKE, 0, 0, 0) == bd.IX_ERR_UNSUPPORTED
+    # the append's rows, the pooled expansion's entries and the block-key pieces
+    assert status_of(bd.ix_append_kv, FAKE, FAKE, FAKE, FAKE, 1 << 12, 1 << 12, 64, 128, 1, 128,
+                     FAKE, FAKE, FAKE) == bd.IX_ERR_UNSUPPORTED
+    fits = args(T=1 << 20, S_max=1 << 16)
+    assert bd.ix_topk_pooled_workspace_bytes(fits, 16, 255) > 0
+    assert bd.ix_topk_pooled_workspace_bytes(fits, 16, 256) == 0
+    assert status_of(bd.ix_topk_pooled, fits, 16, 256, FAKE, FAKE, 1 << 40) == \
+        bd.IX_ERR_UNSUPPORTED
+    assert status_of(bd.ix_pool_keys, FAKE, FAKE, 1 << 8, 1 << 21, 128, 1, FAKE) == \
+        bd.IX_ERR_UNSUPPORTED
+
+
 def test_indexer_kl_validation_codes():
     ok = dict(q=FAKE, kc=FAKE, idx=FAKE, kvl=FAKE, lse=FAKE, sc=FAKE, B=2, T=3, S=64, H_q=16,
               H_kv=1, d=128, k=16, scale=0.1, loss=FAKE, dsc=FAKE)
