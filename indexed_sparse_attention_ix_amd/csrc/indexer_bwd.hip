@@ -11,7 +11,9 @@
 // One block per query, four waves; wave w owns indexer heads [16w, 16w + 16).  The block
 // walks the query's kept keys in chunks of 32:
 //  * the chunk's FP8 key rows are gathered into LDS twice: row-major (operands of the FP8
-//    product) and dimension-major (operands of the dq product);
+//    product) and dimension-major (operands of the dq product).  The gather runs ahead in
+//    registers: the next chunk's rows, and the positions and d loss / d score one chunk
+//    further, are loaded while a chunk is computed;
 //  * each wave computes x^T for its heads with two FP8 MFMAs (A = key rows, B = its query
 //    rows), so a lane holds four keys of one head: the layout of the A operand of the bf16
 //    dq product over keys;
@@ -24,7 +26,7 @@
 //  * d loss / d x goes to LDS for all heads; the chunk's key gradients, summed over all
 //    64 heads, are one bf16 product per 16x16 output tile (A = d loss / d x per key,
 //    B = the query rows transposed), written to LDS and added to dk_I with row-contiguous
-//    fp32 atomics: 32 keys x d_I floats per chunk, which bound the kernel;
+//    fp32 atomics (32 keys x d_I floats per chunk), or written as bf16 pair rows;
 //  * d loss / d x enters the bf16 products as a hi + lo pair of bf16 (residual below
 //    2^-17 relative); the e4m3 operands are exact in bf16.
 #include <algorithm>
@@ -40,6 +42,11 @@ constexpr int kBwdChunk = 32;
 constexpr int kBwdThreads = 256;
 constexpr int kBwdHeads = 64;
 constexpr float kAmbiguous = 1.0f / 1024.0f;
+// Waves per SIMD the register budget is cut for, per form.  The atomic form is bound by its
+// atomics, and more waves only queue more of them.  The pair-row form is bound by its chunk
+// latency, so it is cut to 168 VGPRs (a few spilled) for a third wave.
+template <bool STORE>
+constexpr int kBwdWaves = STORE ? 3 : 2;
 
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
@@ -108,8 +115,9 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ __bf16 bf16_hi(float v) { return (__bf16)v; }
 __device__ __forceinline__ __bf16 bf16_lo(float v, __bf16 hi) { return (__bf16)(v - (float)hi); }
 
-template <int DI>
-__global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
+// STORE: write each kept pair's dk_I row in bf16 to `contrib` instead of adding it to dk.
+template <int DI, bool STORE>
+__global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ kI, const float* __restrict__ w,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ idx,
     const float* __restrict__ dsc, int T, int S_max, int H, int k, float* __restrict__ dq,
@@ -175,20 +183,39 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
   for (int c = 0; c < kDimTiles; ++c) dqacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dwacc = 0.f;
 
-  for (int j0 = 0; j0 < k; j0 += kBwdChunk) {
-    // ---- gather the chunk: thread (kk, p) loads piece p of kept key kk
-    {
-      const int kk = tid >> 3, p = tid & 7;
-      const int j = j0 + kk;
-      int s = -1;
-      float dsv = 0.f;
-      if (j < k) {
-        s = idx_row[j];
-        if (s < 0 || s >= n_keys) s = -1;
-        else dsv = ds_row[j];
+  // The gather is pipelined through registers: thread (kk, p) holds piece p of kept key kk
+  // of the next chunk, and the position and d loss / d score of that key one chunk further,
+  // so their loads are in flight while a chunk is computed.
+  const int kk = tid >> 3, p = tid & 7;
+  auto load_sel = [&](int j, int& s, float& dsv) {
+    s = -1;
+    dsv = 0.f;
+    if (j < k) {
+      const int sv = idx_row[j];
+      const float dv = ds_row[j];
+      if (sv >= 0 && sv < n_keys) {
+        s = sv;
+        dsv = dv;
       }
-      i32x4 v = {0, 0, 0, 0};
-      if (s >= 0 && p < kPieces) v = ld_global_16(kI + ((int64_t)b * S_max + s) * DI + 16 * p);
+    }
+  };
+  auto load_piece = [&](int s) {
+    i32x4 v = {0, 0, 0, 0};
+    if (s >= 0 && p < kPieces) v = ld_global_16(kI + ((int64_t)b * S_max + s) * DI + 16 * p);
+    return v;
+  };
+  int s_next, s_after;
+  float ds_next, ds_after;
+  load_sel(kk, s_next, ds_next);
+  i32x4 v_next = load_piece(s_next);
+  load_sel(kBwdChunk + kk, s_after, ds_after);
+
+  for (int j0 = 0; j0 < k; j0 += kBwdChunk) {
+    // ---- stage the chunk (piece p of kept key kk), then start loading the next two
+    {
+      const int s = s_next;
+      const float dsv = ds_next;
+      const i32x4 v = v_next;
       const uint32_t vw[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
       float ss = sumsq_e4m3(vw, 4);
       ss += __shfl_xor(ss, 1);
@@ -204,8 +231,12 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
         sm.ds[kk] = dsv;
         sm.key[kk] = s;
       }
+      s_next = s_after;
+      ds_next = ds_after;
+      v_next = load_piece(s_next);
+      load_sel(j0 + 2 * kBwdChunk + kk, s_after, ds_after);
       // nothing to add in this chunk (with a pair buffer every kept pair's row is written)
-      if (!__syncthreads_or(s >= 0 && (contrib != nullptr || dsv != 0.f))) continue;
+      if (!__syncthreads_or(s >= 0 && (STORE || dsv != 0.f))) continue;
     }
 
     // ---- x^T, the exact mask, d loss / d x, dw, and dq
@@ -292,7 +323,7 @@ __global__ __launch_bounds__(kBwdThreads) void indexer_bwd_kernel(
     __syncthreads();
 
     // ---- with a pair buffer: the chunk's rows in bf16, in pair order (summed per key later)
-    if (contrib) {
+    if constexpr (STORE) {
       uint16_t* dst0 = contrib + ((size_t)(row - row0) * k + j0) * DI;
       for (int r = 8 * wv; r < 8 * wv + 8; ++r) {
         if (j0 + r >= k) break;
@@ -338,12 +369,14 @@ hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float*
                               float* dw, float* dk, void* ws, size_t ws_bytes, hipStream_t stream) {
   auto grad = [&](int64_t row0, int64_t rows, uint16_t* contrib) {
     const dim3 grid((unsigned)rows), block(kBwdThreads);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, qI, kI, w, kv_len, idx, dscores, T, S_max,
+                         H_I, k, dq, dw, dk, row0, contrib);
+    };
     if (d_I == 128)
-      hipLaunchKernelGGL(indexer_bwd_kernel<128>, grid, block, 0, stream, qI, kI, w, kv_len, idx,
-                         dscores, T, S_max, H_I, k, dq, dw, dk, row0, contrib);
+      contrib ? go(indexer_bwd_kernel<128, true>) : go(indexer_bwd_kernel<128, false>);
     else
-      hipLaunchKernelGGL(indexer_bwd_kernel<64>, grid, block, 0, stream, qI, kI, w, kv_len, idx,
-                         dscores, T, S_max, H_I, k, dq, dw, dk, row0, contrib);
+      contrib ? go(indexer_bwd_kernel<64, true>) : go(indexer_bwd_kernel<64, false>);
   };
   const int64_t all = (int64_t)B * T;
   if (!ws) {
