@@ -11,6 +11,7 @@
 // The order of a key's pairs depends on atomic arrival, so the last bits of the sums vary
 // from run to run.
 #include <algorithm>
+#include <type_traits>
 
 #include "ix_common.h"
 #include "ix_internal.h"
@@ -22,6 +23,7 @@ namespace {
 constexpr int kScanThreads = 256;
 constexpr int kScanPer = 8;
 constexpr int kScanTile = kScanThreads * kScanPer;
+constexpr int kPairUnroll = 16;  // pair rows in flight per wave in the key sums
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -155,31 +157,52 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, c
     float acc[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-    auto add_pair = [&](uint32_t pr) {
-      const uint16_t* src = contrib + ((size_t)pr * H + h) * W + part * (W / 2) + col;
+    // this lane's EPL bf16 of one pair row, and their sum into acc
+    using Raw = std::conditional_t<EPL == 4, uint2, std::conditional_t<EPL == 2, uint32_t, uint16_t>>;
+    auto load_pair = [&](uint32_t pr) -> Raw {
+      return *reinterpret_cast<const Raw*>(contrib + ((size_t)pr * H + h) * W + part * (W / 2) + col);
+    };
+    auto add_raw = [&](Raw v) {
       if constexpr (EPL == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
         acc[0] += bf16_bits_to_f32(v.x & 0xFFFFu);
         acc[1] += bf16_bits_to_f32(v.x >> 16);
         acc[2] += bf16_bits_to_f32(v.y & 0xFFFFu);
         acc[3] += bf16_bits_to_f32(v.y >> 16);
       } else if constexpr (EPL == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(src);
         acc[0] += bf16_bits_to_f32(v & 0xFFFFu);
         acc[1] += bf16_bits_to_f32(v >> 16);
       } else {
-        acc[0] += bf16_bits_to_f32(*src);
+        acc[0] += bf16_bits_to_f32(v);
       }
     };
+    // The key's pair rows, kPairUnroll at a time, summed in segment order: the rows of a
+    // group are all in flight at once, and the positions of the next group load meanwhile.
+    constexpr int U = kPairUnroll;
     uint32_t e = n0;
-    for (; e + 4 <= n1; e += 4) {
-      const uint32_t p0 = inv[e], p1 = inv[e + 1], p2 = inv[e + 2], p3 = inv[e + 3];
-      add_pair(p0);
-      add_pair(p1);
-      add_pair(p2);
-      add_pair(p3);
+    if (n1 - n0 >= (uint32_t)U) {
+      uint32_t pr[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) pr[i] = inv[e + i];
+      while (true) {
+        const uint32_t en = e + U;
+        const bool more = en + U <= n1;
+        uint32_t nx[U] = {};
+        if (more) {
+#pragma unroll
+          for (int i = 0; i < U; ++i) nx[i] = inv[en + i];
+        }
+        Raw raw[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) raw[i] = load_pair(pr[i]);
+#pragma unroll
+        for (int i = 0; i < U; ++i) add_raw(raw[i]);
+        e = en;
+        if (!more) break;
+#pragma unroll
+        for (int i = 0; i < U; ++i) pr[i] = nx[i];
+      }
     }
-    for (; e < n1; ++e) add_pair(inv[e]);
+    for (; e < n1; ++e) add_raw(load_pair(inv[e]));
     float* dst = (part ? dst_b : dst_a) + ((size_t)g * H + h) * stride + col;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) dst[i] += acc[i];
