@@ -141,8 +141,11 @@ ix_status sparse_attn_fwd(const void *q, const void *kc, const void *vc, const i
  * q, kc, vc, idx, kv_len, B..sm_scale: as passed to sparse_attn_fwd; out and lse: its
  * outputs for these inputs (lse is required); dout: bf16 [B, T, H_q, d].
  * dq:       fp32 [B, T, H_q, d], written (0 for a query with no valid entry).
- * dkc, dvc: fp32 [B, S_max, H_kv, d], ADDED TO; the caller clears them first.  The order
- *           of the additions, and so the last bits, vary from run to run.
+ * dkc, dvc: fp32 [B, S_max, H_kv, d], ADDED TO; the caller clears them first.  With
+ *           atomics the order of the additions, and so the last bits, vary from run to run.
+ *           The atomic-free form adds each key's pairs in query-row order: for a given
+ *           workspace size (which sets the passes) the result is bitwise the same every run,
+ *           except that the entries of one row that repeat a key may add in either order.
  * ws, ws_bytes: NULL and 0 -> dK / dV rows are added with fp32 atomics, 2 d per selected
  *           pair.  A workspace (16-byte aligned, at least sparse_attn_bwd_workspace_bytes(...,
  *           1) bytes, contents clobbered) -> no atomics: the query rows are taken in passes
@@ -231,8 +234,9 @@ ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const
  * idx:     int32 [B, T, k] (ix_topk's output or any selection; invalid entries are skipped).
  * dscores: fp32 [B, T, k] (ix_indexer_kl's dscores); ignored at invalid entries.
  * dq_I:    fp32 [B, T, H_I, d_I], written.   dw: fp32 [B, T, H_I], written.
- * dk_I:    fp32 [B, S_max, d_I], ADDED TO; the caller clears it first.  The order of the
- *          additions, and so the last bits, vary from run to run.
+ * dk_I:    fp32 [B, S_max, d_I], ADDED TO; the caller clears it first.  With atomics the
+ *          order of the additions, and so the last bits, vary from run to run; the
+ *          atomic-free form is bitwise reproducible as for sparse_attn_bwd.
  * ws, ws_bytes: NULL and 0 -> dk_I rows are added with fp32 atomics, d_I per kept pair.  A
  *          workspace (16-byte aligned, at least ix_indexer_bwd_workspace_bytes(a, k, 1)
  *          bytes, contents clobbered) -> no atomics: passes of as many query rows as it

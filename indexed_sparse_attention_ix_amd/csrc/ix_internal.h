@@ -70,7 +70,8 @@ constexpr int kAttnLayersPerLaunch = 8;
 // rows whose pairs carry row_bytes of bf16 gradient rows each.
 struct PairLayout {
   int64_t n_keys, nparts;
-  size_t off, cur, part, inv, contrib, total;
+  int64_t n_blk, rows_per_blk, n_slots;  // row blocks of the pass; (key, block) counters
+  size_t off, cnt, cur, part_sum, part, inv, contrib, total;
 };
 PairLayout pair_layout(int B, int S_max, int k, int64_t rows, size_t row_bytes);
 int64_t pair_rows_per_pass(int B, int T, int S_max, int k, size_t row_bytes, size_t ws_bytes);

@@ -3,13 +3,17 @@
 // attention's dK / dV and the indexer's dk_I.  The fp32 atomic units of the L2 take about
 // one 32-bit add per clock per channel, which bounds the atomic form at one add per
 // gradient element per kept pair.  Instead, per pass over a range of query rows:
-//  1. count the kept pairs of each key (b, s) and scan the counts into segment offsets;
-//  2. list every pair's position in the pass under its key (the inverted selection);
+//  1. count the kept pairs of each key (b, s) per block of consecutive query rows, scan the
+//     keys' totals into segment offsets, and split each segment by row block: key g's
+//     segment holds block 0's pairs, then block 1's, and so on;
+//  2. list every pair's position in the pass under its key (the inverted selection): one
+//     workgroup per row block takes its rows in order, so each key's pairs come in row
+//     order and the lists, and the sums below, are the same on every run;
 //  3. the gradient kernel writes each pair's rows (bf16) in pair order;
 //  4. one wave per (key, head) sums its pairs' rows in fp32 and adds the sums to the
 //     gradient rows with ordinary loads and stores (the wave owns those rows).
-// The order of a key's pairs depends on atomic arrival, so the last bits of the sums vary
-// from run to run.
+// Only entries of one query row that repeat a key take an arrival order among themselves.
+// The attention's rows of such entries are equal, so their order changes nothing there.
 #include <algorithm>
 #include <type_traits>
 
@@ -24,6 +28,8 @@ constexpr int kScanThreads = 256;
 constexpr int kScanPer = 8;
 constexpr int kScanTile = kScanThreads * kScanPer;
 constexpr int kPairUnroll = 16;  // pair rows in flight per wave in the key sums
+constexpr int64_t kMaxSlots = (int64_t)1 << 26;  // (key, row block) counters per pass
+constexpr int64_t kBlkChunk = 64;                // row blocks per partial sum
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -44,12 +50,60 @@ __device__ __forceinline__ int64_t pair_key(const int32_t* idx, const int32_t* k
   return (s >= 0 && s < kvl) ? (int64_t)b * S_max + s : -1;
 }
 
+// Counts per (row block, key), block-major: cnt[((row in pass) / rows_per_blk) * n_keys + g].
 __global__ __launch_bounds__(256) void pair_count_kernel(const int32_t* idx, const int32_t* kv_len,
                                                          int T, int S_max, int k, int64_t row0,
-                                                         int64_t pairs, uint32_t* cnt) {
+                                                         int64_t pairs, int64_t n_keys,
+                                                         int64_t rows_per_blk, uint32_t* cnt) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < pairs; e += (int64_t)gridDim.x * 256) {
     const int64_t g = pair_key(idx, kv_len, T, S_max, k, row0, e);
-    if (g >= 0) atomicAdd(cnt + g, 1u);
+    if (g >= 0) atomicAdd(cnt + ((e / k) / rows_per_blk) * n_keys + g, 1u);
+  }
+}
+
+// Row blocks are taken in chunks of kBlkChunk.  part_sum[c * n_keys + g] = key g's pairs in
+// chunk c of the row blocks.
+__global__ __launch_bounds__(256) void pair_chunk_sums(const uint32_t* cnt, int64_t n_keys,
+                                                       int64_t n_blk, uint32_t* part_sum) {
+  const int64_t n_chunks = (n_blk + kBlkChunk - 1) / kBlkChunk;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < n_chunks * n_keys;
+       it += (int64_t)gridDim.x * 256) {
+    const int64_t c = it / n_keys, g = it % n_keys;
+    const int64_t b1 = std::min<int64_t>(n_blk, (c + 1) * kBlkChunk);
+    uint32_t t = 0;
+    for (int64_t blk = c * kBlkChunk; blk < b1; ++blk) t += cnt[blk * n_keys + g];
+    part_sum[it] = t;
+  }
+}
+
+// tot[g] = key g's pairs over all row blocks (tot[n_keys] = 0, the scan's end slot).
+__global__ __launch_bounds__(256) void pair_key_totals(const uint32_t* part_sum, int64_t n_keys,
+                                                       int64_t n_chunks, uint32_t* tot) {
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g <= n_keys; g += (int64_t)gridDim.x * 256) {
+    uint32_t t = 0;
+    if (g < n_keys)
+      for (int64_t c = 0; c < n_chunks; ++c) t += part_sum[c * n_keys + g];
+    tot[g] = t;
+  }
+}
+
+// With tot scanned into segment offsets: cnt[blk][g] becomes where row block blk's pairs of
+// key g start (the segment start plus the earlier blocks' counts).
+__global__ __launch_bounds__(256) void pair_block_offsets(uint32_t* cnt, int64_t n_keys,
+                                                          int64_t n_blk, const uint32_t* part_sum,
+                                                          const uint32_t* off) {
+  const int64_t n_chunks = (n_blk + kBlkChunk - 1) / kBlkChunk;
+  for (int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x; it < n_chunks * n_keys;
+       it += (int64_t)gridDim.x * 256) {
+    const int64_t c = it / n_keys, g = it % n_keys;
+    uint32_t run = off[g];
+    for (int64_t c2 = 0; c2 < c; ++c2) run += part_sum[c2 * n_keys + g];
+    const int64_t b1 = std::min<int64_t>(n_blk, (c + 1) * kBlkChunk);
+    for (int64_t blk = c * kBlkChunk; blk < b1; ++blk) {
+      const uint32_t v = cnt[blk * n_keys + g];
+      cnt[blk * n_keys + g] = run;
+      run += v;
+    }
   }
 }
 
@@ -120,13 +174,36 @@ __global__ __launch_bounds__(kScanThreads) void pair_scan_apply(uint32_t* cnt, i
   }
 }
 
+// One workgroup per row block, its rows one at a time: the entries of a row are spread over
+// the threads, and a barrier separates rows, so a slot's cursor counts the block's earlier
+// rows and each key lists its pairs in row order.
 __global__ __launch_bounds__(256) void pair_fill_inv_kernel(const int32_t* idx, const int32_t* kv_len,
                                                             int T, int S_max, int k, int64_t row0,
-                                                            int64_t pairs, const uint32_t* off,
-                                                            uint32_t* cur, uint32_t* inv) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < pairs; e += (int64_t)gridDim.x * 256) {
-    const int64_t g = pair_key(idx, kv_len, T, S_max, k, row0, e);
-    if (g >= 0) inv[off[g] + atomicAdd(cur + g, 1u)] = (uint32_t)e;
+                                                            int64_t rows, int64_t n_keys,
+                                                            int64_t rows_per_blk,
+                                                            const uint32_t* start, uint32_t* cur,
+                                                            uint32_t* inv) {
+  constexpr int kPer = 8;  // entries of a row per thread, all in flight together
+  const int64_t blk = blockIdx.x;
+  const uint32_t* st = start + blk * n_keys;
+  uint32_t* cu = cur + blk * n_keys;
+  const int64_t r_end = std::min<int64_t>(rows, (blk + 1) * rows_per_blk);
+  for (int64_t r = blk * rows_per_blk; r < r_end; ++r) {
+    for (int j0 = 0; j0 < k; j0 += 256 * kPer) {
+      int64_t g[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int j = j0 + i * 256 + (int)threadIdx.x;
+        g[i] = j < k ? pair_key(idx, kv_len, T, S_max, k, row0, r * k + j) : -1;
+      }
+      uint32_t pos[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) pos[i] = g[i] >= 0 ? st[g[i]] + atomicAdd(cu + g[i], 1u) : 0u;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (g[i] >= 0) inv[pos[i]] = (uint32_t)(r * k + j0 + i * 256 + (int)threadIdx.x);
+    }
+    __syncthreads();
   }
 }
 
@@ -134,10 +211,11 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
   return __builtin_bit_cast(float, v << 16);
 }
 
-// One wave per (key, head), grid-stride over all of them.  A pair's row for head h is W
-// bf16 at contrib + (pair * H + h) * W; lanes 0..31 sum elements [0, W/2) into dst_a,
-// lanes 32..63 elements [W/2, W) into dst_b, EPL consecutive columns each, four pairs in
-// flight; the sums are added to row (key * H + h) of stride `stride` floats.
+// One wave per (key, head), grid-stride over all of them.  Key g's pairs are
+// inv[off[g] .. off[g + 1]).  A pair's row for head h is W bf16 at contrib + (pair * H
+// + h) * W; lanes 0..31 sum elements [0, W/2) into dst_a, lanes 32..63 elements [W/2, W) into
+// dst_b, EPL consecutive columns each; the sums are added to row (key * H + h) of stride
+// `stride` floats.
 template <int W>
 __global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, const uint32_t* inv,
                                                           const uint16_t* contrib, int64_t n_keys,
@@ -216,10 +294,18 @@ dim3 grid_for(int64_t n) { return dim3((unsigned)std::min<int64_t>((n + 255) / 2
 PairLayout pair_layout(int B, int S_max, int k, int64_t rows, size_t row_bytes) {
   PairLayout L{};
   L.n_keys = (int64_t)B * S_max;
+  // row blocks: at least 8 rows each, and at most 2^26 (key, block) slots in all
+  const int64_t by_slots = std::max<int64_t>(1, kMaxSlots / std::max<int64_t>(L.n_keys, 1));
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>((rows + 7) / 8, by_slots));
+  L.rows_per_blk = std::max<int64_t>(1, (rows + want - 1) / want);
+  L.n_blk = std::max<int64_t>(1, (rows + L.rows_per_blk - 1) / L.rows_per_blk);
+  L.n_slots = L.n_keys * L.n_blk;
   L.nparts = (L.n_keys + 1 + kScanTile - 1) / kScanTile;
   L.off = 0;
-  L.cur = L.off + up256((size_t)(L.n_keys + 1) * 4);
-  L.part = L.cur + up256((size_t)L.n_keys * 4);
+  L.cnt = L.off + up256((size_t)(L.n_keys + 1) * 4);
+  L.cur = L.cnt + up256((size_t)L.n_slots * 4);
+  L.part_sum = L.cur + up256((size_t)L.n_slots * 4);
+  L.part = L.part_sum + up256((size_t)((L.n_blk + kBlkChunk - 1) / kBlkChunk) * L.n_keys * 4);
   L.inv = L.part + up256((size_t)L.nparts * 4);
   L.contrib = L.inv + up256((size_t)rows * k * 4);
   L.total = L.contrib + up256((size_t)rows * k * row_bytes);
@@ -249,17 +335,26 @@ hipError_t launch_pair_index(const int32_t* idx, const int32_t* kv_len, int T, i
   uint32_t* part = reinterpret_cast<uint32_t*>(w + L.part);
   uint32_t* inv = reinterpret_cast<uint32_t*>(w + L.inv);
   const int64_t pairs = rows * k;
-  hipLaunchKernelGGL(pair_zero_kernel, grid_for(L.n_keys + 1), dim3(256), 0, stream, off, L.n_keys + 1);
-  hipLaunchKernelGGL(pair_zero_kernel, grid_for(L.n_keys), dim3(256), 0, stream, cur, L.n_keys);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
+  hipLaunchKernelGGL(pair_zero_kernel, grid_for(L.n_slots), dim3(256), 0, stream, cnt, L.n_slots);
+  hipLaunchKernelGGL(pair_zero_kernel, grid_for(L.n_slots), dim3(256), 0, stream, cur, L.n_slots);
   hipLaunchKernelGGL(pair_count_kernel, grid_for(pairs), dim3(256), 0, stream, idx, kv_len, T, S_max,
-                     k, row0, pairs, off);
+                     k, row0, pairs, L.n_keys, L.rows_per_blk, cnt);
+  uint32_t* part_sum = reinterpret_cast<uint32_t*>(w + L.part_sum);
+  const int64_t n_chunks = (L.n_blk + kBlkChunk - 1) / kBlkChunk;
+  hipLaunchKernelGGL(pair_chunk_sums, grid_for(n_chunks * L.n_keys), dim3(256), 0, stream, cnt,
+                     L.n_keys, L.n_blk, part_sum);
+  hipLaunchKernelGGL(pair_key_totals, grid_for(L.n_keys + 1), dim3(256), 0, stream, part_sum,
+                     L.n_keys, n_chunks, off);
   hipLaunchKernelGGL(pair_scan_tiles, dim3((unsigned)L.nparts), dim3(kScanThreads), 0, stream, off,
                      L.n_keys + 1, part);
   hipLaunchKernelGGL(pair_scan_top, dim3(1), dim3(1024), 0, stream, part, L.nparts);
   hipLaunchKernelGGL(pair_scan_apply, dim3((unsigned)L.nparts), dim3(kScanThreads), 0, stream, off,
                      L.n_keys + 1, part);
-  hipLaunchKernelGGL(pair_fill_inv_kernel, grid_for(pairs), dim3(256), 0, stream, idx, kv_len, T,
-                     S_max, k, row0, pairs, off, cur, inv);
+  hipLaunchKernelGGL(pair_block_offsets, grid_for(n_chunks * L.n_keys), dim3(256), 0, stream, cnt,
+                     L.n_keys, L.n_blk, part_sum, off);
+  hipLaunchKernelGGL(pair_fill_inv_kernel, dim3((unsigned)L.n_blk), dim3(256), 0, stream, idx, kv_len,
+                     T, S_max, k, row0, rows, L.n_keys, L.rows_per_blk, cnt, cur, inv);
   return hipGetLastError();
 }
 

@@ -123,6 +123,31 @@ def test_backward_atomic_free_matches_atomics():
         assert err <= 4e-3 * float(x.norm()), f"{('dK', 'dV')[n]}: {err:.3e} vs {float(x.norm()):.3e}"
 
 
+def test_atomic_free_backward_is_reproducible():
+    """Without atomics each key lists its pairs in row order, so dK and dV are bitwise equal
+    from run to run: one pass over many row blocks, and passes of 50 rows.  Keys drawn from a
+    short range are kept by many rows, so their segments span many row blocks."""
+    say("[sparse_attn_bwd] atomic-free determinism")
+    g = torch.Generator(device="cpu").manual_seed(91)
+    B, T, S, H_q, H_kv, d, k = 2, 400, 900, 16, 1, 128, 192
+    q = (torch.randn(B, T, H_q, d, generator=g) * 0.3).to(torch.bfloat16).to(DEV)
+    K = (torch.randn(B, S, H_kv, d, generator=g) * 0.3).to(torch.bfloat16).to(DEV)
+    V = torch.randn(B, S, H_kv, d, generator=g).to(torch.bfloat16).to(DEV)
+    dout = torch.randn(B, T, H_q, d, generator=g).to(torch.bfloat16).to(DEV)
+    rng = np.random.default_rng(91)
+    idx = np.stack([np.stack([np.sort(rng.choice(S // 3, size=k, replace=False)) for _ in range(T)])
+                    for _ in range(B)]).astype(np.int32)
+    didx = torch.from_numpy(idx).to(DEV)
+    scale = d ** -0.5
+    out, lse = bd.sparse_attention(q, K, V, didx, scale, with_lse=True)
+    for rows_per_pass in (1 << 20, 50):
+        runs = [bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, scale,
+                                             rows_per_pass=rows_per_pass) for _ in range(2)]
+        torch.cuda.synchronize()
+        for x, y, name in zip(runs[0], runs[1], ("dq", "dK", "dV")):
+            assert torch.equal(x, y), f"{name} differs between runs ({rows_per_pass} rows per pass)"
+
+
 @pytest.mark.parametrize("rows_per_pass", [None, 10])
 def test_group_backward_shares_the_inversion(rows_per_pass):
     """indexshare_group_bwd: three layers over one selection, the selection inverted once per

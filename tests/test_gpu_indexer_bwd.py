@@ -191,3 +191,15 @@ def test_indexer_bwd_deterministic_dq_dw():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     scale = np.abs(a[2]).max()
     assert np.abs(a[2] - b[2]).max() <= 1e-5 * scale
+
+
+def test_indexer_bwd_atomic_free_is_reproducible():
+    """Without atomics each key lists its pairs in row order, so dk_I too is bitwise equal from
+    run to run: one pass over many row blocks, and passes of 40 rows."""
+    say("[ix_indexer_bwd] atomic-free determinism")
+    qI, kI, w, kvl, idx, ds = _case(207, 2, 300, 700, 64, 128, 160, [700, 650])
+    for rows_per_pass in (1 << 20, 40):
+        a = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=rows_per_pass)
+        b = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=rows_per_pass)
+        for x, y, name in zip(a, b, ("dq_I", "dw", "dk_I")):
+            assert np.array_equal(x, y), f"{name} differs between runs ({rows_per_pass} rows per pass)"
