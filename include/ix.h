@@ -285,6 +285,32 @@ ix_status indexshare_group_fwd(const ix_indexer_args *a, int32_t k, int32_t n_la
                                int32_t H_q, int32_t H_kv, int32_t d, float sm_scale,
                                int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the library's own scratch for indexshare_group_fwd_noalloc (64 MiB per GPU). */
+#define IX_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * indexshare_group_fwd_noalloc -- indexshare_group_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same validation, kernels and results (bit for bit), but the workspace is
+ * a scratch array inside the library, IX_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the
+ * library runs on holds from the first call on it until the process ends.  The call
+ * allocates nothing.  The caller still passes inputs and outputs (idx included).
+ * Sizes: the call needs indexshare_workspace_bytes(a, k, H_q, H_kv, d) <= the scratch
+ * (a decode step of up to about 128 sequences at 128K keys with top-2048 fits); larger
+ * calls return IX_ERR_WORKSPACE before launching anything.
+ * Concurrency: every call on one GPU uses that GPU's one scratch array, so calls that
+ * overlap on one GPU (on different streams, or from different threads) race and give
+ * undefined results; calls on one stream, or serialised by the caller, are safe.  Nothing
+ * in the scratch needs to be cleared between calls.
+ * Errors: as indexshare_group_fwd; IX_ERR_HIP also if the scratch's device address cannot
+ * be found (first call on a device).
+ */
+ix_status indexshare_group_fwd_noalloc(const ix_indexer_args *a, int32_t k, int32_t n_layers,
+                                       const void *const *q, const void *const *kc,
+                                       const void *const *vc, void *const *out,
+                                       float *const *lse, int32_t H_q, int32_t H_kv, int32_t d,
+                                       float sm_scale, int32_t *idx, hipStream_t stream);
+
 /*
  * IndexPool: pooling four indexer keys into one to cut long-context indexing cost
  * (GLM-5.3-Flash as recorded on worldresearchstate.com, "What changed").  The page says

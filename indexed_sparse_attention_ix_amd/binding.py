@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 # every symbol include/ix.h declares
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
            "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
-           "indexshare_group_fwd", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
+           "indexshare_group_fwd", "indexshare_group_fwd_noalloc", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
            "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "indexshare_group_bwd", "ix_indexer_kl", "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes", "ix_peak_mfma_fp8", "ix_peak_copy",
            "ix_peak_gather", "ix_peak_atomic_add")
 
@@ -82,6 +82,11 @@ def load(path: str = LIB_PATH):
                                        P(c_void_p), P(c_void_p), P(c_void_p), P(c_void_p),
                                        c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                        c_size_t, c_void_p]
+    L.indexshare_group_fwd_noalloc.restype = c_int32
+    L.indexshare_group_fwd_noalloc.argtypes = [P(IndexerArgs), c_int32, c_int32, P(c_void_p),
+                                               P(c_void_p), P(c_void_p), P(c_void_p),
+                                               P(c_void_p), c_int32, c_int32, c_int32, c_float,
+                                               c_void_p, c_void_p]
     L.sparse_attn_bwd.restype = c_int32
     L.sparse_attn_bwd.argtypes = ([c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4 +
                                   [c_size_t, c_void_p])
@@ -187,6 +192,25 @@ def indexshare_group_fwd(args: IndexerArgs, k, n_layers, q, kc, vc, out, lse, H_
     _check(load().indexshare_group_fwd(ctypes.byref(args), k, n_layers, conv[0], conv[1],
                                        conv[2], conv[3], conv[4], H_q, H_kv, d, sm_scale, idx,
                                        ws, ws_bytes, stream))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # IX_NOALLOC_SCRATCH_BYTES of include/ix.h
+
+
+def indexshare_group_fwd_noalloc(args: IndexerArgs, k, n_layers, q, kc, vc, out, lse, H_q, H_kv,
+                                 d, sm_scale, idx, stream=0):
+    keep = []
+    conv = []
+    for ptrs in (q, kc, vc, out, lse):
+        r = _ptr_array(ptrs)
+        if r is None:
+            conv.append(None)
+        else:
+            conv.append(r[0])
+            keep.append(r[1])
+    _check(load().indexshare_group_fwd_noalloc(ctypes.byref(args), k, n_layers, conv[0], conv[1],
+                                               conv[2], conv[3], conv[4], H_q, H_kv, d, sm_scale,
+                                               idx, stream))
 
 
 def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I_cache,

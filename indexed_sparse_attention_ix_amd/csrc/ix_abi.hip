@@ -6,10 +6,17 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "ix_internal.h"
 #include "../../include/ix_peaks.h"
+
+// Scratch of indexshare_group_fwd_noalloc: device memory the library owns instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy of this array until
+// the process ends; host code uses the per-device address from hipGetSymbolAddress, never
+// the array's name (which in host code is only a stand-in).
+static __device__ __align__(256) unsigned char scratch[IX_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -124,6 +131,78 @@ ix_status check_attn_ptrs(const void* q, const void* kc, const void* vc, const i
   return IX_OK;
 }
 
+// Address of this device's copy of `scratch`: looked up once per device, with that device
+// current, and kept.  The device is the stream's (the current one for the NULL stream).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t device_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// indexshare_group_fwd, with the caller's workspace or (use_scratch) the library's scratch.
+ix_status group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_layers, const void* const* q,
+                    const void* const* kc, const void* const* vc, void* const* out,
+                    float* const* lse, int32_t H_q, int32_t H_kv, int32_t d, float sm_scale,
+                    int32_t* idx, void* ws, size_t ws_bytes, bool use_scratch, hipStream_t stream) {
+  bool empty = false, empty2 = false;
+  ix_status st = check_indexer(a, &empty);
+  if (st != IX_OK) return st;
+  if ((st = check_k(k)) != IX_OK) return st;
+  if ((st = check_attn_shape(a->B, a->T, a->S_max, H_q, H_kv, d, k, &empty2)) != IX_OK) return st;
+  if (n_layers < 1) return fail(IX_ERR_INVALID, "n_layers=%d must be >= 1", n_layers);
+  if (empty) return ok();
+  if (!idx) return fail(IX_ERR_INVALID, "idx pointer is NULL");
+  if (!q || !kc || !vc || !out) return fail(IX_ERR_INVALID, "NULL per-layer pointer array");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_attn_ptrs(q[l], kc[l], vc[l], idx, out[l])) != IX_OK) return st;
+  }
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  const ix::TopkPlan tp = ix::make_topk_plan(*a, k);
+  const ix::AttnPlan ap = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k);
+  const int per_launch = n_layers < ix::kAttnLayersPerLaunch ? n_layers : ix::kAttnLayersPerLaunch;
+  const size_t attn_need = (size_t)per_launch * ap.ws_bytes;
+  const size_t need = tp.ws_bytes > attn_need ? tp.ws_bytes : attn_need;
+  if (use_scratch) {
+    if (need > IX_NOALLOC_SCRATCH_BYTES)
+      return fail(IX_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu",
+                  need, (size_t)IX_NOALLOC_SCRATCH_BYTES);
+    const hipError_t es = device_scratch(stream, &ws);
+    if (es != hipSuccess) return hip_fail(es, "no-allocation scratch address");
+    ws_bytes = IX_NOALLOC_SCRATCH_BYTES;
+  }
+  if (!ws || ws_bytes < need)
+    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
+  hipError_t e = ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexshare selection launch");
+  e = ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, a->kv_len, a->B, a->T, a->S_max,
+                                    H_q, H_kv, d, k, sm_scale, out, lse, ap, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexshare attention launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,33 +295,17 @@ ix_status indexshare_group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_la
                                void* const* out, float* const* lse, int32_t H_q, int32_t H_kv,
                                int32_t d, float sm_scale, int32_t* idx, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
-  bool empty = false, empty2 = false;
-  ix_status st = check_indexer(a, &empty);
-  if (st != IX_OK) return st;
-  if ((st = check_k(k)) != IX_OK) return st;
-  if ((st = check_attn_shape(a->B, a->T, a->S_max, H_q, H_kv, d, k, &empty2)) != IX_OK) return st;
-  if (n_layers < 1) return fail(IX_ERR_INVALID, "n_layers=%d must be >= 1", n_layers);
-  if (empty) return ok();
-  if (!idx) return fail(IX_ERR_INVALID, "idx pointer is NULL");
-  if (!q || !kc || !vc || !out) return fail(IX_ERR_INVALID, "NULL per-layer pointer array");
-  for (int l = 0; l < n_layers; ++l) {
-    if ((st = check_attn_ptrs(q[l], kc[l], vc[l], idx, out[l])) != IX_OK) return st;
-  }
-  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
-    return fail(IX_ERR_INVALID, "sm_scale must be finite");
-  const ix::TopkPlan tp = ix::make_topk_plan(*a, k);
-  const ix::AttnPlan ap = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k);
-  const int per_launch = n_layers < ix::kAttnLayersPerLaunch ? n_layers : ix::kAttnLayersPerLaunch;
-  const size_t attn_need = (size_t)per_launch * ap.ws_bytes;
-  const size_t need = tp.ws_bytes > attn_need ? tp.ws_bytes : attn_need;
-  if (!ws || ws_bytes < need)
-    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
-  hipError_t e = ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream);
-  if (e != hipSuccess) return hip_fail(e, "indexshare selection launch");
-  e = ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, a->kv_len, a->B, a->T, a->S_max,
-                                    H_q, H_kv, d, k, sm_scale, out, lse, ap, ws, stream);
-  if (e != hipSuccess) return hip_fail(e, "indexshare attention launch");
-  return ok();
+  return group_fwd(a, k, n_layers, q, kc, vc, out, lse, H_q, H_kv, d, sm_scale, idx, ws, ws_bytes,
+                   false, stream);
+}
+
+ix_status indexshare_group_fwd_noalloc(const ix_indexer_args* a, int32_t k, int32_t n_layers,
+                                       const void* const* q, const void* const* kc,
+                                       const void* const* vc, void* const* out,
+                                       float* const* lse, int32_t H_q, int32_t H_kv, int32_t d,
+                                       float sm_scale, int32_t* idx, hipStream_t stream) {
+  return group_fwd(a, k, n_layers, q, kc, vc, out, lse, H_q, H_kv, d, sm_scale, idx, nullptr, 0,
+                   true, stream);
 }
 
 ix_status ix_append_kv(const float* k_I_new, const void* K_new, const void* V_new,

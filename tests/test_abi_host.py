@@ -137,6 +137,34 @@ def test_indexshare_validation_codes():
                                   ctypes.c_float(0.1), FAKE, FAKE, need, None) == bd.IX_ERR_UNSUPPORTED
 
 
+def test_noalloc_validation_codes():
+    # the no-allocation group call validates like indexshare_group_fwd and refuses, before
+    # looking up its scratch or launching, a call whose workspace would exceed the scratch
+    L = bd.load()
+    P = ctypes.POINTER(ctypes.c_void_p)
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    pa = ctypes.cast(arr, P)
+    fn = L.indexshare_group_fwd_noalloc
+    a = args()
+    assert fn(ctypes.byref(a), 64, 0, pa, pa, pa, pa, None, 16, 1, 128, ctypes.c_float(0.1),
+              FAKE, None) == bd.IX_ERR_INVALID
+    assert fn(ctypes.byref(a), 64, 4, pa, pa, pa, pa, None, 16, 1, 128, ctypes.c_float(0.1),
+              None, None) == bd.IX_ERR_INVALID
+    assert fn(ctypes.byref(a), 64, 4, pa, pa, pa, pa, None, 16, 1, 96, ctypes.c_float(0.1),
+              FAKE, None) == bd.IX_ERR_UNSUPPORTED
+    big = args(T=4096, S_max=4096)
+    assert bd.indexshare_workspace_bytes(big, 2048, 16, 1, 128) > bd.NOALLOC_SCRATCH_BYTES
+    assert fn(ctypes.byref(big), 2048, 4, pa, pa, pa, pa, None, 16, 1, 128, ctypes.c_float(0.1),
+              FAKE, None) == bd.IX_ERR_WORKSPACE
+    assert "scratch" in bd.ix_last_error()
+    # a decode step at 128K keys fits
+    dec = args(B=128, T=1, S_max=131072)
+    assert 0 < bd.indexshare_workspace_bytes(dec, 2048, 16, 1, 128) <= bd.NOALLOC_SCRATCH_BYTES
+    empty = args(B=0)
+    assert fn(ctypes.byref(empty), 64, 4, pa, pa, pa, pa, None, 16, 1, 128, ctypes.c_float(0.1),
+              FAKE, None) == bd.IX_OK
+
+
 def test_append_validation_codes():
     ok = dict(kn=FAKE, Kn=FAKE, Vn=FAKE, pos0=FAKE, B=2, T=1, S=64, d_I=128, H_kv=1, d=128,
               kc=FAKE, Kc=FAKE, Vc=FAKE)
