@@ -308,6 +308,62 @@ def sparse_attention_backward_rows(q_bits, K_bits, V_bits, idx, dout, b: int,
     return dq, dK, dV
 
 
+def sparse_attention_backward_magnitudes(q_bits, K_bits, V_bits, idx, dout, b: int,
+                                         rows: Sequence[int], sm_scale: float):
+    """Sums of absolute values along the chain rule of sparse_attention_backward_rows, per
+    gradient entry: the scales that rounding-error bounds of a computed backward are built
+    from (they are not gradients).
+
+    With p, dp_j = dO.V_j, D = sum_j p_j dp_j and dl_j = p_j (dp_j - D) as there, and
+    a_j = sum_c |dO_c V_jc| (the size of dp_j's products), A = sum_j p_j a_j:
+      dq[h, e]:  "ds" = s sum_j |dl_j| |K_je|     "dp" = s sum_j p_j a_j |K_je|
+                 "dd" = s A |sum_j p_j K_je|      "da" = s A sum_j p_j |K_je|
+      dK[j, e]:  "ds" = s sum |dl_j| |q_e|        "dp" = s sum p_j a_j |q_e|
+                 "dd" = s sum p_j A |q_e|         (sums over the (query, head) pairs keeping j)
+      dV[j, e]:  "p"  = sum p_j |dO_e|
+    with s = |sm_scale|.  Returns {"dq": {...}, "dK": {...}, "dV": {...}} of arrays shaped as
+    the corresponding gradients.
+    """
+    Ks = decode_bf16(K_bits[b])
+    V = decode_bf16(V_bits[b])
+    Ka, Va = np.abs(Ks), np.abs(V)
+    S, H_kv, d = Ks.shape
+    H_q = q_bits.shape[2]
+    grp = H_q // H_kv
+    s = abs(sm_scale)
+    zq = lambda: np.zeros((len(rows), H_q, d), dtype=np.float64)  # noqa: E731
+    zk = lambda: np.zeros((S, H_kv, d), dtype=np.float64)  # noqa: E731
+    out = {"dq": {n: zq() for n in ("ds", "dp", "dd", "da")},
+           "dK": {n: zk() for n in ("ds", "dp", "dd")}, "dV": {"p": zk()}}
+    mq, mk, mv = out["dq"], out["dK"], out["dV"]
+    for i, t in enumerate(rows):
+        q = decode_bf16(q_bits[b, t])
+        sel = np.asarray(idx[i])[np.asarray(idx[i]) >= 0]
+        if sel.size == 0:
+            continue
+        for h in range(H_q):
+            g = h // grp
+            logits = sm_scale * (Ks[sel, g, :] @ q[h])
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            do = dout[i, h]
+            dp = V[sel, g, :] @ do
+            D = float(p @ dp)
+            adl = np.abs(p * (dp - D))
+            a = Va[sel, g, :] @ np.abs(do)
+            A = float(p @ a)
+            mq["ds"][i, h] = s * (adl @ Ka[sel, g, :])
+            mq["dp"][i, h] = s * ((p * a) @ Ka[sel, g, :])
+            mq["dd"][i, h] = s * A * np.abs(p @ Ks[sel, g, :])
+            mq["da"][i, h] = s * A * (p @ Ka[sel, g, :])
+            aq = np.abs(q[h])[None, :]
+            np.add.at(mk["ds"][:, g, :], sel, s * adl[:, None] * aq)
+            np.add.at(mk["dp"][:, g, :], sel, s * (p * a)[:, None] * aq)
+            np.add.at(mk["dd"][:, g, :], sel, s * (p * A)[:, None] * aq)
+            np.add.at(mv["p"][:, g, :], sel, p[:, None] * np.abs(do)[None, :])
+    return out
+
+
 def indexer_kl_rows(q_bits, K_bits, idx, scores, b: int, rows: Sequence[int], sm_scale: float,
                     kv_len: int, lse=None):
     """KL objective of the indexer for the listed queries of sequence b.

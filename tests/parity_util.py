@@ -11,18 +11,25 @@ from oracle import ix_oracle as O
 
 # tolerances
 SCORE_RTOL = 1e-2          # indexer scores, relative
-# plus the fp32 accumulation bound: the GPU sums d_I FP8 products per head and H_I
-# weighted heads in fp32, so |err| <= (d_I + H_I + 2) * 2^-24 * sum_h w_h sum_c |q_hc k_c|.
-# It only matters where the exact score is at (or next to) zero, e.g. a head whose dot
-# product cancels exactly; there a relative bound cannot hold.
+# plus the accumulation bound: each head's FP8 MFMA dot product is within FP8_MFMA_REL of
+# sum_c |q_hc k_c|, and the H_I weighted heads are summed in fp32, so
+# |err| <= (FP8_MFMA_REL + (H_I + 2) 2^-24) sum_h w_h sum_c |q_hc k_c|.  It only matters where
+# the exact score is at (or next to) zero, e.g. a head whose dot product cancels exactly;
+# there a relative bound cannot hold.
 FP32_U = 2.0 ** -24
 INDEX_BAND = 1e-3          # swaps allowed among keys within this relative band of the k-th score
 ATTN_MAX_ABS = 2e-2
 ATTN_MEAN_ABS = 2e-3
 ATTN_ROW_REL = 2e-2        # per (row, head) ||o - o_ref||_2 / ||o_ref||_2
 LSE_ABS = 2e-3
-MFMA_REL = 2.0 ** -13      # bound on the FP8 / bf16 MFMAs' accumulation error, relative to the
-                           # sum of the magnitudes of the products (measured up to 7e-5)
+# MFMA dot products of exact products, error relative to the sum of the products' magnitudes
+# (both asserted with a factor-2 margin by test_gpu_mfma_error.py):
+FP8_MFMA_REL = 2.0 ** -10  # FP8 e4m3 16x16x128: its accumulation loses low bits of products of
+                           # mixed sign (measured up to 2.8e-4 on codes spanning the whole range)
+BF16_MFMA_REL = 2.0 ** -19  # bf16 16x16x32: accurate to about one fp32 rounding (8.6e-8 measured)
+FP8_MASK_WINDOW = 2.0 ** -10  # the indexer backward recomputes exactly every x within this times
+                              # |q|_2 |k|_2 of zero, so FP8 MFMA errors must stay below it
+G_SPLIT_REL = 2.0 ** -16   # g as a hi + lo pair of bf16 (round to nearest twice): residual
 
 
 def say(*a):
@@ -45,7 +52,7 @@ def score_magnitude(qI_row_u8, keys_abs, w_row):
 
 
 def score_tolerance(ref, mag, d_I, H_I):
-    return SCORE_RTOL * np.abs(ref) + (d_I + H_I + 2) * FP32_U * mag
+    return SCORE_RTOL * np.abs(ref) + (FP8_MFMA_REL + (H_I + 2) * FP32_U) * mag
 
 
 def check_scores(gpu_rows: np.ndarray, ref_rows: np.ndarray, mag_rows: np.ndarray, d_I, H_I):
@@ -128,6 +135,72 @@ def abs_codes(c):
     return (np.asarray(c) & 0x7F).astype(np.uint8)
 
 
+BF16_U = 2.0 ** -8         # bf16 keeps 8 significant bits: one round-to-nearest is within 2^-8
+
+
+def attn_bwd_bounds(mags, k, n_rows, H_q, d, logit_mag, pair_rows):
+    """Per-entry error bounds (dq, dK, dV) of sparse_attn_bwd, built from the oracle's sums of
+    magnitudes (O.sparse_attention_backward_magnitudes: "ds" the row gradients |dl_j| =
+    p_j |dp_j - D|, "dp" the size p_j a_j of dp's products, "dd"/"da" the shared D term).
+
+    What the kernels round, and what each rounding can move:
+      * P is recomputed in fp32 from the forward's lse: relative error eps_p <= 2.02 *
+        logit_mag * BF16_MFMA_REL (the logits here and inside lse; logit_mag bounds
+        sm_scale sum_c |q_c K_c|) plus fp32 roundings of the exponent, lse and exp2;
+      * dp_j is an MFMA sum of exact bf16 products: off by BF16_MFMA_REL a_j;
+      * D = dout . out uses the forward's bf16 output, off by (2 BF16_U + 2 eps_p) times
+        sum_j p_j |V_jc| per entry, so D is off by cD A; the same error for every key of a
+        (query, head), so in dq it multiplies |sum_j p_j K_j| ("dd"), not sum_j p_j |K_j|;
+      * dS = P (dp - D) is rounded to bf16 (BF16_U) for the products with K (dq) and q (dK),
+        which are MFMA sums (BF16_MFMA_REL) added in fp32 over keys, heads and queries (n 2^-24);
+      * dV sums bf16-rounded P times dout;
+      * the atomic-free form rounds each query's dK and dV pair row to bf16 (one more BF16_U).
+    Every rounding is taken at its worst and in the same direction.
+    """
+    u = FP32_U
+    eps_p = 2.02 * logit_mag * BF16_MFMA_REL + (k + 64 + 8 * logit_mag) * u
+    f = (1 + eps_p) * (1 + BF16_U) * (1 + 4 * u)     # a computed P or dS over the exact one
+    r = (eps_p + BF16_U) * (1 + eps_p) + 2 * u        # relative error of dS (or bf16 P)
+    cD = 2 * BF16_U + 2 * eps_p + (d + 4) * u         # |D_gpu - D| / A
+    g_q = BF16_MFMA_REL + (k + 64) * u                     # sums over the kept keys (dq)
+    g_k = BF16_MFMA_REL + (n_rows * H_q + 64) * u          # sums over heads and queries (dK, dV)
+    pair = BF16_U if pair_rows else 0.0
+    mq, mk, mv = mags["dq"], mags["dK"], mags["dV"]
+    sq = f * (mq["ds"] + BF16_MFMA_REL * mq["dp"] + cD * mq["da"])    # >= s sum_j |dS_gpu| |K_j|
+    b_dq = r * mq["ds"] + f * (BF16_MFMA_REL * mq["dp"] + cD * (mq["dd"] + r * mq["da"])) + g_q * sq
+    sk = f * (mk["ds"] + BF16_MFMA_REL * mk["dp"] + cD * mk["dd"])    # >= s sum |dS_gpu| |q|
+    b_dK = r * mk["ds"] + f * (BF16_MFMA_REL * mk["dp"] + cD * mk["dd"]) + (g_k + pair * (1 + g_k)) * sk
+    b_dV = r * mv["p"] + (g_k + pair * (1 + g_k)) * f * mv["p"]
+    return b_dq, b_dK, b_dV
+
+
+def logit_magnitude(q_f64, K_f64, sm_scale):
+    """max over heads and keys of |sm_scale| sum_c |q_c| |K_c| (an upper bound through the
+    largest |K| entry): q_f64 [..., H_q, d], K_f64 [..., d]."""
+    qa = np.abs(q_f64).reshape(-1, q_f64.shape[-1]).sum(axis=1).max(initial=0.0)
+    return abs(sm_scale) * float(qa) * float(np.abs(K_f64).max(initial=0.0))
+
+
+def check_attn_bwd_entries(got, ref, bound, where="", power=None):
+    """Every entry of got within bound of ref (an entry with bound 0 must be exact).
+    power: also require that a wrong or missing row would be seen, i.e. that at least this
+    fraction of the entries whose reference is not zero exceed their own bound (zeroing them
+    would fail the check).  Returns the worst err / bound."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{where}: {int(bad.sum())} of {bad.size} entries out of tolerance; "
+                           f"e.g. got {got[bad][:3]} ref {ref[bad][:3]} bound {bound[bad][:3]}")
+    if power is not None:
+        nz = ref != 0
+        if nz.any():
+            seen = float((np.abs(ref[nz]) > bound[nz]).mean())
+            assert seen >= power, f"{where}: only {seen:.2f} of entries would show a missing row"
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, 0.0)
+    return float(ratio.max()) if ratio.size else 0.0
+
+
 def _indexer_bwd_oracle(qI, kI, w, idx, ds, kvl):
     """Oracle gradients and their magnitude bounds for every row of every sequence."""
     B, T = idx.shape[:2]
@@ -141,10 +214,23 @@ def _indexer_bwd_oracle(qI, kI, w, idx, ds, kvl):
     return out
 
 
+def indexer_bwd_coefficients(k, n_rows, bf16_rows=False):
+    """Per-entry error bounds of ix_indexer_bwd relative to the oracle's gradients on absolute
+    values (dq_I, dw, dk_I): dq_I and dk_I are bf16 MFMA products of g = dscores * w split into
+    a hi + lo pair of bf16 (G_SPLIT_REL; two MFMAs) with exact e4m3 operands, summed over the
+    kept keys (dq_I) or over heads and the queries keeping a key (dk_I) in fp32; dw sums
+    g max(0, x) with x from the FP8 MFMA (FP8_MFMA_REL).  bf16_rows: the atomic-free form
+    rounds each pair's dk_I row to bf16 (one more 2^-8)."""
+    c_dq = G_SPLIT_REL + 2 * BF16_MFMA_REL + (64 + k) * FP32_U
+    c_dw = FP8_MFMA_REL + (k + 2) * FP32_U
+    c_dk = G_SPLIT_REL + 2 * BF16_MFMA_REL + (64 + n_rows) * FP32_U + (2.0 ** -8 if bf16_rows else 0.0)
+    return c_dq, c_dw, c_dk
+
+
 def check_indexer_bwd(got, qI, kI, w, idx, ds, kvl, extra=None, where="", bf16_rows=False):
     """ix_indexer_bwd outputs got = (dq_I, dw, dk_I) (host arrays) against the oracle, every
     entry, within the bound described in test_gpu_indexer_bwd.py: B = the oracle's gradient on
-    absolute values, times MFMA_REL plus the fp32 additions.  extra: optional per-sequence
+    absolute values, times indexer_bwd_coefficients.  extra: optional per-sequence
     additive bounds (dq, dw, dk) for errors that come in with dscores.  bf16_rows: dk_I came
     through per-pair rows rounded to bf16 (the atomic-free form): each term carries one more
     relative rounding of 2^-9, so dk_I's bound gains 2^-8 B."""
@@ -152,8 +238,7 @@ def check_indexer_bwd(got, qI, kI, w, idx, ds, kvl, extra=None, where="", bf16_r
     B, T, k = idx.shape
     worst = [0.0, 0.0, 0.0]
     for b, (ref, mag) in enumerate(_indexer_bwd_oracle(qI, kI, w, idx, ds, kvl)):
-        tols = (MFMA_REL + (64 + k) * FP32_U, MFMA_REL + (k + 2) * FP32_U,
-                MFMA_REL + (64 + T) * FP32_U + (2.0 ** -8 if bf16_rows else 0.0))
+        tols = indexer_bwd_coefficients(k, T, bf16_rows)
         for n, (g, r, m, tol) in enumerate(zip((dq[b], dw[b], dk[b]), ref, mag, tols)):
             bound = tol * m + (extra[b][n] if extra is not None else 0.0)
             err = np.abs(g.astype(np.float64) - r)

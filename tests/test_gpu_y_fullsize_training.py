@@ -9,14 +9,19 @@ valid set are left out of the checks downstream), its kept scores (which the GPU
 given for those rows, so that both sides start from the same values), the KL loss and score
 gradient, the attention's dq, and the indexer's dq_I and dw with the KL tolerance carried
 through.  dK, dV and dk_I sum over every query that kept a row, which the oracle cannot
-sample, so they are checked through identities that hold at any size: for each query and
-head the row gradients dl_j = p_j (dp_j - D) sum to zero, so sum_j dK_j = 0; sum_j p_j = 1,
-so sum_j dV_j = the sum of dout over the (query, head) pairs with a non-empty selection; and
-the score is linear in w and positively homogeneous of degree 1 in q_I and in k_I, so
-<dk_I, k_I> = <dq_I, q_I> = <dw, w>.  Tolerances as the small-size tests: per query 2e-2
-relative in norm for dq (bf16 P and dS in the products), KL as test_gpu_indexer_kl, the
-indexer gradients per entry as test_gpu_indexer_bwd; the attention identities within 1e-2 of
-the gradients' own size, the indexer identity within 1e-3 of the sum of |terms|.
+sample.  So the test also builds a probe selection: the sampled rows keep the oracle's
+selection, and a set of probe keys taken from it is removed from every other row, so the
+probe keys' gradients are sums over sampled rows only.  The full-size kernels then run on
+that selection, and every entry of dq (sampled rows) and of dK, dV and dk_I (probe keys) is
+checked against the oracle, in both backward forms.  Identities that hold at any size check
+all keys besides: for each query and head the row gradients dl_j = p_j (dp_j - D) sum to
+zero, so sum_j dK_j = 0; sum_j p_j = 1, so sum_j dV_j = the sum of dout over the (query,
+head) pairs with a non-empty selection; and the score is linear in w and positively
+homogeneous of degree 1 in q_I and in k_I, so <dk_I, k_I> = <dq_I, q_I> = <dw, w>.
+Tolerances: the attention gradients per entry as test_gpu_attention_bwd, KL as
+test_gpu_indexer_kl, the indexer gradients per entry as test_gpu_indexer_bwd; the attention
+identities within 1e-2 of the gradients' own size, the indexer identity within 1e-3 of the
+sum of |terms|.
 """
 import numpy as np
 import pytest
@@ -26,7 +31,9 @@ from indexed_sparse_attention_ix_amd import binding as bd
 from indexed_sparse_attention_ix_amd import synth
 from indexed_sparse_attention_ix_amd.workloads import WORKLOADS
 from oracle import ix_oracle as O
-from parity_util import (FP32_U, MFMA_REL, abs_codes, kl_tolerance, oracle_selection, say)
+from parity_util import (FP32_U, abs_codes, attn_bwd_bounds, indexer_bwd_coefficients,
+                         check_attn_bwd_entries, kl_tolerance, logit_magnitude, oracle_selection,
+                         say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -101,13 +108,13 @@ def test_prefill_32k_kl_and_backward_full_size():
     dout_r = dout[0, rows].float().cpu().numpy().astype(np.float64)
     ref_dq, _, _ = O.sparse_attention_backward_rows(q_bits, K_bits, V_bits, ref_idx, dout_r, 0,
                                                     list(range(len(rows))), wl.sm_scale)
+    mags = O.sparse_attention_backward_magnitudes(q_bits, K_bits, V_bits, ref_idx, dout_r, 0,
+                                                  list(range(len(rows))), wl.sm_scale)
     got_dq = dq[0, rows].cpu().numpy()
-    term = wl.sm_scale * float(att["K"].float().abs().max() * dout.float().abs().max() *
-                               att["V"].float().abs().max())
-    for i in sub:
-        err = np.linalg.norm(got_dq[i] - ref_dq[i])
-        assert err <= 2e-2 * np.linalg.norm(ref_dq[i]) + 1e-4 * term * np.sqrt(ref_dq[i].size), \
-            f"dq t={rows[i]}: {err:.3e} vs {np.linalg.norm(ref_dq[i]):.3e}"
+    lmag = logit_magnitude(qf, Kf, wl.sm_scale)
+    bound_dq = attn_bwd_bounds(mags, wl.k, wl.T, wl.H_q, wl.d, lmag, False)[0]
+    check_attn_bwd_entries(got_dq[sub], ref_dq[sub], bound_dq[sub], "dq (sampled rows)",
+                           power=0.5)
 
     # indexer dq_I and dw per sampled query (dk_I through the identity below)
     qI_r = qI_h[0, rows][None]
@@ -118,11 +125,12 @@ def test_prefill_32k_kl_and_backward_full_size():
                                             ref_idx, np.abs(ref_d), 0, list(range(len(rows))), kvl)
     c_dq, c_dw, _ = O.indexer_backward_rows(abs_codes(qI_r), abs_codes(kI_h), np.abs(w_r),
                                             ref_idx, eps_ds, 0, list(range(len(rows))), kvl)
+    coef_I = indexer_bwd_coefficients(wl.k, wl.T)
     g_dq = dq_I[0, rows].cpu().numpy().astype(np.float64)
     g_dw = dw[0, rows].cpu().numpy().astype(np.float64)
     for i in sub:
-        b_dq = (MFMA_REL + (64 + wl.k) * FP32_U) * m_dq[i] + c_dq[i]
-        b_dw = (MFMA_REL + (wl.k + 2) * FP32_U) * m_dw[i] + c_dw[i]
+        b_dq = coef_I[0] * m_dq[i] + c_dq[i]
+        b_dw = coef_I[1] * m_dw[i] + c_dw[i]
         assert np.all(np.abs(g_dq[i] - r_dq[i]) <= b_dq), f"dq_I t={rows[i]}"
         assert np.all(np.abs(g_dw[i] - r_dw[i]) <= b_dw), f"dw t={rows[i]}"
 
@@ -163,3 +171,67 @@ def test_prefill_32k_kl_and_backward_full_size():
     say(f"  ok; |sum dV - want| / |want| = {float((got_dv - want_dv).norm() / want_dv.norm()):.2e}, "
         f"|sum dK| / |dK| = {float(sum_dk.norm() / dK64.norm()):.2e}, indexer identity "
         f"{max(abs(e_q - e_w), abs(e_k - e_w)) / scale_id:.2e} of the sum of |terms|")
+    del dq2, dK2, dV2, dq_I2, dw2, dk_I2, dK, dV, dk_I
+
+    # ------------------------------------------------------------------ probe keys
+    # The sampled rows keep the oracle's selection; probe keys drawn from it (two per sampled
+    # row, plus keys 0 and 1, which the first rows keep) are removed from every other row.
+    # A probe key's dK, dV and dk_I are then sums over sampled rows, which the oracle forms
+    # exactly.  The selection changes, so the forward runs again on it; the KL's score
+    # gradient on the sampled rows is the oracle's (an oracle -> GPU input, rounded to fp32
+    # for both sides).
+    prng = np.random.default_rng(654)
+    probes = {0, 1}
+    for i in range(len(rows)):
+        v = ref_idx[i][ref_idx[i] >= 0]
+        probes |= set(prng.choice(v, size=min(2, len(v)), replace=False).tolist())
+    probes = np.array(sorted(probes), dtype=np.int64)
+    say(f"  probe selection: {len(probes)} probe keys kept only by the {len(rows)} sampled rows")
+    idx2 = idx.clone()
+    idx2[0, rows] = torch.from_numpy(ref_idx.astype(np.int32)).to(DEV)
+    sampled = torch.zeros(wl.T, dtype=torch.bool, device=DEV)
+    sampled[rows] = True
+    probes_t = torch.from_numpy(probes).to(DEV)
+    drop = torch.isin(idx2[0], probes_t) & ~sampled[:, None]
+    idx2[0][drop] = -1
+    del drop
+    out2, lse2 = bd.sparse_attention(att["q"], att["K"], att["V"], idx2, wl.sm_scale,
+                                     kv_len=ind["kv_len"], with_lse=True)
+    dsc2 = dsc.clone()
+    ref_d32 = ref_d.astype(np.float32)
+    dsc2[0, rows] = torch.from_numpy(ref_d32).to(DEV)
+    forms = {}
+    for form, rpp in (("atomics", None), ("atomic-free", 8192)):
+        g3 = bd.sparse_attention_backward(att["q"], att["K"], att["V"], idx2, out2, lse2, dout,
+                                          wl.sm_scale, kv_len=ind["kv_len"], rows_per_pass=rpp)
+        i3 = bd.indexer_bwd(bd.indexer_args(*args), idx2, dsc2, DEV, rows_per_pass=rpp)
+        torch.cuda.synchronize()
+        forms[form] = (g3[0][0, rows].cpu().numpy(),
+                       g3[1][0, probes_t, 0].cpu().numpy(), g3[2][0, probes_t, 0].cpu().numpy(),
+                       i3[2][0, probes_t].cpu().numpy().astype(np.float64))
+        del g3, i3
+    # every probe key is kept by sampled rows only
+    kept_by = torch.isin(idx2[0][~sampled], probes_t).any()
+    assert not bool(kept_by), "a probe key is still kept by a row outside the sample"
+    all_rows = list(range(len(rows)))
+    r_dq, r_dK, r_dV = O.sparse_attention_backward_rows(q_bits, K_bits, V_bits, ref_idx, dout_r, 0,
+                                                        all_rows, wl.sm_scale)
+    mags = O.sparse_attention_backward_magnitudes(q_bits, K_bits, V_bits, ref_idx, dout_r, 0,
+                                                  all_rows, wl.sm_scale)
+    rI = O.indexer_backward_rows(qI_r, kI_h, w_r, ref_idx, ref_d32.astype(np.float64), 0,
+                                 all_rows, kvl)[2]
+    mI = O.indexer_backward_rows(abs_codes(qI_r), abs_codes(kI_h), np.abs(w_r), ref_idx,
+                                 np.abs(ref_d32.astype(np.float64)), 0, all_rows, kvl)[2]
+    n_probe_rows = len(rows)
+    for form, (g_dq, g_dK, g_dV, g_dkI) in forms.items():
+        pair = form == "atomic-free"
+        b_dq, b_dK, b_dV = attn_bwd_bounds(mags, wl.k, n_probe_rows, wl.H_q, wl.d, lmag, pair)
+        w1 = check_attn_bwd_entries(g_dq, r_dq, b_dq, f"{form} dq (sampled rows)", power=0.5)
+        w2 = check_attn_bwd_entries(g_dK, r_dK[probes, 0], b_dK[probes, 0],
+                                    f"{form} dK (probe keys)", power=0.5)
+        w3 = check_attn_bwd_entries(g_dV, r_dV[probes, 0], b_dV[probes, 0],
+                                    f"{form} dV (probe keys)", power=0.5)
+        c_kI = indexer_bwd_coefficients(wl.k, n_probe_rows, pair)[2]
+        w4 = check_attn_bwd_entries(g_dkI, rI[probes], c_kI * mI[probes],
+                                    f"{form} dk_I (probe keys)", power=0.5)
+        say(f"  {form}: worst err / bound: dq {w1:.2e}, dK {w2:.2e}, dV {w3:.2e}, dk_I {w4:.2e}")

@@ -591,6 +591,67 @@ def test_attention_backward_finite_differences_and_closed_forms():
     assert np.allclose(dV[:, 0].sum(axis=0), dout[0, 0])
 
 
+def test_attention_backward_magnitudes_by_enumeration():
+    """Each magnitude is rebuilt with plain Python loops on a tiny input, product by product
+    (dp_j = sum_c dO_c V_jc, D = sum_j p_j dp_j, a_j = sum_c |dO_c V_jc|), and the gradients
+    never exceed their own "ds" (dq, dK) or "p" (dV) magnitudes (triangle inequality: they
+    are exactly those sums taken with signs)."""
+    rng = np.random.default_rng(64)
+    T, S, H_q, H_kv, d, k = 3, 6, 4, 2, 3, 4
+    q = rng.standard_normal((1, T, H_q, d)).astype(np.float32)
+    K = rng.standard_normal((1, S, H_kv, d)).astype(np.float32)
+    V = rng.standard_normal((1, S, H_kv, d)).astype(np.float32)
+    qb, Kb, Vb = (_torch_bf16_bits(torch.from_numpy(x)) for x in (q, K, V))
+    idx = np.array([[0, 2, 5, -1], [1, 2, 3, 4], [3, -1, -1, -1]])
+    dout = rng.standard_normal((T, H_q, d))
+    sc = -0.6
+    m = O.sparse_attention_backward_magnitudes(qb, Kb, Vb, idx, dout, 0, list(range(T)), sc)
+    qv, Kv, Vv = O.decode_bf16(qb)[0], O.decode_bf16(Kb)[0], O.decode_bf16(Vb)[0]
+    bq = {n: np.zeros((T, H_q, d)) for n in ("ds", "dp", "dd", "da")}
+    bk = {n: np.zeros((S, H_kv, d)) for n in ("ds", "dp", "dd")}
+    bv = np.zeros((S, H_kv, d))
+    grp = H_q // H_kv
+    for t in range(T):
+        sel = [int(j) for j in idx[t] if j >= 0]
+        for h in range(H_q):
+            g = h // grp
+            lg = [sc * sum(float(qv[t, h, c]) * float(Kv[j, g, c]) for c in range(d)) for j in sel]
+            ex = [math.exp(x - max(lg)) for x in lg]
+            p = [e / sum(ex) for e in ex]
+            dp = [sum(dout[t, h, c] * Vv[j, g, c] for c in range(d)) for j in sel]
+            D = sum(pj * x for pj, x in zip(p, dp))
+            a = [sum(abs(dout[t, h, c] * Vv[j, g, c]) for c in range(d)) for j in sel]
+            A = sum(pj * x for pj, x in zip(p, a))
+            for e in range(d):
+                bq["ds"][t, h, e] = sum(abs(sc * p[i] * (dp[i] - D) * Kv[j, g, e])
+                                        for i, j in enumerate(sel))
+                bq["dp"][t, h, e] = sum(abs(sc * p[i] * a[i] * Kv[j, g, e]) for i, j in enumerate(sel))
+                bq["dd"][t, h, e] = abs(sc) * A * abs(sum(p[i] * Kv[j, g, e] for i, j in enumerate(sel)))
+                bq["da"][t, h, e] = sum(abs(sc * A * p[i] * Kv[j, g, e]) for i, j in enumerate(sel))
+                for i, j in enumerate(sel):
+                    bk["ds"][j, g, e] += abs(sc * p[i] * (dp[i] - D) * qv[t, h, e])
+                    bk["dp"][j, g, e] += abs(sc * p[i] * a[i] * qv[t, h, e])
+                    bk["dd"][j, g, e] += abs(sc * p[i] * A * qv[t, h, e])
+                    bv[j, g, e] += abs(p[i] * dout[t, h, e])
+    for n in bq:
+        assert np.allclose(m["dq"][n], bq[n], rtol=1e-12, atol=1e-300), n
+    for n in bk:
+        assert np.allclose(m["dK"][n], bk[n], rtol=1e-12, atol=1e-300), n
+    assert np.allclose(m["dV"]["p"], bv, rtol=1e-12, atol=1e-300)
+    dq, dK, dV = O.sparse_attention_backward_rows(qb, Kb, Vb, idx, dout, 0, list(range(T)), sc)
+    assert np.all(np.abs(dq) <= m["dq"]["ds"] * (1 + 1e-12))
+    assert np.all(np.abs(dK) <= m["dK"]["ds"] * (1 + 1e-12))
+    assert np.all(np.abs(dV) <= m["dV"]["p"] * (1 + 1e-12))
+    # terms of one sign: with dout >= 0 every dV term is >= 0, so the magnitude is dV itself
+    _, _, dVp = O.sparse_attention_backward_rows(qb, Kb, Vb, idx, np.abs(dout), 0, list(range(T)), sc)
+    mp = O.sparse_attention_backward_magnitudes(qb, Kb, Vb, idx, np.abs(dout), 0, list(range(T)), sc)
+    assert np.allclose(dVp, mp["dV"]["p"], rtol=1e-12, atol=0)
+    # one kept key: p = 1, dl = 0, so "ds" vanishes and "dd" = "da" = s A |K|
+    one = np.array([[2, -1, -1, -1]])
+    m1 = O.sparse_attention_backward_magnitudes(qb, Kb, Vb, one, dout[:1], 0, [0], sc)
+    assert np.all(m1["dq"]["ds"] == 0) and np.allclose(m1["dq"]["dd"], m1["dq"]["da"])
+
+
 # ---------------------------------------------------------------- indexer KL objective (reading)
 
 
