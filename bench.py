@@ -66,6 +66,11 @@ def parse():
                     help="the JSON line the kernel-trace run printed (quoted beside the trace)")
     ap.add_argument("--profile-commands", nargs=3, metavar=("KT_CMD", "FETCH_CMD", "WRITE_CMD"),
                     default=("", "", ""), help="the three commands, quoted into the summaries")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the decode (decode_b64_128k) and 1M-key (chunk_prefill_1m) legs")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="oracle worker processes for the CPU baseline (at most the host's cores)")
+    ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -223,7 +228,7 @@ def measured_peaks(dev, sh, codes=None):
     codes: e4m3 bytes for the MFMA operands -- the workload's own indexer codes, since the
     MFMA rate depends on the operands' bit activity (power); uniform random codes if None."""
     import torch
-    from indexed_sparse_attention_ix_amd import binding as bd
+    from indexed_sparse_attention_ix_amd import peaks as pk
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(fn, reps=3):
@@ -248,27 +253,81 @@ def measured_peaks(dev, sh, codes=None):
     blocks, iters = 512, 2048
     mfma = {}
     for nv in (0, 4, 8, 12):
-        t = timed(lambda: bd.ix_peak_mfma_fp8(ops.data_ptr(), nv, blocks, iters, chk.data_ptr(), sh))
+        t = timed(lambda: pk.ix_peak_mfma_fp8(ops.data_ptr(), nv, blocks, iters, chk.data_ptr(), sh))
         mfma[str(nv)] = round(blocks * 4 * iters * 16 * 65536 / t / 1e12, 1)
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    t = timed(lambda: bd.ix_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
+    t = timed(lambda: pk.ix_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh))
     copy = round(2 * nbytes / t / 1e9, 1)
-    del src, dst
+    del dst
+    # read-only stream of 2 GiB (past the 256 MB Infinity Cache), as the decode indexer
+    # streams its keys
+    big = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    xr = torch.zeros(4096, dtype=torch.int32, device=dev)
+    t = timed(lambda: pk.ix_peak_read(big.data_ptr(), 2 << 30, xr.data_ptr(), sh))
+    read = round((2 << 30) / t / 1e9, 1)
+    del src, big
     gather = {}
     n = 1 << 25
-    xor = torch.zeros(1, dtype=torch.int32, device=dev)
+    xor = torch.zeros(2048, dtype=torch.int32, device=dev)
     for label, tbytes in (("64MiB", 64 << 20), ("2GiB", 2 << 30)):
         table = torch.empty(tbytes, dtype=torch.uint8, device=dev)
         rows = torch.randint(0, tbytes // 256, (n,), generator=torch.Generator(device="cpu").manual_seed(78),
                              dtype=torch.int32)
         rows = torch.sort(rows.view(-1, 2048), dim=1).values.reshape(-1).to(dev)  # ascending per 2048, like idx rows
-        t = timed(lambda: bd.ix_peak_gather(table.data_ptr(), tbytes, rows.data_ptr(), n, xor.data_ptr(), sh))
+        t = timed(lambda: pk.ix_peak_gather(table.data_ptr(), tbytes, rows.data_ptr(), n, xor.data_ptr(), sh))
         gather[label] = round(n * 256 / t / 1e9, 1)
         del table, rows
     return {"fp8_mfma_tflops_by_valu_per_mfma": mfma, "copy_GB_per_s": copy,
-            "gather_256B_rows_GB_per_s": gather}
+            "read_GB_per_s": read, "gather_256B_rows_GB_per_s": gather}
+
+
+def time_calls(fn, stream, reps, warmup=1, before=None):
+    """ms per call of fn, timed with events on `stream`: the average over reps back-to-back
+    calls; or, with before(r) given (run ahead of call r, outside the timed interval), the
+    median of the calls timed one by one."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if before is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for r in range(reps):
+        before(r)
+        ev[r][0].record(stream)
+        fn()
+        ev[r][1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2]  # the median: one-off stalls of a single call do not move it
+
+
+def gather_ceiling(pk, kc, vc, idx, kv_len, wl, stream, reps, split_options, before=None):
+    """(ms, splits, blocks per CU) of the fastest ix_peak_gather_selection over split_options
+    and occupancy limits (none, or 2 blocks per CU as the attention runs): the K and V rows of
+    this selection read exactly as the attention reads them, with nothing computed."""
+    import torch
+    xr = torch.zeros(wl.B * wl.T * wl.H_kv * max(split_options), dtype=torch.int32,
+                     device=idx.device)
+    sh = stream.cuda_stream
+    best = None
+    for sp in split_options:
+        for occ in (0, 2):
+            ms = time_calls(lambda: pk.ix_peak_gather_selection(
+                kc, vc, idx.data_ptr(), kv_len, wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, sp, occ,
+                xr.data_ptr(), sh), stream, reps, before=before)
+            if best is None or ms < best[0]:
+                best = (ms, sp, occ)
+    return best
 
 
 def kernel_source_hash():
@@ -317,6 +376,269 @@ def algorithmic_work(wl):
     return flops, gathered + other, pairs, sel
 
 
+def cpu_sample(wl, n_max):
+    """The oracle's sample of query rows as chunks [(b, rows)], the fixed rows first: rows 0
+    and T-1 of the first sequence and rows k-2, k-1, k (which see fewer than, exactly and one
+    more than k keys when the chunk starts at position 0), then rows drawn uniformly (seed
+    1234); a decode step (T = 1) samples whole sequences.  Chunks hold up to 4 rows of one
+    sequence, so the work spreads over the workers."""
+    import numpy as np
+    rng = np.random.default_rng(1234)
+    n_max = min(n_max, wl.B * wl.T)
+    if wl.T == 1:
+        return [(b, [0]) for b in range(n_max)], []
+    special = sorted({t for t in (0, wl.k - 2, wl.k - 1, wl.k, wl.T - 1) if 0 <= t < wl.T})
+    flat = rng.choice(wl.B * wl.T, size=n_max, replace=False)
+    picks = [p for p in dict.fromkeys((int(f) // wl.T, int(f) % wl.T) for f in flat)
+             if not (p[0] == 0 and p[1] in special)][:max(0, n_max - len(special))]
+    chunks = [(0, special)]
+    by_seq = {}
+    for b, t in picks:
+        by_seq.setdefault(b, []).append(t)
+    rest = [(b, sorted(ts[i:i + 4])) for b, ts in sorted(by_seq.items()) for i in range(0, len(ts), 4)]
+    order = rng.permutation(len(rest))
+    return chunks + [rest[i] for i in order], special
+
+
+def cpu_baseline(args, wl, name, ind, layers, dev):
+    """The oracle timed on the host's cores.  The sampled rows' inputs (the same bytes the GPU
+    read) go to a temporary folder; a child process that never touches the GPU loads them and
+    runs the oracle's chunks over a pool of worker processes forked from it until
+    --cpu-seconds of wall time, then on one thread alone for a quarter of that."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
+    import torch
+
+    from indexed_sparse_attention_ix_amd import synth
+    n_seq_max = 8 if wl.B > 1 else 1        # caches of a few sequences only (decode: 272 MiB each)
+    chunks, special = cpu_sample(wl, args.cpu_rows if wl.T > 1 else n_seq_max)
+    chunks = [(b, rows) for b, rows in chunks if b < n_seq_max]
+    seqs = sorted({b for b, _ in chunks})
+    tmp = tempfile.mkdtemp(prefix="ix_cpu_baseline_")
+    try:
+        arrays = {"q_pos0": ind["q_pos0"].cpu().numpy(), "kv_len": ind["kv_len"].cpu().numpy()}
+        for b in seqs:
+            rows = sorted({t for bb, rs in chunks if bb == b for t in rs})
+            r = torch.tensor(rows, device=dev)
+            arrays[f"rows_{b}"] = np.array(rows, dtype=np.int64)
+            arrays[f"k_I_{b}"] = ind["k_I"][b].cpu().numpy()
+            arrays[f"q_I_{b}"] = ind["q_I"][b, r].cpu().numpy()
+            arrays[f"w_{b}"] = ind["w"][b, r].cpu().numpy()
+            for l, Lr in enumerate(layers):
+                arrays[f"q_{b}_{l}"] = synth.bf16_bits(Lr["q"][b, r])
+                arrays[f"K_{b}_{l}"] = synth.bf16_bits(Lr["K"][b])
+                arrays[f"V_{b}_{l}"] = synth.bf16_bits(Lr["V"][b])
+        np.savez(os.path.join(tmp, "inputs.npz"), **arrays)
+        del arrays
+        workers = max(1, min(args.cpu_workers, os.cpu_count() or 1))
+        plan = {"chunks": chunks, "seqs": seqs, "T": wl.T, "S": wl.S, "H_I": wl.H_I, "d_I": wl.d_I,
+                "H_q": wl.H_q, "H_kv": wl.H_kv, "d": wl.d, "k": wl.k, "layers": wl.layers,
+                "sm_scale": wl.sm_scale, "seconds": args.cpu_seconds, "workers": workers}
+        with open(os.path.join(tmp, "plan.json"), "w") as f:
+            json.dump(plan, f)
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", tmp],
+                             capture_output=True, text=True, timeout=30 + 4 * args.cpu_seconds + 120)
+        if res.returncode != 0:
+            raise RuntimeError(f"CPU baseline child failed:\n{res.stdout[-2000:]}\n{res.stderr[-2000:]}")
+        out = json.loads(res.stdout.strip().splitlines()[-1])
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    what = (f"the first {out['rows']} sequences' decode queries" if wl.T == 1 else
+            f"{out['rows']} query rows ({len(special)} fixed: t = {special} of sequence 0; "
+            f"the rest drawn uniformly, in chunks of up to 4 rows)")
+    return {"value": round(out["rows"] / out["wall_s"], 3), "unit": "query tokens/s",
+            "cores": out["workers"], "kind": "oracle",
+            "sample": f"{what} from {name} (seed 1234): fp64 scores, selection and "
+                      f"{wl.layers}-layer attention per row, {out['workers']} worker processes "
+                      f"with one BLAS thread each, {out['wall_s']:.1f} s of wall time",
+            "host_cpus": os.cpu_count(),
+            "one_thread_value": round(out["one_rows"] / out["one_s"], 3) if out["one_s"] else None,
+            "one_thread_sample": f"the first {out['one_rows']} of the same rows on one thread, "
+                                 f"{out['one_s']:.1f} s"}
+
+
+_CHILD = {}
+
+
+def _child_chunk(ci):
+    """One chunk of the oracle in a worker (inputs inherited from the child process)."""
+    import numpy as np
+    from oracle import ix_oracle as O
+    P, D = _CHILD["plan"], _CHILD["data"]
+    if time.time() > _CHILD["deadline"]:
+        return 0, 0.0, 0.0
+    b, rows = P["chunks"][ci]
+    pos = {t: i for i, t in enumerate(D[f"rows_{b}"].tolist())}
+    sel = [pos[t] for t in rows]
+    T = P["T"]
+    qI = np.zeros((1, T, P["H_I"], P["d_I"]), dtype=np.uint8)   # only the chunk's rows are set
+    w = np.zeros((1, T, P["H_I"]), dtype=np.float32)
+    qI[0, rows] = D[f"q_I_{b}"][sel]
+    w[0, rows] = D[f"w_{b}"][sel]
+    indexer = {"q_I": qI, "k_I": D[f"k_I_{b}"][None], "w": w,
+               "q_pos0": D["q_pos0"][b:b + 1], "kv_len": D["kv_len"][b:b + 1]}
+    layers = []
+    for l in range(P["layers"]):
+        q = np.zeros((1, T, P["H_q"], P["d"]), dtype=np.uint16)
+        q[0, rows] = D[f"q_{b}_{l}"][sel]
+        layers.append({"q": q, "K": D[f"K_{b}_{l}"][None], "V": D[f"V_{b}_{l}"][None]})
+    t0 = time.time()
+    O.indexshare_group(indexer, layers, P["k"], 0, rows, P["sm_scale"])
+    return len(rows), t0, time.time()
+
+
+def _child_init():
+    from threadpoolctl import threadpool_limits
+    _CHILD["limits"] = threadpool_limits(limits=1)
+
+
+def cpu_baseline_child(path):
+    """Entry of the CPU-baseline child process: no GPU is touched here or in its workers."""
+    import multiprocessing as mp
+
+    import numpy as np
+    plan = json.load(open(os.path.join(path, "plan.json")))
+    with np.load(os.path.join(path, "inputs.npz")) as z:
+        data = {k: z[k] for k in z.files}
+    _CHILD.update(plan=plan, data=data)
+    start = time.time()
+    _CHILD["deadline"] = start + plan["seconds"]
+    with mp.get_context("fork").Pool(plan["workers"], initializer=_child_init) as pool:
+        res = list(pool.imap(_child_chunk, range(len(plan["chunks"]))))
+    done = [r for r in res if r[0] > 0]
+    rows = sum(r[0] for r in done)
+    wall = max(r[2] for r in done) - start
+    # the same chunks on one thread, for a quarter of the time
+    from threadpoolctl import threadpool_limits
+    one_rows, one_s = 0, 0.0
+    _CHILD["deadline"] = float("inf")
+    with threadpool_limits(limits=1):
+        for ci in range(len(plan["chunks"])):
+            n, t0, t1 = _child_chunk(ci)
+            one_rows, one_s = one_rows + n, one_s + (t1 - t0)
+            if one_s >= max(2.0, plan["seconds"] / 4):
+                break
+    print(json.dumps({"rows": rows, "wall_s": wall, "workers": plan["workers"],
+                      "one_rows": one_rows, "one_s": one_s}), flush=True)
+
+
+def run_leg(name, dev, steps):
+    """The benchmark spec's other two figures, each on its own workload, after the main one: the
+    decode step (64 sequences against 128K-token caches), whose attention gathers really go
+    to HBM (4 GiB of K and V per layer), timed with the caches flushed; and the 1M-key
+    chunked prefill, where IndexShare's one indexer per group of 4 layers is compared with
+    indexing every layer.  Returns a dict of timings and rates (inputs resident in HBM)."""
+    import torch
+
+    from indexed_sparse_attention_ix_amd import binding as bd
+    from indexed_sparse_attention_ix_amd import peaks as pk
+    from indexed_sparse_attention_ix_amd import synth
+    from indexed_sparse_attention_ix_amd.workloads import WORKLOADS
+    wl = WORKLOADS[name]
+    L = wl.layers
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ind = synth.indexer_inputs(wl, device=dev)
+    layers = [synth.attention_inputs(wl, layer=l, device=dev) for l in range(L)]
+    a = bd.indexer_args(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"])
+    idx = torch.empty((wl.B, wl.T, wl.k), dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(Lr["q"]) for Lr in layers]
+    ws_bytes = bd.indexshare_workspace_bytes(a, wl.k, wl.H_q, wl.H_kv, wl.d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    qp = [Lr["q"].data_ptr() for Lr in layers]
+    kp = [Lr["K"].data_ptr() for Lr in layers]
+    vp = [Lr["V"].data_ptr() for Lr in layers]
+    op = [o.data_ptr() for o in outs]
+    kvl = ind["kv_len"].data_ptr()
+    topk_ws = bd.ix_topk_workspace_bytes(a, wl.k)
+    attn_ws = bd.sparse_attn_workspace_bytes(wl.B, wl.T, wl.H_q, wl.H_kv, wl.d, wl.k)
+    reps = max(steps, 20 if wl.T > 1 else 50)
+
+    def group_step():
+        bd.indexshare_group_fwd(a, wl.k, L, qp, kp, vp, op, None, wl.H_q, wl.H_kv, wl.d,
+                                wl.sm_scale, idx.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+
+    def attn(l):
+        bd.sparse_attn_fwd(qp[l], kp[l], vp[l], idx.data_ptr(), kvl, wl.B, wl.T, wl.S, wl.H_q,
+                           wl.H_kv, wl.d, wl.k, wl.sm_scale, op[l], 0,
+                           ws.data_ptr() if attn_ws else 0, attn_ws, sh)
+
+    ms_group = time_calls(group_step, stream, reps, warmup=3)
+    ms_topk = time_calls(lambda: bd.ix_topk(a, wl.k, idx.data_ptr(), 0, ws.data_ptr(), topk_ws, sh),
+                         stream, reps)
+    ms_attn = time_calls(lambda: attn(0), stream, reps)
+    flops, attn_bytes, pairs, sel = algorithmic_work(wl)
+    ib = indexer_bytes(wl)
+    # the layers' attention over the shared selection in one call, as the group step runs it
+    gws = bd.sparse_attn_group_workspace_bytes(wl.B, wl.T, wl.H_q, wl.H_kv, wl.d, wl.k, L)
+
+    def attn_group():
+        bd.sparse_attn_group_fwd(L, qp, kp, vp, op, None, idx.data_ptr(), kvl, wl.B, wl.T, wl.S,
+                                 wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale,
+                                 ws.data_ptr() if gws else 0, gws, sh)
+    ms_attn_group = time_calls(attn_group, stream, reps)
+    # cold: a 512 MiB buffer (twice the Infinity Cache) read before every call, as a decode
+    # step's selection streams its keys before the attention (a written buffer would leave
+    # the caches full of dirty lines whose write-backs no step pays)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    xr = torch.zeros(4096, dtype=torch.int32, device=dev)
+    n_cold = 10
+
+    def flush(r):
+        pk.ix_peak_read(scratch.data_ptr(), 512 << 20, xr.data_ptr(), sh)
+    ms_attn_cold = time_calls(lambda: attn(0), stream, n_cold, before=flush)
+    ms_attn_group_cold = time_calls(attn_group, stream, n_cold, before=flush)
+    ms_group_cold = time_calls(group_step, stream, n_cold, before=flush)
+    ms_topk_cold = time_calls(lambda: bd.ix_topk(a, wl.k, idx.data_ptr(), 0, ws.data_ptr(), topk_ws,
+                                                 sh), stream, n_cold, before=flush)
+    split_opts = [1] if wl.B * wl.T * wl.H_kv >= 1024 else [1, 2, 4, 8, 16]
+    c_ms, c_sp, c_occ = gather_ceiling(pk, kp[0], vp[0], idx, kvl, wl, stream, n_cold, split_opts,
+                                       before=flush)
+    del scratch, xr
+    # per-layer indexing: every layer with its own indexer inputs and its own top-k
+    inds = [ind] + [synth.indexer_inputs(wl, layer=l, device=dev) for l in range(1, L)]
+    aa = [bd.indexer_args(x["q_I"], x["k_I"], x["w"], x["q_pos0"], x["kv_len"]) for x in inds]
+
+    def per_layer_step():
+        for l in range(L):
+            bd.ix_topk(aa[l], wl.k, idx.data_ptr(), 0, ws.data_ptr(), topk_ws, sh)
+            attn(l)
+    ms_pl = time_calls(per_layer_step, stream, max(2, reps // 2))
+    gbs_cold = attn_bytes / (ms_attn_cold / 1e3) / 1e9
+    gbs_group_cold = L * attn_bytes / (ms_attn_group_cold / 1e3) / 1e9
+    out = {"workload": name, "B": wl.B, "T": wl.T, "S": wl.S, "k": wl.k, "layers": L,
+           "group_ms": round(ms_group, 4), "group_ms_cold": round(ms_group_cold, 4),
+           "query_tokens_per_s": round(wl.B * wl.T / (ms_group / 1e3), 1),
+           "per_layer_indexing_ms": round(ms_pl, 4), "indexshare_speedup": round(ms_pl / ms_group, 3),
+           "ix_topk_ms": round(ms_topk, 4), "ix_topk_ms_cold": round(ms_topk_cold, 4),
+           "indexer_tflop": round(flops / 1e12, 3),
+           "indexer_fp8_frac": round(flops / (ms_topk / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+           "indexer_bytes": ib,
+           "indexer_hbm_frac_cold": round(ib / (ms_topk_cold / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+           "attention_ms_per_layer": round(ms_attn, 4),
+           "attention_ms_per_layer_cold": round(ms_attn_cold, 4),
+           "attention_gb_per_layer": round(attn_bytes / 1e9, 4),
+           "attention_GB_per_s_cold": round(gbs_cold, 1),
+           "attention_hbm_frac_cold": round(gbs_cold / PEAK_HBM_GBS, 4),
+           "group_attention_ms": round(ms_attn_group, 4),
+           "group_attention_ms_cold": round(ms_attn_group_cold, 4),
+           "group_attention_ms_per_layer_cold": round(ms_attn_group_cold / L, 4),
+           "group_attention_GB_per_s_cold": round(gbs_group_cold, 1),
+           "group_attention_hbm_frac_cold": round(gbs_group_cold / PEAK_HBM_GBS, 4),
+           "gather_ceiling_cold": {"ms": round(c_ms, 4), "splits": c_sp,
+                                   "blocks_per_cu": c_occ or None,
+                                   "GB_per_s": round(attn_bytes / (c_ms / 1e3) / 1e9, 1),
+                                   "attention_frac": round(c_ms / ms_attn_cold, 4)},
+           "flush": "512 MiB buffer read before each cold call, outside the events"}
+    del inds, aa, ind, layers, outs, ws, idx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -325,6 +647,9 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.cpu_baseline_child)
+        return
     from indexed_sparse_attention_ix_amd.workloads import BENCH_WORKLOAD, WORKLOADS
     if args.summarize_profiles:
         summarize_profiles(args, args.workload or BENCH_WORKLOAD)
@@ -439,6 +764,24 @@ def main():
         if tb:
             roof["traffic_GB_per_s"] = round(tb / (tm / 1e3) / 1e9, 1)
             roof["traffic_frac"] = round(tb / (tm / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
+    # The attention's own ceiling: ix_peak_gather_selection reads exactly the rows of this
+    # selection with the attention's block shape and order and computes nothing, under the
+    # same conditions (back-to-back launches).  Where a layer's K and V fit in the Infinity
+    # Cache (prefill up to 128K) the gathers are served from the caches, faster than HBM
+    # could: the bound is then "cache", against that measured ceiling, not the HBM peak.
+    from indexed_sparse_attention_ix_amd import peaks as pk
+    split_opts = [1] if wl.B * wl.T * wl.H_kv >= 1024 else [1, 2, 4, 8, 16]
+    t_ceil, sp_ceil, occ_ceil = gather_ceiling(pk, kp[0], vp[0], idx, ind["kv_len"].data_ptr(), wl,
+                                               stream, reps, split_opts)
+    ceil_gbs = attn_bytes / (t_ceil / 1e3) / 1e9
+    attn_roof["gather_ceiling"] = {"ms": round(t_ceil, 4), "GB_per_s": round(ceil_gbs, 1),
+                                   "splits": sp_ceil, "blocks_per_cu": occ_ceil or None,
+                                   "frac": round(t_ceil / t_attn, 4)}
+    if attn_gbs > PEAK_HBM_GBS:
+        attn_roof.update(bound="cache", peak=round(ceil_gbs, 1), frac=round(t_ceil / t_attn, 4),
+                         peak_source="measured: ix_peak_gather_selection, the same rows gathered "
+                                     "with nothing computed",
+                         hbm_frac_if_all_from_hbm=round(attn_gbs / PEAK_HBM_GBS, 4))
     dominant_is_indexer = t_topk >= t_attn * L
     roofline = idx_roof if dominant_is_indexer else attn_roof
     roofline = dict(roofline, kernel="ix_topk (indexer + selection)" if dominant_is_indexer
@@ -446,17 +789,18 @@ def main():
 
     # ---------------------------------------------------------------- cold attention
     # Where one layer's K and V exceed the 256 MB Infinity Cache (decode, the 1M chunk) the
-    # gathers are HBM-bound: time the attention also after writing a 512 MiB scratch buffer
-    # before every launch, so no row is left in the caches from the previous launch.
+    # gathers are HBM-bound: time the attention also after reading a 512 MiB buffer before
+    # every launch, so no row is left in the caches from the previous launch.
     attn_cold = None
     kv_layer_bytes = 2 * wl.B * wl.S * wl.H_kv * wl.d * 2
     if not args.no_extras and kv_layer_bytes > (256 << 20):
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        xr = torch.zeros(4096, dtype=torch.int32, device=dev)
         n_cold = max(3, min(reps, 10))
         evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_cold)]
         for r in range(n_cold):
-            scratch.fill_(r & 0xFF)
+            pk.ix_peak_read(scratch.data_ptr(), 512 << 20, xr.data_ptr(), sh)
             evc[r][0].record(stream)
             bd.sparse_attn_fwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(),
                                wl.B, wl.T, wl.S, wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale,
@@ -467,8 +811,8 @@ def main():
         attn_cold = {"ms_per_layer": round(t_cold, 4),
                      "GB_per_s": round(attn_bytes / (t_cold / 1e3) / 1e9, 1),
                      "frac_of_hbm_peak": round(attn_bytes / (t_cold / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "flush": "512 MiB scratch written before each launch"}
-        del scratch
+                     "flush": "512 MiB buffer read before each launch"}
+        del scratch, xr
 
     # ---------------------------------------------------------------- cache append (producer)
     # The step before the indexer in a serving loop: this step's T tokens per sequence go
@@ -628,11 +972,11 @@ def main():
             n_at = 1 << 22
             rr = torch.randint(0, rows_tab, (n_at,), dtype=torch.int32,
                                generator=torch.Generator(device="cpu").manual_seed(79)).to(dev)
-            bd.ix_peak_atomic_add(tab.data_ptr(), rows_tab, rr.data_ptr(), n_at, sh)
+            pk.ix_peak_atomic_add(tab.data_ptr(), rows_tab, rr.data_ptr(), n_at, sh)
             torch.cuda.synchronize()
             e0.record(stream)
             for _ in range(3):
-                bd.ix_peak_atomic_add(tab.data_ptr(), rows_tab, rr.data_ptr(), n_at, sh)
+                pk.ix_peak_atomic_add(tab.data_ptr(), rows_tab, rr.data_ptr(), n_at, sh)
             e1.record(stream)
             torch.cuda.synchronize()
             t_at = e0.elapsed_time(e1) / 3 / 1e3
@@ -744,99 +1088,54 @@ def main():
             peaks["indexer_frac_of_mfma_with_8_valu"] = round(
                 idx_roof["achieved"] / peaks["fp8_mfma_tflops_by_valu_per_mfma"]["8"], 3)
         else:
-            peaks["indexer_frac_of_copy"] = round(idx_roof["achieved"] / peaks["copy_GB_per_s"], 3)
+            peaks["indexer_frac_of_read"] = round(idx_roof["achieved"] / peaks["read_GB_per_s"], 3)
         peaks["attention_frac_of_gather_64MiB"] = round(
             attn_roof["achieved"] / peaks["gather_256B_rows_GB_per_s"]["64MiB"], 3)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        from oracle import ix_oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-        except Exception:  # noqa: BLE001
-            threads = os.cpu_count() or 1
-        # Sample: query rows drawn uniformly (seed 1234) from the workload; a decode step
-        # has one query per sequence, so its sample is the first sequences.  Rows are run in
-        # chunks of up to 32 (one sequence per chunk) until --cpu-seconds of oracle time is
-        # spent or --cpu-rows rows are done.
-        rng = np.random.default_rng(1234)
-        n_max = min(args.cpu_rows, wl.B * wl.T)
-        if wl.T == 1:
-            picks = [(b, 0) for b in range(n_max)]
-            special = []
-        else:
-            # Always sampled, as one chunk that runs first: rows 0 and T-1 of the first
-            # sequence (the chunk's first and last queries) and rows k-2, k-1, k, which see
-            # fewer than, exactly and one more than k keys when the chunk starts at position 0.
-            special = sorted({t for t in (0, wl.k - 2, wl.k - 1, wl.k, wl.T - 1) if 0 <= t < wl.T})
-            flat = rng.choice(wl.B * wl.T, size=n_max, replace=False)
-            picks = [p for p in dict.fromkeys((int(f) // wl.T, int(f) % wl.T) for f in flat)
-                     if not (p[0] == 0 and p[1] in special)][:max(0, n_max - len(special))]
-        chunks = [(0, special)] if special else []
-        for b in sorted({b for b, _ in picks}):
-            rows_b = [t for bb, t in picks if bb == b]
-            chunks += [(b, sorted(rows_b[i:i + 32])) for i in range(0, len(rows_b), 32)]
-        order = (list(range(len(chunks))) if not special else
-                 [0] + [1 + int(i) for i in rng.permutation(len(chunks) - 1)])
-        host = {}
+        cpu = cpu_baseline(args, wl, name, ind, layers, dev)
 
-        def run_chunk(ci):
-            nonlocal host
-            b, rows = chunks[ci]
-            if b not in host:
-                host = {b: {"k_I": ind["k_I"][b:b + 1].cpu().numpy(),
-                            "K": [synth.bf16_bits(Lr["K"][b:b + 1]) for Lr in layers],
-                            "V": [synth.bf16_bits(Lr["V"][b:b + 1]) for Lr in layers]}}
-            hb = host[b]
-            ri = torch.tensor(rows, device=dev)
-            qI_h = np.zeros((1, wl.T, wl.H_I, wl.d_I), dtype=np.uint8)
-            w_h = np.zeros((1, wl.T, wl.H_I), dtype=np.float32)
-            qI_h[0, rows] = ind["q_I"][b, ri].cpu().numpy()
-            w_h[0, rows] = ind["w"][b, ri].cpu().numpy()
-            indexer_np = {"q_I": qI_h, "k_I": hb["k_I"], "w": w_h,
-                          "q_pos0": ind["q_pos0"][b:b + 1].cpu().numpy(),
-                          "kv_len": ind["kv_len"][b:b + 1].cpu().numpy()}
-            layers_np = []
-            for li, Lr in enumerate(layers):
-                qb = np.zeros((1, wl.T, wl.H_q, wl.d), dtype=np.uint16)
-                qb[0, rows] = synth.bf16_bits(Lr["q"][b, ri])
-                layers_np.append({"q": qb, "K": hb["K"][li], "V": hb["V"][li]})
-            t0 = time.perf_counter()
-            O.indexshare_group(indexer_np, layers_np, wl.k, 0, rows, wl.sm_scale)
-            return len(rows), time.perf_counter() - t0
-
-        def timed(limit_s):
-            done, spent = 0, 0.0
-            for ci in order:
-                n, dt = run_chunk(ci)
-                done, spent = done + n, spent + dt
-                if spent >= limit_s:
-                    break
-            return done, spent
-
-        done, t_cpu = timed(args.cpu_seconds)
-        # the same chunks again with the BLAS pool held to one thread, for a shorter time
-        one = None
-        try:
-            from threadpoolctl import threadpool_limits
-            with threadpool_limits(limits=1):
-                one = timed(max(2.0, args.cpu_seconds / 4))
-        except ImportError:
-            pass
-        what = (f"the first {done} sequences' decode queries" if wl.T == 1 else
-                f"{done} query rows ({len(special)} fixed: t = {special} of sequence 0; "
-                f"the rest drawn uniformly)")
-        cpu = {"value": round(done / t_cpu, 3), "unit": "query tokens/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{what} from {name} (seed 1234), run until {args.cpu_seconds:.0f} s of "
-                         f"oracle time: fp64 scores, selection and {L}-layer attention per row, "
-                         f"{t_cpu:.1f} s",
-               "host_cpus": os.cpu_count(),
-               "one_thread_value": round(one[0] / one[1], 3) if one else None,
-               "one_thread_sample": (f"the first {one[0]} of the same rows, {one[1]:.1f} s"
-                                     if one else None)}
+    # ---------------------------------------------------------------- decode and 1M legs
+    legs = {}
+    if not args.no_legs and not args.no_extras:
+        del ind, layers, outs, ws, idx, a
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        for leg_name in ("decode_b64_128k", "chunk_prefill_1m"):
+            if leg_name != name:
+                legs[leg_name] = run_leg(leg_name, dev, args.steps)
+    gather_hbm = None
+    if "decode_b64_128k" in legs:
+        d = legs["decode_b64_128k"]
+        gather_hbm = {"workload": "decode_b64_128k",
+                      "kernel": "sparse_attn_group_fwd: the 4 layers' attention of the decode "
+                                "step in one launch, caches flushed",
+                      "bound": "hbm", "achieved": d["group_attention_GB_per_s_cold"],
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": d["group_attention_hbm_frac_cold"],
+                      "ms_per_layer": d["group_attention_ms_per_layer_cold"],
+                      "one_layer_call": {"ms": d["attention_ms_per_layer_cold"],
+                                         "GB_per_s": d["attention_GB_per_s_cold"],
+                                         "frac": d["attention_hbm_frac_cold"],
+                                         "gather_ceiling": d["gather_ceiling_cold"]}}
+    if "decode_b64_128k" in legs and peaks:
+        d = legs["decode_b64_128k"]
+        rate = d["indexer_bytes"] / (d["ix_topk_ms"] / 1e3) / 1e9
+        d["indexer_GB_per_s"] = round(rate, 1)
+        d["indexer_frac_of_read_ceiling"] = round(rate / peaks["read_GB_per_s"], 4)
+        d["indexer_frac_of_read_ceiling_cold"] = round(
+            d["indexer_bytes"] / (d["ix_topk_ms_cold"] / 1e3) / 1e9 / peaks["read_GB_per_s"], 4)
+        if gather_hbm:
+            gather_hbm["frac_of_random_gather_ceiling"] = round(
+                gather_hbm["achieved"] / peaks["gather_256B_rows_GB_per_s"]["2GiB"], 4)
+    indexshare_1m = None
+    if "chunk_prefill_1m" in legs:
+        c = legs["chunk_prefill_1m"]
+        indexshare_1m = {"workload": "chunk_prefill_1m", "group_ms": c["group_ms"],
+                         "per_layer_indexing_ms": c["per_layer_indexing_ms"],
+                         "speedup": c["indexshare_speedup"], "target": 2.0}
 
     line = {
         "metric": "query tokens/s (indexer+topk+sparse attn) at 128K; FP8 MFMA % and HBM % of peak",
@@ -856,6 +1155,8 @@ def main():
                    "layers": L, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "gather_hbm_128k": gather_hbm,
+        "indexshare_1m": indexshare_1m,
         "detail": {
             "ix_topk_ms": round(t_topk, 3),
             "sparse_attn_ms_per_layer": round(t_attn, 3),
@@ -874,6 +1175,7 @@ def main():
             "attention_backward": backward,
             "attention_cold": attn_cold,
             "measured_peaks": peaks,
+            "legs": legs,
             "wall_s_timed_region": round(t_wall, 3),
             "kernel_source_hash": kernel_source_hash(),
         },

@@ -257,8 +257,36 @@ ix_status ix_indexer_bwd(const ix_indexer_args *a, int32_t k, const int32_t *idx
  * 0 on invalid arguments. */
 size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t rows_per_pass);
 
+/* Workspace bytes sparse_attn_group_fwd needs for n_layers layers (0 on invalid arguments;
+ * may be 0): the split partials of the layers that share one launch. */
+size_t sparse_attn_group_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32_t H_kv,
+                                         int32_t d, int32_t k, int32_t n_layers);
+
+/*
+ * sparse_attn_group_fwd -- the attention of the n_layers layers of an IndexShare group over
+ * one selection (the layers reuse one index tensor: "IndexShare: Amortizing the Indexer"),
+ * with the selection computed by the caller (ix_topk, ix_topk_pooled or any other): layer l
+ * gets what sparse_attn_fwd gives for q[l], kc[l], vc[l], out[l], lse[l] and the shared idx.
+ * When one layer's grid is small (decode: B * T * H_kv < 1024 query rows) up to 8 layers
+ * share one launch, and each selection is then split over as many blocks as make the
+ * launch about one block per CU; a layer's output equals sparse_attn_fwd's up to the
+ * rounding of the merge of those splits (bit for bit where the split counts agree).
+ * q, kc, vc, out: HOST arrays of n_layers device pointers (shapes as in sparse_attn_fwd).
+ * lse: nullable host array of n_layers nullable device pointers.
+ * idx, kv_len, B..sm_scale: shared by the layers, as in sparse_attn_fwd.
+ * ws: at least sparse_attn_group_workspace_bytes(B, T, H_q, H_kv, d, k, n_layers) bytes
+ *     (NULL when that is 0; contents need no initialisation).
+ * Errors: as sparse_attn_fwd for every layer, plus IX_ERR_INVALID for n_layers < 1 or a NULL
+ * pointer array.
+ */
+ix_status sparse_attn_group_fwd(int32_t n_layers, const void *const *q, const void *const *kc,
+                                const void *const *vc, void *const *out, float *const *lse,
+                                const int32_t *idx, const int32_t *kv_len, int32_t B, int32_t T,
+                                int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,
+                                float sm_scale, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes indexshare_group_fwd needs, for any n_layers: the selection's, or the
- * split partials of the attention of up to 8 layers, which run in one launch. */
+ * split partials of the attention of the layers that share one launch. */
 size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H_q,
                                   int32_t H_kv, int32_t d);
 
@@ -267,17 +295,16 @@ size_t indexshare_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t H
  * selection is computed once from the group's indexer inputs and every layer
  * attends over that same index tensor ("IndexShare: Amortizing the Indexer";
  * group of 4 in the pages).  Equivalent to ix_topk(a, k, idx) followed by
- * sparse_attn_fwd for each layer l with q[l], kc[l], vc[l], out[l], lse[l] and the
- * shared idx, bit for bit.
+ * sparse_attn_group_fwd over the n_layers layers with the shared idx, bit for bit
+ * (and so to sparse_attn_fwd per layer up to the rounding of split merges).
  * q, kc, vc, out: HOST arrays of n_layers device pointers (shapes as in
  *                 sparse_attn_fwd; kc/vc use S_max = a->S_max, kv_len = a->kv_len).
  * lse:            nullable host array of n_layers nullable device pointers.
  * idx:            caller-owned int32 [B, T, k]: written once, read n_layers times.
  * When one layer's attention grid is small (decode), the attention of up to 8 layers
- * runs in one launch; each block serves one layer and does the work of the standalone
- * call, so the outputs stay bit for bit those of sparse_attn_fwd.
+ * runs in one launch (as sparse_attn_group_fwd).
  * ws_bytes: at least indexshare_workspace_bytes (less is accepted while it covers the
- * selection and min(n_layers, 8) layers' split partials).
+ * selection and sparse_attn_group_workspace_bytes for n_layers).
  */
 ix_status indexshare_group_fwd(const ix_indexer_args *a, int32_t k, int32_t n_layers,
                                const void *const *q, const void *const *kc,

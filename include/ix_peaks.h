@@ -1,11 +1,12 @@
 /*
- * ix_peaks.h -- measured ceilings for the roofline fractions of libix.so (gfx950).
+ * ix_peaks.h -- measured ceilings for the roofline fractions (libix_peaks.so, gfx950).
  *
- * Not part of the method: three microbenchmark kernels that say what the chip delivers
- * on the shapes of work the path is made of, so each kernel's time can be read against
- * a measured ceiling as well as the datasheet peak.  The caller times a call with events
- * on `stream`; every buffer is device memory owned by the caller, nothing is allocated,
- * and the statuses and ix_last_error() are those of ix.h.
+ * Not part of the method and not in the path's library: microbenchmark kernels that say
+ * what the chip delivers on the shapes of work the path is made of, so each kernel's time
+ * can be read against a measured ceiling as well as the datasheet peak.  The caller times
+ * a call with events on `stream`; every buffer is device memory owned by the caller,
+ * nothing is allocated.  Statuses are those of ix.h; the message of the last non-OK status
+ * on the calling thread is ix_peak_last_error().
  */
 #ifndef IX_PEAKS_H
 #define IX_PEAKS_H
@@ -15,6 +16,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Message for the last non-OK status of an ix_peak_* call on this thread ("" if none). */
+const char *ix_peak_last_error(void);
 
 /*
  * ix_peak_mfma_fp8 -- blocks x 4 waves, each wave issuing 16 * iters FP8 MFMAs
@@ -33,14 +37,39 @@ ix_status ix_peak_mfma_fp8(const void *operands, int32_t valu_per_mfma, int32_t 
  * bytes: a multiple of 16; src and dst 16-byte aligned, not overlapping. */
 ix_status ix_peak_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+/* ix_peak_read -- reads src[0, bytes) once with 16-byte loads over 4096 blocks (a read-only
+ * stream, as the decode indexer streams its keys).  out: uint32 [4096], entry i written with
+ * the XOR of the 32-bit words block i read (the XOR of all entries is the XOR of the bytes).
+ * bytes: a multiple of 16; src 16-byte aligned. */
+ix_status ix_peak_read(const void *src, size_t bytes, uint32_t *out, hipStream_t stream);
+
 /*
  * ix_peak_gather -- reads the 256-byte rows table[rows[i]], i < n, each by 16
- * consecutive lanes with 16-byte loads, 16 loads in flight per lane.
+ * consecutive lanes with 16-byte loads, 16 loads in flight per lane, over 2048 blocks.
  * table_bytes: <= 2 GiB, a multiple of 256; rows outside the table read as zero.
- * out: one uint32, XORed with a checksum of the bytes read.
+ * out: uint32 [2048], entry i written with the XOR of the words block i read.
  */
 ix_status ix_peak_gather(const void *table, size_t table_bytes, const int32_t *rows, int64_t n,
                          uint32_t *out, hipStream_t stream);
+
+/*
+ * ix_peak_gather_selection -- reads, for every query and KV head, the K and V rows its
+ * selection names, exactly as sparse_attn_fwd gathers them (one block of 4 waves per query,
+ * KV head and split, 32-entry chunks, two chunks in flight per wave, the same block order),
+ * and computes nothing with them: the memory system's rate for the attention's own access
+ * pattern.  kc, vc, idx, kv_len, B, T, S_max, H_kv, d, k: as for sparse_attn_fwd (entries
+ * < 0 or >= kv_len read nothing).  splits: blocks per (query, KV head), each taking a
+ * contiguous share of the selection's chunks.  blocks_per_cu: 0, or 2 or 3 to hold the
+ * launch to that many resident blocks per CU (through unused LDS), as the attention's LDS
+ * holds it to 2.  out: uint32 [B * T * H_kv * splits], entry i
+ * written with the XOR of the words block i read (each row read once per selection entry).
+ * Errors: IX_ERR_INVALID for NULL pointers, sizes out of range or misaligned caches;
+ * IX_ERR_UNSUPPORTED for d outside {64, 128} or a grid too large for one launch.
+ */
+ix_status ix_peak_gather_selection(const void *kc, const void *vc, const int32_t *idx,
+                                   const int32_t *kv_len, int32_t B, int32_t T, int32_t S_max,
+                                   int32_t H_kv, int32_t d, int32_t k, int32_t splits,
+                                   int32_t blocks_per_cu, uint32_t *out, hipStream_t stream);
 
 /*
  * ix_peak_atomic_add -- for each i < n, adds 1.0f with fp32 atomics to all 128 floats of
@@ -49,7 +78,7 @@ ix_status ix_peak_gather(const void *table, size_t table_bytes, const int32_t *r
  * table: fp32 [rows, 128], ADDED TO; rows <= 2^24.
  */
 ix_status ix_peak_atomic_add(float *table, int64_t rows, const int32_t *idx, int64_t n,
-                            hipStream_t stream);
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,10 +27,12 @@ STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
 
 # every symbol include/ix.h declares
 EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_bytes", "ix_topk",
-           "sparse_attn_workspace_bytes", "sparse_attn_fwd", "indexshare_workspace_bytes",
-           "indexshare_group_fwd", "indexshare_group_fwd_noalloc", "ix_append_kv", "ix_pool_keys", "ix_topk_pooled_workspace_bytes",
-           "ix_topk_pooled", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "indexshare_group_bwd", "ix_indexer_kl", "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes", "ix_peak_mfma_fp8", "ix_peak_copy",
-           "ix_peak_gather", "ix_peak_atomic_add")
+           "sparse_attn_workspace_bytes", "sparse_attn_fwd", "sparse_attn_group_workspace_bytes",
+           "sparse_attn_group_fwd", "indexshare_workspace_bytes",
+           "indexshare_group_fwd", "indexshare_group_fwd_noalloc", "ix_append_kv",
+           "ix_pool_keys", "ix_topk_pooled_workspace_bytes", "ix_topk_pooled", "sparse_attn_bwd",
+           "sparse_attn_bwd_workspace_bytes", "indexshare_group_bwd", "ix_indexer_kl",
+           "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes")
 
 
 class IxError(RuntimeError):
@@ -75,6 +77,11 @@ def load(path: str = LIB_PATH):
     L.sparse_attn_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                   c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.sparse_attn_group_workspace_bytes.restype = c_size_t
+    L.sparse_attn_group_workspace_bytes.argtypes = [c_int32] * 7
+    L.sparse_attn_group_fwd.restype = c_int32
+    L.sparse_attn_group_fwd.argtypes = ([c_int32] + [P(c_void_p)] * 5 + [c_void_p, c_void_p] +
+                                        [c_int32] * 7 + [c_float, c_void_p, c_size_t, c_void_p])
     L.indexshare_workspace_bytes.restype = c_size_t
     L.indexshare_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32, c_int32, c_int32]
     L.indexshare_group_fwd.restype = c_int32
@@ -102,14 +109,6 @@ def load(path: str = LIB_PATH):
     L.ix_indexer_bwd_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32]
     L.ix_indexer_kl.restype = c_int32
     L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
-    L.ix_peak_mfma_fp8.restype = c_int32
-    L.ix_peak_mfma_fp8.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]
-    L.ix_peak_atomic_add.restype = c_int32
-    L.ix_peak_atomic_add.argtypes = [c_void_p, c_int64, c_void_p, c_int64, c_void_p]
-    L.ix_peak_copy.restype = c_int32
-    L.ix_peak_copy.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
-    L.ix_peak_gather.restype = c_int32
-    L.ix_peak_gather.argtypes = [c_void_p, c_size_t, c_void_p, c_int64, c_void_p, c_void_p]
     L.ix_pool_keys.restype = c_int32
     L.ix_pool_keys.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                c_void_p]
@@ -165,6 +164,25 @@ def sparse_attn_fwd(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k, sm_sca
                     ws, ws_bytes, stream=0):
     _check(load().sparse_attn_fwd(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
                                   sm_scale, out, lse, ws, ws_bytes, stream))
+
+
+def sparse_attn_group_workspace_bytes(B, T, H_q, H_kv, d, k, n_layers) -> int:
+    return load().sparse_attn_group_workspace_bytes(B, T, H_q, H_kv, d, k, n_layers)
+
+
+def sparse_attn_group_fwd(n_layers, q, kc, vc, out, lse, idx, kv_len, B, T, S_max, H_q, H_kv, d,
+                          k, sm_scale, ws, ws_bytes, stream=0):
+    keep = []
+    conv = []
+    for ptrs in (q, kc, vc, out, lse):
+        r = _ptr_array(ptrs)
+        if r is None:
+            conv.append(None)
+        else:
+            conv.append(r[0])
+            keep.append(r[1])
+    _check(load().sparse_attn_group_fwd(n_layers, *conv, idx, kv_len, B, T, S_max, H_q, H_kv, d,
+                                        k, sm_scale, ws, ws_bytes, stream))
 
 
 def indexshare_workspace_bytes(args: IndexerArgs, k, H_q, H_kv, d) -> int:
@@ -242,20 +260,8 @@ def sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass):
     return load().sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass)
 
 
-def ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream=0):
-    _check(load().ix_peak_mfma_fp8(operands, valu_per_mfma, blocks, iters, out, stream))
 
 
-def ix_peak_atomic_add(table, rows, idx, n, stream=0):
-    _check(load().ix_peak_atomic_add(table, rows, idx, n, stream))
-
-
-def ix_peak_copy(src, dst, nbytes, stream=0):
-    _check(load().ix_peak_copy(src, dst, nbytes, stream))
-
-
-def ix_peak_gather(table, table_bytes, rows, n, out, stream=0):
-    _check(load().ix_peak_gather(table, table_bytes, rows, n, out, stream))
 
 
 def ix_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv, d, k, sm_scale,
@@ -377,6 +383,31 @@ def indexshare_group(q_I, k_I, w, q_pos0, kv_len, k, layers, sm_scale, with_lse=
                          H_q, H_kv, d, float(sm_scale), _ptr(idx), _ptr(ws), ws.numel(),
                          _stream())
     return (idx, outs, lses) if with_lse else (idx, outs)
+
+
+def group_attention(layers, idx, sm_scale, kv_len=None, with_lse=False, ws=None):
+    """The attention of every layer over one selection (sparse_attn_group_fwd): layers is a
+    list of dicts with q, K, V device tensors; returns [out] (and [lse]) per layer."""
+    torch = _torch()
+    q0 = layers[0]["q"]
+    B, T, H_q, d = q0.shape
+    S, H_kv = layers[0]["K"].shape[1], layers[0]["K"].shape[2]
+    k = idx.shape[2]
+    for L in layers:
+        for t in (L["q"], L["K"], L["V"]):
+            assert t.is_contiguous(), "attention tensors must be contiguous"
+    outs = [torch.empty_like(L["q"]) for L in layers]
+    lses = ([torch.empty((B, T, H_q), dtype=torch.float32, device=q0.device) for _ in layers]
+            if with_lse else None)
+    nb = sparse_attn_group_workspace_bytes(B, T, H_q, H_kv, d, k, len(layers))
+    if ws is None and nb:
+        ws = workspace(nb, q0.device)
+    sparse_attn_group_fwd(len(layers), [_ptr(L["q"]) for L in layers], [_ptr(L["K"]) for L in layers],
+                          [_ptr(L["V"]) for L in layers], [_ptr(o) for o in outs],
+                          [_ptr(x) for x in lses] if lses else None, _ptr(idx), _ptr(kv_len), B,
+                          T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(ws) if ws is not None else 0,
+                          nb, _stream())
+    return (outs, lses) if with_lse else outs
 
 
 def append_kv(pos0, k_I_new=None, k_I_cache=None, K_new=None, V_new=None, K_cache=None,

@@ -1,9 +1,11 @@
-"""Builds libix.so (HIP, gfx950) in-tree with hipcc.
+"""Builds the HIP libraries (gfx950) in-tree with hipcc.
 
 Every .hip source under csrc/ is compiled to an object in _build/ (in parallel) and
-linked into indexed_sparse_attention_ix_amd/libix.so.  Packed-FP32 VALU instructions
-are disabled for the device code (-packed-fp32-ops): the kernels are written with
-scalar fp32 arithmetic throughout.
+linked into indexed_sparse_attention_ix_amd/libix.so, the path's library (include/ix.h).
+The measured-ceiling microbenchmarks under csrc_peaks/ become libix_peaks.so
+(include/ix_peaks.h), a library of their own.  Packed-FP32 VALU instructions are disabled
+for the device code (-packed-fp32-ops): the kernels are written with scalar fp32
+arithmetic throughout.
 """
 from __future__ import annotations
 
@@ -15,8 +17,10 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+CSRC_PEAKS = os.path.join(PKG, "csrc_peaks")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libix.so")
+PEAKS_LIB = os.path.join(PKG, "libix_peaks.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,12 +32,13 @@ CFLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder=CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD, os.path.basename(os.path.dirname(src)) + "_" +
+                       os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -45,21 +50,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
-        raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources(CSRC)
+    peak_srcs = sources(CSRC_PEAKS)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(peak_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + peak_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

@@ -10,7 +10,6 @@
 #include <string>
 
 #include "ix_internal.h"
-#include "../../include/ix_peaks.h"
 
 // Scratch of indexshare_group_fwd_noalloc: device memory the library owns instead of a
 // caller workspace.  Each GPU the library runs on holds its own copy of this array until
@@ -180,9 +179,8 @@ ix_status group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_layers, const
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
   const ix::TopkPlan tp = ix::make_topk_plan(*a, k);
-  const ix::AttnPlan ap = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k);
-  const int per_launch = n_layers < ix::kAttnLayersPerLaunch ? n_layers : ix::kAttnLayersPerLaunch;
-  const size_t attn_need = (size_t)per_launch * ap.ws_bytes;
+  const ix::AttnPlan ap = ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k, n_layers);
+  const size_t attn_need = ap.ws_bytes;
   const size_t need = tp.ws_bytes > attn_need ? tp.ws_bytes : attn_need;
   if (use_scratch) {
     if (need > IX_NOALLOC_SCRATCH_BYTES)
@@ -253,7 +251,7 @@ size_t sparse_attn_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32_t H_
                                    int32_t k) {
   bool empty = false;
   if (check_attn_shape(B, T, 1, H_q, H_kv, d, k, &empty) != IX_OK || empty) return 0;
-  return ix::make_attn_plan(B, T, H_q, H_kv, d, k).ws_bytes;
+  return ix::make_attn_plan(B, T, H_q, H_kv, d, k, 1).ws_bytes;
 }
 
 ix_status sparse_attn_fwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
@@ -267,13 +265,46 @@ ix_status sparse_attn_fwd(const void* q, const void* kc, const void* vc, const i
   if ((st = check_attn_ptrs(q, kc, vc, idx, out)) != IX_OK) return st;
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
-  const ix::AttnPlan plan = ix::make_attn_plan(B, T, H_q, H_kv, d, k);
+  const ix::AttnPlan plan = ix::make_attn_plan(B, T, H_q, H_kv, d, k, 1);
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 plan.ws_bytes);
   hipError_t e = ix::launch_sparse_attn(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
                                         sm_scale, out, lse, plan, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_fwd launch");
+  return ok();
+}
+
+size_t sparse_attn_group_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int32_t H_kv,
+                                         int32_t d, int32_t k, int32_t n_layers) {
+  bool empty = false;
+  if (n_layers < 1 || check_attn_shape(B, T, 1, H_q, H_kv, d, k, &empty) != IX_OK || empty) return 0;
+  return ix::make_attn_plan(B, T, H_q, H_kv, d, k, n_layers).ws_bytes;
+}
+
+ix_status sparse_attn_group_fwd(int32_t n_layers, const void* const* q, const void* const* kc,
+                                const void* const* vc, void* const* out, float* const* lse,
+                                const int32_t* idx, const int32_t* kv_len, int32_t B, int32_t T,
+                                int32_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int32_t k,
+                                float sm_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  bool empty = false;
+  ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
+  if (st != IX_OK) return st;
+  if (n_layers < 1) return fail(IX_ERR_INVALID, "n_layers=%d must be >= 1", n_layers);
+  if (empty) return ok();
+  if (!q || !kc || !vc || !out) return fail(IX_ERR_INVALID, "NULL per-layer pointer array");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_attn_ptrs(q[l], kc[l], vc[l], idx, out[l])) != IX_OK) return st;
+  }
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  const ix::AttnPlan ap = ix::make_attn_plan(B, T, H_q, H_kv, d, k, n_layers);
+  if (ap.ws_bytes && (!ws || ws_bytes < ap.ws_bytes))
+    return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
+                ap.ws_bytes);
+  hipError_t e = ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, kv_len, B, T, S_max, H_q,
+                                               H_kv, d, k, sm_scale, out, lse, ap, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse_attn_group_fwd launch");
   return ok();
 }
 
@@ -284,9 +315,9 @@ size_t indexshare_workspace_bytes(const ix_indexer_args* a, int32_t k, int32_t H
   if (check_attn_shape(a->B, a->T, a->S_max, H_q, H_kv, d, k, &empty2) != IX_OK) return 0;
   if (empty) return 0;
   const size_t t = ix::make_topk_plan(*a, k).ws_bytes;
-  // the selection, then the attention of up to 8 layers per launch (one partial buffer
-  // per layer of a launch), one after the other on the same stream
-  const size_t s = ix::kAttnLayersPerLaunch * ix::make_attn_plan(a->B, a->T, H_q, H_kv, d, k).ws_bytes;
+  // the selection, then the attention of the layers (split partials of up to 8 layers per
+  // launch), one after the other on the same stream
+  const size_t s = ix::attn_group_ws_bytes(a->B, a->T, H_q, H_kv, d, k);
   return t > s ? t : s;
 }
 
@@ -535,52 +566,6 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
                                         a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, ws, ws_bytes,
                                         stream);
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");
-  return ok();
-}
-
-ix_status ix_peak_mfma_fp8(const void* operands, int32_t valu_per_mfma, int32_t blocks,
-                           int32_t iters, float* out, hipStream_t stream) {
-  if (!operands || !out) return fail(IX_ERR_INVALID, "NULL operands or out");
-  if (blocks < 1 || iters < 1) return fail(IX_ERR_INVALID, "blocks=%d iters=%d must be >= 1", blocks, iters);
-  if (valu_per_mfma != 0 && valu_per_mfma != 4 && valu_per_mfma != 8 && valu_per_mfma != 12)
-    return fail(IX_ERR_INVALID, "valu_per_mfma=%d (0, 4, 8 or 12)", valu_per_mfma);
-  if (!aligned16(operands)) return fail(IX_ERR_INVALID, "operands must be 16-byte aligned");
-  hipError_t e = ix::launch_peak_mfma(operands, valu_per_mfma, blocks, iters, out, stream);
-  if (e != hipSuccess) return hip_fail(e, "ix_peak_mfma_fp8 launch");
-  return ok();
-}
-
-ix_status ix_peak_atomic_add(float* table, int64_t rows, const int32_t* idx, int64_t n,
-                            hipStream_t stream) {
-  if (!table || !idx) return fail(IX_ERR_INVALID, "NULL table or idx");
-  if (rows < 1 || rows > ((int64_t)1 << 31) / 128 || n < 0)
-    return fail(IX_ERR_INVALID, "rows=%lld n=%lld out of range", (long long)rows, (long long)n);
-  if (n == 0) return ok();
-  hipError_t e = ix::launch_peak_atomic(table, rows, idx, n, stream);
-  if (e != hipSuccess) return hip_fail(e, "ix_peak_atomic_add launch");
-  return ok();
-}
-
-ix_status ix_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
-  if (!src || !dst) return fail(IX_ERR_INVALID, "NULL src or dst");
-  if (bytes % 16 || !aligned16(src) || !aligned16(dst))
-    return fail(IX_ERR_INVALID, "bytes and both pointers must be multiples of 16");
-  if (bytes == 0) return ok();
-  hipError_t e = ix::launch_peak_copy(src, dst, bytes, stream);
-  if (e != hipSuccess) return hip_fail(e, "ix_peak_copy launch");
-  return ok();
-}
-
-ix_status ix_peak_gather(const void* table, size_t table_bytes, const int32_t* rows, int64_t n,
-                         uint32_t* out, hipStream_t stream) {
-  if (!table || !rows || !out) return fail(IX_ERR_INVALID, "NULL table, rows or out");
-  if (n < 0) return fail(IX_ERR_INVALID, "n=%lld must be >= 0", (long long)n);
-  if (table_bytes == 0 || table_bytes % 256 || table_bytes > ((size_t)1 << 31))
-    return fail(IX_ERR_INVALID, "table_bytes must be a positive multiple of 256, at most 2 GiB");
-  if (!aligned16(table)) return fail(IX_ERR_INVALID, "table must be 16-byte aligned");
-  if (n == 0) return ok();
-  hipError_t e = ix::launch_peak_gather(table, table_bytes, rows, n, out, stream);
-  if (e != hipSuccess) return hip_fail(e, "ix_peak_gather launch");
   return ok();
 }
 

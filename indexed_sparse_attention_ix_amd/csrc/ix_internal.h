@@ -32,13 +32,19 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k);
 
 // Sparse attention launch shape.
 struct AttnPlan {
+  int layers;       // layers per launch: up to 8 share one grid when one layer's grid is small
   int n_splits;     // blocks per (query, kv head); >1 writes partials then combines
   int chunks;       // ceil(k / 32)
   int chunks_per_split;
-  size_t ws_bytes;
+  size_t part_bytes;  // split partials of one layer of a launch (0 without splits)
+  size_t ws_bytes;    // layers * part_bytes
 };
 
-AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k);
+// The launch shape for the attention of n_layers layers over one selection (1 for
+// sparse_attn_fwd).
+AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k, int n_layers);
+// The largest workspace the attention of any number of layers needs.
+size_t attn_group_ws_bytes(int B, int T, int H_q, int H_kv, int d, int k);
 
 hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, float* scores,
                            hipStream_t stream);
@@ -56,16 +62,15 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                               int d, int k, float sm_scale, void* out, float* lse,
                               const AttnPlan& p, void* ws, hipStream_t stream);
 
-// The attention of n_layers layers over one selection: up to 8 layers per launch when one
-// layer's grid is small (fewer than 1024 blocks), else one launch per layer; layer l of a
-// launch uses ws + l * pl.ws_bytes for its split partials.
+// The attention of n_layers layers over one selection, pl = make_attn_plan(..., n_layers):
+// pl.layers layers per launch; layer l of a launch uses ws + l * pl.part_bytes for its
+// split partials.
 hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const void* const* kc,
                                      const void* const* vc, const int32_t* idx,
                                      const int32_t* kv_len, int B, int T, int S_max, int H_q,
                                      int H_kv, int d, int k, float sm_scale, void* const* out,
                                      float* const* lse, const AttnPlan& pl, void* ws,
                                      hipStream_t stream);
-constexpr int kAttnLayersPerLaunch = 8;
 // Atomic-free key gradients (pair_reduce.hip): workspace layout for passes of `rows` query
 // rows whose pairs carry row_bytes of bf16 gradient rows each.
 struct PairLayout {
@@ -104,13 +109,6 @@ hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float*
                               const int32_t* kv_len, const int32_t* idx, const float* dscores,
                               int B, int T, int S_max, int H_I, int d_I, int k, float* dq,
                               float* dw, float* dk, void* ws, size_t ws_bytes, hipStream_t stream);
-hipError_t launch_peak_mfma(const void* operands, int valu_per_mfma, int blocks, int iters,
-                            float* out, hipStream_t stream);
-hipError_t launch_peak_atomic(float* table, int64_t rows, const int32_t* idx, int64_t n,
-                              hipStream_t stream);
-hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
-hipError_t launch_peak_gather(const void* table, size_t table_bytes, const int32_t* rows, int64_t n,
-                              uint32_t* out, hipStream_t stream);
 hipError_t launch_append_kv(const float* k_I_new, const void* K_new, const void* V_new,
                             const int32_t* pos0, int B, int T_new, int S_max, int d_I, int H_kv,
                             int d, uint8_t* k_I_cache, void* K_cache, void* V_cache,

@@ -22,7 +22,9 @@
 // The four waves' (m, l, O) are merged through LDS at the end.  Small batches split
 // the selection over several blocks and merge the normalised partials by lse; when one
 // layer's grid is that small, the layers of an IndexShare group share one launch (each
-// block serves one layer and does exactly the work of the single-layer launch).
+// block serves one layer; the split count follows the launch's total grid, so a layer's
+// result equals the single-layer call's up to the rounding of the partials' merge, and
+// bit for bit when both use the same split count).
 #include <algorithm>
 
 #include "attn_common.h"
@@ -33,8 +35,7 @@ namespace ix {
 
 namespace {
 
-// Layers whose attention one launch can run: each block serves one layer, with the same
-// work and the same result as a launch for that layer alone.
+// Layers whose attention one launch can run: each block serves one layer.
 constexpr int kAttnMaxLayers = 8;
 
 struct AttnArgs {
@@ -370,18 +371,26 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, in
 
 }  // namespace
 
-AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
+// Grids of fewer than 1024 blocks per layer (decode) are latency- and miss-bound: one launch
+// then serves up to 8 layers, and each selection is split over as many blocks as make the
+// launch about one block per CU (256), with at least two chunks per wave.  Measured on the
+// 64-sequence decode step with the caches cold: 4 layers at 1 block per query take 16 us per
+// layer (8 per query: 20 us; 16: 39 us), one layer is fastest at 4 per query (29 us; 8: 31 us).
+// More blocks put more row requests in flight at once than the memory system serves well.
+AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k, int n_layers) {
   (void)H_q;
   AttnPlan p{};
   p.chunks = (k + kChunk - 1) / kChunk;
   const int64_t base = (int64_t)B * T * H_kv;
   int ns = 1;
+  p.layers = 1;
   if (base > 0 && base < 1024) {
-    // one round of resident blocks (2 per CU), at least two chunks per wave so the
-    // gathers of a wave's next chunk overlap the current one
-    const int64_t want = (512 + base - 1) / base;
+    p.layers = n_layers < kAttnMaxLayers ? (n_layers < 1 ? 1 : n_layers) : kAttnMaxLayers;
+    const int64_t grid = base * p.layers;
+    int64_t want = (256 + grid / 2) / grid;
     int64_t by_chunks = p.chunks / (2 * kAttnWaves);
     if (by_chunks < 1) by_chunks = 1;
+    if (want < 1) want = 1;
     ns = (int)(want < by_chunks ? want : by_chunks);
   }
   p.n_splits = ns;
@@ -390,9 +399,19 @@ AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k) {
     const size_t parts = (size_t)base * ns;
     const size_t o_bytes = parts * 16 * d * sizeof(float);
     const size_t l_bytes = parts * 16 * sizeof(float);
-    p.ws_bytes = ((o_bytes + 255) / 256) * 256 + ((l_bytes + 255) / 256) * 256;
+    p.part_bytes = ((o_bytes + 255) / 256) * 256 + ((l_bytes + 255) / 256) * 256;
   }
+  p.ws_bytes = (size_t)p.layers * p.part_bytes;
   return p;
+}
+
+size_t attn_group_ws_bytes(int B, int T, int H_q, int H_kv, int d, int k) {
+  size_t m = 0;
+  for (int n = 1; n <= kAttnMaxLayers; ++n) {
+    const size_t w = make_attn_plan(B, T, H_q, H_kv, d, k, n).ws_bytes;
+    m = w > m ? w : m;
+  }
+  return m;
 }
 
 hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const void* const* kc,
@@ -417,9 +436,7 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
   x.chunks_per_split = pl.chunks_per_split;
   const size_t parts = (size_t)B * T * H_kv * pl.n_splits;
   const size_t o_bytes = ((parts * 16 * d * sizeof(float) + 255) / 256) * 256;
-  // Layers share a launch only when one layer's grid is short of two rounds of resident
-  // blocks (decode): there the launches are latency-bound and the layers overlap.
-  const int per_launch = parts < 1024 ? kAttnMaxLayers : 1;
+  const int per_launch = pl.layers;
   for (int l0 = 0; l0 < n_layers; l0 += per_launch) {
     const int nl = n_layers - l0 < per_launch ? n_layers - l0 : per_launch;
     x.layers = nl;
@@ -430,7 +447,7 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
       x.vc[l] = reinterpret_cast<const uint16_t*>(vc[src]);
       x.out[l] = reinterpret_cast<uint16_t*>(out[src]);
       x.lse[l] = lse ? lse[src] : nullptr;
-      char* part = reinterpret_cast<char*>(ws) + (size_t)(l < nl ? l : 0) * pl.ws_bytes;
+      char* part = reinterpret_cast<char*>(ws) + (size_t)(l < nl ? l : 0) * pl.part_bytes;
       x.part_o[l] = pl.n_splits > 1 ? reinterpret_cast<float*>(part) : nullptr;
       x.part_lse[l] = pl.n_splits > 1 ? reinterpret_cast<float*>(part + o_bytes) : nullptr;
     }

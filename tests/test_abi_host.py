@@ -7,16 +7,16 @@ import re
 import pytest
 
 from indexed_sparse_attention_ix_amd import binding as bd
+from indexed_sparse_attention_ix_amd import peaks as pk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
-           if f.endswith(".h")]
+INCLUDE = os.path.join(ROOT, "include")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH), reason="libix.so not built")
 
 
-def declared_functions():
-    text = "\n".join(open(h).read() for h in HEADERS)
+def declared_functions(header):
+    text = open(os.path.join(INCLUDE, header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                        text, flags=re.M)
@@ -24,11 +24,19 @@ def declared_functions():
 
 
 def test_every_declared_symbol_is_exported():
-    names = declared_functions()
+    # ix.h is libix.so's interface; ix_peaks.h is the microbenchmark library's
+    assert sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h")) == ["ix.h", "ix_peaks.h"]
+    names = declared_functions("ix.h")
     assert set(names) == set(bd.EXPORTS)
     lib = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
+    assert not any(hasattr(lib, n) for n in pk.EXPORTS), "microbenchmarks in the path's library"
+    pnames = declared_functions("ix_peaks.h")
+    assert set(pnames) == set(pk.EXPORTS)
+    plib = ctypes.CDLL(pk.LIB_PATH)
+    for n in pnames:
+        assert hasattr(plib, n), n
 
 
 def test_abi_version_and_clean_error():
@@ -330,19 +338,31 @@ def test_indexer_bwd_validation_codes():
 
 
 def test_peak_validation_codes():
-    assert status_of(bd.ix_peak_mfma_fp8, 0, 8, 1, 1, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_mfma_fp8, FAKE, 6, 1, 1, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_mfma_fp8, FAKE, 8, 0, 1, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_copy, FAKE, FAKE, 24) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_copy, FAKE, FAKE, 0) == bd.IX_OK
-    assert status_of(bd.ix_peak_gather, FAKE, 1000, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_gather, FAKE, 1 << 32, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_gather, FAKE, 256, FAKE, -1, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_gather, FAKE, 256, FAKE, 0, FAKE) == bd.IX_OK
-    assert status_of(bd.ix_peak_atomic_add, 0, 10, FAKE, 5) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_atomic_add, FAKE, 0, FAKE, 5) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_atomic_add, FAKE, (1 << 24) + 1, FAKE, 5) == bd.IX_ERR_INVALID
-    assert status_of(bd.ix_peak_atomic_add, FAKE, 10, FAKE, 0) == bd.IX_OK
+    assert status_of(pk.ix_peak_mfma_fp8, 0, 8, 1, 1, FAKE) == bd.IX_ERR_INVALID
+    assert "NULL" in pk.load().ix_peak_last_error().decode()
+    assert status_of(pk.ix_peak_mfma_fp8, FAKE, 6, 1, 1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_mfma_fp8, FAKE, 8, 0, 1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_copy, FAKE, FAKE, 24) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_copy, FAKE, FAKE, 0) == bd.IX_OK
+    assert status_of(pk.ix_peak_read, FAKE, 24, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, 0, 32, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, FAKE, 0, FAKE) == bd.IX_OK
+    assert status_of(pk.ix_peak_gather, FAKE, 1000, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 1 << 32, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, -1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, 0, FAKE) == bd.IX_OK
+    sel = pk.ix_peak_gather_selection
+    assert status_of(sel, FAKE, FAKE, 0, FAKE, 1, 4, 100, 1, 128, 64, 1, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, 1, 96, 64, 1, 0, FAKE) == bd.IX_ERR_UNSUPPORTED
+    assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, 1, 128, 4096, 1, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, 1, 128, 64, 0, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, 1, 128, 64, 1, 1, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(sel, FAKE + 8, FAKE, FAKE, FAKE, 1, 4, 100, 1, 128, 64, 1, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 0, 4, 100, 1, 128, 64, 1, 2, FAKE) == bd.IX_OK
+    assert status_of(pk.ix_peak_atomic_add, 0, 10, FAKE, 5) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_atomic_add, FAKE, 0, FAKE, 5) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_atomic_add, FAKE, (1 << 24) + 1, FAKE, 5) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_atomic_add, FAKE, 10, FAKE, 0) == bd.IX_OK
 
 
 def test_workspace_sizes_for_the_named_workloads():

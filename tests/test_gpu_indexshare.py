@@ -24,6 +24,68 @@ def _group_case(**kw):
     return Workload(**base)
 
 
+def _same_as_group_attention(layers, idx, kv_len, sm_scale, outs, lses):
+    """The group's outputs are sparse_attn_group_fwd's on the same selection, bit for bit,
+    and each layer's standalone sparse_attn_fwd's up to a different split of the selection:
+    each split rounds P to bf16 against its own running maximum, so the two differ by bf16
+    roundings of the terms (random in sign, so per (row, head) in norm within 2^-5 of the
+    output) and lse by fp32 sums of the k weights in another order ((k + 64) 2^-23)."""
+    go, gl = bd.group_attention([dict(q=L["q"], K=L["K"], V=L["V"]) for L in layers], idx,
+                                sm_scale, kv_len=kv_len, with_lse=True)
+    k = idx.shape[-1]
+    for l, L in enumerate(layers):
+        assert torch.equal(outs[l], go[l]) and torch.equal(lses[l], gl[l]), f"layer {l}"
+        o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, sm_scale, kv_len=kv_len,
+                                     with_lse=True)
+        a, b = outs[l].double(), o2.double()
+        num, den = (a - b).norm(dim=-1), b.norm(dim=-1)
+        assert bool((num <= 2.0 ** -5 * den + 1e-7).all()), \
+            f"layer {l}: worst relative difference {float((num / den.clamp(min=1e-30)).max()):.3e}"
+        fin = torch.isfinite(l2)
+        assert torch.equal(fin, torch.isfinite(lses[l]))
+        assert bool(((lses[l] - l2).abs()[fin] <= (k + 64) * 2.0 ** -23 * (1 + l2.abs()[fin])).all()), \
+            f"layer {l} lse"
+
+
+def test_group_attention_entry_point_against_standalone_and_oracle():
+    """sparse_attn_group_fwd on a caller's selection: a ragged prefill (one launch per layer,
+    the same split as standalone calls: bit for bit) and a decode batch (layers in one
+    launch), against the oracle."""
+    for case in (dict(B=2, T=150, S=3000, pos0s=(2850, 1000), kv_lens=(3000, 2500), k=256,
+                      layers=3, seed=45),
+                 dict(B=8, T=1, S=9000, pos0=8999, pos0s=None, kv_lens=None, k=2048, layers=3,
+                      seed=46, planted=16)):
+        wl = _group_case(**case)
+        say(f"[sparse_attn_group_fwd] B={wl.B} T={wl.T} S={wl.S} k={wl.k} layers={wl.layers}")
+        ind = synth.indexer_inputs(wl, device=DEV)
+        layers = [synth.attention_inputs(wl, layer=l, device=DEV) for l in range(wl.layers)]
+        args = (ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"])
+        idx = bd.topk(*args, wl.k)
+        outs, lses = bd.group_attention([dict(q=L["q"], K=L["K"], V=L["V"]) for L in layers],
+                                        idx, wl.sm_scale, kv_len=ind["kv_len"], with_lse=True)
+        for l, L in enumerate(layers):
+            o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
+                                         kv_len=ind["kv_len"], with_lse=True)
+            if wl.T > 1:
+                assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2), f"layer {l}"
+        torch.cuda.synchronize()
+        h = to_host_indexer(ind)
+        idx_np = idx.cpu().numpy()
+        for b in range(wl.B):
+            keys = O.decode_e4m3(h["k_I"][b])
+            rows = list(range(0, wl.T, 7)) + [wl.T - 1]
+            ns = [O.visible_count(h["q_pos0"][b], h["kv_len"][b], t) for t in rows]
+            scs = [O.score_row(h["q_I"][b, t], keys[:n], h["w"][b, t], n) for t, n in zip(rows, ns)]
+            ref_idx, same = oracle_selection(idx_np[b, rows], scs, wl.k, ns, where=f"b={b}")
+            for l in range(wl.layers):
+                hl = to_host_attn(layers[l])
+                ref_o, ref_l = O.sparse_attention_rows(hl["q"], hl["K"], hl["V"], ref_idx, b, rows,
+                                                       wl.sm_scale)
+                check_attention(bf16_to_f64(outs[l])[b][rows][same], ref_o[same],
+                                lses[l].cpu().numpy()[b][rows][same], ref_l[same],
+                                where=f"layer={l} b={b}")
+
+
 def test_group_matches_standalone_calls_bitwise_and_oracle():
     wl = _group_case()
     say(f"[indexshare_group_fwd] B={wl.B} T={wl.T} S={wl.S} k={wl.k} layers={wl.layers}")
@@ -78,12 +140,9 @@ def test_group_decode_shape():
     idx, outs, lses = bd.indexshare_group(*args, wl.k, [dict(q=L["q"], K=L["K"], V=L["V"])
                                                         for L in layers], wl.sm_scale,
                                           with_lse=True)
-    # the layers share one attention launch (split partials per layer, one combine): the
-    # same bits as standalone calls
-    for l, L in enumerate(layers):
-        o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
-                                     kv_len=ind["kv_len"], with_lse=True)
-        assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2), f"layer {l}"
+    # the layers share one attention launch: bit for bit sparse_attn_group_fwd on the same
+    # selection, and standalone calls up to the rounding of the split merges
+    _same_as_group_attention(layers, idx, ind["kv_len"], wl.sm_scale, outs, lses)
     torch.cuda.synchronize()
     h = to_host_indexer(ind)
     idx_np = idx.cpu().numpy()
@@ -102,8 +161,8 @@ def test_group_decode_shape():
 
 
 def test_group_of_ten_layers_decode_two_launches():
-    """More layers than one launch takes (8): the attention runs as 8 + 2, still bit for bit
-    the standalone calls."""
+    """More layers than one launch takes (8): the attention runs as 8 + 2, bit for bit
+    sparse_attn_group_fwd and standalone calls up to the rounding of split merges."""
     wl = _group_case(B=4, T=1, S=5000, pos0s=None, kv_lens=None, pos0=4999, k=512, seed=44,
                      layers=10, planted=16)
     say(f"[indexshare_group_fwd] decode B={wl.B} S={wl.S} layers={wl.layers}")
@@ -114,8 +173,5 @@ def test_group_of_ten_layers_decode_two_launches():
                                                         for L in layers], wl.sm_scale,
                                           with_lse=True)
     assert torch.equal(idx, bd.topk(*args, wl.k))
-    for l, L in enumerate(layers):
-        o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
-                                     kv_len=ind["kv_len"], with_lse=True)
-        assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2), f"layer {l}"
+    _same_as_group_attention(layers, idx, ind["kv_len"], wl.sm_scale, outs, lses)
     torch.cuda.synchronize()

@@ -1,11 +1,11 @@
 """GPU: the measured-ceiling kernels (ix_peaks.h) do the work they are timed on: the copy is
-exact, the gather reads exactly the listed rows (XOR checksum against numpy), and the
-MFMA loop runs for every VALU setting."""
+exact, the read-only stream, the row gather and the selection gather read exactly the bytes
+they should (XOR checksums against numpy), and the MFMA loop runs for every VALU setting."""
 import numpy as np
 import pytest
 import torch
 
-from indexed_sparse_attention_ix_amd import binding as bd
+from indexed_sparse_attention_ix_amd import peaks as pk
 from parity_util import say
 
 pytestmark = pytest.mark.gpu
@@ -17,7 +17,7 @@ def test_peak_copy_exact():
     n = 3 * (1 << 20) + 48
     src = torch.randint(0, 256, (n,), dtype=torch.int32).to(torch.uint8).to(DEV)
     dst = torch.zeros_like(src)
-    bd.ix_peak_copy(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+    pk.ix_peak_copy(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
 
@@ -27,9 +27,9 @@ def test_peak_gather_checksum():
     g = torch.Generator().manual_seed(5)
     table = torch.randint(-2**31, 2**31 - 1, (4096 * 64,), generator=g, dtype=torch.int32)
     rows = torch.randint(-5, 4096 + 5, (100003,), generator=g, dtype=torch.int32)
-    out = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.zeros(2048, dtype=torch.int32, device=DEV)
     table_d, rows_d = table.to(DEV), rows.to(DEV)   # kept alive until the kernel has run
-    bd.ix_peak_gather(table_d.data_ptr(), 4096 * 256, rows_d.data_ptr(), rows.numel(),
+    pk.ix_peak_gather(table_d.data_ptr(), 4096 * 256, rows_d.data_ptr(), rows.numel(),
                       out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     t = table.numpy().view(np.uint32).reshape(4096, 64)
@@ -38,7 +38,7 @@ def test_peak_gather_checksum():
     valid = r[(r >= 0) & (r < 4096)]
     counts = np.bincount(valid, minlength=4096)
     want = np.bitwise_xor.reduce(np.where(counts % 2 == 1, row_x, 0))
-    assert int(out.cpu().numpy().view(np.uint32)[0]) == int(want)
+    assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
 
 
 def test_peak_mfma_runs():
@@ -46,7 +46,7 @@ def test_peak_mfma_runs():
     for nv in (0, 4, 8, 12):
         say(f"[ix_peak_mfma_fp8] valu_per_mfma={nv}")
         out = torch.zeros(1, dtype=torch.float32, device=DEV)
-        bd.ix_peak_mfma_fp8(ops.data_ptr(), nv, 8, 4, out.data_ptr(),
+        pk.ix_peak_mfma_fp8(ops.data_ptr(), nv, 8, 4, out.data_ptr(),
                             torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         assert torch.isfinite(out).all() and out.item() != 0.0
@@ -58,10 +58,54 @@ def test_peak_atomic_add_counts():
     rows = torch.randint(-3, 1003, (50007,), generator=g, dtype=torch.int32)
     table = torch.zeros(1000 * 128, dtype=torch.float32, device=DEV)
     rows_d = rows.to(DEV)
-    bd.ix_peak_atomic_add(table.data_ptr(), 1000, rows_d.data_ptr(), rows.numel(),
+    pk.ix_peak_atomic_add(table.data_ptr(), 1000, rows_d.data_ptr(), rows.numel(),
                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     r = rows.numpy()
     want = np.bincount(r[(r >= 0) & (r < 1000)], minlength=1000).astype(np.float32)
     got = table.view(1000, 128).cpu().numpy()
     assert np.array_equal(got, np.repeat(want[:, None], 128, axis=1))
+
+
+def test_peak_read_checksum():
+    say("[ix_peak_read] 5 MiB + 32 bytes")
+    g = torch.Generator().manual_seed(6)
+    n = 5 * (1 << 20) + 32
+    src = torch.randint(-2**31, 2**31 - 1, (n // 4,), generator=g, dtype=torch.int32)
+    out = torch.zeros(4096, dtype=torch.int32, device=DEV)
+    src_d = src.to(DEV)
+    pk.ix_peak_read(src_d.data_ptr(), n, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+    assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
+
+
+@pytest.mark.parametrize("d,splits,occ", [(128, 1, 0), (128, 3, 2), (64, 2, 3)])
+def test_peak_gather_selection_checksum(d, splits, occ):
+    say(f"[ix_peak_gather_selection] d={d} splits={splits} blocks_per_cu={occ}, ragged kv_len")
+    g = torch.Generator().manual_seed(7 + d + splits)
+    B, T, S, H_kv, k = 2, 37, 700, 2, 100
+    kc = torch.randint(-2**15, 2**15 - 1, (B, S, H_kv, d), generator=g, dtype=torch.int16)
+    vc = torch.randint(-2**15, 2**15 - 1, (B, S, H_kv, d), generator=g, dtype=torch.int16)
+    idx = torch.randint(-3, S, (B, T, k), generator=g, dtype=torch.int32)
+    kvl = torch.tensor([S, 450], dtype=torch.int32)
+    out = torch.zeros(B * T * H_kv * splits, dtype=torch.int32, device=DEV)
+    dev = [x.to(DEV) for x in (kc, vc, idx, kvl)]
+    pk.ix_peak_gather_selection(dev[0].data_ptr(), dev[1].data_ptr(), dev[2].data_ptr(),
+                                dev[3].data_ptr(), B, T, S, H_kv, d, k, splits, occ, out.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    # XOR of each valid entry's K and V rows (per KV head), counted once per entry
+    want = np.uint32(0)
+    K = kc.numpy().view(np.uint16).astype(np.uint32)
+    V = vc.numpy().view(np.uint16).astype(np.uint32)
+    for b in range(B):
+        rows = idx[b].numpy().reshape(-1)
+        rows = rows[(rows >= 0) & (rows < int(kvl[b]))]
+        cnt = np.bincount(rows, minlength=S) % 2
+        for h in range(H_kv):
+            kw = (K[b, :, h, 0::2] | (K[b, :, h, 1::2] << 16)).astype(np.uint32)
+            vw = (V[b, :, h, 0::2] | (V[b, :, h, 1::2] << 16)).astype(np.uint32)
+            rx = np.bitwise_xor.reduce(kw, axis=1) ^ np.bitwise_xor.reduce(vw, axis=1)
+            want ^= np.bitwise_xor.reduce(np.where(cnt == 1, rx, 0).astype(np.uint32))
+    assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
