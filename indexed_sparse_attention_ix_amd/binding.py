@@ -18,7 +18,9 @@ import os
 from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
 from typing import Optional, Sequence
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix.so")
+# IX_LIB names another build of the same ABI (the CPU tests load a sanitized host-only one).
+LIB_PATH = os.environ.get("IX_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                    "libix.so")
 
 ABI_VERSION = 4  # IX_ABI_VERSION of include/ix.h
 IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4

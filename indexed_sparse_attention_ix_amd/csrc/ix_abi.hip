@@ -17,6 +17,21 @@
 // the array's name (which in host code is only a stand-in).
 static __device__ __align__(256) unsigned char scratch[IX_NOALLOC_SCRATCH_BYTES];
 
+// Launches go through IX_LAUNCH.  A test build (-DIX_TEST_HOOKS) adds an exported hook that
+// makes them return a chosen HIP error without launching, so the IX_ERR_HIP path and its
+// message are exercised on a machine without a GPU; the release library has no hook.
+#ifdef IX_TEST_HOOKS
+#include <atomic>
+static std::atomic<int> g_test_launch_error{0};
+extern "C" __attribute__((visibility("default"))) void ix_test_fail_launches(int32_t hip_error) {
+  g_test_launch_error.store(hip_error);
+}
+#define IX_LAUNCH(call) \
+  (g_test_launch_error.load() ? static_cast<hipError_t>(g_test_launch_error.load()) : (call))
+#else
+#define IX_LAUNCH(call) (call)
+#endif
+
 namespace {
 
 thread_local std::string g_err;
@@ -187,16 +202,16 @@ ix_status group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_layers, const
       return fail(IX_ERR_WORKSPACE,
                   "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu",
                   need, (size_t)IX_NOALLOC_SCRATCH_BYTES);
-    const hipError_t es = device_scratch(stream, &ws);
+    const hipError_t es = IX_LAUNCH(device_scratch(stream, &ws));
     if (es != hipSuccess) return hip_fail(es, "no-allocation scratch address");
     ws_bytes = IX_NOALLOC_SCRATCH_BYTES;
   }
   if (!ws || ws_bytes < need)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
-  hipError_t e = ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "indexshare selection launch");
-  e = ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, a->kv_len, a->B, a->T, a->S_max,
-                                    H_q, H_kv, d, k, sm_scale, out, lse, ap, ws, stream);
+  e = IX_LAUNCH(ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, a->kv_len, a->B, a->T, a->S_max,
+                                    H_q, H_kv, d, k, sm_scale, out, lse, ap, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "indexshare attention launch");
   return ok();
 }
@@ -218,7 +233,7 @@ ix_status ix_score(const ix_indexer_args* a, int32_t t_begin, int32_t t_end, flo
     return fail(IX_ERR_INVALID, "row range [%d,%d) outside [0,%d)", t_begin, t_end, a->T);
   if (empty || t_end == t_begin) return ok();
   if (!scores) return fail(IX_ERR_INVALID, "scores pointer is NULL");
-  hipError_t e = ix::launch_ix_score(*a, t_begin, t_end, scores, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_ix_score(*a, t_begin, t_end, scores, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_score launch");
   return ok();
 }
@@ -242,7 +257,7 @@ ix_status ix_topk(const ix_indexer_args* a, int32_t k, int32_t* idx, float* sel_
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 plan.ws_bytes);
-  hipError_t e = ix::launch_ix_topk(*a, k, plan, idx, sel_scores, ws, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(*a, k, plan, idx, sel_scores, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_topk launch");
   return ok();
 }
@@ -269,8 +284,8 @@ ix_status sparse_attn_fwd(const void* q, const void* kc, const void* vc, const i
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 plan.ws_bytes);
-  hipError_t e = ix::launch_sparse_attn(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
-                                        sm_scale, out, lse, plan, ws, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_sparse_attn(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
+                                        sm_scale, out, lse, plan, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_fwd launch");
   return ok();
 }
@@ -302,8 +317,8 @@ ix_status sparse_attn_group_fwd(int32_t n_layers, const void* const* q, const vo
   if (ap.ws_bytes && (!ws || ws_bytes < ap.ws_bytes))
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 ap.ws_bytes);
-  hipError_t e = ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, kv_len, B, T, S_max, H_q,
-                                               H_kv, d, k, sm_scale, out, lse, ap, ws, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, kv_len, B, T, S_max, H_q,
+                                               H_kv, d, k, sm_scale, out, lse, ap, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_group_fwd launch");
   return ok();
 }
@@ -366,8 +381,8 @@ ix_status ix_append_kv(const float* k_I_new, const void* K_new, const void* V_ne
   if ((int64_t)B * T_new > kMaxBlocks)
     return fail(IX_ERR_UNSUPPORTED, "B*T_new=%lld rows: one launch holds at most %lld",
                 (long long)((int64_t)B * T_new), (long long)kMaxBlocks);
-  hipError_t e = ix::launch_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
-                                      k_I_cache, K_cache, V_cache, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
+                                      k_I_cache, K_cache, V_cache, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_append_kv launch");
   return ok();
 }
@@ -386,7 +401,7 @@ ix_status ix_pool_keys(const uint8_t* k_I, const int32_t* kv_len, int32_t B, int
   if (block_rows > ((int64_t)1 << 40) || !items_fit(block_rows * pieces_per_row))
     return fail(IX_ERR_UNSUPPORTED, "B*ceil(S_max/pool)=%lld block keys: too many for one launch",
                 (long long)block_rows);
-  hipError_t e = ix::launch_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_pool_keys(k_I, kv_len, B, S_max, d_I, pool, k_pooled, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_pool_keys launch");
   return ok();
 }
@@ -420,10 +435,10 @@ ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_block
   if (!ws || ws_bytes < need)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
   int32_t* blocks = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + plan.ws_bytes);
-  hipError_t e = ix::launch_ix_topk(u, k_blocks, plan, blocks, nullptr, ws, stream, pool);
+  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(u, k_blocks, plan, blocks, nullptr, ws, stream, pool));
   if (e != hipSuccess) return hip_fail(e, "ix_topk_pooled launch");
-  e = ix::launch_expand_blocks(blocks, a->q_pos0, a->kv_len, a->B, a->T, a->S_max, k_blocks, pool,
-                               idx, stream);
+  e = IX_LAUNCH(ix::launch_expand_blocks(blocks, a->q_pos0, a->kv_len, a->B, a->T, a->S_max, k_blocks, pool,
+                               idx, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_topk_pooled expansion launch");
   return ok();
 }
@@ -465,9 +480,9 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
   } else if (ws_bytes != 0) {
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
-  hipError_t e = ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
+  hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
                                             H_q, H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes,
-                                            stream);
+                                            stream));
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_bwd launch");
   return ok();
 }
@@ -503,9 +518,9 @@ ix_status indexshare_group_bwd(const int32_t* idx, const int32_t* kv_len, int32_
   if (ix::pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes) < 1)
     return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
                 ws_bytes, ix::pair_layout(B, S_max, k, 1, row_bytes).total);
-  hipError_t e = ix::launch_sparse_attn_bwd_layers(n_layers, q, kc, vc, idx, kv_len, out, lse, dout,
+  hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_bwd_layers(n_layers, q, kc, vc, idx, kv_len, out, lse, dout,
                                                    B, T, S_max, H_q, H_kv, d, k, sm_scale, dq, dkc,
-                                                   dvc, ws, ws_bytes, stream);
+                                                   dvc, ws, ws_bytes, stream));
   if (e != hipSuccess) return hip_fail(e, "indexshare_group_bwd launch");
   return ok();
 }
@@ -524,8 +539,8 @@ ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const
     return fail(IX_ERR_INVALID, "bf16 q/kc base pointers must be 16-byte aligned");
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
-  hipError_t e = ix::launch_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv,
-                                       d, k, sm_scale, loss, dscores, stream);
+  hipError_t e = IX_LAUNCH(ix::launch_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv,
+                                       d, k, sm_scale, loss, dscores, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_kl launch");
   return ok();
 }
@@ -562,9 +577,9 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
   } else if (ws_bytes != 0) {
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
-  hipError_t e = ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
+  hipError_t e = IX_LAUNCH(ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
                                         a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, ws, ws_bytes,
-                                        stream);
+                                        stream));
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");
   return ok();
 }
