@@ -904,31 +904,39 @@ def main():
         dK = torch.zeros((wl.B, wl.S, wl.H_kv, wl.d), dtype=torch.float32, device=dev)
         dV = torch.zeros_like(dK)
 
-        # two forms: fp32 atomics (no workspace), and the atomic-free one (inverted
-        # selection, per-pair bf16 rows, key-major sums) in passes that fit a 32 GiB workspace
-        per_row = bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, 2) - \
-            bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, 1)
-        rows_pp = int(max(1, min(wl.B * wl.T, (32 << 30) // max(per_row, 1))))
-        bws_n = bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k, rows_pp)
-        bws = torch.empty(bws_n, dtype=torch.uint8, device=dev)
+        # three forms: fp32 atomics (no workspace), and the atomic-free one (inverted
+        # selection, per-pair rows, key-major sums) with bf16 or fp32 pair rows, in passes that
+        # fit a 32 GiB workspace
+        def pass_plan(pair_rows):
+            def need(rows):
+                return bd.sparse_attn_bwd_workspace_bytes(wl.B, wl.T, wl.S, wl.H_kv, wl.d, wl.k,
+                                                          rows, pair_rows)
+            rows = int(max(1, min(wl.B * wl.T, (32 << 30) // max(need(2) - need(1), 1))))
+            return rows, need(rows)
+        plans = {pr: pass_plan(pr) for pr in (bd.PAIR_ROWS_BF16, bd.PAIR_ROWS_FP32)}
+        rows_pp, bws_n = plans[bd.PAIR_ROWS_BF16]
+        bws = torch.empty(max(n for _, n in plans.values()), dtype=torch.uint8, device=dev)
 
-        def bwd(use_ws):
+        def bwd(use_ws, pair_rows=bd.PAIR_ROWS_BF16):
+            n = plans[pair_rows][1]
             bd.sparse_attn_bwd(qp[0], kp[0], vp[0], idx.data_ptr(), ind["kv_len"].data_ptr(),
                                op[0], lse0.data_ptr(), dout.data_ptr(), wl.B, wl.T, wl.S, wl.H_q,
                                wl.H_kv, wl.d, wl.k, wl.sm_scale, dq.data_ptr(), dK.data_ptr(),
-                               dV.data_ptr(), bws.data_ptr() if use_ws else 0,
-                               bws_n if use_ws else 0, sh)
+                               dV.data_ptr(), pair_rows, bws.data_ptr() if use_ws else 0,
+                               n if use_ws else 0, sh)
         nb = max(2, min(reps, 5))
         ms_form = {}
-        for use_ws in (False, True):
-            bwd(use_ws)
+        for form in ("atomics", "bf16", "fp32"):
+            use_ws = form != "atomics"
+            pr = bd.PAIR_ROWS_FP32 if form == "fp32" else bd.PAIR_ROWS_BF16
+            bwd(use_ws, pr)
             torch.cuda.synchronize()
             e0.record(stream)
             for _ in range(nb):
-                bwd(use_ws)
+                bwd(use_ws, pr)
             e1.record(stream)
             torch.cuda.synchronize()
-            ms_form[use_ws] = e0.elapsed_time(e1) / nb
+            ms_form[form] = e0.elapsed_time(e1) / nb
         # IndexShare group: the L layers' backward with the selection inverted once per pass
         # (layer 0's inputs stand in for every layer: the same work per layer)
         ms_group = None
@@ -939,7 +947,8 @@ def main():
                                         [lse0.data_ptr()] * L, [dout.data_ptr()] * L, wl.B, wl.T,
                                         wl.S, wl.H_q, wl.H_kv, wl.d, wl.k, wl.sm_scale,
                                         [dq.data_ptr()] * L, [dK.data_ptr()] * L,
-                                        [dV.data_ptr()] * L, bws.data_ptr(), bws_n, sh)
+                                        [dV.data_ptr()] * L, bd.PAIR_ROWS_BF16, bws.data_ptr(),
+                                        bws_n, sh)
             gbwd()
             torch.cuda.synchronize()
             e0.record(stream)
@@ -949,12 +958,14 @@ def main():
             torch.cuda.synchronize()
             ms_group = e0.elapsed_time(e1) / nb
         del bws
-        ms_b = ms_form[False]
+        ms_b = ms_form["atomics"]
         bflops = sel * 10.0 * wl.H_q * wl.d   # S, dP, dq, dK, dV: 2 H_q d flop each per pair
         backward = {"ms_per_layer": round(min(ms_form.values()), 3),
-                    "ms_per_layer_atomics": round(ms_form[False], 3),
-                    "ms_per_layer_atomic_free": round(ms_form[True], 3),
+                    "ms_per_layer_atomics": round(ms_form["atomics"], 3),
+                    "ms_per_layer_atomic_free": round(ms_form["bf16"], 3),
                     "atomic_free_rows_per_pass": rows_pp,
+                    "ms_per_layer_atomic_free_fp32_rows": round(ms_form["fp32"], 3),
+                    "atomic_free_fp32_rows_per_pass": plans[bd.PAIR_ROWS_FP32][0],
                     "group_ms_per_layer_atomic_free": (round(ms_group / L, 3)
                                                        if ms_group is not None else None),
                     # rates of the faster form; the atomic rates below are the atomic form's
@@ -1017,34 +1028,44 @@ def main():
         dw_I = torch.empty((wl.B, wl.T, wl.H_I), dtype=torch.float32, device=dev)
         dk_I = torch.zeros((wl.B, wl.S, wl.d_I), dtype=torch.float32, device=dev)
 
-        # the two forms, as for the attention: atomics, and atomic-free within 32 GiB
-        per_row_i = bd.ix_indexer_bwd_workspace_bytes(a, wl.k, 2) - bd.ix_indexer_bwd_workspace_bytes(a, wl.k, 1)
-        rows_i = int(max(1, min(wl.B * wl.T, (32 << 30) // max(per_row_i, 1))))
-        iws_n = bd.ix_indexer_bwd_workspace_bytes(a, wl.k, rows_i)
-        iws = torch.empty(iws_n, dtype=torch.uint8, device=dev)
+        # the forms, as for the attention: atomics, and atomic-free within 32 GiB with bf16 or
+        # fp32 pair rows
+        def ipass_plan(pair_rows):
+            def need(rows):
+                return bd.ix_indexer_bwd_workspace_bytes(a, wl.k, rows, pair_rows)
+            rows = int(max(1, min(wl.B * wl.T, (32 << 30) // max(need(2) - need(1), 1))))
+            return rows, need(rows)
+        iplans = {pr: ipass_plan(pr) for pr in (bd.PAIR_ROWS_BF16, bd.PAIR_ROWS_FP32)}
+        rows_i = iplans[bd.PAIR_ROWS_BF16][0]
+        iws = torch.empty(max(n for _, n in iplans.values()), dtype=torch.uint8, device=dev)
 
-        def ibwd(use_ws):
+        def ibwd(use_ws, pair_rows=bd.PAIR_ROWS_BF16):
+            iws_n = iplans[pair_rows][1]
             bd.ix_indexer_bwd(a, wl.k, idx.data_ptr(), kl_dsc.data_ptr(), dq_I.data_ptr(),
-                              dw_I.data_ptr(), dk_I.data_ptr(), iws.data_ptr() if use_ws else 0,
-                              iws_n if use_ws else 0, sh)
+                              dw_I.data_ptr(), dk_I.data_ptr(), pair_rows,
+                              iws.data_ptr() if use_ws else 0, iws_n if use_ws else 0, sh)
         ms_iform = {}
-        for use_ws in (False, True):
-            ibwd(use_ws)
+        for form in ("atomics", "bf16", "fp32"):
+            use_ws = form != "atomics"
+            pr = bd.PAIR_ROWS_FP32 if form == "fp32" else bd.PAIR_ROWS_BF16
+            ibwd(use_ws, pr)
             torch.cuda.synchronize()
             e0.record(stream)
             for _ in range(nb):
-                ibwd(use_ws)
+                ibwd(use_ws, pr)
             e1.record(stream)
             torch.cuda.synchronize()
-            ms_iform[use_ws] = e0.elapsed_time(e1) / nb
+            ms_iform[form] = e0.elapsed_time(e1) / nb
         del iws
-        ms_ib = ms_iform[False]
+        ms_ib = ms_iform["atomics"]
         adds = sel * wl.d_I
         backward["indexer_backward"] = {
             "ms_per_group": round(min(ms_iform.values()), 3),
-            "ms_per_group_atomics": round(ms_iform[False], 3),
-            "ms_per_group_atomic_free": round(ms_iform[True], 3),
+            "ms_per_group_atomics": round(ms_iform["atomics"], 3),
+            "ms_per_group_atomic_free": round(ms_iform["bf16"], 3),
             "atomic_free_rows_per_pass": rows_i,
+            "ms_per_group_atomic_free_fp32_rows": round(ms_iform["fp32"], 3),
+            "atomic_free_fp32_rows_per_pass": iplans[bd.PAIR_ROWS_FP32][0],
             "mfma_tflops": round(sel * 6.0 * wl.H_I * wl.d_I / (ms_ib / 1e3) / 1e12, 2),
             "fp32_atomic_adds": int(adds),
             "fp32_atomic_adds_per_s": round(adds / (ms_ib / 1e3) / 1e9, 1)}

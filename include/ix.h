@@ -74,8 +74,16 @@ typedef struct ix_indexer_args {
   int32_t B, T, S_max, H_I, d_I;
 } ix_indexer_args;
 
+/* Precision of the per-kept-pair gradient rows that the atomic-free backward forms
+ * (sparse_attn_bwd and ix_indexer_bwd with a workspace, indexshare_group_bwd) write and then
+ * sum per key in fp32.  Not from the pages: an implementation choice.  BF16 rounds each row
+ * once (relative error at most 2^-9 per element) and halves the rows' workspace and traffic;
+ * FP32 stores the rows as the matrix cores left them, so the key sums round as the atomic
+ * form's do, and stay bitwise reproducible. */
+typedef enum ix_pair_rows { IX_PAIR_ROWS_BF16 = 0, IX_PAIR_ROWS_FP32 = 1 } ix_pair_rows;
+
 /* ABI version of this header (bumped on any incompatible change). */
-#define IX_ABI_VERSION 4
+#define IX_ABI_VERSION 5
 int32_t ix_abi_version(void);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
@@ -146,29 +154,34 @@ ix_status sparse_attn_fwd(const void *q, const void *kc, const void *vc, const i
  *           The atomic-free form adds each key's pairs in query-row order: for a given
  *           workspace size (which sets the passes) the result is bitwise the same every run,
  *           except that the entries of one row that repeat a key may add in either order.
+ * pair_rows: an ix_pair_rows value, the precision of the atomic-free form's pair rows
+ *           (checked, and unused, without a workspace).
  * ws, ws_bytes: NULL and 0 -> dK / dV rows are added with fp32 atomics, 2 d per selected
  *           pair.  A workspace (16-byte aligned, at least sparse_attn_bwd_workspace_bytes(...,
- *           1) bytes, contents clobbered) -> no atomics: the query rows are taken in passes
- *           of as many rows as the workspace holds; each pass inverts the selection (pairs
- *           listed per key), writes every pair's dV and dK rows rounded to bf16, and sums
- *           them per key in fp32.
+ *           1, pair_rows) bytes, contents clobbered) -> no atomics: the query rows are taken
+ *           in passes of as many rows as the workspace holds; each pass inverts the selection
+ *           (pairs listed per key), writes every pair's dV and dK rows (in bf16 or fp32), and
+ *           sums them per key in fp32.
  * Errors: as sparse_attn_fwd, plus IX_ERR_INVALID for NULL lse, dout or gradients, for
- * out/dout not 16-byte aligned, for lse or a gradient not 4-byte aligned, or for a
- * misaligned workspace; IX_ERR_WORKSPACE for a workspace below one row's need, or ws_bytes
- * without a workspace.
+ * out/dout not 16-byte aligned, for lse or a gradient not 4-byte aligned, for another
+ * pair_rows or for a misaligned workspace; IX_ERR_WORKSPACE for a workspace below one row's
+ * need, or ws_bytes without a workspace.
  */
 ix_status sparse_attn_bwd(const void *q, const void *kc, const void *vc, const int32_t *idx,
                           const int32_t *kv_len, const void *out, const float *lse,
                           const void *dout, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
                           int32_t H_kv, int32_t d, int32_t k, float sm_scale, float *dq,
-                          float *dkc, float *dvc, void *ws, size_t ws_bytes, hipStream_t stream);
+                          float *dkc, float *dvc, int32_t pair_rows, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* Workspace bytes for sparse_attn_bwd's atomic-free form in passes of rows_per_pass query
- * rows (clamped to B * T): the per-key offsets and cursors (B * S_max + 1 each), the
- * inverted selection (4 bytes per pair) and the pairs' bf16 dV | dK rows (4 d H_kv bytes
- * per pair).  0 on invalid arguments. */
+ * rows (clamped to B * T) with pair rows of precision pair_rows: the per-key offsets and
+ * cursors (B * S_max + 1 each), the inverted selection (4 bytes per pair) and the pairs'
+ * dV | dK rows (4 d H_kv bytes per pair in bf16, 8 d H_kv in fp32).  0 on invalid
+ * arguments. */
 size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int32_t H_kv,
-                                       int32_t d, int32_t k, int32_t rows_per_pass);
+                                       int32_t d, int32_t k, int32_t rows_per_pass,
+                                       int32_t pair_rows);
 
 /*
  * indexshare_group_bwd -- the attention backward of the n_layers layers of an IndexShare
@@ -180,9 +193,9 @@ size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int3
  * dV up to the order of the per-key sums).
  * q, kc, vc, out, lse, dout, dq, dkc, dvc: HOST arrays of n_layers device pointers, each as in
  *          sparse_attn_bwd (dkc[l], dvc[l] ADDED TO; the caller clears them first).
- * idx, kv_len, B..sm_scale: shared by the layers, as in sparse_attn_bwd.
- * ws:      required: at least sparse_attn_bwd_workspace_bytes(..., 1) bytes, 16-byte aligned;
- *          the same layout and pass size as sparse_attn_bwd.
+ * idx, kv_len, B..sm_scale, pair_rows: shared by the layers, as in sparse_attn_bwd.
+ * ws:      required: at least sparse_attn_bwd_workspace_bytes(..., 1, pair_rows) bytes,
+ *          16-byte aligned; the same layout and pass size as sparse_attn_bwd.
  * Errors: as sparse_attn_bwd for every layer, plus IX_ERR_INVALID for n_layers < 1 or a NULL
  * pointer array, IX_ERR_WORKSPACE without a workspace.
  */
@@ -191,8 +204,8 @@ ix_status indexshare_group_bwd(const int32_t *idx, const int32_t *kv_len, int32_
                                const void *const *out, const float *const *lse,
                                const void *const *dout, int32_t B, int32_t T, int32_t S_max,
                                int32_t H_q, int32_t H_kv, int32_t d, int32_t k, float sm_scale,
-                               float *const *dq, float *const *dkc, float *const *dvc, void *ws,
-                               size_t ws_bytes, hipStream_t stream);
+                               float *const *dq, float *const *dkc, float *const *dvc,
+                               int32_t pair_rows, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * ix_indexer_kl -- the indexer's training objective (the twiscan post on GLM-5.2's
@@ -237,25 +250,28 @@ ix_status ix_indexer_kl(const void *q, const void *kc, const int32_t *idx, const
  * dk_I:    fp32 [B, S_max, d_I], ADDED TO; the caller clears it first.  With atomics the
  *          order of the additions, and so the last bits, vary from run to run; the
  *          atomic-free form is bitwise reproducible as for sparse_attn_bwd.
+ * pair_rows: an ix_pair_rows value, the precision of the atomic-free form's dk_I rows
+ *          (checked, and unused, without a workspace).
  * ws, ws_bytes: NULL and 0 -> dk_I rows are added with fp32 atomics, d_I per kept pair.  A
- *          workspace (16-byte aligned, at least ix_indexer_bwd_workspace_bytes(a, k, 1)
- *          bytes, contents clobbered) -> no atomics: passes of as many query rows as it
- *          holds, each inverting the selection, writing every pair's dk_I row rounded to
- *          bf16 and summing them per key in fp32 (as sparse_attn_bwd).
+ *          workspace (16-byte aligned, at least ix_indexer_bwd_workspace_bytes(a, k, 1,
+ *          pair_rows) bytes, contents clobbered) -> no atomics: passes of as many query rows
+ *          as it holds, each inverting the selection, writing every pair's dk_I row (bf16 or
+ *          fp32) and summing them per key in fp32 (as sparse_attn_bwd).
  * Errors: as ix_topk for the indexer arguments and k, plus IX_ERR_INVALID for NULL idx,
- * dscores or gradients, for w, idx, dscores or a gradient not 4-byte aligned, or for a
- * misaligned workspace; IX_ERR_WORKSPACE for a workspace below one row's need, or
- * ws_bytes without a workspace.
+ * dscores or gradients, for w, idx, dscores or a gradient not 4-byte aligned, for another
+ * pair_rows or for a misaligned workspace; IX_ERR_WORKSPACE for a workspace below one row's
+ * need, or ws_bytes without a workspace.
  */
 ix_status ix_indexer_bwd(const ix_indexer_args *a, int32_t k, const int32_t *idx,
-                         const float *dscores, float *dq_I, float *dw, float *dk_I, void *ws,
-                         size_t ws_bytes, hipStream_t stream);
+                         const float *dscores, float *dq_I, float *dw, float *dk_I,
+                         int32_t pair_rows, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for ix_indexer_bwd's atomic-free form in passes of rows_per_pass query
- * rows (clamped to B * T): per-key offsets and cursors (B * S_max + 1 each), the inverted
- * selection (4 bytes per pair) and the pairs' bf16 dk_I rows (2 d_I bytes per pair).
- * 0 on invalid arguments. */
-size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t rows_per_pass);
+ * rows (clamped to B * T) with dk_I rows of precision pair_rows: per-key offsets and cursors
+ * (B * S_max + 1 each), the inverted selection (4 bytes per pair) and the pairs' dk_I rows
+ * (2 d_I bytes per pair in bf16, 4 d_I in fp32).  0 on invalid arguments. */
+size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args *a, int32_t k, int32_t rows_per_pass,
+                                      int32_t pair_rows);
 
 /* Workspace bytes sparse_attn_group_fwd needs for n_layers layers (0 on invalid arguments;
  * may be 0): the split partials of the layers that share one launch. */

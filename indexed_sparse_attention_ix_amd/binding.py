@@ -22,8 +22,9 @@ from typing import Optional, Sequence
 LIB_PATH = os.environ.get("IX_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                     "libix.so")
 
-ABI_VERSION = 4  # IX_ABI_VERSION of include/ix.h
+ABI_VERSION = 5  # IX_ABI_VERSION of include/ix.h
 IX_OK, IX_ERR_INVALID, IX_ERR_UNSUPPORTED, IX_ERR_WORKSPACE, IX_ERR_HIP = 0, -1, -2, -3, -4
+PAIR_ROWS_BF16, PAIR_ROWS_FP32 = 0, 1  # ix_pair_rows of include/ix.h
 STATUS_NAMES = {0: "IX_OK", -1: "IX_ERR_INVALID", -2: "IX_ERR_UNSUPPORTED",
                 -3: "IX_ERR_WORKSPACE", -4: "IX_ERR_HIP"}
 
@@ -97,18 +98,19 @@ def load(path: str = LIB_PATH):
                                                P(c_void_p), c_int32, c_int32, c_int32, c_float,
                                                c_void_p, c_void_p]
     L.sparse_attn_bwd.restype = c_int32
-    L.sparse_attn_bwd.argtypes = ([c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 4 +
-                                  [c_size_t, c_void_p])
+    L.sparse_attn_bwd.argtypes = ([c_void_p] * 8 + [c_int32] * 7 + [c_float] + [c_void_p] * 3 +
+                                  [c_int32, c_void_p, c_size_t, c_void_p])
     L.indexshare_group_bwd.restype = c_int32
     L.indexshare_group_bwd.argtypes = ([c_void_p, c_void_p, c_int32] + [P(c_void_p)] * 6 +
                                        [c_int32] * 7 + [c_float] + [P(c_void_p)] * 3 +
-                                       [c_void_p, c_size_t, c_void_p])
+                                       [c_int32, c_void_p, c_size_t, c_void_p])
     L.sparse_attn_bwd_workspace_bytes.restype = c_size_t
-    L.sparse_attn_bwd_workspace_bytes.argtypes = [c_int32] * 7
+    L.sparse_attn_bwd_workspace_bytes.argtypes = [c_int32] * 8
     L.ix_indexer_bwd.restype = c_int32
-    L.ix_indexer_bwd.argtypes = [P(IndexerArgs), c_int32] + [c_void_p] * 6 + [c_size_t, c_void_p]
+    L.ix_indexer_bwd.argtypes = ([P(IndexerArgs), c_int32] + [c_void_p] * 5 +
+                                 [c_int32, c_void_p, c_size_t, c_void_p])
     L.ix_indexer_bwd_workspace_bytes.restype = c_size_t
-    L.ix_indexer_bwd_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32]
+    L.ix_indexer_bwd_workspace_bytes.argtypes = [P(IndexerArgs), c_int32, c_int32, c_int32]
     L.ix_indexer_kl.restype = c_int32
     L.ix_indexer_kl.argtypes = [c_void_p] * 6 + [c_int32] * 7 + [c_float] + [c_void_p] * 3
     L.ix_pool_keys.restype = c_int32
@@ -240,13 +242,14 @@ def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I
 
 
 def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_kv, d, k,
-                    sm_scale, dq, dkc, dvc, ws=0, ws_bytes=0, stream=0):
+                    sm_scale, dq, dkc, dvc, pair_rows=0, ws=0, ws_bytes=0, stream=0):
     _check(load().sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q,
-                                  H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes, stream))
+                                  H_kv, d, k, sm_scale, dq, dkc, dvc, pair_rows, ws, ws_bytes,
+                                  stream))
 
 
 def indexshare_group_bwd(idx, kv_len, n_layers, q, kc, vc, out, lse, dout, B, T, S_max, H_q,
-                         H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes, stream=0):
+                         H_kv, d, k, sm_scale, dq, dkc, dvc, pair_rows, ws, ws_bytes, stream=0):
     keep = []
     conv = []
     for ptrs in (q, kc, vc, out, lse, dout, dq, dkc, dvc):
@@ -255,11 +258,13 @@ def indexshare_group_bwd(idx, kv_len, n_layers, q, kc, vc, out, lse, dout, B, T,
         if r is not None:
             keep.append(r[1])
     _check(load().indexshare_group_bwd(idx, kv_len, n_layers, *conv[:6], B, T, S_max, H_q, H_kv,
-                                       d, k, sm_scale, *conv[6:], ws, ws_bytes, stream))
+                                       d, k, sm_scale, *conv[6:], pair_rows, ws, ws_bytes,
+                                       stream))
 
 
-def sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass):
-    return load().sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass)
+def sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass, pair_rows=0):
+    return load().sparse_attn_bwd_workspace_bytes(B, T, S_max, H_kv, d, k, rows_per_pass,
+                                                  pair_rows)
 
 
 
@@ -456,11 +461,12 @@ def topk_pooled(q_I, k_pooled, w, q_pos0, kv_len, S_max, pool, k_blocks, ws=None
 
 
 def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=None,
-                              rows_per_pass=None):
+                              rows_per_pass=None, pair_rows=PAIR_ROWS_BF16):
     """(dq fp32 [B,T,H_q,d], dK fp32 [B,S,H_kv,d], dV fp32 [B,S,H_kv,d]) of
     sparse_attention(q, K, V, idx) for the given dout (out, lse: its forward outputs).
     rows_per_pass: None adds dK / dV with atomics; a row count takes the atomic-free form
-    with a workspace for passes of that many query rows."""
+    with a workspace for passes of that many query rows, its pair rows in the precision
+    pair_rows names (PAIR_ROWS_BF16 or PAIR_ROWS_FP32)."""
     torch = _torch()
     B, T, H_q, d = q.shape
     S, H_kv = K.shape[1], K.shape[2]
@@ -472,19 +478,20 @@ def sparse_attention_backward(q, K, V, idx, out, lse, dout, sm_scale, kv_len=Non
     dV = torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q.device)
     ws, nb = None, 0
     if rows_per_pass is not None:
-        nb = sparse_attn_bwd_workspace_bytes(B, T, S, H_kv, d, k, rows_per_pass)
+        nb = sparse_attn_bwd_workspace_bytes(B, T, S, H_kv, d, k, rows_per_pass, pair_rows)
         ws = workspace(nb, q.device)
     sparse_attn_bwd(_ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(kv_len), _ptr(out), _ptr(lse),
                     _ptr(dout), B, T, S, H_q, H_kv, d, k, float(sm_scale), _ptr(dq), _ptr(dK),
-                    _ptr(dV), _ptr(ws) if ws is not None else 0, nb, _stream())
+                    _ptr(dV), pair_rows, _ptr(ws) if ws is not None else 0, nb, _stream())
     return dq, dK, dV
 
 
-def group_attention_backward(idx, layers, sm_scale, kv_len=None, rows_per_pass=None):
+def group_attention_backward(idx, layers, sm_scale, kv_len=None, rows_per_pass=None,
+                             pair_rows=PAIR_ROWS_BF16):
     """The attention backward of every layer of an IndexShare group over the shared idx,
     atomic-free with the selection inverted once per pass.  layers: list of dicts with q, K,
     V, out, lse, dout device tensors.  Returns [(dq, dK, dV) per layer].  rows_per_pass:
-    None takes all rows in one pass."""
+    None takes all rows in one pass; pair_rows: the precision of the pair rows."""
     torch = _torch()
     q0 = layers[0]["q"]
     B, T, H_q, d = q0.shape
@@ -493,31 +500,35 @@ def group_attention_backward(idx, layers, sm_scale, kv_len=None, rows_per_pass=N
     grads = [(torch.empty((B, T, H_q, d), dtype=torch.float32, device=q0.device),
               torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q0.device),
               torch.zeros((B, S, H_kv, d), dtype=torch.float32, device=q0.device)) for _ in layers]
-    nb = sparse_attn_bwd_workspace_bytes(B, T, S, H_kv, d, k, rows_per_pass or B * T)
+    nb = sparse_attn_bwd_workspace_bytes(B, T, S, H_kv, d, k, rows_per_pass or B * T, pair_rows)
     ws = workspace(nb, q0.device)
     names = ("q", "K", "V", "out", "lse", "dout")
     ptrs = [[_ptr(L[n]) for L in layers] for n in names]
     indexshare_group_bwd(_ptr(idx), _ptr(kv_len), len(layers), *ptrs, B, T, S, H_q, H_kv, d, k,
                          float(sm_scale), [_ptr(g[0]) for g in grads], [_ptr(g[1]) for g in grads],
-                         [_ptr(g[2]) for g in grads], _ptr(ws), nb, _stream())
+                         [_ptr(g[2]) for g in grads], pair_rows, _ptr(ws), nb, _stream())
     return grads
 
 
 def ix_indexer_bwd(args: IndexerArgs, k: int, idx: int, dscores: int, dq_I: int, dw: int,
-                   dk_I: int, ws: int = 0, ws_bytes: int = 0, stream: int = 0):
-    _check(load().ix_indexer_bwd(ctypes.byref(args), k, idx, dscores, dq_I, dw, dk_I, ws,
-                                 ws_bytes, stream))
+                   dk_I: int, pair_rows: int = 0, ws: int = 0, ws_bytes: int = 0,
+                   stream: int = 0):
+    _check(load().ix_indexer_bwd(ctypes.byref(args), k, idx, dscores, dq_I, dw, dk_I, pair_rows,
+                                 ws, ws_bytes, stream))
 
 
-def ix_indexer_bwd_workspace_bytes(args: IndexerArgs, k: int, rows_per_pass: int) -> int:
-    return load().ix_indexer_bwd_workspace_bytes(ctypes.byref(args), k, rows_per_pass)
+def ix_indexer_bwd_workspace_bytes(args: IndexerArgs, k: int, rows_per_pass: int,
+                                   pair_rows: int = 0) -> int:
+    return load().ix_indexer_bwd_workspace_bytes(ctypes.byref(args), k, rows_per_pass, pair_rows)
 
 
-def indexer_bwd(args: IndexerArgs, idx, dscores, device, rows_per_pass=None):
+def indexer_bwd(args: IndexerArgs, idx, dscores, device, rows_per_pass=None,
+                pair_rows=PAIR_ROWS_BF16):
     """(dq_I fp32 [B,T,H_I,d_I], dw fp32 [B,T,H_I], dk_I fp32 [B,S_max,d_I]): the indexer
     inputs' gradients from d loss / d sel_scores (dk_I starts from zero here).
     rows_per_pass: None adds dk_I with atomics; a row count takes the atomic-free form
-    with a workspace for passes of that many query rows."""
+    with a workspace for passes of that many query rows, its dk_I rows in the precision
+    pair_rows names."""
     torch = _torch()
     for t in (idx, dscores):
         assert t.is_contiguous(), "indexer backward tensors must be contiguous"
@@ -528,10 +539,10 @@ def indexer_bwd(args: IndexerArgs, idx, dscores, device, rows_per_pass=None):
     dk = torch.zeros((B, S, D), dtype=torch.float32, device=device)
     ws, nb = None, 0
     if rows_per_pass is not None:
-        nb = ix_indexer_bwd_workspace_bytes(args, idx.shape[2], rows_per_pass)
+        nb = ix_indexer_bwd_workspace_bytes(args, idx.shape[2], rows_per_pass, pair_rows)
         ws = workspace(nb, device)
     ix_indexer_bwd(args, idx.shape[2], _ptr(idx), _ptr(dscores), _ptr(dq), _ptr(dw), _ptr(dk),
-                   _ptr(ws), nb, _stream())
+                   pair_rows, _ptr(ws), nb, _stream())
     return dq, dw, dk
 
 

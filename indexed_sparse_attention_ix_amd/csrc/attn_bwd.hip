@@ -30,7 +30,7 @@ struct AttnBwdArgs {
   float* dkc;
   float* dvc;
   int64_t row0;       // first query row (b * T + t) of this launch
-  uint16_t* contrib;  // non-null: per-pair dV | dK rows (bf16) instead of atomics
+  void* contrib;      // non-null: per-pair dV | dK rows instead of atomics
 };
 
 // bf16 16x16x16: D += A(16x16) * B(16x16); lane l supplies A[l & 15][4(l>>4) .. +3] and
@@ -59,7 +59,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
 //    (heads x d), giving dV and dK rows that are added to the fp32 gradient caches with
 //    float atomics (the same key is selected by many queries).
 // The four waves' dq^T partials are summed through LDS.
-template <int D>
+// F32ROWS: the pair rows (p.contrib, required) in fp32; otherwise in bf16, or atomics
+// without p.contrib.
+template <int D, bool F32ROWS = false>
 __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdArgs p) {
   constexpr int MC = D / 32;
   constexpr int NT = D / 16;
@@ -272,8 +274,45 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
     lds_wait();
 
     // dV += P^T dO and dK += (sm_scale dS)^T Q, row by row into the gradient caches, or
-    // (with a pair buffer) each selected pair's dV | dK rows in bf16, staged in the K / V
-    // stage (no longer read in this chunk) and written in pair order
+    // (with a pair buffer) each selected pair's dV | dK rows in bf16 or fp32, staged in the
+    // K / V stage (no longer read in this chunk) and written in pair order
+    if constexpr (F32ROWS) {
+      // fp32: the dV rows, then the dK rows, each a [pair][D] tile filling the stage.  The
+      // 16-byte pieces of a row are swizzled by the pair's lane group (pair bits 2..3), so
+      // the four lane groups' writes of one instruction fall in different banks.
+      float* cf = reinterpret_cast<float*>(stage_all[wid][0]);
+      static_assert(kChunk * D * 4 <= 2 * kChunk * ROWB, "fp32 pair staging");
+      constexpr int kPieces = D / 4;  // 16-byte pieces of one pair's dV (or dK) row
+      float* dst0 = reinterpret_cast<float*>(p.contrib) +
+                    ((size_t)(row - p.row0) * p.k * p.H_kv + kvh) * 2 * D;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)((half ? pts : ptp) + pt_r + 16 * tt));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 v = mfma_bf16_16x16x16(a, half ? qB[nt] : doB[nt], z);
+            const int piece = (4 * nt + (r16 >> 2)) ^ (4 * lg);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cf[(16 * tt + 4 * lg + i) * D + 4 * piece + (r16 & 3)] = v[i];
+          }
+        }
+        lds_wait();
+        for (int q2 = lane; q2 < kChunk * kPieces; q2 += kWave) {
+          const int e = q2 / kPieces, pc = q2 % kPieces;
+          const int ent = c * kChunk + e;
+          if (ent < p.k) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(cf + e * D + 4 * (pc ^ (4 * ((e >> 2) & 3))));
+            *reinterpret_cast<f32x4*>(dst0 + (size_t)ent * p.H_kv * 2 * D + half * D + 4 * pc) = v;
+          }
+        }
+        lds_wait();
+      }
+      continue;
+    }
     if (p.contrib) {
       uint16_t* cb = reinterpret_cast<uint16_t*>(stage_all[wid][0]);
       static_assert(kChunk * 4 * D <= 2 * kChunk * ROWB, "pair staging");
@@ -298,7 +337,8 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
       }
       lds_wait();
       constexpr int kPieces = 4 * D / 16;  // 16-byte pieces of one pair's dV | dK rows
-      uint16_t* dst0 = p.contrib + ((size_t)(row - p.row0) * p.k * p.H_kv + kvh) * 2 * D;
+      uint16_t* dst0 = reinterpret_cast<uint16_t*>(p.contrib) +
+                       ((size_t)(row - p.row0) * p.k * p.H_kv + kvh) * 2 * D;
       for (int q2 = lane; q2 < kChunk * kPieces; q2 += kWave) {
         const int e = q2 / kPieces, pc = q2 % kPieces;
         const int ent = c * kChunk + e;
@@ -603,8 +643,8 @@ hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, con
                                          const float* const* lse, const void* const* dout, int B,
                                          int T, int S_max, int H_q, int H_kv, int d, int k,
                                          float sm_scale, float* const* dq, float* const* dkc,
-                                         float* const* dvc, void* ws, size_t ws_bytes,
-                                         hipStream_t stream) {
+                                         float* const* dvc, bool f32_rows, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
   auto args = [&](int l) {
     AttnBwdArgs x{};
     x.q = reinterpret_cast<const uint16_t*>(q[l]);
@@ -630,12 +670,13 @@ hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, con
     x.dvc = dvc[l];
     return x;
   };
-  auto grad = [&](const AttnBwdArgs& x, int64_t rows) {
+  auto grad = [&](const AttnBwdArgs& x, int64_t rows, bool f32) {
     const dim3 grid((unsigned)(rows * H_kv));
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kAttnBlock), 0, stream, x); };
     if (d == 128)
-      hipLaunchKernelGGL(sparse_attn_bwd_kernel<128>, grid, dim3(kAttnBlock), 0, stream, x);
+      f32 ? go(sparse_attn_bwd_kernel<128, true>) : go(sparse_attn_bwd_kernel<128>);
     else
-      hipLaunchKernelGGL(sparse_attn_bwd_kernel<64>, grid, dim3(kAttnBlock), 0, stream, x);
+      f32 ? go(sparse_attn_bwd_kernel<64, true>) : go(sparse_attn_bwd_kernel<64>);
   };
   const int64_t all = (int64_t)B * T;
   if (!ws) {
@@ -643,17 +684,17 @@ hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, con
       AttnBwdArgs x = args(l);
       x.row0 = 0;
       x.contrib = nullptr;
-      grad(x, all);
+      grad(x, all, false);
     }
     return hipGetLastError();
   }
   // atomic-free: per pass, the inverted selection, then per layer the pair rows [dV | dK]
-  // in bf16 and their key sums
-  const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
+  // (bf16 or fp32) and their key sums
+  const size_t row_bytes = (size_t)H_kv * 2 * d * (f32_rows ? 4 : 2);
   const int64_t per_pass = pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes);
   if (per_pass < 1) return hipErrorInvalidValue;
   const PairLayout L = pair_layout(B, S_max, k, per_pass, row_bytes);
-  uint16_t* contrib = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.contrib);
+  void* contrib = reinterpret_cast<char*>(ws) + L.contrib;
   for (int64_t r0 = 0; r0 < all; r0 += per_pass) {
     const int64_t rows = std::min(per_pass, all - r0);
     hipError_t e = launch_pair_index(idx, kv_len, T, S_max, k, r0, rows, L, ws, stream);
@@ -662,8 +703,8 @@ hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, con
       AttnBwdArgs x = args(l);
       x.row0 = r0;
       x.contrib = contrib;
-      grad(x, rows);
-      e = launch_pair_reduce(L, ws, 2 * d, H_kv, dvc[l], dkc[l], d, stream);
+      grad(x, rows, f32_rows);
+      e = launch_pair_reduce(L, ws, 2 * d, f32_rows, H_kv, dvc[l], dkc[l], d, stream);
       if (e != hipSuccess) return e;
     }
   }
@@ -674,10 +715,10 @@ hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,
                                   int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
-                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+                                  bool f32_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
   return launch_sparse_attn_bwd_layers(1, &q, &kc, &vc, idx, kv_len, &out, &lse, &dout, B, T, S_max,
-                                       H_q, H_kv, d, k, sm_scale, &dq, &dkc, &dvc, ws, ws_bytes,
-                                       stream);
+                                       H_q, H_kv, d, k, sm_scale, &dq, &dkc, &dvc, f32_rows, ws,
+                                       ws_bytes, stream);
 }
 
 hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,

@@ -115,13 +115,14 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ __bf16 bf16_hi(float v) { return (__bf16)v; }
 __device__ __forceinline__ __bf16 bf16_lo(float v, __bf16 hi) { return (__bf16)(v - (float)hi); }
 
-// STORE: write each kept pair's dk_I row in bf16 to `contrib` instead of adding it to dk.
-template <int DI, bool STORE>
+// STORE: write each kept pair's dk_I row to `contrib` (bf16, or fp32 with F32ROWS) instead
+// of adding it to dk.
+template <int DI, bool STORE, bool F32ROWS = false>
 __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ kI, const float* __restrict__ w,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ idx,
     const float* __restrict__ dsc, int T, int S_max, int H, int k, float* __restrict__ dq,
-    float* __restrict__ dw, float* __restrict__ dk, int64_t row0, uint16_t* __restrict__ contrib) {
+    float* __restrict__ dw, float* __restrict__ dk, int64_t row0, void* __restrict__ contrib) {
   __shared__ BwdSmem<DI> sm;
   constexpr int kPieces = DI / 16;   // 16-byte pieces per row
   constexpr int kDimTiles = DI / 16;
@@ -322,9 +323,21 @@ __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_ker
     }
     __syncthreads();
 
-    // ---- with a pair buffer: the chunk's rows in bf16, in pair order (summed per key later)
+    // ---- with a pair buffer: the chunk's rows in bf16 or fp32, in pair order (summed per
+    // key later)
     if constexpr (STORE) {
-      uint16_t* dst0 = contrib + ((size_t)(row - row0) * k + j0) * DI;
+      if constexpr (F32ROWS) {
+        float* dst0 = reinterpret_cast<float*>(contrib) + ((size_t)(row - row0) * k + j0) * DI;
+        for (int r = 8 * wv; r < 8 * wv + 8; ++r) {
+          if (j0 + r >= k) break;
+          if (2 * lane < DI)
+            *reinterpret_cast<float2*>(dst0 + (size_t)r * DI + 2 * lane) =
+                make_float2(sm.dk[r][2 * lane], sm.dk[r][2 * lane + 1]);
+        }
+        __syncthreads();
+        continue;
+      }
+      uint16_t* dst0 = reinterpret_cast<uint16_t*>(contrib) + ((size_t)(row - row0) * k + j0) * DI;
       for (int r = 8 * wv; r < 8 * wv + 8; ++r) {
         if (j0 + r >= k) break;
         if (2 * lane < DI) {
@@ -366,35 +379,41 @@ __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_ker
 hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float* w,
                               const int32_t* kv_len, const int32_t* idx, const float* dscores,
                               int B, int T, int S_max, int H_I, int d_I, int k, float* dq,
-                              float* dw, float* dk, void* ws, size_t ws_bytes, hipStream_t stream) {
-  auto grad = [&](int64_t row0, int64_t rows, uint16_t* contrib) {
+                              float* dw, float* dk, bool f32_rows, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  auto grad = [&](int64_t row0, int64_t rows, void* contrib) {
     const dim3 grid((unsigned)rows), block(kBwdThreads);
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, block, 0, stream, qI, kI, w, kv_len, idx, dscores, T, S_max,
                          H_I, k, dq, dw, dk, row0, contrib);
     };
-    if (d_I == 128)
-      contrib ? go(indexer_bwd_kernel<128, true>) : go(indexer_bwd_kernel<128, false>);
-    else
-      contrib ? go(indexer_bwd_kernel<64, true>) : go(indexer_bwd_kernel<64, false>);
+    if (d_I == 128) {
+      if (!contrib) go(indexer_bwd_kernel<128, false>);
+      else if (f32_rows) go(indexer_bwd_kernel<128, true, true>);
+      else go(indexer_bwd_kernel<128, true>);
+    } else {
+      if (!contrib) go(indexer_bwd_kernel<64, false>);
+      else if (f32_rows) go(indexer_bwd_kernel<64, true, true>);
+      else go(indexer_bwd_kernel<64, true>);
+    }
   };
   const int64_t all = (int64_t)B * T;
   if (!ws) {
     grad(0, all, nullptr);
     return hipGetLastError();
   }
-  // atomic-free: per pass, the inverted selection, pair rows of dk_I in bf16, key sums
-  const size_t row_bytes = (size_t)d_I * 2;
+  // atomic-free: per pass, the inverted selection, pair rows of dk_I (bf16 or fp32), key sums
+  const size_t row_bytes = (size_t)d_I * (f32_rows ? 4 : 2);
   const int64_t per_pass = pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes);
   if (per_pass < 1) return hipErrorInvalidValue;
   const PairLayout L = pair_layout(B, S_max, k, per_pass, row_bytes);
-  uint16_t* contrib = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + L.contrib);
+  void* contrib = reinterpret_cast<char*>(ws) + L.contrib;
   for (int64_t r0 = 0; r0 < all; r0 += per_pass) {
     const int64_t rows = std::min(per_pass, all - r0);
     hipError_t e = launch_pair_index(idx, kv_len, T, S_max, k, r0, rows, L, ws, stream);
     if (e != hipSuccess) return e;
     grad(r0, rows, contrib);
-    e = launch_pair_reduce(L, ws, d_I, 1, dk, dk + d_I / 2, d_I, stream);
+    e = launch_pair_reduce(L, ws, d_I, f32_rows, 1, dk, dk + d_I / 2, d_I, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

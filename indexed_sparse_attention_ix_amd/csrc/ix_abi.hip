@@ -126,6 +126,27 @@ ix_status check_attn_shape(int32_t B, int32_t T, int32_t S_max, int32_t H_q, int
 
 bool pool_ok(int32_t pool) { return pool == 1 || pool == 2 || pool == 4 || pool == 8 || pool == 16; }
 
+bool pair_rows_valid(int32_t pair_rows) {
+  return pair_rows == IX_PAIR_ROWS_BF16 || pair_rows == IX_PAIR_ROWS_FP32;
+}
+
+ix_status check_pair_rows(int32_t pair_rows) {
+  if (!pair_rows_valid(pair_rows))
+    return fail(IX_ERR_INVALID, "pair_rows=%d: IX_PAIR_ROWS_BF16 (0) or IX_PAIR_ROWS_FP32 (1)",
+                pair_rows);
+  return IX_OK;
+}
+
+// Bytes of one kept pair's gradient rows in the atomic-free backward forms: the attention's
+// dV | dK rows (H_kv heads of 2 d) and the indexer's dk_I row (d_I).
+size_t attn_pair_row_bytes(int32_t H_kv, int32_t d, int32_t pair_rows) {
+  return (size_t)H_kv * 2 * d * (pair_rows == IX_PAIR_ROWS_FP32 ? 4 : 2);
+}
+
+size_t indexer_pair_row_bytes(int32_t d_I, int32_t pair_rows) {
+  return (size_t)d_I * (pair_rows == IX_PAIR_ROWS_FP32 ? 4 : 2);
+}
+
 // The indexer arguments as the top-k sees them under IndexPool: one key row per block.
 ix_indexer_args pooled_args(const ix_indexer_args& a, int32_t pool) {
   ix_indexer_args u = a;
@@ -444,23 +465,26 @@ ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_block
 }
 
 size_t sparse_attn_bwd_workspace_bytes(int32_t B, int32_t T, int32_t S_max, int32_t H_kv,
-                                       int32_t d, int32_t k, int32_t rows_per_pass) {
+                                       int32_t d, int32_t k, int32_t rows_per_pass,
+                                       int32_t pair_rows) {
   bool empty = false;
   if (check_attn_shape(B, T, S_max, H_kv, H_kv, d, k, &empty) != IX_OK || empty) return 0;
-  if (rows_per_pass < 1) return 0;
+  if (rows_per_pass < 1 || !pair_rows_valid(pair_rows)) return 0;
   const int64_t rows = std::min<int64_t>(rows_per_pass, (int64_t)B * T);
   if (rows * k > ((int64_t)1 << 31)) return 0;
-  return ix::pair_layout(B, S_max, k, rows, (size_t)H_kv * 2 * d * 2).total;
+  return ix::pair_layout(B, S_max, k, rows, attn_pair_row_bytes(H_kv, d, pair_rows)).total;
 }
 
 ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                           const int32_t* kv_len, const void* out, const float* lse,
                           const void* dout, int32_t B, int32_t T, int32_t S_max, int32_t H_q,
                           int32_t H_kv, int32_t d, int32_t k, float sm_scale, float* dq,
-                          float* dkc, float* dvc, void* ws, size_t ws_bytes, hipStream_t stream) {
+                          float* dkc, float* dvc, int32_t pair_rows, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   bool empty = false;
   ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
   if (st != IX_OK) return st;
+  if ((st = check_pair_rows(pair_rows)) != IX_OK) return st;
   if (empty) return ok();
   if ((st = check_attn_ptrs(q, kc, vc, idx, out)) != IX_OK) return st;
   if (!lse || !dout || !dq || !dkc || !dvc)
@@ -473,7 +497,7 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
   if (ws) {
     if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
-    const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
+    const size_t row_bytes = attn_pair_row_bytes(H_kv, d, pair_rows);
     if (ix::pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes) < 1)
       return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
                   ws_bytes, ix::pair_layout(B, S_max, k, 1, row_bytes).total);
@@ -481,8 +505,8 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
   hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
-                                            H_q, H_kv, d, k, sm_scale, dq, dkc, dvc, ws, ws_bytes,
-                                            stream));
+                                            H_q, H_kv, d, k, sm_scale, dq, dkc, dvc,
+                                            pair_rows == IX_PAIR_ROWS_FP32, ws, ws_bytes, stream));
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_bwd launch");
   return ok();
 }
@@ -492,12 +516,13 @@ ix_status indexshare_group_bwd(const int32_t* idx, const int32_t* kv_len, int32_
                                const void* const* out, const float* const* lse,
                                const void* const* dout, int32_t B, int32_t T, int32_t S_max,
                                int32_t H_q, int32_t H_kv, int32_t d, int32_t k, float sm_scale,
-                               float* const* dq, float* const* dkc, float* const* dvc, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+                               float* const* dq, float* const* dkc, float* const* dvc,
+                               int32_t pair_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
   bool empty = false;
   ix_status st = check_attn_shape(B, T, S_max, H_q, H_kv, d, k, &empty);
   if (st != IX_OK) return st;
   if (n_layers < 1) return fail(IX_ERR_INVALID, "n_layers=%d must be >= 1", n_layers);
+  if ((st = check_pair_rows(pair_rows)) != IX_OK) return st;
   if (empty) return ok();
   if (!q || !kc || !vc || !out || !lse || !dout || !dq || !dkc || !dvc)
     return fail(IX_ERR_INVALID, "NULL per-layer pointer array");
@@ -514,13 +539,14 @@ ix_status indexshare_group_bwd(const int32_t* idx, const int32_t* kv_len, int32_
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
   if (!ws) return fail(IX_ERR_WORKSPACE, "the group backward needs a workspace");
   if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
-  const size_t row_bytes = (size_t)H_kv * 2 * d * 2;
+  const size_t row_bytes = attn_pair_row_bytes(H_kv, d, pair_rows);
   if (ix::pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes) < 1)
     return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
                 ws_bytes, ix::pair_layout(B, S_max, k, 1, row_bytes).total);
   hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_bwd_layers(n_layers, q, kc, vc, idx, kv_len, out, lse, dout,
                                                    B, T, S_max, H_q, H_kv, d, k, sm_scale, dq, dkc,
-                                                   dvc, ws, ws_bytes, stream));
+                                                   dvc, pair_rows == IX_PAIR_ROWS_FP32, ws,
+                                                   ws_bytes, stream));
   if (e != hipSuccess) return hip_fail(e, "indexshare_group_bwd launch");
   return ok();
 }
@@ -545,23 +571,25 @@ ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const
   return ok();
 }
 
-size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args* a, int32_t k, int32_t rows_per_pass) {
+size_t ix_indexer_bwd_workspace_bytes(const ix_indexer_args* a, int32_t k, int32_t rows_per_pass,
+                                      int32_t pair_rows) {
   bool empty = false;
   if (check_indexer(a, &empty) != IX_OK || empty || check_k(k) != IX_OK) return 0;
-  if (rows_per_pass < 1) return 0;
+  if (rows_per_pass < 1 || !pair_rows_valid(pair_rows)) return 0;
   const int64_t rows = std::min<int64_t>(rows_per_pass, (int64_t)a->B * a->T);
   if (rows * k > ((int64_t)1 << 31)) return 0;
-  return ix::pair_layout(a->B, a->S_max, k, rows, (size_t)a->d_I * 2).total;
+  return ix::pair_layout(a->B, a->S_max, k, rows, indexer_pair_row_bytes(a->d_I, pair_rows)).total;
 }
 
 ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx,
-                         const float* dscores, float* dq_I, float* dw, float* dk_I, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+                         const float* dscores, float* dq_I, float* dw, float* dk_I,
+                         int32_t pair_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
   bool empty = false;
   ix_status st = check_indexer(a, &empty);
   if (st != IX_OK) return st;
   st = check_k(k);
   if (st != IX_OK) return st;
+  if ((st = check_pair_rows(pair_rows)) != IX_OK) return st;
   if (empty) return ok();
   if (!idx || !dscores || !dq_I || !dw || !dk_I)
     return fail(IX_ERR_INVALID, "NULL idx, dscores, dq_I, dw or dk_I pointer");
@@ -570,7 +598,7 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
     return fail(IX_ERR_INVALID, "w, idx, dscores and gradient pointers must be 4-byte aligned");
   if (ws) {
     if (!aligned16(ws)) return fail(IX_ERR_INVALID, "workspace must be 16-byte aligned");
-    const size_t row_bytes = (size_t)a->d_I * 2;
+    const size_t row_bytes = indexer_pair_row_bytes(a->d_I, pair_rows);
     if (ix::pair_rows_per_pass(a->B, a->T, a->S_max, k, row_bytes, ws_bytes) < 1)
       return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
                   ws_bytes, ix::pair_layout(a->B, a->S_max, k, 1, row_bytes).total);
@@ -578,8 +606,8 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
   hipError_t e = IX_LAUNCH(ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
-                                        a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I, ws, ws_bytes,
-                                        stream));
+                                        a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I,
+                                        pair_rows == IX_PAIR_ROWS_FP32, ws, ws_bytes, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");
   return ok();
 }

@@ -72,7 +72,7 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
                                      float* const* lse, const AttnPlan& pl, void* ws,
                                      hipStream_t stream);
 // Atomic-free key gradients (pair_reduce.hip): workspace layout for passes of `rows` query
-// rows whose pairs carry row_bytes of bf16 gradient rows each.
+// rows whose pairs carry row_bytes of gradient rows (bf16 or fp32) each.
 struct PairLayout {
   int64_t n_keys, nparts;
   int64_t n_blk, rows_per_blk, n_slots;  // row blocks of the pass; (key, block) counters
@@ -84,23 +84,25 @@ int64_t pair_rows_per_pass(int B, int T, int S_max, int k, size_t row_bytes, siz
 hipError_t launch_pair_index(const int32_t* idx, const int32_t* kv_len, int T, int S_max, int k,
                              int64_t row0, int64_t rows, const PairLayout& L, void* ws,
                              hipStream_t stream);
-// Per-key sums of the pass's pair rows (row_width bf16 per (pair, head), H heads), first
-// half added to dst_a, second half to dst_b, at row (key * H + head) of `stride` floats.
-hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, int H,
-                              float* dst_a, float* dst_b, int64_t stride, hipStream_t stream);
+// Per-key sums of the pass's pair rows (row_width elements per (pair, head), bf16, or fp32
+// with f32_rows; H heads), first half added to dst_a, second half to dst_b, at row
+// (key * H + head) of `stride` floats.
+hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, bool f32_rows,
+                              int H, float* dst_a, float* dst_b, int64_t stride,
+                              hipStream_t stream);
 hipError_t launch_sparse_attn_bwd_layers(int n_layers, const void* const* q, const void* const* kc,
                                          const void* const* vc, const int32_t* idx,
                                          const int32_t* kv_len, const void* const* out,
                                          const float* const* lse, const void* const* dout, int B,
                                          int T, int S_max, int H_q, int H_kv, int d, int k,
                                          float sm_scale, float* const* dq, float* const* dkc,
-                                         float* const* dvc, void* ws, size_t ws_bytes,
-                                         hipStream_t stream);
+                                         float* const* dvc, bool f32_rows, void* ws,
+                                         size_t ws_bytes, hipStream_t stream);
 hipError_t launch_sparse_attn_bwd(const void* q, const void* kc, const void* vc, const int32_t* idx,
                                   const int32_t* kv_len, const void* out, const float* lse,
                                   const void* dout, int B, int T, int S_max, int H_q, int H_kv,
                                   int d, int k, float sm_scale, float* dq, float* dkc, float* dvc,
-                                  void* ws, size_t ws_bytes, hipStream_t stream);
+                                  bool f32_rows, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
                              const int32_t* kv_len, const float* lse, const float* sel_scores,
                              int B, int T, int S_max, int H_q, int H_kv, int d, int k,
@@ -108,7 +110,8 @@ hipError_t launch_indexer_kl(const void* q, const void* kc, const int32_t* idx,
 hipError_t launch_indexer_bwd(const uint8_t* qI, const uint8_t* kI, const float* w,
                               const int32_t* kv_len, const int32_t* idx, const float* dscores,
                               int B, int T, int S_max, int H_I, int d_I, int k, float* dq,
-                              float* dw, float* dk, void* ws, size_t ws_bytes, hipStream_t stream);
+                              float* dw, float* dk, bool f32_rows, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 hipError_t launch_append_kv(const float* k_I_new, const void* K_new, const void* V_new,
                             const int32_t* pos0, int B, int T_new, int S_max, int d_I, int H_kv,
                             int d, uint8_t* k_I_cache, void* K_cache, void* V_cache,

@@ -9,7 +9,8 @@
 //  2. list every pair's position in the pass under its key (the inverted selection): one
 //     workgroup per row block takes its rows in order, so each key's pairs come in row
 //     order and the lists, and the sums below, are the same on every run;
-//  3. the gradient kernel writes each pair's rows (bf16) in pair order;
+//  3. the gradient kernel writes each pair's rows (bf16, or fp32 at the caller's choice) in
+//     pair order;
 //  4. one wave per (key, head) sums its pairs' rows in fp32 and adds the sums to the
 //     gradient rows with ordinary loads and stores (the wave owns those rows).
 // Only entries of one query row that repeat a key take an arrival order among themselves.
@@ -212,13 +213,13 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t v) {
 }
 
 // One wave per (key, head), grid-stride over all of them.  Key g's pairs are
-// inv[off[g] .. off[g + 1]).  A pair's row for head h is W bf16 at contrib + (pair * H
-// + h) * W; lanes 0..31 sum elements [0, W/2) into dst_a, lanes 32..63 elements [W/2, W) into
-// dst_b, EPL consecutive columns each; the sums are added to row (key * H + h) of stride
-// `stride` floats.
-template <int W>
+// inv[off[g] .. off[g + 1]).  A pair's row for head h is W elements (bf16, or fp32 with F32)
+// at contrib + (pair * H + h) * W; lanes 0..31 sum elements [0, W/2) into dst_a, lanes 32..63
+// elements [W/2, W) into dst_b, EPL consecutive columns each; the sums are added to row
+// (key * H + h) of stride `stride` floats.
+template <int W, bool F32>
 __global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, const uint32_t* inv,
-                                                          const uint16_t* contrib, int64_t n_keys,
+                                                          const void* contrib, int64_t n_keys,
                                                           int H, float* dst_a, float* dst_b,
                                                           int64_t stride) {
   constexpr int EPL = W / kWave;
@@ -227,6 +228,8 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, c
   const int part = lane >> 5;
   const int col = (lane & 31) * EPL;
   const int64_t waves = ((int64_t)gridDim.x * 256) >> 6;
+  using Elem = std::conditional_t<F32, float, uint16_t>;
+  const Elem* rows_base = reinterpret_cast<const Elem*>(contrib);
   for (int64_t it = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6; it < n_keys * H; it += waves) {
     const int64_t g = it / H;
     const int h = (int)(it % H);
@@ -235,13 +238,27 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, c
     float acc[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-    // this lane's EPL bf16 of one pair row, and their sum into acc
-    using Raw = std::conditional_t<EPL == 4, uint2, std::conditional_t<EPL == 2, uint32_t, uint16_t>>;
+    // this lane's EPL elements of one pair row, and their sum into acc
+    using Raw = std::conditional_t<
+        F32, std::conditional_t<EPL == 4, float4, std::conditional_t<EPL == 2, float2, float>>,
+        std::conditional_t<EPL == 4, uint2, std::conditional_t<EPL == 2, uint32_t, uint16_t>>>;
     auto load_pair = [&](uint32_t pr) -> Raw {
-      return *reinterpret_cast<const Raw*>(contrib + ((size_t)pr * H + h) * W + part * (W / 2) + col);
+      return *reinterpret_cast<const Raw*>(rows_base + ((size_t)pr * H + h) * W + part * (W / 2) + col);
     };
     auto add_raw = [&](Raw v) {
-      if constexpr (EPL == 4) {
+      if constexpr (F32) {
+        if constexpr (EPL == 4) {
+          acc[0] += v.x;
+          acc[1] += v.y;
+          acc[2] += v.z;
+          acc[3] += v.w;
+        } else if constexpr (EPL == 2) {
+          acc[0] += v.x;
+          acc[1] += v.y;
+        } else {
+          acc[0] += v;
+        }
+      } else if constexpr (EPL == 4) {
         acc[0] += bf16_bits_to_f32(v.x & 0xFFFFu);
         acc[1] += bf16_bits_to_f32(v.x >> 16);
         acc[2] += bf16_bits_to_f32(v.y & 0xFFFFu);
@@ -358,27 +375,23 @@ hipError_t launch_pair_index(const int32_t* idx, const int32_t* kv_len, int T, i
   return hipGetLastError();
 }
 
-hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, int H,
-                              float* dst_a, float* dst_b, int64_t stride, hipStream_t stream) {
+hipError_t launch_pair_reduce(const PairLayout& L, const void* ws, int row_width, bool f32_rows,
+                              int H, float* dst_a, float* dst_b, int64_t stride,
+                              hipStream_t stream) {
   const char* w = reinterpret_cast<const char*>(ws);
   const uint32_t* off = reinterpret_cast<const uint32_t*>(w + L.off);
   const uint32_t* inv = reinterpret_cast<const uint32_t*>(w + L.inv);
-  const uint16_t* contrib = reinterpret_cast<const uint16_t*>(w + L.contrib);
+  const void* contrib = w + L.contrib;
   const int64_t items = L.n_keys * H;
   const dim3 grid((unsigned)std::min<int64_t>((items + 3) / 4, 65536));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, off, inv, contrib, L.n_keys, H, dst_a,
+                       dst_b, stride);
+  };
   switch (row_width) {
-    case 256:
-      hipLaunchKernelGGL(pair_reduce_kernel<256>, grid, dim3(256), 0, stream, off, inv, contrib,
-                         L.n_keys, H, dst_a, dst_b, stride);
-      break;
-    case 128:
-      hipLaunchKernelGGL(pair_reduce_kernel<128>, grid, dim3(256), 0, stream, off, inv, contrib,
-                         L.n_keys, H, dst_a, dst_b, stride);
-      break;
-    case 64:
-      hipLaunchKernelGGL(pair_reduce_kernel<64>, grid, dim3(256), 0, stream, off, inv, contrib,
-                         L.n_keys, H, dst_a, dst_b, stride);
-      break;
+    case 256: f32_rows ? go(pair_reduce_kernel<256, true>) : go(pair_reduce_kernel<256, false>); break;
+    case 128: f32_rows ? go(pair_reduce_kernel<128, true>) : go(pair_reduce_kernel<128, false>); break;
+    case 64: f32_rows ? go(pair_reduce_kernel<64, true>) : go(pair_reduce_kernel<64, false>); break;
     default:
       return hipErrorInvalidValue;
   }

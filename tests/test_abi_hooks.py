@@ -58,14 +58,15 @@ def _calls():
         ("ix_topk_pooled", lambda: L.ix_topk_pooled(ctypes.byref(a), 4, 16, FAKE, FAKE, ws_p, None)),
         ("sparse_attn_bwd", lambda: L.sparse_attn_bwd(
             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 256, 16, 1, 128, 64, sc, FAKE,
-            FAKE, FAKE, None, 0, None)),
+            FAKE, FAKE, bd.PAIR_ROWS_BF16, None, 0, None)),
         ("indexshare_group_bwd", lambda: L.indexshare_group_bwd(
-            FAKE, FAKE, 4, pa, pa, pa, pa, fa, pa, 2, 16, 256, 16, 1, 128, 64, sc, fa, fa, fa, FAKE,
-            bd.sparse_attn_bwd_workspace_bytes(2, 16, 256, 1, 128, 64, 32), None)),
+            FAKE, FAKE, 4, pa, pa, pa, pa, fa, pa, 2, 16, 256, 16, 1, 128, 64, sc, fa, fa, fa,
+            bd.PAIR_ROWS_FP32, FAKE,
+            bd.sparse_attn_bwd_workspace_bytes(2, 16, 256, 1, 128, 64, 32, bd.PAIR_ROWS_FP32), None)),
         ("ix_indexer_kl", lambda: L.ix_indexer_kl(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 256, 16,
                                                   1, 128, 64, sc, FAKE, FAKE, None)),
         ("ix_indexer_bwd", lambda: L.ix_indexer_bwd(ctypes.byref(a), 64, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                                    None, 0, None)),
+                                                    bd.PAIR_ROWS_BF16, None, 0, None)),
     ]
 
 

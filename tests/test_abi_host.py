@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_clean_error():
-    assert bd.ix_abi_version() == bd.ABI_VERSION == 4
+    assert bd.ix_abi_version() == bd.ABI_VERSION == 5
 
 
 FAKE = 1 << 20  # 16-byte aligned non-null stand-in address; never dereferenced on failure
@@ -247,14 +247,15 @@ def test_indexer_kl_validation_codes():
 
 def test_attention_bwd_validation_codes():
     ok = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, kvl=FAKE, out=FAKE, lse=FAKE, dout=FAKE, B=2,
-              T=3, S=64, H_q=16, H_kv=1, d=128, k=16, scale=0.1, dq=FAKE, dk=FAKE, dv=FAKE)
+              T=3, S=64, H_q=16, H_kv=1, d=128, k=16, scale=0.1, dq=FAKE, dk=FAKE, dv=FAKE,
+              pr=bd.PAIR_ROWS_BF16)
 
     def call(**kw):
         a = dict(ok)
         a.update(kw)
         return status_of(bd.sparse_attn_bwd, a["q"], a["kc"], a["vc"], a["idx"], a["kvl"], a["out"],
                          a["lse"], a["dout"], a["B"], a["T"], a["S"], a["H_q"], a["H_kv"], a["d"],
-                         a["k"], a["scale"], a["dq"], a["dk"], a["dv"])
+                         a["k"], a["scale"], a["dq"], a["dk"], a["dv"], a["pr"])
 
     for name in ("q", "kc", "vc", "idx", "out", "lse", "dout", "dq", "dk", "dv"):
         assert call(**{name: 0}) == bd.IX_ERR_INVALID, name
@@ -266,9 +267,14 @@ def test_attention_bwd_validation_codes():
     assert call(k=0) == bd.IX_ERR_UNSUPPORTED and call(d=96) == bd.IX_ERR_UNSUPPORTED
     assert call(H_q=12, H_kv=8) == bd.IX_ERR_UNSUPPORTED
     assert call(B=0, q=0, kc=0, vc=0, idx=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0) == bd.IX_OK
+    # the pair-row precision is checked with or without a workspace
+    for bad in (-1, 2):
+        assert call(pr=bad) == bd.IX_ERR_INVALID
+        assert "pair_rows" in bd.ix_last_error()
     # the atomic-free form's workspace
-    a = [ok[n] for n in ("q", "kc", "vc", "idx", "kvl", "out", "lse", "dout", "B", "T", "S", "H_q",
-                         "H_kv", "d", "k", "scale", "dq", "dk", "dv")]
+    names = ("q", "kc", "vc", "idx", "kvl", "out", "lse", "dout", "B", "T", "S", "H_q", "H_kv", "d",
+             "k", "scale", "dq", "dk", "dv", "pr")
+    a = [ok[n] for n in names]
     one = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 1)
     six = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 6)
     assert 0 < one < six
@@ -278,6 +284,13 @@ def test_attention_bwd_validation_codes():
     assert status_of(bd.sparse_attn_bwd, *a, FAKE, one - 1) == bd.IX_ERR_WORKSPACE
     assert status_of(bd.sparse_attn_bwd, *a, 0, one) == bd.IX_ERR_WORKSPACE
     assert status_of(bd.sparse_attn_bwd, *a, FAKE + 8, one) == bd.IX_ERR_INVALID
+    # fp32 pair rows: 1024 instead of 512 bytes per pair at d = 128 (6 rows of 16 pairs)
+    one32 = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 1, bd.PAIR_ROWS_FP32)
+    six32 = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 6, bd.PAIR_ROWS_FP32)
+    assert six32 - six >= 6 * 16 * 512 and one32 > one
+    assert bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 1, 2) == 0
+    a32 = [dict(ok, pr=bd.PAIR_ROWS_FP32)[n] for n in names]
+    assert status_of(bd.sparse_attn_bwd, *a32, FAKE, one) == bd.IX_ERR_WORKSPACE
 
 
 def test_group_bwd_validation_codes():
@@ -287,12 +300,12 @@ def test_group_bwd_validation_codes():
               S=64, H_q=16, H_kv=1, d=128, k=16, scale=0.1, dq=arr, dk=arr, dv=arr)
     one = bd.sparse_attn_bwd_workspace_bytes(2, 3, 64, 1, 128, 16, 1)
 
-    def call(ws=FAKE, nb=one, **kw):
+    def call(ws=FAKE, nb=one, pr=bd.PAIR_ROWS_BF16, **kw):
         a = dict(ok)
         a.update(kw)
         return status_of(bd.indexshare_group_bwd, a["idx"], a["kvl"], a["n"], a["q"], a["kc"], a["vc"],
                          a["out"], a["lse"], a["dout"], a["B"], a["T"], a["S"], a["H_q"], a["H_kv"],
-                         a["d"], a["k"], a["scale"], a["dq"], a["dk"], a["dv"], ws, nb)
+                         a["d"], a["k"], a["scale"], a["dq"], a["dk"], a["dv"], pr, ws, nb)
 
     assert call(n=0) == bd.IX_ERR_INVALID
     for name in ("q", "kc", "vc", "out", "lse", "dout", "dq", "dk", "dv"):
@@ -304,6 +317,8 @@ def test_group_bwd_validation_codes():
     assert call(nb=one - 1) == bd.IX_ERR_WORKSPACE
     assert call(ws=FAKE + 8) == bd.IX_ERR_INVALID
     assert call(d=96) == bd.IX_ERR_UNSUPPORTED
+    assert call(pr=3) == bd.IX_ERR_INVALID
+    assert call(pr=bd.PAIR_ROWS_FP32) == bd.IX_ERR_WORKSPACE    # a bf16-sized workspace
     assert call(B=0, ws=0, nb=0) == bd.IX_OK
 
 
@@ -322,7 +337,9 @@ def test_indexer_bwd_validation_codes():
     assert call(a=args(d_I=96)) == bd.IX_ERR_UNSUPPORTED
     assert call(a=args(H_I=6)) == bd.IX_ERR_UNSUPPORTED
     assert call(k=0) == bd.IX_ERR_UNSUPPORTED and call(k=4096) == bd.IX_ERR_UNSUPPORTED
-    assert bd.load().ix_indexer_bwd(None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == bd.IX_ERR_INVALID
+    assert bd.load().ix_indexer_bwd(None, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 0, None) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_indexer_bwd, args(), 16, FAKE, FAKE, FAKE, FAKE, FAKE, 2) == bd.IX_ERR_INVALID
+    assert "pair_rows" in bd.ix_last_error()
     # empty calls launch nothing
     assert call(a=args(B=0, q=0, k=0, w=0, q_pos0=0, kv_len=0), idx=0, ds=0, dq=0, dw=0, dk=0) == bd.IX_OK
     # the atomic-free form's workspace
@@ -331,10 +348,16 @@ def test_indexer_bwd_validation_codes():
     assert bd.ix_indexer_bwd_workspace_bytes(args(), 16, 10 ** 6) == \
         bd.ix_indexer_bwd_workspace_bytes(args(), 16, 128)                      # clamped to B*T
     assert bd.ix_indexer_bwd_workspace_bytes(args(d_I=96), 16, 1) == 0
+    assert bd.ix_indexer_bwd_workspace_bytes(args(), 16, 1, -1) == 0
     a = args()
-    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, one - 1) == bd.IX_ERR_WORKSPACE
-    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, one) == bd.IX_ERR_WORKSPACE
-    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, one) == bd.IX_ERR_INVALID
+    bf, f32 = bd.PAIR_ROWS_BF16, bd.PAIR_ROWS_FP32
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, bf, FAKE, one - 1) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, bf, 0, one) == bd.IX_ERR_WORKSPACE
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, bf, FAKE + 8, one) == bd.IX_ERR_INVALID
+    # fp32 dk_I rows: 512 instead of 256 bytes per pair at d_I = 128
+    one32 = bd.ix_indexer_bwd_workspace_bytes(args(), 16, 1, f32)
+    assert one32 >= one + 16 * 256
+    assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, f32, FAKE, one) == bd.IX_ERR_WORKSPACE
 
 
 def test_peak_validation_codes():

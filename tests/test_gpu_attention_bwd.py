@@ -3,7 +3,8 @@ oracle's chain rule, entry by entry.
 
 Tolerance (parity_util.attn_bwd_bounds): each entry of dq, dK and dV is a sum of terms, and
 every rounding the kernels make -- bf16 P and dS in the matrix products, D = dout . out from
-the bf16 forward output, the atomic-free form's bf16 pair rows, MFMA and fp32 sums -- moves it
+the bf16 forward output, the atomic-free form's pair rows when they are bf16, MFMA and fp32
+sums -- moves it
 by at most a small multiple (a few 2^-8) of sums of magnitudes along the chain rule that the
 oracle forms for that entry (O.sparse_attention_backward_magnitudes).  Each entry must lie
 within that worst-case bound of the oracle; an entry that no query reaches has bound 0 and
@@ -67,9 +68,17 @@ def _pair_bounds(mags, n_rows, H_q, orders, pair_rows):
     return c * sk, c * grow * mags["dV"]["p"]
 
 
-def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=(), rows_per_pass=None):
+def _form(rows_per_pass, pair_rows):
+    if rows_per_pass is None:
+        return "atomics"
+    rows = "fp32" if pair_rows == bd.PAIR_ROWS_FP32 else "bf16"
+    return f"key-major, {rows_per_pass} rows per pass, {rows} pair rows"
+
+
+def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=(), rows_per_pass=None,
+         pair_rows=bd.PAIR_ROWS_BF16):
     say(f"[sparse_attn_bwd] B={B} T={T} S={S} H_q={H_q} H_kv={H_kv} d={d} k={k} seed={seed} "
-        f"{'atomics' if rows_per_pass is None else f'key-major, {rows_per_pass} rows per pass'}")
+        f"{_form(rows_per_pass, pair_rows)}")
     g = torch.Generator(device="cpu").manual_seed(seed)
     q = (torch.randn(B, T, H_q, d, generator=g) * 0.3).to(torch.bfloat16)
     K = (torch.randn(B, S, H_kv, d, generator=g) * 0.3).to(torch.bfloat16)
@@ -91,38 +100,43 @@ def _run(B, T, S, H_q, H_kv, d, k, seed, kv_lens=None, empty_rows=(), rows_per_p
     scale = d ** -0.5
     out, lse = bd.sparse_attention(dq_, dK_, dV_, didx, scale, kv_len=dkvl, with_lse=True)
     gq, gK, gV = bd.sparse_attention_backward(dq_, dK_, dV_, didx, out, lse, dout.to(DEV), scale,
-                                              kv_len=dkvl, rows_per_pass=rows_per_pass)
+                                              kv_len=dkvl, rows_per_pass=rows_per_pass,
+                                              pair_rows=pair_rows)
     torch.cuda.synchronize()
     got = (gq.cpu().numpy(), gK.cpu().numpy(), gV.cpu().numpy())
     check_backward(got, _bits(q), _bits(K), _bits(V), idx, kvl, dout.float().numpy(), scale,
-                   rows_per_pass is not None, "sparse_attn_bwd")
+                   rows_per_pass is not None and pair_rows == bd.PAIR_ROWS_BF16, "sparse_attn_bwd")
 
 
-# None: dK / dV added with atomics; a row count: the atomic-free form (inverted selection,
-# per-pair rows, key-major sums), in passes of that many query rows
-MODES = [None, 1 << 20, 7]
+# (rows_per_pass, pair_rows).  None: dK / dV added with atomics; a row count: the atomic-free
+# form (inverted selection, per-pair rows, key-major sums), in passes of that many query rows,
+# with bf16 or fp32 pair rows
+MODES = [(None, bd.PAIR_ROWS_BF16), (1 << 20, bd.PAIR_ROWS_BF16), (7, bd.PAIR_ROWS_BF16),
+         (1 << 20, bd.PAIR_ROWS_FP32), (7, bd.PAIR_ROWS_FP32)]
 
 
-@pytest.mark.parametrize("rows_per_pass", MODES)
-def test_backward_gqa_ragged_d64(rows_per_pass):
+@pytest.mark.parametrize("rows_per_pass,pair_rows", MODES)
+def test_backward_gqa_ragged_d64(rows_per_pass, pair_rows):
     _run(B=2, T=40, S=300, H_q=8, H_kv=2, d=64, k=48, seed=71, kv_lens=[300, 170],
-         empty_rows={(0, 3)}, rows_per_pass=rows_per_pass)
+         empty_rows={(0, 3)}, rows_per_pass=rows_per_pass, pair_rows=pair_rows)
 
 
-@pytest.mark.parametrize("rows_per_pass", MODES)
-def test_backward_mqa_d128_many_chunks(rows_per_pass):
-    _run(B=1, T=64, S=4096, H_q=16, H_kv=1, d=128, k=256, seed=72, rows_per_pass=rows_per_pass)
+@pytest.mark.parametrize("rows_per_pass,pair_rows", MODES)
+def test_backward_mqa_d128_many_chunks(rows_per_pass, pair_rows):
+    _run(B=1, T=64, S=4096, H_q=16, H_kv=1, d=128, k=256, seed=72, rows_per_pass=rows_per_pass,
+         pair_rows=pair_rows)
 
 
-@pytest.mark.parametrize("rows_per_pass", MODES)
-def test_backward_k_not_a_multiple_of_4(rows_per_pass):
-    _run(B=1, T=33, S=500, H_q=16, H_kv=1, d=128, k=37, seed=73, rows_per_pass=rows_per_pass)
+@pytest.mark.parametrize("rows_per_pass,pair_rows", MODES)
+def test_backward_k_not_a_multiple_of_4(rows_per_pass, pair_rows):
+    _run(B=1, T=33, S=500, H_q=16, H_kv=1, d=128, k=37, seed=73, rows_per_pass=rows_per_pass,
+         pair_rows=pair_rows)
 
 
 def test_backward_atomic_free_matches_atomics():
-    """The two forms sum the same fp32 products; the atomic-free one rounds each pair's rows
-    to bf16 first, so dK and dV agree to bf16 rounding of the terms, and dq is the same
-    computation (bitwise)."""
+    """The forms sum the same fp32 products; the atomic-free one with bf16 pair rows rounds
+    each pair's rows to bf16 first, so dK and dV agree to bf16 rounding of the terms; with fp32
+    pair rows only the order of the fp32 sums differs.  dq is the same computation (bitwise)."""
     say("[sparse_attn_bwd] atomic-free vs atomics, hot keys shared by every query")
     g = torch.Generator(device="cpu").manual_seed(74)
     B, T, S, H_q, d, k = 2, 48, 600, 16, 128, 64
@@ -138,22 +152,35 @@ def test_backward_atomic_free_matches_atomics():
     out, lse = bd.sparse_attention(q, K, V, didx, d ** -0.5, with_lse=True)
     a = bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, d ** -0.5)
     f = bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, d ** -0.5, rows_per_pass=10)
+    f32 = bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, d ** -0.5, rows_per_pass=10,
+                                       pair_rows=bd.PAIR_ROWS_FP32)
     torch.cuda.synchronize()
-    assert torch.equal(a[0], f[0]), "dq differs"
-    # per entry: the atomic-free form's only extra rounding is each pair row's bf16 rounding,
-    # and the two forms add in different orders
+    assert torch.equal(a[0], f[0]) and torch.equal(a[0], f32[0]), "dq differs"
+    # per entry: the bf16 atomic-free form's only extra rounding is each pair row's bf16
+    # rounding; the fp32 one has none; and the forms add in different orders
     qb, Kb, Vb = _bits(q), _bits(K), _bits(V)
     dob = dout.float().cpu().numpy().astype(np.float64)
     for b in range(B):
         mags = O.sparse_attention_backward_magnitudes(qb, Kb, Vb, idx[b], dob[b], b,
                                                       list(range(T)), d ** -0.5)
-        bK, bV = _pair_bounds(mags, T, H_q, 2, True)
-        for n, bnd in ((1, bK), (2, bV)):
-            x = a[n][b].double().cpu().numpy()
-            y = f[n][b].double().cpu().numpy()
-            check_attn_bwd_entries(y, x, bnd, f"{('dK', 'dV')[n - 1]} b={b}: atomic-free vs atomics")
-    # and both against the oracle
-    for form, got in (("atomics", a), ("atomic-free", f)):
+        for got, bf16_rows, form in ((f, True, "bf16 rows"), (f32, False, "fp32 rows")):
+            bK, bV = _pair_bounds(mags, T, H_q, 2, bf16_rows)
+            for n, bnd in ((1, bK), (2, bV)):
+                x = a[n][b].double().cpu().numpy()
+                y = got[n][b].double().cpu().numpy()
+                # the fp32 rows differ from the atomics only by reordering: few entries come
+                # near that bound, so no share of them is asked to
+                check_attn_bwd_entries(y, x, bnd, f"{('dK', 'dV')[n - 1]} b={b}: atomic-free "
+                                       f"({form}) vs atomics", power=0.5 if bf16_rows else None)
+    # fp32 rows sit far closer to the atomic form than bf16 rows do
+    for n in (1, 2):
+        dev16 = (f[n] - a[n]).abs().max().item()
+        dev32 = (f32[n] - a[n]).abs().max().item()
+        say(f"  {('dK', 'dV')[n - 1]}: max |bf16 rows - atomics| {dev16:.3e}, "
+            f"max |fp32 rows - atomics| {dev32:.3e}")
+        assert dev32 * 16 <= dev16, "fp32 pair rows are not tighter than bf16 ones"
+    # and every form against the oracle
+    for form, got in (("atomics", a), ("atomic-free", f), ("atomic-free fp32 rows", f32)):
         # 16 hot keys kept by every query sum 768 terms each, so fewer entries stand out
         check_backward(tuple(x.cpu().numpy() for x in got), qb, Kb, Vb, idx, np.array([S] * B),
                        dout.float().cpu().numpy(), d ** -0.5, form == "atomic-free", form,
@@ -177,20 +204,24 @@ def test_atomic_free_backward_is_reproducible():
     didx = torch.from_numpy(idx).to(DEV)
     scale = d ** -0.5
     out, lse = bd.sparse_attention(q, K, V, didx, scale, with_lse=True)
-    for rows_per_pass in (1 << 20, 50):
+    for rows_per_pass, pair_rows in ((1 << 20, bd.PAIR_ROWS_BF16), (50, bd.PAIR_ROWS_BF16),
+                                     (50, bd.PAIR_ROWS_FP32)):
         runs = [bd.sparse_attention_backward(q, K, V, didx, out, lse, dout, scale,
-                                             rows_per_pass=rows_per_pass) for _ in range(2)]
+                                             rows_per_pass=rows_per_pass, pair_rows=pair_rows)
+                for _ in range(2)]
         torch.cuda.synchronize()
         for x, y, name in zip(runs[0], runs[1], ("dq", "dK", "dV")):
-            assert torch.equal(x, y), f"{name} differs between runs ({rows_per_pass} rows per pass)"
+            assert torch.equal(x, y), f"{name} differs between runs ({_form(rows_per_pass, pair_rows)})"
 
 
-@pytest.mark.parametrize("rows_per_pass", [None, 10])
-def test_group_backward_shares_the_inversion(rows_per_pass):
+@pytest.mark.parametrize("rows_per_pass,pair_rows", [(None, bd.PAIR_ROWS_BF16),
+                                                    (10, bd.PAIR_ROWS_BF16),
+                                                    (10, bd.PAIR_ROWS_FP32)])
+def test_group_backward_shares_the_inversion(rows_per_pass, pair_rows):
     """indexshare_group_bwd: three layers over one selection, the selection inverted once per
     pass.  Each layer equals sparse_attn_bwd's atomic-free form on its own inputs (dq bit for
     bit; dK, dV up to the order of the per-key fp32 sums), and the oracle's chain rule."""
-    say(f"[indexshare_group_bwd] 3 layers, rows per pass {rows_per_pass}")
+    say(f"[indexshare_group_bwd] 3 layers, {_form(rows_per_pass or 'all', pair_rows)}")
     g = torch.Generator(device="cpu").manual_seed(75)
     B, T, S, H_q, H_kv, d, k = 2, 30, 400, 8, 2, 64, 40
     rng = np.random.default_rng(75)
@@ -213,14 +244,16 @@ def test_group_backward_shares_the_inversion(rows_per_pass):
         L["out"], L["lse"] = bd.sparse_attention(L["q"], L["K"], L["V"], didx, scale, kv_len=dkvl,
                                                  with_lse=True)
         layers.append(L)
-    grads = bd.group_attention_backward(didx, layers, scale, kv_len=dkvl, rows_per_pass=rows_per_pass)
+    grads = bd.group_attention_backward(didx, layers, scale, kv_len=dkvl, rows_per_pass=rows_per_pass,
+                                        pair_rows=pair_rows)
     torch.cuda.synchronize()
     for l, L in enumerate(layers):
         ref = bd.sparse_attention_backward(L["q"], L["K"], L["V"], didx, L["out"], L["lse"], L["dout"],
-                                           scale, kv_len=dkvl, rows_per_pass=rows_per_pass or B * T)
+                                           scale, kv_len=dkvl, rows_per_pass=rows_per_pass or B * T,
+                                           pair_rows=pair_rows)
         torch.cuda.synchronize()
         assert torch.equal(grads[l][0], ref[0]), f"layer {l}: dq differs"
-        # the same bf16 pair rows, summed per key in fp32 (in row order in both)
+        # the same pair rows, summed per key in fp32 (in row order in both)
         qb, Kb, Vb = _bits(L["q"]), _bits(L["K"]), _bits(L["V"])
         dob = L["dout"].float().cpu().numpy().astype(np.float64)
         for b in range(B):
@@ -235,5 +268,5 @@ def test_group_backward_shares_the_inversion(rows_per_pass):
     # and every layer against the oracle
     for l, L in enumerate(layers):
         check_backward(tuple(x.cpu().numpy() for x in grads[l]), _bits(L["q"]), _bits(L["K"]),
-                       _bits(L["V"]), idx, kvl, L["dout"].float().cpu().numpy(), scale, True,
-                       f"group layer {l}")
+                       _bits(L["V"]), idx, kvl, L["dout"].float().cpu().numpy(), scale,
+                       pair_rows == bd.PAIR_ROWS_BF16, f"group layer {l}")

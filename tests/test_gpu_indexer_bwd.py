@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(qI, kI, w, kvl, idx, ds, rows_per_pass=None):
+def _run(qI, kI, w, kvl, idx, ds, rows_per_pass=None, pair_rows=bd.PAIR_ROWS_BF16):
     B, T, H, d_I = qI.shape
     t = {n: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
          for n, v in (("q", qI), ("k", kI), ("w", w.astype(np.float32)),
@@ -35,7 +35,8 @@ def _run(qI, kI, w, kvl, idx, ds, rows_per_pass=None):
                       ("ds", ds.astype(np.float32)))}
     pos0 = torch.zeros(B, dtype=torch.int32, device=DEV)
     args = bd.indexer_args(t["q"], t["k"], t["w"], pos0, t["kvl"])
-    dq, dw, dk = bd.indexer_bwd(args, t["idx"], t["ds"], DEV, rows_per_pass=rows_per_pass)
+    dq, dw, dk = bd.indexer_bwd(args, t["idx"], t["ds"], DEV, rows_per_pass=rows_per_pass,
+                                pair_rows=pair_rows)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), dw.cpu().numpy(), dk.cpu().numpy()
 
@@ -66,36 +67,42 @@ def _case(seed, B, T, S, H, d_I, k, kv_lens, values=None, empty_rows=(), past_kv
     return qI, kI, w, kvl, idx, ds
 
 
-# None: dk_I added with atomics; a row count: the atomic-free form (inverted selection,
-# per-pair bf16 rows, key-major sums) in passes of that many query rows
-MODES = [None, 1 << 20, 7]
+# (rows_per_pass, pair_rows).  None: dk_I added with atomics; a row count: the atomic-free form
+# (inverted selection, per-pair rows in bf16 or fp32, key-major sums) in passes of that many
+# query rows
+BF, F32 = bd.PAIR_ROWS_BF16, bd.PAIR_ROWS_FP32
+MODES = [(None, BF), (1 << 20, BF), (7, BF), (1 << 20, F32), (7, F32)]
 
 
-@pytest.mark.parametrize("rows_per_pass", MODES)
-def test_indexer_bwd_ragged_64_heads_d128(rows_per_pass):
+def _bf16_rows(rows_per_pass, pair_rows):
+    return rows_per_pass is not None and pair_rows == BF
+
+
+@pytest.mark.parametrize("rows_per_pass,pair_rows", MODES)
+def test_indexer_bwd_ragged_64_heads_d128(rows_per_pass, pair_rows):
     say(f"[ix_indexer_bwd] B=2 T=40 S=500 H_I=64 d_I=128 k=96, ragged kv_len, empty row, "
-        f"rows per pass {rows_per_pass}")
+        f"rows per pass {rows_per_pass}, pair rows {pair_rows}")
     qI, kI, w, kvl, idx, ds = _case(201, 2, 40, 500, 64, 128, 96, [500, 213], empty_rows={(1, 7)},
                                     past_kv=20)
-    got = _run(qI, kI, w, kvl, idx, ds, rows_per_pass)
+    got = _run(qI, kI, w, kvl, idx, ds, rows_per_pass, pair_rows)
     assert np.all(got[0][1, 7] == 0) and np.all(got[1][1, 7] == 0)
-    check_indexer_bwd(got, qI, kI, w, idx, ds, kvl, bf16_rows=rows_per_pass is not None)
+    check_indexer_bwd(got, qI, kI, w, idx, ds, kvl, bf16_rows=_bf16_rows(rows_per_pass, pair_rows))
 
 
-@pytest.mark.parametrize("rows_per_pass", MODES)
-def test_indexer_bwd_exact_zero_dots_partial_head_tile_d64(rows_per_pass):
+@pytest.mark.parametrize("rows_per_pass,pair_rows", MODES)
+def test_indexer_bwd_exact_zero_dots_partial_head_tile_d64(rows_per_pass, pair_rows):
     """Codes in {0, +-1, +-2}: many dot products are exactly 0 (gradient 0 there on both
     sides); 20 heads leave a partial tile of 16; k = 37 leaves a ragged chunk."""
     say(f"[ix_indexer_bwd] B=1 T=33 S=300 H_I=20 d_I=64 k=37, integer codes, rows per pass "
-        f"{rows_per_pass}")
+        f"{rows_per_pass}, pair rows {pair_rows}")
     qI, kI, w, kvl, idx, ds = _case(202, 1, 33, 300, 20, 64, 37, [300],
                                     values=[0.0, 0.0, 0.0, 1.0, -1.0, 2.0, -2.0])
     keys = O.decode_e4m3(kI[0])
     x0 = O.decode_e4m3(qI[0]) @ keys.T
     say(f"  exact zero dot products: {int((x0 == 0).sum())} of {x0.size}")
     assert (x0 == 0).sum() > 100
-    check_indexer_bwd(_run(qI, kI, w, kvl, idx, ds, rows_per_pass), qI, kI, w, idx, ds, kvl,
-                      bf16_rows=rows_per_pass is not None)
+    check_indexer_bwd(_run(qI, kI, w, kvl, idx, ds, rows_per_pass, pair_rows), qI, kI, w, idx, ds,
+                      kvl, bf16_rows=_bf16_rows(rows_per_pass, pair_rows))
 
 
 def test_indexer_bwd_full_k_and_few_heads():
@@ -198,8 +205,31 @@ def test_indexer_bwd_atomic_free_is_reproducible():
     run to run: one pass over many row blocks, and passes of 40 rows."""
     say("[ix_indexer_bwd] atomic-free determinism")
     qI, kI, w, kvl, idx, ds = _case(207, 2, 300, 700, 64, 128, 160, [700, 650])
-    for rows_per_pass in (1 << 20, 40):
-        a = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=rows_per_pass)
-        b = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=rows_per_pass)
+    for rows_per_pass, pair_rows in ((1 << 20, BF), (40, BF), (40, F32)):
+        a = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=rows_per_pass, pair_rows=pair_rows)
+        b = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=rows_per_pass, pair_rows=pair_rows)
         for x, y, name in zip(a, b, ("dq_I", "dw", "dk_I")):
-            assert np.array_equal(x, y), f"{name} differs between runs ({rows_per_pass} rows per pass)"
+            assert np.array_equal(x, y), (f"{name} differs between runs ({rows_per_pass} rows per "
+                                          f"pass, pair rows {pair_rows})")
+
+
+def test_indexer_bwd_fp32_rows_match_atomics():
+    """With fp32 dk_I pair rows the atomic-free form adds the same fp32 rows as the atomic
+    form, only in another order: dk_I agrees with the atomics to fp32 reordering, far inside
+    the bf16 rows' distance; dq_I and dw are the same computation (bitwise)."""
+    say("[ix_indexer_bwd] fp32 pair rows vs atomics, keys kept by many rows")
+    qI, kI, w, kvl, idx, ds = _case(208, 1, 200, 300, 64, 128, 128, [300])
+    a = _run(qI, kI, w, kvl, idx, ds)
+    f16 = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=30, pair_rows=BF)
+    f32 = _run(qI, kI, w, kvl, idx, ds, rows_per_pass=30, pair_rows=F32)
+    for got in (f16, f32):
+        assert np.array_equal(a[0], got[0]) and np.array_equal(a[1], got[1])
+    mag = O.indexer_backward_rows(abs_codes(qI), abs_codes(kI), np.abs(w), idx[0], np.abs(ds[0]),
+                                  0, list(range(200)), int(kvl[0]))[2]
+    # two orders of the same fp32 additions: at most (T + 64) u of the magnitude each
+    bound = 2 * (200 + 64) * 2.0 ** -24 * mag
+    err32 = np.abs(f32[2][0].astype(np.float64) - a[2][0])
+    assert np.all(err32 <= bound), f"fp32 rows off the atomics by up to {(err32 / np.maximum(bound, 1e-300)).max():.2f} bounds"
+    dev16 = np.abs(f16[2] - a[2]).max()
+    say(f"  max |bf16 rows - atomics| {dev16:.3e}, max |fp32 rows - atomics| {err32.max():.3e}")
+    assert err32.max() * 16 <= dev16
