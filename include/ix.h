@@ -408,6 +408,46 @@ ix_status ix_append_kv(const float *k_I_new, const void *K_new, const void *V_ne
                        int32_t H_kv, int32_t d, uint8_t *k_I_cache, void *K_cache, void *V_cache,
                        hipStream_t stream);
 
+/*
+ * Debug status -- not from the pages: a way to see, without a trap, what the kernels do
+ * quietly.  Off by default.  While on (process-wide, from the next call), the library counts
+ * into a status block that each GPU holds until the process ends:
+ *   idx_out_of_range:      entries of a selection passed in by the caller that name no key,
+ *                          i.e. lie outside [-1, kv_len) (-1 is the padding value); the
+ *                          kernels skip such entries.  Each call that takes a selection
+ *                          (sparse_attn_fwd, sparse_attn_group_fwd, sparse_attn_bwd,
+ *                          indexshare_group_bwd, ix_indexer_kl, ix_indexer_bwd) counts each
+ *                          such entry once, with one extra pass over idx;
+ *   topk_compactions:      candidate buffers of the top-k that filled and were compacted in
+ *                          place (a normal event; many of them mean a poor starting threshold);
+ *   topk_resweeps:         top-k sweeps restarted from zero because the sampled starting
+ *                          threshold kept too few keys (normal, and rare);
+ *   topk_split_recomputes: queries whose key-split merge could not prove it held the top-k
+ *                          and that were selected again without splits (normal);
+ *   topk_overflow:         candidate entries dropped because a buffer had no room.  The
+ *                          buffers are sized so that this cannot happen; the kernel skips
+ *                          such a write rather than trapping, and a nonzero count means a
+ *                          wrong selection.
+ * Counting adds device-scope atomics and a pass over idx; the results are the same either
+ * way.  Calls that overlap on one GPU add into the same block.
+ */
+typedef struct ix_debug_status {
+  uint64_t idx_out_of_range;
+  uint64_t topk_compactions;
+  uint64_t topk_resweeps;
+  uint64_t topk_split_recomputes;
+  uint64_t topk_overflow;
+} ix_debug_status;
+
+/* Turns the debug status on (on = 1) or off (on = 0) for the calls that follow.
+ * Errors: IX_ERR_INVALID for another value of on. */
+ix_status ix_debug_enable(int32_t on);
+
+/* Copies the debug status block of the stream's GPU to *status once the work queued on
+ * `stream` has finished (the call synchronizes the stream), then, with reset != 0, zeroes
+ * the block.  Errors: IX_ERR_INVALID for a NULL status; IX_ERR_HIP if the copy fails. */
+ix_status ix_debug_read(ix_debug_status *status, int32_t reset, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

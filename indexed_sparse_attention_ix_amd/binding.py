@@ -35,7 +35,7 @@ EXPORTS = ("ix_abi_version", "ix_last_error", "ix_score", "ix_topk_workspace_byt
            "indexshare_group_fwd", "indexshare_group_fwd_noalloc", "ix_append_kv",
            "ix_pool_keys", "ix_topk_pooled_workspace_bytes", "ix_topk_pooled", "sparse_attn_bwd",
            "sparse_attn_bwd_workspace_bytes", "indexshare_group_bwd", "ix_indexer_kl",
-           "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes")
+           "ix_indexer_bwd", "ix_indexer_bwd_workspace_bytes", "ix_debug_enable", "ix_debug_read")
 
 
 class IxError(RuntimeError):
@@ -48,6 +48,13 @@ class IndexerArgs(ctypes.Structure):
     _fields_ = [("q", c_void_p), ("k", c_void_p), ("w", c_void_p), ("q_pos0", c_void_p),
                 ("kv_len", c_void_p), ("B", c_int32), ("T", c_int32), ("S_max", c_int32),
                 ("H_I", c_int32), ("d_I", c_int32)]
+
+
+class DebugStatus(ctypes.Structure):
+    """ix_debug_status of include/ix.h."""
+    _fields_ = [("idx_out_of_range", ctypes.c_uint64), ("topk_compactions", ctypes.c_uint64),
+                ("topk_resweeps", ctypes.c_uint64), ("topk_split_recomputes", ctypes.c_uint64),
+                ("topk_overflow", ctypes.c_uint64)]
 
 
 _lib = None
@@ -124,6 +131,10 @@ def load(path: str = LIB_PATH):
     L.ix_append_kv.restype = c_int32
     L.ix_append_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.ix_debug_enable.restype = c_int32
+    L.ix_debug_enable.argtypes = [c_int32]
+    L.ix_debug_read.restype = c_int32
+    L.ix_debug_read.argtypes = [P(DebugStatus), c_int32, c_void_p]
     if L.ix_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI version {L.ix_abi_version()}, this binding expects "
                            f"{ABI_VERSION}: rebuild with __graft_entry__.build()")
@@ -239,6 +250,17 @@ def ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d, k_I
                  K_cache, V_cache, stream=0):
     _check(load().ix_append_kv(k_I_new, K_new, V_new, pos0, B, T_new, S_max, d_I, H_kv, d,
                                k_I_cache, K_cache, V_cache, stream))
+
+
+def ix_debug_enable(on: int):
+    _check(load().ix_debug_enable(on))
+
+
+def ix_debug_read(reset: int = 0, stream: int = 0) -> dict:
+    """The debug status of the stream's GPU (ix_debug_read) as a dict of its counters."""
+    st = DebugStatus()
+    _check(load().ix_debug_read(ctypes.byref(st), reset, stream))
+    return {name: int(getattr(st, name)) for name, _ in DebugStatus._fields_}
 
 
 def sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max, H_q, H_kv, d, k,

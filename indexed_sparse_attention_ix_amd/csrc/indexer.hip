@@ -73,6 +73,7 @@ struct IxArgs {
   int32_t* idx;
   float* sel;
   float* scores;
+  unsigned long long* dbg;  // debug status words (DebugWord), or null: no counting
 };
 
 // 32 bytes of an FP8 row for lane group lg (bytes [32*lg, 32*lg + 32)); rows of width
@@ -486,8 +487,12 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   uint64_t th_lane = 0ull;    // own query's threshold: keep keys >= it
   const int limit = p.ksel + (p.cap - WSTG - p.ksel) / 2;
 
-  // stage -> per-query buffers, each query's entries in stage (= key) order
+  // stage -> per-query buffers, each query's entries in stage (= key) order.  The buffers
+  // are sized so that a flush always fits (a compaction follows any flush that leaves less
+  // than a stage of room); entries that would not fit are dropped, not written, and counted
+  // in the debug status.
   auto flush = [&]() {
+    int lost = 0;
     for (int e0 = 0; e0 < stotal; e0 += 64) {
       const int e = e0 + lane;
       const bool valid = e < stotal;
@@ -497,13 +502,16 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       for (int i = 0; i < QC; ++i) {
         const bool mine = valid && q == i;
         const uint64_t m = ballot64(mine);
-        if (mine)
-          qbuf(i)[gcnt[i] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0))] = v;
-        gcnt[i] += popc64(m);
+        const int pos = gcnt[i] + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (mine && pos < p.cap) qbuf(i)[pos] = v;
+        const int n = gcnt[i] + popc64(m);
+        lost += n > p.cap ? n - max(gcnt[i], p.cap) : 0;
+        gcnt[i] = min(n, p.cap);
       }
     }
     stotal = 0;
+    if (lost && p.dbg && lane == 0) atomicAdd(p.dbg + kDbgTopkOverflow, (unsigned long long)lost);
   };
   auto select_on = [&](auto nb, uint64_t* buf, int n, int kk, int lim_kept) -> SelectResult {
     constexpr int NB = decltype(nb)::value;
@@ -576,6 +584,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
             mem_fence_wave();
             dropped |= 1u << i;
             if (qi == i) th_lane = sr.theta;
+            if (p.dbg && lane == 0) atomicAdd(p.dbg + kDbgTopkCompactions, 1ull);
           }
         }
       }
@@ -614,6 +623,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
 #pragma unroll
   for (int i = 0; i < QC; ++i) short_q |= gcnt[i] < min(p.ksel, unit_keys(i));
   if (short_q) {
+    if (p.dbg && lane == 0) atomicAdd(p.dbg + kDbgTopkResweeps, 1ull);
 #pragma unroll
     for (int i = 0; i < QC; ++i) gcnt[i] = 0;
     dropped = 0;
@@ -843,6 +853,7 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
       for (int w = 1; w < kMergeWaves; ++w) kth = red64[w] < kth ? red64[w] : kth;
       const bool proven = trunc_max == 0ull || (N >= p.kout && trunc_max <= kth);
       p.fb_flags[row] = proven ? 0 : 1;
+      if (!proven && p.dbg) atomicAdd(p.dbg + kDbgTopkSplitRecomputes, 1ull);
     }
   }
 }
@@ -973,8 +984,10 @@ static IxArgs make_args(const ix_indexer_args& a) {
 }
 
 hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& pl, int32_t* idx,
-                          float* sel_scores, void* ws, hipStream_t stream, int pool) {
+                          float* sel_scores, void* ws, hipStream_t stream, int pool,
+                          unsigned long long* dbg) {
   IxArgs x = make_args(a);
+  x.dbg = dbg;
   x.g = pl.g;
   x.qgroups = pl.qgroups;
   x.n_splits = pl.n_splits;

@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -17,11 +18,15 @@
 // the array's name (which in host code is only a stand-in).
 static __device__ __align__(256) unsigned char scratch[IX_NOALLOC_SCRATCH_BYTES];
 
+// Debug status block (ix_debug_enable / ix_debug_read), one per GPU, reached the same way.
+static __device__ __align__(64) unsigned long long debug_words[ix::kDbgWords];
+static_assert(sizeof(ix_debug_status) == sizeof(unsigned long long) * ix::kDbgWords,
+              "ix_debug_status holds the debug words in order");
+
 // Launches go through IX_LAUNCH.  A test build (-DIX_TEST_HOOKS) adds an exported hook that
 // makes them return a chosen HIP error without launching, so the IX_ERR_HIP path and its
 // message are exercised on a machine without a GPU; the release library has no hook.
 #ifdef IX_TEST_HOOKS
-#include <atomic>
 static std::atomic<int> g_test_launch_error{0};
 extern "C" __attribute__((visibility("default"))) void ix_test_fail_launches(int32_t hip_error) {
   g_test_launch_error.store(hip_error);
@@ -166,33 +171,68 @@ ix_status check_attn_ptrs(const void* q, const void* kc, const void* vc, const i
   return IX_OK;
 }
 
-// Address of this device's copy of `scratch`: looked up once per device, with that device
-// current, and kept.  The device is the stream's (the current one for the NULL stream).
+// Address of this device's copy of a library-owned device array (`scratch`,
+// `debug_words`): looked up once per device, with that device current, and kept in `table`.
+// The device is the stream's (the current one for the NULL stream).
 constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
+std::mutex g_symbol_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
+void* g_debug_ptr[kMaxDevices] = {};
 
-hipError_t device_scratch(hipStream_t stream, void** out) {
+hipError_t device_symbol(const void* symbol, void** table, hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
+  std::lock_guard<std::mutex> lock(g_symbol_mu);
+  if (!table[dev]) {
     int cur = 0;
     if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
     if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    e = hipGetSymbolAddress(&p, symbol);
     if (cur != dev) {
       const hipError_t e2 = hipSetDevice(cur);
       if (e == hipSuccess) e = e2;
     }
     if (e != hipSuccess) return e;
-    g_scratch_ptr[dev] = p;
+    table[dev] = p;
   }
-  *out = g_scratch_ptr[dev];
+  *out = table[dev];
   return hipSuccess;
+}
+
+hipError_t device_scratch(hipStream_t stream, void** out) {
+  return device_symbol(HIP_SYMBOL(scratch), g_scratch_ptr, stream, out);
+}
+
+// The debug status: off unless ix_debug_enable(1).  debug_ptr gives the stream's GPU's
+// status block while it is on, else NULL (the kernels then count nothing).
+std::atomic<bool> g_debug{false};
+
+hipError_t debug_ptr(hipStream_t stream, unsigned long long** out) {
+  *out = nullptr;
+  if (!g_debug.load()) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = device_symbol(HIP_SYMBOL(debug_words), g_debug_ptr, stream, &p);
+  if (e == hipSuccess) *out = static_cast<unsigned long long*>(p);
+  return e;
+}
+
+// With the debug status on: count the caller's selection entries that name no key.
+ix_status debug_check_idx(const int32_t* idx, const int32_t* kv_len, int32_t B, int32_t T,
+                          int32_t S_max, int32_t k, hipStream_t stream) {
+  if (!g_debug.load()) return IX_OK;
+  unsigned long long* dbg = nullptr;
+  hipError_t e = IX_LAUNCH(debug_ptr(stream, &dbg));
+  if (e == hipSuccess && dbg) e = IX_LAUNCH(ix::launch_idx_check(idx, kv_len, B, T, S_max, k, dbg, stream));
+  return e == hipSuccess ? IX_OK : hip_fail(e, "debug check of idx");
+}
+
+// The debug status block for a launch (NULL while off).
+ix_status debug_words_for(hipStream_t stream, unsigned long long** dbg) {
+  const hipError_t e = IX_LAUNCH(debug_ptr(stream, dbg));
+  return e == hipSuccess ? IX_OK : hip_fail(e, "debug status address");
 }
 
 // indexshare_group_fwd, with the caller's workspace or (use_scratch) the library's scratch.
@@ -229,7 +269,9 @@ ix_status group_fwd(const ix_indexer_args* a, int32_t k, int32_t n_layers, const
   }
   if (!ws || ws_bytes < need)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
-  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream));
+  unsigned long long* dbg = nullptr;
+  if ((st = debug_words_for(stream, &dbg)) != IX_OK) return st;
+  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(*a, k, tp, idx, nullptr, ws, stream, 1, dbg));
   if (e != hipSuccess) return hip_fail(e, "indexshare selection launch");
   e = IX_LAUNCH(ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, a->kv_len, a->B, a->T, a->S_max,
                                     H_q, H_kv, d, k, sm_scale, out, lse, ap, ws, stream));
@@ -278,7 +320,9 @@ ix_status ix_topk(const ix_indexer_args* a, int32_t k, int32_t* idx, float* sel_
   if (!ws || ws_bytes < plan.ws_bytes)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 plan.ws_bytes);
-  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(*a, k, plan, idx, sel_scores, ws, stream));
+  unsigned long long* dbg = nullptr;
+  if ((st = debug_words_for(stream, &dbg)) != IX_OK) return st;
+  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(*a, k, plan, idx, sel_scores, ws, stream, 1, dbg));
   if (e != hipSuccess) return hip_fail(e, "ix_topk launch");
   return ok();
 }
@@ -305,6 +349,7 @@ ix_status sparse_attn_fwd(const void* q, const void* kc, const void* vc, const i
   if (plan.ws_bytes && (!ws || ws_bytes < plan.ws_bytes))
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 plan.ws_bytes);
+  if ((st = debug_check_idx(idx, kv_len, B, T, S_max, k, stream)) != IX_OK) return st;
   hipError_t e = IX_LAUNCH(ix::launch_sparse_attn(q, kc, vc, idx, kv_len, B, T, S_max, H_q, H_kv, d, k,
                                         sm_scale, out, lse, plan, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_fwd launch");
@@ -338,6 +383,7 @@ ix_status sparse_attn_group_fwd(int32_t n_layers, const void* const* q, const vo
   if (ap.ws_bytes && (!ws || ws_bytes < ap.ws_bytes))
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0,
                 ap.ws_bytes);
+  if ((st = debug_check_idx(idx, kv_len, B, T, S_max, k, stream)) != IX_OK) return st;
   hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_layers(n_layers, q, kc, vc, idx, kv_len, B, T, S_max, H_q,
                                                H_kv, d, k, sm_scale, out, lse, ap, ws, stream));
   if (e != hipSuccess) return hip_fail(e, "sparse_attn_group_fwd launch");
@@ -456,7 +502,9 @@ ix_status ix_topk_pooled(const ix_indexer_args* a, int32_t pool, int32_t k_block
   if (!ws || ws_bytes < need)
     return fail(IX_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws ? ws_bytes : (size_t)0, need);
   int32_t* blocks = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + plan.ws_bytes);
-  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(u, k_blocks, plan, blocks, nullptr, ws, stream, pool));
+  unsigned long long* dbg = nullptr;
+  if ((st = debug_words_for(stream, &dbg)) != IX_OK) return st;
+  hipError_t e = IX_LAUNCH(ix::launch_ix_topk(u, k_blocks, plan, blocks, nullptr, ws, stream, pool, dbg));
   if (e != hipSuccess) return hip_fail(e, "ix_topk_pooled launch");
   e = IX_LAUNCH(ix::launch_expand_blocks(blocks, a->q_pos0, a->kv_len, a->B, a->T, a->S_max, k_blocks, pool,
                                idx, stream));
@@ -504,6 +552,7 @@ ix_status sparse_attn_bwd(const void* q, const void* kc, const void* vc, const i
   } else if (ws_bytes != 0) {
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
+  if ((st = debug_check_idx(idx, kv_len, B, T, S_max, k, stream)) != IX_OK) return st;
   hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_bwd(q, kc, vc, idx, kv_len, out, lse, dout, B, T, S_max,
                                             H_q, H_kv, d, k, sm_scale, dq, dkc, dvc,
                                             pair_rows == IX_PAIR_ROWS_FP32, ws, ws_bytes, stream));
@@ -543,6 +592,7 @@ ix_status indexshare_group_bwd(const int32_t* idx, const int32_t* kv_len, int32_
   if (ix::pair_rows_per_pass(B, T, S_max, k, row_bytes, ws_bytes) < 1)
     return fail(IX_ERR_WORKSPACE, "workspace of %zu bytes is below one query row's need (%zu)",
                 ws_bytes, ix::pair_layout(B, S_max, k, 1, row_bytes).total);
+  if ((st = debug_check_idx(idx, kv_len, B, T, S_max, k, stream)) != IX_OK) return st;
   hipError_t e = IX_LAUNCH(ix::launch_sparse_attn_bwd_layers(n_layers, q, kc, vc, idx, kv_len, out, lse, dout,
                                                    B, T, S_max, H_q, H_kv, d, k, sm_scale, dq, dkc,
                                                    dvc, pair_rows == IX_PAIR_ROWS_FP32, ws,
@@ -565,6 +615,7 @@ ix_status ix_indexer_kl(const void* q, const void* kc, const int32_t* idx, const
     return fail(IX_ERR_INVALID, "bf16 q/kc base pointers must be 16-byte aligned");
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(IX_ERR_INVALID, "sm_scale must be finite");
+  if ((st = debug_check_idx(idx, kv_len, B, T, S_max, k, stream)) != IX_OK) return st;
   hipError_t e = IX_LAUNCH(ix::launch_indexer_kl(q, kc, idx, kv_len, lse, sel_scores, B, T, S_max, H_q, H_kv,
                                        d, k, sm_scale, loss, dscores, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_kl launch");
@@ -605,10 +656,37 @@ ix_status ix_indexer_bwd(const ix_indexer_args* a, int32_t k, const int32_t* idx
   } else if (ws_bytes != 0) {
     return fail(IX_ERR_WORKSPACE, "ws_bytes given without a workspace");
   }
+  if ((st = debug_check_idx(idx, a->kv_len, a->B, a->T, a->S_max, k, stream)) != IX_OK) return st;
   hipError_t e = IX_LAUNCH(ix::launch_indexer_bwd(a->q, a->k, a->w, a->kv_len, idx, dscores, a->B, a->T,
                                         a->S_max, a->H_I, a->d_I, k, dq_I, dw, dk_I,
                                         pair_rows == IX_PAIR_ROWS_FP32, ws, ws_bytes, stream));
   if (e != hipSuccess) return hip_fail(e, "ix_indexer_bwd launch");
+  return ok();
+}
+
+ix_status ix_debug_enable(int32_t on) {
+  if (on != 0 && on != 1) return fail(IX_ERR_INVALID, "on=%d: 0 or 1", on);
+  g_debug.store(on == 1);
+  return ok();
+}
+
+ix_status ix_debug_read(ix_debug_status* status, int32_t reset, hipStream_t stream) {
+  if (!status) return fail(IX_ERR_INVALID, "NULL status pointer");
+  void* p = nullptr;
+  hipError_t e = IX_LAUNCH(device_symbol(HIP_SYMBOL(debug_words), g_debug_ptr, stream, &p));
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  unsigned long long w[ix::kDbgWords] = {};
+  if (e == hipSuccess) e = hipMemcpy(w, p, sizeof(w), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) {
+    const unsigned long long zero[ix::kDbgWords] = {};
+    e = hipMemcpy(p, zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ix_debug_read");
+  status->idx_out_of_range = w[ix::kDbgIdxOutOfRange];
+  status->topk_compactions = w[ix::kDbgTopkCompactions];
+  status->topk_resweeps = w[ix::kDbgTopkResweeps];
+  status->topk_split_recomputes = w[ix::kDbgTopkSplitRecomputes];
+  status->topk_overflow = w[ix::kDbgTopkOverflow];
   return ok();
 }
 

@@ -48,10 +48,25 @@ size_t attn_group_ws_bytes(int B, int T, int H_q, int H_kv, int d, int k);
 
 hipError_t launch_ix_score(const ix_indexer_args& a, int t_begin, int t_end, float* scores,
                            hipStream_t stream);
+// Debug status words (unsigned long long each, in the order of ix_debug_status).
+enum DebugWord {
+  kDbgIdxOutOfRange = 0,
+  kDbgTopkCompactions,
+  kDbgTopkResweeps,
+  kDbgTopkSplitRecomputes,
+  kDbgTopkOverflow,
+  kDbgWords
+};
+
 // a.k holds one key row per unit of `pool` positions (1: tokens) and a.S_max counts
-// units; a.q_pos0 and a.kv_len count positions.
+// units; a.q_pos0 and a.kv_len count positions.  dbg: the debug status words, or null.
 hipError_t launch_ix_topk(const ix_indexer_args& a, int k, const TopkPlan& p, int32_t* idx,
-                          float* sel_scores, void* ws, hipStream_t stream, int pool = 1);
+                          float* sel_scores, void* ws, hipStream_t stream, int pool = 1,
+                          unsigned long long* dbg = nullptr);
+// Debug: adds to dbg[kDbgIdxOutOfRange] the entries of idx [B, T, k] outside [-1, kv_len)
+// (kv_len[b] clamped to [0, S_max]; NULL kv_len: S_max).
+hipError_t launch_idx_check(const int32_t* idx, const int32_t* kv_len, int B, int T, int S_max,
+                            int k, unsigned long long* dbg, hipStream_t stream);
 hipError_t launch_pool_keys(const uint8_t* k_I, const int32_t* kv_len, int B, int S_max, int d_I,
                             int pool, uint8_t* k_pooled, hipStream_t stream);
 hipError_t launch_expand_blocks(const int32_t* blocks, const int32_t* q_pos0,

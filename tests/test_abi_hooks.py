@@ -67,21 +67,27 @@ def _calls():
                                                   1, 128, 64, sc, FAKE, FAKE, None)),
         ("ix_indexer_bwd", lambda: L.ix_indexer_bwd(ctypes.byref(a), 64, FAKE, FAKE, FAKE, FAKE, FAKE,
                                                     bd.PAIR_ROWS_BF16, None, 0, None)),
+        ("ix_debug_read", lambda: L.ix_debug_read(ctypes.byref(bd.DebugStatus()), 1, None)),
     ]
 
 
-def test_every_launching_entry_point_reports_the_hip_error():
+@pytest.mark.parametrize("debug", [0, 1])
+def test_every_launching_entry_point_reports_the_hip_error(debug):
+    """With the debug status on, the calls first look up its address or check idx: the
+    failure of those steps is reported the same way."""
     lib = _hooked_lib()
     lib.ix_test_fail_launches(HIP_ERROR_LAUNCH_FAILURE)
+    bd.ix_debug_enable(debug)
     try:
         for name, call in _calls():
             st = call()
             msg = bd.ix_last_error()
             assert st == bd.IX_ERR_HIP, f"{name}: status {st} ({msg})"
-            assert "launch" in msg or "scratch" in msg, f"{name}: {msg}"
+            assert any(w in msg for w in ("launch", "scratch", "debug")), f"{name}: {msg}"
             assert len(msg) > len(name), f"{name}: no HIP error text in {msg!r}"
     finally:
         lib.ix_test_fail_launches(0)
+        bd.ix_debug_enable(0)
     # a failing validation still wins over the hook, and a clean status clears the message
     lib.ix_test_fail_launches(HIP_ERROR_LAUNCH_FAILURE)
     try:

@@ -360,6 +360,16 @@ def test_indexer_bwd_validation_codes():
     assert status_of(bd.ix_indexer_bwd, a, 16, FAKE, FAKE, FAKE, FAKE, FAKE, f32, FAKE, one) == bd.IX_ERR_WORKSPACE
 
 
+def test_debug_status_validation():
+    assert status_of(bd.ix_debug_enable, 2) == bd.IX_ERR_INVALID
+    assert status_of(bd.ix_debug_enable, -1) == bd.IX_ERR_INVALID
+    assert bd.load().ix_debug_read(None, 0, None) == bd.IX_ERR_INVALID
+    assert "NULL" in bd.ix_last_error()
+    assert status_of(bd.ix_debug_enable, 1) == bd.IX_OK
+    assert status_of(bd.ix_debug_enable, 0) == bd.IX_OK
+    assert ctypes.sizeof(bd.DebugStatus) == 5 * 8
+
+
 def test_peak_validation_codes():
     assert status_of(pk.ix_peak_mfma_fp8, 0, 8, 1, 1, FAKE) == bd.IX_ERR_INVALID
     assert "NULL" in pk.load().ix_peak_last_error().decode()
