@@ -37,20 +37,29 @@ ix_status ix_peak_mfma_fp8(const void *operands, int32_t valu_per_mfma, int32_t 
  * bytes: a multiple of 16; src and dst 16-byte aligned, not overlapping. */
 ix_status ix_peak_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
-/* ix_peak_read -- reads src[0, bytes) once with 16-byte loads over 4096 blocks (a read-only
- * stream, as the decode indexer streams its keys).  out: uint32 [4096], entry i written with
- * the XOR of the 32-bit words block i read (the XOR of all entries is the XOR of the bytes).
- * bytes: a multiple of 16; src 16-byte aligned. */
-ix_status ix_peak_read(const void *src, size_t bytes, uint32_t *out, hipStream_t stream);
+/* ix_peak_read -- reads src[0, bytes) once with 16-byte loads, four in flight per lane, over
+ * `blocks` blocks of 256 threads (a read-only stream, as the decode indexer streams its keys;
+ * the best grid depends on the machine, so the caller sweeps it).  nontemporal = 1 marks the
+ * loads non-temporal (the faster stream; the data does not stay in the caches), 0 makes them
+ * ordinary loads, which fill the caches (reading a buffer larger than the caches this way
+ * evicts what they held).  out: uint32 [blocks], entry i written with the XOR of the 32-bit
+ * words block i read (the XOR of all entries is the XOR of the bytes).  bytes: a multiple of
+ * 16; src 16-byte aligned.  Errors: IX_ERR_INVALID for NULL pointers, misalignment, blocks
+ * outside 1..65536 or nontemporal outside {0, 1}. */
+ix_status ix_peak_read(const void *src, size_t bytes, int32_t blocks, int32_t nontemporal,
+                       uint32_t *out, hipStream_t stream);
 
 /*
  * ix_peak_gather -- reads the 256-byte rows table[rows[i]], i < n, each by 16
- * consecutive lanes with 16-byte loads, 16 loads in flight per lane, over 2048 blocks.
+ * consecutive lanes with 16-byte loads, 8 loads in flight per lane, over
+ * `blocks` blocks of 256 threads.
  * table_bytes: <= 2 GiB, a multiple of 256; rows outside the table read as zero.
- * out: uint32 [2048], entry i written with the XOR of the words block i read.
+ * out: uint32 [blocks], entry i written with the XOR of the words block i read.
+ * Errors: IX_ERR_INVALID for NULL pointers, n < 0, a bad table size or alignment, or blocks
+ * outside 1..65536.
  */
 ix_status ix_peak_gather(const void *table, size_t table_bytes, const int32_t *rows, int64_t n,
-                         uint32_t *out, hipStream_t stream);
+                         int32_t blocks, uint32_t *out, hipStream_t stream);
 
 /*
  * ix_peak_gather_selection -- reads, for every query and KV head, the K and V rows its

@@ -593,14 +593,25 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
     mem_fence_wave();
   };
 
-  // Sampled starting threshold: score one tile of every stride first (stride >= 4, at most
-  // 64 tiles) and start each query at the r-th best sampled key, r a few standard deviations
-  // above the number of the query's top-k' keys the sample is expected to hold.  That is
-  // a guess; the check after the sweep keeps the result exact.
+  // Sampled starting threshold: score a 1/stride share of the unit's tiles first (stride >= 4,
+  // at most samp_tiles tiles) and start each query at the r-th best sampled key, r a few
+  // standard deviations above the number of the query's top-k' keys the sample is expected
+  // to hold.  That is a guess; the check after the sweep keeps the result exact.
+  //  * 4-query units: one hashed tile of every stride group, scored again by the sweep (the
+  //    query groups of a sequence share their key rows, so the second read hits the caches);
+  //  * 1-query units (decode): each unit reads its keys alone, so a second read would come
+  //    from memory.  The sample is the unit's first tiles instead: their entries stay in
+  //    the buffer, filtered by the threshold (order kept), and the sweep goes on after them.
   const int n_tiles = ke > ks ? (ke - ks + 15) / 16 : 0;
   const int stride = p.samp_tiles > 0 ? n_tiles / p.samp_tiles : 0;
+  int first = 0;  // tiles already swept
   if (stride >= 4) {
-    sweep(ks, stride, p.samp_tiles);
+    if constexpr (QC == 1) {
+      sweep(ks, 1, p.samp_tiles);
+      first = p.samp_tiles;
+    } else {
+      sweep(ks, stride, p.samp_tiles);
+    }
 #pragma unroll
     for (int i = 0; i < QC; ++i) {
       const int keff = min(p.ksel, unit_keys(i));
@@ -610,13 +621,18 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       if (rank < gcnt[i]) {
         th = select_on(SweepBatch{}, qbuf(i), gcnt[i], rank, 0).theta;
         dropped |= 1u << i;
+        if constexpr (QC == 1) {
+          uint64_t* buf = qbuf(i);
+          gcnt[i] = wave_filter<kHistBatch>(buf, gcnt[i], th,
+                                            [&](int pos, uint64_t v) { buf[pos] = v; });
+        }
       }
       if (qi == i) th_lane = th;
-      gcnt[i] = 0;
+      if constexpr (QC != 1) gcnt[i] = 0;
     }
     mem_fence_wave();
   }
-  sweep(ks, 1, n_tiles);
+  sweep(ks + 16 * first, 1, n_tiles - first);
   // Every query must end with at least min(k', visible) entries, which proves that its
   // k'-th key is at or above its starting threshold; otherwise sweep again from zero.
   bool short_q = false;

@@ -72,6 +72,9 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // Wait for this wave's outstanding vector-memory operations.
 __device__ __forceinline__ void vmem_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Cache-policy operand of a buffer load that marks it non-temporal (data read once).
+constexpr int kLoadNT = 2;
+
 // Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,

@@ -29,8 +29,8 @@ namespace {
 
 constexpr int kPeakBlock = 256;
 constexpr int kPeakHeads = 16;  // B operands held in registers, as in the indexer
-constexpr int kReadBlocks = 4096;    // grid of the copy and read-only stream kernels
-constexpr int kGatherBlocks = 2048;  // grid of the row-gather kernel
+constexpr int kReadBlocks = 4096;    // grid of the copy kernel
+constexpr int kMaxPeakBlocks = 65536;  // grids the read and gather ceilings accept
 
 // XOR of x over the block, stored by thread 0 at out[blockIdx.x] (a plain store per block:
 // no atomics on one shared word, which would serialise at one L2 channel).
@@ -117,9 +117,12 @@ __global__ __launch_bounds__(kPeakBlock) void peak_copy_kernel(const i32x4* __re
 }
 
 // Rows of 256 bytes: lane piece s = lane % 16 of row rows[r], four rows per load
-// instruction, 16 loads in flight per lane.  The table is read through a buffer resource
-// whose size bounds every access (an out-of-range row reads as zero).
-constexpr int kGatherInFlight = 16;
+// instruction, 8 loads in flight per lane (deeper queues measured slower from a 2 GiB table:
+// 16 in flight 5.0-5.1 TB/s, 32 in flight 4.2, against 6.3 for 2 to 8).  No non-temporal
+// hint: it costs 15 % when the table sits in the Infinity Cache (8.5 -> 7.3 TB/s from 64 MiB)
+// and gains 2.5 % from HBM.  The table is read through a buffer resource whose size bounds
+// every access (an out-of-range row reads as zero).
+constexpr int kGatherInFlight = 8;
 
 __global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const void* __restrict__ table,
                                                                  uint32_t table_bytes,
@@ -145,20 +148,37 @@ __global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const void* __r
   block_xor_store(x, out);
 }
 
-// Read-only stream: each lane reads 16-byte pieces, four loads in flight per step.
-__global__ __launch_bounds__(kPeakBlock) void peak_read_kernel(const i32x4* __restrict__ src,
-                                                               int64_t n, uint32_t* __restrict__ out) {
-  const int64_t stride = (int64_t)gridDim.x * kPeakBlock;
+// Read-only stream: 16-byte buffer loads, four in flight per lane; one load instruction of a
+// wave reads 1 KiB contiguous, and thread t reads pieces t, t + S, ... (S threads in the
+// grid).  The region goes in segments of at most 1 GiB, each behind its own buffer resource
+// (32-bit offsets).  Global loads of the same pattern measured 5.0-5.6 TB/s against 6.1-6.6
+// for these.  AUX: the loads' cache-policy operand (non-temporal for the ceiling; ordinary
+// loads, which fill the caches, to evict other data from them).
+constexpr int kReadInFlight = 4;
+constexpr int64_t kReadSegment = (int64_t)1 << 30;
+
+template <int AUX>
+__global__ __launch_bounds__(kPeakBlock) void peak_read_kernel(const unsigned char* __restrict__ src,
+                                                               int64_t bytes,
+                                                               uint32_t* __restrict__ out) {
+  const int64_t S = (int64_t)gridDim.x * kPeakBlock;
+  const int64_t t = (int64_t)blockIdx.x * kPeakBlock + threadIdx.x;
   uint32_t x = 0;
-  int64_t i = (int64_t)blockIdx.x * kPeakBlock + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const i32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    x ^= (uint32_t)(a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3]);
-    x ^= (uint32_t)(c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^ d[2] ^ d[3]);
-  }
-  for (; i < n; i += stride) {
-    const i32x4 a = src[i];
-    x ^= (uint32_t)(a[0] ^ a[1] ^ a[2] ^ a[3]);
+  for (int64_t seg = 0; seg < bytes; seg += kReadSegment) {
+    const int64_t sb = bytes - seg < kReadSegment ? bytes - seg : kReadSegment;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + seg, (uint32_t)sb);
+    const int64_t n16 = sb / 16;
+    for (int64_t i = t; i < n16; i += S * kReadInFlight) {
+      i32x4 v[kReadInFlight];
+#pragma unroll
+      for (int j = 0; j < kReadInFlight; ++j) {
+        const int64_t e = i + (int64_t)j * S;
+        const uint32_t off = e < n16 ? (uint32_t)(e * 16) : 0x80000000u;
+        v[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX));
+      }
+#pragma unroll
+      for (int j = 0; j < kReadInFlight; ++j) x ^= (uint32_t)(v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3]);
+    }
   }
   block_xor_store(x, out);
 }
@@ -345,27 +365,39 @@ ix_status ix_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t str
   return launched("ix_peak_copy");
 }
 
-ix_status ix_peak_read(const void* src, size_t bytes, uint32_t* out, hipStream_t stream) {
+ix_status ix_peak_read(const void* src, size_t bytes, int32_t blocks, int32_t nontemporal,
+                       uint32_t* out, hipStream_t stream) {
   using namespace ix;
   if (!src || !out) return peak_fail(IX_ERR_INVALID, "NULL src or out");
   if (bytes % 16 || !aligned16(src))
     return peak_fail(IX_ERR_INVALID, "bytes and src must be multiples of 16");
+  if (blocks < 1 || blocks > kMaxPeakBlocks)
+    return peak_fail(IX_ERR_INVALID, "blocks=%d (1..%d)", blocks, kMaxPeakBlocks);
+  if (nontemporal != 0 && nontemporal != 1)
+    return peak_fail(IX_ERR_INVALID, "nontemporal=%d (0 or 1)", nontemporal);
   if (bytes == 0) return IX_OK;
-  hipLaunchKernelGGL(peak_read_kernel, dim3(kReadBlocks), dim3(kPeakBlock), 0, stream,
-                     reinterpret_cast<const i32x4*>(src), (int64_t)(bytes / 16), out);
+  const unsigned char* s = reinterpret_cast<const unsigned char*>(src);
+  if (nontemporal)
+    hipLaunchKernelGGL(peak_read_kernel<kLoadNT>, dim3(blocks), dim3(kPeakBlock), 0, stream, s,
+                       (int64_t)bytes, out);
+  else
+    hipLaunchKernelGGL(peak_read_kernel<0>, dim3(blocks), dim3(kPeakBlock), 0, stream, s,
+                       (int64_t)bytes, out);
   return launched("ix_peak_read");
 }
 
 ix_status ix_peak_gather(const void* table, size_t table_bytes, const int32_t* rows, int64_t n,
-                         uint32_t* out, hipStream_t stream) {
+                         int32_t blocks, uint32_t* out, hipStream_t stream) {
   using namespace ix;
   if (!table || !rows || !out) return peak_fail(IX_ERR_INVALID, "NULL table, rows or out");
   if (n < 0) return peak_fail(IX_ERR_INVALID, "n=%lld must be >= 0", (long long)n);
+  if (blocks < 1 || blocks > kMaxPeakBlocks)
+    return peak_fail(IX_ERR_INVALID, "blocks=%d (1..%d)", blocks, kMaxPeakBlocks);
   if (table_bytes == 0 || table_bytes % 256 || table_bytes > ((size_t)1 << 31))
     return peak_fail(IX_ERR_INVALID, "table_bytes must be a positive multiple of 256, at most 2 GiB");
   if (!aligned16(table)) return peak_fail(IX_ERR_INVALID, "table must be 16-byte aligned");
   if (n == 0) return IX_OK;
-  hipLaunchKernelGGL(peak_gather_kernel, dim3(kGatherBlocks), dim3(kPeakBlock), 0, stream, table,
+  hipLaunchKernelGGL(peak_gather_kernel, dim3(blocks), dim3(kPeakBlock), 0, stream, table,
                      (uint32_t)table_bytes, rows, n, out);
   return launched("ix_peak_gather");
 }

@@ -32,9 +32,9 @@ def load(path: str = LIB_PATH):
     L.ix_peak_copy.restype = c_int32
     L.ix_peak_copy.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
     L.ix_peak_read.restype = c_int32
-    L.ix_peak_read.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+    L.ix_peak_read.argtypes = [c_void_p, c_size_t, c_int32, c_int32, c_void_p, c_void_p]
     L.ix_peak_gather.restype = c_int32
-    L.ix_peak_gather.argtypes = [c_void_p, c_size_t, c_void_p, c_int64, c_void_p, c_void_p]
+    L.ix_peak_gather.argtypes = [c_void_p, c_size_t, c_void_p, c_int64, c_int32, c_void_p, c_void_p]
     L.ix_peak_gather_selection.restype = c_int32
     L.ix_peak_gather_selection.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p] + [c_int32] * 8 + \
         [c_void_p, c_void_p]
@@ -57,12 +57,12 @@ def ix_peak_copy(src, dst, nbytes, stream=0):
     _check(load().ix_peak_copy(src, dst, nbytes, stream))
 
 
-def ix_peak_read(src, nbytes, out, stream=0):
-    _check(load().ix_peak_read(src, nbytes, out, stream))
+def ix_peak_read(src, nbytes, blocks, nontemporal, out, stream=0):
+    _check(load().ix_peak_read(src, nbytes, blocks, nontemporal, out, stream))
 
 
-def ix_peak_gather(table, table_bytes, rows, n, out, stream=0):
-    _check(load().ix_peak_gather(table, table_bytes, rows, n, out, stream))
+def ix_peak_gather(table, table_bytes, rows, n, blocks, out, stream=0):
+    _check(load().ix_peak_gather(table, table_bytes, rows, n, blocks, out, stream))
 
 
 def ix_peak_gather_selection(kc, vc, idx, kv_len, B, T, S_max, H_kv, d, k, splits, blocks_per_cu,

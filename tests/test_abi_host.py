@@ -377,13 +377,17 @@ def test_peak_validation_codes():
     assert status_of(pk.ix_peak_mfma_fp8, FAKE, 8, 0, 1, FAKE) == bd.IX_ERR_INVALID
     assert status_of(pk.ix_peak_copy, FAKE, FAKE, 24) == bd.IX_ERR_INVALID
     assert status_of(pk.ix_peak_copy, FAKE, FAKE, 0) == bd.IX_OK
-    assert status_of(pk.ix_peak_read, FAKE, 24, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(pk.ix_peak_read, 0, 32, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(pk.ix_peak_read, FAKE, 0, FAKE) == bd.IX_OK
-    assert status_of(pk.ix_peak_gather, FAKE, 1000, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(pk.ix_peak_gather, FAKE, 1 << 32, FAKE, 5, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, -1, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, 0, FAKE) == bd.IX_OK
+    assert status_of(pk.ix_peak_read, FAKE, 24, 1024, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, 0, 32, 1024, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, FAKE, 32, 0, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, FAKE, 32, 65537, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, FAKE, 32, 1024, 2, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_read, FAKE, 0, 1024, 1, FAKE) == bd.IX_OK
+    assert status_of(pk.ix_peak_gather, FAKE, 1000, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 1 << 32, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, -1, 2048, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, 5, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, 0, 2048, FAKE) == bd.IX_OK
     sel = pk.ix_peak_gather_selection
     assert status_of(sel, FAKE, FAKE, 0, FAKE, 1, 4, 100, 1, 128, 64, 1, 0, FAKE) == bd.IX_ERR_INVALID
     assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, 1, 96, 64, 1, 0, FAKE) == bd.IX_ERR_UNSUPPORTED

@@ -22,14 +22,15 @@ def test_peak_copy_exact():
     assert torch.equal(src, dst)
 
 
-def test_peak_gather_checksum():
-    say("[ix_peak_gather] 4096 rows of 256 B, 100003 gathers with out-of-range rows")
+@pytest.mark.parametrize("blocks", [1000, 4096])
+def test_peak_gather_checksum(blocks):
+    say(f"[ix_peak_gather] 4096 rows of 256 B, 100003 gathers with out-of-range rows, {blocks} blocks")
     g = torch.Generator().manual_seed(5)
     table = torch.randint(-2**31, 2**31 - 1, (4096 * 64,), generator=g, dtype=torch.int32)
     rows = torch.randint(-5, 4096 + 5, (100003,), generator=g, dtype=torch.int32)
-    out = torch.zeros(2048, dtype=torch.int32, device=DEV)
+    out = torch.zeros(blocks, dtype=torch.int32, device=DEV)
     table_d, rows_d = table.to(DEV), rows.to(DEV)   # kept alive until the kernel has run
-    pk.ix_peak_gather(table_d.data_ptr(), 4096 * 256, rows_d.data_ptr(), rows.numel(),
+    pk.ix_peak_gather(table_d.data_ptr(), 4096 * 256, rows_d.data_ptr(), rows.numel(), blocks,
                       out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     t = table.numpy().view(np.uint32).reshape(4096, 64)
@@ -67,14 +68,17 @@ def test_peak_atomic_add_counts():
     assert np.array_equal(got, np.repeat(want[:, None], 128, axis=1))
 
 
-def test_peak_read_checksum():
-    say("[ix_peak_read] 5 MiB + 32 bytes")
+@pytest.mark.parametrize("n,blocks,nt", [(5 * (1 << 20) + 32, 777, 1), (5 * (1 << 20) + 32, 4096, 0),
+                                         ((1 << 30) + 48, 1024, 1)])
+def test_peak_read_checksum(n, blocks, nt):
+    """The last case crosses the 1 GiB segment boundary of the kernel's buffer resources."""
+    say(f"[ix_peak_read] {n} bytes, {blocks} blocks, nontemporal {nt}")
     g = torch.Generator().manual_seed(6)
-    n = 5 * (1 << 20) + 32
     src = torch.randint(-2**31, 2**31 - 1, (n // 4,), generator=g, dtype=torch.int32)
-    out = torch.zeros(4096, dtype=torch.int32, device=DEV)
+    out = torch.zeros(blocks, dtype=torch.int32, device=DEV)
     src_d = src.to(DEV)
-    pk.ix_peak_read(src_d.data_ptr(), n, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    pk.ix_peak_read(src_d.data_ptr(), n, blocks, nt, out.data_ptr(),
+                    torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
     assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
