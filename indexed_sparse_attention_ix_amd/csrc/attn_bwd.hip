@@ -33,12 +33,6 @@ struct AttnBwdArgs {
   void* contrib;      // non-null: per-pair dV | dK rows instead of atomics
 };
 
-// bf16 16x16x16: D += A(16x16) * B(16x16); lane l supplies A[l & 15][4(l>>4) .. +3] and
-// B[4(l>>4) .. +3][l & 15].
-__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __builtin_bit_cast(float, (uint32_t)v << 16);
 }

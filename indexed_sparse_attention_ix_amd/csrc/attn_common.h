@@ -51,6 +51,12 @@ __device__ __forceinline__ float sum_across_rows(float v) {
   return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
 }
 
+// bf16 16x16x16: D += A(16x16) * B(16x16); lane l supplies A[l & 15][4(l>>4) .. +3] and
+// B[4(l>>4) .. +3][l & 15].
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // Transposing LDS read: within each 16-lane group, lane i receives element (i & 3) of
 // the 8-byte reads of lanes 4r + (i >> 2), r = 0..3.
 __device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char* p) {

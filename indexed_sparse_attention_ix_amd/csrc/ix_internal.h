@@ -34,7 +34,8 @@ TopkPlan make_topk_plan(const ix_indexer_args& a, int k);
 struct AttnPlan {
   int layers;       // layers per launch: up to 8 share one grid when one layer's grid is small
   int n_splits;     // blocks per (query, kv head); >1 writes partials then combines
-  int chunks;       // ceil(k / 32)
+  bool light;       // the light kernel (16-row chunks, many waves per CU) for small grids
+  int chunks;       // ceil(k / 32), or ceil(k / 16) for the light kernel
   int chunks_per_split;
   size_t part_bytes;  // split partials of one layer of a launch (0 without splits)
   size_t ws_bytes;    // layers * part_bytes

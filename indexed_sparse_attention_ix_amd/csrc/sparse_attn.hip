@@ -65,6 +65,64 @@ __device__ __forceinline__ T pick_layer(T const (&a)[kAttnMaxLayers], int layer)
   return v;
 }
 
+// End of a block: the four waves' (m, l, O^T) merged through LDS (wave w's O^T staged at
+// lds + w * wave_bytes as [head][d] floats; ml: each wave's per-head m and l), then the
+// normalised output and lse, or with splits this block's normalised partial and its lse.
+template <int D, bool ML>
+__device__ __forceinline__ void finish_block(const AttnArgs& p, int layer, int64_t rk, int kvh,
+                                             int64_t row, int split, const f32x4 (&o)[D / 16],
+                                             float m_run, float l_run, unsigned char* lds,
+                                             size_t wave_bytes, float (*ml)[2][16]) {
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  // per-head l: sum the four lane groups' shares
+  l_run = sum_across_rows(l_run);
+  __syncthreads();
+  float* os = reinterpret_cast<float*>(lds + wid * wave_bytes);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) os[r16 * D + 16 * nt + 4 * lg + i] = o[nt][i];
+  if (lg == 0) {
+    ml[wid][0][r16] = m_run;
+    ml[wid][1][r16] = l_run;
+  }
+  __syncthreads();
+
+  const float ln2 = 0.69314718055994530942f;
+  for (int e = threadIdx.x; e < 16 * D; e += kAttnBlock) {
+    const int h = e / D, dcol = e % D;
+    if (h >= p.grp) continue;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml[w][0][h]);
+    float L = 0.f, acc = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = ml[w][0][h];
+        const float f = mw == -__builtin_inff() ? 0.f : exp2f(mw - M);
+        L += f * ml[w][1][h];
+        acc += f * reinterpret_cast<const float*>(lds + w * wave_bytes)[h * D + dcol];
+      }
+    }
+    const float val = L > 0.f ? acc / L : 0.f;
+    const float lse_v = L > 0.f ? (M + log2f(L)) * ln2 : -__builtin_inff();
+    const int head = kvh * p.grp + h;
+    if (p.n_splits == 1) {
+      pick_layer(p.out, layer)[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(val);
+      float* const lse_l = pick_layer(p.lse, layer);
+      if (lse_l && dcol == 0) lse_l[(size_t)row * p.H_q + head] = lse_v;
+    } else {
+      const size_t pr = (size_t)rk * p.n_splits + split;
+      pick_layer(p.part_o, layer)[(pr * 16 + h) * D + dcol] = val;
+      if (dcol == 0) pick_layer(p.part_lse, layer)[pr * 16 + h] = lse_v;
+    }
+  }
+}
+
 // ML: the grid covers several layers (p.layers > 1); a single-layer launch reads entry 0
 // of the pointer arrays directly.
 template <int D, bool ML>
@@ -284,53 +342,186 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     if (c + W < c_end) step(c + W, kdB, vdB, maskB);
   }
 
-  // per-head l: sum the four lane groups' shares
-  l_run = sum_across_rows(l_run);
+  finish_block<D, ML>(p, layer, rk, kvh, row, split, o, m_run, l_run, &stage_all[0][0][0],
+                      sizeof(stage_all[0]), ml_all);
+}
 
-  // merge the 4 waves through LDS: os[head][d]
-  __syncthreads();
-  float* os = reinterpret_cast<float*>(kst);
-  static_assert(16 * D * sizeof(float) <= 2 * kChunk * ROWB, "O staging");
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) os[r16 * D + 16 * nt + 4 * lg + i] = o[nt][i];
-  if (lg == 0) {
-    ml_all[wid][0][r16] = m_run;
-    ml_all[wid][1][r16] = l_run;
-  }
-  __syncthreads();
+// Launches of few query rows (decode) gather from HBM, and scattered row gathers run at a
+// rate set by the waves each CU holds (4 waves per CU gather at about a third of what 16 do,
+// whatever the loads in flight per wave).  The kernel above holds at most 8 waves per CU: two
+// register sets of chunk rows (248-256 VGPRs) and 64 KiB of LDS per block.  This variant keeps
+// its math but takes 16-row chunks, loads each K row straight into the MFMA operand registers
+// (lane (g, r) reads row r's 16-byte pieces 4m + g, the A-operand layout of S^T = K Q^T; no
+// LDS), stages only V (4 KiB per wave at d = 128) for the transposing read of O^T += V^T P^T
+// (bf16 16x16x16).  Each wave keeps the rows of its next two chunks in registers, as the
+// kernel above does, so their gathers overlap a chunk's arithmetic: 32 KiB of LDS per block and
+// few enough registers for three blocks, 12 waves, per CU.  The launch splits each selection
+// over as many blocks as make about two per CU.
+constexpr int kLightChunk = 16;
 
-  const float ln2 = 0.69314718055994530942f;
-  for (int e = threadIdx.x; e < 16 * D; e += kAttnBlock) {
-    const int h = e / D, dcol = e % D;
-    if (h >= p.grp) continue;
-    float M = -__builtin_inff();
+template <int D, bool ML>
+__global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnArgs p) {
+  constexpr int MC = D / 32;               // depth tiles of the QK^T product
+  constexpr int NT = D / 16;               // 16-row tiles of O^T
+  constexpr int ROWB = D * 2;              // bytes per K or V row
+  constexpr int PI = ROWB / 16;            // 16-byte pieces per row
+  constexpr int RPI = kWave / PI;          // rows per 64-lane load
+  constexpr int NIV = kLightChunk / RPI;   // V loads per chunk per lane
+  constexpr int WAVE_LDS = 16 * D * 4;     // per wave: the V stage, then O^T for the merge
+  static_assert(kLightChunk * ROWB <= WAVE_LDS, "V stage");
+  __shared__ __attribute__((aligned(16))) unsigned char lds_all[kAttnWaves][WAVE_LDS];
+  __shared__ float ml_all[kAttnWaves][2][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, lg = lane >> 4;
+  unsigned bid = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
+  const int layer = ML ? (int)(bid / p.blocks_per_layer) : 0;
+  if (ML) bid -= (unsigned)layer * p.blocks_per_layer;
+  const uint16_t* const q_l = pick_layer(p.q, layer);
+  const uint16_t* const kc_l = pick_layer(p.kc, layer);
+  const uint16_t* const vc_l = pick_layer(p.vc, layer);
+  const int split = bid % p.n_splits;
+  const int64_t rk = bid / p.n_splits;  // (b*T + t) * H_kv + kvh
+  const int kvh = (int)(rk % p.H_kv);
+  const int64_t row = rk / p.H_kv;      // b*T + t
+  const int b = (int)(row / p.T);
+  int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
+  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+
+  // Q as the B operand of S^T = K Q^T: column = head, depth slice [32m + 8lg, +8)
+  bf16x8 qb[MC];
+  const bool hvalid = r16 < p.grp;
+  {
+    const int head = kvh * p.grp + (hvalid ? r16 : 0);
+    const uint16_t* qrow = q_l + ((size_t)row * p.H_q + head) * D;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml_all[w][0][h]);
-    float L = 0.f, acc = 0.f;
-    if (M != -__builtin_inff()) {
-#pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = ml_all[w][0][h];
-        const float f = mw == -__builtin_inff() ? 0.f : exp2f(mw - M);
-        L += f * ml_all[w][1][h];
-        acc += f * reinterpret_cast<const float*>(stage_all[w][0])[h * D + dcol];
-      }
-    }
-    const float val = L > 0.f ? acc / L : 0.f;
-    const float lse_v = L > 0.f ? (M + log2f(L)) * ln2 : -__builtin_inff();
-    const int head = kvh * p.grp + h;
-    if (p.n_splits == 1) {
-      pick_layer(p.out, layer)[((size_t)row * p.H_q + head) * D + dcol] = f32_to_bf16_rne(val);
-      float* const lse_l = pick_layer(p.lse, layer);
-      if (lse_l && dcol == 0) lse_l[(size_t)row * p.H_q + head] = lse_v;
-    } else {
-      const size_t pr = (size_t)rk * p.n_splits + split;
-      pick_layer(p.part_o, layer)[(pr * 16 + h) * D + dcol] = val;
-      if (dcol == 0) pick_layer(p.part_lse, layer)[pr * 16 + h] = lse_v;
+    for (int m = 0; m < MC; ++m) {
+      qb[m] = load_bf16x8(qrow + 32 * m + 8 * lg);
+      if (!hvalid) qb[m] = (bf16x8){};
     }
   }
+
+  const int32_t* irow = p.idx + (size_t)row * p.k;
+  const uint32_t kv_stride_b = (uint32_t)(p.H_kv * ROWB);
+  const size_t seq_off = ((size_t)b * p.S_max * p.H_kv + kvh) * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc_l + seq_off, (uint32_t)kvl * kv_stride_b);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc_l + seq_off, (uint32_t)kvl * kv_stride_b);
+  unsigned char* vst = lds_all[wid];
+
+  // V stage: lane (rho, s) of load j fetches piece s of slot n = rho * NIV + j
+  const int rho = lane / PI, s = lane % PI;
+  uint32_t woff[NIV];
+#pragma unroll
+  for (int j = 0; j < NIV; ++j) {
+    const int n = rho * NIV + j;
+    woff[j] = (uint32_t)(n * ROWB + 16 * (s ^ stage_swz<D>(n)));
+  }
+  // transposed V read: slot 4lg + r16/4, logical bytes [32nt + 8(r16 & 3), +8)
+  uint32_t voff[NT];
+  {
+    const int n = 4 * lg + (r16 >> 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      voff[nt] = (uint32_t)(n * ROWB + 16 * ((2 * nt + ((r16 >> 1) & 1)) ^ stage_swz<D>(n)) + 8 * (r16 & 1));
+  }
+
+  float m_run = -__builtin_inff();  // running max of head r16 (log2 domain)
+  float l_run = 0.f;                // this lane's share of the running sum
+  f32x4 o[NT];                      // O^T: rows 16nt + 4lg + i (d), column r16 (head)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int c_begin = split * p.chunks_per_split;
+  const int c_end = min(c_begin + p.chunks_per_split, p.chunks);
+  // entry r16 of chunk c (the same in the four lane groups), -1 if padding or not visible
+  auto key_of = [&](int c) -> int {
+    const int e = c * kLightChunk + r16;
+    const int j = (c < c_end && e < p.k) ? irow[e] : -1;
+    return (j >= 0 && j < kvl) ? j : -1;
+  };
+  // one chunk in registers: its K rows as A operands (lane: row r16, pieces 4m + lg), its V
+  // rows for the stage, and which of its 16 keys are valid
+  struct Rows {
+    bf16x8 ka[MC];
+    i32x4 vd[NIV];
+    uint32_t mask;
+  };
+  auto issue = [&](int jk, Rows& r) {
+    const uint32_t kbase = jk >= 0 ? (uint32_t)jk * kv_stride_b + 16u * lg : 0x80000000u;
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+      r.ka[m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(kbase + 64u * m), 0, 0));
+#pragma unroll
+    for (int j = 0; j < NIV; ++j) {
+      const int jv = __shfl(jk, rho * NIV + j);
+      const uint32_t off = jv >= 0 ? (uint32_t)jv * kv_stride_b + 16u * s : 0x80000000u;
+      r.vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+    }
+    r.mask = (uint32_t)ballot64(jk >= 0) & 0xFFFFu;  // lanes 0..15 hold keys 0..15
+  };
+
+  constexpr int W = kAttnWaves;
+  const int c0 = c_begin + wid;
+  Rows rA, rB;
+  issue(key_of(c0), rA);
+  issue(key_of(c0 + W), rB);
+  int jnext = key_of(c0 + 2 * W);
+
+  // chunk c, whose rows are in r: S^T from the K operands, V staged, then r refilled with
+  // chunk c + 2W (its gathers in flight during this chunk's softmax and O^T update)
+  auto step = [&](int c, Rows& r) __attribute__((always_inline)) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < MC; ++m) s0 = mfma_bf16_16x16x32(r.ka[m], qb[m], s0);
+#pragma unroll
+    for (int j = 0; j < NIV; ++j) *reinterpret_cast<i32x4*>(vst + woff[j]) = r.vd[j];
+    const uint32_t vmask = r.mask;
+    if (c + 2 * W < c_end) {
+      issue(jnext, r);
+      jnext = key_of(c + 3 * W);
+    }
+    lds_wait();
+
+    float x[4];
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = (vmask >> (4 * lg + i)) & 1u;
+      x[i] = ok ? s0[i] * p.scale_log2 : -__builtin_inff();
+      mloc = fmaxf(mloc, x[i]);
+    }
+    mloc = max_across_rows(mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    const bool any = m_new != -__builtin_inff();
+    const float alpha = (any && m_run != -__builtin_inff()) ? exp2f(m_run - m_new) : (any ? 0.f : 1.f);
+    i16x4 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pr = (x[i] != -__builtin_inff()) ? exp2f(x[i] - m_new) : 0.f;
+      psum += pr;
+      pb[i] = (short)f32_to_bf16_rne(pr);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // O^T += V^T P^T: P^T (keys 4lg..4lg+3 of head r16) is the B operand as the lane holds it
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nt][i] *= alpha;
+      o[nt] = mfma_bf16_16x16x16(lds_read_tr16(vst + voff[nt]), pb, o[nt]);
+    }
+    lds_wait();  // the stage is rewritten by the next chunk
+  };
+  for (int c = c0; c < c_end; c += 2 * W) {
+    step(c, rA);
+    if (c + W < c_end) step(c + W, rB);
+  }
+
+  finish_block<D, ML>(p, layer, rk, kvh, row, split, o, m_run, l_run, &lds_all[0][0],
+                      sizeof(lds_all[0]), ml_all);
 }
 
 // Merge of split partials: out = sum_s exp(lse_s - LSE) o_s, LSE = log sum_s exp(lse_s).
@@ -371,12 +562,15 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, in
 
 }  // namespace
 
-// Grids of fewer than 1024 blocks per layer (decode) are latency- and miss-bound: one launch
-// then serves up to 8 layers, and each selection is split over as many blocks as make the
-// launch about one block per CU (256), with at least two chunks per wave.  Measured on the
-// 64-sequence decode step with the caches cold: 4 layers at 1 block per query take 16 us per
-// layer (8 per query: 20 us; 16: 39 us), one layer is fastest at 4 per query (29 us; 8: 31 us).
-// More blocks put more row requests in flight at once than the memory system serves well.
+// Grids of fewer than 1024 blocks per layer (decode) gather from HBM and are miss-bound: one
+// launch then serves up to 8 layers, and each selection is split over several blocks.  A
+// launch of several layers takes the light kernel, split so that the launch holds about 512
+// blocks; one layer takes the kernel above, split to about one block per CU (256).  Each wave
+// gets at least two chunks.  Measured on the 64-sequence decode step with the caches cold:
+// the 4 layers in one launch take 15.9-16.1 us per layer with the light kernel at 2 blocks per
+// query (1, 3, 4 and 8 blocks: 18.2, 16.3, 18.1 and 20.0 us), 17.0-17.4 us with the kernel
+// above at 1 block per query; one layer is fastest with the kernel above at 4 blocks per query
+// (28.8-29.0 us; the light kernel 29.9-35 us).
 AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k, int n_layers) {
   (void)H_q;
   AttnPlan p{};
@@ -384,10 +578,14 @@ AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k, int n_lay
   const int64_t base = (int64_t)B * T * H_kv;
   int ns = 1;
   p.layers = 1;
+  p.light = false;
   if (base > 0 && base < 1024) {
     p.layers = n_layers < kAttnMaxLayers ? (n_layers < 1 ? 1 : n_layers) : kAttnMaxLayers;
+    p.light = p.layers > 1;
+    if (p.light) p.chunks = (k + kLightChunk - 1) / kLightChunk;
     const int64_t grid = base * p.layers;
-    int64_t want = (256 + grid / 2) / grid;
+    const int64_t target = p.light ? 512 : 256;
+    int64_t want = (target + grid / 2) / grid;
     int64_t by_chunks = p.chunks / (2 * kAttnWaves);
     if (by_chunks < 1) by_chunks = 1;
     if (want < 1) want = 1;
@@ -454,8 +652,13 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
     const size_t per_layer = (size_t)B * T * H_kv * pl.n_splits;
     x.blocks_per_layer = (unsigned)per_layer;
     const dim3 grid((unsigned)(per_layer * nl));
-    auto* kern = d == 128 ? (nl > 1 ? &sparse_attn_kernel<128, true> : &sparse_attn_kernel<128, false>)
-                          : (nl > 1 ? &sparse_attn_kernel<64, true> : &sparse_attn_kernel<64, false>);
+    auto* kern =
+        pl.light
+            ? (d == 128 ? (nl > 1 ? &sparse_attn_light_kernel<128, true> : &sparse_attn_light_kernel<128, false>)
+                        : (nl > 1 ? &sparse_attn_light_kernel<64, true> : &sparse_attn_light_kernel<64, false>))
+            : (d == 128 ? (nl > 1 ? &sparse_attn_kernel<128, true> : &sparse_attn_kernel<128, false>)
+                        : (nl > 1 ? &sparse_attn_kernel<64, true> : &sparse_attn_kernel<64, false>));
+    // (a launch of the light kernel may hold a single layer: the last of a group of 9 or more)
     hipLaunchKernelGGL(kern, grid, dim3(kAttnBlock), 0, stream, x);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -24,12 +24,25 @@ def _group_case(**kw):
     return Workload(**base)
 
 
+def _close_to_standalone(o, lse, o2, l2, k, where):
+    """A layer's output from a launch that splits the selection differently from the
+    standalone call's: each split rounds P to bf16 against its own running maximum, so the
+    two differ by bf16 roundings of the terms (random in sign, so per (row, head) in norm
+    within 2^-5 of the output), and lse by fp32 sums of the k weights in another order
+    ((k + 64) 2^-23)."""
+    a, b = o.double(), o2.double()
+    num, den = (a - b).norm(dim=-1), b.norm(dim=-1)
+    assert bool((num <= 2.0 ** -5 * den + 1e-7).all()), \
+        f"{where}: worst relative difference {float((num / den.clamp(min=1e-30)).max()):.3e}"
+    fin = torch.isfinite(l2)
+    assert torch.equal(fin, torch.isfinite(lse))
+    assert bool(((lse - l2).abs()[fin] <= (k + 64) * 2.0 ** -23 * (1 + l2.abs()[fin])).all()), \
+        f"{where} lse"
+
+
 def _same_as_group_attention(layers, idx, kv_len, sm_scale, outs, lses):
     """The group's outputs are sparse_attn_group_fwd's on the same selection, bit for bit,
-    and each layer's standalone sparse_attn_fwd's up to a different split of the selection:
-    each split rounds P to bf16 against its own running maximum, so the two differ by bf16
-    roundings of the terms (random in sign, so per (row, head) in norm within 2^-5 of the
-    output) and lse by fp32 sums of the k weights in another order ((k + 64) 2^-23)."""
+    and each layer's standalone sparse_attn_fwd's up to a different split of the selection."""
     go, gl = bd.group_attention([dict(q=L["q"], K=L["K"], V=L["V"]) for L in layers], idx,
                                 sm_scale, kv_len=kv_len, with_lse=True)
     k = idx.shape[-1]
@@ -37,22 +50,19 @@ def _same_as_group_attention(layers, idx, kv_len, sm_scale, outs, lses):
         assert torch.equal(outs[l], go[l]) and torch.equal(lses[l], gl[l]), f"layer {l}"
         o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, sm_scale, kv_len=kv_len,
                                      with_lse=True)
-        a, b = outs[l].double(), o2.double()
-        num, den = (a - b).norm(dim=-1), b.norm(dim=-1)
-        assert bool((num <= 2.0 ** -5 * den + 1e-7).all()), \
-            f"layer {l}: worst relative difference {float((num / den.clamp(min=1e-30)).max()):.3e}"
-        fin = torch.isfinite(l2)
-        assert torch.equal(fin, torch.isfinite(lses[l]))
-        assert bool(((lses[l] - l2).abs()[fin] <= (k + 64) * 2.0 ** -23 * (1 + l2.abs()[fin])).all()), \
-            f"layer {l} lse"
+        _close_to_standalone(outs[l], lses[l], o2, l2, k, f"layer {l}")
 
 
 def test_group_attention_entry_point_against_standalone_and_oracle():
-    """sparse_attn_group_fwd on a caller's selection: a ragged prefill (one launch per layer,
-    the same split as standalone calls: bit for bit) and a decode batch (layers in one
-    launch), against the oracle."""
-    for case in (dict(B=2, T=150, S=3000, pos0s=(2850, 1000), kv_lens=(3000, 2500), k=256,
+    """sparse_attn_group_fwd on a caller's selection, against standalone calls and the oracle:
+    a ragged prefill of 1200 query rows (one launch per layer with the standalone call's
+    split: bit for bit), and two small batches whose layers share one launch of the light
+    kernel (a standalone call runs the other kernel: within the split-rounding bound): 300
+    ragged query rows, and a decode batch."""
+    for case in (dict(B=2, T=600, S=3000, pos0s=(2400, 1000), kv_lens=(3000, 2500), k=256,
                       layers=3, seed=45),
+                 dict(B=2, T=150, S=3000, pos0s=(2850, 1000), kv_lens=(3000, 2500), k=256,
+                      layers=3, seed=47),
                  dict(B=8, T=1, S=9000, pos0=8999, pos0s=None, kv_lens=None, k=2048, layers=3,
                       seed=46, planted=16)):
         wl = _group_case(**case)
@@ -66,8 +76,10 @@ def test_group_attention_entry_point_against_standalone_and_oracle():
         for l, L in enumerate(layers):
             o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
                                          kv_len=ind["kv_len"], with_lse=True)
-            if wl.T > 1:
+            if wl.B * wl.T >= 1024:
                 assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2), f"layer {l}"
+            else:
+                _close_to_standalone(outs[l], lses[l], o2, l2, wl.k, f"layer {l}")
         torch.cuda.synchronize()
         h = to_host_indexer(ind)
         idx_np = idx.cpu().numpy()
@@ -86,7 +98,7 @@ def test_group_attention_entry_point_against_standalone_and_oracle():
                                 where=f"layer={l} b={b}")
 
 
-def test_group_matches_standalone_calls_bitwise_and_oracle():
+def test_group_matches_standalone_calls_and_oracle():
     wl = _group_case()
     say(f"[indexshare_group_fwd] B={wl.B} T={wl.T} S={wl.S} k={wl.k} layers={wl.layers}")
     ind = synth.indexer_inputs(wl, device=DEV)
@@ -95,13 +107,12 @@ def test_group_matches_standalone_calls_bitwise_and_oracle():
     idx, outs, lses = bd.indexshare_group(*args, wl.k, [dict(q=L["q"], K=L["K"], V=L["V"])
                                                         for L in layers], wl.sm_scale,
                                           with_lse=True)
-    # the same selection as a standalone ix_topk, the same outputs as standalone attention
+    # the same selection as a standalone ix_topk, the same outputs as standalone attention (300
+    # query rows: the group's layers share the light kernel's launch, a standalone call runs
+    # the other kernel, so within the split-rounding bound; bit for bit in the group attention)
     idx2 = bd.topk(*args, wl.k)
     assert torch.equal(idx, idx2)
-    for l, L in enumerate(layers):
-        o2, l2 = bd.sparse_attention(L["q"], L["K"], L["V"], idx, wl.sm_scale,
-                                     kv_len=ind["kv_len"], with_lse=True)
-        assert torch.equal(outs[l], o2) and torch.equal(lses[l], l2)
+    _same_as_group_attention(layers, idx, ind["kv_len"], wl.sm_scale, outs, lses)
     torch.cuda.synchronize()
     # and against the oracle: its own selection from the group's indexer, attention per layer
     h = to_host_indexer(ind)
