@@ -691,3 +691,27 @@ ix_status ix_debug_read(ix_debug_status* status, int32_t reset, hipStream_t stre
 }
 
 }  // extern "C"
+
+#ifdef IX_TEST_HOOKS
+// Test build only: the launch plans, for host tests of their invariants (no GPU needed).
+// out[]: the plan's fields in the order listed; returns the number written.
+extern "C" __attribute__((visibility("default"))) int32_t ix_test_attn_plan(
+    int32_t B, int32_t T, int32_t H_q, int32_t H_kv, int32_t d, int32_t k, int32_t n_layers,
+    int64_t* out) {
+  const ix::AttnPlan p = ix::make_attn_plan(B, T, H_q, H_kv, d, k, n_layers);
+  const int64_t v[] = {p.layers, p.n_splits, p.light ? 1 : 0, p.chunks, p.chunks_per_split,
+                       (int64_t)p.part_bytes, (int64_t)p.ws_bytes};
+  for (int i = 0; i < 7; ++i) out[i] = v[i];
+  return 7;
+}
+
+extern "C" __attribute__((visibility("default"))) int32_t ix_test_topk_plan(
+    const ix_indexer_args* a, int32_t k, int64_t* out) {
+  const ix::TopkPlan p = ix::make_topk_plan(*a, k);
+  const int64_t v[] = {p.qc, p.hc, p.g, p.gmax, p.qgroups, p.n_splits, p.split_len, p.cap,
+                       p.ksplit, p.fb_cap, p.samp_tiles, p.fb_samp_tiles, p.units,
+                       (int64_t)p.ws_bytes};
+  for (int i = 0; i < 14; ++i) out[i] = v[i];
+  return 14;
+}
+#endif

@@ -1,5 +1,6 @@
 """The C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer: the ABI tests
-(test_abi_host.py) and the launch-failure tests (test_abi_hooks.py) run in a child Python
+(test_abi_host.py), the launch-failure tests (test_abi_hooks.py) and the launch-plan
+invariants (test_plans_host.py) run in a child Python
 against a host-only build of the library with both sanitizers and the test hook
 (build.build_check), with the sanitizer runtime preloaded.  Any sanitizer report aborts the
 child, which fails this test."""
@@ -22,7 +23,8 @@ def test_abi_tests_pass_under_asan_and_ubsan():
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1:halt_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
-                        "tests/test_abi_host.py", "tests/test_abi_hooks.py"],
+                        "tests/test_abi_host.py", "tests/test_abi_hooks.py",
+                        "tests/test_plans_host.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
     assert r.returncode == 0, out[-4000:]
