@@ -284,11 +284,12 @@ size_t sparse_attn_group_workspace_bytes(int32_t B, int32_t T, int32_t H_q, int3
  * with the selection computed by the caller (ix_topk, ix_topk_pooled or any other): layer l
  * gets what sparse_attn_fwd gives for q[l], kc[l], vc[l], out[l], lse[l] and the shared idx.
  * When one layer's grid is small (decode: B * T * H_kv < 1024 query rows) up to 8 layers
- * share one launch of a kernel made for few query rows (16-row chunks, more waves per CU),
- * and each selection is then split over as many blocks as make the launch about two blocks
- * per CU; a layer's output equals sparse_attn_fwd's up to the rounding of P to bf16 against
- * other running maxima and of the merge of those splits.  With 1024 query rows or more each
- * layer runs as sparse_attn_fwd does, bit for bit.
+ * share one launch of the kernel made for few query rows that sparse_attn_fwd also uses
+ * there (16-row chunks, K rows loaded straight into the matrix-core operands), and each
+ * selection is split over as many blocks as make the launch about one block per CU, so over
+ * fewer blocks than in a single-layer call; a layer's output then equals sparse_attn_fwd's up
+ * to the rounding of P to bf16 against other running maxima and of the merge of the splits.
+ * With 1024 query rows or more each layer runs as sparse_attn_fwd does, bit for bit.
  * q, kc, vc, out: HOST arrays of n_layers device pointers (shapes as in sparse_attn_fwd).
  * lse: nullable host array of n_layers nullable device pointers.
  * idx, kv_len, B..sm_scale: shared by the layers, as in sparse_attn_fwd.

@@ -19,12 +19,12 @@
 //    V^T operands are read with the gfx950 transposing LDS read (each lane receives
 //    four keys of one column), so output lane (g, h) holds head h and the per-head
 //    rescale stays in-lane.
-// The four waves' (m, l, O) are merged through LDS at the end.  Small batches split
-// the selection over several blocks and merge the normalised partials by lse; when one
-// layer's grid is that small, the layers of an IndexShare group share one launch (each
-// block serves one layer; the split count follows the launch's total grid, so a layer's
-// result equals the single-layer call's up to the rounding of the partials' merge, and
-// bit for bit when both use the same split count).
+// The four waves' (m, l, O) are merged through LDS at the end.  Small batches (decode) take
+// a lighter variant of the kernel, may split the selection over several blocks and merge the
+// normalised partials by lse; when one layer's grid is that small, the layers of an
+// IndexShare group share one launch (each block serves one layer; the split count follows the
+// launch's total grid, so a layer's result equals the single-layer call's up to the rounding
+// of the partials' merge, and bit for bit when both use the same split count).
 #include <algorithm>
 
 #include "attn_common.h"
@@ -135,6 +135,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   constexpr int NI = kChunk / RPI;    // loads per chunk per tensor
   __shared__ __attribute__((aligned(16))) unsigned char stage_all[kAttnWaves][2][kChunk * ROWB];
   __shared__ float ml_all[kAttnWaves][2][16];
+  __shared__ bf16x8 q_lds[MC][kWave];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   // queries (which tend to select overlapping keys) share one L2.
   unsigned bid = blockIdx.x;
   if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
-  const int layer = ML ? (int)(bid / p.blocks_per_layer) : 0;
+  const int layer = ML ? __builtin_amdgcn_readfirstlane((int)(bid / p.blocks_per_layer)) : 0;
   if (ML) bid -= (unsigned)layer * p.blocks_per_layer;
   const uint16_t* const q_l = pick_layer(p.q, layer);
   const uint16_t* const kc_l = pick_layer(p.kc, layer);
@@ -155,20 +156,21 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   const int64_t row = rk / p.H_kv;      // b*T + t
   const int b = (int)(row / p.T);
   int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
-  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+  // uniform: the buffer bounds built on it stay in scalar registers
+  kvl = __builtin_amdgcn_readfirstlane(kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl));
 
-  // Q as the B operand of S^T = K Q^T: column = head, depth slice [32m + 8lg, +8)
-  bf16x8 qb[MC];
+  // Q as the B operand of S^T = K Q^T: column = head, depth slice [32m + 8lg, +8).  The four
+  // waves use the same operands: wave 0 stages them in LDS, in lane order, and every chunk
+  // reads them from there (registers hold the rows in flight instead).
   const bool hvalid = r16 < p.grp;
-  {
+  if (wid == 0) {
     const int head = kvh * p.grp + (hvalid ? r16 : 0);
     const uint16_t* qrow = q_l + ((size_t)row * p.H_q + head) * D;
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      qb[m] = load_bf16x8(qrow + 32 * m + 8 * lg);
-      if (!hvalid) qb[m] = (bf16x8){};
-    }
+    for (int m = 0; m < MC; ++m)
+      q_lds[m][lane] = hvalid ? load_bf16x8(qrow + 32 * m + 8 * lg) : (bf16x8){};
   }
+  __syncthreads();
 
   const int32_t* irow = p.idx + (size_t)row * p.k;
   const uint32_t kv_stride_b = (uint32_t)(p.H_kv * ROWB);
@@ -208,74 +210,57 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
 
   const int c_begin = split * p.chunks_per_split;
   const int c_end = min(c_begin + p.chunks_per_split, p.chunks);
-  const bool idx_vec = (p.k & 3) == 0;
 
-  // Selected positions of this lane's NI slots of chunk c (-1: padding or not visible).
-  auto load_idx = [&](int c, int (&jv)[NI]) {
-    const int e0 = c * kChunk + rho * NI;
-    if (c >= c_end) {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) jv[j] = -1;
-    } else if (idx_vec && c * kChunk + kChunk <= p.k) {
-#pragma unroll
-      for (int j = 0; j < NI; j += 4) {
-        const i32x4 v = ld_global_16(irow + e0 + j);
-        jv[j] = v[0]; jv[j + 1] = v[1]; jv[j + 2] = v[2]; jv[j + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) jv[j] = e0 + j < p.k ? irow[e0 + j] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j) jv[j] = (jv[j] >= 0 && jv[j] < kvl) ? jv[j] : -1;
+  // Entry e_lane of chunk c as stored (lanes 32..63 repeat lanes 0..31), 0 past the row or the
+  // split (such loads fall outside the buffer and fetch nothing).
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(irow, (uint32_t)p.k * 4u);
+  const int e_lane = lane & (kChunk - 1);
+  auto raw_of = [&](int c) -> int {
+    const uint32_t off = c < c_end ? (uint32_t)(c * kChunk + e_lane) * 4u : 0x80000000u;
+    return __builtin_amdgcn_raw_buffer_load_b32(irs, (int)off, 0, 0);
   };
-  // Bit n of the result: slot n of the chunk holds a valid key.
-  auto slot_mask = [&](const int (&jv)[NI]) -> uint32_t {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) bits |= (jv[j] >= 0 ? 1u : 0u) << j;
-    uint32_t mask = 0;
-#pragma unroll
-    for (int r = 0; r < RPI; ++r) mask |= (uint32_t)__builtin_amdgcn_readlane((int)bits, r * PI) << (r * NI);
-    return mask;
-  };
-  // Two register sets of chunk rows alternate: while a chunk is computed, the gathers of
-  // the next two chunks of this wave are in flight.
+  // Gathers the rows of chunk c, whose raw entries are j, into (kd, vd): lane (rho, s) takes
+  // the keys of slots rho * NI + i from the lanes that hold them.  Returns the chunk's slot
+  // mask (bit n: slot n holds a valid key; padding, past the row and not visible are not).
   i32x4 kdA[NI], vdA[NI], kdB[NI], vdB[NI];
-  auto issue_rows = [&](const int (&jv)[NI], i32x4 (&kd)[NI], i32x4 (&vd)[NI]) {
+  auto issue = [&](int c, int j, i32x4 (&kd)[NI], i32x4 (&vd)[NI]) -> uint32_t {
+    const int e = c * kChunk + e_lane;
+    const int key = (c < c_end && e < p.k && j >= 0 && j < kvl) ? j : -1;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * kv_stride_b + 16u * s : 0x80000000u;
-      kd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
-      vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+    for (int i = 0; i < NI; ++i) {
+      const int jv = __shfl(key, rho * NI + i);
+      const uint32_t off = jv >= 0 ? (uint32_t)jv * kv_stride_b + 16u * s : 0x80000000u;
+      kd[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      vd[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
     }
+    return (uint32_t)ballot64(key >= 0);
   };
 
+  // Two register sets of chunk rows alternate, each serving every other chunk of the wave:
+  // while a chunk is computed, the gathers of the next two are in flight.  A set's raw entries
+  // for its next chunk are loaded right after its rows, so the wait for them, a step later,
+  // leaves the other set's rows in flight; past the split the loads are issued all the same
+  // (they fetch nothing), which keeps the wait counts exact.
   constexpr int W = kAttnWaves;
-  int jv[NI];  // positions of the next chunk to gather
   const int c0 = c_begin + wid;
-  load_idx(c0, jv);
-  uint32_t maskA = slot_mask(jv);
-  issue_rows(jv, kdA, vdA);
-  load_idx(c0 + W, jv);
-  uint32_t maskB = slot_mask(jv);
-  issue_rows(jv, kdB, vdB);
-  load_idx(c0 + 2 * W, jv);
+  int jA = raw_of(c0), jB = raw_of(c0 + W);
+  uint32_t maskA = issue(c0, jA, kdA, vdA);
+  jA = raw_of(c0 + 2 * W);
+  uint32_t maskB = issue(c0 + W, jB, kdB, vdB);
+  jB = raw_of(c0 + 3 * W);
 
   // chunk c, whose rows are in (kd, vd): stage them (bank-swizzled), refill the set with
   // chunk c + 2W, then compute
-  auto step = [&](int c, i32x4 (&kd)[NI], i32x4 (&vd)[NI], uint32_t& mask) __attribute__((always_inline)) {
+  auto step = [&](int c, i32x4 (&kd)[NI], i32x4 (&vd)[NI], uint32_t& mask, int& jr)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       *reinterpret_cast<i32x4*>(kst + woff[j]) = kd[j];
       *reinterpret_cast<i32x4*>(vst + woff[j]) = vd[j];
     }
     const uint32_t vmask = mask;
-    if (c + 2 * W < c_end) {
-      mask = slot_mask(jv);
-      issue_rows(jv, kd, vd);
-      load_idx(c + 3 * W, jv);
-    }
+    mask = issue(c + 2 * W, jr, kd, vd);
+    jr = raw_of(c + 4 * W);
     lds_wait();
 
     // S^T tiles: lane holds keys 16*tt + 4*lg + i for head r16
@@ -284,8 +269,9 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     for (int m = 0; m < MC; ++m) {
       const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(kst + koff[m]);
       const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(kst + koff[m] + 16 * ROWB);
-      s0 = mfma_bf16_16x16x32(ka0, qb[m], s0);
-      s1 = mfma_bf16_16x16x32(ka1, qb[m], s1);
+      const bf16x8 qb = q_lds[m][lane];
+      s0 = mfma_bf16_16x16x32(ka0, qb, s0);
+      s1 = mfma_bf16_16x16x32(ka1, qb, s1);
     }
     float x[8];
     float mloc = -__builtin_inff();
@@ -337,26 +323,27 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     }
     lds_wait();
   };
-  for (int c = c0; c < c_end; c += 2 * W) {
-    step(c, kdA, vdA, maskA);
-    if (c + W < c_end) step(c + W, kdB, vdB, maskB);
+  // pairs of steps, then a last one if the wave has an odd number of chunks: every path back
+  // to the loop head has issued the same loads
+  int c = c0;
+  for (; c + W < c_end; c += 2 * W) {
+    step(c, kdA, vdA, maskA, jA);
+    step(c + W, kdB, vdB, maskB, jB);
   }
+  if (c < c_end) step(c, kdA, vdA, maskA, jA);
 
   finish_block<D, ML>(p, layer, rk, kvh, row, split, o, m_run, l_run, &stage_all[0][0][0],
                       sizeof(stage_all[0]), ml_all);
 }
 
-// Launches of few query rows (decode) gather from HBM, and scattered row gathers run at a
-// rate set by the waves each CU holds (4 waves per CU gather at about a third of what 16 do,
-// whatever the loads in flight per wave).  The kernel above holds at most 8 waves per CU: two
-// register sets of chunk rows (248-256 VGPRs) and 64 KiB of LDS per block.  This variant keeps
-// its math but takes 16-row chunks, loads each K row straight into the MFMA operand registers
-// (lane (g, r) reads row r's 16-byte pieces 4m + g, the A-operand layout of S^T = K Q^T; no
-// LDS), stages only V (4 KiB per wave at d = 128) for the transposing read of O^T += V^T P^T
-// (bf16 16x16x16).  Each wave keeps the rows of its next two chunks in registers, as the
-// kernel above does, so their gathers overlap a chunk's arithmetic: 32 KiB of LDS per block and
-// few enough registers for three blocks, 12 waves, per CU.  The launch splits each selection
-// over as many blocks as make about two per CU.
+// Launches of few query rows (decode) gather their rows from HBM.  This variant keeps the math
+// of the kernel above but takes 16-row chunks and loads each K row straight into the MFMA
+// operand registers (lane (g, r) reads row r's 16-byte pieces 4m + g, the A-operand layout of
+// S^T = K Q^T; no LDS); only V is staged (4 KiB per wave at d = 128) for the transposing read
+// of O^T += V^T P^T (bf16 16x16x16).  Each wave keeps the rows of its next two chunks in
+// registers, so their gathers overlap a chunk's arithmetic: 158-167 VGPRs and 32 KiB of LDS per
+// block.  On the decode step it beats the kernel above (14.1 against 17 us per layer for a
+// 4-layer launch; loading K whole, as V, and staging it in LDS as well takes 16.4 us).
 constexpr int kLightChunk = 16;
 
 template <int D, bool ML>
@@ -377,7 +364,7 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
   const int r16 = lane & 15, lg = lane >> 4;
   unsigned bid = blockIdx.x;
   if ((gridDim.x & 7u) == 0) bid = (bid & 7u) * (gridDim.x >> 3) + (bid >> 3);
-  const int layer = ML ? (int)(bid / p.blocks_per_layer) : 0;
+  const int layer = ML ? __builtin_amdgcn_readfirstlane((int)(bid / p.blocks_per_layer)) : 0;
   if (ML) bid -= (unsigned)layer * p.blocks_per_layer;
   const uint16_t* const q_l = pick_layer(p.q, layer);
   const uint16_t* const kc_l = pick_layer(p.kc, layer);
@@ -388,7 +375,8 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
   const int64_t row = rk / p.H_kv;      // b*T + t
   const int b = (int)(row / p.T);
   int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
-  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+  // uniform: the buffer bounds built on it stay in scalar registers
+  kvl = __builtin_amdgcn_readfirstlane(kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl));
 
   // Q as the B operand of S^T = K Q^T: column = head, depth slice [32m + 8lg, +8)
   bf16x8 qb[MC];
@@ -435,11 +423,17 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
 
   const int c_begin = split * p.chunks_per_split;
   const int c_end = min(c_begin + p.chunks_per_split, p.chunks);
-  // entry r16 of chunk c (the same in the four lane groups), -1 if padding or not visible
-  auto key_of = [&](int c) -> int {
+  // Entry r16 of chunk c (the same in the four lane groups) as stored, 0 past the row or the
+  // split (such loads fall outside the buffer and fetch nothing).
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(irow, (uint32_t)p.k * 4u);
+  auto raw_of = [&](int c) -> int {
+    const uint32_t off = c < c_end ? (uint32_t)(c * kLightChunk + r16) * 4u : 0x80000000u;
+    return __builtin_amdgcn_raw_buffer_load_b32(irs, (int)off, 0, 0);
+  };
+  // the key of a raw entry of chunk c, -1 if padding, past the row or not visible
+  auto key_of = [&](int c, int j) -> int {
     const int e = c * kLightChunk + r16;
-    const int j = (c < c_end && e < p.k) ? irow[e] : -1;
-    return (j >= 0 && j < kvl) ? j : -1;
+    return (c < c_end && e < p.k && j >= 0 && j < kvl) ? j : -1;
   };
   // one chunk in registers: its K rows as A operands (lane: row r16, pieces 4m + lg), its V
   // rows for the stage, and which of its 16 keys are valid
@@ -462,26 +456,31 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
     r.mask = (uint32_t)ballot64(jk >= 0) & 0xFFFFu;  // lanes 0..15 hold keys 0..15
   };
 
+  // Each register set (rows and the raw entries of its next chunk) serves every other chunk
+  // of the wave.  A set's entries are loaded right after its rows, so the wait for them, one
+  // step later, leaves the other set's rows in flight; past the split the loads are issued
+  // all the same (they fetch nothing), which keeps the wait counts exact.
   constexpr int W = kAttnWaves;
   const int c0 = c_begin + wid;
   Rows rA, rB;
-  issue(key_of(c0), rA);
-  issue(key_of(c0 + W), rB);
-  int jnext = key_of(c0 + 2 * W);
+  int jA = raw_of(c0), jB = raw_of(c0 + W);
+  issue(key_of(c0, jA), rA);
+  jA = raw_of(c0 + 2 * W);
+  issue(key_of(c0 + W, jB), rB);
+  jB = raw_of(c0 + 3 * W);
 
   // chunk c, whose rows are in r: S^T from the K operands, V staged, then r refilled with
-  // chunk c + 2W (its gathers in flight during this chunk's softmax and O^T update)
-  auto step = [&](int c, Rows& r) __attribute__((always_inline)) {
+  // chunk c + 2W (its gathers in flight during this chunk's softmax and O^T update, with
+  // those of chunk c + W)
+  auto step = [&](int c, Rows& r, int& jr) __attribute__((always_inline)) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < MC; ++m) s0 = mfma_bf16_16x16x32(r.ka[m], qb[m], s0);
 #pragma unroll
     for (int j = 0; j < NIV; ++j) *reinterpret_cast<i32x4*>(vst + woff[j]) = r.vd[j];
     const uint32_t vmask = r.mask;
-    if (c + 2 * W < c_end) {
-      issue(jnext, r);
-      jnext = key_of(c + 3 * W);
-    }
+    issue(key_of(c + 2 * W, jr), r);
+    jr = raw_of(c + 4 * W);
     lds_wait();
 
     float x[4];
@@ -515,10 +514,14 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
     }
     lds_wait();  // the stage is rewritten by the next chunk
   };
-  for (int c = c0; c < c_end; c += 2 * W) {
-    step(c, rA);
-    if (c + W < c_end) step(c + W, rB);
+  // pairs of steps, then a last one if the wave has an odd number of chunks: every path back
+  // to the loop head has issued the same loads
+  int c = c0;
+  for (; c + W < c_end; c += 2 * W) {
+    step(c, rA, jA);
+    step(c + W, rB, jB);
   }
+  if (c < c_end) step(c, rA, jA);
 
   finish_block<D, ML>(p, layer, rk, kvh, row, split, o, m_run, l_run, &lds_all[0][0],
                       sizeof(lds_all[0]), ml_all);
@@ -562,15 +565,14 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs p, in
 
 }  // namespace
 
-// Grids of fewer than 1024 blocks per layer (decode) gather from HBM and are miss-bound: one
-// launch then serves up to 8 layers, and each selection is split over several blocks.  A
-// launch of several layers takes the light kernel, split so that the launch holds about 512
-// blocks; one layer takes the kernel above, split to about one block per CU (256).  Each wave
-// gets at least two chunks.  Measured on the 64-sequence decode step with the caches cold:
-// the 4 layers in one launch take 15.9-16.1 us per layer with the light kernel at 2 blocks per
-// query (1, 3, 4 and 8 blocks: 18.2, 16.3, 18.1 and 20.0 us), 17.0-17.4 us with the kernel
-// above at 1 block per query; one layer is fastest with the kernel above at 4 blocks per query
-// (28.8-29.0 us; the light kernel 29.9-35 us).
+// Grids of fewer than 1024 blocks per layer (decode) gather from HBM: one launch then serves
+// up to 8 layers with the light kernel, each selection split over as many blocks as make the
+// launch about one block per CU (256), each wave getting at least two chunks.  Measured on the
+// 64-sequence decode step with the caches cold: the 4 layers in one launch take 14.1 us per
+// layer at 1 block per query (2, 3, 4 and 6 blocks: 15.8-15.9, 16.5, 16.7 and 18.2 us; more
+// blocks put more requests in flight and add the combine launch), one layer 26.8 us at 4
+// blocks per query (2, 3, 6 and 8: 28.7, 27.2, 30.5 and 29.9 us; the kernel above: 31.2 us).
+// Larger grids (prefill) take the kernel above, faster there (128K: 13.7 against 15.5 ms).
 AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k, int n_layers) {
   (void)H_q;
   AttnPlan p{};
@@ -581,10 +583,10 @@ AttnPlan make_attn_plan(int B, int T, int H_q, int H_kv, int d, int k, int n_lay
   p.light = false;
   if (base > 0 && base < 1024) {
     p.layers = n_layers < kAttnMaxLayers ? (n_layers < 1 ? 1 : n_layers) : kAttnMaxLayers;
-    p.light = p.layers > 1;
-    if (p.light) p.chunks = (k + kLightChunk - 1) / kLightChunk;
+    p.light = true;
+    p.chunks = (k + kLightChunk - 1) / kLightChunk;
     const int64_t grid = base * p.layers;
-    const int64_t target = p.light ? 512 : 256;
+    const int64_t target = 256;
     int64_t want = (target + grid / 2) / grid;
     int64_t by_chunks = p.chunks / (2 * kAttnWaves);
     if (by_chunks < 1) by_chunks = 1;
@@ -656,9 +658,9 @@ hipError_t launch_sparse_attn_layers(int n_layers, const void* const* q, const v
         pl.light
             ? (d == 128 ? (nl > 1 ? &sparse_attn_light_kernel<128, true> : &sparse_attn_light_kernel<128, false>)
                         : (nl > 1 ? &sparse_attn_light_kernel<64, true> : &sparse_attn_light_kernel<64, false>))
-            : (d == 128 ? (nl > 1 ? &sparse_attn_kernel<128, true> : &sparse_attn_kernel<128, false>)
-                        : (nl > 1 ? &sparse_attn_kernel<64, true> : &sparse_attn_kernel<64, false>));
-    // (a launch of the light kernel may hold a single layer: the last of a group of 9 or more)
+            : (d == 128 ? &sparse_attn_kernel<128, false> : &sparse_attn_kernel<64, false>);
+    // (a launch of the light kernel may hold a single layer; the kernel above runs one layer
+    // per launch: only small grids share launches, and those take the light kernel)
     hipLaunchKernelGGL(kern, grid, dim3(kAttnBlock), 0, stream, x);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kPeakBlock) void peak_gather_selection_kernel(SelAr
   const int64_t row = rk / p.H_kv;
   const int b = (int)(row / p.T);
   int kvl = p.kv_len ? p.kv_len[b] : p.S_max;
-  kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
+  kvl = __builtin_amdgcn_readfirstlane(kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl));
   const int32_t* irow = p.idx + (size_t)row * p.k;
   const uint32_t stride_b = (uint32_t)(p.H_kv * ROWB);
   const size_t seq_off = ((size_t)b * p.S_max * p.H_kv + kvh) * D;
@@ -219,34 +219,23 @@ __global__ __launch_bounds__(kPeakBlock) void peak_gather_selection_kernel(SelAr
   const int rho = lane / PI, s = lane % PI;
   const int c_begin = split * p.chunks_per_split;
   const int c_end = min(c_begin + p.chunks_per_split, p.chunks);
-  const bool idx_vec = (p.k & 3) == 0;
-  auto load_idx = [&](int c, int (&jv)[NI]) {
-    const int e0 = c * 32 + rho * NI;
-    if (c >= c_end) {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) jv[j] = -1;
-    } else if (idx_vec && c * 32 + 32 <= p.k) {
-#pragma unroll
-      for (int j = 0; j < NI; j += 4) {
-        const i32x4 v = ld_global_16(irow + e0 + j);
-        jv[j] = v[0];
-        jv[j + 1] = v[1];
-        jv[j + 2] = v[2];
-        jv[j + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) jv[j] = e0 + j < p.k ? irow[e0 + j] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j) jv[j] = (jv[j] >= 0 && jv[j] < kvl) ? jv[j] : -1;
+  // as the attention: lane e_lane holds entry e_lane of a chunk as stored; the rows of slots
+  // rho * NI + i are fetched with the keys taken from those lanes
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(irow, (uint32_t)p.k * 4u);
+  const int e_lane = lane & 31;
+  auto raw_of = [&](int c) -> int {
+    const uint32_t off = c < c_end ? (uint32_t)(c * 32 + e_lane) * 4u : 0x80000000u;
+    return __builtin_amdgcn_raw_buffer_load_b32(irs, (int)off, 0, 0);
   };
-  auto issue = [&](const int (&jv)[NI], i32x4 (&kd)[NI], i32x4 (&vd)[NI]) {
+  auto issue = [&](int c, int j, i32x4 (&kd)[NI], i32x4 (&vd)[NI]) {
+    const int e = c * 32 + e_lane;
+    const int key = (c < c_end && e < p.k && j >= 0 && j < kvl) ? j : -1;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * stride_b + 16u * s : 0x80000000u;
-      kd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
-      vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+    for (int i = 0; i < NI; ++i) {
+      const int jv = __shfl(key, rho * NI + i);
+      const uint32_t off = jv >= 0 ? (uint32_t)jv * stride_b + 16u * s : 0x80000000u;
+      kd[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      vd[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
     }
   };
   uint32_t x = 0;
@@ -256,29 +245,26 @@ __global__ __launch_bounds__(kPeakBlock) void peak_gather_selection_kernel(SelAr
       x ^= (uint32_t)(kd[j][0] ^ kd[j][1] ^ kd[j][2] ^ kd[j][3] ^ vd[j][0] ^ vd[j][1] ^ vd[j][2] ^
                       vd[j][3]);
   };
-  // as the attention: the positions of the next chunk to gather are loaded one step ahead
+  // as the attention: two register sets, each with the raw entries of its next chunk loaded
+  // right after its rows, so two chunks' gathers are in flight while one is consumed
   i32x4 kA[NI], vA[NI], kB[NI], vB[NI];
-  int jv[NI];
   const int c0 = c_begin + wid;
-  load_idx(c0, jv);
-  issue(jv, kA, vA);
-  load_idx(c0 + W, jv);
-  issue(jv, kB, vB);
-  load_idx(c0 + 2 * W, jv);
-  for (int c = c0; c < c_end; c += 2 * W) {
-    consume(kA, vA);
-    if (c + 2 * W < c_end) {
-      issue(jv, kA, vA);
-      load_idx(c + 3 * W, jv);
-    }
-    if (c + W < c_end) {
-      consume(kB, vB);
-      if (c + 3 * W < c_end) {
-        issue(jv, kB, vB);
-        load_idx(c + 4 * W, jv);
-      }
-    }
+  int jA = raw_of(c0), jB = raw_of(c0 + W);
+  issue(c0, jA, kA, vA);
+  jA = raw_of(c0 + 2 * W);
+  issue(c0 + W, jB, kB, vB);
+  jB = raw_of(c0 + 3 * W);
+  auto step = [&](int c, i32x4 (&kd)[NI], i32x4 (&vd)[NI], int& jr) __attribute__((always_inline)) {
+    consume(kd, vd);
+    issue(c + 2 * W, jr, kd, vd);
+    jr = raw_of(c + 4 * W);
+  };
+  int c = c0;
+  for (; c + W < c_end; c += 2 * W) {
+    step(c, kA, vA, jA);
+    step(c + W, kB, vB, jB);
   }
+  if (c < c_end) step(c, kA, vA, jA);
   block_xor_store(x, p.out);
 }
 

@@ -134,3 +134,35 @@ def test_attention_is_deterministic():
     b = bd.sparse_attention(att["q"], att["K"], att["V"], idx, wl.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# Grids of 1024 query rows (B * T * H_kv) or more take the main kernel (32-entry chunks staged
+# in LDS); the cases above, all smaller, take the light kernel.  These repeat the awkward
+# shapes there: a selection length that is not a whole number of chunks (nor of 4 entries),
+# grouped heads with d = 64, padding, empty rows, entries past kv_len and S_max, k = 1.
+@pytest.mark.parametrize("case", ["ragged_gqa_d64", "sharp_padding", "k1", "two_sequences"])
+def test_attention_main_kernel_shapes(case):
+    if case == "ragged_gqa_d64":
+        wl = _wl(B=1, T=520, S=1500, pos0=980, k=130, H_q=16, H_kv=2, d=64, seed=41, qkv_std=1.0)
+    elif case == "sharp_padding":
+        wl = _wl(B=1, T=1030, S=3000, pos0=1970, k=301, seed=42)
+    elif case == "k1":
+        wl = _wl(B=2, T=520, S=2000, pos0=1480, k=1, seed=43)
+    else:
+        wl = _wl(B=2, T=600, S=3000, pos0=2400, k=37, H_q=8, seed=44)
+    assert wl.B * wl.T * wl.H_kv >= 1024
+    rng = np.random.default_rng(wl.seed)
+    idx = _random_idx(wl, rng, frac_pad=0.0 if case == "k1" else 0.3)
+    att = synth.attention_inputs(wl, device=DEV)
+    if case == "sharp_padding":
+        att["q"] = (att["q"].float() * (4.0 * wl.d)).to(torch.bfloat16)
+        idx[0, 3, :] = -1
+        idx[0, 4, 10] = wl.S + 50
+        idx[0, 4, 11] = 1 << 30
+    out, _ = _run_attn(wl, idx, att=att, tag="main " + case)
+    if case == "k1":
+        V = att["V"].cpu()
+        for b in range(wl.B):
+            for t in range(0, wl.T, 7):
+                row = V[b, idx[b, t, 0], 0]
+                assert torch.equal(out[b, t].cpu(), row[None, :].expand(wl.H_q, -1))

@@ -42,9 +42,9 @@ def _topk_plan(lib, a, k):
 
 def test_attention_plans():
     """Every chunk of the selection belongs to a split, a split gives each wave at least two
-    chunks, small grids (decode) share launches and take the light kernel only for several
-    layers, large grids run one layer per launch unsplit, and the ABI's workspace sizes are
-    the plan's."""
+    chunks, small grids (decode) take the light kernel and share launches, split towards one
+    block per CU, large grids run one layer per launch unsplit with the main kernel, and the
+    ABI's workspace sizes are the plan's."""
     lib = _lib()
     n = 0
     for B, T, H_kv, d, k, layers in itertools.product((1, 2, 64), (1, 3, 150, 600, 4096),
@@ -66,8 +66,12 @@ def test_attention_plans():
         if base >= 1024:
             assert p["layers"] == 1 and p["n_splits"] == 1 and not p["light"], where
         else:
-            assert p["layers"] == min(layers, 8), where
-            assert p["light"] == (p["layers"] > 1), where
+            assert p["layers"] == min(layers, 8) and p["light"], where
+            blocks = base * p["layers"] * p["n_splits"]
+            if p["n_splits"] > 1:
+                assert blocks <= 256 + base * p["layers"] // 2 + base * p["layers"], where
+            if p["chunks"] >= 2 * WAVES * 2 and base * p["layers"] <= 128:
+                assert p["n_splits"] > 1, where  # a small launch is split
         assert base * p["n_splits"] * p["layers"] < 2 ** 31, where
         assert p["ws_bytes"] == p["layers"] * p["part_bytes"], where
         if layers == 1:
