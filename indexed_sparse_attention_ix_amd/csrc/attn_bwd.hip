@@ -484,51 +484,38 @@ __global__ __launch_bounds__(kAttnBlock, 2) void indexer_kl_kernel(KlArgs p) {
     }
   };
 
-  const bool idx_vec = (p.k & 3) == 0;
-  auto load_idx = [&](int c, int (&jv)[NI]) {
-    const int e0 = c * kChunk + rho * NI;
-    if (c >= p.chunks) {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) jv[j] = -1;
-    } else if (idx_vec && c * kChunk + kChunk <= p.k) {
-#pragma unroll
-      for (int j = 0; j < NI; j += 4) {
-        const i32x4 v = ld_global_16(irow + e0 + j);
-        jv[j] = v[0]; jv[j + 1] = v[1]; jv[j + 2] = v[2]; jv[j + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) jv[j] = e0 + j < p.k ? irow[e0 + j] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j) jv[j] = (jv[j] >= 0 && jv[j] < kvl) ? jv[j] : -1;
+  // Entry e_lane of chunk c as stored (lanes 32..63 repeat lanes 0..31), 0 past the row; it
+  // is loaded a chunk ahead and checked where the rows are issued, so the wait for it does
+  // not take the rows issued just before it.
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(irow, (uint32_t)p.k * 4u);
+  const int e_lane = lane & (kChunk - 1);
+  auto raw_of = [&](int c) -> int {
+    const uint32_t off = c < p.chunks ? (uint32_t)(c * kChunk + e_lane) * 4u : 0x80000000u;
+    return __builtin_amdgcn_raw_buffer_load_b32(irs, (int)off, 0, 0);
   };
-  auto slot_mask = [&](const int (&jv)[NI]) -> uint32_t {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < NI; ++j) bits |= (jv[j] >= 0 ? 1u : 0u) << j;
-    uint32_t mask = 0;
-#pragma unroll
-    for (int r = 0; r < RPI; ++r) mask |= (uint32_t)__builtin_amdgcn_readlane((int)bits, r * PI) << (r * NI);
-    return mask;
+  auto key_of = [&](int c, int j) -> int {
+    const int e = c * kChunk + e_lane;
+    return (c < p.chunks && e < p.k && j >= 0 && j < kvl) ? j : -1;
   };
+  // the K rows (KV head kvh) of the chunk whose keys, one per lane e_lane, are `key`: lane
+  // (rho, s) takes slots rho * NI + j from the lanes that hold them
   i32x4 kd[NI];
-  auto issue_rows = [&](const int (&jv)[NI], int kvh) {
+  auto issue_rows = [&](int key, int kvh) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const uint32_t off = jv[j] >= 0 ? (uint32_t)jv[j] * kv_stride_b + (uint32_t)(kvh * ROWB) + 16u * s
-                                      : 0x80000000u;
+      const int jv = __shfl(key, rho * NI + j);
+      const uint32_t off = jv >= 0 ? (uint32_t)jv * kv_stride_b + (uint32_t)(kvh * ROWB) + 16u * s
+                                   : 0x80000000u;
       kd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
     }
   };
 
   load_head_data(0);
-  int jc[NI], jn[NI];
   const int c0 = wid;
-  load_idx(c0, jc);
-  uint32_t mask_c = slot_mask(jc);
-  issue_rows(jc, 0);
-  load_idx(c0 + kAttnWaves, jn);
+  int key_c = key_of(c0, raw_of(c0));
+  uint32_t mask_c = (uint32_t)ballot64(key_c >= 0);  // bit n: slot n holds a valid key
+  issue_rows(key_c, 0);
+  int jn = raw_of(c0 + kAttnWaves);
 
   for (int c = c0; c < p.chunks; c += kAttnWaves) {
     const uint32_t vmask = mask_c;
@@ -537,13 +524,12 @@ __global__ __launch_bounds__(kAttnBlock, 2) void indexer_kl_kernel(KlArgs p) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) *reinterpret_cast<i32x4*>(kst + woff[j]) = kd[j];
       if (kvh + 1 < p.H_kv) {
-        issue_rows(jc, kvh + 1);
-      } else if (c + kAttnWaves < p.chunks) {
-        mask_c = slot_mask(jn);
-        issue_rows(jn, 0);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) jc[j] = jn[j];
-        load_idx(c + 2 * kAttnWaves, jn);
+        issue_rows(key_c, kvh + 1);
+      } else {  // past the last chunk the keys are -1 and nothing is fetched
+        key_c = key_of(c + kAttnWaves, jn);
+        mask_c = (uint32_t)ballot64(key_c >= 0);
+        issue_rows(key_c, 0);
+        jn = raw_of(c + 2 * kAttnWaves);
       }
       if (p.H_kv > 1) load_head_data(kvh);  // one KV head: loaded once above
       lds_wait();

@@ -186,23 +186,22 @@ __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_ker
 
   // The gather is pipelined through registers: thread (kk, p) holds piece p of kept key kk
   // of the next chunk, and the position and d loss / d score of that key one chunk further,
-  // so their loads are in flight while a chunk is computed.
+  // so their loads are in flight while a chunk is computed.  The position is checked only
+  // where its piece is requested: checked at once, the wait for it would also wait for the
+  // pieces requested just before it.
   const int kk = tid >> 3, p = tid & 7;
-  auto load_sel = [&](int j, int& s, float& dsv) {
+  auto load_sel = [&](int j, int& s, float& dsv) {  // as stored (-1, 0 past the row)
     s = -1;
     dsv = 0.f;
     if (j < k) {
-      const int sv = idx_row[j];
-      const float dv = ds_row[j];
-      if (sv >= 0 && sv < n_keys) {
-        s = sv;
-        dsv = dv;
-      }
+      s = idx_row[j];
+      dsv = ds_row[j];
     }
   };
+  auto valid = [&](int s) { return s >= 0 && s < n_keys; };
   auto load_piece = [&](int s) {
     i32x4 v = {0, 0, 0, 0};
-    if (s >= 0 && p < kPieces) v = ld_global_16(kI + ((int64_t)b * S_max + s) * DI + 16 * p);
+    if (valid(s) && p < kPieces) v = ld_global_16(kI + ((int64_t)b * S_max + s) * DI + 16 * p);
     return v;
   };
   int s_next, s_after;
@@ -214,8 +213,9 @@ __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_ker
   for (int j0 = 0; j0 < k; j0 += kBwdChunk) {
     // ---- stage the chunk (piece p of kept key kk), then start loading the next two
     {
-      const int s = s_next;
-      const float dsv = ds_next;
+      const bool ok = valid(s_next);
+      const int s = ok ? s_next : -1;
+      const float dsv = ok ? ds_next : 0.f;
       const i32x4 v = v_next;
       const uint32_t vw[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
       float ss = sumsq_e4m3(vw, 4);
