@@ -121,12 +121,16 @@ def summarize_profiles(args, name):
     # splits, a merge and a recompute pass whose waves mostly exit at once: its traffic is
     # the sum over all those dispatches divided by the number of main sweeps (the
     # dispatches within 10 % of the largest).  Attention: the single-layer launches (the
-    # ones timed per launch), without the small combine kernel.
+    # ones timed per launch; sparse_attn_light_kernel for small grids), without the small
+    # combine kernel.
     def is_topk(n):
         return "ix_topk_partial_kernel" in n or "ix_topk_merge_kernel" in n
 
     def is_attn(n):
-        return "sparse_attn_kernel<" in n and ", false>" in n
+        return ("sparse_attn_kernel<" in n or "sparse_attn_light_kernel<" in n) and ", false>" in n
+
+    def is_attn_group(n):  # a launch of several layers (small grids)
+        return "sparse_attn_light_kernel<" in n and ", true>" in n
 
     def per_call(rows, fac, pick, main_key):
         sel = [(n, v) for n, v in rows if pick(n)]
@@ -146,7 +150,7 @@ def summarize_profiles(args, name):
         return round(fb + wb), n_main, f_kib, w_kib
 
     idx_tr = traffic_bytes(is_topk, "ix_topk_partial_kernel")
-    attn_tr = traffic_bytes(is_attn, "sparse_attn_kernel")
+    attn_tr = traffic_bytes(is_attn, "sparse_attn")
     tr = {"workload": name, "source_hash": kernel_source_hash(),
           "indexer_bytes": idx_tr[0], "attention_bytes": attn_tr[0],
           "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5)}
@@ -165,6 +169,7 @@ def summarize_profiles(args, name):
         tk = [(n, d) for n, d in durs if is_topk(n)]
         sweeps = [d for n, d in tk if "ix_topk_partial_kernel" in n]
         at = [d for n, d in durs if is_attn(n)]
+        ag = [d for n, d in durs if is_attn_group(n)]
         per_call_md = ["Per call, from `kernel_trace.csv` (microseconds):", "",
                        "| call | calls | average us |", "|---|---|---|"]
         if sweeps:
@@ -173,7 +178,12 @@ def summarize_profiles(args, name):
             per_call_md.append(f"| `ix_topk` (sweeps, merges and recompute pass) | {n_main} | "
                                f"{sum(d for _, d in tk) / n_main:.1f} |")
         if at:
-            per_call_md.append(f"| `sparse_attn_kernel` (one layer) | {len(at)} | {sum(at) / len(at):.1f} |")
+            kn = sorted({short_kernel_name(n) for n, _ in durs if is_attn(n)})
+            per_call_md.append(f"| {', '.join('`%s`' % k for k in kn)} (one layer) | {len(at)} | "
+                               f"{sum(at) / len(at):.1f} |")
+        if ag:
+            per_call_md.append(f"| `sparse_attn_light_kernel` (a launch of several layers) | {len(ag)} | "
+                               f"{sum(ag) / len(ag):.1f} |")
         if args.profile_bench_json and os.path.exists(args.profile_bench_json):
             try:
                 bj = json.loads(open(args.profile_bench_json).read().strip().splitlines()[-1])
@@ -208,10 +218,11 @@ def summarize_profiles(args, name):
           f"| WRITE_SIZE | {w_copy:.0f} | {w_fac:.4f} |", "",
           "Per call: `ix_topk` = its sweep plus, with key splits, the merges and the recompute",
           "pass (summed, divided by the number of sweeps); attention = one single-layer",
-          "`sparse_attn_kernel` launch (the small combine kernel of split launches excluded).", "",
+          "launch (`sparse_attn_kernel`, or `sparse_attn_light_kernel` for small grids; the small",
+          "combine kernel of split launches excluded).", "",
           "| call | calls counted | FETCH KiB (raw) | WRITE KiB (raw) | scaled bytes per call |",
           "|---|---|---|---|---|"]
-    for label, t in (("ix_topk", idx_tr), ("sparse_attn_kernel (one layer)", attn_tr)):
+    for label, t in (("ix_topk", idx_tr), ("sparse attention (one layer)", attn_tr)):
         if t[0] is not None:
             tm.append(f"| `{label}` | {t[1]} | {t[2]:.0f} | {t[3]:.0f} | {t[0]:.4g} |")
     tm += ["", f"Kernel sources hash {tr['source_hash']} (bench.py reads these numbers only while the",
@@ -225,7 +236,8 @@ def measured_peaks(dev, sh, codes=None):
     """What the chip delivers on the path's three shapes of work (ix_peaks.h): FP8 MFMA
     alone and with 4/8/12 fp32 VALU ops per MFMA (the indexer's epilogue is 8), a 1 GiB
     device copy, and random 256-byte row gathers from a 64 MiB table (one layer's K and V
-    at 128K) and from a 2 GiB table (past the 256 MB Infinity Cache).
+    at 128K), from a 2 GiB table (past the 256 MB Infinity Cache) and from 16 GiB (the
+    footprint of the decode step's 4 layers of K and V: 64 sequences of 128K keys).
 
     codes: e4m3 bytes for the MFMA operands -- the workload's own indexer codes, since the
     MFMA rate depends on the operands' bit activity (power); uniform random codes if None."""
@@ -288,6 +300,19 @@ def measured_peaks(dev, sh, codes=None):
             if n * 256 / t / 1e9 > gather[label]:
                 gather[label], gather_grid[label] = round(n * 256 / t / 1e9, 1), blocks
         del table, rows
+    # 16 segments of 1 GiB, each load step of a wave in one of them (ix_peak_gather_wide)
+    seg = 1 << 30
+    table = torch.empty(16 * seg, dtype=torch.uint8, device=dev)
+    rows = torch.randint(0, seg // 256, (n,), generator=torch.Generator(device="cpu").manual_seed(79),
+                         dtype=torch.int32)
+    rows = torch.sort(rows.view(-1, 2048), dim=1).values.reshape(-1).to(dev)
+    gather["16GiB"] = 0.0
+    for blocks in PEAK_GRIDS:
+        t = timed(lambda: pk.ix_peak_gather_wide(table.data_ptr(), seg, 16, rows.data_ptr(), n, blocks,
+                                                 xr.data_ptr(), sh))
+        if n * 256 / t / 1e9 > gather["16GiB"]:
+            gather["16GiB"], gather_grid["16GiB"] = round(n * 256 / t / 1e9, 1), blocks
+    del table, rows
     return {"fp8_mfma_tflops_by_valu_per_mfma": mfma, "copy_GB_per_s": copy,
             "read_GB_per_s": read, "read_grid": read_grid, "gather_256B_rows_GB_per_s": gather,
             "gather_grid": gather_grid}
@@ -319,6 +344,34 @@ def time_calls(fn, stream, reps, warmup=1, before=None):
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in ev)
     return ts[len(ts) // 2]  # the median: one-off stalls of a single call do not move it
+
+
+def time_after(fn, before, stream, reps, warmup=1):
+    """ms of fn run straight after before(r) on `stream`, with no event between the two: the
+    median of before + fn, each pair timed with events around it, minus the median of before
+    alone.  An event recorded between the two would charge fn the gap it adds (its dispatch
+    then starts from an idle queue); the kernel trace's duration of fn is what this measures."""
+    import torch
+    for _ in range(warmup):
+        before(0)
+        fn()
+    torch.cuda.synchronize()
+
+    def med(call):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for r in range(reps):
+            ev[r][0].record(stream)
+            call(r)
+            ev[r][1].record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return ts[len(ts) // 2]
+
+    def both(r):
+        before(r)
+        fn()
+    return med(both) - med(before)
 
 
 def gather_ceiling(pk, kc, vc, idx, kv_len, wl, stream, reps, split_options, before=None):
@@ -601,6 +654,9 @@ def run_leg(name, dev, steps):
         pk.ix_peak_read(scratch.data_ptr(), 512 << 20, 1024, 0, xr.data_ptr(), sh)
     ms_attn_cold = time_calls(lambda: attn(0), stream, n_cold, before=flush)
     ms_attn_group_cold = time_calls(attn_group, stream, n_cold, before=flush)
+    # the same calls issued straight after the flush (no event between): the kernels' own time
+    ms_attn_cold_b2b = time_after(lambda: attn(0), flush, stream, n_cold)
+    ms_attn_group_cold_b2b = time_after(attn_group, flush, stream, n_cold)
     ms_group_cold = time_calls(group_step, stream, n_cold, before=flush)
     ms_topk_cold = time_calls(lambda: bd.ix_topk(a, wl.k, idx.data_ptr(), 0, ws.data_ptr(), topk_ws,
                                                  sh), stream, n_cold, before=flush)
@@ -619,6 +675,8 @@ def run_leg(name, dev, steps):
     ms_pl = time_calls(per_layer_step, stream, max(2, reps // 2))
     gbs_cold = attn_bytes / (ms_attn_cold / 1e3) / 1e9
     gbs_group_cold = L * attn_bytes / (ms_attn_group_cold / 1e3) / 1e9
+    gbs_cold_b2b = attn_bytes / (ms_attn_cold_b2b / 1e3) / 1e9
+    gbs_group_cold_b2b = L * attn_bytes / (ms_attn_group_cold_b2b / 1e3) / 1e9
     out = {"workload": name, "B": wl.B, "T": wl.T, "S": wl.S, "k": wl.k, "layers": L,
            "group_ms": round(ms_group, 4), "group_ms_cold": round(ms_group_cold, 4),
            "query_tokens_per_s": round(wl.B * wl.T / (ms_group / 1e3), 1),
@@ -638,11 +696,18 @@ def run_leg(name, dev, steps):
            "group_attention_ms_per_layer_cold": round(ms_attn_group_cold / L, 4),
            "group_attention_GB_per_s_cold": round(gbs_group_cold, 1),
            "group_attention_hbm_frac_cold": round(gbs_group_cold / PEAK_HBM_GBS, 4),
+           "attention_ms_per_layer_cold_back_to_back": round(ms_attn_cold_b2b, 4),
+           "attention_hbm_frac_cold_back_to_back": round(gbs_cold_b2b / PEAK_HBM_GBS, 4),
+           "group_attention_ms_per_layer_cold_back_to_back": round(ms_attn_group_cold_b2b / L, 4),
+           "group_attention_GB_per_s_cold_back_to_back": round(gbs_group_cold_b2b, 1),
+           "group_attention_hbm_frac_cold_back_to_back": round(gbs_group_cold_b2b / PEAK_HBM_GBS, 4),
            "gather_ceiling_cold": {"ms": round(c_ms, 4), "splits": c_sp,
                                    "blocks_per_cu": c_occ or None,
                                    "GB_per_s": round(attn_bytes / (c_ms / 1e3) / 1e9, 1),
                                    "attention_frac": round(c_ms / ms_attn_cold, 4)},
-           "flush": "512 MiB buffer read before each cold call, outside the events"}
+           "flush": "512 MiB buffer read before each cold call, outside the events; "
+                    "back_to_back: the call issued straight after the flush, flush time "
+                    "subtracted"}
     del inds, aa, ind, layers, outs, ws, idx
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -1142,14 +1207,18 @@ def main():
         d = legs["decode_b64_128k"]
         gather_hbm = {"workload": "decode_b64_128k",
                       "kernel": "sparse_attn_group_fwd: the 4 layers' attention of the decode "
-                                "step in one launch, caches flushed",
-                      "bound": "hbm", "achieved": d["group_attention_GB_per_s_cold"],
+                                "step in one launch, caches flushed, issued straight after "
+                                "the flush",
+                      "bound": "hbm", "achieved": d["group_attention_GB_per_s_cold_back_to_back"],
                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                      "frac": d["group_attention_hbm_frac_cold"],
-                      "ms_per_layer": d["group_attention_ms_per_layer_cold"],
-                      "one_layer_call": {"ms": d["attention_ms_per_layer_cold"],
-                                         "GB_per_s": d["attention_GB_per_s_cold"],
-                                         "frac": d["attention_hbm_frac_cold"],
+                      "frac": d["group_attention_hbm_frac_cold_back_to_back"],
+                      "ms_per_layer": d["group_attention_ms_per_layer_cold_back_to_back"],
+                      "per_call": {"ms_per_layer": d["group_attention_ms_per_layer_cold"],
+                                   "frac": d["group_attention_hbm_frac_cold"],
+                                   "note": "events around each call: adds the dispatch gap"},
+                      "one_layer_call": {"ms": d["attention_ms_per_layer_cold_back_to_back"],
+                                         "frac": d["attention_hbm_frac_cold_back_to_back"],
+                                         "ms_per_call_timed": d["attention_ms_per_layer_cold"],
                                          "gather_ceiling": d["gather_ceiling_cold"]}}
     if "decode_b64_128k" in legs and peaks:
         d = legs["decode_b64_128k"]
@@ -1159,8 +1228,12 @@ def main():
         d["indexer_frac_of_read_ceiling_cold"] = round(
             d["indexer_bytes"] / (d["ix_topk_ms_cold"] / 1e3) / 1e9 / peaks["read_GB_per_s"], 4)
         if gather_hbm:
-            gather_hbm["frac_of_random_gather_ceiling"] = round(
-                gather_hbm["achieved"] / peaks["gather_256B_rows_GB_per_s"]["2GiB"], 4)
+            g = peaks["gather_256B_rows_GB_per_s"]
+            ceil = g.get("16GiB", g["2GiB"])
+            gather_hbm["random_gather_ceiling"] = {
+                "GB_per_s": ceil, "footprint": "16GiB" if "16GiB" in g else "2GiB",
+                "note": "random 256-byte rows over the decode step's 4 layers of K and V"}
+            gather_hbm["frac_of_random_gather_ceiling"] = round(gather_hbm["achieved"] / ceil, 4)
     indexshare_1m = None
     if "chunk_prefill_1m" in legs:
         c = legs["chunk_prefill_1m"]

@@ -62,11 +62,23 @@ ix_status ix_peak_gather(const void *table, size_t table_bytes, const int32_t *r
                          int32_t blocks, uint32_t *out, hipStream_t stream);
 
 /*
+ * ix_peak_gather_wide -- ix_peak_gather over a table of n_seg segments of seg_bytes each
+ * (a footprint of up to 64 GiB): load step i of wave w (8 rows per lane group) reads the rows
+ * rows[r], counted within segment (w + i) mod n_seg.  seg_bytes: <= 1 GiB, a multiple of 256;
+ * rows outside a segment read as zero.  n_seg: 1..64.  out: as for ix_peak_gather.
+ * Errors: IX_ERR_INVALID for NULL pointers, n < 0, a bad segment size, count or alignment,
+ * or blocks outside 1..65536.
+ */
+ix_status ix_peak_gather_wide(const void *table, size_t seg_bytes, int32_t n_seg,
+                              const int32_t *rows, int64_t n, int32_t blocks, uint32_t *out,
+                              hipStream_t stream);
+
+/*
  * ix_peak_gather_selection -- reads, for every query and KV head, the K and V rows its
  * selection names, exactly as sparse_attn_fwd gathers them (one block of 4 waves per query,
  * KV head and split, 32-entry chunks, two chunks in flight per wave, the same block order),
  * and computes nothing with them: the memory system's rate for the attention's own access
- * pattern.  kc, vc, idx, kv_len, B, T, S_max, H_kv, d, k: as for sparse_attn_fwd (entries
+ * pattern (the main kernel's, taken for 1024 query rows or more).  kc, vc, idx, kv_len, B, T, S_max, H_kv, d, k: as for sparse_attn_fwd (entries
  * < 0 or >= kv_len read nothing).  splits: blocks per (query, KV head), each taking a
  * contiguous share of the selection's chunks.  blocks_per_cu: 0, or 2 or 3 to hold the
  * launch to that many resident blocks per CU (through unused LDS), as the attention's LDS

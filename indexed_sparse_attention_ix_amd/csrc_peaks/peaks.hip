@@ -120,21 +120,27 @@ __global__ __launch_bounds__(kPeakBlock) void peak_copy_kernel(const i32x4* __re
 // instruction, 8 loads in flight per lane (deeper queues measured slower from a 2 GiB table:
 // 16 in flight 5.0-5.1 TB/s, 32 in flight 4.2, against 6.3 for 2 to 8).  No non-temporal
 // hint: it costs 15 % when the table sits in the Infinity Cache (8.5 -> 7.3 TB/s from 64 MiB)
-// and gains 2.5 % from HBM.  The table is read through a buffer resource whose size bounds
-// every access (an out-of-range row reads as zero).
+// and gains 2.5 % from HBM.  The table is n_seg segments of seg_bytes, each read through a
+// buffer resource whose size bounds every access (an out-of-range row reads as zero); load
+// step i of wave w reads in segment (w + i) mod n_seg, so a footprint past the 32-bit offsets
+// of one resource is spread over the whole grid.
 constexpr int kGatherInFlight = 8;
 
-__global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const void* __restrict__ table,
-                                                                 uint32_t table_bytes,
+__global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const unsigned char* __restrict__ table,
+                                                                 uint32_t seg_bytes, int n_seg,
                                                                  const int32_t* __restrict__ rows,
                                                                  int64_t n, uint32_t* __restrict__ out) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(table, table_bytes);
   const int lane = threadIdx.x & 63;
   const int s = lane & 15;
-  const int64_t group = ((int64_t)blockIdx.x * kPeakBlock + threadIdx.x) >> 4;
+  const int64_t tid = (int64_t)blockIdx.x * kPeakBlock + threadIdx.x;
+  const int64_t wave = tid >> 6;
+  const int64_t group = tid >> 4;
   const int64_t groups = ((int64_t)gridDim.x * kPeakBlock) >> 4;
   uint32_t x = 0;
-  for (int64_t base = group; base < n; base += groups * kGatherInFlight) {
+  int64_t step = 0;
+  for (int64_t base = group; base < n; base += groups * kGatherInFlight, ++step) {
+    const int seg = __builtin_amdgcn_readfirstlane((int)((wave + step) % n_seg));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(table + (size_t)seg * seg_bytes, seg_bytes);
     i32x4 v[kGatherInFlight];
 #pragma unroll
     for (int j = 0; j < kGatherInFlight; ++j) {
@@ -383,9 +389,29 @@ ix_status ix_peak_gather(const void* table, size_t table_bytes, const int32_t* r
     return peak_fail(IX_ERR_INVALID, "table_bytes must be a positive multiple of 256, at most 2 GiB");
   if (!aligned16(table)) return peak_fail(IX_ERR_INVALID, "table must be 16-byte aligned");
   if (n == 0) return IX_OK;
-  hipLaunchKernelGGL(peak_gather_kernel, dim3(blocks), dim3(kPeakBlock), 0, stream, table,
-                     (uint32_t)table_bytes, rows, n, out);
+  hipLaunchKernelGGL(peak_gather_kernel, dim3(blocks), dim3(kPeakBlock), 0, stream,
+                     reinterpret_cast<const unsigned char*>(table), (uint32_t)table_bytes, 1, rows,
+                     n, out);
   return launched("ix_peak_gather");
+}
+
+ix_status ix_peak_gather_wide(const void* table, size_t seg_bytes, int32_t n_seg,
+                              const int32_t* rows, int64_t n, int32_t blocks, uint32_t* out,
+                              hipStream_t stream) {
+  using namespace ix;
+  if (!table || !rows || !out) return peak_fail(IX_ERR_INVALID, "NULL table, rows or out");
+  if (n < 0) return peak_fail(IX_ERR_INVALID, "n=%lld must be >= 0", (long long)n);
+  if (blocks < 1 || blocks > kMaxPeakBlocks)
+    return peak_fail(IX_ERR_INVALID, "blocks=%d (1..%d)", blocks, kMaxPeakBlocks);
+  if (seg_bytes == 0 || seg_bytes % 256 || seg_bytes > ((size_t)1 << 30))
+    return peak_fail(IX_ERR_INVALID, "seg_bytes must be a positive multiple of 256, at most 1 GiB");
+  if (n_seg < 1 || n_seg > 64) return peak_fail(IX_ERR_INVALID, "n_seg=%d (1..64)", n_seg);
+  if (!aligned16(table)) return peak_fail(IX_ERR_INVALID, "table must be 16-byte aligned");
+  if (n == 0) return IX_OK;
+  hipLaunchKernelGGL(peak_gather_kernel, dim3(blocks), dim3(kPeakBlock), 0, stream,
+                     reinterpret_cast<const unsigned char*>(table), (uint32_t)seg_bytes, (int)n_seg,
+                     rows, n, out);
+  return launched("ix_peak_gather_wide");
 }
 
 ix_status ix_peak_gather_selection(const void* kc, const void* vc, const int32_t* idx,

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libix_peaks
 
 # every symbol include/ix_peaks.h declares
 EXPORTS = ("ix_peak_last_error", "ix_peak_mfma_fp8", "ix_peak_copy", "ix_peak_read",
-           "ix_peak_gather", "ix_peak_gather_selection", "ix_peak_atomic_add")
+           "ix_peak_gather", "ix_peak_gather_wide", "ix_peak_gather_selection", "ix_peak_atomic_add")
 
 _lib = None
 
@@ -35,6 +35,9 @@ def load(path: str = LIB_PATH):
     L.ix_peak_read.argtypes = [c_void_p, c_size_t, c_int32, c_int32, c_void_p, c_void_p]
     L.ix_peak_gather.restype = c_int32
     L.ix_peak_gather.argtypes = [c_void_p, c_size_t, c_void_p, c_int64, c_int32, c_void_p, c_void_p]
+    L.ix_peak_gather_wide.restype = c_int32
+    L.ix_peak_gather_wide.argtypes = [c_void_p, c_size_t, c_int32, c_void_p, c_int64, c_int32,
+                                      c_void_p, c_void_p]
     L.ix_peak_gather_selection.restype = c_int32
     L.ix_peak_gather_selection.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p] + [c_int32] * 8 + \
         [c_void_p, c_void_p]
@@ -63,6 +66,10 @@ def ix_peak_read(src, nbytes, blocks, nontemporal, out, stream=0):
 
 def ix_peak_gather(table, table_bytes, rows, n, blocks, out, stream=0):
     _check(load().ix_peak_gather(table, table_bytes, rows, n, blocks, out, stream))
+
+
+def ix_peak_gather_wide(table, seg_bytes, n_seg, rows, n, blocks, out, stream=0):
+    _check(load().ix_peak_gather_wide(table, seg_bytes, n_seg, rows, n, blocks, out, stream))
 
 
 def ix_peak_gather_selection(kc, vc, idx, kv_len, B, T, S_max, H_kv, d, k, splits, blocks_per_cu,

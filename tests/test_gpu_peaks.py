@@ -42,6 +42,34 @@ def test_peak_gather_checksum(blocks):
     assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
 
 
+@pytest.mark.parametrize("blocks", [7, 1000])
+def test_peak_gather_wide_checksum(blocks):
+    """Load step i of wave w reads its rows in segment (w + i) mod n_seg: the XOR of all words
+    read, computed on the host from that mapping, with rows outside a segment reading zero."""
+    n_seg, seg_rows, n = 3, 1024, 70001
+    say(f"[ix_peak_gather_wide] {n_seg} segments of {seg_rows} rows, {n} gathers, {blocks} blocks")
+    g = torch.Generator().manual_seed(6)
+    table = torch.randint(-2**31, 2**31 - 1, (n_seg * seg_rows * 64,), generator=g, dtype=torch.int32)
+    rows = torch.randint(-3, seg_rows + 3, (n,), generator=g, dtype=torch.int32)
+    out = torch.zeros(blocks, dtype=torch.int32, device=DEV)
+    table_d, rows_d = table.to(DEV), rows.to(DEV)
+    pk.ix_peak_gather_wide(table_d.data_ptr(), seg_rows * 256, n_seg, rows_d.data_ptr(), n, blocks,
+                           out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    row_x = np.bitwise_xor.reduce(table.numpy().view(np.uint32).reshape(n_seg, seg_rows, 64), axis=2)
+    groups = blocks * 256 // 16           # 16 lanes per row read
+    r = np.arange(n)
+    step, rem = r // (groups * 8), r % (groups * 8)
+    wave = (rem % groups) // 4            # 4 lane groups per wave
+    seg = (wave + step) % n_seg
+    rv = rows.numpy()
+    ok = (rv >= 0) & (rv < seg_rows)
+    counts = np.zeros((n_seg, seg_rows), dtype=np.int64)
+    np.add.at(counts, (seg[ok], rv[ok]), 1)
+    want = np.bitwise_xor.reduce(np.where(counts % 2 == 1, row_x, 0).ravel())
+    assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
+
+
 def test_peak_mfma_runs():
     ops = torch.full((34 * 64 * 32,), 0x38, dtype=torch.uint8, device=DEV)
     for nv in (0, 4, 8, 12):
