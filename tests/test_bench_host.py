@@ -16,7 +16,7 @@ import bench  # noqa: E402
 TOPK = "void ix::(anonymous namespace)::ix_topk_partial_kernel<4, 16, 128, true>(ix::(anonymous namespace)::IxArgs)"
 MERGE = "ix::(anonymous namespace)::ix_topk_merge_kernel(ix::(anonymous namespace)::IxArgs)"
 ATT1 = "void ix::(anonymous namespace)::sparse_attn_kernel<128, false>(ix::(anonymous namespace)::AttnArgs)"
-ATTN = "void ix::(anonymous namespace)::sparse_attn_kernel<128, true>(ix::(anonymous namespace)::AttnArgs)"
+ATTN = "void ix::(anonymous namespace)::sparse_attn_light_kernel<128, true>(ix::(anonymous namespace)::AttnArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -73,11 +73,12 @@ def test_summarizer_per_call_traffic_and_durations(tmp_path, monkeypatch):
     # ix_topk per call: (2 sweeps + 2 recompute passes + 2 merges) / 2 sweeps
     want_topk = (2120.0 * 1024 * 2.0 + 216.0 * 1024 * 1.0) / 2
     assert tr["indexer_bytes"] == round(want_topk)
-    # attention: the single-layer launches only
+    # attention: the single-layer launches only (not the launch of several layers)
     assert tr["attention_bytes"] == round(300.0 * 1024 * 2.0 + 64.0 * 1024)
     assert tr["fetch_scale"] == 2.0 and tr["write_scale"] == 1.0
     kt = open(tmp_path / "profiles" / "kernel_trace_wl.md").read()
     # per call: (2 x 1000 + 2 x 20 + 2 x 4 + 2 x 5) us / 2 sweeps = 1029 us; attention 305 us
     assert "| `ix_topk` (sweeps, merges and recompute pass) | 2 | 1029.0 |" in kt
-    assert "| `sparse_attn_kernel` (one layer) | 2 | 305.0 |" in kt
+    assert "| `sparse_attn_kernel<128, false>(AttnArgs)` (one layer) | 2 | 305.0 |" in kt
+    assert "| `sparse_attn_light_kernel` (a launch of several layers) | 1 | 900.0 |" in kt
     assert "`ix_topk` 1030.0 us" in kt
