@@ -368,6 +368,10 @@ __device__ uint64_t wave_min_key(const uint64_t* buf, int n) {
   return wave_min_u64(m);
 }
 
+// s_waitcnt immediate that waits for this wave's vector-memory operations only (vmcnt 0,
+// expcnt and lgkmcnt at their maxima: no wait on those)
+constexpr int kWaitVmemOnly = 0x0F70;
+
 __device__ __forceinline__ void mem_fence_wave() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
 }
@@ -546,15 +550,24 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       return step * jj + (step > 1 ? (int)((((uint32_t)jj * 2654435761u) >> 16) % (uint32_t)step) : 0);
     };
     auto tile_off = [&](int jj) { return voff + min(base + 16 * tile_idx(jj), kvl) * DI; };
+    // One-query units (decode) run one wave per SIMD, so no other wave covers this one's
+    // memory waits: the tiles are scored and refilled strictly in ring order (scheduling
+    // barriers), so the wait for a tile leaves the other PF - 1 in flight.  Left free, the
+    // scheduler interleaves all PF tiles' products at the top of the ring and sinks their
+    // refills to the bottom, and every step waits for the whole ring.
     i32x8 ring[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) ring[i] = load_key_tile(krs, tile_off(i));
+    for (int i = 0; i < PF; ++i) {
+      ring[i] = load_key_tile(krs, tile_off(i));
+      if constexpr (QC == 1) __builtin_amdgcn_sched_barrier(0);
+    }
     for (int j0 = 0; j0 < count; j0 += PF) {
       float sc[PF];
 #pragma unroll
       for (int ui = 0; ui < PF; ++ui) {
         sc[ui] = qo.template tile_score<EXACT>(ring[ui], p.g, jsel);
         ring[ui] = load_key_tile(krs, tile_off(j0 + ui + PF));
+        if constexpr (QC == 1) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int ui = 0; ui < PF; ++ui) {
@@ -587,6 +600,11 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
             if (p.dbg && lane == 0) atomicAdd(p.dbg + kDbgTopkCompactions, 1ull);
           }
         }
+        // Vector loads and stores complete in order under one counter, and the flush stores
+        // a count of entries no one knows in advance: without a wait here the wait for the
+        // next step's first tile could not be counted and would take every tile in flight.
+        // This branch is rare; waiting in it keeps the other tiles' loads in flight.
+        __builtin_amdgcn_s_waitcnt(kWaitVmemOnly);
       }
     }
     flush();
