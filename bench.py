@@ -151,6 +151,7 @@ def summarize_profiles(args, name):
 
     idx_tr = traffic_bytes(is_topk, "ix_topk_partial_kernel")
     attn_tr = traffic_bytes(is_attn, "sparse_attn")
+    group_tr = traffic_bytes(is_attn_group, "sparse_attn_light_kernel")
     tr = {"workload": name, "source_hash": kernel_source_hash(),
           "indexer_bytes": idx_tr[0], "attention_bytes": attn_tr[0],
           "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5)}
@@ -222,7 +223,8 @@ def summarize_profiles(args, name):
           "combine kernel of split launches excluded).", "",
           "| call | calls counted | FETCH KiB (raw) | WRITE KiB (raw) | scaled bytes per call |",
           "|---|---|---|---|---|"]
-    for label, t in (("ix_topk", idx_tr), ("sparse attention (one layer)", attn_tr)):
+    for label, t in (("ix_topk", idx_tr), ("sparse attention (one layer)", attn_tr),
+                     ("sparse_attn_light_kernel (a launch of several layers)", group_tr)):
         if t[0] is not None:
             tm.append(f"| `{label}` | {t[1]} | {t[2]:.0f} | {t[3]:.0f} | {t[0]:.4g} |")
     tm += ["", f"Kernel sources hash {tr['source_hash']} (bench.py reads these numbers only while the",
