@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok0 = kr[i] >= 0, ok1 = kr[4 + i] >= 0;
-      pr[i] = ok0 ? exp2f(s0[i] * p.scale_log2 - lse2) : 0.f;
-      pr[4 + i] = ok1 ? exp2f(s1[i] * p.scale_log2 - lse2) : 0.f;
+      pr[i] = ok0 ? exp2_hw(s0[i] * p.scale_log2 - lse2) : 0.f;
+      pr[4 + i] = ok1 ? exp2_hw(s1[i] * p.scale_log2 - lse2) : 0.f;
       ds[i] = pr[i] * (dp0[i] - Dh);
       ds[4 + i] = pr[4 + i] * (dp1[i] - Dh);
     }
@@ -240,8 +240,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
       i32x4 dk;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        dk[e] = (int)((uint32_t)f32_to_bf16_rne(ds[2 * e]) |
-                      ((uint32_t)f32_to_bf16_rne(ds[2 * e + 1]) << 16));
+        dk[e] = (int)pack_bf16x2(ds[2 * e], ds[2 * e + 1]);
       const bf16x8 dsb = __builtin_bit_cast(bf16x8, dk);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -543,8 +542,8 @@ __global__ __launch_bounds__(kAttnBlock, 2) void indexer_kl_kernel(KlArgs p) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u0 += exp2f(s0[i] * p.scale_log2 - lse2[i]);
-        u1 += exp2f(s1[i] * p.scale_log2 - lse2[i]);
+        u0 += exp2_hw(s0[i] * p.scale_log2 - lse2[i]);
+        u1 += exp2_hw(s1[i] * p.scale_log2 - lse2[i]);
       }
       lds_wait();
     }

@@ -11,11 +11,24 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = kAttnWaves * kWave;
 constexpr int kChunk = 32;
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+
+// Two floats to packed bf16 (lo in bits 0-15), rounded to nearest even by the gfx950
+// conversion instruction (one instruction for the pair; NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
+
+// One float to bf16 bits, rounded to nearest even (the same conversion).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// 2^x by the hardware instruction alone: exact to its rounding for results of 2^-126 and up;
+// below that (a softmax weight under 2^-126 of the running maximum, far below what a bf16
+// output or an fp32 sum of such weights can show) it need not give the denormal.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, ld_global_16(p));

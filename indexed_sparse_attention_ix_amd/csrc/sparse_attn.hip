@@ -225,15 +225,17 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
   i32x4 kdA[NI], vdA[NI], kdB[NI], vdB[NI];
   auto issue = [&](int c, int j, i32x4 (&kd)[NI], i32x4 (&vd)[NI]) -> uint32_t {
     const int e = c * kChunk + e_lane;
-    const int key = (c < c_end && e < p.k && j >= 0 && j < kvl) ? j : -1;
+    const bool valid = c < c_end && e < p.k && j >= 0 && j < kvl;
+    // the row's byte offset, formed once by the lane that holds the entry (an invalid entry
+    // reads past the buffer: 0x80000000 plus a piece offset stays out of range)
+    const uint32_t roff = valid ? (uint32_t)j * kv_stride_b : 0x80000000u;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int jv = __shfl(key, rho * NI + i);
-      const uint32_t off = jv >= 0 ? (uint32_t)jv * kv_stride_b + 16u * s : 0x80000000u;
+      const uint32_t off = (uint32_t)__shfl((int)roff, rho * NI + i) + 16u * s;
       kd[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
       vd[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
     }
-    return (uint32_t)ballot64(key >= 0);
+    return (uint32_t)ballot64(valid);
   };
 
   // Two register sets of chunk rows alternate, each serving every other chunk of the wave:
@@ -286,12 +288,12 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     mloc = max_across_rows(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const bool any = m_new != -__builtin_inff();
-    const float alpha = (any && m_run != -__builtin_inff()) ? exp2f(m_run - m_new) : (any ? 0.f : 1.f);
+    const float alpha = (any && m_run != -__builtin_inff()) ? exp2_hw(m_run - m_new) : (any ? 0.f : 1.f);
     float pr[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pr[e] = (x[e] != -__builtin_inff()) ? exp2f(x[e] - m_new) : 0.f;
+      pr[e] = (x[e] != -__builtin_inff()) ? exp2_hw(x[e] - m_new) : 0.f;
       psum += pr[e];
     }
     l_run = l_run * alpha + psum;
@@ -307,9 +309,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_kernel(AttnArgs p) 
     {
       i32x4 pk;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pk[e] = (int)((uint32_t)f32_to_bf16_rne(pr[2 * e]) |
-                      ((uint32_t)f32_to_bf16_rne(pr[2 * e + 1]) << 16));
+      for (int e = 0; e < 4; ++e) pk[e] = (int)pack_bf16x2(pr[2 * e], pr[2 * e + 1]);
       pb = __builtin_bit_cast(bf16x8, pk);
     }
 #pragma unroll
@@ -443,14 +443,16 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
     uint32_t mask;
   };
   auto issue = [&](int jk, Rows& r) {
-    const uint32_t kbase = jk >= 0 ? (uint32_t)jk * kv_stride_b + 16u * lg : 0x80000000u;
+    // the row's byte offset, formed once by the lane that holds the entry (an invalid entry
+    // reads past the buffer: 0x80000000 plus a piece offset stays out of range)
+    const uint32_t roff = jk >= 0 ? (uint32_t)jk * kv_stride_b : 0x80000000u;
+    const uint32_t kbase = roff + 16u * lg;
 #pragma unroll
     for (int m = 0; m < MC; ++m)
       r.ka[m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(kbase + 64u * m), 0, 0));
 #pragma unroll
     for (int j = 0; j < NIV; ++j) {
-      const int jv = __shfl(jk, rho * NIV + j);
-      const uint32_t off = jv >= 0 ? (uint32_t)jv * kv_stride_b + 16u * s : 0x80000000u;
+      const uint32_t off = (uint32_t)__shfl((int)roff, rho * NIV + j) + 16u * s;
       r.vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
     }
     r.mask = (uint32_t)ballot64(jk >= 0) & 0xFFFFu;  // lanes 0..15 hold keys 0..15
@@ -494,15 +496,16 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
     mloc = max_across_rows(mloc);
     const float m_new = fmaxf(m_run, mloc);
     const bool any = m_new != -__builtin_inff();
-    const float alpha = (any && m_run != -__builtin_inff()) ? exp2f(m_run - m_new) : (any ? 0.f : 1.f);
-    i16x4 pb;
+    const float alpha = (any && m_run != -__builtin_inff()) ? exp2_hw(m_run - m_new) : (any ? 0.f : 1.f);
+    float pr[4];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pr = (x[i] != -__builtin_inff()) ? exp2f(x[i] - m_new) : 0.f;
-      psum += pr;
-      pb[i] = (short)f32_to_bf16_rne(pr);
+      pr[i] = (x[i] != -__builtin_inff()) ? exp2_hw(x[i] - m_new) : 0.f;
+      psum += pr[i];
     }
+    const i16x4 pb = __builtin_bit_cast(
+        i16x4, (uint32_t __attribute__((ext_vector_type(2)))){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // O^T += V^T P^T: P^T (keys 4lg..4lg+3 of head r16) is the B operand as the lane holds it
