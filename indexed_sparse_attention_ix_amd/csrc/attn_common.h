@@ -78,16 +78,23 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char* p) {
 }
 
 // Bank swizzle of the staged K/V rows: 16-byte piece p of chunk slot n sits at piece
-// position p ^ swz(n).  Rows are 256 B (D = 128: one row per 64-bank line) or 128 B
-// (D = 64: two rows per line); swz rotates the slot's position within the line left by
-// one bit, so the 16 slots of an A-operand read hit 16 distinct 16-byte bank groups and
-// the 8 slots of a half-wave transposed read hit 8 distinct 32-byte groups.
+// position p ^ swz(n).  D = 128 (256-byte rows): swz(n) over n mod 16 is the permutation
+// 0 2 4 6 9 11 13 15 1 3 5 7 8 10 12 14, so that the 16 slots of an A-operand read (16 bytes
+// per lane) take 16 distinct 16-byte positions and each 8 of them distinct positions modulo 8,
+// the slots of a transposed read (8 bytes per lane) distinct 8-byte positions per 32 and per
+// 16 lanes, and a row's 16 pieces written by 16 lanes distinct positions per 16 and per 8
+// lanes: no bank conflict whether a 16-byte access serves 8 or 16 lanes per cycle.  (A plain
+// one-bit rotation gave the A-operand reads two-way conflicts in the 8-lane case.)  D = 64
+// (128-byte rows, two per 256 bytes): the slot pair's position rotated left by one bit.
 template <int D>
 __device__ __forceinline__ int stage_swz(int n) {
-  constexpr int PI = D / 8;                     // 16-byte pieces per row
-  constexpr int LOG = D == 128 ? 4 : 3;
-  const int m = (D == 128 ? n : (n >> 1)) & (PI - 1);
-  return ((m << 1) & (PI - 1)) | (m >> (LOG - 1));
+  if constexpr (D == 128) {
+    const int m = n & 15;
+    return (2 * (m & 3)) | (((m >> 2) & 1) << 3) | (((m >> 2) ^ (m >> 3)) & 1);
+  } else {
+    const int m = (n >> 1) & 7;
+    return ((m << 1) & 7) | (m >> 2);
+  }
 }
 
 }  // namespace ix
