@@ -236,7 +236,8 @@ def summarize_profiles(args, name):
 
 def measured_peaks(dev, sh, codes=None):
     """What the chip delivers on the path's three shapes of work (ix_peaks.h): FP8 MFMA
-    alone and with 4/8/12 fp32 VALU ops per MFMA (the indexer's epilogue is 8), a 1 GiB
+    alone and with 4/8/12 fp32 VALU ops per MFMA (the indexer's plain epilogue is 8, its
+    64-head form about 5 over 17 MFMAs per 16 useful), a 1 GiB
     device copy, and random 256-byte row gathers from a 64 MiB table (one layer's K and V
     at 128K), from a 2 GiB table (past the 256 MB Infinity Cache) and from 16 GiB (the
     footprint of the decode step's 4 layers of K and V: 64 sequences of 128K keys).
@@ -1183,8 +1184,12 @@ def main():
         peaks = measured_peaks(dev, sh, codes=torch.cat([ind["k_I"].reshape(-1)[:1 << 20],
                                                           ind["q_I"].reshape(-1)[:1 << 20]]))
         if idx_roof["bound"] == "mfma":
-            peaks["indexer_frac_of_mfma_with_8_valu"] = round(
-                idx_roof["achieved"] / peaks["fp8_mfma_tflops_by_valu_per_mfma"]["8"], 3)
+            by_valu = peaks["fp8_mfma_tflops_by_valu_per_mfma"]
+            # the plain epilogue's ceiling (8 VALU ops per MFMA), and that of the 64-head
+            # |x| + linear-MFMA form: about 4-5 VALU ops per MFMA, 16 of every 17 MFMAs useful
+            peaks["indexer_frac_of_mfma_with_8_valu"] = round(idx_roof["achieved"] / by_valu["8"], 3)
+            peaks["indexer_frac_of_mfma_with_4_valu_16_of_17"] = round(
+                idx_roof["achieved"] / (by_valu["4"] * 16 / 17), 3)
         else:
             peaks["indexer_frac_of_read"] = round(idx_roof["achieved"] / peaks["read_GB_per_s"], 3)
         peaks["attention_frac_of_gather_64MiB"] = round(

@@ -105,10 +105,26 @@ __device__ __forceinline__ int visible_keys(int pos0, int kvl, int t) {
 }
 
 // Per-wave query operands: B operands for every head block and the matching weights.
-template <int QC, int GMAX, int DI>
+//
+// LIN (4 queries per wave, all 16 head blocks): the head sum is taken as
+//   sum_h w_h max(0, x_h) = 1/2 sum_h w_h |x_h| + 1/2 sum_h w_h x_h,
+// where the linear half is one more MFMA per key tile: sum_h w_h x_h = k . u with
+// u = sum_h w_h q_h.  u is split into four e4m3 vectors with power-of-two scales,
+// u ~= sum_j 2^E_j e_j (each term captures the next 4 significant bits of the residual;
+// what the four leave is below 2^-16 of max|u|), and column (query, j) of the extra
+// B operand holds e_j, so the head-sum reduction adds the four terms as it adds heads.
+// That leaves one VALU op per head dot product (an FMA with an |x| source modifier)
+// instead of two.  A key whose true score is 0 (every head dot product <= 0) would
+// come out as rounding noise, so a visible key whose score is not above 1/16 of its
+// |x| sum A is scored again the plain way in the same tile, which keeps exact zeros
+// exact -- unless its query's threshold is already above A/8: its score, either way, is
+// at most A/16 plus rounding error, far below A/8, so it cannot be kept.
+template <int QC, int GMAX, int DI, bool LIN>
 struct QueryOperands {
   i32x8 bq[GMAX];
-  float wv[GMAX];
+  float wv[GMAX];  // LIN: w / 2
+  i32x8 bl;        // LIN: e_j of the lane's (query, term j) column
+  float sl;        // LIN: 2^E_j
 
   __device__ __forceinline__ void load(const IxArgs& p, int b, int t, bool valid, int safe_t,
                                        int j, int lg) {
@@ -122,9 +138,73 @@ struct QueryOperands {
         const int head = g * HC + j;
         const size_t row = ((size_t)b * p.T + tq) * p.H_I + head;
         bq[g] = load_row_slice<DI>(p.q + row * DI, lg);
-        wv[g] = valid ? p.w[row] : 0.f;
+        wv[g] = valid ? (LIN ? 0.5f : 1.f) * p.w[row] : 0.f;
       }
     }
+    if constexpr (LIN) split_linear(j);
+  }
+
+  // u/2 over the lane's 32 depth elements (its lane group's slice) for query (lane&15)/4,
+  // then the four terms; lane (query, j) keeps term j.
+  __device__ __forceinline__ void split_linear(int j) {
+    static_assert(QC == 4, "the linear terms fill the four columns of a query");
+    float r[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) r[c] = 0.f;
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+#pragma unroll
+      for (int dw = 0; dw < 8; ++dw) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(bq[g][dw], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(bq[g][dw], true);
+        r[4 * dw + 0] = fmaf(wv[g], lo[0], r[4 * dw + 0]);
+        r[4 * dw + 1] = fmaf(wv[g], lo[1], r[4 * dw + 1]);
+        r[4 * dw + 2] = fmaf(wv[g], hi[0], r[4 * dw + 2]);
+        r[4 * dw + 3] = fmaf(wv[g], hi[1], r[4 * dw + 3]);
+      }
+    }
+    // the quad's four lanes hold heads 4g + 0..3 of one query: add them (same bits in all four)
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      r[c] += dpp_f32<kDppQuadXor1>(r[c]);
+      r[c] += dpp_f32<kDppQuadXor2>(r[c]);
+    }
+    i32x8 keep = {0, 0, 0, 0, 0, 0, 0, 0};
+    float keep_scale = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float m = 0.f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) m = fmaxf(m, fabsf(r[c]));
+      // the query's four lane groups hold the four depth slices
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      // scale 2^E with max|r| / 2^E in (224, 448]: m = f 2^e, f in [1, 2), 448 = 1.75 2^8.
+      // Residuals below 2^-100 are dropped.
+      const uint32_t mb = __builtin_bit_cast(uint32_t, m);
+      const bool live = m >= 0x1p-100f;
+      const int e = (int)(mb >> 23) - 127;
+      const int E = e - ((mb & 0x7FFFFFu) <= 0x600000u ? 8 : 7);
+      const float scale = live ? __builtin_bit_cast(float, (uint32_t)(E + 127) << 23) : 0.f;
+      const float inv = live ? __builtin_bit_cast(float, (uint32_t)(127 - E) << 23) : 0.f;
+#pragma unroll
+      for (int dw = 0; dw < 8; ++dw) {
+        // |r * inv| <= 448: round to nearest e4m3, then take the rounded value off the
+        // residual (exact: the difference is representable in fp32)
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * dw + 0] * inv, r[4 * dw + 1] * inv, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * dw + 2] * inv, r[4 * dw + 3] * inv, pk, true);
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+        r[4 * dw + 0] = fmaf(-scale, lo[0], r[4 * dw + 0]);
+        r[4 * dw + 1] = fmaf(-scale, lo[1], r[4 * dw + 1]);
+        r[4 * dw + 2] = fmaf(-scale, hi[0], r[4 * dw + 2]);
+        r[4 * dw + 3] = fmaf(-scale, hi[1], r[4 * dw + 3]);
+        if (jj == j) keep[dw] = pk;
+      }
+      if (jj == j) keep_scale = scale;
+    }
+    bl = keep;
+    sl = keep_scale;
   }
 
   // ReLU on the float bits: a signed-integer max with 0 maps every negative float
@@ -138,32 +218,18 @@ struct QueryOperands {
     acc[2] = fmaf(w, relu(x[2]), acc[2]);
     acc[3] = fmaf(w, relu(x[3]), acc[3]);
   }
+  static __device__ __forceinline__ void accumulate_abs(f32x4& acc, const f32x4& x, float w) {
+    acc[0] = fmaf(w, fabsf(x[0]), acc[0]);
+    acc[1] = fmaf(w, fabsf(x[1]), acc[1]);
+    acc[2] = fmaf(w, fabsf(x[2]), acc[2]);
+    acc[3] = fmaf(w, fabsf(x[3]), acc[3]);
+  }
 
-  // Score of one (query, key) pair per lane for the 16-key tile held in `a`.
-  // Lane l ends up with key 4*(l>>4) + (j & 3) and query (l & 15) / HC, where
-  // j = (l & 15) % HC; for HC = 16 only lanes with j < 4 carry a distinct pair.
-  // EXACT: all GMAX head blocks are used; the MFMA of block g+1 is issued before the
-  // epilogue of block g so that the matrix core and the VALU overlap.
-  template <bool EXACT>
-  __device__ __forceinline__ float tile_score(const i32x8& a, int g_rt, int jsel) const {
+  // Sum of the HC adjacent columns of one query: lane l ends up with key
+  // 4*(l>>4) + (j & 3) and query (l & 15) / HC, where j = (l & 15) % HC; for HC = 16
+  // only lanes with j < 4 carry a distinct pair.
+  static __device__ __forceinline__ float head_sum(const f32x4& acc, int jsel) {
     constexpr int HC = 16 / QC;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (EXACT) {
-      f32x4 x = mfma_e4m3_16x16x128(a, bq[0]);
-#pragma unroll
-      for (int g = 1; g < GMAX; ++g) {
-        const f32x4 y = mfma_e4m3_16x16x128(a, bq[g]);
-        accumulate(acc, x, wv[g - 1]);
-        x = y;
-      }
-      accumulate(acc, x, wv[GMAX - 1]);
-
-    } else {
-#pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        if (g < g_rt) accumulate(acc, mfma_e4m3_16x16x128(a, bq[g]), wv[g]);
-      }
-    }
     const bool b1 = (jsel & 2) != 0, b0 = (jsel & 1) != 0;
     const float keep0 = b1 ? acc[2] : acc[0], send0 = b1 ? acc[0] : acc[2];
     const float keep1 = b1 ? acc[3] : acc[1], send1 = b1 ? acc[1] : acc[3];
@@ -175,6 +241,61 @@ struct QueryOperands {
       v += dpp_f32<kDppRowRor8>(v);
     }
     return v;
+  }
+
+  // Score of one (query, key) pair per lane for the 16-key tile held in `a` (pair as in
+  // head_sum).  EXACT: all GMAX head blocks are used; the MFMA of block g+1 is issued
+  // before the epilogue of block g so that the matrix core and the VALU overlap.
+  // `need`: the lane's key is visible to its query; `th_hi`: the high word of the query's
+  // threshold key (0: none yet).  LIN rescoring looks only at keys that could be kept.
+  template <bool EXACT>
+  __device__ __forceinline__ float tile_score(const i32x8& a, int g_rt, int jsel, bool need,
+                                              uint32_t th_hi) const {
+    if constexpr (LIN) {
+      static_assert(EXACT, "the linear form uses every head block");
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 x = mfma_e4m3_16x16x128(a, bq[0]);
+#pragma unroll
+      for (int g = 1; g < GMAX; ++g) {
+        const f32x4 y = mfma_e4m3_16x16x128(a, bq[g]);
+        accumulate_abs(acc, x, wv[g - 1]);
+        x = y;
+      }
+      const f32x4 l = mfma_e4m3_16x16x128(a, bl);
+      accumulate_abs(acc, x, wv[GMAX - 1]);
+      const f32x4 lin = {l[0] * sl, l[1] * sl, l[2] * sl, l[3] * sl};
+      const float ah = head_sum(acc, jsel);  // 1/2 sum_h w_h |x_h|
+      float s = ah + head_sum(lin, jsel);    // + 1/2 sum_h w_h x_h
+      const bool again = need && !(s > 0.125f * ah) && th_hi <= f32_to_ordered(0.25f * ah);
+      if (ballot64(again)) {
+        const float e = 2.f * plain_score(a, jsel);
+        s = again ? e : s;
+      }
+      return s;
+    } else if constexpr (EXACT) {
+      return plain_score(a, jsel);
+    } else {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (g < g_rt) accumulate(acc, mfma_e4m3_16x16x128(a, bq[g]), wv[g]);
+      }
+      return head_sum(acc, jsel);
+    }
+  }
+
+  // sum_h wv_h max(0, x_h) over all GMAX head blocks
+  __device__ __forceinline__ float plain_score(const i32x8& a, int jsel) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 x = mfma_e4m3_16x16x128(a, bq[0]);
+#pragma unroll
+    for (int g = 1; g < GMAX; ++g) {
+      const f32x4 y = mfma_e4m3_16x16x128(a, bq[g]);
+      accumulate(acc, x, wv[g - 1]);
+      x = y;
+    }
+    accumulate(acc, x, wv[GMAX - 1]);
+    return head_sum(acc, jsel);
   }
 };
 
@@ -469,7 +590,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   const int ks = split * p.split_len;
   const int ke = min(ks + p.split_len, n_max);
 
-  QueryOperands<QC, GMAX, DI> qo;
+  QueryOperands<QC, GMAX, DI, (QC == 4 && GMAX == 16 && EXACT)> qo;
   qo.load(p, b, t, qvalid, t0, j, lg);
 
   // lane constants: key offset of the lane's pair within a tile, the bound on candidate
@@ -565,7 +686,8 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
       float sc[PF];
 #pragma unroll
       for (int ui = 0; ui < PF; ++ui) {
-        sc[ui] = qo.template tile_score<EXACT>(ring[ui], p.g, jsel);
+        const bool need = (j0 + ui < count) & (base + 16 * tile_idx(j0 + ui) + koff < lim);
+        sc[ui] = qo.template tile_score<EXACT>(ring[ui], p.g, jsel, need, (uint32_t)(th_lane >> 32));
         ring[ui] = load_key_tile(krs, tile_off(j0 + ui + PF));
         if constexpr (QC == 1) __builtin_amdgcn_sched_barrier(0);
       }
@@ -916,7 +1038,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
   kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
   const int n_q = qvalid ? visible_keys(pos0, kvl, t) : 0;
 
-  QueryOperands<QC, GMAX, DI> qo;
+  QueryOperands<QC, GMAX, DI, (GMAX == 16 && EXACT)> qo;
   qo.load(p, b, t, qvalid, p.t_begin + i0, j, lg);
 
   const uint8_t* kbase = p.k + (size_t)b * p.S_max * DI;
@@ -924,8 +1046,8 @@ __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
   for (int s0 = 0; s0 < p.S_max; s0 += 16) {
     const int srow = min(s0 + r16, p.S_max - 1);
     const i32x8 a = load_row_slice<DI>(kbase + (size_t)srow * DI, lg);
-    const float sc = qo.template tile_score<EXACT>(a, p.g, jsel);
     const int s = s0 + 4 * lg + jsel;
+    const float sc = qo.template tile_score<EXACT>(a, p.g, jsel, qvalid && s < n_q, 0u);
     if (qvalid && s < p.S_max) orow[s] = s < n_q ? sc + 0.0f : -__builtin_inff();
   }
 }

@@ -181,11 +181,14 @@ def _e4m3_code(v):
     return int(np.nonzero(O.E4M3_TABLE == v)[0][0])
 
 
-def test_topk_known_top_set_with_zero_ties():
+@pytest.mark.parametrize("H,S", [(8, 3000), (64, 3000), (64, 20000)])
+def test_topk_known_top_set_with_zero_ties(H, S):
     """Queries >= 0 and unplanted keys <= 0 give exact zero scores; planted keys have
-    closed-form distinct scores.  The kept set is known exactly (no tie band)."""
+    closed-form distinct scores.  The kept set is known exactly (no tie band).  With 64
+    heads the scores come from the |x| + linear-MFMA form, whose zero keys are rescored
+    (20000 keys: also after a threshold sample)."""
     rng = np.random.default_rng(21)
-    B, T, S, H, d, k = 2, 8, 3000, 8, 128, 100
+    B, T, d, k = 2, 8, 128, 100
     neg = [c for c in range(256) if O.E4M3_TABLE[c] <= 0 and not np.isnan(O.E4M3_TABLE[c])]
     kc = rng.choice(neg, size=(B, S, d)).astype(np.uint8)
     vals = [0.5 + 0.0625 * i for i in range(8)] + [1.0 + 0.125 * i for i in range(8)]
@@ -211,6 +214,16 @@ def test_topk_known_top_set_with_zero_ties():
             order = sorted(vis, key=lambda s: -vis[s])[:k]
             zeros = [s for s in range(n) if s not in vis][: k - len(order)]
             assert idx[b, t].tolist() == sorted(order + zeros), f"b={b} t={t}"
+    # every score is exact here: 0 for the unplanted keys, H * d * 0.25 * x for planted ones
+    sc = bd.score(dev(qc), dev(kc), dev(w), dev(pos0), dev(kvl)).cpu().numpy()
+    for b in range(B):
+        for t in range(T):
+            n = min(int(pos0[b]) + t + 1, S)
+            want = np.zeros(n, dtype=np.float32)
+            for s, x in planted[b].items():
+                if s < n:
+                    want[s] = H * d * 0.25 * x
+            assert np.array_equal(sc[b, t, :n], want), f"scores b={b} t={t}"
 
 
 def test_topk_is_deterministic():
