@@ -118,7 +118,9 @@ __device__ __forceinline__ int visible_keys(int pos0, int kvl, int t) {
 // come out as rounding noise, so a visible key whose score is not above 1/16 of its
 // |x| sum A is scored again the plain way in the same tile, which keeps exact zeros
 // exact -- unless its query's threshold is already above A/8: its score, either way, is
-// at most A/16 plus rounding error, far below A/8, so it cannot be kept.
+// at most A/16 plus rounding error, far below A/8, so it cannot be kept.  That test needs
+// w >= 0 (then A bounds the rounding of both halves): the kernels take this form only for
+// waves whose queries' head weights are all >= 0, and the plain one otherwise.
 template <int QC, int GMAX, int DI, bool LIN>
 struct QueryOperands {
   i32x8 bq[GMAX];
@@ -546,25 +548,27 @@ __device__ __forceinline__ int32_t untag_index(uint64_t key) {
   return (int32_t)(kIndexMask - ((uint32_t)key & kIndexMask));
 }
 
-template <int QC, int GMAX, int DI, bool EXACT>
-__global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
+// Whether every head weight of query rows [t0, min(t0 + 4, t_end)) of sequence b is >= 0;
+// the same answer in every lane.  A wave's four queries share one scoring form, so with
+// mixed-sign weights a query's scores depend on its neighbours' weights through that choice
+// (both forms stay within the same error bound).
+__device__ __forceinline__ bool weights_nonneg(const IxArgs& p, int b, int t0, int t_end) {
+  bool neg = false;
+  for (int e = (int)(threadIdx.x & 63); e < 4 * p.H_I; e += 64) {
+    const int t = t0 + e / p.H_I;
+    if (t < t_end) neg |= p.w[((size_t)b * p.T + t) * p.H_I + e % p.H_I] < 0.f;
+  }
+  return ballot64(neg) == 0;
+}
+
+template <int QC, int GMAX, int DI, bool EXACT, bool LIN>
+__device__ __forceinline__ void topk_partial_body(const IxArgs& p, int64_t u, int split, int b,
+                                                  int t0, uint32_t* hist, uint64_t* stage) {
   constexpr int HC = 16 / QC;
   // key tiles in flight per wave (the 16-block case keeps 128 VGPRs of query operands)
   constexpr int PF = prefetch_tiles(GMAX);
   constexpr int WSTG = wave_stage_entries(GMAX);
-  __shared__ uint32_t hist_all[kBlockWaves][kHistBins];
-  __shared__ uint64_t stage_all[kBlockWaves][WSTG];
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  uint32_t* hist = hist_all[wid];
-  uint64_t* stage = stage_all[wid];
-  const int64_t u = (int64_t)blockIdx.x * kBlockWaves + wid;
-  if (u >= p.units) return;
-  const int split = (int)(u % p.n_splits);
-  const int64_t r = u / p.n_splits;
-  const int b = (int)(r % p.B);
-  const int qg = p.qgroups - 1 - (int)(r / p.B);  // latest (heaviest) query groups first
-  const int t0 = qg * QC;
   const int r16 = lane & 15, lg = lane >> 4;
   const int qi = r16 / HC, j = r16 % HC;
   const int jsel = j & 3;
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   const int ks = split * p.split_len;
   const int ke = min(ks + p.split_len, n_max);
 
-  QueryOperands<QC, GMAX, DI, (QC == 4 && GMAX == 16 && EXACT)> qo;
+  QueryOperands<QC, GMAX, DI, LIN> qo;
   qo.load(p, b, t, qvalid, t0, j, lg);
 
   // lane constants: key offset of the lane's pair within a tile, the bound on candidate
@@ -825,6 +829,29 @@ __global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
   }
 }
 
+template <int QC, int GMAX, int DI, bool EXACT>
+__global__ __launch_bounds__(kBlock, 2) void ix_topk_partial_kernel(IxArgs p) {
+  constexpr int WSTG = wave_stage_entries(GMAX);
+  __shared__ uint32_t hist_all[kBlockWaves][kHistBins];
+  __shared__ uint64_t stage_all[kBlockWaves][WSTG];
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int64_t u = (int64_t)blockIdx.x * kBlockWaves + wid;
+  if (u >= p.units) return;
+  const int split = (int)(u % p.n_splits);
+  const int64_t r = u / p.n_splits;
+  const int b = (int)(r % p.B);
+  const int qg = p.qgroups - 1 - (int)(r / p.B);  // latest (heaviest) query groups first
+  const int t0 = qg * QC;
+  // the |x| + linear-MFMA form at 4 queries and 64 heads when the weights allow it
+  if constexpr (QC == 4 && GMAX == 16 && EXACT) {
+    if (weights_nonneg(p, b, t0, p.T)) {
+      topk_partial_body<QC, GMAX, DI, EXACT, true>(p, u, split, b, t0, hist_all[wid], stage_all[wid]);
+      return;
+    }
+  }
+  topk_partial_body<QC, GMAX, DI, EXACT, false>(p, u, split, b, t0, hist_all[wid], stage_all[wid]);
+}
+
 // ------------------------------------------------------------------ merge of key splits
 
 constexpr int kMergeBlock = 512;
@@ -1016,16 +1043,10 @@ __global__ __launch_bounds__(kMergeBlock) void ix_topk_merge_kernel(IxArgs p) {
 
 // ------------------------------------------------------------------ score rows (Stage 1 only)
 
-template <int GMAX, int DI, bool EXACT>
-__global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
+template <int GMAX, int DI, bool EXACT, bool LIN>
+__device__ __forceinline__ void score_body(const IxArgs& p, int b, int i0) {
   constexpr int QC = 4, HC = 4;
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int64_t u = (int64_t)blockIdx.x * kBlockWaves + wid;
-  if (u >= p.units) return;
-  const int b = (int)(u % p.B);
-  const int qg = (int)(u / p.B);
-  const int i0 = qg * QC;  // row within the window
   const int r16 = lane & 15, lg = lane >> 4;
   const int qi = r16 / HC, j = r16 % HC;
   const int jsel = j & 3;
@@ -1038,7 +1059,7 @@ __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
   kvl = kvl < 0 ? 0 : (kvl > p.S_max ? p.S_max : kvl);
   const int n_q = qvalid ? visible_keys(pos0, kvl, t) : 0;
 
-  QueryOperands<QC, GMAX, DI, (GMAX == 16 && EXACT)> qo;
+  QueryOperands<QC, GMAX, DI, LIN> qo;
   qo.load(p, b, t, qvalid, p.t_begin + i0, j, lg);
 
   const uint8_t* kbase = p.k + (size_t)b * p.S_max * DI;
@@ -1050,6 +1071,22 @@ __global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
     const float sc = qo.template tile_score<EXACT>(a, p.g, jsel, qvalid && s < n_q, 0u);
     if (qvalid && s < p.S_max) orow[s] = s < n_q ? sc + 0.0f : -__builtin_inff();
   }
+}
+
+template <int GMAX, int DI, bool EXACT>
+__global__ __launch_bounds__(kBlock, 2) void ix_score_kernel(IxArgs p) {
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int64_t u = (int64_t)blockIdx.x * kBlockWaves + wid;
+  if (u >= p.units) return;
+  const int b = (int)(u % p.B);
+  const int i0 = (int)(u / p.B) * 4;  // row within the window
+  if constexpr (GMAX == 16 && EXACT) {
+    if (weights_nonneg(p, b, p.t_begin + i0, p.t_begin + p.rows)) {
+      score_body<GMAX, DI, EXACT, true>(p, b, i0);
+      return;
+    }
+  }
+  score_body<GMAX, DI, EXACT, false>(p, b, i0);
 }
 
 template <typename F>

@@ -21,9 +21,11 @@ def _wl(**kw):
     return Workload(**base)
 
 
-def _run_scores(wl, t_begin=0, t_end=None):
+def _run_scores(wl, t_begin=0, t_end=None, tweak=None):
     say(f"[ix_score] {wl.name} B={wl.B} T={wl.T} S={wl.S} H_I={wl.H_I} d_I={wl.d_I} seed={wl.seed}")
     ind = synth.indexer_inputs(wl, device=DEV)
+    if tweak:
+        tweak(ind)
     t_end = wl.T if t_end is None else t_end
     sc = bd.score(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], t_begin, t_end)
     torch.cuda.synchronize()
@@ -49,10 +51,12 @@ def test_score_ragged_lengths_and_head_counts():
     _run_scores(wl2)
 
 
-def _run_topk(wl, check_sel=True):
+def _run_topk(wl, check_sel=True, tweak=None):
     say(f"[ix_topk] {wl.name} B={wl.B} T={wl.T} S={wl.S} H_I={wl.H_I} d_I={wl.d_I} k={wl.k} "
         f"seed={wl.seed}")
     ind = synth.indexer_inputs(wl, device=DEV)
+    if tweak:
+        tweak(ind)
     idx, sel = bd.topk(ind["q_I"], ind["k_I"], ind["w"], ind["q_pos0"], ind["kv_len"], wl.k,
                        with_scores=True)
     torch.cuda.synchronize()
@@ -75,6 +79,23 @@ def _run_topk(wl, check_sel=True):
                 assert np.all(np.isneginf(sel[b, t, m:]))
     say(f"  swaps inside the tie band: {swaps}")
     return idx
+
+
+def _flip_every_third_head(ind):
+    H = ind["w"].shape[-1]
+    sign = torch.where(torch.arange(H, device=ind["w"].device) % 3 == 0, -1.0, 1.0)
+    ind["w"] = (ind["w"] * sign).contiguous()
+
+
+def test_mixed_sign_head_weights():
+    """Head weights of both signs at 64 heads (scores may be negative; keys whose heads are
+    all <= 0 still score exactly 0), through ix_score and the fused top-k with and without a
+    threshold sample."""
+    wl = _wl(B=2, T=40, S=700, pos0s=(660, 300), kv_lens=(700, 500), seed=31)
+    _run_scores(wl, tweak=_flip_every_third_head)
+    _run_topk(wl, tweak=_flip_every_third_head)
+    wl2 = _wl(B=1, T=9, S=9000, pos0=8991, k=256, seed=32, planted=8)
+    _run_topk(wl2, tweak=_flip_every_third_head)
 
 
 def test_topk_tiny_all_rows():
@@ -181,12 +202,13 @@ def _e4m3_code(v):
     return int(np.nonzero(O.E4M3_TABLE == v)[0][0])
 
 
-@pytest.mark.parametrize("H,S", [(8, 3000), (64, 3000), (64, 20000)])
-def test_topk_known_top_set_with_zero_ties(H, S):
+@pytest.mark.parametrize("H,S,mixed", [(8, 3000, False), (64, 3000, False), (64, 20000, False),
+                                       (64, 3000, True)])
+def test_topk_known_top_set_with_zero_ties(H, S, mixed):
     """Queries >= 0 and unplanted keys <= 0 give exact zero scores; planted keys have
     closed-form distinct scores.  The kept set is known exactly (no tie band).  With 64
     heads the scores come from the |x| + linear-MFMA form, whose zero keys are rescored
-    (20000 keys: also after a threshold sample)."""
+    (20000 keys: also after a threshold sample; mixed: every third head weight is -1)."""
     rng = np.random.default_rng(21)
     B, T, d, k = 2, 8, 128, 100
     neg = [c for c in range(256) if O.E4M3_TABLE[c] <= 0 and not np.isnan(O.E4M3_TABLE[c])]
@@ -202,6 +224,8 @@ def test_topk_known_top_set_with_zero_ties(H, S):
             kc[b, s, :] = _e4m3_code(x)
     qc = np.full((B, T, H, d), _e4m3_code(0.25), dtype=np.uint8)
     w = np.ones((B, T, H), dtype=np.float32)
+    if mixed:
+        w[..., ::3] = -1.0
     pos0 = np.array([S - T, 1500], dtype=np.int32)
     kvl = np.array([S, S], dtype=np.int32)
     dev = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
@@ -222,7 +246,7 @@ def test_topk_known_top_set_with_zero_ties(H, S):
             want = np.zeros(n, dtype=np.float32)
             for s, x in planted[b].items():
                 if s < n:
-                    want[s] = H * d * 0.25 * x
+                    want[s] = w[b, t].sum() * d * 0.25 * x
             assert np.array_equal(sc[b, t, :n], want), f"scores b={b} t={t}"
 
 
