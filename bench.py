@@ -288,6 +288,10 @@ def measured_peaks(dev, sh, codes=None):
             t = timed(lambda: pk.ix_peak_read(big.data_ptr(), 2 << 30, blocks, nt, xr.data_ptr(), sh))
             if (2 << 30) / t / 1e9 > read:
                 read, read_grid = round((2 << 30) / t / 1e9, 1), {"blocks": blocks, "nontemporal": nt}
+    # the same stream drawn by 1024 waves (256 blocks), the decode step's indexer sweep: one
+    # wave per (query, key split), 64 queries x 16 splits
+    read_1024 = round(max((2 << 30) / timed(lambda: pk.ix_peak_read(
+        big.data_ptr(), 2 << 30, 256, nt, xr.data_ptr(), sh)) / 1e9 for nt in (1, 0)), 1)
     del src, big
     gather, gather_grid = {}, {}
     n = 1 << 25
@@ -317,7 +321,7 @@ def measured_peaks(dev, sh, codes=None):
             gather["16GiB"], gather_grid["16GiB"] = round(n * 256 / t / 1e9, 1), blocks
     del table, rows
     return {"fp8_mfma_tflops_by_valu_per_mfma": mfma, "copy_GB_per_s": copy,
-            "read_GB_per_s": read, "read_grid": read_grid, "gather_256B_rows_GB_per_s": gather,
+            "read_GB_per_s": read, "read_grid": read_grid, "read_GB_per_s_1024_waves": read_1024, "gather_256B_rows_GB_per_s": gather,
             "gather_grid": gather_grid}
 
 
@@ -1234,6 +1238,8 @@ def main():
         d["indexer_frac_of_read_ceiling"] = round(rate / peaks["read_GB_per_s"], 4)
         d["indexer_frac_of_read_ceiling_cold"] = round(
             d["indexer_bytes"] / (d["ix_topk_ms_cold"] / 1e3) / 1e9 / peaks["read_GB_per_s"], 4)
+        # against the stream at the sweep's own occupancy (the best grid has 2-4x the waves)
+        d["indexer_frac_of_read_at_1024_waves"] = round(rate / peaks["read_GB_per_s_1024_waves"], 4)
         if gather_hbm:
             g = peaks["gather_256B_rows_GB_per_s"]
             ceil = g.get("16GiB", g["2GiB"])
