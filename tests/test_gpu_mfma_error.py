@@ -78,6 +78,36 @@ def test_fp8_mfma_error_within_half_the_bounds(d_I):
         f"FP8 MFMA error {worst_l2:.3e} |q||k| within 2x of the backward's exact-mask window"
 
 
+@pytest.mark.parametrize("d_I", [64, 128])
+def test_64_head_scores_within_half_the_bound(d_I):
+    """At 64 heads the indexer takes the head sum as 1/2 sum w|x| plus one MFMA of the keys with
+    u = sum_h w_h q_h split into four scaled e4m3 terms.  Its error against the exact score,
+    relative to N = sum_h w_h sum_c |q_hc k_c|, must stay within half of FP8_MFMA_REL too, on
+    the same three kinds of codes, with dense weights (u then spans a wide range)."""
+    rng = np.random.default_rng(91 + d_I)
+    H, T, S = 64, 64, 2048
+    worst = 0.0
+    for kind in ("full range", "normal", "dominant"):
+        q, k = _fp8_case(kind, d_I, rng, T=T, S=S, H=H)
+        T_ = q.shape[1]
+        w = rng.uniform(0.0, 1.0, (1, T_, H)).astype(np.float32)
+        sc = bd.score(torch.from_numpy(q).to(DEV), torch.from_numpy(k).to(DEV),
+                      torch.from_numpy(w).to(DEV),
+                      torch.tensor([S - 1], dtype=torch.int32, device=DEV),
+                      torch.tensor([S], dtype=torch.int32, device=DEV)).cpu().numpy()[0]
+        qv = O.decode_e4m3(q[0])                                       # [T, H, d_I]
+        kv = O.decode_e4m3(k[0])                                       # [S, d_I]
+        wd = w[0].astype(np.float64)
+        x = np.einsum("thc,sc->ths", qv, kv)                           # exact
+        exact = np.einsum("th,ths->ts", wd, np.maximum(x, 0.0))
+        mag = np.einsum("th,thc->tc", wd, np.abs(qv)) @ np.abs(kv).T
+        err = np.abs(sc.astype(np.float64) - exact)
+        r = float((err / np.maximum(mag, 1e-300)).max())
+        say(f"[64-head scores] d_I={d_I} {kind}: {T_} x {S} scores; worst err / N {r:.3e}")
+        worst = max(worst, r)
+    assert worst <= FP8_MFMA_REL / 2, f"64-head score error ratio {worst:.3e} within 2x of the bound"
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bf16_mfma_error_within_half_the_bound(d):
     g = torch.Generator(device="cpu").manual_seed(83 + d)
