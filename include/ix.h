@@ -15,6 +15,12 @@
  * Concrete indexer form implemented here: for query token t and key token s,
  *     score(t,s) = sum_h w[t,h] * max(0, sum_c q_I[t,h,c] * k_I[s,c])
  * with FP8 (OCP e4m3) q_I/k_I, fp32 w, fp32 accumulation.
+ * Accuracy of a score: within about eps * sum_h |w_h| sum_c |q_I[t,h,c] k_I[s,c]|, eps the
+ * FP8 matrix core's relative error (measured below 2.4e-4).  With 64 indexer heads and
+ * more than 3 query rows, a group of 4 query rows whose head weights are all >= 0 takes
+ * the head sum as 1/2 sum_h w_h |x_h| + 1/2 k . u, u = sum_h w_h q_I[t,h,:] in four scaled
+ * e4m3 terms (about 1.05x that bound).  Either way a key whose every head dot product is
+ * <= 0 scores exactly 0 wherever the top-k could still keep it, and in ix_score always.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE memory owned by the caller; the library never
