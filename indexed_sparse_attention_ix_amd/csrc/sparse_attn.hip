@@ -436,7 +436,9 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
     return (c < c_end && e < p.k && j >= 0 && j < kvl) ? j : -1;
   };
   // one chunk in registers: its K rows as A operands (lane: row r16, pieces 4m + lg), its V
-  // rows for the stage, and which of its 16 keys are valid
+  // rows for the stage, and which of its 16 keys are valid.  The rows are loaded
+  // non-temporal: this kernel serves decode-size grids, whose caches (gigabytes per layer)
+  // come from HBM and are read once per step
   struct Rows {
     bf16x8 ka[MC];
     i32x4 vd[NIV];
@@ -449,11 +451,11 @@ __global__ __launch_bounds__(kAttnBlock, 3) void sparse_attn_light_kernel(AttnAr
     const uint32_t kbase = roff + 16u * lg;
 #pragma unroll
     for (int m = 0; m < MC; ++m)
-      r.ka[m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(kbase + 64u * m), 0, 0));
+      r.ka[m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(kbase + 64u * m), 0, kLoadNT));
 #pragma unroll
     for (int j = 0; j < NIV; ++j) {
       const uint32_t off = (uint32_t)__shfl((int)roff, rho * NIV + j) + 16u * s;
-      r.vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+      r.vd[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, kLoadNT));
     }
     r.mask = (uint32_t)ballot64(jk >= 0) & 0xFFFFu;  // lanes 0..15 hold keys 0..15
   };
