@@ -65,13 +65,15 @@ ix_status ix_peak_gather(const void *table, size_t table_bytes, const int32_t *r
  * ix_peak_gather_wide -- ix_peak_gather over a table of n_seg segments of seg_bytes each
  * (a footprint of up to 64 GiB): load step i of wave w (8 rows per lane group) reads the rows
  * rows[r], counted within segment (w + i) mod n_seg.  seg_bytes: <= 1 GiB, a multiple of 256;
- * rows outside a segment read as zero.  n_seg: 1..64.  out: as for ix_peak_gather.
+ * rows outside a segment read as zero.  n_seg: 1..64.  nontemporal = 1 marks the loads
+ * non-temporal (as the decode attention's row loads), 0 makes them ordinary loads.
+ * out: as for ix_peak_gather.
  * Errors: IX_ERR_INVALID for NULL pointers, n < 0, a bad segment size, count or alignment,
- * or blocks outside 1..65536.
+ * blocks outside 1..65536 or nontemporal outside {0, 1}.
  */
 ix_status ix_peak_gather_wide(const void *table, size_t seg_bytes, int32_t n_seg,
-                              const int32_t *rows, int64_t n, int32_t blocks, uint32_t *out,
-                              hipStream_t stream);
+                              const int32_t *rows, int64_t n, int32_t blocks, int32_t nontemporal,
+                              uint32_t *out, hipStream_t stream);
 
 /*
  * ix_peak_gather_selection -- reads, for every query and KV head, the K and V rows its

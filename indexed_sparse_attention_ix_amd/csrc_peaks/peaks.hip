@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kPeakBlock) void peak_copy_kernel(const i32x4* __re
 // of one resource is spread over the whole grid.
 constexpr int kGatherInFlight = 8;
 
+template <int AUX>
 __global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const unsigned char* __restrict__ table,
                                                                  uint32_t seg_bytes, int n_seg,
                                                                  const int32_t* __restrict__ rows,
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kPeakBlock) void peak_gather_kernel(const unsigned 
     for (int j = 0; j < kGatherInFlight; ++j) {
       const int64_t r = base + (int64_t)j * groups;
       const uint32_t off = r < n ? (uint32_t)rows[r] * 256u + 16u * s : 0x80000000u;
-      v[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+      v[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, AUX));
     }
 #pragma unroll
     for (int j = 0; j < kGatherInFlight; ++j) x ^= (uint32_t)(v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3]);
@@ -389,15 +390,15 @@ ix_status ix_peak_gather(const void* table, size_t table_bytes, const int32_t* r
     return peak_fail(IX_ERR_INVALID, "table_bytes must be a positive multiple of 256, at most 2 GiB");
   if (!aligned16(table)) return peak_fail(IX_ERR_INVALID, "table must be 16-byte aligned");
   if (n == 0) return IX_OK;
-  hipLaunchKernelGGL(peak_gather_kernel, dim3(blocks), dim3(kPeakBlock), 0, stream,
+  hipLaunchKernelGGL(peak_gather_kernel<0>, dim3(blocks), dim3(kPeakBlock), 0, stream,
                      reinterpret_cast<const unsigned char*>(table), (uint32_t)table_bytes, 1, rows,
                      n, out);
   return launched("ix_peak_gather");
 }
 
 ix_status ix_peak_gather_wide(const void* table, size_t seg_bytes, int32_t n_seg,
-                              const int32_t* rows, int64_t n, int32_t blocks, uint32_t* out,
-                              hipStream_t stream) {
+                              const int32_t* rows, int64_t n, int32_t blocks, int32_t nontemporal,
+                              uint32_t* out, hipStream_t stream) {
   using namespace ix;
   if (!table || !rows || !out) return peak_fail(IX_ERR_INVALID, "NULL table, rows or out");
   if (n < 0) return peak_fail(IX_ERR_INVALID, "n=%lld must be >= 0", (long long)n);
@@ -406,9 +407,12 @@ ix_status ix_peak_gather_wide(const void* table, size_t seg_bytes, int32_t n_seg
   if (seg_bytes == 0 || seg_bytes % 256 || seg_bytes > ((size_t)1 << 30))
     return peak_fail(IX_ERR_INVALID, "seg_bytes must be a positive multiple of 256, at most 1 GiB");
   if (n_seg < 1 || n_seg > 64) return peak_fail(IX_ERR_INVALID, "n_seg=%d (1..64)", n_seg);
+  if (nontemporal != 0 && nontemporal != 1)
+    return peak_fail(IX_ERR_INVALID, "nontemporal=%d (0 or 1)", nontemporal);
   if (!aligned16(table)) return peak_fail(IX_ERR_INVALID, "table must be 16-byte aligned");
   if (n == 0) return IX_OK;
-  hipLaunchKernelGGL(peak_gather_kernel, dim3(blocks), dim3(kPeakBlock), 0, stream,
+  auto kern = nontemporal ? peak_gather_kernel<kLoadNT> : peak_gather_kernel<0>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kPeakBlock), 0, stream,
                      reinterpret_cast<const unsigned char*>(table), (uint32_t)seg_bytes, (int)n_seg,
                      rows, n, out);
   return launched("ix_peak_gather_wide");

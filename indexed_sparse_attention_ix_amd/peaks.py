@@ -37,7 +37,7 @@ def load(path: str = LIB_PATH):
     L.ix_peak_gather.argtypes = [c_void_p, c_size_t, c_void_p, c_int64, c_int32, c_void_p, c_void_p]
     L.ix_peak_gather_wide.restype = c_int32
     L.ix_peak_gather_wide.argtypes = [c_void_p, c_size_t, c_int32, c_void_p, c_int64, c_int32,
-                                      c_void_p, c_void_p]
+                                      c_int32, c_void_p, c_void_p]
     L.ix_peak_gather_selection.restype = c_int32
     L.ix_peak_gather_selection.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p] + [c_int32] * 8 + \
         [c_void_p, c_void_p]
@@ -68,8 +68,9 @@ def ix_peak_gather(table, table_bytes, rows, n, blocks, out, stream=0):
     _check(load().ix_peak_gather(table, table_bytes, rows, n, blocks, out, stream))
 
 
-def ix_peak_gather_wide(table, seg_bytes, n_seg, rows, n, blocks, out, stream=0):
-    _check(load().ix_peak_gather_wide(table, seg_bytes, n_seg, rows, n, blocks, out, stream))
+def ix_peak_gather_wide(table, seg_bytes, n_seg, rows, n, blocks, nontemporal, out, stream=0):
+    _check(load().ix_peak_gather_wide(table, seg_bytes, n_seg, rows, n, blocks, nontemporal, out,
+                                      stream))
 
 
 def ix_peak_gather_selection(kc, vc, idx, kv_len, B, T, S_max, H_kv, d, k, splits, blocks_per_cu,

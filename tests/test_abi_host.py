@@ -389,14 +389,15 @@ def test_peak_validation_codes():
     assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, 5, 0, FAKE) == bd.IX_ERR_INVALID
     assert status_of(pk.ix_peak_gather, FAKE, 256, FAKE, 0, 2048, FAKE) == bd.IX_OK
     wide = pk.ix_peak_gather_wide
-    assert status_of(wide, FAKE, 1000, 2, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, FAKE, (1 << 30) + 256, 2, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, FAKE, 256, 0, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, FAKE, 256, 65, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, FAKE, 256, 2, FAKE, -1, 2048, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, FAKE, 256, 2, FAKE, 5, 0, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, 0, 256, 2, FAKE, 5, 2048, FAKE) == bd.IX_ERR_INVALID
-    assert status_of(wide, FAKE, 1 << 30, 64, FAKE, 0, 2048, FAKE) == bd.IX_OK
+    assert status_of(wide, FAKE, 1000, 2, FAKE, 5, 2048, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, (1 << 30) + 256, 2, FAKE, 5, 2048, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, 256, 0, FAKE, 5, 2048, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, 256, 65, FAKE, 5, 2048, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, 256, 2, FAKE, -1, 2048, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, 256, 2, FAKE, 5, 0, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, 256, 2, FAKE, 5, 2048, 2, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, 0, 256, 2, FAKE, 5, 2048, 0, FAKE) == bd.IX_ERR_INVALID
+    assert status_of(wide, FAKE, 1 << 30, 64, FAKE, 0, 2048, 1, FAKE) == bd.IX_OK
     sel = pk.ix_peak_gather_selection
     assert status_of(sel, FAKE, FAKE, 0, FAKE, 1, 4, 100, 1, 128, 64, 1, 0, FAKE) == bd.IX_ERR_INVALID
     assert status_of(sel, FAKE, FAKE, FAKE, FAKE, 1, 4, 100, 1, 96, 64, 1, 0, FAKE) == bd.IX_ERR_UNSUPPORTED

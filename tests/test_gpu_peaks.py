@@ -42,8 +42,8 @@ def test_peak_gather_checksum(blocks):
     assert int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))) == int(want)
 
 
-@pytest.mark.parametrize("blocks", [7, 1000])
-def test_peak_gather_wide_checksum(blocks):
+@pytest.mark.parametrize("blocks,nt", [(7, 0), (1000, 0), (1000, 1)])
+def test_peak_gather_wide_checksum(blocks, nt):
     """Load step i of wave w reads its rows in segment (w + i) mod n_seg: the XOR of all words
     read, computed on the host from that mapping, with rows outside a segment reading zero."""
     n_seg, seg_rows, n = 3, 1024, 70001
@@ -54,7 +54,7 @@ def test_peak_gather_wide_checksum(blocks):
     out = torch.zeros(blocks, dtype=torch.int32, device=DEV)
     table_d, rows_d = table.to(DEV), rows.to(DEV)
     pk.ix_peak_gather_wide(table_d.data_ptr(), seg_rows * 256, n_seg, rows_d.data_ptr(), n, blocks,
-                           out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                           nt, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     row_x = np.bitwise_xor.reduce(table.numpy().view(np.uint32).reshape(n_seg, seg_rows, 64), axis=2)
     groups = blocks * 256 // 16           # 16 lanes per row read
