@@ -268,7 +268,9 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
 
     // dV += P^T dO and dK += (sm_scale dS)^T Q, row by row into the gradient caches, or
     // (with a pair buffer) each selected pair's dV | dK rows in bf16 or fp32, staged in the
-    // K / V stage (no longer read in this chunk) and written in pair order
+    // K / V stage (no longer read in this chunk) and written in pair order, non-temporal: the
+    // rows (tens of GB) are read back once by the key sums, and cached they would evict the
+    // K / V rows this kernel gathers
     if constexpr (F32ROWS) {
       // fp32: the dV rows, then the dK rows, each a [pair][D] tile filling the stage.  The
       // 16-byte pieces of a row are swizzled by the pair's lane group (pair bits 2..3), so
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
           const int ent = c * kChunk + e;
           if (ent < p.k) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(cf + e * D + 4 * (pc ^ (4 * ((e >> 2) & 3))));
-            *reinterpret_cast<f32x4*>(dst0 + (size_t)ent * p.H_kv * 2 * D + half * D + 4 * pc) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst0 + (size_t)ent * p.H_kv * 2 * D + half * D + 4 * pc));
           }
         }
         lds_wait();
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(kAttnBlock, 2) void sparse_attn_bwd_kernel(AttnBwdA
         const int ent = c * kChunk + e;
         if (ent < p.k) {
           const i32x4 v = *reinterpret_cast<const i32x4*>(cb + (size_t)e * 2 * D + 8 * pc);
-          *reinterpret_cast<i32x4*>(dst0 + (size_t)ent * p.H_kv * 2 * D + 8 * pc) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(dst0 + (size_t)ent * p.H_kv * 2 * D + 8 * pc));
         }
       }
       lds_wait();

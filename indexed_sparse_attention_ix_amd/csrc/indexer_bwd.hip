@@ -38,6 +38,8 @@ namespace ix {
 
 namespace {
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
 constexpr int kBwdChunk = 32;
 constexpr int kBwdThreads = 256;
 constexpr int kBwdHeads = 64;
@@ -324,15 +326,16 @@ __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_ker
     __syncthreads();
 
     // ---- with a pair buffer: the chunk's rows in bf16 or fp32, in pair order (summed per
-    // key later)
+    // key later), stored non-temporal (read back once, and too large to keep in the caches)
     if constexpr (STORE) {
       if constexpr (F32ROWS) {
         float* dst0 = reinterpret_cast<float*>(contrib) + ((size_t)(row - row0) * k + j0) * DI;
         for (int r = 8 * wv; r < 8 * wv + 8; ++r) {
           if (j0 + r >= k) break;
           if (2 * lane < DI)
-            *reinterpret_cast<float2*>(dst0 + (size_t)r * DI + 2 * lane) =
-                make_float2(sm.dk[r][2 * lane], sm.dk[r][2 * lane + 1]);
+            __builtin_nontemporal_store(
+                (f32x2v){sm.dk[r][2 * lane], sm.dk[r][2 * lane + 1]},
+                reinterpret_cast<f32x2v*>(dst0 + (size_t)r * DI + 2 * lane));
         }
         __syncthreads();
         continue;
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kBwdThreads, kBwdWaves<STORE>) void indexer_bwd_ker
         if (2 * lane < DI) {
           const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)sm.dk[r][2 * lane]) |
                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)sm.dk[r][2 * lane + 1]) << 16);
-          *reinterpret_cast<uint32_t*>(dst0 + (size_t)r * DI + 2 * lane) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(dst0 + (size_t)r * DI + 2 * lane));
         }
       }
       __syncthreads();
