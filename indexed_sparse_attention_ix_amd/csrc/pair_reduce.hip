@@ -11,8 +11,9 @@
 //     order and the lists, and the sums below, are the same on every run;
 //  3. the gradient kernel writes each pair's rows (bf16, or fp32 at the caller's choice) in
 //     pair order;
-//  4. one wave per (key, head) sums its pairs' rows in fp32 and adds the sums to the
-//     gradient rows with ordinary loads and stores (the wave owns those rows).
+//  4. one wave per (key, head) sums its pairs' rows (each read once, non-temporal) in fp32
+//     and adds the sums to the gradient rows with ordinary loads and stores (the wave owns
+//     those rows).
 // Only entries of one query row that repeat a key take an arrival order among themselves.
 // The attention's rows of such entries are equal, so their order changes nothing there.
 #include <algorithm>
@@ -242,8 +243,20 @@ __global__ __launch_bounds__(256) void pair_reduce_kernel(const uint32_t* off, c
     using Raw = std::conditional_t<
         F32, std::conditional_t<EPL == 4, float4, std::conditional_t<EPL == 2, float2, float>>,
         std::conditional_t<EPL == 4, uint2, std::conditional_t<EPL == 2, uint32_t, uint16_t>>>;
+    // each pair row is read once: non-temporal loads (as ext-vector words of the same size)
     auto load_pair = [&](uint32_t pr) -> Raw {
-      return *reinterpret_cast<const Raw*>(rows_base + ((size_t)pr * H + h) * W + part * (W / 2) + col);
+      const void* ptr = rows_base + ((size_t)pr * H + h) * W + part * (W / 2) + col;
+      typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+      typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+      if constexpr (sizeof(Raw) == 16) {
+        return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(ptr)));
+      } else if constexpr (sizeof(Raw) == 8) {
+        return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(ptr)));
+      } else if constexpr (sizeof(Raw) == 4) {
+        return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ptr)));
+      } else {
+        return __builtin_bit_cast(Raw, __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(ptr)));
+      }
     };
     auto add_raw = [&](Raw v) {
       if constexpr (F32) {
